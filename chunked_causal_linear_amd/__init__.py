@@ -1,0 +1,184 @@
+"""Chunked causal linear attention on MI355X: thin Python binding over liblasp.so.
+
+Only argument marshalling lives here; every step runs in the HIP library.  torch
+tensors serve as device buffers and torch's current stream is the HIP stream.
+The binding raises if the library is missing: there is no fallback path.
+
+  fwd(Q, K, V, chunk, ...) -> (O, M_out, state_cache)
+  bwd(Q, K, V, dO, chunk, ...) -> (dQ, dK, dV, dM_in)
+
+Semantics, layouts and error codes are those of include/lasp.h ("Linear Attention
+Sequence Parallelism", arXiv 2404.02882, Sec. 3.2, Algorithms 2 and 3).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["fwd", "bwd", "LaspError", "lib", "Shape", "LASP_FP32", "LASP_BF16",
+           "state_cache_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblasp.so")
+LASP_FP32, LASP_BF16 = 0, 1
+_lib = None
+
+
+class LaspError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: status %d (%s)" % (what, status, _status_string(status)))
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "H", "N", "d", "chunk", "nseq")]
+
+
+def lib():
+    """The loaded liblasp.so (ImportError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("liblasp.so is not built (run __graft_entry__.build() or "
+                              "python -m chunked_causal_linear_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.c_void_p, ctypes.c_size_t
+        SP = ctypes.POINTER(Shape)
+        L.lasp_state_cache_bytes.argtypes = [SP, ctypes.c_int]
+        L.lasp_state_cache_bytes.restype = S
+        for f in (L.lasp_fwd_workspace_bytes, L.lasp_bwd_workspace_bytes):
+            f.argtypes = [SP, ctypes.c_int, ctypes.c_int]
+            f.restype = S
+        L.lasp_fwd.argtypes = [SP, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.lasp_fwd.restype = ctypes.c_int
+        L.lasp_bwd.argtypes = [SP, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.lasp_bwd.restype = ctypes.c_int
+        L.lasp_status_string.argtypes = [ctypes.c_int]
+        L.lasp_status_string.restype = ctypes.c_char_p
+        L.lasp_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _status_string(st):
+    try:
+        return lib().lasp_status_string(int(st)).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return "?"
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return LASP_BF16
+    if t.dtype == torch.float32:
+        return LASP_FP32
+    raise TypeError("Q/K/V must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _shape(Q, chunk, cu_seqlens):
+    B, H, N, d = Q.shape
+    nseq = 0 if cu_seqlens is None else int(cu_seqlens.numel()) - 1
+    return Shape(B, H, N, d, int(chunk), nseq)
+
+
+def state_cache_bytes(shape: Shape, dtype: int) -> int:
+    return int(lib().lasp_state_cache_bytes(ctypes.byref(shape), dtype))
+
+
+def fwd_workspace_bytes(shape: Shape, dtype: int, with_cache: bool) -> int:
+    return int(lib().lasp_fwd_workspace_bytes(ctypes.byref(shape), dtype, int(with_cache)))
+
+
+def bwd_workspace_bytes(shape: Shape, dtype: int, with_cache: bool) -> int:
+    return int(lib().lasp_bwd_workspace_bytes(ctypes.byref(shape), dtype, int(with_cache)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(name, t, device, dtype=None, shape=None):
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError("%s must be on %s (got %s)" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def fwd(Q, K, V, chunk, decay=None, cu_seqlens=None, M_in=None, *, want_m_out=True,
+        want_state_cache=True, out=None, workspace=None):
+    """Forward pass.  Q, K, V: [B, H, N, d] bf16 or fp32 CUDA tensors.
+    decay: float32 [H] CUDA tensor or None.  cu_seqlens: int32 [nseq+1] CUDA tensor
+    or None.  M_in: float32 [S, H, d, d] or None.  Returns (O, M_out, state_cache)
+    (M_out / state_cache are None when not requested)."""
+    import torch
+    dev = Q.device
+    S_ = _shape(Q, chunk, cu_seqlens)
+    dt = _dtype_code(Q)
+    nS = S_.nseq if S_.nseq else S_.B
+    st_shape = (nS, S_.H, S_.d, S_.d)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_dev(n, t, dev, Q.dtype, Q.shape)
+    _check_dev("decay", decay, dev, torch.float32, (S_.H,))
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    _check_dev("M_in", M_in, dev, torch.float32, st_shape)
+    O = torch.empty_like(Q) if out is None else out
+    M_out = torch.empty(st_shape, dtype=torch.float32, device=dev) if want_m_out else None
+    cache = None
+    if want_state_cache:
+        cache = torch.empty(max(1, state_cache_bytes(S_, dt)), dtype=torch.uint8, device=dev)
+    nws = fwd_workspace_bytes(S_, dt, cache is not None)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
+    rc = lib().lasp_fwd(ctypes.byref(S_), dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(decay),
+                        _ptr(cu_seqlens), _ptr(M_in), _ptr(O), _ptr(M_out), _ptr(cache),
+                        _ptr(workspace), nws, _stream(dev))
+    if rc != 0:
+        raise LaspError(rc, "lasp_fwd")
+    return O, M_out, cache
+
+
+def bwd(Q, K, V, dO, chunk, decay=None, cu_seqlens=None, M_in=None, dM_out=None,
+        state_cache=None, *, want_dm_in=True, workspace=None):
+    """Backward pass for l = <dO, O> + <dM_out, M_out>.  state_cache: the buffer
+    fwd returned for the same inputs, or None (states are recomputed).
+    Returns (dQ, dK, dV, dM_in)."""
+    import torch
+    dev = Q.device
+    S_ = _shape(Q, chunk, cu_seqlens)
+    dt = _dtype_code(Q)
+    nS = S_.nseq if S_.nseq else S_.B
+    st_shape = (nS, S_.H, S_.d, S_.d)
+    for n, t in (("Q", Q), ("K", K), ("V", V), ("dO", dO)):
+        _check_dev(n, t, dev, Q.dtype, Q.shape)
+    _check_dev("decay", decay, dev, torch.float32, (S_.H,))
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    _check_dev("M_in", M_in, dev, torch.float32, st_shape)
+    _check_dev("dM_out", dM_out, dev, torch.float32, st_shape)
+    if state_cache is not None:
+        _check_dev("state_cache", state_cache, dev, torch.uint8)
+        if state_cache.numel() < state_cache_bytes(S_, dt):
+            raise ValueError("state_cache is smaller than lasp_state_cache_bytes()")
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    dM_in = torch.empty(st_shape, dtype=torch.float32, device=dev) if want_dm_in else None
+    nws = bwd_workspace_bytes(S_, dt, state_cache is not None)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
+    rc = lib().lasp_bwd(ctypes.byref(S_), dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(decay),
+                        _ptr(cu_seqlens), _ptr(M_in), _ptr(dM_out), _ptr(state_cache),
+                        _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dM_in), _ptr(workspace), nws,
+                        _stream(dev))
+    if rc != 0:
+        raise LaspError(rc, "lasp_bwd")
+    return dQ, dK, dV, dM_in

@@ -1,0 +1,282 @@
+// C ABI of the chunked causal linear attention library: argument checks,
+// workspace / state-cache layout and kernel launches (declared in include/lasp.h).
+#include "../../include/lasp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "lasp_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+thread_local std::string g_hip_error;
+
+// Sizes derived from the shape.  G (chunks per segment) is a pure function of
+// the shape so that lasp_fwd and lasp_bwd agree on the state-cache layout.
+struct Plan {
+    int D, C, G, H, nseq, T_fixed, S_fixed, n_chunks_ub, n_segs_ub;
+    bool varlen;
+    size_t esz;          // element size of Q/K/V
+    size_t table_b;      // packed-batch tables
+    size_t local_b;      // per-chunk local states (Lc or Rc)
+    size_t seg_b;        // per-segment f32 states (Pseg, Z, Rseg or W)
+    size_t cache_b;      // state cache = [Lc][Pseg]
+};
+
+int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl) {
+    if (!s) return LASP_EINVAL;
+    if (s->B <= 0 || s->H <= 0 || s->N <= 0 || s->d <= 0 || s->chunk <= 0 || s->nseq < 0)
+        return LASP_EINVAL;
+    if (s->nseq > 0 && s->B != 1) return LASP_EINVAL;
+    if (dt != LASP_FP32 && dt != LASP_BF16) return LASP_EUNSUPPORTED;
+    if (s->d != 32 && s->d != 64 && s->d != 128) return LASP_EUNSUPPORTED;
+    if (s->chunk != 64 && s->chunk != 128 && s->chunk != 256) return LASP_EUNSUPPORTED;
+    pl.D = s->d;
+    pl.C = s->chunk;
+    pl.H = s->H;
+    pl.varlen = s->nseq > 0;
+    pl.nseq = pl.varlen ? s->nseq : s->B;
+    pl.esz = dt == LASP_BF16 ? 2 : 4;
+    const int64_t per_seq_chunks = ((int64_t)s->N + s->chunk - 1) / s->chunk;
+    int64_t chunks_ub = pl.varlen ? (int64_t)s->N / s->chunk + s->nseq
+                                  : per_seq_chunks * (int64_t)s->B;
+    // Segments: enough (segment, head) workgroups to fill the GPU, few enough
+    // segment states to keep the cross-segment scan cheap.
+    int64_t g = chunks_ub * s->H / 2048;
+    pl.G = (int)(g < 2 ? 2 : (g > 16 ? 16 : g));
+    // Test hook: LASP_SEGMENT_CHUNKS overrides G (must be the same for the
+    // forward and backward calls that share a state cache).
+    if (const char *e = getenv("LASP_SEGMENT_CHUNKS")) {
+        const long v = strtol(e, nullptr, 10);
+        if (v >= 1 && v <= (1 << 20)) pl.G = (int)v;
+    }
+    int64_t segs_ub;
+    if (pl.varlen) {
+        segs_ub = chunks_ub / pl.G + s->nseq;
+        pl.T_fixed = pl.S_fixed = 0;
+    } else {
+        pl.T_fixed = (int)per_seq_chunks;
+        pl.S_fixed = (int)((per_seq_chunks + pl.G - 1) / pl.G);
+        segs_ub = (int64_t)pl.S_fixed * s->B;
+    }
+    // grid and index limits (grids are 1-D: chunks * H workgroups)
+    if (chunks_ub * s->H > (int64_t)0x3fffffff || (int64_t)s->B * s->H * s->N > ((int64_t)1 << 40))
+        return LASP_EINVAL;
+    pl.n_chunks_ub = (int)chunks_ub;
+    pl.n_segs_ub = (int)segs_ub;
+    const size_t dd = (size_t)pl.D * pl.D;
+    pl.table_b = pl.varlen ? align_up(2 * sizeof(int32_t) * ((size_t)pl.nseq + 1)) : 0;
+    pl.local_b = align_up((size_t)pl.n_chunks_ub * pl.H * dd * pl.esz);
+    pl.seg_b = align_up((size_t)pl.n_segs_ub * pl.H * dd * sizeof(float));
+    pl.cache_b = pl.local_b + pl.seg_b;
+    return LASP_OK;
+}
+
+size_t fwd_ws(const Plan &pl, bool cache) {
+    return pl.table_b + pl.seg_b /*Z*/ + (cache ? 0 : pl.cache_b);
+}
+size_t bwd_ws(const Plan &pl, bool cache) {
+    return pl.table_b + pl.local_b /*Rc*/ + 2 * pl.seg_b /*Rseg, W*/ +
+           (cache ? 0 : pl.cache_b + pl.seg_b /*Lc, Pseg, Z*/);
+}
+
+bool misaligned(const void *p, size_t a) { return p && ((uintptr_t)p % a) != 0; }
+
+struct Range {
+    const void *p;
+    size_t n;
+};
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || !a.n || !b.n) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+// Every output range must be disjoint from every other listed range.
+bool any_overlap(const Range *outs, int no, const Range *ins, int ni) {
+    for (int i = 0; i < no; ++i) {
+        for (int j = 0; j < ni; ++j)
+            if (overlap(outs[i], ins[j])) return true;
+        for (int j = i + 1; j < no; ++j)
+            if (overlap(outs[i], outs[j])) return true;
+    }
+    return false;
+}
+
+void fill_common(lasp::Params &p, const lasp_shape *s, const Plan &pl, const int32_t *cu,
+                 const float *decay) {
+    memset(&p, 0, sizeof(p));
+    p.B = s->B;
+    p.H = s->H;
+    p.N = s->N;
+    p.nseq = pl.nseq;
+    p.D = pl.D;
+    p.C = pl.C;
+    p.G = pl.G;
+    p.varlen = pl.varlen ? 1 : 0;
+    p.T_fixed = pl.T_fixed;
+    p.S_fixed = pl.S_fixed;
+    p.n_chunks_ub = pl.n_chunks_ub;
+    p.n_segs_ub = pl.n_segs_ub;
+    p.cu = cu;
+    p.decay = decay;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return LASP_OK;
+    g_hip_error = hipGetErrorString(e);
+    return LASP_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lasp_state_cache_bytes(const lasp_shape *shape, lasp_dtype dtype) {
+    Plan pl;
+    return make_plan(shape, dtype, pl) == LASP_OK ? pl.cache_b : 0;
+}
+
+size_t lasp_fwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype, int with_state_cache) {
+    Plan pl;
+    return make_plan(shape, dtype, pl) == LASP_OK ? fwd_ws(pl, with_state_cache != 0) : 0;
+}
+
+size_t lasp_bwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype, int with_state_cache) {
+    Plan pl;
+    return make_plan(shape, dtype, pl) == LASP_OK ? bwd_ws(pl, with_state_cache != 0) : 0;
+}
+
+int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+             const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
+             void *O, float *M_out, void *state_cache, void *workspace, size_t workspace_bytes,
+             void *stream) {
+    Plan pl;
+    int rc = make_plan(shape, dtype, pl);
+    if (rc != LASP_OK) return rc;
+    if (!Q || !K || !V || !O) return LASP_EINVAL;
+    if ((shape->nseq > 0) != (cu_seqlens != nullptr)) return LASP_EINVAL;
+    const void *a16[] = {Q, K, V, O, M_in, M_out, state_cache, workspace};
+    for (const void *ptr : a16)
+        if (misaligned(ptr, 16)) return LASP_EINVAL;
+    if (misaligned(decay, 4) || misaligned(cu_seqlens, 4)) return LASP_EINVAL;
+    const bool cache = state_cache != nullptr;
+    const size_t need = fwd_ws(pl, cache);
+    if (workspace_bytes < need || (need && !workspace)) return LASP_EWORKSPACE;
+
+    const size_t tens = (size_t)shape->B * shape->H * shape->N * shape->d * pl.esz;
+    const size_t st = (size_t)pl.nseq * pl.H * pl.D * pl.D * sizeof(float);
+    const Range ins[] = {{Q, tens}, {K, tens}, {V, tens}, {M_in, st},
+                         {decay, (size_t)pl.H * 4},
+                         {cu_seqlens, cu_seqlens ? ((size_t)pl.nseq + 1) * 4 : 0}};
+    const Range outs[] = {{O, tens}, {M_out, st}, {state_cache, cache ? pl.cache_b : 0},
+                          {workspace, need}};
+    if (any_overlap(outs, 4, ins, 6)) return LASP_EINVAL;
+
+    lasp::Params p;
+    fill_common(p, shape, pl, cu_seqlens, decay);
+    p.Q = Q;
+    p.K = K;
+    p.V = V;
+    p.O = O;
+    p.M_in = M_in;
+    p.M_out = M_out;
+    char *w = (char *)workspace;
+    if (pl.varlen) {
+        p.chunk_prefix = (int32_t *)w;
+        p.seg_prefix = p.chunk_prefix + (pl.nseq + 1);
+        w += pl.table_b;
+    }
+    p.Z = (float *)w;
+    w += pl.seg_b;
+    char *c = cache ? (char *)state_cache : w;
+    p.Lc = c;
+    p.Pseg = (float *)(c + pl.local_b);
+    return hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, true, (hipStream_t)stream));
+}
+
+int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+             const void *V, const void *dO, const float *decay, const int32_t *cu_seqlens,
+             const float *M_in, const float *dM_out, const void *state_cache, void *dQ, void *dK,
+             void *dV, float *dM_in, void *workspace, size_t workspace_bytes, void *stream) {
+    Plan pl;
+    int rc = make_plan(shape, dtype, pl);
+    if (rc != LASP_OK) return rc;
+    if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return LASP_EINVAL;
+    if ((shape->nseq > 0) != (cu_seqlens != nullptr)) return LASP_EINVAL;
+    const void *a16[] = {Q, K, V, dO, M_in, dM_out, state_cache, dQ, dK, dV, dM_in, workspace};
+    for (const void *ptr : a16)
+        if (misaligned(ptr, 16)) return LASP_EINVAL;
+    if (misaligned(decay, 4) || misaligned(cu_seqlens, 4)) return LASP_EINVAL;
+    const bool cache = state_cache != nullptr;
+    const size_t need = bwd_ws(pl, cache);
+    if (workspace_bytes < need || (need && !workspace)) return LASP_EWORKSPACE;
+
+    const size_t tens = (size_t)shape->B * shape->H * shape->N * shape->d * pl.esz;
+    const size_t st = (size_t)pl.nseq * pl.H * pl.D * pl.D * sizeof(float);
+    const Range ins[] = {{Q, tens}, {K, tens}, {V, tens}, {dO, tens}, {M_in, st}, {dM_out, st},
+                         {state_cache, cache ? pl.cache_b : 0},
+                         {decay, (size_t)pl.H * 4},
+                         {cu_seqlens, cu_seqlens ? ((size_t)pl.nseq + 1) * 4 : 0}};
+    const Range outs[] = {{dQ, tens}, {dK, tens}, {dV, tens}, {dM_in, st}, {workspace, need}};
+    if (any_overlap(outs, 5, ins, 9)) return LASP_EINVAL;
+
+    lasp::Params p;
+    fill_common(p, shape, pl, cu_seqlens, decay);
+    p.Q = Q;
+    p.K = K;
+    p.V = V;
+    p.dO = dO;
+    p.dQ = dQ;
+    p.dK = dK;
+    p.dV = dV;
+    p.M_in = M_in;
+    p.dM_out = dM_out;
+    p.dM_in = dM_in;
+    char *w = (char *)workspace;
+    if (pl.varlen) {
+        p.chunk_prefix = (int32_t *)w;
+        p.seg_prefix = p.chunk_prefix + (pl.nseq + 1);
+        w += pl.table_b;
+    }
+    p.Rc = w;
+    w += pl.local_b;
+    p.Rseg = (float *)w;
+    w += pl.seg_b;
+    p.W = (float *)w;
+    w += pl.seg_b;
+    const hipStream_t hs = (hipStream_t)stream;
+    if (cache) {
+        p.Lc = const_cast<void *>(state_cache);
+        p.Pseg = (float *)((char *)state_cache + pl.local_b);
+    } else {   // recompute the forward states (no output, no M_out)
+        p.Lc = w;
+        p.Pseg = (float *)(w + pl.local_b);
+        p.Z = (float *)(w + pl.cache_b);
+        rc = hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, false, hs));
+        if (rc != LASP_OK) return rc;
+    }
+    return hip_status(lasp::launch_bwd(p, dtype == LASP_BF16, hs));
+}
+
+const char *lasp_status_string(int status) {
+    switch (status) {
+    case LASP_OK: return "ok";
+    case LASP_EINVAL: return "invalid argument";
+    case LASP_EUNSUPPORTED: return "unsupported configuration (d in {32,64,128}, chunk in {64,128,256}, dtype fp32/bf16)";
+    case LASP_EWORKSPACE: return "workspace too small";
+    case LASP_EHIP: return g_hip_error.empty() ? "HIP error" : g_hip_error.c_str();
+    }
+    return "unknown status";
+}
+
+int lasp_version(void) { return 100; }
+
+}  // extern "C"

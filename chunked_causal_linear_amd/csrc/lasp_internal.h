@@ -1,0 +1,46 @@
+// Internal interface between the C ABI (lasp_api.cpp) and the HIP kernels
+// (lasp_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lasp {
+
+// Everything a kernel needs, by value in the kernel argument segment.
+//
+// Work decomposition (one head h of one sequence i, T chunks of length C, the
+// last one possibly shorter):
+//   chunks are numbered globally (over sequences) gc = c0(i) + t;
+//   G consecutive chunks form a segment, numbered globally gs = s0(i) + t / G.
+// State arrays are indexed [(global index) * H + h][D][D].
+struct Params {
+    int B, H, N;        // N: tokens per sequence (packed batch: total tokens)
+    int nseq;           // number of sequences: B, or the packed count
+    int D, C, G;        // head dim, chunk length, chunks per segment
+    int varlen;         // 1: packed batch described by cu
+    int T_fixed, S_fixed;          // chunks / segments per sequence (not packed)
+    int n_chunks_ub, n_segs_ub;    // grid bounds (upper bounds when packed)
+    const int32_t *cu;             // [nseq+1] device (packed)
+    int32_t *chunk_prefix;         // [nseq+1] device (packed): first global chunk
+    int32_t *seg_prefix;           // [nseq+1] device (packed): first global segment
+    const float *decay;            // [H] device or null
+    const void *Q, *K, *V, *dO;
+    void *O, *dQ, *dK, *dV;
+    const float *M_in, *dM_out;    // [nseq][H][D][D] or null
+    float *M_out, *dM_in;          // [nseq][H][D][D] or null
+    void *Lc;      // [chunks][H][D][D] elem: local prefix state entering each chunk, [dv][dk]
+    float *Pseg;   // [segs][H][D][D] f32: state entering each segment, [dv][dk]
+    float *Z;      // [segs][H][D][D] f32: local state at each segment end, [dv][dk]
+    void *Rc;      // [chunks][H][D][D] elem: local reverse state of each chunk, [dv][dk]
+    float *Rseg;   // [segs][H][D][D] f32: reverse state entering each segment's last chunk
+    float *W;      // [segs][H][D][D] f32: local reverse state at each segment start
+};
+
+// Enqueue the forward kernels: (packed-batch tables), local chunk states,
+// segment scan, and (if with_output) the output kernel.
+hipError_t launch_fwd(const Params &p, bool bf16, bool with_output, hipStream_t stream);
+// Enqueue the backward kernels: (tables), reverse local states, reverse
+// segment scan, gradient kernel.  The forward states (Lc, Pseg) must be valid.
+hipError_t launch_bwd(const Params &p, bool bf16, hipStream_t stream);
+
+}  // namespace lasp

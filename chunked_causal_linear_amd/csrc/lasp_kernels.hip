@@ -1,0 +1,962 @@
+// HIP kernels (gfx950 / MI355X) for chunked causal linear attention.
+//
+// Sources: "Linear Attention Sequence Parallelism" (arXiv 2404.02882), Sec. 3.2:
+// chunk decomposition into intra-chunk (Eq. 7) and inter-chunk (Eq. 9) terms,
+// the chunk state update (Eq. 10), backward terms (Eqs. 14-23); and the LASP-2
+// review page (arXiv 2502.07563): chunk memory states M_t and their prefix /
+// suffix sums replace the serial exchange.
+//
+// Notation (one head of one sequence, chunk t of length C_t, 0-based row i):
+//   D_t[i][j]  = lambda^(i-j) for i >= j else 0      (the decayed causal mask)
+//   Lam_t      = diag(lambda^(i+1))                   (Lambda of Alg. 2)
+//   Gam_t      = diag(lambda^(C_t-1-j))               (lambda^C Lambda^-1 of Eq. 10)
+//   P_t        = state entering chunk t (the cached KV_{t-1})
+//   R_t        = reverse state entering chunk t from the right (dKV_{t+1})
+//   fwd:  O_t  = [(Q_t K_t^T) . D_t] V_t + Lam_t Q_t P_t
+//         P_{t+1} = lambda^C_t P_t + (Gam_t K_t)^T V_t
+//   bwd:  R_{t-1} = lambda^C_t R_t + (Lam_t Q_t)^T dO_t
+//         dQ_t = [(dO_t V_t^T) . D_t] K_t + Lam_t dO_t P_t^T
+//         dK_t = [(dO_t V_t^T) . D_t]^T Q_t + Gam_t V_t R_t^T
+//         dV_t = [(Q_t K_t^T) . D_t]^T dO_t + Gam_t K_t R_t
+//
+// The serial recurrence over chunks is split two-level for parallelism: G
+// chunks form a segment; one workgroup per (segment, head) sweeps its chunks
+// carrying a local state in MFMA accumulators (k_*_local), a small scan carries
+// states across segments (k_*_segscan), and the output / gradient kernels run
+// one workgroup per (chunk, head), combining the segment state with the local
+// one.  All products run on MFMA (32x32x16 bf16 or 32x32x2 f32) with operands
+// staged in LDS so that the contraction index is contiguous for every operand.
+#include "lasp_internal.h"
+
+namespace lasp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16 {
+    uint16_t u;
+};
+
+template <typename T> struct Tr;
+template <> struct Tr<float> {
+    using frag = f32x4;
+    static constexpr int VEC = 4;   // elements per 16 bytes
+};
+template <> struct Tr<bf16> {
+    using frag = bf16x8_t;
+    static constexpr int VEC = 8;
+};
+
+constexpr int NTHR = 256;   // 4 waves of 64
+constexpr int NWAVE = 4;
+
+// ---------------------------------------------------------------------------
+// MFMA micro-kernel.  32x32 output tile, fp32 accumulate.  Lane l holds, for
+// both element types, output rows (r/4)*8 + (l/32)*4 + r%4 (r = 0..15) of
+// column l%32.  An operand fragment is 16 bytes per lane: row (l%32) of A (or
+// column of B), contraction elements [(l/32)*VEC, (l/32)*VEC + VEC) of a
+// 2*VEC-wide k-step.  bf16: one 32x32x16 MFMA; f32: four 32x32x2 MFMAs where
+// step s pairs element s of both lane halves (A and B agree on the pairing).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void mma(f32x16 &c, const bf16x8_t &a, const bf16x8_t &b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16 &c, const f32x4 &a, const f32x4 &b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], b[3], c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Row (within the 32x32 tile) of accumulator element r for this lane.
+__device__ __forceinline__ int crow(int r) {
+    return (r >> 2) * 8 + ((threadIdx.x & 63) >> 5) * 4 + (r & 3);
+}
+
+__device__ __forceinline__ float tof(float x) { return x; }
+__device__ __forceinline__ float tof(bf16 x) { return __uint_as_float(((uint32_t)x.u) << 16); }
+template <typename T> __device__ __forceinline__ T fromf(float x);
+template <> __device__ __forceinline__ float fromf<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 fromf<bf16>(float x) {
+    __bf16 h = (__bf16)x;   // round to nearest even (v_cvt_pk_bf16_f32)
+    bf16 r;
+    r.u = __builtin_bit_cast(uint16_t, h);
+    return r;
+}
+
+// 16-byte load of VEC elements, widened to float.
+__device__ __forceinline__ void load16(const float *p, float *f) {
+    float4 v = *(const float4 *)p;
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+}
+__device__ __forceinline__ void load16(const bf16 *p, float *f) {
+    uint4 v = *(const uint4 *)p;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+// Store 4 consecutive values (converted) at p.
+__device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
+    *(float4 *)p = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16 *p, float a, float b, float c, float d) {
+    const uint32_t lo = (uint32_t)fromf<bf16>(a).u | ((uint32_t)fromf<bf16>(b).u << 16);
+    const uint32_t hi = (uint32_t)fromf<bf16>(c).u | ((uint32_t)fromf<bf16>(d).u << 16);
+    *(uint2 *)p = make_uint2(lo, hi);
+}
+
+// lambda^e with lambda = 2^l2; lambda^0 = 1 exactly (also for lambda = 0).
+__device__ __forceinline__ float dpow(float l2, float e) {
+    return e == 0.f ? 1.f : exp2f(e * l2);
+}
+__device__ __forceinline__ float head_log2_decay(const Params &p, int h) {
+    return p.decay ? log2f(p.decay[h]) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Sequence bookkeeping
+// ---------------------------------------------------------------------------
+struct Seq {
+    int i;          // sequence index
+    int64_t tok0;   // first token (packed batch: offset inside N)
+    int len;        // tokens
+    int T, S;       // chunks, segments
+    int c0, s0;     // first global chunk / segment
+};
+
+__device__ __forceinline__ int last_le(const int32_t *pre, int n, int x) {
+    // largest i in [0, n) with pre[i] <= x (pre non-decreasing, pre[0] = 0)
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Token range of packed sequence i, clamped into [0, N] so that malformed
+// cu_seqlens can never address outside the tensors.
+__device__ __forceinline__ void packed_bounds(const Params &p, int i, int &tok0, int &len) {
+    const int a = min(max(p.cu[i], 0), p.N);
+    const int b = min(max(p.cu[i + 1], a), p.N);
+    tok0 = a;
+    len = b - a;
+}
+
+__device__ __forceinline__ void seq_fill(const Params &p, int i, Seq &s) {
+    s.i = i;
+    if (!p.varlen) {
+        s.tok0 = 0;
+        s.len = p.N;
+        s.T = p.T_fixed;
+        s.S = p.S_fixed;
+        s.c0 = i * p.T_fixed;
+        s.s0 = i * p.S_fixed;
+    } else {
+        int tok0, len;
+        packed_bounds(p, i, tok0, len);
+        s.tok0 = tok0;
+        s.len = len;
+        s.c0 = p.chunk_prefix[i];
+        s.T = p.chunk_prefix[i + 1] - s.c0;
+        s.s0 = p.seg_prefix[i];
+        s.S = p.seg_prefix[i + 1] - s.s0;
+    }
+}
+
+// Global chunk gc -> (sequence, local chunk t).  False if gc is past the end.
+__device__ __forceinline__ bool chunk_seq(const Params &p, int gc, Seq &s, int &t) {
+    int i;
+    if (!p.varlen) {
+        if (gc >= p.nseq * p.T_fixed) return false;
+        i = gc / p.T_fixed;
+    } else {
+        if (gc >= p.chunk_prefix[p.nseq]) return false;
+        i = last_le(p.chunk_prefix, p.nseq, gc);
+    }
+    seq_fill(p, i, s);
+    t = gc - s.c0;
+    return gc < p.n_chunks_ub;
+}
+
+__device__ __forceinline__ bool seg_seq(const Params &p, int gs, Seq &s, int &sl) {
+    int i;
+    if (!p.varlen) {
+        if (gs >= p.nseq * p.S_fixed) return false;
+        i = gs / p.S_fixed;
+    } else {
+        if (gs >= p.seg_prefix[p.nseq]) return false;
+        i = last_le(p.seg_prefix, p.nseq, gs);
+    }
+    seq_fill(p, i, s);
+    sl = gs - s.s0;
+    return gs < p.n_segs_ub;
+}
+
+// First row (token) of sequence s, head h, in the [B, H, N, d] layout.
+__device__ __forceinline__ int64_t row_base(const Params &p, const Seq &s, int h) {
+    return p.varlen ? ((int64_t)h * p.N + s.tok0) : (((int64_t)s.i * p.H + h) * p.N);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Map ids so
+// that each XCD gets a contiguous range of logical work items: neighbouring
+// chunks of one head then share that XCD's L2.  n is a multiple of 8.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    return (bid & 7) * (n >> 3) + (bid >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// LDS staging and tile GEMM helpers (all 256 threads take part in staging)
+// ---------------------------------------------------------------------------
+// dst[r][c] = src[r][c] for a R x W tile; rows >= nvalid become zero.
+template <typename T, int R, int W>
+__device__ __forceinline__ void stage_rows(T *dst, int pitch, const T *src, int nvalid) {
+    constexpr int V = Tr<T>::VEC;
+    constexpr int PR = W / V;
+    for (int i = threadIdx.x; i < R * PR; i += NTHR) {
+        const int r = i / PR, c = (i % PR) * V;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < nvalid) v = *(const uint4 *)(src + (int64_t)r * W + c);
+        *(uint4 *)(dst + r * pitch + c) = v;
+    }
+}
+
+// dst[c][r] = scale(r) * src[r][c] (transposed, token index contiguous);
+// rows >= nvalid become zero.
+template <typename T, int R, int W, typename F>
+__device__ __forceinline__ void stage_rows_T(T *dst, int pitch, const T *src, int nvalid,
+                                             F scale) {
+    constexpr int V = Tr<T>::VEC;
+    for (int i = threadIdx.x; i < R * (W / V); i += NTHR) {
+        const int r = i % R, c = (i / R) * V;
+        float f[V];
+        if (r < nvalid) {
+            load16(src + (int64_t)r * W + c, f);
+            const float s = scale(r);
+#pragma unroll
+            for (int e = 0; e < V; ++e) f[e] *= s;
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) f[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) dst[(c + e) * pitch + r] = fromf<T>(f[e]);
+    }
+}
+
+struct One {
+    __device__ float operator()(int) const { return 1.f; }
+};
+
+// acc += A[m0..m0+32)[0..K) * B[n0..n0+32)[0..K)^T, A and B in LDS with the
+// contraction index contiguous (pitches pa, pb in elements).
+template <typename T, int K>
+__device__ __forceinline__ void gemm(f32x16 &acc, const T *As, int pa, int m0, const T *Bs,
+                                     int pb, int n0) {
+    constexpr int V = Tr<T>::VEC;
+    using Fr = typename Tr<T>::frag;
+    const int l = lane_id();
+    const T *ap = As + (m0 + (l & 31)) * pa + (l >> 5) * V;
+    const T *bp = Bs + (n0 + (l & 31)) * pb + (l >> 5) * V;
+#pragma unroll
+    for (int k = 0; k < K; k += 2 * V) {
+        const Fr a = *(const Fr *)(ap + k);
+        const Fr b = *(const Fr *)(bp + k);
+        mma(acc, a, b);
+    }
+}
+
+// Y[n0 + col][m0 + row] = f(acc, m0 + row, n0 + col): transposed store of a
+// 32x32 tile (4 consecutive rows per lane per store).  Y in LDS or global.
+template <typename T, typename F>
+__device__ __forceinline__ void store_T(const f32x16 &acc, T *Y, int64_t py, int m0, int n0,
+                                        F f) {
+    const int l = lane_id(), col = l & 31, g = l >> 5;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int m = m0 + q * 8 + g * 4;
+        store4(Y + (int64_t)(n0 + col) * py + m, f(acc[q * 4 + 0], m + 0, n0 + col),
+               f(acc[q * 4 + 1], m + 1, n0 + col), f(acc[q * 4 + 2], m + 2, n0 + col),
+               f(acc[q * 4 + 3], m + 3, n0 + col));
+    }
+}
+
+struct Ident {
+    __device__ float operator()(float x, int, int) const { return x; }
+};
+
+// G[(m0+row)][n0+col] = acc for rows < nvalid (row-major global store).
+template <typename T>
+__device__ __forceinline__ void store_rows(const f32x16 &acc, T *G, int64_t ld, int m0, int n0,
+                                           int nvalid) {
+    const int col = lane_id() & 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = m0 + crow(r);
+        if (row < nvalid) G[(int64_t)row * ld + n0 + col] = fromf<T>(acc[r]);
+    }
+}
+
+// Tiles of a (MT*32) x (NT*32) output are dealt to the 4 waves round-robin.
+template <int MT, int NT>
+struct Tiles {
+    static constexpr int N = MT * NT;
+    static constexpr int PER_WAVE = (N + NWAVE - 1) / NWAVE;
+    __device__ static bool get(int k, int &mi, int &ni) {
+        const int tile = wave_id() + k * NWAVE;
+        mi = tile / NT;
+        ni = tile % NT;
+        return tile < N;
+    }
+};
+
+__device__ __forceinline__ void zero(f32x16 &a) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[r] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Packed-batch tables: chunk_prefix[i] = sum_{i'<i} ceil(L_i'/C),
+// seg_prefix[i] = sum_{i'<i} ceil(T_i'/G).  One workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NTHR) void k_setup(Params p) {
+    __shared__ int sc[NTHR], ss[NTHR];
+    __shared__ int carry_c, carry_s;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        carry_c = 0;
+        carry_s = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base < p.nseq; base += NTHR) {
+        const int i = base + tid;
+        int tc = 0, ts = 0;
+        if (i < p.nseq) {
+            int t0, L;
+            packed_bounds(p, i, t0, L);
+            tc = L > 0 ? (L + p.C - 1) / p.C : 0;
+            ts = (tc + p.G - 1) / p.G;
+        }
+        sc[tid] = tc;
+        ss[tid] = ts;
+        __syncthreads();
+        for (int off = 1; off < NTHR; off <<= 1) {   // inclusive scan
+            const int a = tid >= off ? sc[tid - off] : 0;
+            const int b = tid >= off ? ss[tid - off] : 0;
+            __syncthreads();
+            sc[tid] += a;
+            ss[tid] += b;
+            __syncthreads();
+        }
+        if (i < p.nseq) {
+            p.chunk_prefix[i] = carry_c + sc[tid] - tc;
+            p.seg_prefix[i] = carry_s + ss[tid] - ts;
+        }
+        __syncthreads();
+        if (tid == NTHR - 1) {
+            carry_c += sc[tid];
+            carry_s += ss[tid];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        p.chunk_prefix[p.nseq] = carry_c;
+        p.seg_prefix[p.nseq] = carry_s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward 1: local states.  One workgroup per (segment, head).  Sweeps the
+// segment's chunks in order, with L = 0 at the segment start:
+//   Lc[t] = L (stored, bf16/f32, [dv][dk]);  L = lambda^C_t L + (Gam_t K_t)^T V_t
+// and finally Z[segment] = L (f32).  (LASP Eq. 10 / Alg. 2 state update;
+// LASP-2's M_t = K_t^T V_t accumulated.)
+// ---------------------------------------------------------------------------
+template <typename T, int D, int BT>
+__global__ __launch_bounds__(NTHR) void k_fwd_local(Params p) {
+    constexpr int PT = BT + Tr<T>::VEC;
+    __shared__ __attribute__((aligned(16))) T KT_s[D * PT];
+    __shared__ __attribute__((aligned(16))) T VT_s[D * PT];
+    using TL = Tiles<D / 32, D / 32>;
+
+    const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
+    Seq s;
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const float l2 = head_log2_decay(p, h);
+    const int64_t rb = row_base(p, s, h);
+    const T *K = (const T *)p.K + rb * D;
+    const T *V = (const T *)p.V + rb * D;
+    const bool store_local = p.G > 1;
+
+    f32x16 acc[TL::PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) zero(acc[k]);
+
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    for (int t = t0; t < t1; ++t) {
+        const int tok = t * p.C;
+        const int Ct = min(p.C, s.len - tok);
+        if (store_local) {
+            T *Lt = (T *)p.Lc + ((int64_t)(s.c0 + t) * p.H + h) * D * D;
+#pragma unroll
+            for (int k = 0; k < TL::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TL::get(k, mi, ni)) store_T(acc[k], Lt, D, mi * 32, ni * 32, Ident());
+            }
+        }
+        const float dc = dpow(l2, (float)Ct);
+#pragma unroll
+        for (int k = 0; k < TL::PER_WAVE; ++k) acc[k] *= dc;
+        for (int b0 = 0; b0 < Ct; b0 += BT) {
+            const int nv = min(BT, Ct - b0);
+            __syncthreads();
+            stage_rows_T<T, BT, D>(KT_s, PT, K + (int64_t)(tok + b0) * D, nv,
+                                   [&](int r) { return dpow(l2, (float)(Ct - 1 - (b0 + r))); });
+            stage_rows_T<T, BT, D>(VT_s, PT, V + (int64_t)(tok + b0) * D, nv, One());
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < TL::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TL::get(k, mi, ni)) gemm<T, BT>(acc[k], KT_s, PT, mi * 32, VT_s, PT, ni * 32);
+            }
+        }
+    }
+    float *Zs = p.Z + ((int64_t)gs * p.H + h) * D * D;
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) {
+        int mi, ni;
+        if (TL::get(k, mi, ni)) store_T(acc[k], Zs, D, mi * 32, ni * 32, Ident());
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward 2: scan over segments, one thread per state element.
+//   Pseg[0] = M_in;  Pseg[s+1] = lambda^len_s Pseg[s] + Z[s];  M_out = last.
+// (LASP-2 prefix sum of gathered states; LASP Alg. 2 receive/send as a scan.)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NTHR) void k_fwd_segscan(Params p) {
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    const int ih = blockIdx.x / NB;
+    const int e = (blockIdx.x % NB) * NTHR + threadIdx.x;
+    if (e >= D * D) return;
+    const int i = ih / p.H, h = ih % p.H;
+    Seq s;
+    seq_fill(p, i, s);
+    const float l2 = head_log2_decay(p, h);
+    const int dv = e / D, dk = e % D;
+    const int64_t mo = ((int64_t)ih * D + dk) * D + dv;   // [dk][dv] of the API states
+    float P = p.M_in ? p.M_in[mo] : 0.f;
+    const int seg_tokens = p.G * p.C;
+    const int nS = min(s.S, p.n_segs_ub - s.s0);
+    for (int sl = 0; sl < nS; ++sl) {
+        const int64_t idx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D + e;
+        p.Pseg[idx] = P;
+        const int len_s = min(seg_tokens, s.len - sl * seg_tokens);
+        P = dpow(l2, (float)len_s) * P + p.Z[idx];
+    }
+    if (p.M_out) p.M_out[mo] = P;
+}
+
+// ---------------------------------------------------------------------------
+// Forward 3: output, one workgroup per (chunk, head).
+//   O_t = [(Q_t K_t^T) . D_t] V_t + Lam_t Q_t P_t      (LASP Eqs. 7, 9, 11)
+// with P_t = lambda^off Pseg + Lc[t] (off = tokens from the segment start).
+// Query blocks of 64 rows; key blocks 0..qb; the score tile is computed
+// transposed (keys x queries) so that its transposed store gives the A operand.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int BT>
+__global__ __launch_bounds__(NTHR) void k_fwd_out(Params p) {
+    constexpr int V = Tr<T>::VEC;
+    constexpr int PD = D + V;    // pitch: feature-contiguous rows
+    constexpr int PT = BT + V;   // pitch: token-contiguous rows
+    __shared__ __attribute__((aligned(16))) T PT_s[D * PD];   // P^T [dv][dk]
+    __shared__ __attribute__((aligned(16))) T Q_s[BT * PD];
+    __shared__ __attribute__((aligned(16))) T K_s[BT * PD];
+    __shared__ __attribute__((aligned(16))) T VT_s[D * PT];   // V^T [dv][key]
+    __shared__ __attribute__((aligned(16))) T S_s[BT * PT];   // masked scores [query][key]
+    using TO = Tiles<BT / 32, D / 32>;
+    using TS = Tiles<BT / 32, BT / 32>;
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = lid % p.H, gc = lid / p.H;
+    Seq s;
+    int t;
+    if (!chunk_seq(p, gc, s, t)) return;
+    const float l2 = head_log2_decay(p, h);
+    const int tok = t * p.C;
+    const int Ct = min(p.C, s.len - tok);
+    const int sl = t / p.G;
+    if (s.s0 + sl >= p.n_segs_ub) return;   // only with malformed cu_seqlens
+    const int off = (t - sl * p.G) * p.C;
+    const int64_t rb = row_base(p, s, h) + tok;
+    const T *Q = (const T *)p.Q + rb * D;
+    const T *K = (const T *)p.K + rb * D;
+    const T *Vg = (const T *)p.V + rb * D;
+    T *O = (T *)p.O + rb * D;
+
+    {   // P_t^T into LDS
+        const float *Ps = p.Pseg + ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
+        const T *Lt = (const T *)p.Lc + ((int64_t)(s.c0 + t) * p.H + h) * D * D;
+        const float doff = dpow(l2, (float)off);
+        const bool has_local = p.G > 1;
+        for (int e = threadIdx.x * V; e < D * D; e += NTHR * V) {
+            float pf[V], lf[V];
+#pragma unroll
+            for (int j = 0; j < V; j += 4) load16(Ps + e + j, pf + j);
+            if (has_local) load16(Lt + e, lf);
+            else {
+#pragma unroll
+                for (int j = 0; j < V; ++j) lf[j] = 0.f;
+            }
+            const int dv = e / D, dk = e % D;
+#pragma unroll
+            for (int j = 0; j < V; ++j) PT_s[dv * PD + dk + j] = fromf<T>(doff * pf[j] + lf[j]);
+        }
+    }
+
+    const int nb = (Ct + BT - 1) / BT;
+    for (int qb = 0; qb < nb; ++qb) {
+        const int nvq = min(BT, Ct - qb * BT);
+        __syncthreads();
+        stage_rows<T, BT, D>(Q_s, PD, Q + (int64_t)qb * BT * D, nvq);
+        __syncthreads();
+        f32x16 o[TO::PER_WAVE];
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            zero(o[k]);
+            int mi, ni;
+            if (TO::get(k, mi, ni)) {
+                gemm<T, D>(o[k], Q_s, PD, mi * 32, PT_s, PD, ni * 32);   // Q_t P_t
+#pragma unroll
+                for (int r = 0; r < 16; ++r)                              // Lam_t rows
+                    o[k][r] *= dpow(l2, (float)(qb * BT + mi * 32 + crow(r) + 1));
+            }
+        }
+        for (int kb = 0; kb <= qb; ++kb) {
+            const int nvk = min(BT, Ct - kb * BT);
+            __syncthreads();
+            stage_rows<T, BT, D>(K_s, PD, K + (int64_t)kb * BT * D, nvk);
+            stage_rows_T<T, BT, D>(VT_s, PT, Vg + (int64_t)kb * BT * D, nvk, One());
+            __syncthreads();
+            {   // S^T tiles (keys x queries)
+                for (int k = 0; k < TS::PER_WAVE; ++k) {
+                    int mi, ni;
+                    if (!TS::get(k, mi, ni)) continue;
+                    f32x16 st;
+                    zero(st);
+                    gemm<T, D>(st, K_s, PD, mi * 32, Q_s, PD, ni * 32);
+                    store_T(st, S_s, PT, mi * 32, ni * 32, [&](float x, int j, int i) {
+                        const int gi = qb * BT + i, gj = kb * BT + j;
+                        return (gi >= gj && gi < Ct) ? x * dpow(l2, (float)(gi - gj)) : 0.f;
+                    });
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < TO::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TO::get(k, mi, ni)) gemm<T, BT>(o[k], S_s, PT, mi * 32, VT_s, PT, ni * 32);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (TO::get(k, mi, ni))
+                store_rows(o[k], O + (int64_t)qb * BT * D, D, mi * 32, ni * 32, nvq);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward 1: local reverse states, one workgroup per (segment, head), chunks
+// swept last to first with Rl = 0 at the segment end:
+//   Rc[t] = Rl;  Rl = lambda^C_t Rl + (Lam_t Q_t)^T dO_t;   W[segment] = Rl.
+// (LASP Eq. 20 / Alg. 3 dKV update; LASP-2 suffix sums of dM_t.)
+// ---------------------------------------------------------------------------
+template <typename T, int D, int BT>
+__global__ __launch_bounds__(NTHR) void k_bwd_local(Params p) {
+    constexpr int PT = BT + Tr<T>::VEC;
+    __shared__ __attribute__((aligned(16))) T QT_s[D * PT];
+    __shared__ __attribute__((aligned(16))) T OT_s[D * PT];
+    using TL = Tiles<D / 32, D / 32>;
+
+    const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
+    Seq s;
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const float l2 = head_log2_decay(p, h);
+    const int64_t rb = row_base(p, s, h);
+    const T *Q = (const T *)p.Q + rb * D;
+    const T *dO = (const T *)p.dO + rb * D;
+    const bool store_local = p.G > 1;
+
+    f32x16 acc[TL::PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) zero(acc[k]);
+
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    for (int t = t1 - 1; t >= t0; --t) {
+        const int tok = t * p.C;
+        const int Ct = min(p.C, s.len - tok);
+        if (store_local) {
+            T *Rt = (T *)p.Rc + ((int64_t)(s.c0 + t) * p.H + h) * D * D;
+#pragma unroll
+            for (int k = 0; k < TL::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TL::get(k, mi, ni)) store_T(acc[k], Rt, D, mi * 32, ni * 32, Ident());
+            }
+        }
+        const float dc = dpow(l2, (float)Ct);
+#pragma unroll
+        for (int k = 0; k < TL::PER_WAVE; ++k) acc[k] *= dc;
+        for (int b0 = 0; b0 < Ct; b0 += BT) {
+            const int nv = min(BT, Ct - b0);
+            __syncthreads();
+            stage_rows_T<T, BT, D>(QT_s, PT, Q + (int64_t)(tok + b0) * D, nv,
+                                   [&](int r) { return dpow(l2, (float)(b0 + r + 1)); });
+            stage_rows_T<T, BT, D>(OT_s, PT, dO + (int64_t)(tok + b0) * D, nv, One());
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < TL::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TL::get(k, mi, ni)) gemm<T, BT>(acc[k], QT_s, PT, mi * 32, OT_s, PT, ni * 32);
+            }
+        }
+    }
+    float *Ws = p.W + ((int64_t)gs * p.H + h) * D * D;
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) {
+        int mi, ni;
+        if (TL::get(k, mi, ni)) store_T(acc[k], Ws, D, mi * 32, ni * 32, Ident());
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward 2: reverse scan over segments, one thread per state element.
+//   Rseg[S-1] = dM_out;  Rseg[s-1] = lambda^len_s Rseg[s] + W[s];  dM_in = last.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NTHR) void k_bwd_segscan(Params p) {
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    const int ih = blockIdx.x / NB;
+    const int e = (blockIdx.x % NB) * NTHR + threadIdx.x;
+    if (e >= D * D) return;
+    const int i = ih / p.H, h = ih % p.H;
+    Seq s;
+    seq_fill(p, i, s);
+    const float l2 = head_log2_decay(p, h);
+    const int dv = e / D, dk = e % D;
+    const int64_t mo = ((int64_t)ih * D + dk) * D + dv;
+    float R = p.dM_out ? p.dM_out[mo] : 0.f;
+    const int seg_tokens = p.G * p.C;
+    const int nS = min(s.S, p.n_segs_ub - s.s0);
+    for (int sl = nS - 1; sl >= 0; --sl) {
+        const int64_t idx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D + e;
+        p.Rseg[idx] = R;
+        const int len_s = min(seg_tokens, s.len - sl * seg_tokens);
+        R = dpow(l2, (float)len_s) * R + p.W[idx];
+    }
+    if (p.dM_in) p.dM_in[mo] = R;
+}
+
+// Combine a segment state and a local state into LDS:
+//   X = scale * seg[dv][dk] + loc[dv][dk];  stored as Y[dv][dk] (transpose =
+//   false) or Y[dk][dv] (transpose = true).
+template <typename T, int D>
+__device__ __forceinline__ void combine_state(T *Y, int py, const float *seg, const T *loc,
+                                              float scale, bool transpose) {
+    constexpr int V = Tr<T>::VEC;
+    for (int e = threadIdx.x * V; e < D * D; e += NTHR * V) {
+        float pf[V], lf[V];
+#pragma unroll
+        for (int j = 0; j < V; j += 4) load16(seg + e + j, pf + j);
+        if (loc) load16(loc + e, lf);
+        else {
+#pragma unroll
+            for (int j = 0; j < V; ++j) lf[j] = 0.f;
+        }
+        const int dv = e / D, dk = e % D;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const T x = fromf<T>(scale * pf[j] + lf[j]);
+            if (transpose) Y[(dk + j) * py + dv] = x;
+            else Y[dv * py + dk + j] = x;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward 3: gradients, one workgroup per (chunk, head), three phases that
+// share one LDS footprint:
+//   A  dQ_t = [(dO_t V_t^T) . D_t] K_t + Lam_t dO_t P_t^T      (LASP Eqs. 14, 16)
+//   B  dV_t = [(Q_t K_t^T) . D_t]^T dO_t + Gam_t K_t R_t        (LASP Eqs. 21, 22)
+//   C  dK_t = [(dO_t V_t^T) . D_t]^T Q_t + Gam_t V_t R_t^T      (LASP Eqs. 17, 19)
+// ---------------------------------------------------------------------------
+template <typename T, int D, int BT>
+__global__ __launch_bounds__(NTHR) void k_bwd_grads(Params p) {
+    constexpr int V = Tr<T>::VEC;
+    constexpr int PD = D + V;
+    constexpr int PT = BT + V;
+    __shared__ __attribute__((aligned(16))) T St_s[D * PD];   // state operand
+    __shared__ __attribute__((aligned(16))) T A_s[BT * PD];   // query-block rows
+    __shared__ __attribute__((aligned(16))) T B_s[BT * PD];   // key-block rows
+    __shared__ __attribute__((aligned(16))) T X_s[D * PT];    // transposed block
+    __shared__ __attribute__((aligned(16))) T S_s[BT * PT];   // masked score tile
+    using TO = Tiles<BT / 32, D / 32>;
+    using TS = Tiles<BT / 32, BT / 32>;
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = lid % p.H, gc = lid / p.H;
+    Seq s;
+    int t;
+    if (!chunk_seq(p, gc, s, t)) return;
+    const float l2 = head_log2_decay(p, h);
+    const int tok = t * p.C;
+    const int Ct = min(p.C, s.len - tok);
+    const int sl = t / p.G;
+    if (s.s0 + sl >= p.n_segs_ub) return;   // only with malformed cu_seqlens
+    const int off = (t - sl * p.G) * p.C;                                // tokens before, in segment
+    const int seg_end = min((sl + 1) * p.G * p.C, s.len);
+    const int roff = seg_end - (tok + Ct);                               // tokens after, in segment
+    const int64_t rb = row_base(p, s, h) + tok;
+    const T *Q = (const T *)p.Q + rb * D;
+    const T *K = (const T *)p.K + rb * D;
+    const T *Vg = (const T *)p.V + rb * D;
+    const T *dO = (const T *)p.dO + rb * D;
+    const int64_t sidx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
+    const int64_t cidx = ((int64_t)(s.c0 + t) * p.H + h) * D * D;
+    const bool has_local = p.G > 1;
+    const int nb = (Ct + BT - 1) / BT;
+
+    // ---- phase A: dQ ----
+    combine_state<T, D>(St_s, PD, p.Pseg + sidx, has_local ? (const T *)p.Lc + cidx : nullptr,
+                        dpow(l2, (float)off), true);                    // P [dk][dv]
+    for (int qb = 0; qb < nb; ++qb) {
+        const int nvq = min(BT, Ct - qb * BT);
+        __syncthreads();
+        stage_rows<T, BT, D>(A_s, PD, dO + (int64_t)qb * BT * D, nvq);
+        __syncthreads();
+        f32x16 acc[TO::PER_WAVE];
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            zero(acc[k]);
+            int mi, ni;
+            if (TO::get(k, mi, ni)) {
+                gemm<T, D>(acc[k], A_s, PD, mi * 32, St_s, PD, ni * 32);   // dO_t P_t^T
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[k][r] *= dpow(l2, (float)(qb * BT + mi * 32 + crow(r) + 1));
+            }
+        }
+        for (int kb = 0; kb <= qb; ++kb) {
+            const int nvk = min(BT, Ct - kb * BT);
+            __syncthreads();
+            stage_rows<T, BT, D>(B_s, PD, Vg + (int64_t)kb * BT * D, nvk);
+            stage_rows_T<T, BT, D>(X_s, PT, K + (int64_t)kb * BT * D, nvk, One());
+            __syncthreads();
+            {   // E^T tiles (keys x queries) = V dO^T
+                for (int k = 0; k < TS::PER_WAVE; ++k) {
+                    int mi, ni;
+                    if (!TS::get(k, mi, ni)) continue;
+                    f32x16 et;
+                    zero(et);
+                    gemm<T, D>(et, B_s, PD, mi * 32, A_s, PD, ni * 32);
+                    store_T(et, S_s, PT, mi * 32, ni * 32, [&](float x, int j, int i) {
+                        const int gi = qb * BT + i, gj = kb * BT + j;
+                        return (gi >= gj && gi < Ct) ? x * dpow(l2, (float)(gi - gj)) : 0.f;
+                    });
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < TO::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TO::get(k, mi, ni)) gemm<T, BT>(acc[k], S_s, PT, mi * 32, X_s, PT, ni * 32);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (TO::get(k, mi, ni))
+                store_rows(acc[k], (T *)p.dQ + (rb + (int64_t)qb * BT) * D, D, mi * 32, ni * 32,
+                           nvq);
+        }
+    }
+
+    // ---- phase B: dV ----
+    const float droff = dpow(l2, (float)roff);
+    const T *Rloc = has_local ? (const T *)p.Rc + cidx : nullptr;
+    __syncthreads();
+    combine_state<T, D>(St_s, PD, p.Rseg + sidx, Rloc, droff, false);   // R^T [dv][dk]
+    for (int kb = 0; kb < nb; ++kb) {
+        const int nvk = min(BT, Ct - kb * BT);
+        __syncthreads();
+        stage_rows<T, BT, D>(B_s, PD, K + (int64_t)kb * BT * D, nvk);
+        __syncthreads();
+        f32x16 acc[TO::PER_WAVE];
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            zero(acc[k]);
+            int mi, ni;
+            if (TO::get(k, mi, ni)) {
+                gemm<T, D>(acc[k], B_s, PD, mi * 32, St_s, PD, ni * 32);   // K_t R_t
+#pragma unroll
+                for (int r = 0; r < 16; ++r)                                // Gam_t rows
+                    acc[k][r] *= dpow(l2, (float)(Ct - 1 - (kb * BT + mi * 32 + crow(r))));
+            }
+        }
+        for (int qb = kb; qb < nb; ++qb) {
+            const int nvq = min(BT, Ct - qb * BT);
+            __syncthreads();
+            stage_rows<T, BT, D>(A_s, PD, Q + (int64_t)qb * BT * D, nvq);
+            stage_rows_T<T, BT, D>(X_s, PT, dO + (int64_t)qb * BT * D, nvq, One());
+            __syncthreads();
+            {   // S tiles (queries x keys) = Q K^T, stored transposed: [key][query]
+                for (int k = 0; k < TS::PER_WAVE; ++k) {
+                    int mi, ni;
+                    if (!TS::get(k, mi, ni)) continue;
+                    f32x16 st;
+                    zero(st);
+                    gemm<T, D>(st, A_s, PD, mi * 32, B_s, PD, ni * 32);
+                    store_T(st, S_s, PT, mi * 32, ni * 32, [&](float x, int i, int j) {
+                        const int gi = qb * BT + i, gj = kb * BT + j;
+                        return (gi >= gj && gi < Ct) ? x * dpow(l2, (float)(gi - gj)) : 0.f;
+                    });
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < TO::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TO::get(k, mi, ni)) gemm<T, BT>(acc[k], S_s, PT, mi * 32, X_s, PT, ni * 32);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (TO::get(k, mi, ni))
+                store_rows(acc[k], (T *)p.dV + (rb + (int64_t)kb * BT) * D, D, mi * 32, ni * 32,
+                           nvk);
+        }
+    }
+
+    // ---- phase C: dK ----
+    __syncthreads();
+    combine_state<T, D>(St_s, PD, p.Rseg + sidx, Rloc, droff, true);    // R [dk][dv]
+    for (int kb = 0; kb < nb; ++kb) {
+        const int nvk = min(BT, Ct - kb * BT);
+        __syncthreads();
+        stage_rows<T, BT, D>(B_s, PD, Vg + (int64_t)kb * BT * D, nvk);
+        __syncthreads();
+        f32x16 acc[TO::PER_WAVE];
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            zero(acc[k]);
+            int mi, ni;
+            if (TO::get(k, mi, ni)) {
+                gemm<T, D>(acc[k], B_s, PD, mi * 32, St_s, PD, ni * 32);   // V_t R_t^T
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[k][r] *= dpow(l2, (float)(Ct - 1 - (kb * BT + mi * 32 + crow(r))));
+            }
+        }
+        for (int qb = kb; qb < nb; ++qb) {
+            const int nvq = min(BT, Ct - qb * BT);
+            __syncthreads();
+            stage_rows<T, BT, D>(A_s, PD, dO + (int64_t)qb * BT * D, nvq);
+            stage_rows_T<T, BT, D>(X_s, PT, Q + (int64_t)qb * BT * D, nvq, One());
+            __syncthreads();
+            {   // E tiles (queries x keys) = dO V^T, stored transposed: [key][query]
+                for (int k = 0; k < TS::PER_WAVE; ++k) {
+                    int mi, ni;
+                    if (!TS::get(k, mi, ni)) continue;
+                    f32x16 et;
+                    zero(et);
+                    gemm<T, D>(et, A_s, PD, mi * 32, B_s, PD, ni * 32);
+                    store_T(et, S_s, PT, mi * 32, ni * 32, [&](float x, int i, int j) {
+                        const int gi = qb * BT + i, gj = kb * BT + j;
+                        return (gi >= gj && gi < Ct) ? x * dpow(l2, (float)(gi - gj)) : 0.f;
+                    });
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < TO::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TO::get(k, mi, ni)) gemm<T, BT>(acc[k], S_s, PT, mi * 32, X_s, PT, ni * 32);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (TO::get(k, mi, ni))
+                store_rows(acc[k], (T *)p.dK + (rb + (int64_t)kb * BT) * D, D, mi * 32, ni * 32,
+                           nvk);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+static inline int round8(int n) { return (n + 7) & ~7; }
+
+// Token block: 64, except float32 with d = 128 where 32 keeps LDS under 160 KB.
+template <typename T, int D> struct Block {
+    static constexpr int BT = (sizeof(T) == 4 && D == 128) ? 32 : 64;
+};
+
+template <typename T, int D>
+static hipError_t fwd_impl(const Params &p, bool with_output, hipStream_t st) {
+    constexpr int BT = Block<T, D>::BT;
+    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
+    hipLaunchKernelGGL((k_fwd_local<T, D, BT>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    hipLaunchKernelGGL((k_fwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    if (with_output)
+        hipLaunchKernelGGL((k_fwd_out<T, D, BT>), dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), 0,
+                           st, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t bwd_impl(const Params &p, hipStream_t st) {
+    constexpr int BT = Block<T, D>::BT;
+    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
+    hipLaunchKernelGGL((k_bwd_local<T, D, BT>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    hipLaunchKernelGGL((k_bwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    hipLaunchKernelGGL((k_bwd_grads<T, D, BT>), dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), 0, st,
+                       p);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd(const Params &p, bool bf, bool with_output, hipStream_t st) {
+    switch (p.D) {
+    case 32: return bf ? fwd_impl<bf16, 32>(p, with_output, st) : fwd_impl<float, 32>(p, with_output, st);
+    case 64: return bf ? fwd_impl<bf16, 64>(p, with_output, st) : fwd_impl<float, 64>(p, with_output, st);
+    case 128: return bf ? fwd_impl<bf16, 128>(p, with_output, st) : fwd_impl<float, 128>(p, with_output, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const Params &p, bool bf, hipStream_t st) {
+    switch (p.D) {
+    case 32: return bf ? bwd_impl<bf16, 32>(p, st) : bwd_impl<float, 32>(p, st);
+    case 64: return bf ? bwd_impl<bf16, 64>(p, st) : bwd_impl<float, 64>(p, st);
+    case 128: return bf ? bwd_impl<bf16, 128>(p, st) : bwd_impl<float, 128>(p, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lasp

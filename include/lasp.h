@@ -1,0 +1,132 @@
+/*
+ * lasp.h - C ABI of the MI355X (gfx950) chunked causal linear attention library.
+ *
+ * What it computes (one head of one sequence, tokens p = 0..L-1, row vectors
+ * q_p, k_p, v_p of length d, decay lambda; lambda = 1 means no decay):
+ *
+ *   kv_p  = lambda * kv_{p-1} + k_p^T v_p,   kv_{-1} = M_in,   o_p = q_p kv_p
+ *   M_out = kv_{L-1}
+ *
+ * i.e. o_p = sum_{i<=p} lambda^(p-i) (q_p . k_i) v_i + lambda^(p+1) q_p M_in.
+ * Sources: "Linear Attention Sequence Parallelism" (arXiv 2404.02882), Sec. 3.2,
+ * Eqs. 4-6 (token form and recurrence), Eqs. 7-11 (chunked intra/inter form,
+ * Algorithm 2) and Eqs. 12-23 (backward, Algorithm 3); "LASP-2: Rethinking
+ * Sequence Parallelism for Linear Attention and Its Hybrid" (arXiv 2502.07563),
+ * review page: the chunk memory state M_t = K_t^T V_t and its prefix sums.
+ * The Norm(.) of LASP Eq. 2 is not applied (the derivations omit it); Q, K, V
+ * are used as given (no feature map, no scaling).
+ *
+ * M_in stands for the state handed over by the previous device in the pages'
+ * sequence-parallel scheme (LASP Alg. 2, the received KV_{t-1}); M_out is the
+ * state that device would send on.  The backward takes dM_out (the gradient of
+ * the following device) and returns dM_in (LASP Alg. 3, dKV sent back).
+ *
+ * Data layout (all device memory, row-major, contiguous):
+ *   Q, K, V, O, dO, dQ, dK, dV : [B, H, N, d], element type = dtype
+ *   M_in, M_out, dM_out, dM_in : [S, H, d, d] float32, row = key feature,
+ *                                column = value feature; S = B, or nseq for a
+ *                                packed batch
+ *   decay                      : float32 [H] (lambda per head), or NULL (= 1)
+ *   cu_seqlens                 : int32 [nseq + 1] for a packed batch (B = 1,
+ *                                N = total tokens, sequence i = tokens
+ *                                [cu[i], cu[i+1]) of every head), else NULL
+ * The state is reset at every sequence start of a packed batch.  Sequences may
+ * be empty; N need not be a multiple of the chunk.
+ *
+ * Ownership and threading: the caller owns every buffer; the library never
+ * allocates or frees memory and keeps no mutable global state.  Calls are
+ * asynchronous on the given HIP stream (hipStream_t passed as void*, NULL = the
+ * default stream): buffers must stay alive until the stream reaches them.
+ * Outputs are fully overwritten; outputs must not overlap inputs.
+ *
+ * Errors: every argument is checked before anything is enqueued; on error
+ * nothing runs and a lasp_status code is returned.  cu_seqlens contents are
+ * trusted (monotone, cu[0] = 0, cu[nseq] = N); NaN/Inf inputs propagate.
+ * Numbers: bf16 inputs are multiplied on bf16 MFMA with float32 accumulation;
+ * states are float32 in HBM between kernels and rounded to bf16 where they are
+ * MFMA operands.  float32 inputs use float32 MFMA throughout.
+ */
+#ifndef LASP_H
+#define LASP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LASP_FP32 = 0, LASP_BF16 = 1 } lasp_dtype;
+
+typedef enum {
+    LASP_OK = 0,
+    LASP_EINVAL = 1,        /* bad argument: dims, NULL, alignment, overlap, nseq/B */
+    LASP_EUNSUPPORTED = 2,  /* d not in {32,64,128}, chunk not in {64,128,256}, dtype */
+    LASP_EWORKSPACE = 3,    /* workspace_bytes smaller than the size query returns */
+    LASP_EHIP = 4           /* a HIP call or kernel launch failed */
+} lasp_status;
+
+/* B: batch; H: heads; N: tokens per sequence (packed batch: total tokens);
+ * d: head dimension; chunk: chunk length C; nseq: 0, or the number of packed
+ * sequences (then B must be 1 and cu_seqlens is required). */
+typedef struct {
+    int32_t B, H, N, d, chunk, nseq;
+} lasp_shape;
+
+/* Size in bytes of the state cache written by lasp_fwd and read by lasp_bwd:
+ * the per-chunk states the backward pass reuses (LASP Sec. 3.2, the cached
+ * KV_{t-1}).  Depends only on the shape and dtype. */
+size_t lasp_state_cache_bytes(const lasp_shape *shape, lasp_dtype dtype);
+
+/* Workspace needed by lasp_fwd / lasp_bwd.  with_state_cache != 0 means the
+ * call is given a state cache buffer; without one the workspace also holds the
+ * states (and lasp_bwd recomputes them). */
+size_t lasp_fwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype,
+                                int with_state_cache);
+size_t lasp_bwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype,
+                                int with_state_cache);
+
+/* Forward pass (LASP Alg. 2 on one device; LASP-2 prefix sums of M_t).
+ *   Q, K, V     inputs (required)
+ *   decay       device float32 [H] or NULL
+ *   cu_seqlens  device int32 [nseq+1] or NULL (nseq == 0)
+ *   M_in        device float32 [S,H,d,d] or NULL (= zero state)
+ *   O           output (required)
+ *   M_out       output float32 [S,H,d,d] or NULL (not written)
+ *   state_cache lasp_state_cache_bytes() bytes, or NULL; pass the same buffer to
+ *               lasp_bwd to skip recomputing the states there
+ *   workspace   lasp_fwd_workspace_bytes(shape, dtype, state_cache != NULL)
+ *               bytes of device scratch (may be NULL if that size is 0)
+ * All device pointers must be 16-byte aligned. */
+int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype,
+             const void *Q, const void *K, const void *V,
+             const float *decay, const int32_t *cu_seqlens, const float *M_in,
+             void *O, float *M_out, void *state_cache,
+             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward pass (LASP Alg. 3 on one device; LASP-2 suffix sums of dM_t) for the
+ * loss l = <dO, O> + <dM_out, M_out>.
+ *   Q, K, V, dO, decay, cu_seqlens, M_in : as given to lasp_fwd
+ *   dM_out      device float32 [S,H,d,d] or NULL (= zero)
+ *   state_cache the buffer lasp_fwd filled for the same inputs, or NULL
+ *               (then the states are recomputed from K, V, M_in)
+ *   dQ, dK, dV  outputs (required); dM_in output or NULL (not written)
+ *   workspace   lasp_bwd_workspace_bytes(shape, dtype, state_cache != NULL) */
+int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype,
+             const void *Q, const void *K, const void *V, const void *dO,
+             const float *decay, const int32_t *cu_seqlens, const float *M_in,
+             const float *dM_out, const void *state_cache,
+             void *dQ, void *dK, void *dV, float *dM_in,
+             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable text for a status code (for LASP_EHIP: the last HIP error of
+ * the calling thread). */
+const char *lasp_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int lasp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LASP_H */

@@ -203,50 +203,59 @@ def _pow(lam, e):
     return np.power(float(lam), np.asarray(e, dtype=np.float64))
 
 
-def sampled_o(q, k, v, rows, lam=1.0, m_in=None):
-    """o_p for p in rows, each an O(L d) direct sum of [LASP] Eq. 4 (+ M_in term)."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
-    L, d = q.shape
-    m = _zeros_state(d, m_in)
+def _row_weights(a, b, rows, lam, forward=True):
+    """W[n, i] = lam^(p_n - i) (a_{p_n} . b_i) for i <= p_n (forward), or
+    W[n, i] = lam^(i - p_n) (a_i . b_{p_n}) for i >= p_n (backward), zero elsewhere:
+    the rows p_n of the masked score matrix of [LASP] Eq. 7 with C = L."""
     rows = np.asarray(rows)
-    out = np.zeros((len(rows), v.shape[1]))
-    for n, p in enumerate(rows):
-        w = (k[: p + 1] @ q[p]) * _pow(lam, p - np.arange(p + 1))
-        out[n] = w @ v[: p + 1] + float(lam) ** (p + 1) * (q[p] @ m)
-    return out
+    L = a.shape[0]
+    i = np.arange(L)[None, :]
+    p = rows[:, None]
+    if forward:
+        e = (p - i).astype(np.float64)
+        S = a[rows] @ b.T
+        keep = i <= p
+    else:
+        e = (i - p).astype(np.float64)
+        S = (a @ b[rows].T).T
+        keep = i >= p
+    return np.where(keep, S * np.power(float(lam), np.where(keep, e, 0.0)), 0.0)
+
+
+def sampled_o(q, k, v, rows, lam=1.0, m_in=None):
+    """o_p for p in rows: sum_{i<=p} lam^(p-i) (q_p . k_i) v_i + lam^(p+1) q_p M_in."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    rows = np.asarray(rows)
+    m = _zeros_state(q.shape[1], m_in)
+    return _row_weights(q, k, rows, lam) @ v + _pow(lam, rows + 1)[:, None] * (q[rows] @ m)
 
 
 def sampled_dq(q, k, v, do, rows, lam=1.0, m_in=None):
+    """dq_p = sum_{j<=p} lam^(p-j) (do_p . v_j) k_j + lam^(p+1) do_p M_in^T."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    L, d = q.shape
-    m = _zeros_state(d, m_in)
-    out = np.zeros((len(rows), d))
-    for n, p in enumerate(np.asarray(rows)):
-        w = (v[: p + 1] @ do[p]) * _pow(lam, p - np.arange(p + 1))
-        out[n] = w @ k[: p + 1] + float(lam) ** (p + 1) * (do[p] @ m.T)
-    return out
+    rows = np.asarray(rows)
+    m = _zeros_state(q.shape[1], m_in)
+    return _row_weights(do, v, rows, lam) @ k + _pow(lam, rows + 1)[:, None] * (do[rows] @ m.T)
 
 
 def sampled_dk(q, k, v, do, rows, lam=1.0, dm_out=None):
+    """dk_j = sum_{p>=j} lam^(p-j) (do_p . v_j) q_p + lam^(L-1-j) v_j dM_out^T."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    rows = np.asarray(rows)
     L, d = q.shape
     dm = _zeros_state(d, dm_out)
-    out = np.zeros((len(rows), d))
-    for n, j in enumerate(np.asarray(rows)):
-        w = (do[j:] @ v[j]) * _pow(lam, np.arange(L - j))
-        out[n] = w @ q[j:] + float(lam) ** (L - 1 - j) * (v[j] @ dm.T)
-    return out
+    return (_row_weights(do, v, rows, lam, forward=False) @ q
+            + _pow(lam, L - 1 - rows)[:, None] * (v[rows] @ dm.T))
 
 
 def sampled_dv(q, k, v, do, rows, lam=1.0, dm_out=None):
+    """dv_j = sum_{p>=j} lam^(p-j) (q_p . k_j) do_p + lam^(L-1-j) k_j dM_out."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    rows = np.asarray(rows)
     L, d = q.shape
     dm = _zeros_state(d, dm_out)
-    out = np.zeros((len(rows), v.shape[1]))
-    for n, j in enumerate(np.asarray(rows)):
-        w = (q[j:] @ k[j]) * _pow(lam, np.arange(L - j))
-        out[n] = w @ do[j:] + float(lam) ** (L - 1 - j) * (k[j] @ dm)
-    return out
+    return (_row_weights(q, k, rows, lam, forward=False) @ do
+            + _pow(lam, L - 1 - rows)[:, None] * (k[rows] @ dm))
 
 
 def closed_m_out(k, v, lam=1.0, m_in=None):

@@ -1,0 +1,139 @@
+"""C ABI contract, checked without a GPU: the library loads, exports every symbol
+include/lasp.h declares, and rejects bad arguments before any HIP call (so fake,
+never-dereferenced pointers are safe here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_causal_linear_amd as cca
+from chunked_causal_linear_amd import Shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lasp.h")
+
+OK, EINVAL, EUNSUP, EWS, EHIP = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(cca.LIB_PATH):
+        from chunked_causal_linear_amd import build
+        build.build()
+    return cca.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lasp_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"lasp_fwd", "lasp_bwd", "lasp_state_cache_bytes", "lasp_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    for s in (OK, EINVAL, EUNSUP, EWS, EHIP, 99):
+        assert isinstance(L.lasp_status_string(s), bytes)
+    assert L.lasp_version() >= 100
+
+
+A = 1 << 20        # fake, 16-byte aligned, never dereferenced device addresses
+GAP = 1 << 36
+
+
+def fake(i):
+    return ctypes.c_void_p(A + i * GAP)
+
+
+def fwd_call(L, shape, dtype=1, Q=0, K=1, V=2, decay=None, cu=None, M_in=None, O=3, M_out=None,
+             cache=None, ws=5, ws_bytes=None, overrides=None):
+    args = dict(Q=fake(Q) if Q is not None else None, K=fake(K) if K is not None else None,
+                V=fake(V), decay=None if decay is None else fake(decay),
+                cu=None if cu is None else fake(cu), M_in=None if M_in is None else fake(M_in),
+                O=None if O is None else fake(O), M_out=None if M_out is None else fake(M_out),
+                cache=None if cache is None else fake(cache), ws=None if ws is None else fake(ws))
+    if overrides:
+        args.update(overrides)
+    if ws_bytes is None:
+        ws_bytes = L.lasp_fwd_workspace_bytes(ctypes.byref(shape), dtype, int(cache is not None))
+    return L.lasp_fwd(ctypes.byref(shape), dtype, args["Q"], args["K"], args["V"], args["decay"],
+                      args["cu"], args["M_in"], args["O"], args["M_out"], args["cache"],
+                      args["ws"], ws_bytes, None)
+
+
+def test_fwd_rejects_bad_arguments(L):
+    good = Shape(2, 4, 1000, 64, 128, 0)
+    # dims
+    for bad in [Shape(0, 4, 1000, 64, 128, 0), Shape(2, 0, 1000, 64, 128, 0),
+                Shape(2, 4, 0, 64, 128, 0), Shape(2, 4, 1000, 64, 128, -1)]:
+        assert fwd_call(L, bad) == EINVAL
+    # unsupported d / chunk / dtype
+    assert fwd_call(L, Shape(2, 4, 1000, 48, 128, 0)) == EUNSUP
+    assert fwd_call(L, Shape(2, 4, 1000, 64, 100, 0)) == EUNSUP
+    assert fwd_call(L, Shape(2, 4, 1000, 64, 32, 0)) == EUNSUP
+    assert fwd_call(L, good, dtype=7) == EUNSUP
+    # required pointers
+    assert fwd_call(L, good, Q=None) == EINVAL
+    assert fwd_call(L, good, O=None) == EINVAL
+    # packed batch needs B == 1 and cu_seqlens; cu_seqlens needs nseq > 0
+    assert fwd_call(L, Shape(2, 4, 1000, 64, 128, 3), cu=6) == EINVAL
+    assert fwd_call(L, Shape(1, 4, 1000, 64, 128, 3)) == EINVAL
+    assert fwd_call(L, good, cu=6) == EINVAL
+    # alignment
+    assert fwd_call(L, good, overrides=dict(Q=ctypes.c_void_p(A + 8))) == EINVAL
+    assert fwd_call(L, good, overrides=dict(decay=ctypes.c_void_p(A + 7 * GAP + 2))) == EINVAL
+    # workspace
+    need = L.lasp_fwd_workspace_bytes(ctypes.byref(good), 1, 0)
+    assert need > 0
+    assert fwd_call(L, good, ws_bytes=need - 1) == EWS
+    assert fwd_call(L, good, ws=None) == EWS
+    # outputs overlapping inputs
+    assert fwd_call(L, good, O=0) == EINVAL
+    assert fwd_call(L, good, overrides=dict(O=ctypes.c_void_p(A + 2 * GAP + 4096))) == EINVAL
+    assert fwd_call(L, good, M_out=3) == EINVAL            # M_out inside O
+    assert fwd_call(L, good, ws=2) == EINVAL               # workspace inside V
+
+
+def test_bwd_rejects_bad_arguments(L):
+    s = Shape(1, 2, 300, 32, 64, 0)
+    need = L.lasp_bwd_workspace_bytes(ctypes.byref(s), 0, 0)
+    p = [fake(i) for i in range(12)]
+
+    def call(shape=s, dt=0, ws_bytes=need, **kw):
+        a = dict(Q=p[0], K=p[1], V=p[2], dO=p[3], decay=None, cu=None, M_in=None, dM_out=None,
+                 cache=None, dQ=p[4], dK=p[5], dV=p[6], dM_in=None, ws=p[7])
+        a.update(kw)
+        return L.lasp_bwd(ctypes.byref(shape), dt, a["Q"], a["K"], a["V"], a["dO"], a["decay"],
+                          a["cu"], a["M_in"], a["dM_out"], a["cache"], a["dQ"], a["dK"], a["dV"],
+                          a["dM_in"], a["ws"], ws_bytes, None)
+
+    assert call(dO=None) == EINVAL
+    assert call(dK=None) == EINVAL
+    assert call(shape=Shape(1, 2, 300, 256, 64, 0)) == EUNSUP
+    assert call(ws_bytes=need - 256) == EWS
+    assert call(dQ=p[3]) == EINVAL                 # dQ aliases dO
+    assert call(dV=p[5]) == EINVAL                 # two outputs alias
+    assert call(dM_in=ctypes.c_void_p(A + 4)) == EINVAL   # misaligned
+    # with a state cache the workspace may be smaller
+    assert L.lasp_bwd_workspace_bytes(ctypes.byref(s), 0, 1) < need
+
+
+def test_sizes_follow_the_shape(L):
+    # state cache = per-chunk local states (elem) + per-segment f32 states
+    c3 = Shape(1, 32, 131072, 128, 256, 0)
+    n = L.lasp_state_cache_bytes(ctypes.byref(c3), 1)
+    chunks = 131072 // 256
+    assert n >= chunks * 32 * 128 * 128 * 2
+    assert n <= chunks * 32 * 128 * 128 * 2 * 1.5
+    # packed batch bounds cover any split of N into nseq sequences
+    pk = Shape(1, 8, 5000, 64, 128, 7)
+    assert L.lasp_state_cache_bytes(ctypes.byref(pk), 1) >= (5000 // 128 + 7) * 8 * 64 * 64 * 2
+    # invalid shapes report 0
+    assert L.lasp_state_cache_bytes(ctypes.byref(Shape(1, 1, 1, 33, 64, 0)), 1) == 0
+    assert L.lasp_fwd_workspace_bytes(None, 1, 0) == 0

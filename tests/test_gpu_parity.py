@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Metric per output tensor: max|gpu - ref| / max|ref| (over all its elements, or
+over the sampled rows at full size).  Bars: 1e-4 for float32 inputs, 2e-2 for
+bfloat16 inputs with float32 accumulation.  The oracle reads the very values the
+GPU reads (bf16 inputs are upcast exactly).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_causal_linear_amd as cca
+from chunked_causal_linear_amd.workloads import CONFIGS, make_inputs, small
+from oracle import crecurrent
+from oracle import lasp_oracle as lo
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    cca.lib()       # raises if the HIP library is missing: no fallback
+    yield
+
+
+def dev(x):
+    return None if x is None else x.cuda()
+
+
+def np64(x):
+    return None if x is None else x.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel(a, ref):
+    a, ref = np.asarray(a, np.float64), np.asarray(ref, np.float64)
+    den = np.abs(ref).max()
+    return float(np.abs(a - ref).max() / (den if den > 0 else 1.0))
+
+
+def run_gpu(inp, backward=True, use_cache=True):
+    sh = inp["shape"]
+    Q, K, V = dev(inp["Q"]), dev(inp["K"]), dev(inp["V"])
+    decay, cu, M_in = dev(inp["decay"]), dev(inp["cu_seqlens"]), dev(inp["M_in"])
+    O, M_out, cache = cca.fwd(Q, K, V, sh["chunk"], decay, cu, M_in,
+                              want_state_cache=backward and use_cache)
+    out = {"O": O, "M_out": M_out}
+    if backward:
+        dQ, dK, dV, dM_in = cca.bwd(Q, K, V, dev(inp["dO"]), sh["chunk"], decay, cu, M_in,
+                                    dev(inp["dM_out"]), cache)
+        out.update(dQ=dQ, dK=dK, dV=dV, dM_in=dM_in)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_full(inp, backward=True):
+    a = {k: np64(inp[k]) for k in ("Q", "K", "V", "dO", "M_in", "dM_out", "decay")}
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy()
+    O, Mo = lo.batched_fwd(a["Q"], a["K"], a["V"], a["decay"], a["M_in"], cu)
+    ref = {"O": O, "M_out": Mo}
+    if backward:
+        dQ, dK, dV, dMi = lo.batched_bwd(a["Q"], a["K"], a["V"], a["dO"], a["decay"], a["M_in"],
+                                         a["dM_out"], cu)
+        ref.update(dQ=dQ, dK=dK, dV=dV, dM_in=dMi)
+    return ref
+
+
+def check(name, out, ref, tol, keys=None):
+    keys = keys or list(ref)
+    errs = {}
+    for k in keys:
+        got = np64(out[k])
+        errs[k] = rel(got, ref[k])
+    say(name, " ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {k: e for k, e in errs.items() if not e <= tol}
+    assert not bad, "%s: %s exceed %g" % (name, bad, tol)
+
+
+# ---------------------------------------------------------------------------
+# small cases against the full quadratic oracle
+# ---------------------------------------------------------------------------
+SMALL = [
+    small("bf16 d64 C64 ragged decay Min dMout", "bf16", B=2, H=2, N=300, d=64, chunk=64,
+          seed=10, decay="lightning", m_in_scale=0.1, dm_out_scale=0.1),
+    small("bf16 d128 C256 ragged decay Min", "bf16", B=1, H=2, N=700, d=128, chunk=256, seed=11,
+          decay="lightning", m_in_scale=0.05),
+    small("bf16 d128 C128 B2H3 no decay", "bf16", B=2, H=3, N=1100, d=128, chunk=128, seed=12),
+    small("bf16 d32 C64 Min dMout", "bf16", B=3, H=1, N=200, d=32, chunk=64, seed=13,
+          m_in_scale=0.1, dm_out_scale=0.1),
+    small("fp32 d32 C64 decay Min dMout", "fp32", B=2, H=2, N=300, d=32, chunk=64, seed=14,
+          decay="lightning", m_in_scale=0.1, dm_out_scale=0.1),
+    small("fp32 d64 C128 ragged", "fp32", B=1, H=2, N=333, d=64, chunk=128, seed=15,
+          m_in_scale=0.1),
+    small("fp32 d128 C64 decay (32-token blocks)", "fp32", B=1, H=2, N=333, d=128, chunk=64,
+          seed=16, decay="lightning", m_in_scale=0.05, dm_out_scale=0.05),
+    small("bf16 packed d64 C128 edge lengths", "bf16", H=2, d=64, chunk=128, seed=17,
+          lengths=[1, 127, 128, 129, 0, 300, 64], decay="lightning", m_in_scale=0.1,
+          dm_out_scale=0.1),
+    small("fp32 packed d32 C64", "fp32", H=3, d=32, chunk=64, seed=18, lengths=[5, 0, 64, 65, 200],
+          m_in_scale=0.1, dm_out_scale=0.1),
+    small("bf16 one token", "bf16", B=1, H=1, N=1, d=64, chunk=64, seed=19, m_in_scale=0.1,
+          dm_out_scale=0.1),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_parity(w):
+    say("case:", w.name)
+    inp = make_inputs(w)
+    out = run_gpu(inp)
+    ref = oracle_full(inp)
+    check(w.name, out, ref, TOL[w.dtype])
+
+
+@pytest.mark.parametrize("G", ["1", "3", "16"])
+def test_segment_sizes(G, monkeypatch):
+    """The two-level scan gives the same result for any segment length."""
+    monkeypatch.setenv("LASP_SEGMENT_CHUNKS", G)
+    w = small("bf16 d64 C64 many chunks", "bf16", B=2, H=2, N=64 * 11 + 17, d=64, chunk=64,
+              seed=20, decay="lightning", m_in_scale=0.1, dm_out_scale=0.1)
+    say("case: segment chunks", G)
+    inp = make_inputs(w)
+    check("G=" + G, run_gpu(inp), oracle_full(inp), TOL["bf16"])
+
+
+def test_zero_decay():
+    """lambda = 0: only the current token contributes."""
+    w = small("bf16 d64 C64", "bf16", B=1, H=2, N=130, d=64, chunk=64, seed=21, m_in_scale=0.1,
+              dm_out_scale=0.1)
+    inp = make_inputs(w)
+    inp["decay"] = torch.tensor([0.0, 0.5], dtype=torch.float32)
+    say("case: zero decay")
+    check("lambda=0", run_gpu(inp), oracle_full(inp), TOL["bf16"])
+
+
+def test_recompute_equals_cache_and_determinism():
+    w = small("bf16 d128 C128", "bf16", B=1, H=2, N=900, d=128, chunk=128, seed=22,
+              decay="lightning", m_in_scale=0.1, dm_out_scale=0.1)
+    inp = make_inputs(w)
+    say("case: recompute vs cache")
+    a = run_gpu(inp, use_cache=True)
+    b = run_gpu(inp, use_cache=False)
+    c = run_gpu(inp, use_cache=True)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k     # same kernels, same order: bitwise
+        assert torch.equal(a[k], c[k]), k     # deterministic reruns
+
+
+def test_decay_none_equals_ones():
+    w = small("bf16 d64 C64", "bf16", B=1, H=2, N=200, d=64, chunk=64, seed=23)
+    inp = make_inputs(w)
+    a = run_gpu(inp)
+    inp["decay"] = torch.ones(2, dtype=torch.float32)
+    b = run_gpu(inp)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_config1_forward_fp32():
+    """fp32 B1 H2 N256 d32 C64, forward only: quadratic and recurrent oracle."""
+    inp = make_inputs(CONFIGS[1])
+    out = run_gpu(inp, backward=False)
+    a = {k: np64(inp[k]) for k in ("Q", "K", "V")}
+    O_q, M_q = lo.batched_fwd(a["Q"], a["K"], a["V"])
+    O_r, M_r = lo.batched_fwd(a["Q"], a["K"], a["V"], form="recurrent")
+    check("config1 vs quadratic", out, {"O": O_q, "M_out": M_q}, TOL["fp32"])
+    check("config1 vs recurrent", out, {"O": O_r, "M_out": M_r}, TOL["fp32"])
+
+
+# ---------------------------------------------------------------------------
+# full-size configurations
+# ---------------------------------------------------------------------------
+def full_config_check(w, rows_per_seq=48, seed=0):
+    """Sampled rows of O, dQ, dK, dV for every (sequence, head) against the
+    oracle's direct sums, and full M_out / dM_in against their closed forms.
+    Converts one (sequence, head) slice at a time to keep host memory small."""
+    say("case:", w.name)
+    inp = make_inputs(w)
+    out = run_gpu(inp)
+    sh = inp["shape"]
+    H = sh["H"]
+    if inp["cu_seqlens"] is not None:
+        cu = inp["cu_seqlens"].numpy()
+        seqs = [(0, int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1)]
+    else:
+        seqs = [(b, 0, sh["N"]) for b in range(sh["B"])]
+    r = np.random.default_rng(seed)
+    dec = np64(inp["decay"])
+    M_in, dM_out = inp["M_in"], inp["dM_out"]
+    acc = {k: ([], []) for k in ("O", "dQ", "dK", "dV")}
+    Mo_g, dMi_g = np64(out["M_out"]), np64(out["dM_in"])
+    Mo_r, dMi_r = np.zeros_like(Mo_g), np.zeros_like(dMi_g)
+    for si, (b, s, e) in enumerate(seqs):
+        L = e - s
+        rows = (np.unique(np.concatenate([[0, L - 1], r.integers(0, L, rows_per_seq)]))
+                if L > 0 else np.zeros(0, dtype=np.int64))
+        idx = torch.as_tensor(s + rows)
+        for h in range(H):
+            lam = 1.0 if dec is None else float(dec[h])
+            q, k, v, do = (np64(inp[x][b, h, s:e]) for x in ("Q", "K", "V", "dO"))
+            mi = None if M_in is None else np64(M_in[si, h])
+            dmo = None if dM_out is None else np64(dM_out[si, h])
+            Mo_r[si, h] = lo.closed_m_out(k, v, lam, mi)
+            dMi_r[si, h] = lo.closed_dm_in(q, do, lam, dmo)
+            if L == 0:
+                continue
+            refs = {"O": lo.sampled_o(q, k, v, rows, lam, mi),
+                    "dQ": lo.sampled_dq(q, k, v, do, rows, lam, mi),
+                    "dK": lo.sampled_dk(q, k, v, do, rows, lam, dmo),
+                    "dV": lo.sampled_dv(q, k, v, do, rows, lam, dmo)}
+            for kk, rv in refs.items():
+                acc[kk][0].append(np64(out[kk][b, h].index_select(0, idx.to(out[kk].device))))
+                acc[kk][1].append(rv)
+    errs = {kk: rel(np.concatenate(g), np.concatenate(rv)) for kk, (g, rv) in acc.items()}
+    errs["M_out"] = rel(Mo_g, Mo_r)
+    errs["dM_in"] = rel(dMi_g, dMi_r)
+    say(w.name, " ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL[w.dtype]}
+    assert not bad, bad
+
+
+def test_config2_full_tensors():
+    """bf16 B4 H16 N8192 d128 C256: every element against the C float64 recurrence."""
+    w = CONFIGS[2]
+    say("case: config 2 full tensors")
+    inp = make_inputs(w)
+    out = run_gpu(inp)
+    a = {k: inp[k].float().numpy() for k in ("Q", "K", "V", "dO")}
+    ref = crecurrent.run(a["Q"], a["K"], a["V"], a["dO"])
+    check("config2", out, ref, TOL["bf16"], ["O", "dQ", "dK", "dV", "M_out", "dM_in"])
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_full_config_sampled(cfg):
+    full_config_check(CONFIGS[cfg], seed=100 + cfg)
+
+
+def test_config3_with_dm_out():
+    """One device's share with both incoming state and incoming state gradient."""
+    import dataclasses
+    w = dataclasses.replace(CONFIGS[3], name=CONFIGS[3].name + " + dM_out", dm_out_scale=0.01,
+                            seed=33)
+    full_config_check(w, rows_per_seq=16, seed=133)
