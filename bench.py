@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = lasp_fwd + lasp_bwd (the whole hot path: chunk states,
+state scan, fused output, reverse scan, dQ/dK/dV) over one batch of synthetic
+input on one MI355X, with inputs resident in HBM.
+
+Default workload: bf16, B=1, H=32, N=131072, d=128, chunk=256, with an incoming
+state M_in and the outgoing M_out (one device's share of a long sequence).
+
+Prints ONE JSON line.  Besides the contract fields it carries:
+  roofline      for the dominant kernel, timed live with HIP events recorded on
+                the launch stream around that kernel inside the library;
+  cpu_baseline  the float64 C oracle (token recurrence) timed on the host cores
+                over a bounded sample of the same workload;
+  kernels_ms    average duration of every kernel of the step.
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+KERNEL_SRC = os.path.join(ROOT, "chunked_causal_linear_amd", "csrc", "lasp_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def hip():
+    L = ctypes.CDLL("libamdhip64.so")
+    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return L
+
+
+def make_events(L, n):
+    arr = (ctypes.c_void_p * n)()
+    for i in range(n):
+        h = ctypes.c_void_p()
+        assert L.hipEventCreate(ctypes.byref(h)) == 0
+        arr[i] = h
+    return arr
+
+
+def elapsed(L, a, b):
+    ms = ctypes.c_float()
+    assert L.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+    return ms.value
+
+
+def kernel_work(sh, local_b, seg_b):
+    """Algorithmic HBM bytes and flops per launch of every kernel of a step.
+    U = token-heads; local_b / seg_b: bytes of the per-chunk (element type) and
+    per-segment (float32) state arrays, from the library's size queries."""
+    B, H, N, d, C = sh["B"], sh["H"], sh["N"], sh["d"], sh["chunk"]
+    e = 2 if sh["dtype"] == "bf16" else 4
+    U = B * H * N
+    nS = sh["nseq"] or B
+    st_io = nS * H * d * d * 4                    # M_in / M_out, dM_out / dM_in
+    return {
+        "fwd_local": (2 * U * d * e + local_b + seg_b, 2 * U * d * d),
+        "fwd_scan": (2 * seg_b + 2 * st_io, seg_b // 2),
+        "fwd_out": (4 * U * d * e + local_b + seg_b, U * (4 * C * d + 2 * d * d)),
+        "bwd_local": (2 * U * d * e + local_b + seg_b, 2 * U * d * d),
+        "bwd_scan": (2 * seg_b + 2 * st_io, seg_b // 2),
+        "bwd_grads": (7 * U * d * e + 2 * local_b + 2 * seg_b, U * (10 * C * d + 6 * d * d)),
+    }
+
+
+def src_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were taken
+    on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != src_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, H, tokens):
+    """The float64 C oracle over a bounded sample: the first `tokens` tokens of
+    `threads` heads (one head per host thread), forward + backward."""
+    from oracle import crecurrent
+    threads = crecurrent.threads()
+    nh = min(H, threads)
+    take = lambda x: x[:, :nh, :tokens].float().cpu().numpy()
+    Q, K, V, dO = (take(inp[k]) for k in ("Q", "K", "V", "dO"))
+    M_in = None if inp["M_in"] is None else inp["M_in"][:, :nh].double().cpu().numpy()
+    t0 = time.perf_counter()
+    crecurrent.run(Q, K, V, dO, None, M_in, None)
+    dt = time.perf_counter() - t0
+    th = Q.shape[0] * nh * Q.shape[2]            # token-heads processed
+    return {"value": th / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d heads x first %d tokens, fwd+bwd float64 token recurrence "
+                      "(C, OpenMP over heads), %.2f s; tokens/s counts all %d heads per token"
+                      % (nh, H, Q.shape[2], dt, H)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (a.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_causal_linear_amd as cca
+    from chunked_causal_linear_amd.workloads import CONFIGS, make_inputs
+
+    w = CONFIGS[a.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w, device="cuda")
+    sh = dict(inp["shape"], dtype=w.dtype)
+    Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
+    decay, cu, M_in, dM_out = inp["decay"], inp["cu_seqlens"], inp["M_in"], inp["dM_out"]
+    C = sh["chunk"]
+
+    S = cca.Shape(sh["B"], sh["H"], sh["N"], sh["d"], C, sh["nseq"])
+    dt_code = cca.LASP_BF16 if w.dtype == "bf16" else cca.LASP_FP32
+    wsf = torch.empty(max(1, cca.fwd_workspace_bytes(S, dt_code, True)), dtype=torch.uint8,
+                      device=dev)
+    wsb = torch.empty(max(1, cca.bwd_workspace_bytes(S, dt_code, True)), dtype=torch.uint8,
+                      device=dev)
+
+    L = hip()
+    n = a.warmup + a.steps
+    evf = [make_events(L, 4) for _ in range(n)]
+    evb = [make_events(L, 4) for _ in range(n)]
+
+    def step(i):
+        O, M_out, cache = cca.fwd(Q, K, V, C, decay, cu, M_in, workspace=wsf, events=evf[i])
+        g = cca.bwd(Q, K, V, dO, C, decay, cu, M_in, dM_out, cache, workspace=wsb,
+                    events=evb[i])
+        return O, g
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.warmup, n):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / a.steps
+
+    names = ["fwd_local", "fwd_scan", "fwd_out", "bwd_local", "bwd_scan", "bwd_grads"]
+    kms = {k: 0.0 for k in names}
+    for i in range(a.warmup, n):
+        for j in range(3):
+            kms[names[j]] += elapsed(L, evf[i][j], evf[i][j + 1]) / a.steps
+            kms[names[3 + j]] += elapsed(L, evb[i][j], evb[i][j + 1]) / a.steps
+
+    # state array sizes (fwd workspace with a cache = tables + per-segment states)
+    table_b = 0 if not sh["nseq"] else -(-8 * (sh["nseq"] + 1) // 256) * 256
+    seg_b = cca.fwd_workspace_bytes(S, dt_code, True) - table_b
+    local_b = cca.state_cache_bytes(S, dt_code) - seg_b
+    work = kernel_work(sh, local_b, seg_b)
+    dom = max(names, key=lambda k: kms[k])
+    bytes_, flops = work[dom]
+    t_dom = kms[dom] * 1e-3
+    hbm_time, mfma_time = bytes_ / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if hbm_time >= mfma_time:
+        roof = {"bound": "hbm", "achieved": bytes_ / t_dom / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(dom)
+    roof.update(kernel=dom, ms=kms[dom], algorithmic_bytes=bytes_, algorithmic_flops=flops)
+
+    tokens = sh["B"] * sh["N"]
+    d = sh["d"]
+    U = tokens * sh["H"]
+    f_dense = U * (12 * d * d + 14 * C * d)
+    f_causal = U * (12 * d * d + 7 * C * d)
+    out = {
+        "metric": "causal linear-attn fwd+bwd tokens/s and % bf16 MFMA peak, d=128, N=131072",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": sh["B"], "H": sh["H"], "N": sh["N"], "d": d,
+                   "chunk": C, "nseq": sh["nseq"], "decay": w.decay,
+                   "m_in": M_in is not None, "parallelism": "single GPU"},
+        "tflops_dense_chunk": f_dense / (ms * 1e-3) / 1e12,
+        "tflops_causal_useful": f_causal / (ms * 1e-3) / 1e12,
+        "mfma_peak_frac_dense": f_dense / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "compulsory_io_GBs": (U * d * (8 + 14) * (2 if w.dtype == "bf16" else 4) / 2)
+                             / (ms * 1e-3) / 1e9,
+        "kernels_ms": kms,
+        "roofline": roof,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, sh["H"], min(a.cpu_tokens, sh["N"]))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

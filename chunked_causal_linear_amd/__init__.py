@@ -53,6 +53,10 @@ def lib():
         L.lasp_fwd.restype = ctypes.c_int
         L.lasp_bwd.argtypes = [SP, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
         L.lasp_bwd.restype = ctypes.c_int
+        L.lasp_fwd_ex.argtypes = L.lasp_fwd.argtypes + [P]
+        L.lasp_fwd_ex.restype = ctypes.c_int
+        L.lasp_bwd_ex.argtypes = L.lasp_bwd.argtypes + [P]
+        L.lasp_bwd_ex.restype = ctypes.c_int
         L.lasp_status_string.argtypes = [ctypes.c_int]
         L.lasp_status_string.restype = ctypes.c_char_p
         L.lasp_version.restype = ctypes.c_int
@@ -117,11 +121,12 @@ def _stream(device):
 
 
 def fwd(Q, K, V, chunk, decay=None, cu_seqlens=None, M_in=None, *, want_m_out=True,
-        want_state_cache=True, out=None, workspace=None):
+        want_state_cache=True, out=None, workspace=None, events=None):
     """Forward pass.  Q, K, V: [B, H, N, d] bf16 or fp32 CUDA tensors.
     decay: float32 [H] CUDA tensor or None.  cu_seqlens: int32 [nseq+1] CUDA tensor
     or None.  M_in: float32 [S, H, d, d] or None.  Returns (O, M_out, state_cache)
-    (M_out / state_cache are None when not requested)."""
+    (M_out / state_cache are None when not requested).  events: optional ctypes
+    array of 4 hipEvent_t handles for per-kernel timing (see lasp_fwd_ex)."""
     import torch
     dev = Q.device
     S_ = _shape(Q, chunk, cu_seqlens)
@@ -141,16 +146,16 @@ def fwd(Q, K, V, chunk, decay=None, cu_seqlens=None, M_in=None, *, want_m_out=Tr
     nws = fwd_workspace_bytes(S_, dt, cache is not None)
     if workspace is None or workspace.numel() < nws:
         workspace = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
-    rc = lib().lasp_fwd(ctypes.byref(S_), dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(decay),
-                        _ptr(cu_seqlens), _ptr(M_in), _ptr(O), _ptr(M_out), _ptr(cache),
-                        _ptr(workspace), nws, _stream(dev))
+    rc = lib().lasp_fwd_ex(ctypes.byref(S_), dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(decay),
+                           _ptr(cu_seqlens), _ptr(M_in), _ptr(O), _ptr(M_out), _ptr(cache),
+                           _ptr(workspace), nws, _stream(dev), events)
     if rc != 0:
         raise LaspError(rc, "lasp_fwd")
     return O, M_out, cache
 
 
 def bwd(Q, K, V, dO, chunk, decay=None, cu_seqlens=None, M_in=None, dM_out=None,
-        state_cache=None, *, want_dm_in=True, workspace=None):
+        state_cache=None, *, want_dm_in=True, workspace=None, events=None):
     """Backward pass for l = <dO, O> + <dM_out, M_out>.  state_cache: the buffer
     fwd returned for the same inputs, or None (states are recomputed).
     Returns (dQ, dK, dV, dM_in)."""
@@ -175,10 +180,10 @@ def bwd(Q, K, V, dO, chunk, decay=None, cu_seqlens=None, M_in=None, dM_out=None,
     nws = bwd_workspace_bytes(S_, dt, state_cache is not None)
     if workspace is None or workspace.numel() < nws:
         workspace = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
-    rc = lib().lasp_bwd(ctypes.byref(S_), dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(decay),
-                        _ptr(cu_seqlens), _ptr(M_in), _ptr(dM_out), _ptr(state_cache),
-                        _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dM_in), _ptr(workspace), nws,
-                        _stream(dev))
+    rc = lib().lasp_bwd_ex(ctypes.byref(S_), dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(dO),
+                           _ptr(decay), _ptr(cu_seqlens), _ptr(M_in), _ptr(dM_out),
+                           _ptr(state_cache), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dM_in),
+                           _ptr(workspace), nws, _stream(dev), events)
     if rc != 0:
         raise LaspError(rc, "lasp_bwd")
     return dQ, dK, dV, dM_in

@@ -154,10 +154,10 @@ size_t lasp_bwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype, int w
     return make_plan(shape, dtype, pl) == LASP_OK ? bwd_ws(pl, with_state_cache != 0) : 0;
 }
 
-int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
-             const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
-             void *O, float *M_out, void *state_cache, void *workspace, size_t workspace_bytes,
-             void *stream) {
+int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
+                void *O, float *M_out, void *state_cache, void *workspace,
+                size_t workspace_bytes, void *stream, void **events) {
     Plan pl;
     int rc = make_plan(shape, dtype, pl);
     if (rc != LASP_OK) return rc;
@@ -199,13 +199,23 @@ int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const voi
     char *c = cache ? (char *)state_cache : w;
     p.Lc = c;
     p.Pseg = (float *)(c + pl.local_b);
-    return hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, true, (hipStream_t)stream));
+    return hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, true, (hipStream_t)stream,
+                                       (hipEvent_t *)events));
 }
 
-int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
-             const void *V, const void *dO, const float *decay, const int32_t *cu_seqlens,
-             const float *M_in, const float *dM_out, const void *state_cache, void *dQ, void *dK,
-             void *dV, float *dM_in, void *workspace, size_t workspace_bytes, void *stream) {
+int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+             const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
+             void *O, float *M_out, void *state_cache, void *workspace, size_t workspace_bytes,
+             void *stream) {
+    return lasp_fwd_ex(shape, dtype, Q, K, V, decay, cu_seqlens, M_in, O, M_out, state_cache,
+                       workspace, workspace_bytes, stream, nullptr);
+}
+
+int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                const void *V, const void *dO, const float *decay, const int32_t *cu_seqlens,
+                const float *M_in, const float *dM_out, const void *state_cache, void *dQ,
+                void *dK, void *dV, float *dM_in, void *workspace, size_t workspace_bytes,
+                void *stream, void **events) {
     Plan pl;
     int rc = make_plan(shape, dtype, pl);
     if (rc != LASP_OK) return rc;
@@ -263,7 +273,15 @@ int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const voi
         rc = hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, false, hs));
         if (rc != LASP_OK) return rc;
     }
-    return hip_status(lasp::launch_bwd(p, dtype == LASP_BF16, hs));
+    return hip_status(lasp::launch_bwd(p, dtype == LASP_BF16, hs, (hipEvent_t *)events));
+}
+
+int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+             const void *V, const void *dO, const float *decay, const int32_t *cu_seqlens,
+             const float *M_in, const float *dM_out, const void *state_cache, void *dQ, void *dK,
+             void *dV, float *dM_in, void *workspace, size_t workspace_bytes, void *stream) {
+    return lasp_bwd_ex(shape, dtype, Q, K, V, dO, decay, cu_seqlens, M_in, dM_out, state_cache,
+                       dQ, dK, dV, dM_in, workspace, workspace_bytes, stream, nullptr);
 }
 
 const char *lasp_status_string(int status) {

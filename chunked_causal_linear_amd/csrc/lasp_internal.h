@@ -38,9 +38,12 @@ struct Params {
 
 // Enqueue the forward kernels: (packed-batch tables), local chunk states,
 // segment scan, and (if with_output) the output kernel.
-hipError_t launch_fwd(const Params &p, bool bf16, bool with_output, hipStream_t stream);
+// ev (nullable): 4 events recorded on the stream before the local-state kernel,
+// before the scan, before the last kernel and after it.
+hipError_t launch_fwd(const Params &p, bool bf16, bool with_output, hipStream_t stream,
+                      hipEvent_t *ev = nullptr);
 // Enqueue the backward kernels: (tables), reverse local states, reverse
 // segment scan, gradient kernel.  The forward states (Lc, Pseg) must be valid.
-hipError_t launch_bwd(const Params &p, bool bf16, hipStream_t stream);
+hipError_t launch_bwd(const Params &p, bool bf16, hipStream_t stream, hipEvent_t *ev = nullptr);
 
 }  // namespace lasp

@@ -916,45 +916,57 @@ template <typename T, int D> struct Block {
     static constexpr int BT = (sizeof(T) == 4 && D == 128) ? 32 : 64;
 };
 
+static inline void rec(hipEvent_t *ev, int i, hipStream_t st) {
+    if (ev) (void)hipEventRecord(ev[i], st);
+}
+
 template <typename T, int D>
-static hipError_t fwd_impl(const Params &p, bool with_output, hipStream_t st) {
+static hipError_t fwd_impl(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
     constexpr int BT = Block<T, D>::BT;
     if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
+    rec(ev, 0, st);
     hipLaunchKernelGGL((k_fwd_local<T, D, BT>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
+    rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     hipLaunchKernelGGL((k_fwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    rec(ev, 2, st);
     if (with_output)
         hipLaunchKernelGGL((k_fwd_out<T, D, BT>), dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), 0,
                            st, p);
+    rec(ev, 3, st);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t bwd_impl(const Params &p, hipStream_t st) {
+static hipError_t bwd_impl(const Params &p, hipStream_t st, hipEvent_t *ev) {
     constexpr int BT = Block<T, D>::BT;
     if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
+    rec(ev, 0, st);
     hipLaunchKernelGGL((k_bwd_local<T, D, BT>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
+    rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     hipLaunchKernelGGL((k_bwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    rec(ev, 2, st);
     hipLaunchKernelGGL((k_bwd_grads<T, D, BT>), dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), 0, st,
                        p);
+    rec(ev, 3, st);
     return hipGetLastError();
 }
 
-hipError_t launch_fwd(const Params &p, bool bf, bool with_output, hipStream_t st) {
+hipError_t launch_fwd(const Params &p, bool bf, bool with_output, hipStream_t st, hipEvent_t *ev) {
     switch (p.D) {
-    case 32: return bf ? fwd_impl<bf16, 32>(p, with_output, st) : fwd_impl<float, 32>(p, with_output, st);
-    case 64: return bf ? fwd_impl<bf16, 64>(p, with_output, st) : fwd_impl<float, 64>(p, with_output, st);
-    case 128: return bf ? fwd_impl<bf16, 128>(p, with_output, st) : fwd_impl<float, 128>(p, with_output, st);
+    case 32: return bf ? fwd_impl<bf16, 32>(p, with_output, st, ev) : fwd_impl<float, 32>(p, with_output, st, ev);
+    case 64: return bf ? fwd_impl<bf16, 64>(p, with_output, st, ev) : fwd_impl<float, 64>(p, with_output, st, ev);
+    case 128: return bf ? fwd_impl<bf16, 128>(p, with_output, st, ev) : fwd_impl<float, 128>(p, with_output, st, ev);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(const Params &p, bool bf, hipStream_t st) {
+hipError_t launch_bwd(const Params &p, bool bf, hipStream_t st, hipEvent_t *ev) {
     switch (p.D) {
-    case 32: return bf ? bwd_impl<bf16, 32>(p, st) : bwd_impl<float, 32>(p, st);
-    case 64: return bf ? bwd_impl<bf16, 64>(p, st) : bwd_impl<float, 64>(p, st);
-    case 128: return bf ? bwd_impl<bf16, 128>(p, st) : bwd_impl<float, 128>(p, st);
+    case 32: return bf ? bwd_impl<bf16, 32>(p, st, ev) : bwd_impl<float, 32>(p, st, ev);
+    case 64: return bf ? bwd_impl<bf16, 64>(p, st, ev) : bwd_impl<float, 64>(p, st, ev);
+    case 128: return bf ? bwd_impl<bf16, 128>(p, st, ev) : bwd_impl<float, 128>(p, st, ev);
     }
     return hipErrorInvalidValue;
 }

@@ -60,14 +60,18 @@ def lightning_decay(H: int) -> torch.Tensor:
                         dtype=torch.float64).to(torch.float32)
 
 
-def make_inputs(w: Workload, backward: Optional[bool] = None) -> dict:
-    """Draw the inputs of workload w on the CPU.  Returns a dict with
+def make_inputs(w: Workload, backward: Optional[bool] = None, device: str = "cpu") -> dict:
+    """Draw the inputs of workload w on `device` (a generator on that device,
+    seeded with w.seed; draws on the GPU give other values than on the CPU, with
+    the same recipe).  Returns a dict with
     Q, K, V (and dO when backward) in w's dtype [B, H, N, d]; decay float32 [H]
     or None; cu_seqlens int32 [nseq+1] or None; M_in / dM_out float32
     [S, H, d, d] or None; and the resolved shape (B, H, N, d, chunk, nseq)."""
     backward = w.backward if backward is None else backward
     g = torch.Generator("cpu").manual_seed(w.seed)
     lens = _lengths(w, g)
+    if str(device) != "cpu":
+        g = torch.Generator(device).manual_seed(w.seed)
     B, H, d = w.B, w.H, w.d
     if lens is not None:
         B, N = 1, int(sum(lens))
@@ -79,7 +83,7 @@ def make_inputs(w: Workload, backward: Optional[bool] = None) -> dict:
     scale = 1.0 / math.sqrt(d)
 
     def draw(shape, s):
-        return (torch.randn(shape, generator=g, dtype=torch.float32) * s)
+        return torch.randn(shape, generator=g, dtype=torch.float32, device=device) * s
 
     Q = draw((B, H, N, d), scale).to(w.torch_dtype)
     K = draw((B, H, N, d), scale).to(w.torch_dtype)
@@ -88,7 +92,9 @@ def make_inputs(w: Workload, backward: Optional[bool] = None) -> dict:
     M_in = draw((S, H, d, d), w.m_in_scale) if w.m_in_scale is not None else None
     dM_out = (draw((S, H, d, d), w.dm_out_scale)
               if (backward and w.dm_out_scale is not None) else None)
-    decay = lightning_decay(H) if w.decay == "lightning" else None
+    decay = lightning_decay(H).to(device) if w.decay == "lightning" else None
+    if cu is not None:
+        cu = cu.to(device)
     return dict(Q=Q, K=K, V=V, dO=dO, M_in=M_in, dM_out=dM_out, decay=decay,
                 cu_seqlens=cu, lengths=lens,
                 shape=dict(B=B, H=H, N=N, d=d, chunk=w.chunk,

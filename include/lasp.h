@@ -119,6 +119,22 @@ int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype,
              void *dQ, void *dK, void *dV, float *dM_in,
              void *workspace, size_t workspace_bytes, void *stream);
 
+/* As lasp_fwd / lasp_bwd, plus per-kernel timing: events is NULL or an array of
+ * 4 hipEvent_t (created by the caller) that are recorded on the stream before
+ * the local chunk-state kernel, before the cross-segment scan, before the last
+ * kernel (output, resp. gradients) and after it.  Nothing else changes. */
+int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype,
+                const void *Q, const void *K, const void *V,
+                const float *decay, const int32_t *cu_seqlens, const float *M_in,
+                void *O, float *M_out, void *state_cache,
+                void *workspace, size_t workspace_bytes, void *stream, void **events);
+int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype,
+                const void *Q, const void *K, const void *V, const void *dO,
+                const float *decay, const int32_t *cu_seqlens, const float *M_in,
+                const float *dM_out, const void *state_cache,
+                void *dQ, void *dK, void *dV, float *dM_in,
+                void *workspace, size_t workspace_bytes, void *stream, void **events);
+
 /* Human-readable text for a status code (for LASP_EHIP: the last HIP error of
  * the calling thread). */
 const char *lasp_status_string(int status);
