@@ -906,6 +906,387 @@ __global__ __launch_bounds__(NTHR) void k_bwd_grads(Params p) {
     }
 }
 
+// ===========================================================================
+// bf16 path for gfx950.  Operand tiles are staged row-major (16-byte copies);
+// operands whose contraction index is the token index are read with the LDS
+// transpose read (ds_read_b64_tr_b16), so no transposed copies are made.
+// Score tiles stay in registers: the 32x32 accumulator of S^T (tokens c x
+// rows r) is, lane for lane, the A operand of S.Cv once its k order is
+// permuted, and the Cv operand is read in the same permuted order.
+// ===========================================================================
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// Operand fragment from a row-major LDS tile X[r][k] (k contiguous):
+// rows r0 + lane%32, k elements k0 + (lane/32)*8 + [0, 8).
+__device__ __forceinline__ bf16x8_t frag_rows(const bf16 *X, int pitch, int r0, int k0) {
+    const int l = lane_id();
+    return *(const bf16x8_t *)(X + (r0 + (l & 31)) * pitch + k0 + (l >> 5) * 8);
+}
+
+// Operand fragment from an LDS tile stored X[k][n] (n contiguous), operand row
+// n0 + lane%32.  With g = lane/32 the 8 contraction elements are
+// k0 + 8g + [0, 8) (PERM = false) or k0 + 4g + {0..3, 8..11} (PERM = true).
+// ds_read_b64_tr_b16 works on groups of 16 lanes: when lane i of a group reads
+// the 4 elements at row rb + i/4, columns cb + 4*(i%4), lane j of the group
+// receives rows rb + 0..3 of column cb + j.
+template <bool PERM>
+__device__ __forceinline__ bf16x8_t frag_cols(const bf16 *X, int pitch, int k0, int n0) {
+    const int l = lane_id(), i = l & 15, h = l >> 4, g = h >> 1;
+    const int col = n0 + (h & 1) * 16 + 4 * (i & 3);
+    const int ra = k0 + (PERM ? 4 * g : 8 * g) + (i >> 2);
+    const int rb = ra + (PERM ? 8 : 4);
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(X + ra * pitch + col));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(X + rb * pitch + col));
+    const v8s c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, c);
+}
+
+__device__ __forceinline__ bf16x8_t pack8(float a0, float a1, float a2, float a3, float a4,
+                                          float a5, float a6, float a7) {
+    bf16x8_t r;
+    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+    r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+    return r;
+}
+
+__device__ __forceinline__ uint4 scale8(uint4 v, float s) {
+    float f[8];
+    load16((const bf16 *)&v, f);
+    const bf16x8_t b = pack8(f[0] * s, f[1] * s, f[2] * s, f[3] * s, f[4] * s, f[5] * s,
+                             f[6] * s, f[7] * s);
+    return __builtin_bit_cast(uint4, b);
+}
+
+// Roles of the chunk kernel.  All four compute, for the output rows r of one
+// chunk (length Ct),
+//   Out[r] = sum_{c in causal range of r} lambda^|r-c| (A_r . B_c) Cv_c
+//            + lambda^e(r) A_r X
+// with X = scale * seg + loc the chunk's state ([dv][dk] in memory):
+//   0  O  : A=Q,  B=K,  Cv=V,  X=P,   c <= r, e = r+1        (LASP Eqs. 7, 9, 11)
+//   1  dQ : A=dO, B=V,  Cv=K,  X=P^T, c <= r, e = r+1        (LASP Eqs. 14-16)
+//   2  dV : A=K,  B=Q,  Cv=dO, X=R,   c >= r, e = Ct-1-r     (LASP Eqs. 21-22)
+//   3  dK : A=V,  B=dO, Cv=Q,  X=R^T, c >= r, e = Ct-1-r     (LASP Eqs. 17-19)
+template <int C> struct ChunkCfg {
+    static constexpr int NRT = C / 32;                 // 32-row tiles per chunk
+    static constexpr int NW = NRT >= 4 ? 4 : NRT;      // waves per workgroup
+    static constexpr int TPW = NRT / NW;               // row tiles per wave (1 or 2)
+    static constexpr int NT = 64 * NW;
+};
+
+template <int D, int C>
+__global__ __launch_bounds__(ChunkCfg<C>::NT) void k_chunk_bf16(Params p, int role0, int nroles) {
+    using Cfg = ChunkCfg<C>;
+    constexpr int NW = Cfg::NW, TPW = Cfg::TPW, NT = Cfg::NT, NRT = Cfg::NRT;
+    constexpr int PX = D + 8;                 // LDS pitch (elements)
+    constexpr int KS = D / 16;                // k-steps over the feature dim
+    constexpr int NDT = D / 32;               // 32-wide feature tiles
+    constexpr int PIECES = 32 * D / 8;        // 16-byte pieces per 32-token tile
+    constexpr int PPT = (PIECES + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) bf16 X_s[D * PX];
+    __shared__ __attribute__((aligned(16))) bf16 B_s[2][32 * PX];
+    __shared__ __attribute__((aligned(16))) bf16 V_s[2][32 * PX];
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int role = role0 + lid % nroles;
+    const int rest = lid / nroles;
+    const int h = rest % p.H, gc = rest / p.H;
+    Seq s;
+    int t;
+    if (!chunk_seq(p, gc, s, t)) return;
+    const int tok = t * p.C;
+    const int Ct = min(p.C, s.len - tok);
+    const int sl = t / p.G;
+    if (s.s0 + sl >= p.n_segs_ub) return;   // only with malformed cu_seqlens
+    const float l2 = head_log2_decay(p, h);
+    const bool decay = l2 != 0.f;
+    const int64_t rb = row_base(p, s, h) + tok;
+    const int64_t sidx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
+    const int64_t cidx = ((int64_t)(s.c0 + t) * p.H + h) * D * D;
+
+    const bf16 *A, *Bm, *Cv;
+    bf16 *Out;
+    const float *seg;
+    const bf16 *loc;
+    int soff;
+    const bool rev = role >= 2;                // contraction over c >= r
+    const bool xt = role & 1;                  // state read transposed
+    if (role < 2) {
+        soff = (t - sl * p.G) * p.C;           // tokens from the segment start
+        seg = p.Pseg + sidx;
+        loc = p.G > 1 ? (const bf16 *)p.Lc + cidx : nullptr;
+    } else {
+        const int seg_end = min((sl + 1) * p.G * p.C, s.len);
+        soff = seg_end - (tok + Ct);           // tokens after the chunk, in the segment
+        seg = p.Rseg + sidx;
+        loc = p.G > 1 ? (const bf16 *)p.Rc + cidx : nullptr;
+    }
+    const bf16 *Qg = (const bf16 *)p.Q + rb * D, *Kg = (const bf16 *)p.K + rb * D;
+    const bf16 *Vg = (const bf16 *)p.V + rb * D;
+    const bf16 *Og = role ? (const bf16 *)p.dO + rb * D : nullptr;
+    switch (role) {
+    case 0: A = Qg; Bm = Kg; Cv = Vg; Out = (bf16 *)p.O + rb * D; break;
+    case 1: A = Og; Bm = Vg; Cv = Kg; Out = (bf16 *)p.dQ + rb * D; break;
+    case 2: A = Kg; Bm = Qg; Cv = Og; Out = (bf16 *)p.dV + rb * D; break;
+    default: A = Vg; Bm = Og; Cv = Qg; Out = (bf16 *)p.dK + rb * D; break;
+    }
+
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    int tiles[TPW];
+    tiles[0] = w;
+    if (TPW == 2) tiles[TPW - 1] = NRT - 1 - w;
+
+    // ---- state X = lambda^soff seg + loc -> X_s [dv][dk] (bf16) ----
+    {
+        const float sc = dpow(l2, (float)soff);
+        for (int e = tid * 8; e < D * D; e += NT * 8) {
+            const float4 s0 = *(const float4 *)(seg + e), s1 = *(const float4 *)(seg + e + 4);
+            float lf[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (loc) load16(loc + e, lf);
+            const bf16x8_t v = pack8(sc * s0.x + lf[0], sc * s0.y + lf[1], sc * s0.z + lf[2],
+                                     sc * s0.w + lf[3], sc * s1.x + lf[4], sc * s1.y + lf[5],
+                                     sc * s1.z + lf[6], sc * s1.w + lf[7]);
+            *(bf16x8_t *)(X_s + (e / D) * PX + (e % D)) = v;
+        }
+    }
+
+    // ---- A fragments of this wave's row tiles (registers) ----
+    bf16x8_t af[TPW][KS];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        const int row = tiles[tt] * 32 + (l & 31);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (row < Ct) v = *(const uint4 *)(A + (int64_t)row * D + ks * 16 + (l >> 5) * 8);
+            af[tt][ks] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+
+    // ---- staging of 32-token tiles of B and Cv, with register prefetch ----
+    const int nct = (Ct + 31) / 32;
+    uint4 pb[PPT], pv[PPT];
+    auto fetch = [&](int ct) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = tid + k * NT;
+            const int r = i / (D / 8), c = (i % (D / 8)) * 8;
+            const int row = ct * 32 + r;
+            pb[k] = pv[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (i < PIECES && row < Ct) {
+                pb[k] = *(const uint4 *)(Bm + (int64_t)row * D + c);
+                pv[k] = *(const uint4 *)(Cv + (int64_t)row * D + c);
+            }
+        }
+    };
+    auto deposit = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = tid + k * NT;
+            if (i < PIECES) {
+                const int r = i / (D / 8), c = (i % (D / 8)) * 8;
+                *(uint4 *)(&B_s[buf][r * PX + c]) = pb[k];
+                *(uint4 *)(&V_s[buf][r * PX + c]) = pv[k];
+            }
+        }
+    };
+    fetch(0);
+    deposit(0);
+    __syncthreads();   // X_s and the first tile
+
+    // ---- inter-chunk term: acc = lambda^e(r) A_r X ----
+    f32x16 acc[TPW][NDT];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt) zero(acc[tt][nt]);
+#pragma unroll
+    for (int nt = 0; nt < NDT; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8_t xf = xt ? frag_cols<false>(X_s, PX, ks * 16, nt * 32)
+                                   : frag_rows(X_s, PX, nt * 32, ks * 16);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) mma(acc[tt][nt], af[tt][ks], xf);
+        }
+    if (decay || rev) {
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = tiles[tt] * 32 + crow(r);
+                const float sc = dpow(l2, (float)(rev ? (Ct - 1 - row) : (row + 1)));
+#pragma unroll
+                for (int nt = 0; nt < NDT; ++nt) acc[tt][nt][r] *= sc;
+            }
+    }
+
+    // ---- intra-chunk term over 32-token tiles of c ----
+    for (int ct = 0; ct < nct; ++ct) {
+        const int buf = ct & 1;
+        if (ct + 1 < nct) fetch(ct + 1);
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int rt = tiles[tt];
+            if (rt * 32 >= Ct || (rev ? (ct < rt) : (ct > rt))) continue;
+            f32x16 st;
+            zero(st);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                mma(st, frag_rows(B_s[buf], PX, 0, ks * 16), af[tt][ks]);   // S^T: c x r
+            const int r = rt * 32 + (l & 31);
+            const bool diag = ct == rt;
+            if (diag || decay || (ct + 1) * 32 > Ct) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int c = ct * 32 + crow(i);
+                    const int dist = rev ? (c - r) : (r - c);
+                    const bool ok = dist >= 0 && c < Ct && r < Ct;
+                    st[i] = ok ? (decay ? st[i] * dpow(l2, (float)dist) : st[i]) : 0.f;
+                }
+            }
+            const bf16x8_t s0 = pack8(st[0], st[1], st[2], st[3], st[4], st[5], st[6], st[7]);
+            const bf16x8_t s1 = pack8(st[8], st[9], st[10], st[11], st[12], st[13], st[14], st[15]);
+#pragma unroll
+            for (int nt = 0; nt < NDT; ++nt) {
+                mma(acc[tt][nt], s0, frag_cols<true>(V_s[buf], PX, 0, nt * 32));
+                mma(acc[tt][nt], s1, frag_cols<true>(V_s[buf], PX, 16, nt * 32));
+            }
+        }
+        if (ct + 1 < nct) deposit(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- store ----
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt)
+            store_rows(acc[tt][nt], Out, D, tiles[tt] * 32, nt * 32, Ct);
+}
+
+// Local chunk states (bf16): one workgroup per (segment, head).
+//   which = 0: L_t = state entering chunk t from the segment start (chunks in
+//              order), L += (Gam_t K_t)^T V_t, stored to Lc, total to Z;
+//   which = 1: R_t = reverse state from the segment end (chunks in reverse),
+//              R += (Lam_t Q_t)^T dO_t, stored to Rc, total to W.
+// The K^T V (Q^T dO) products read both operands with the transpose read.
+template <int D>
+__global__ __launch_bounds__(256) void k_local_bf16(Params p, int which) {
+    constexpr int NT = 256, TT = 64, PX = D + 8;
+    constexpr int PIECES = TT * D / 8;
+    constexpr int PPT = (PIECES + NT - 1) / NT;
+    using TL = Tiles<D / 32, D / 32>;
+    __shared__ __attribute__((aligned(16))) bf16 A_s[2][TT * PX];
+    __shared__ __attribute__((aligned(16))) bf16 B_s[2][TT * PX];
+
+    const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
+    Seq s;
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const float l2 = head_log2_decay(p, h);
+    const int64_t rb = row_base(p, s, h);
+    const bf16 *Ag = (const bf16 *)(which ? p.Q : p.K) + rb * D;
+    const bf16 *Bg = (const bf16 *)(which ? p.dO : p.V) + rb * D;
+    bf16 *Lout = (bf16 *)(which ? p.Rc : p.Lc);
+    float *Tot = which ? p.W : p.Z;
+    const bool store_local = p.G > 1;
+    const int tid = threadIdx.x;
+
+    f32x16 acc[TL::PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) zero(acc[k]);
+
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    const int nchunks = t1 - t0;
+    // flattened (chunk, 64-token tile) steps in sweep order
+    auto chunk_of = [&](int i) { return which ? (t1 - 1 - i) : (t0 + i); };
+    auto tiles_of = [&](int t) { return (min(p.C, s.len - t * p.C) + TT - 1) / TT; };
+    uint4 pa[PPT], pb[PPT];
+    auto fetch = [&](int t, int tl) {
+        const int Ct = min(p.C, s.len - t * p.C);
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = tid + k * NT;
+            const int r = i / (D / 8), c = (i % (D / 8)) * 8;
+            const int row = tl * TT + r;      // token within chunk
+            pa[k] = pb[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (i < PIECES && row < Ct) {
+                const int64_t off = (int64_t)(t * p.C + row) * D + c;
+                const float sc = dpow(l2, (float)(which ? row + 1 : Ct - 1 - row));
+                pa[k] = *(const uint4 *)(Ag + off);
+                if (sc != 1.f) pa[k] = scale8(pa[k], sc);
+                pb[k] = *(const uint4 *)(Bg + off);
+            }
+        }
+    };
+    auto deposit = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = tid + k * NT;
+            if (i < PIECES) {
+                const int r = i / (D / 8), c = (i % (D / 8)) * 8;
+                *(uint4 *)(&A_s[buf][r * PX + c]) = pa[k];
+                *(uint4 *)(&B_s[buf][r * PX + c]) = pb[k];
+            }
+        }
+    };
+    if (nchunks <= 0) return;
+    int ci = 0, tl = 0, buf = 0;
+    int t = chunk_of(0);
+    fetch(t, 0);
+    deposit(0);
+    __syncthreads();
+    // state written before each chunk's contribution is added
+    bool first_tile = true;
+    while (true) {
+        const int ntl = tiles_of(t);
+        if (first_tile) {
+            if (store_local) {
+                bf16 *Lt = Lout + ((int64_t)(s.c0 + t) * p.H + h) * D * D;
+#pragma unroll
+                for (int k = 0; k < TL::PER_WAVE; ++k) {
+                    int mi, ni;
+                    if (TL::get(k, mi, ni)) store_T(acc[k], Lt, D, mi * 32, ni * 32, Ident());
+                }
+            }
+            const float dc = dpow(l2, (float)min(p.C, s.len - t * p.C));
+#pragma unroll
+            for (int k = 0; k < TL::PER_WAVE; ++k) acc[k] *= dc;
+        }
+        // next step
+        int nci = ci, ntl2 = tl + 1, nt_ = t;
+        if (ntl2 >= ntl) { nci = ci + 1; ntl2 = 0; nt_ = nci < nchunks ? chunk_of(nci) : -1; }
+        const bool more = nci < nchunks;
+        if (more) fetch(nt_, ntl2);
+#pragma unroll
+        for (int k = 0; k < TL::PER_WAVE; ++k) {
+            int mi, ni;
+            if (TL::get(k, mi, ni)) {
+#pragma unroll
+                for (int k0 = 0; k0 < TT; k0 += 16)
+                    mma(acc[k], frag_cols<false>(A_s[buf], PX, k0, mi * 32),
+                        frag_cols<false>(B_s[buf], PX, k0, ni * 32));
+            }
+        }
+        if (!more) break;
+        deposit(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+        first_tile = nci != ci;
+        ci = nci;
+        tl = ntl2;
+        t = nt_;
+    }
+    float *Ts = Tot + ((int64_t)gs * p.H + h) * D * D;
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) {
+        int mi, ni;
+        if (TL::get(k, mi, ni)) store_T(acc[k], Ts, D, mi * 32, ni * 32, Ident());
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -953,20 +1334,64 @@ static hipError_t bwd_impl(const Params &p, hipStream_t st, hipEvent_t *ev) {
     return hipGetLastError();
 }
 
+// bf16: transpose-read local-state kernel and the shared chunk kernel.
+template <int D, int C>
+static void chunk_launch(const Params &p, int role0, int nroles, hipStream_t st) {
+    hipLaunchKernelGGL((k_chunk_bf16<D, C>), dim3(round8(p.n_chunks_ub * p.H * nroles)),
+                       dim3(ChunkCfg<C>::NT), 0, st, p, role0, nroles);
+}
+
+template <int D>
+static void chunk_dispatch(const Params &p, int role0, int nroles, hipStream_t st) {
+    switch (p.C) {
+    case 64: chunk_launch<D, 64>(p, role0, nroles, st); break;
+    case 128: chunk_launch<D, 128>(p, role0, nroles, st); break;
+    default: chunk_launch<D, 256>(p, role0, nroles, st); break;
+    }
+}
+
+template <int D>
+static hipError_t fwd_bf16(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
+    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
+    rec(ev, 0, st);
+    hipLaunchKernelGGL((k_local_bf16<D>), dim3(p.n_segs_ub * p.H), dim3(256), 0, st, p, 0);
+    rec(ev, 1, st);
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    hipLaunchKernelGGL((k_fwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    rec(ev, 2, st);
+    if (with_output) chunk_dispatch<D>(p, 0, 1, st);
+    rec(ev, 3, st);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t bwd_bf16(const Params &p, hipStream_t st, hipEvent_t *ev) {
+    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
+    rec(ev, 0, st);
+    hipLaunchKernelGGL((k_local_bf16<D>), dim3(p.n_segs_ub * p.H), dim3(256), 0, st, p, 1);
+    rec(ev, 1, st);
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    hipLaunchKernelGGL((k_bwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    rec(ev, 2, st);
+    chunk_dispatch<D>(p, 1, 3, st);   // dQ, dV, dK of a chunk are neighbours in launch order
+    rec(ev, 3, st);
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd(const Params &p, bool bf, bool with_output, hipStream_t st, hipEvent_t *ev) {
     switch (p.D) {
-    case 32: return bf ? fwd_impl<bf16, 32>(p, with_output, st, ev) : fwd_impl<float, 32>(p, with_output, st, ev);
-    case 64: return bf ? fwd_impl<bf16, 64>(p, with_output, st, ev) : fwd_impl<float, 64>(p, with_output, st, ev);
-    case 128: return bf ? fwd_impl<bf16, 128>(p, with_output, st, ev) : fwd_impl<float, 128>(p, with_output, st, ev);
+    case 32: return bf ? fwd_bf16<32>(p, with_output, st, ev) : fwd_impl<float, 32>(p, with_output, st, ev);
+    case 64: return bf ? fwd_bf16<64>(p, with_output, st, ev) : fwd_impl<float, 64>(p, with_output, st, ev);
+    case 128: return bf ? fwd_bf16<128>(p, with_output, st, ev) : fwd_impl<float, 128>(p, with_output, st, ev);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd(const Params &p, bool bf, hipStream_t st, hipEvent_t *ev) {
     switch (p.D) {
-    case 32: return bf ? bwd_impl<bf16, 32>(p, st, ev) : bwd_impl<float, 32>(p, st, ev);
-    case 64: return bf ? bwd_impl<bf16, 64>(p, st, ev) : bwd_impl<float, 64>(p, st, ev);
-    case 128: return bf ? bwd_impl<bf16, 128>(p, st, ev) : bwd_impl<float, 128>(p, st, ev);
+    case 32: return bf ? bwd_bf16<32>(p, st, ev) : bwd_impl<float, 32>(p, st, ev);
+    case 64: return bf ? bwd_bf16<64>(p, st, ev) : bwd_impl<float, 64>(p, st, ev);
+    case 128: return bf ? bwd_bf16<128>(p, st, ev) : bwd_impl<float, 128>(p, st, ev);
     }
     return hipErrorInvalidValue;
 }
