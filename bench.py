@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times), to calibrate "
+                         "the HBM byte counters of a profiler against known traffic")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -126,6 +129,17 @@ def main():
         sys.exit(2)
 
     import torch
+    if a.copy_calib:
+        n = a.copy_calib << 20
+        x = torch.empty(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        x.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n}), flush=True)
+        return
     import chunked_causal_linear_amd as cca
     from chunked_causal_linear_amd.workloads import CONFIGS, make_inputs
 

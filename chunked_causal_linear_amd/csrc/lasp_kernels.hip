@@ -114,7 +114,7 @@ __device__ __forceinline__ void store4(bf16 *p, float a, float b, float c, float
 
 // lambda^e with lambda = 2^l2; lambda^0 = 1 exactly (also for lambda = 0).
 __device__ __forceinline__ float dpow(float l2, float e) {
-    return e == 0.f ? 1.f : exp2f(e * l2);
+    return e == 0.f ? 1.f : __builtin_amdgcn_exp2f(e * l2);
 }
 __device__ __forceinline__ float head_log2_decay(const Params &p, int h) {
     return p.decay ? log2f(p.decay[h]) : 0.f;
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NTHR) void k_fwd_local(Params p) {
 //   Pseg[0] = M_in;  Pseg[s+1] = lambda^len_s Pseg[s] + Z[s];  M_out = last.
 // (LASP-2 prefix sum of gathered states; LASP Alg. 2 receive/send as a scan.)
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(NTHR) void k_fwd_segscan(Params p) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     const int ih = blockIdx.x / NB;
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(NTHR) void k_fwd_segscan(Params p) {
     const int nS = min(s.S, p.n_segs_ub - s.s0);
     for (int sl = 0; sl < nS; ++sl) {
         const int64_t idx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D + e;
-        p.Pseg[idx] = P;
+        ((T *)p.Pseg)[idx] = fromf<T>(P);
         const int len_s = min(seg_tokens, s.len - sl * seg_tokens);
         P = dpow(l2, (float)len_s) * P + p.Z[idx];
     }
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(NTHR) void k_bwd_local(Params p) {
 // Backward 2: reverse scan over segments, one thread per state element.
 //   Rseg[S-1] = dM_out;  Rseg[s-1] = lambda^len_s Rseg[s] + W[s];  dM_in = last.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(NTHR) void k_bwd_segscan(Params p) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     const int ih = blockIdx.x / NB;
@@ -662,7 +662,7 @@ __global__ __launch_bounds__(NTHR) void k_bwd_segscan(Params p) {
     const int nS = min(s.S, p.n_segs_ub - s.s0);
     for (int sl = nS - 1; sl >= 0; --sl) {
         const int64_t idx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D + e;
-        p.Rseg[idx] = R;
+        ((T *)p.Rseg)[idx] = fromf<T>(R);
         const int len_s = min(seg_tokens, s.len - sl * seg_tokens);
         R = dpow(l2, (float)len_s) * R + p.W[idx];
     }
@@ -963,34 +963,47 @@ __device__ __forceinline__ uint4 scale8(uint4 v, float s) {
 // chunk (length Ct),
 //   Out[r] = sum_{c in causal range of r} lambda^|r-c| (A_r . B_c) Cv_c
 //            + lambda^e(r) A_r X
-// with X = scale * seg + loc the chunk's state ([dv][dk] in memory):
+// with X = lambda^soff seg + loc the chunk's state ([dv][dk] in memory):
 //   0  O  : A=Q,  B=K,  Cv=V,  X=P,   c <= r, e = r+1        (LASP Eqs. 7, 9, 11)
 //   1  dQ : A=dO, B=V,  Cv=K,  X=P^T, c <= r, e = r+1        (LASP Eqs. 14-16)
 //   2  dV : A=K,  B=Q,  Cv=dO, X=R,   c >= r, e = Ct-1-r     (LASP Eqs. 21-22)
 //   3  dK : A=V,  B=dO, Cv=Q,  X=R^T, c >= r, e = Ct-1-r     (LASP Eqs. 17-19)
+// Each wave owns one 32-row tile.  A 256-token chunk is split over two
+// workgroups with row tiles {0,1,6,7} and {2,3,4,5}, which carry equal work in
+// both directions; shorter chunks use one workgroup of C/32 waves.
 template <int C> struct ChunkCfg {
     static constexpr int NRT = C / 32;                 // 32-row tiles per chunk
-    static constexpr int NW = NRT >= 4 ? 4 : NRT;      // waves per workgroup
-    static constexpr int TPW = NRT / NW;               // row tiles per wave (1 or 2)
+    static constexpr int NG = NRT >= 8 ? 2 : 1;        // workgroups per chunk
+    static constexpr int NW = NRT / NG;                // waves per workgroup
     static constexpr int NT = 64 * NW;
+    __device__ static int tile(int g, int w) {
+        return NG == 1 ? w : (g ? 2 + w : (w < 2 ? w : w + 4));
+    }
 };
 
 template <int D, int C>
 __global__ __launch_bounds__(ChunkCfg<C>::NT) void k_chunk_bf16(Params p, int role0, int nroles) {
     using Cfg = ChunkCfg<C>;
-    constexpr int NW = Cfg::NW, TPW = Cfg::TPW, NT = Cfg::NT, NRT = Cfg::NRT;
-    constexpr int PX = D + 8;                 // LDS pitch (elements)
+    constexpr int NW = Cfg::NW, NT = Cfg::NT, NG = Cfg::NG;
+    constexpr int PX = D + 8;                 // LDS pitch of feature-contiguous rows
+    constexpr int PO = 32 + 8;                // LDS pitch of the transposed output tile
     constexpr int KS = D / 16;                // k-steps over the feature dim
     constexpr int NDT = D / 32;               // 32-wide feature tiles
     constexpr int PIECES = 32 * D / 8;        // 16-byte pieces per 32-token tile
     constexpr int PPT = (PIECES + NT - 1) / NT;
-    __shared__ __attribute__((aligned(16))) bf16 X_s[D * PX];
-    __shared__ __attribute__((aligned(16))) bf16 B_s[2][32 * PX];
-    __shared__ __attribute__((aligned(16))) bf16 V_s[2][32 * PX];
+    constexpr int XPT = (D * D / 8 + NT - 1) / NT;
+    constexpr int X_SZ = D * PX, RING = 4 * 32 * PX, OUT_SZ = NW * D * PO;
+    constexpr int LDS = X_SZ > RING ? (X_SZ > OUT_SZ ? X_SZ : OUT_SZ) : (RING > OUT_SZ ? RING : OUT_SZ);
+    __shared__ __attribute__((aligned(16))) bf16 lds[LDS];
+    bf16 *X_s = lds;                                   // phase 1: state
+    bf16 *B_s[2] = {lds, lds + 32 * PX};               // phase 2: token tiles
+    bf16 *V_s[2] = {lds + 64 * PX, lds + 96 * PX};
 
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int role = role0 + lid % nroles;
-    const int rest = lid / nroles;
+    int rest = lid / nroles;
+    const int grp = rest % NG;
+    rest /= NG;
     const int h = rest % p.H, gc = rest / p.H;
     Seq s;
     int t;
@@ -1005,26 +1018,25 @@ __global__ __launch_bounds__(ChunkCfg<C>::NT) void k_chunk_bf16(Params p, int ro
     const int64_t sidx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
     const int64_t cidx = ((int64_t)(s.c0 + t) * p.H + h) * D * D;
 
-    const bf16 *A, *Bm, *Cv;
-    bf16 *Out;
-    const float *seg;
-    const bf16 *loc;
-    int soff;
     const bool rev = role >= 2;                // contraction over c >= r
     const bool xt = role & 1;                  // state read transposed
-    if (role < 2) {
+    const bf16 *seg, *loc;
+    int soff;
+    if (!rev) {
         soff = (t - sl * p.G) * p.C;           // tokens from the segment start
-        seg = p.Pseg + sidx;
+        seg = (const bf16 *)p.Pseg + sidx;
         loc = p.G > 1 ? (const bf16 *)p.Lc + cidx : nullptr;
     } else {
         const int seg_end = min((sl + 1) * p.G * p.C, s.len);
         soff = seg_end - (tok + Ct);           // tokens after the chunk, in the segment
-        seg = p.Rseg + sidx;
+        seg = (const bf16 *)p.Rseg + sidx;
         loc = p.G > 1 ? (const bf16 *)p.Rc + cidx : nullptr;
     }
     const bf16 *Qg = (const bf16 *)p.Q + rb * D, *Kg = (const bf16 *)p.K + rb * D;
     const bf16 *Vg = (const bf16 *)p.V + rb * D;
     const bf16 *Og = role ? (const bf16 *)p.dO + rb * D : nullptr;
+    const bf16 *A, *Bm, *Cv;
+    bf16 *Out;
     switch (role) {
     case 0: A = Qg; Bm = Kg; Cv = Vg; Out = (bf16 *)p.O + rb * D; break;
     case 1: A = Og; Bm = Vg; Cv = Kg; Out = (bf16 *)p.dQ + rb * D; break;
@@ -1033,137 +1045,449 @@ __global__ __launch_bounds__(ChunkCfg<C>::NT) void k_chunk_bf16(Params p, int ro
     }
 
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-    int tiles[TPW];
-    tiles[0] = w;
-    if (TPW == 2) tiles[TPW - 1] = NRT - 1 - w;
-
-    // ---- state X = lambda^soff seg + loc -> X_s [dv][dk] (bf16) ----
-    {
-        const float sc = dpow(l2, (float)soff);
-        for (int e = tid * 8; e < D * D; e += NT * 8) {
-            const float4 s0 = *(const float4 *)(seg + e), s1 = *(const float4 *)(seg + e + 4);
-            float lf[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (loc) load16(loc + e, lf);
-            const bf16x8_t v = pack8(sc * s0.x + lf[0], sc * s0.y + lf[1], sc * s0.z + lf[2],
-                                     sc * s0.w + lf[3], sc * s1.x + lf[4], sc * s1.y + lf[5],
-                                     sc * s1.z + lf[6], sc * s1.w + lf[7]);
-            *(bf16x8_t *)(X_s + (e / D) * PX + (e % D)) = v;
-        }
+    const int rt = Cfg::tile(grp, w);
+    const bool live = rt * 32 < Ct;            // this wave has output rows
+    const int nct = (Ct + 31) / 32;
+    // token tiles this workgroup needs: [c0, c1)
+    int tmin = C, tmax = -1;
+    for (int ww = 0; ww < NW; ++ww) {
+        const int tt = Cfg::tile(grp, ww);
+        if (tt < nct) { tmin = min(tmin, tt); tmax = max(tmax, tt); }
     }
+    if (tmax < 0) return;                      // no rows in this group (short chunk)
+    const int c0 = rev ? tmin : 0, c1 = rev ? nct : tmax + 1;
 
-    // ---- A fragments of this wave's row tiles (registers) ----
-    bf16x8_t af[TPW][KS];
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int row = tiles[tt] * 32 + (l & 31);
+    // ---- loads issued up front: A fragments, first two token tiles ----
+    bf16x8_t af[KS];
+    {
+        const int row = rt * 32 + (l & 31);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
             if (row < Ct) v = *(const uint4 *)(A + (int64_t)row * D + ks * 16 + (l >> 5) * 8);
-            af[tt][ks] = __builtin_bit_cast(bf16x8_t, v);
+            af[ks] = __builtin_bit_cast(bf16x8_t, v);
         }
     }
-
-    // ---- staging of 32-token tiles of B and Cv, with register prefetch ----
-    const int nct = (Ct + 31) / 32;
-    uint4 pb[PPT], pv[PPT];
-    auto fetch = [&](int ct) {
+    uint4 pA[2 * PPT], pB[2 * PPT];            // two prefetch sets: [B pieces | Cv pieces]
+    auto fetch = [&](int ct, uint4 (&set)[2 * PPT]) {
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
             const int i = tid + k * NT;
             const int r = i / (D / 8), c = (i % (D / 8)) * 8;
             const int row = ct * 32 + r;
-            pb[k] = pv[k] = make_uint4(0u, 0u, 0u, 0u);
+            set[k] = set[PPT + k] = make_uint4(0u, 0u, 0u, 0u);
             if (i < PIECES && row < Ct) {
-                pb[k] = *(const uint4 *)(Bm + (int64_t)row * D + c);
-                pv[k] = *(const uint4 *)(Cv + (int64_t)row * D + c);
+                set[k] = *(const uint4 *)(Bm + (int64_t)row * D + c);
+                set[PPT + k] = *(const uint4 *)(Cv + (int64_t)row * D + c);
             }
         }
     };
-    auto deposit = [&](int buf) {
+    auto deposit = [&](const uint4 (&set)[2 * PPT], int buf) {
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
             const int i = tid + k * NT;
             if (i < PIECES) {
                 const int r = i / (D / 8), c = (i % (D / 8)) * 8;
-                *(uint4 *)(&B_s[buf][r * PX + c]) = pb[k];
-                *(uint4 *)(&V_s[buf][r * PX + c]) = pv[k];
+                *(uint4 *)(B_s[buf] + r * PX + c) = set[k];
+                *(uint4 *)(V_s[buf] + r * PX + c) = set[PPT + k];
             }
         }
     };
-    fetch(0);
-    deposit(0);
-    __syncthreads();   // X_s and the first tile
+    fetch(c0, pA);
+    if (c0 + 1 < c1) fetch(c0 + 1, pB);
+
+    // ---- state X = lambda^soff seg + loc -> X_s [dv][dk] ----
+    {
+        const float sc = dpow(l2, (float)soff);
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+            const int e = (tid + k * NT) * 8;
+            if (e < D * D) {
+                float sf[8], lf[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                load16(seg + e, sf);
+                if (loc) load16(loc + e, lf);
+                *(bf16x8_t *)(X_s + (e / D) * PX + (e % D)) =
+                    pack8(sc * sf[0] + lf[0], sc * sf[1] + lf[1], sc * sf[2] + lf[2],
+                          sc * sf[3] + lf[3], sc * sf[4] + lf[4], sc * sf[5] + lf[5],
+                          sc * sf[6] + lf[6], sc * sf[7] + lf[7]);
+            }
+        }
+    }
+    __syncthreads();
 
     // ---- inter-chunk term: acc = lambda^e(r) A_r X ----
-    f32x16 acc[TPW][NDT];
+    f32x16 acc[NDT];
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-        for (int nt = 0; nt < NDT; ++nt) zero(acc[tt][nt]);
-#pragma unroll
-    for (int nt = 0; nt < NDT; ++nt)
+    for (int nt = 0; nt < NDT; ++nt) {
+        zero(acc[nt]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8_t xf = xt ? frag_cols<false>(X_s, PX, ks * 16, nt * 32)
                                    : frag_rows(X_s, PX, nt * 32, ks * 16);
-#pragma unroll
-            for (int tt = 0; tt < TPW; ++tt) mma(acc[tt][nt], af[tt][ks], xf);
+            mma(acc[nt], af[ks], xf);
         }
-    if (decay || rev) {
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = tiles[tt] * 32 + crow(r);
-                const float sc = dpow(l2, (float)(rev ? (Ct - 1 - row) : (row + 1)));
-#pragma unroll
-                for (int nt = 0; nt < NDT; ++nt) acc[tt][nt][r] *= sc;
-            }
     }
+    if (decay) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = rt * 32 + crow(r);
+            const float sc = dpow(l2, (float)(rev ? (Ct - 1 - row) : (row + 1)));
+#pragma unroll
+            for (int nt = 0; nt < NDT; ++nt) acc[nt][r] *= sc;
+        }
+    }
+    __syncthreads();              // X_s is dead; its space becomes the token-tile ring
+    deposit(pA, 0);
+    __syncthreads();
 
-    // ---- intra-chunk term over 32-token tiles of c ----
-    for (int ct = 0; ct < nct; ++ct) {
-        const int buf = ct & 1;
-        if (ct + 1 < nct) fetch(ct + 1);
+    // ---- intra-chunk term over 32-token tiles c0 .. c1-1 ----
+    auto compute = [&](int ct, int buf) {
+        if (!live || (rev ? (ct < rt) : (ct > rt))) return;
+        f32x16 st;
+        zero(st);
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const int rt = tiles[tt];
-            if (rt * 32 >= Ct || (rev ? (ct < rt) : (ct > rt))) continue;
-            f32x16 st;
-            zero(st);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                mma(st, frag_rows(B_s[buf], PX, 0, ks * 16), af[tt][ks]);   // S^T: c x r
+        for (int ks = 0; ks < KS; ++ks)
+            mma(st, frag_rows(B_s[buf], PX, 0, ks * 16), af[ks]);   // S^T: c x r
+        if (ct == rt || decay || (ct + 1) * 32 > Ct) {
             const int r = rt * 32 + (l & 31);
-            const bool diag = ct == rt;
-            if (diag || decay || (ct + 1) * 32 > Ct) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int c = ct * 32 + crow(i);
-                    const int dist = rev ? (c - r) : (r - c);
-                    const bool ok = dist >= 0 && c < Ct && r < Ct;
-                    st[i] = ok ? (decay ? st[i] * dpow(l2, (float)dist) : st[i]) : 0.f;
-                }
-            }
-            const bf16x8_t s0 = pack8(st[0], st[1], st[2], st[3], st[4], st[5], st[6], st[7]);
-            const bf16x8_t s1 = pack8(st[8], st[9], st[10], st[11], st[12], st[13], st[14], st[15]);
-#pragma unroll
-            for (int nt = 0; nt < NDT; ++nt) {
-                mma(acc[tt][nt], s0, frag_cols<true>(V_s[buf], PX, 0, nt * 32));
-                mma(acc[tt][nt], s1, frag_cols<true>(V_s[buf], PX, 16, nt * 32));
+            for (int i = 0; i < 16; ++i) {
+                const int c = ct * 32 + crow(i);
+                const int dist = rev ? (c - r) : (r - c);
+                const bool ok = dist >= 0 && c < Ct && r < Ct;
+                st[i] = ok ? (decay ? st[i] * dpow(l2, (float)dist) : st[i]) : 0.f;
             }
         }
-        if (ct + 1 < nct) deposit(buf ^ 1);
+        const bf16x8_t s0 = pack8(st[0], st[1], st[2], st[3], st[4], st[5], st[6], st[7]);
+        const bf16x8_t s1 = pack8(st[8], st[9], st[10], st[11], st[12], st[13], st[14], st[15]);
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt) {
+            mma(acc[nt], s0, frag_cols<true>(V_s[buf], PX, 0, nt * 32));
+            mma(acc[nt], s1, frag_cols<true>(V_s[buf], PX, 16, nt * 32));
+        }
+    };
+    // step ct: tile ct is in LDS buffer (ct - c0) & 1, tile ct+1 in `cur`
+    // (registers), `nxt` receives tile ct+2.
+    auto step = [&](int ct, uint4 (&cur)[2 * PPT], uint4 (&nxt)[2 * PPT]) {
+        const int buf = (ct - c0) & 1;
+        if (ct + 2 < c1) fetch(ct + 2, nxt);
+        compute(ct, buf);
+        if (ct + 1 < c1) deposit(cur, buf ^ 1);
         __syncthreads();
+    };
+    for (int ct = c0; ct < c1; ct += 2) {
+        step(ct, pB, pA);
+        if (ct + 1 < c1) step(ct + 1, pA, pB);
     }
 
-    // ---- store ----
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
+    // ---- store: accumulators -> LDS (transposed) -> 16-byte rows ----
+    bf16 *O_s = lds + w * D * PO;              // [feature][row] for this wave
+    {
+        const int col = l & 31, g = l >> 5;
 #pragma unroll
         for (int nt = 0; nt < NDT; ++nt)
-            store_rows(acc[tt][nt], Out, D, tiles[tt] * 32, nt * 32, Ct);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                store4(O_s + (nt * 32 + col) * PO + q * 8 + g * 4, acc[nt][q * 4 + 0],
+                       acc[nt][q * 4 + 1], acc[nt][q * 4 + 2], acc[nt][q * 4 + 3]);
+    }
+    __syncthreads();
+    if (live) {
+        const int row = rt * 32 + (l & 31);
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+            const bf16x8_t v = frag_cols<false>(O_s, PO, j * 16, 0);   // row, features 16j+8g..
+            if (row < Ct)
+                *(bf16x8_t *)(Out + (int64_t)row * D + j * 16 + (l >> 5) * 8) = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk kernel with direct-to-LDS staging.  global_load_lds_dwordx4 writes lane
+// l's 16 bytes to lds_base + 16*l, so tiles are stored unpadded with an XOR
+// swizzle of their 16-byte pieces: piece p of row r sits in slot
+// r*PR + (p ^ (r % PR)), PR = pieces per row.  Token tiles go through a ring
+// of three distinct LDS buffers (two tiles in flight while one is consumed);
+// barriers fence LDS only, and each wave waits with an explicit vmcnt for its
+// own copies of the tile it is about to read.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+__device__ __forceinline__ int sw_off(int r, int c) {
+    constexpr int PR = D / 8;
+    return (r * PR + ((c >> 3) ^ (r & (PR - 1)))) * 8 + (c & 7);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t frag_rows_sw(const bf16 *X, int r0, int k0) {
+    const int l = lane_id();
+    return *(const bf16x8_t *)(X + sw_off<D>(r0 + (l & 31), k0 + (l >> 5) * 8));
+}
+
+template <int D, bool PERM>
+__device__ __forceinline__ bf16x8_t frag_cols_sw(const bf16 *X, int k0, int n0) {
+    const int l = lane_id(), i = l & 15, h = l >> 4, g = h >> 1;
+    const int col = n0 + (h & 1) * 16 + 4 * (i & 3);
+    const int ra = k0 + (PERM ? 4 * g : 8 * g) + (i >> 2);
+    const int rb = ra + (PERM ? 8 : 4);
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(X + sw_off<D>(ra, col)));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(X + sw_off<D>(rb, col)));
+    const v8s c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, c);
+}
+
+// s_waitcnt: vmcnt(vm), no wait on the other counters.
+#define LASP_WAIT_VM(vm) __builtin_amdgcn_s_waitcnt(((vm) & 15) | (((vm) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Workgroup barrier for LDS traffic only.  A release fence would also wait for
+// every outstanding global->LDS copy (they count in vmcnt), draining the
+// prefetch ring; instead each wave drains its own LDS operations (lgkmcnt) and,
+// before calling this, waits (vmcnt) for exactly the copies whose data the
+// workgroup reads next.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int N> struct IC { static constexpr int value = N; };
+
+template <int D, int C>
+__global__ __launch_bounds__(ChunkCfg<C>::NT) void k_chunk_dma(Params p, int role0, int nroles) {
+    using Cfg = ChunkCfg<C>;
+    constexpr int NW = Cfg::NW, NT = Cfg::NT, NG = Cfg::NG;
+    constexpr int PR = D / 8;                 // 16-byte pieces per row
+    constexpr int PO = 32 + 8;                // pitch of the transposed output tile
+    constexpr int KS = D / 16, NDT = D / 32;
+    constexpr int TILE = 32 * D;              // elements of one 32-token tile
+    constexpr int NI_T = 2 * TILE / 512;      // wave copies per B+Cv tile pair (512 elem each)
+    constexpr int DPW = NI_T / NW;            // copies per wave per tile pair
+    static_assert(NI_T % NW == 0, "tile copies must split evenly over waves");
+    constexpr int NI_X = D * D / 512;         // wave copies of the state
+    constexpr int XPW = (NI_X + NW - 1) / NW;
+    constexpr int X_ELEMS = D * D > D * PO ? D * D : D * PO;
+    __shared__ __attribute__((aligned(16))) bf16 XS[X_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 R0[2 * TILE];
+    __shared__ __attribute__((aligned(16))) bf16 R1[2 * TILE];
+    __shared__ __attribute__((aligned(16))) bf16 R2[2 * TILE];
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int role = role0 + lid % nroles;
+    int rest = lid / nroles;
+    const int grp = rest % NG;
+    rest /= NG;
+    const int h = rest % p.H, gc = rest / p.H;
+    Seq s;
+    int t;
+    if (!chunk_seq(p, gc, s, t)) return;
+    const int tok = t * p.C;
+    const int Ct = min(p.C, s.len - tok);
+    const int sl = t / p.G;
+    if (s.s0 + sl >= p.n_segs_ub) return;   // only with malformed cu_seqlens
+    const float l2 = head_log2_decay(p, h);
+    const bool decay = l2 != 0.f;
+    const int64_t rb = row_base(p, s, h) + tok;
+    const int64_t sidx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
+    const int64_t cidx = ((int64_t)(s.c0 + t) * p.H + h) * D * D;
+
+    const bool rev = role >= 2;                // contraction over c >= r
+    const bool xt = role & 1;                  // state read transposed
+    const bf16 *seg, *loc;
+    int soff;
+    if (!rev) {
+        soff = (t - sl * p.G) * p.C;
+        seg = (const bf16 *)p.Pseg + sidx;
+        loc = p.G > 1 ? (const bf16 *)p.Lc + cidx : nullptr;
+    } else {
+        const int seg_end = min((sl + 1) * p.G * p.C, s.len);
+        soff = seg_end - (tok + Ct);
+        seg = (const bf16 *)p.Rseg + sidx;
+        loc = p.G > 1 ? (const bf16 *)p.Rc + cidx : nullptr;
+    }
+    const bf16 *Qg = (const bf16 *)p.Q + rb * D, *Kg = (const bf16 *)p.K + rb * D;
+    const bf16 *Vg = (const bf16 *)p.V + rb * D;
+    const bf16 *Og = role ? (const bf16 *)p.dO + rb * D : nullptr;
+    const bf16 *A, *Bm, *Cv;
+    bf16 *Out;
+    switch (role) {
+    case 0: A = Qg; Bm = Kg; Cv = Vg; Out = (bf16 *)p.O + rb * D; break;
+    case 1: A = Og; Bm = Vg; Cv = Kg; Out = (bf16 *)p.dQ + rb * D; break;
+    case 2: A = Kg; Bm = Qg; Cv = Og; Out = (bf16 *)p.dV + rb * D; break;
+    default: A = Vg; Bm = Og; Cv = Qg; Out = (bf16 *)p.dK + rb * D; break;
+    }
+
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int rt = Cfg::tile(grp, w);
+    const bool live = rt * 32 < Ct;
+    const int nct = (Ct + 31) / 32;
+    int tmin = C, tmax = -1;
+    for (int ww = 0; ww < NW; ++ww) {
+        const int tt = Cfg::tile(grp, ww);
+        if (tt < nct) { tmin = min(tmin, tt); tmax = max(tmax, tt); }
+    }
+    if (tmax < 0) return;
+    const int c0 = rev ? tmin : 0, c1 = rev ? nct : tmax + 1;
+
+    // copy token tile ct (B rows then Cv rows, swizzled) into buffer dst
+    auto dma_tile = [&](int ct, bf16 *dst) {
+#pragma unroll
+        for (int k = 0; k < DPW; ++k) {
+            const int j = w + k * NW;                       // wave copy index
+            const int half = j / (NI_T / 2);                // 0: B, 1: Cv
+            const int slot = (j % (NI_T / 2)) * 64 + l;
+            const int r = slot / PR, pc = (slot % PR) ^ (r & (PR - 1));
+            const int row = min(ct * 32 + r, Ct - 1);       // rows past Ct: any valid row
+            const bf16 *src = (half ? Cv : Bm) + (int64_t)row * D + pc * 8;
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + j * 512), 16, 0, 0);
+        }
+    };
+
+    // ---- loads issued up front ----
+    bf16x8_t af[KS];
+    {
+        const int row = rt * 32 + (l & 31);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (row < Ct) v = *(const uint4 *)(A + (int64_t)row * D + ks * 16 + (l >> 5) * 8);
+            af[ks] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+    constexpr int SPT = (D * D / 8 + NT - 1) / NT;          // state pieces per thread
+    uint4 sg[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+        const int q = tid + k * NT;
+        sg[k] = q < D * D / 8 ? *(const uint4 *)(seg + q * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (loc) {
+#pragma unroll
+        for (int k = 0; k < XPW; ++k) {
+            const int j = w + k * NW;
+            if (j < NI_X) {
+                const int slot = j * 64 + l;
+                const int r = slot / PR, pc = (slot % PR) ^ (r & (PR - 1));
+                __builtin_amdgcn_global_load_lds((const void *)(loc + r * D + pc * 8),
+                                                 (lds_void *)(XS + j * 512), 16, 0, 0);
+            }
+        }
+    }
+    dma_tile(c0, R0);
+    if (c0 + 1 < c1) dma_tile(c0 + 1, R1);
+
+    // ---- state X = lambda^soff seg + loc (in XS, swizzled) ----
+    if (c0 + 1 < c1) LASP_WAIT_VM(2 * DPW);
+    else LASP_WAIT_VM(DPW);
+    lds_barrier();
+    {
+        const float sc = dpow(l2, (float)soff);
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const int q = tid + k * NT;
+            if (q < D * D / 8) {
+                const int r = q / PR, pc = q % PR;
+                bf16 *dst = XS + (r * PR + (pc ^ (r & (PR - 1)))) * 8;
+                float sf[8], lf[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                load16((const bf16 *)&sg[k], sf);
+                if (loc) load16(dst, lf);
+                *(bf16x8_t *)dst = pack8(sc * sf[0] + lf[0], sc * sf[1] + lf[1], sc * sf[2] + lf[2],
+                                         sc * sf[3] + lf[3], sc * sf[4] + lf[4], sc * sf[5] + lf[5],
+                                         sc * sf[6] + lf[6], sc * sf[7] + lf[7]);
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- inter-chunk term ----
+    f32x16 acc[NDT];
+#pragma unroll
+    for (int nt = 0; nt < NDT; ++nt) {
+        zero(acc[nt]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8_t xf = xt ? frag_cols_sw<D, false>(XS, ks * 16, nt * 32)
+                                   : frag_rows_sw<D>(XS, nt * 32, ks * 16);
+            mma(acc[nt], af[ks], xf);
+        }
+    }
+    if (decay) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = rt * 32 + crow(r);
+            const float sc = dpow(l2, (float)(rev ? (Ct - 1 - row) : (row + 1)));
+#pragma unroll
+            for (int nt = 0; nt < NDT; ++nt) acc[nt][r] *= sc;
+        }
+    }
+
+    // ---- intra-chunk term: ring of three buffers ----
+    auto compute = [&](int ct, const bf16 *T) {
+        if (!live || (rev ? (ct < rt) : (ct > rt))) return;
+        const bf16 *Bt = T, *Vt = T + TILE;
+        f32x16 st;
+        zero(st);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) mma(st, frag_rows_sw<D>(Bt, 0, ks * 16), af[ks]);
+        if (ct == rt || decay || (ct + 1) * 32 > Ct) {
+            const int r = rt * 32 + (l & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int c = ct * 32 + crow(i);
+                const int dist = rev ? (c - r) : (r - c);
+                const bool ok = dist >= 0 && c < Ct && r < Ct;
+                st[i] = ok ? (decay ? st[i] * dpow(l2, (float)dist) : st[i]) : 0.f;
+            }
+        }
+        const bf16x8_t s0 = pack8(st[0], st[1], st[2], st[3], st[4], st[5], st[6], st[7]);
+        const bf16x8_t s1 = pack8(st[8], st[9], st[10], st[11], st[12], st[13], st[14], st[15]);
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt) {
+            mma(acc[nt], s0, frag_cols_sw<D, true>(Vt, 0, nt * 32));
+            mma(acc[nt], s1, frag_cols_sw<D, true>(Vt, 16, nt * 32));
+        }
+    };
+    auto iter = [&](auto bufc, int ct) {
+        constexpr int b = decltype(bufc)::value;
+        bf16 *cur = b == 0 ? R0 : (b == 1 ? R1 : R2);
+        bf16 *nxt2 = b == 0 ? R2 : (b == 1 ? R0 : R1);     // buffer of tile ct+2
+        if (ct + 1 < c1) LASP_WAIT_VM(DPW);
+        else LASP_WAIT_VM(0);
+        lds_barrier();
+        if (ct + 2 < c1) dma_tile(ct + 2, nxt2);
+        compute(ct, cur);
+    };
+    for (int ct = c0; ct < c1; ct += 3) {
+        iter(IC<0>(), ct);
+        if (ct + 1 < c1) iter(IC<1>(), ct + 1);
+        if (ct + 2 < c1) iter(IC<2>(), ct + 2);
+    }
+
+    // ---- store: accumulators -> LDS (transposed) -> 16-byte rows ----
+    lds_barrier();
+    bf16 *O_s = w == 0 ? R0 : (w == 1 ? R1 : (w == 2 ? R2 : XS));
+    {
+        const int col = l & 31, g = l >> 5;
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                store4(O_s + (nt * 32 + col) * PO + q * 8 + g * 4, acc[nt][q * 4 + 0],
+                       acc[nt][q * 4 + 1], acc[nt][q * 4 + 2], acc[nt][q * 4 + 3]);
+    }
+    lds_barrier();
+    if (live) {
+        const int row = rt * 32 + (l & 31);
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+            const bf16x8_t v = frag_cols<false>(O_s, PO, j * 16, 0);
+            if (row < Ct)
+                *(bf16x8_t *)(Out + (int64_t)row * D + j * 16 + (l >> 5) * 8) = v;
+        }
+    }
 }
 
 // Local chunk states (bf16): one workgroup per (segment, head).
@@ -1309,7 +1633,7 @@ static hipError_t fwd_impl(const Params &p, bool with_output, hipStream_t st, hi
     hipLaunchKernelGGL((k_fwd_local<T, D, BT>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
     rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_fwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    hipLaunchKernelGGL((k_fwd_segscan<D, T>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
     rec(ev, 2, st);
     if (with_output)
         hipLaunchKernelGGL((k_fwd_out<T, D, BT>), dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), 0,
@@ -1326,7 +1650,7 @@ static hipError_t bwd_impl(const Params &p, hipStream_t st, hipEvent_t *ev) {
     hipLaunchKernelGGL((k_bwd_local<T, D, BT>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
     rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_bwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    hipLaunchKernelGGL((k_bwd_segscan<D, T>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
     rec(ev, 2, st);
     hipLaunchKernelGGL((k_bwd_grads<T, D, BT>), dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), 0, st,
                        p);
@@ -1337,8 +1661,15 @@ static hipError_t bwd_impl(const Params &p, hipStream_t st, hipEvent_t *ev) {
 // bf16: transpose-read local-state kernel and the shared chunk kernel.
 template <int D, int C>
 static void chunk_launch(const Params &p, int role0, int nroles, hipStream_t st) {
-    hipLaunchKernelGGL((k_chunk_bf16<D, C>), dim3(round8(p.n_chunks_ub * p.H * nroles)),
+#ifdef LASP_CHUNK_REGISTER_STAGING
+    hipLaunchKernelGGL((k_chunk_bf16<D, C>),
+                       dim3(round8(p.n_chunks_ub * p.H * nroles * ChunkCfg<C>::NG)),
                        dim3(ChunkCfg<C>::NT), 0, st, p, role0, nroles);
+#else
+    hipLaunchKernelGGL((k_chunk_dma<D, C>),
+                       dim3(round8(p.n_chunks_ub * p.H * nroles * ChunkCfg<C>::NG)),
+                       dim3(ChunkCfg<C>::NT), 0, st, p, role0, nroles);
+#endif
 }
 
 template <int D>
@@ -1357,7 +1688,7 @@ static hipError_t fwd_bf16(const Params &p, bool with_output, hipStream_t st, hi
     hipLaunchKernelGGL((k_local_bf16<D>), dim3(p.n_segs_ub * p.H), dim3(256), 0, st, p, 0);
     rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_fwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    hipLaunchKernelGGL((k_fwd_segscan<D, bf16>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
     rec(ev, 2, st);
     if (with_output) chunk_dispatch<D>(p, 0, 1, st);
     rec(ev, 3, st);
@@ -1371,7 +1702,7 @@ static hipError_t bwd_bf16(const Params &p, hipStream_t st, hipEvent_t *ev) {
     hipLaunchKernelGGL((k_local_bf16<D>), dim3(p.n_segs_ub * p.H), dim3(256), 0, st, p, 1);
     rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_bwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    hipLaunchKernelGGL((k_bwd_segscan<D, bf16>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
     rec(ev, 2, st);
     chunk_dispatch<D>(p, 1, 3, st);   // dQ, dV, dK of a chunk are neighbours in launch order
     rec(ev, 3, st);
