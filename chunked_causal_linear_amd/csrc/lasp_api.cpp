@@ -74,7 +74,9 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl) {
     pl.n_segs_ub = (int)segs_ub;
     const size_t dd = (size_t)pl.D * pl.D;
     pl.table_b = pl.varlen ? align_up(2 * sizeof(int32_t) * ((size_t)pl.nseq + 1)) : 0;
-    pl.local_b = align_up((size_t)pl.n_chunks_ub * pl.H * dd * pl.esz);
+    // per-chunk local states: only the float32 path keeps them (the bf16 path
+    // recomputes chunk states inside its segment sweep)
+    pl.local_b = dt == LASP_BF16 ? 0 : align_up((size_t)pl.n_chunks_ub * pl.H * dd * pl.esz);
     pl.seg_b = align_up((size_t)pl.n_segs_ub * pl.H * dd * sizeof(float));
     pl.cache_b = pl.local_b + pl.seg_b;
     return LASP_OK;
@@ -197,7 +199,7 @@ int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
     p.Z = (float *)w;
     w += pl.seg_b;
     char *c = cache ? (char *)state_cache : w;
-    p.Lc = c;
+    p.Lc = pl.local_b ? c : nullptr;
     p.Pseg = (float *)(c + pl.local_b);
     return hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, true, (hipStream_t)stream,
                                        (hipEvent_t *)events));
@@ -256,7 +258,7 @@ int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
         p.seg_prefix = p.chunk_prefix + (pl.nseq + 1);
         w += pl.table_b;
     }
-    p.Rc = w;
+    p.Rc = pl.local_b ? w : nullptr;
     w += pl.local_b;
     p.Rseg = (float *)w;
     w += pl.seg_b;
@@ -264,10 +266,10 @@ int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
     w += pl.seg_b;
     const hipStream_t hs = (hipStream_t)stream;
     if (cache) {
-        p.Lc = const_cast<void *>(state_cache);
+        p.Lc = pl.local_b ? const_cast<void *>(state_cache) : nullptr;
         p.Pseg = (float *)((char *)state_cache + pl.local_b);
     } else {   // recompute the forward states (no output, no M_out)
-        p.Lc = w;
+        p.Lc = pl.local_b ? w : nullptr;
         p.Pseg = (float *)(w + pl.local_b);
         p.Z = (float *)(w + pl.cache_b);
         rc = hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, false, hs));

@@ -72,8 +72,8 @@ __device__ __forceinline__ void mma(f32x16 &c, const f32x4 &a, const f32x4 &b) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // Row (within the 32x32 tile) of accumulator element r for this lane.
-__device__ __forceinline__ int crow(int r) {
-    return (r >> 2) * 8 + ((threadIdx.x & 63) >> 5) * 4 + (r & 3);
+__device__ __forceinline__ int crow(int r, int l = threadIdx.x & 63) {
+    return (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
 }
 
 __device__ __forceinline__ float tof(float x) { return x; }
@@ -918,13 +918,6 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-// Operand fragment from a row-major LDS tile X[r][k] (k contiguous):
-// rows r0 + lane%32, k elements k0 + (lane/32)*8 + [0, 8).
-__device__ __forceinline__ bf16x8_t frag_rows(const bf16 *X, int pitch, int r0, int k0) {
-    const int l = lane_id();
-    return *(const bf16x8_t *)(X + (r0 + (l & 31)) * pitch + k0 + (l >> 5) * 8);
-}
-
 // Operand fragment from an LDS tile stored X[k][n] (n contiguous), operand row
 // n0 + lane%32.  With g = lane/32 the 8 contraction elements are
 // k0 + 8g + [0, 8) (PERM = false) or k0 + 4g + {0..3, 8..11} (PERM = true).
@@ -932,8 +925,9 @@ __device__ __forceinline__ bf16x8_t frag_rows(const bf16 *X, int pitch, int r0, 
 // the 4 elements at row rb + i/4, columns cb + 4*(i%4), lane j of the group
 // receives rows rb + 0..3 of column cb + j.
 template <bool PERM>
-__device__ __forceinline__ bf16x8_t frag_cols(const bf16 *X, int pitch, int k0, int n0) {
-    const int l = lane_id(), i = l & 15, h = l >> 4, g = h >> 1;
+__device__ __forceinline__ bf16x8_t frag_cols(const bf16 *X, int pitch, int k0, int n0,
+                                              int l = lane_id()) {
+    const int i = l & 15, h = l >> 4, g = h >> 1;
     const int col = n0 + (h & 1) * 16 + 4 * (i & 3);
     const int ra = k0 + (PERM ? 4 * g : 8 * g) + (i >> 2);
     const int rb = ra + (PERM ? 8 : 4);
@@ -959,276 +953,55 @@ __device__ __forceinline__ uint4 scale8(uint4 v, float s) {
     return __builtin_bit_cast(uint4, b);
 }
 
-// Roles of the chunk kernel.  All four compute, for the output rows r of one
-// chunk (length Ct),
-//   Out[r] = sum_{c in causal range of r} lambda^|r-c| (A_r . B_c) Cv_c
-//            + lambda^e(r) A_r X
-// with X = lambda^soff seg + loc the chunk's state ([dv][dk] in memory):
-//   0  O  : A=Q,  B=K,  Cv=V,  X=P,   c <= r, e = r+1        (LASP Eqs. 7, 9, 11)
-//   1  dQ : A=dO, B=V,  Cv=K,  X=P^T, c <= r, e = r+1        (LASP Eqs. 14-16)
-//   2  dV : A=K,  B=Q,  Cv=dO, X=R,   c >= r, e = Ct-1-r     (LASP Eqs. 21-22)
-//   3  dK : A=V,  B=dO, Cv=Q,  X=R^T, c >= r, e = Ct-1-r     (LASP Eqs. 17-19)
-// Each wave owns one 32-row tile.  A 256-token chunk is split over two
-// workgroups with row tiles {0,1,6,7} and {2,3,4,5}, which carry equal work in
-// both directions; shorter chunks use one workgroup of C/32 waves.
-template <int C> struct ChunkCfg {
-    static constexpr int NRT = C / 32;                 // 32-row tiles per chunk
-    static constexpr int NG = NRT >= 8 ? 2 : 1;        // workgroups per chunk
-    static constexpr int NW = NRT / NG;                // waves per workgroup
-    static constexpr int NT = 64 * NW;
-    __device__ static int tile(int g, int w) {
-        return NG == 1 ? w : (g ? 2 + w : (w < 2 ? w : w + 4));
-    }
-};
-
-template <int D, int C>
-__global__ __launch_bounds__(ChunkCfg<C>::NT) void k_chunk_bf16(Params p, int role0, int nroles) {
-    using Cfg = ChunkCfg<C>;
-    constexpr int NW = Cfg::NW, NT = Cfg::NT, NG = Cfg::NG;
-    constexpr int PX = D + 8;                 // LDS pitch of feature-contiguous rows
-    constexpr int PO = 32 + 8;                // LDS pitch of the transposed output tile
-    constexpr int KS = D / 16;                // k-steps over the feature dim
-    constexpr int NDT = D / 32;               // 32-wide feature tiles
-    constexpr int PIECES = 32 * D / 8;        // 16-byte pieces per 32-token tile
-    constexpr int PPT = (PIECES + NT - 1) / NT;
-    constexpr int XPT = (D * D / 8 + NT - 1) / NT;
-    constexpr int X_SZ = D * PX, RING = 4 * 32 * PX, OUT_SZ = NW * D * PO;
-    constexpr int LDS = X_SZ > RING ? (X_SZ > OUT_SZ ? X_SZ : OUT_SZ) : (RING > OUT_SZ ? RING : OUT_SZ);
-    __shared__ __attribute__((aligned(16))) bf16 lds[LDS];
-    bf16 *X_s = lds;                                   // phase 1: state
-    bf16 *B_s[2] = {lds, lds + 32 * PX};               // phase 2: token tiles
-    bf16 *V_s[2] = {lds + 64 * PX, lds + 96 * PX};
-
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int role = role0 + lid % nroles;
-    int rest = lid / nroles;
-    const int grp = rest % NG;
-    rest /= NG;
-    const int h = rest % p.H, gc = rest / p.H;
-    Seq s;
-    int t;
-    if (!chunk_seq(p, gc, s, t)) return;
-    const int tok = t * p.C;
-    const int Ct = min(p.C, s.len - tok);
-    const int sl = t / p.G;
-    if (s.s0 + sl >= p.n_segs_ub) return;   // only with malformed cu_seqlens
-    const float l2 = head_log2_decay(p, h);
-    const bool decay = l2 != 0.f;
-    const int64_t rb = row_base(p, s, h) + tok;
-    const int64_t sidx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
-    const int64_t cidx = ((int64_t)(s.c0 + t) * p.H + h) * D * D;
-
-    const bool rev = role >= 2;                // contraction over c >= r
-    const bool xt = role & 1;                  // state read transposed
-    const bf16 *seg, *loc;
-    int soff;
-    if (!rev) {
-        soff = (t - sl * p.G) * p.C;           // tokens from the segment start
-        seg = (const bf16 *)p.Pseg + sidx;
-        loc = p.G > 1 ? (const bf16 *)p.Lc + cidx : nullptr;
-    } else {
-        const int seg_end = min((sl + 1) * p.G * p.C, s.len);
-        soff = seg_end - (tok + Ct);           // tokens after the chunk, in the segment
-        seg = (const bf16 *)p.Rseg + sidx;
-        loc = p.G > 1 ? (const bf16 *)p.Rc + cidx : nullptr;
-    }
-    const bf16 *Qg = (const bf16 *)p.Q + rb * D, *Kg = (const bf16 *)p.K + rb * D;
-    const bf16 *Vg = (const bf16 *)p.V + rb * D;
-    const bf16 *Og = role ? (const bf16 *)p.dO + rb * D : nullptr;
-    const bf16 *A, *Bm, *Cv;
-    bf16 *Out;
-    switch (role) {
-    case 0: A = Qg; Bm = Kg; Cv = Vg; Out = (bf16 *)p.O + rb * D; break;
-    case 1: A = Og; Bm = Vg; Cv = Kg; Out = (bf16 *)p.dQ + rb * D; break;
-    case 2: A = Kg; Bm = Qg; Cv = Og; Out = (bf16 *)p.dV + rb * D; break;
-    default: A = Vg; Bm = Og; Cv = Qg; Out = (bf16 *)p.dK + rb * D; break;
-    }
-
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-    const int rt = Cfg::tile(grp, w);
-    const bool live = rt * 32 < Ct;            // this wave has output rows
-    const int nct = (Ct + 31) / 32;
-    // token tiles this workgroup needs: [c0, c1)
-    int tmin = C, tmax = -1;
-    for (int ww = 0; ww < NW; ++ww) {
-        const int tt = Cfg::tile(grp, ww);
-        if (tt < nct) { tmin = min(tmin, tt); tmax = max(tmax, tt); }
-    }
-    if (tmax < 0) return;                      // no rows in this group (short chunk)
-    const int c0 = rev ? tmin : 0, c1 = rev ? nct : tmax + 1;
-
-    // ---- loads issued up front: A fragments, first two token tiles ----
-    bf16x8_t af[KS];
-    {
-        const int row = rt * 32 + (l & 31);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (row < Ct) v = *(const uint4 *)(A + (int64_t)row * D + ks * 16 + (l >> 5) * 8);
-            af[ks] = __builtin_bit_cast(bf16x8_t, v);
-        }
-    }
-    uint4 pA[2 * PPT], pB[2 * PPT];            // two prefetch sets: [B pieces | Cv pieces]
-    auto fetch = [&](int ct, uint4 (&set)[2 * PPT]) {
-#pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const int i = tid + k * NT;
-            const int r = i / (D / 8), c = (i % (D / 8)) * 8;
-            const int row = ct * 32 + r;
-            set[k] = set[PPT + k] = make_uint4(0u, 0u, 0u, 0u);
-            if (i < PIECES && row < Ct) {
-                set[k] = *(const uint4 *)(Bm + (int64_t)row * D + c);
-                set[PPT + k] = *(const uint4 *)(Cv + (int64_t)row * D + c);
-            }
-        }
-    };
-    auto deposit = [&](const uint4 (&set)[2 * PPT], int buf) {
-#pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const int i = tid + k * NT;
-            if (i < PIECES) {
-                const int r = i / (D / 8), c = (i % (D / 8)) * 8;
-                *(uint4 *)(B_s[buf] + r * PX + c) = set[k];
-                *(uint4 *)(V_s[buf] + r * PX + c) = set[PPT + k];
-            }
-        }
-    };
-    fetch(c0, pA);
-    if (c0 + 1 < c1) fetch(c0 + 1, pB);
-
-    // ---- state X = lambda^soff seg + loc -> X_s [dv][dk] ----
-    {
-        const float sc = dpow(l2, (float)soff);
-#pragma unroll
-        for (int k = 0; k < XPT; ++k) {
-            const int e = (tid + k * NT) * 8;
-            if (e < D * D) {
-                float sf[8], lf[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                load16(seg + e, sf);
-                if (loc) load16(loc + e, lf);
-                *(bf16x8_t *)(X_s + (e / D) * PX + (e % D)) =
-                    pack8(sc * sf[0] + lf[0], sc * sf[1] + lf[1], sc * sf[2] + lf[2],
-                          sc * sf[3] + lf[3], sc * sf[4] + lf[4], sc * sf[5] + lf[5],
-                          sc * sf[6] + lf[6], sc * sf[7] + lf[7]);
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- inter-chunk term: acc = lambda^e(r) A_r X ----
-    f32x16 acc[NDT];
-#pragma unroll
-    for (int nt = 0; nt < NDT; ++nt) {
-        zero(acc[nt]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8_t xf = xt ? frag_cols<false>(X_s, PX, ks * 16, nt * 32)
-                                   : frag_rows(X_s, PX, nt * 32, ks * 16);
-            mma(acc[nt], af[ks], xf);
-        }
-    }
-    if (decay) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = rt * 32 + crow(r);
-            const float sc = dpow(l2, (float)(rev ? (Ct - 1 - row) : (row + 1)));
-#pragma unroll
-            for (int nt = 0; nt < NDT; ++nt) acc[nt][r] *= sc;
-        }
-    }
-    __syncthreads();              // X_s is dead; its space becomes the token-tile ring
-    deposit(pA, 0);
-    __syncthreads();
-
-    // ---- intra-chunk term over 32-token tiles c0 .. c1-1 ----
-    auto compute = [&](int ct, int buf) {
-        if (!live || (rev ? (ct < rt) : (ct > rt))) return;
-        f32x16 st;
-        zero(st);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            mma(st, frag_rows(B_s[buf], PX, 0, ks * 16), af[ks]);   // S^T: c x r
-        if (ct == rt || decay || (ct + 1) * 32 > Ct) {
-            const int r = rt * 32 + (l & 31);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int c = ct * 32 + crow(i);
-                const int dist = rev ? (c - r) : (r - c);
-                const bool ok = dist >= 0 && c < Ct && r < Ct;
-                st[i] = ok ? (decay ? st[i] * dpow(l2, (float)dist) : st[i]) : 0.f;
-            }
-        }
-        const bf16x8_t s0 = pack8(st[0], st[1], st[2], st[3], st[4], st[5], st[6], st[7]);
-        const bf16x8_t s1 = pack8(st[8], st[9], st[10], st[11], st[12], st[13], st[14], st[15]);
-#pragma unroll
-        for (int nt = 0; nt < NDT; ++nt) {
-            mma(acc[nt], s0, frag_cols<true>(V_s[buf], PX, 0, nt * 32));
-            mma(acc[nt], s1, frag_cols<true>(V_s[buf], PX, 16, nt * 32));
-        }
-    };
-    // step ct: tile ct is in LDS buffer (ct - c0) & 1, tile ct+1 in `cur`
-    // (registers), `nxt` receives tile ct+2.
-    auto step = [&](int ct, uint4 (&cur)[2 * PPT], uint4 (&nxt)[2 * PPT]) {
-        const int buf = (ct - c0) & 1;
-        if (ct + 2 < c1) fetch(ct + 2, nxt);
-        compute(ct, buf);
-        if (ct + 1 < c1) deposit(cur, buf ^ 1);
-        __syncthreads();
-    };
-    for (int ct = c0; ct < c1; ct += 2) {
-        step(ct, pB, pA);
-        if (ct + 1 < c1) step(ct + 1, pA, pB);
-    }
-
-    // ---- store: accumulators -> LDS (transposed) -> 16-byte rows ----
-    bf16 *O_s = lds + w * D * PO;              // [feature][row] for this wave
-    {
-        const int col = l & 31, g = l >> 5;
-#pragma unroll
-        for (int nt = 0; nt < NDT; ++nt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                store4(O_s + (nt * 32 + col) * PO + q * 8 + g * 4, acc[nt][q * 4 + 0],
-                       acc[nt][q * 4 + 1], acc[nt][q * 4 + 2], acc[nt][q * 4 + 3]);
-    }
-    __syncthreads();
-    if (live) {
-        const int row = rt * 32 + (l & 31);
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) {
-            const bf16x8_t v = frag_cols<false>(O_s, PO, j * 16, 0);   // row, features 16j+8g..
-            if (row < Ct)
-                *(bf16x8_t *)(Out + (int64_t)row * D + j * 16 + (l >> 5) * 8) = v;
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Chunk kernel with direct-to-LDS staging.  global_load_lds_dwordx4 writes lane
-// l's 16 bytes to lds_base + 16*l, so tiles are stored unpadded with an XOR
-// swizzle of their 16-byte pieces: piece p of row r sits in slot
-// r*PR + (p ^ (r % PR)), PR = pieces per row.  Token tiles go through a ring
-// of three distinct LDS buffers (two tiles in flight while one is consumed);
-// barriers fence LDS only, and each wave waits with an explicit vmcnt for its
-// own copies of the tile it is about to read.
+// Unpadded LDS tiles.  global_load_lds_dwordx4 writes lane l's 16 bytes to
+// lds_base + 16*l, so token tiles are stored without padding and their 16-byte
+// pieces are permuted within each row: piece p of row r sits in slot
+// r*PR + (p ^ key(r)), PR = pieces per row.  key(r) depends on r mod 16 and is
+// linear over GF(2) in its four bits; it is chosen (by exhaustive search over
+// such keys) so that the operand reads below touch every LDS bank once per
+// access group, both for 128-byte and for 256-byte bank rows:
+//   frag_rows_sw  ds_read_b128, 32 consecutive rows, one piece each;
+//   frag_cols_sw  ds_read_b64_tr_b16, 4 consecutive rows x 2 or 4 pieces.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D> struct SwKey {
+    // images of row bits 0..3; key(r) = XOR of the images of the set bits
+    static constexpr int m0 = D == 128 ? 4 : (D == 64 ? 2 : 0);
+    static constexpr int m1 = D == 128 ? 10 : (D == 64 ? 4 : 2);
+    static constexpr int m2 = 1, m3 = 2;
+    static constexpr unsigned long long table() {
+        unsigned long long t = 0;
+        for (int r = 0; r < 16; ++r) {
+            const int k = ((r & 1) ? m0 : 0) ^ ((r & 2) ? m1 : 0) ^ ((r & 4) ? m2 : 0) ^
+                          ((r & 8) ? m3 : 0);
+            t |= (unsigned long long)k << (4 * r);
+        }
+        return t;
+    }
+    static constexpr unsigned long long T = table();
+};
+
+template <int D>
+__device__ __forceinline__ int sw_key(int r) {
+    return (int)((SwKey<D>::T >> (4 * (r & 15))) & 15);
+}
 
 template <int D>
 __device__ __forceinline__ int sw_off(int r, int c) {
     constexpr int PR = D / 8;
-    return (r * PR + ((c >> 3) ^ (r & (PR - 1)))) * 8 + (c & 7);
+    return (r * PR + ((c >> 3) ^ sw_key<D>(r))) * 8 + (c & 7);
 }
 
 template <int D>
-__device__ __forceinline__ bf16x8_t frag_rows_sw(const bf16 *X, int r0, int k0) {
-    const int l = lane_id();
+__device__ __forceinline__ bf16x8_t frag_rows_sw(const bf16 *X, int r0, int k0, int l = lane_id()) {
     return *(const bf16x8_t *)(X + sw_off<D>(r0 + (l & 31), k0 + (l >> 5) * 8));
 }
 
 template <int D, bool PERM>
-__device__ __forceinline__ bf16x8_t frag_cols_sw(const bf16 *X, int k0, int n0) {
-    const int l = lane_id(), i = l & 15, h = l >> 4, g = h >> 1;
+__device__ __forceinline__ bf16x8_t frag_cols_sw(const bf16 *X, int k0, int n0, int l = lane_id()) {
+    const int i = l & 15, h = l >> 4, g = h >> 1;
     const int col = n0 + (h & 1) * 16 + 4 * (i & 3);
     const int ra = k0 + (PERM ? 4 * g : 8 * g) + (i >> 2);
     const int rb = ra + (PERM ? 8 : 4);
@@ -1236,6 +1009,23 @@ __device__ __forceinline__ bf16x8_t frag_cols_sw(const bf16 *X, int k0, int n0) 
     const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(X + sw_off<D>(rb, col)));
     const v8s c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8_t, c);
+}
+
+// global -> LDS copy of 16 bytes per lane (lane l's bytes land at dst + 16*l).
+// Issued from inline assembly on purpose: the compiler then does not track the
+// copy as a pending LDS write, and so does not wait for it before LDS reads it
+// cannot prove disjoint (it cannot for the transpose reads).  The caller waits
+// (vmcnt) and synchronizes before reading the destination, like for any
+// asynchronous copy.  M0 holds the LDS address; the kernels that use this
+// leave M0 to these copies alone.
+__device__ __forceinline__ void dma16(const void *src, const bf16 *dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)dst);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is clobbered on purpose
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
 }
 
 // s_waitcnt: vmcnt(vm), no wait on the other counters.
@@ -1256,240 +1046,330 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int N> struct IC { static constexpr int value = N; };
 
+// ---------------------------------------------------------------------------
+// Segment sweep (bf16).  One workgroup per (segment, head, role) walks the
+// segment's chunks in sweep order (forward for O and dQ, backward for dV and
+// dK), carrying the d x d state in float32 accumulators spread over the waves
+// and a bf16 copy in LDS for the inter-chunk product:
+//   forward roles:  P <- lambda^Ct P + (Gam_t K_t)^T V_t   (LASP Eq. 10)
+//   backward roles: R <- lambda^Ct R + (Lam_t Q_t)^T dO_t  (LASP Eq. 20)
+// The state update reads the same token tiles as the intra-chunk product, so
+// no per-chunk state is ever written to memory.
+//
+// Roles.  O, dQ, dV and dK are one computation.  For the rows r of one chunk
+// (length Ct) and the state X carried into it ([dv][dk] in memory):
+//   Out[r] = sum_{c in causal range of r} lambda^|r-c| (A_r . B_c) Cv_c
+//            + lambda^e(r) A_r X
+//   0  O  : A=Q,  B=K,  Cv=V,  X=P,   c <= r, e = r+1        (LASP Eqs. 7, 9, 11)
+//   1  dQ : A=dO, B=V,  Cv=K,  X=P^T, c <= r, e = r+1        (LASP Eqs. 14-16)
+//   2  dV : A=K,  B=Q,  Cv=dO, X=R,   c >= r, e = Ct-1-r     (LASP Eqs. 21-22)
+//   3  dK : A=V,  B=dO, Cv=Q,  X=R^T, c >= r, e = Ct-1-r     (LASP Eqs. 17-19)
+// Roles 0 and 1 carry P forward, roles 2 and 3 carry R backward; the state
+// update takes its token rows from B (roles 0, 2) or from Cv (roles 1, 3).
+//
+// Work split.  Wave w owns one 32-row tile of every chunk (its A rows live in
+// registers, loaded one chunk ahead) and a fixed share of the 32x32 state
+// tiles.  The chunk's B and Cv rows are all resident in LDS, so the waves run
+// through the chunk's 32-token tiles without a barrier per tile.  The tiles
+// are taken in two groups, the outer ones ({0,1,6,7} of 8) and the inner ones,
+// which give every SIMD (two waves with row tiles s and 7-s) the same amount
+// of causal work in each group.  One barrier separates the groups: after it
+// the first group's LDS slots are refilled with the next chunk, and after the
+// chunk-start barrier the second group's.  The output is accumulated
+// transposed (features x rows), so each lane holds whole 4-feature pieces of
+// one row and stores them directly.
+// ---------------------------------------------------------------------------
+template <int C> struct SweepCfg {
+    static constexpr int NCT = C / 32;                 // token tiles per chunk
+    static constexpr int NW = NCT < 4 ? 4 : NCT;       // waves per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int NG = NCT / 2;                 // tiles per group
+    // waves w and w+4 share a SIMD; pair row tiles s and 7-s on SIMD s
+    __device__ static int tile(int w) {
+        return NCT == 8 ? (w < 4 ? w : 11 - w) : (w < NCT ? w : -1);
+    }
+    // k-th tile of group g: 8 tiles {0,1,6,7},{2,3,4,5}; 4 tiles {0,3},{1,2}; 2 tiles {0},{1}
+    __device__ static int group_tile(int g, int k) {
+        if (NCT == 2) return g;
+        constexpr int q = NCT / 4;
+        return g == 0 ? (k < q ? k : NCT - 2 * q + k) : q + k;
+    }
+};
+
 template <int D, int C>
-__global__ __launch_bounds__(ChunkCfg<C>::NT) void k_chunk_dma(Params p, int role0, int nroles) {
-    using Cfg = ChunkCfg<C>;
-    constexpr int NW = Cfg::NW, NT = Cfg::NT, NG = Cfg::NG;
-    constexpr int PR = D / 8;                 // 16-byte pieces per row
-    constexpr int PO = 32 + 8;                // pitch of the transposed output tile
-    constexpr int KS = D / 16, NDT = D / 32;
-    constexpr int TILE = 32 * D;              // elements of one 32-token tile
-    constexpr int NI_T = 2 * TILE / 512;      // wave copies per B+Cv tile pair (512 elem each)
-    constexpr int DPW = NI_T / NW;            // copies per wave per tile pair
-    static_assert(NI_T % NW == 0, "tile copies must split evenly over waves");
-    constexpr int NI_X = D * D / 512;         // wave copies of the state
-    constexpr int XPW = (NI_X + NW - 1) / NW;
-    constexpr int X_ELEMS = D * D > D * PO ? D * D : D * PO;
-    __shared__ __attribute__((aligned(16))) bf16 XS[X_ELEMS];
-    __shared__ __attribute__((aligned(16))) bf16 R0[2 * TILE];
-    __shared__ __attribute__((aligned(16))) bf16 R1[2 * TILE];
-    __shared__ __attribute__((aligned(16))) bf16 R2[2 * TILE];
+__global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p, int role0, int nroles) {
+    using Cfg = SweepCfg<C>;
+    constexpr int NCT = Cfg::NCT, NW = Cfg::NW, NG = Cfg::NG;
+    constexpr int PR = D / 8, KS = D / 16, NDT = D / 32;
+    constexpr int TILE = 32 * D;                       // elements of one 32-token operand tile
+    constexpr int CPT = TILE / 512;                    // wave copies per operand tile
+    constexpr int NIG = NG * 2 * CPT;                  // wave copies per group (B and Cv)
+    constexpr int CPW = (NIG + NW - 1) / NW;           // copies per wave per group (at most)
+    constexpr int NSTT = NDT * NDT;                    // 32x32 state tiles
+    constexpr int STW = (NSTT + NW - 1) / NW;
+    __shared__ __attribute__((aligned(16))) bf16 XS[D * D];
+    // B and Cv tiles of the two groups.  Two distinct arrays: the compiler
+    // then sees that copies in flight into one group's slots do not alias
+    // reads of the other's, and does not wait for them.
+    __shared__ __attribute__((aligned(16))) bf16 BG0[NG * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) bf16 BG1[NG * 2 * TILE];
 
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int role = role0 + lid % nroles;
-    int rest = lid / nroles;
-    const int grp = rest % NG;
-    rest /= NG;
-    const int h = rest % p.H, gc = rest / p.H;
+    const int rest = lid / nroles;
+    const int h = rest % p.H, gs = rest / p.H;
     Seq s;
-    int t;
-    if (!chunk_seq(p, gc, s, t)) return;
-    const int tok = t * p.C;
-    const int Ct = min(p.C, s.len - tok);
-    const int sl = t / p.G;
-    if (s.s0 + sl >= p.n_segs_ub) return;   // only with malformed cu_seqlens
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    const int nch = t1 - t0;
+    if (nch <= 0) return;
+    const bool rev = role >= 2;                // c >= r, chunks swept backwards
+    const bool xt = role & 1;                  // state operand read transposed
+    const bool u_is_b = !(role & 1);           // state rows from B (else from Cv)
     const float l2 = head_log2_decay(p, h);
     const bool decay = l2 != 0.f;
-    const int64_t rb = row_base(p, s, h) + tok;
-    const int64_t sidx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
-    const int64_t cidx = ((int64_t)(s.c0 + t) * p.H + h) * D * D;
-
-    const bool rev = role >= 2;                // contraction over c >= r
-    const bool xt = role & 1;                  // state read transposed
-    const bf16 *seg, *loc;
-    int soff;
-    if (!rev) {
-        soff = (t - sl * p.G) * p.C;
-        seg = (const bf16 *)p.Pseg + sidx;
-        loc = p.G > 1 ? (const bf16 *)p.Lc + cidx : nullptr;
-    } else {
-        const int seg_end = min((sl + 1) * p.G * p.C, s.len);
-        soff = seg_end - (tok + Ct);
-        seg = (const bf16 *)p.Rseg + sidx;
-        loc = p.G > 1 ? (const bf16 *)p.Rc + cidx : nullptr;
-    }
-    const bf16 *Qg = (const bf16 *)p.Q + rb * D, *Kg = (const bf16 *)p.K + rb * D;
-    const bf16 *Vg = (const bf16 *)p.V + rb * D;
-    const bf16 *Og = role ? (const bf16 *)p.dO + rb * D : nullptr;
+    const int64_t rbase = row_base(p, s, h);
+    const bf16 *Qg = (const bf16 *)p.Q + rbase * D, *Kg = (const bf16 *)p.K + rbase * D;
+    const bf16 *Vg = (const bf16 *)p.V + rbase * D;
+    const bf16 *Og = role ? (const bf16 *)p.dO + rbase * D : nullptr;
     const bf16 *A, *Bm, *Cv;
     bf16 *Out;
     switch (role) {
-    case 0: A = Qg; Bm = Kg; Cv = Vg; Out = (bf16 *)p.O + rb * D; break;
-    case 1: A = Og; Bm = Vg; Cv = Kg; Out = (bf16 *)p.dQ + rb * D; break;
-    case 2: A = Kg; Bm = Qg; Cv = Og; Out = (bf16 *)p.dV + rb * D; break;
-    default: A = Vg; Bm = Og; Cv = Qg; Out = (bf16 *)p.dK + rb * D; break;
+    case 0: A = Qg; Bm = Kg; Cv = Vg; Out = (bf16 *)p.O + rbase * D; break;
+    case 1: A = Og; Bm = Vg; Cv = Kg; Out = (bf16 *)p.dQ + rbase * D; break;
+    case 2: A = Kg; Bm = Qg; Cv = Og; Out = (bf16 *)p.dV + rbase * D; break;
+    default: A = Vg; Bm = Og; Cv = Qg; Out = (bf16 *)p.dK + rbase * D; break;
     }
+    const float *seg = (rev ? p.Rseg : p.Pseg) + ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
 
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-    const int rt = Cfg::tile(grp, w);
-    const bool live = rt * 32 < Ct;
-    const int nct = (Ct + 31) / 32;
-    int tmin = C, tmax = -1;
-    for (int ww = 0; ww < NW; ++ww) {
-        const int tt = Cfg::tile(grp, ww);
-        if (tt < nct) { tmin = min(tmin, tt); tmax = max(tmax, tt); }
-    }
-    if (tmax < 0) return;
-    const int c0 = rev ? tmin : 0, c1 = rev ? nct : tmax + 1;
+    const int w = wave_id(), l = lane_id();
+    const int rt = Cfg::tile(w);
+    // The lane index is made opaque at each use site so that lane-derived
+    // addresses are recomputed where they are used instead of being hoisted
+    // out of the loops, where they would pin many registers.
+    auto opaque_lane = [&]() {
+        int lz = l;
+        asm volatile("" : "+v"(lz));
+        return lz;
+    };
+    auto chunk_t = [&](int i) { return rev ? t1 - 1 - i : t0 + i; };
+    auto chunk_len = [&](int t) { return min(p.C, s.len - t * p.C); };
 
-    // copy token tile ct (B rows then Cv rows, swizzled) into buffer dst
-    auto dma_tile = [&](int ct, bf16 *dst) {
+    // group g of chunk i: 32-token tiles of B and Cv (swizzled rows) into their slots
+    auto dma_group = [&](int i, auto G) {
+        constexpr int g = decltype(G)::value;
+        bf16 *BG = g == 0 ? BG0 : BG1;
+        const int lz = opaque_lane();
+        const int t = chunk_t(i);
+        const int tok = t * p.C, Ct = chunk_len(t);
 #pragma unroll
-        for (int k = 0; k < DPW; ++k) {
-            const int j = w + k * NW;                       // wave copy index
-            const int half = j / (NI_T / 2);                // 0: B, 1: Cv
-            const int slot = (j % (NI_T / 2)) * 64 + l;
-            const int r = slot / PR, pc = (slot % PR) ^ (r & (PR - 1));
-            const int row = min(ct * 32 + r, Ct - 1);       // rows past Ct: any valid row
-            const bf16 *src = (half ? Cv : Bm) + (int64_t)row * D + pc * 8;
-            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + j * 512), 16, 0, 0);
+        for (int k = 0; k < CPW; ++k) {
+            const int jj = w + k * NW;
+            if (NIG % NW == 0 || jj < NIG) {
+                const int ti = jj / (2 * CPT), half = (jj / CPT) & 1, pc0 = jj % CPT;
+                const int ct = Cfg::group_tile(g, ti);
+                const int slot = pc0 * 64 + lz;
+                const int r = slot / PR, pc = (slot % PR) ^ sw_key<D>(r);
+                const int row = tok + min(ct * 32 + r, Ct - 1);   // rows past Ct: a valid row
+                const bf16 *src = (half ? Cv : Bm) + (int64_t)row * D + pc * 8;
+                dma16(src, BG + ti * 2 * TILE + half * TILE + pc0 * 512);
+            }
+        }
+    };
+    // chunk i's A rows of this wave's row tile, as MFMA operand fragments
+    auto load_a = [&](int i, bf16x8_t *dst) {
+        if (rt >= 0) {
+            const int lz = opaque_lane();
+            const int t = chunk_t(i);
+            const int row = t * p.C + min(rt * 32 + (lz & 31), chunk_len(t) - 1);
+            const bf16 *src = A + (int64_t)row * D + (lz >> 5) * 8;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) dst[ks] = *(const bf16x8_t *)(src + ks * 16);
         }
     };
 
-    // ---- loads issued up front ----
-    bf16x8_t af[KS];
-    {
-        const int row = rt * 32 + (l & 31);
+    // ---- prologue: first chunk's A rows and first group, incoming state ----
+    bf16x8_t af[KS], afn[KS];
+    dma_group(0, IC<0>());
+    load_a(0, afn);
+
+    f32x16 sacc[STW];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (row < Ct) v = *(const uint4 *)(A + (int64_t)row * D + ks * 16 + (l >> 5) * 8);
-            af[ks] = __builtin_bit_cast(bf16x8_t, v);
-        }
-    }
-    constexpr int SPT = (D * D / 8 + NT - 1) / NT;          // state pieces per thread
-    uint4 sg[SPT];
+    for (int k = 0; k < STW; ++k) {
+        const int tl = w + k * NW;
+        zero(sacc[k]);
+        if (tl < NSTT) {
+            const int mi = tl / NDT, ni = tl % NDT, lc = l & 31, lg = l >> 5;
 #pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-        const int q = tid + k * NT;
-        sg[k] = q < D * D / 8 ? *(const uint4 *)(seg + q * 8) : make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (loc) {
-#pragma unroll
-        for (int k = 0; k < XPW; ++k) {
-            const int j = w + k * NW;
-            if (j < NI_X) {
-                const int slot = j * 64 + l;
-                const int r = slot / PR, pc = (slot % PR) ^ (r & (PR - 1));
-                __builtin_amdgcn_global_load_lds((const void *)(loc + r * D + pc * 8),
-                                                 (lds_void *)(XS + j * 512), 16, 0, 0);
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = *(const float4 *)(seg + (int64_t)(ni * 32 + lc) * D + mi * 32 + q * 8 + lg * 4);
+                sacc[k][q * 4 + 0] = v.x; sacc[k][q * 4 + 1] = v.y;
+                sacc[k][q * 4 + 2] = v.z; sacc[k][q * 4 + 3] = v.w;
             }
         }
     }
-    dma_tile(c0, R0);
-    if (c0 + 1 < c1) dma_tile(c0 + 1, R1);
-
-    // ---- state X = lambda^soff seg + loc (in XS, swizzled) ----
-    if (c0 + 1 < c1) LASP_WAIT_VM(2 * DPW);
-    else LASP_WAIT_VM(DPW);
-    lds_barrier();
-    {
-        const float sc = dpow(l2, (float)soff);
+    auto write_state = [&]() {   // XS[col feature][row feature] = bf16(state)
+        const int lz = opaque_lane();
+        const int lc = lz & 31, lg = lz >> 5;
 #pragma unroll
-        for (int k = 0; k < SPT; ++k) {
-            const int q = tid + k * NT;
-            if (q < D * D / 8) {
-                const int r = q / PR, pc = q % PR;
-                bf16 *dst = XS + (r * PR + (pc ^ (r & (PR - 1)))) * 8;
-                float sf[8], lf[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                load16((const bf16 *)&sg[k], sf);
-                if (loc) load16(dst, lf);
-                *(bf16x8_t *)dst = pack8(sc * sf[0] + lf[0], sc * sf[1] + lf[1], sc * sf[2] + lf[2],
-                                         sc * sf[3] + lf[3], sc * sf[4] + lf[4], sc * sf[5] + lf[5],
-                                         sc * sf[6] + lf[6], sc * sf[7] + lf[7]);
+        for (int k = 0; k < STW; ++k) {
+            const int tl = w + k * NW;
+            if (tl < NSTT) {
+                const int mi = tl / NDT, ni = tl % NDT;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    store4(XS + sw_off<D>(ni * 32 + lc, mi * 32 + q * 8 + lg * 4), sacc[k][q * 4 + 0],
+                           sacc[k][q * 4 + 1], sacc[k][q * 4 + 2], sacc[k][q * 4 + 3]);
             }
         }
-    }
-    lds_barrier();
+    };
+    write_state();
 
-    // ---- inter-chunk term ----
+    // acc[nt]: output tile transposed, [feature nt*32 + crow(e)][row rt*32 + lane%32]
     f32x16 acc[NDT];
-#pragma unroll
-    for (int nt = 0; nt < NDT; ++nt) {
-        zero(acc[nt]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8_t xf = xt ? frag_cols_sw<D, false>(XS, ks * 16, nt * 32)
-                                   : frag_rows_sw<D>(XS, nt * 32, ks * 16);
-            mma(acc[nt], af[ks], xf);
-        }
-    }
-    if (decay) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = rt * 32 + crow(r);
-            const float sc = dpow(l2, (float)(rev ? (Ct - 1 - row) : (row + 1)));
-#pragma unroll
-            for (int nt = 0; nt < NDT; ++nt) acc[nt][r] *= sc;
-        }
-    }
 
-    // ---- intra-chunk term: ring of three buffers ----
-    auto compute = [&](int ct, const bf16 *T) {
-        if (!live || (rev ? (ct < rt) : (ct > rt))) return;
-        const bf16 *Bt = T, *Vt = T + TILE;
-        f32x16 st;
+    // pair product of row tile rt with column tile ct (both in range, causal),
+    // whose B and Cv rows are at Bt
+    auto pair = [&](const bf16 *Bt, int ct, int Ct) {
+        const int lz = opaque_lane();
+        const int lc = lz & 31;
+        const bf16 *Vt = Bt + TILE;
+        f32x16 st;                     // S^T: [column token ct*32 + crow(e)][row rt*32 + lane%32]
         zero(st);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mma(st, frag_rows_sw<D>(Bt, 0, ks * 16), af[ks]);
+        for (int ks = 0; ks < KS; ++ks) mma(st, frag_rows_sw<D>(Bt, 0, ks * 16, lz), af[ks]);
         if (ct == rt || decay || (ct + 1) * 32 > Ct) {
-            const int r = rt * 32 + (l & 31);
+            const int r = rt * 32 + lc;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int c = ct * 32 + crow(i);
+            for (int e = 0; e < 16; ++e) {
+                const int c = ct * 32 + crow(e, lz);
                 const int dist = rev ? (c - r) : (r - c);
-                const bool ok = dist >= 0 && c < Ct && r < Ct;
-                st[i] = ok ? (decay ? st[i] * dpow(l2, (float)dist) : st[i]) : 0.f;
+                const bool ok = dist >= 0 && c < Ct;
+                st[e] = ok ? (decay ? st[e] * dpow(l2, (float)dist) : st[e]) : 0.f;
             }
         }
+        // as an operand, S^T's k order is permuted; the Cv fragment follows it
         const bf16x8_t s0 = pack8(st[0], st[1], st[2], st[3], st[4], st[5], st[6], st[7]);
         const bf16x8_t s1 = pack8(st[8], st[9], st[10], st[11], st[12], st[13], st[14], st[15]);
 #pragma unroll
         for (int nt = 0; nt < NDT; ++nt) {
-            mma(acc[nt], s0, frag_cols_sw<D, true>(Vt, 0, nt * 32));
-            mma(acc[nt], s1, frag_cols_sw<D, true>(Vt, 16, nt * 32));
+            mma(acc[nt], frag_cols_sw<D, true>(Vt, 0, nt * 32, lz), s0);
+            mma(acc[nt], frag_cols_sw<D, true>(Vt, 16, nt * 32, lz), s1);
         }
     };
-    auto iter = [&](auto bufc, int ct) {
-        constexpr int b = decltype(bufc)::value;
-        bf16 *cur = b == 0 ? R0 : (b == 1 ? R1 : R2);
-        bf16 *nxt2 = b == 0 ? R2 : (b == 1 ? R0 : R1);     // buffer of tile ct+2
-        if (ct + 1 < c1) LASP_WAIT_VM(DPW);
-        else LASP_WAIT_VM(0);
-        lds_barrier();
-        if (ct + 2 < c1) dma_tile(ct + 2, nxt2);
-        compute(ct, cur);
+    // state += (scaled U)^T W over the tokens of column tile ct
+    auto state_update = [&](const bf16 *Bt, int ct, int Ct) {
+        const int lz = opaque_lane();
+        const int lg = lz >> 5;
+        // (offsets, not a choice between pointers: the compiler keeps track
+        // of which LDS array a pointer reads only through offsets)
+        const bf16 *Ut = Bt + (u_is_b ? 0 : TILE), *Wt = Bt + (u_is_b ? TILE : 0);
+        const bool scale = decay || (ct + 1) * 32 > Ct;
+#pragma unroll
+        for (int k = 0; k < STW; ++k) {
+            const int tl = w + k * NW;
+            if (tl < NSTT) {
+                const int mi = tl / NDT, ni = tl % NDT;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8_t ua = frag_cols_sw<D, false>(Ut, kk * 16, mi * 32, lz);
+                    if (scale) {
+                        float f[8];
+                        load16((const bf16 *)&ua, f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int tk = ct * 32 + kk * 16 + lg * 8 + e;
+                            f[e] *= tk >= Ct ? 0.f : dpow(l2, (float)(rev ? tk + 1 : Ct - 1 - tk));
+                        }
+                        ua = pack8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+                    }
+                    mma(sacc[k], ua, frag_cols_sw<D, false>(Wt, kk * 16, ni * 32, lz));
+                }
+            }
+        }
     };
-    for (int ct = c0; ct < c1; ct += 3) {
-        iter(IC<0>(), ct);
-        if (ct + 1 < c1) iter(IC<1>(), ct + 1);
-        if (ct + 2 < c1) iter(IC<2>(), ct + 2);
-    }
+    // one group of column tiles
+    auto run_group = [&](auto G, int Ct, bool upd) {
+        constexpr int g = decltype(G)::value;
+        const bf16 *BG = g == 0 ? BG0 : BG1;
+#pragma unroll 1
+        for (int k = 0; k < NG; ++k) {
+            const int ct = Cfg::group_tile(g, k);
+            if (ct * 32 >= Ct) continue;
+            const bf16 *Bt = BG + k * 2 * TILE;
+            if (rt >= 0 && rt * 32 < Ct && (ct == rt || (rev ? ct > rt : ct < rt))) pair(Bt, ct, Ct);
+            if (upd) state_update(Bt, ct, Ct);
+        }
+    };
 
-    // ---- store: accumulators -> LDS (transposed) -> 16-byte rows ----
-    lds_barrier();
-    bf16 *O_s = w == 0 ? R0 : (w == 1 ? R1 : (w == 2 ? R2 : XS));
-    {
-        const int col = l & 31, g = l >> 5;
+#pragma unroll 1
+    for (int i = 0; i < nch; ++i) {
+        const int t = chunk_t(i), Ct = chunk_len(t);
+        const bool upd = i + 1 < nch;  // the state after the segment's last chunk is not needed
+        // chunk start: this chunk's first group and A rows have landed (nothing
+        // newer is outstanding), every wave has published the state into XS
+        LASP_WAIT_VM(0);
+        lds_barrier();
+        dma_group(i, IC<1>());         // slots of the second group are free now
 #pragma unroll
-        for (int nt = 0; nt < NDT; ++nt)
+        for (int ks = 0; ks < KS; ++ks) af[ks] = afn[ks];
+        // inter-chunk term: acc = (A X)^T, rows scaled by lambda^e(r)
+        {
+            const int lz = opaque_lane();
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                store4(O_s + (nt * 32 + col) * PO + q * 8 + g * 4, acc[nt][q * 4 + 0],
-                       acc[nt][q * 4 + 1], acc[nt][q * 4 + 2], acc[nt][q * 4 + 3]);
-    }
-    lds_barrier();
-    if (live) {
-        const int row = rt * 32 + (l & 31);
+            for (int nt = 0; nt < NDT; ++nt) {
+                zero(acc[nt]);
+                if (rt >= 0 && rt * 32 < Ct) {
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j) {
-            const bf16x8_t v = frag_cols<false>(O_s, PO, j * 16, 0);
-            if (row < Ct)
-                *(bf16x8_t *)(Out + (int64_t)row * D + j * 16 + (l >> 5) * 8) = v;
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8_t xf = xt ? frag_cols_sw<D, false>(XS, ks * 16, nt * 32, lz)
+                                               : frag_rows_sw<D>(XS, nt * 32, ks * 16, lz);
+                        mma(acc[nt], xf, af[ks]);
+                    }
+                }
+            }
+            if (decay && rt >= 0) {
+                const int r = rt * 32 + (lz & 31);
+                const float sc = dpow(l2, (float)(rev ? (Ct - 1 - r) : (r + 1)));
+#pragma unroll
+                for (int nt = 0; nt < NDT; ++nt) acc[nt] *= sc;
+            }
         }
+        if (upd) {
+            const float dc = dpow(l2, (float)Ct);
+#pragma unroll
+            for (int k = 0; k < STW; ++k) sacc[k] *= dc;
+        }
+        run_group(IC<0>(), Ct, upd);
+        // mid-chunk: the second group has landed; the first group's slots and
+        // XS are no longer read by any wave
+        LASP_WAIT_VM(0);
+        lds_barrier();
+        if (i + 1 < nch) {
+            dma_group(i + 1, IC<0>());
+            load_a(i + 1, afn);
+        }
+        run_group(IC<1>(), Ct, upd);
+        // rows out: lane holds row rt*32 + lane%32, features nt*32 + 8j + 4*(lane/32) + [0,4)
+        if (rt >= 0 && rt * 32 < Ct) {
+            const int lz = opaque_lane();
+            const int row = rt * 32 + (lz & 31);
+            bf16 *dst = Out + ((int64_t)t * p.C + row) * D + (lz >> 5) * 4;
+            if (row < Ct) {
+#pragma unroll
+                for (int nt = 0; nt < NDT; ++nt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        store4(dst + nt * 32 + j * 8, acc[nt][4 * j + 0], acc[nt][4 * j + 1],
+                               acc[nt][4 * j + 2], acc[nt][4 * j + 3]);
+            }
+        }
+        if (upd) write_state();
     }
 }
 
+// ---------------------------------------------------------------------------
 // Local chunk states (bf16): one workgroup per (segment, head).
 //   which = 0: L_t = state entering chunk t from the segment start (chunks in
 //              order), L += (Gam_t K_t)^T V_t, stored to Lc, total to Z;
@@ -1515,7 +1395,7 @@ __global__ __launch_bounds__(256) void k_local_bf16(Params p, int which) {
     const bf16 *Bg = (const bf16 *)(which ? p.dO : p.V) + rb * D;
     bf16 *Lout = (bf16 *)(which ? p.Rc : p.Lc);
     float *Tot = which ? p.W : p.Z;
-    const bool store_local = p.G > 1;
+    const bool store_local = p.G > 1 && Lout != nullptr;
     const int tid = threadIdx.x;
 
     f32x16 acc[TL::PER_WAVE];
@@ -1658,26 +1538,19 @@ static hipError_t bwd_impl(const Params &p, hipStream_t st, hipEvent_t *ev) {
     return hipGetLastError();
 }
 
-// bf16: transpose-read local-state kernel and the shared chunk kernel.
+// bf16: segment totals (transpose-read local kernel), segment scan, sweep.
 template <int D, int C>
-static void chunk_launch(const Params &p, int role0, int nroles, hipStream_t st) {
-#ifdef LASP_CHUNK_REGISTER_STAGING
-    hipLaunchKernelGGL((k_chunk_bf16<D, C>),
-                       dim3(round8(p.n_chunks_ub * p.H * nroles * ChunkCfg<C>::NG)),
-                       dim3(ChunkCfg<C>::NT), 0, st, p, role0, nroles);
-#else
-    hipLaunchKernelGGL((k_chunk_dma<D, C>),
-                       dim3(round8(p.n_chunks_ub * p.H * nroles * ChunkCfg<C>::NG)),
-                       dim3(ChunkCfg<C>::NT), 0, st, p, role0, nroles);
-#endif
+static void sweep_launch(const Params &p, int role0, int nroles, hipStream_t st) {
+    hipLaunchKernelGGL((k_sweep_bf16<D, C>), dim3(round8(p.n_segs_ub * p.H * nroles)),
+                       dim3(SweepCfg<C>::NT), 0, st, p, role0, nroles);
 }
 
 template <int D>
-static void chunk_dispatch(const Params &p, int role0, int nroles, hipStream_t st) {
+static void sweep_dispatch(const Params &p, int role0, int nroles, hipStream_t st) {
     switch (p.C) {
-    case 64: chunk_launch<D, 64>(p, role0, nroles, st); break;
-    case 128: chunk_launch<D, 128>(p, role0, nroles, st); break;
-    default: chunk_launch<D, 256>(p, role0, nroles, st); break;
+    case 64: sweep_launch<D, 64>(p, role0, nroles, st); break;
+    case 128: sweep_launch<D, 128>(p, role0, nroles, st); break;
+    default: sweep_launch<D, 256>(p, role0, nroles, st); break;
     }
 }
 
@@ -1688,9 +1561,9 @@ static hipError_t fwd_bf16(const Params &p, bool with_output, hipStream_t st, hi
     hipLaunchKernelGGL((k_local_bf16<D>), dim3(p.n_segs_ub * p.H), dim3(256), 0, st, p, 0);
     rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_fwd_segscan<D, bf16>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    hipLaunchKernelGGL((k_fwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
     rec(ev, 2, st);
-    if (with_output) chunk_dispatch<D>(p, 0, 1, st);
+    if (with_output) sweep_dispatch<D>(p, 0, 1, st);
     rec(ev, 3, st);
     return hipGetLastError();
 }
@@ -1702,9 +1575,9 @@ static hipError_t bwd_bf16(const Params &p, hipStream_t st, hipEvent_t *ev) {
     hipLaunchKernelGGL((k_local_bf16<D>), dim3(p.n_segs_ub * p.H), dim3(256), 0, st, p, 1);
     rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_bwd_segscan<D, bf16>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    hipLaunchKernelGGL((k_bwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
     rec(ev, 2, st);
-    chunk_dispatch<D>(p, 1, 3, st);   // dQ, dV, dK of a chunk are neighbours in launch order
+    sweep_dispatch<D>(p, 1, 3, st);   // dQ, dV, dK of a segment are neighbours in launch order
     rec(ev, 3, st);
     return hipGetLastError();
 }

@@ -125,15 +125,18 @@ def test_bwd_rejects_bad_arguments(L):
 
 
 def test_sizes_follow_the_shape(L):
-    # state cache = per-chunk local states (elem) + per-segment f32 states
+    # bf16: the state cache holds one float32 state per (segment, head); the
+    # per-chunk states are recomputed inside the segment sweep
     c3 = Shape(1, 32, 131072, 128, 256, 0)
     n = L.lasp_state_cache_bytes(ctypes.byref(c3), 1)
     chunks = 131072 // 256
-    assert n >= chunks * 32 * 128 * 128 * 2
-    assert n <= chunks * 32 * 128 * 128 * 2 * 1.5
+    assert 32 * 128 * 128 * 4 <= n <= chunks * 32 * 128 * 128 * 4 // 2
+    # float32: per-chunk local states (float32) + per-segment states
+    n32 = L.lasp_state_cache_bytes(ctypes.byref(c3), 0)
+    assert chunks * 32 * 128 * 128 * 4 <= n32 <= chunks * 32 * 128 * 128 * 4 * 1.5
     # packed batch bounds cover any split of N into nseq sequences
     pk = Shape(1, 8, 5000, 64, 128, 7)
-    assert L.lasp_state_cache_bytes(ctypes.byref(pk), 1) >= (5000 // 128 + 7) * 8 * 64 * 64 * 2
+    assert L.lasp_state_cache_bytes(ctypes.byref(pk), 0) >= (5000 // 128 + 7) * 8 * 64 * 64 * 4
     # invalid shapes report 0
     assert L.lasp_state_cache_bytes(ctypes.byref(Shape(1, 1, 1, 33, 64, 0)), 1) == 0
     assert L.lasp_fwd_workspace_bytes(None, 1, 0) == 0
