@@ -994,21 +994,59 @@ __device__ __forceinline__ int sw_off(int r, int c) {
     return (r * PR + ((c >> 3) ^ sw_key<D>(r))) * 8 + (c & 7);
 }
 
+// Operand fragments from swizzled tiles (the layout of frag_cols above, with
+// sw_off placement).  The lane-dependent part of every fragment address is a
+// per-lane byte offset computed once (FragOffs); a fragment address is then
+// that offset XOR a wave-uniform term, plus a wave-uniform base: one VALU
+// operation.  This holds for tiles whose first row is a multiple of 16: the
+// XOR only touches the piece bits of the offset.
+//   frag_rows: rows r0 + lane%32, k = k0 + (lane/32)*8 + [0, 8)   (k0 % 16 == 0)
+//   frag_cols: operand row n0 + lane%32 of a tile stored [k][n]      (n0 % 32 == 0)
+template <int D> struct FragOffs {
+    uint32_t rows;          // frag_rows: XOR 2*k0, add 2*r0*D
+    uint32_t cols[2][2];    // frag_cols [PERM][first/second read]: XOR 2*n0, add 2*k0*D
+};
+
 template <int D>
-__device__ __forceinline__ bf16x8_t frag_rows_sw(const bf16 *X, int r0, int k0, int l = lane_id()) {
-    return *(const bf16x8_t *)(X + sw_off<D>(r0 + (l & 31), k0 + (l >> 5) * 8));
+__device__ __forceinline__ FragOffs<D> frag_offs(int l) {
+    FragOffs<D> o;
+    o.rows = 2u * sw_off<D>(l & 31, (l >> 5) * 8);
+    const int i = l & 15, h = l >> 4, g = h >> 1;
+    const int col = (h & 1) * 16 + 4 * (i & 3);
+#pragma unroll
+    for (int perm = 0; perm < 2; ++perm) {
+        const int ra = (perm ? 4 * g : 8 * g) + (i >> 2);
+        o.cols[perm][0] = 2u * sw_off<D>(ra, col);
+        o.cols[perm][1] = 2u * sw_off<D>(ra + (perm ? 8 : 4), col);
+    }
+    return o;
+}
+
+// A copy of o that the compiler cannot see through: address terms derived from
+// it are then computed where they are used rather than hoisted out of loops
+// into registers of their own.
+template <int D>
+__device__ __forceinline__ FragOffs<D> opaque(FragOffs<D> o) {
+    asm volatile("" : "+v"(o.rows), "+v"(o.cols[0][0]), "+v"(o.cols[0][1]), "+v"(o.cols[1][0]),
+                 "+v"(o.cols[1][1]));
+    return o;
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t frag_rows_sw(const bf16 *X, const FragOffs<D> &o, int r0, int k0) {
+    const char *b = (const char *)X + 2 * r0 * D;
+    return *(const bf16x8_t *)(b + (o.rows ^ (uint32_t)(2 * k0)));
 }
 
 template <int D, bool PERM>
-__device__ __forceinline__ bf16x8_t frag_cols_sw(const bf16 *X, int k0, int n0, int l = lane_id()) {
-    const int i = l & 15, h = l >> 4, g = h >> 1;
-    const int col = n0 + (h & 1) * 16 + 4 * (i & 3);
-    const int ra = k0 + (PERM ? 4 * g : 8 * g) + (i >> 2);
-    const int rb = ra + (PERM ? 8 : 4);
-    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(X + sw_off<D>(ra, col)));
-    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(X + sw_off<D>(rb, col)));
-    const v8s c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8_t, c);
+__device__ __forceinline__ bf16x8_t frag_cols_sw(const bf16 *X, const FragOffs<D> &o, int k0, int n0) {
+    const char *b = (const char *)X + 2 * k0 * D;
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s *)(b + (o.cols[PERM][0] ^ (uint32_t)(2 * n0))));
+    const v4s c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s *)(b + (o.cols[PERM][1] ^ (uint32_t)(2 * n0))));
+    const v8s r = __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, r);
 }
 
 // global -> LDS copy of 16 bytes per lane (lane l's bytes land at dst + 16*l).
@@ -1148,16 +1186,17 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p, int ro
     // The lane index is made opaque at each use site so that lane-derived
     // addresses are recomputed where they are used instead of being hoisted
     // out of the loops, where they would pin many registers.
-    auto opaque_lane = [&]() {
+    auto opaque_lane = [&]() __attribute__((always_inline)) {
         int lz = l;
         asm volatile("" : "+v"(lz));
         return lz;
     };
-    auto chunk_t = [&](int i) { return rev ? t1 - 1 - i : t0 + i; };
-    auto chunk_len = [&](int t) { return min(p.C, s.len - t * p.C); };
+    const FragOffs<D> fo0 = frag_offs<D>(l);
+    auto chunk_t = [&](int i) __attribute__((always_inline)) { return rev ? t1 - 1 - i : t0 + i; };
+    auto chunk_len = [&](int t) __attribute__((always_inline)) { return min(p.C, s.len - t * p.C); };
 
     // group g of chunk i: 32-token tiles of B and Cv (swizzled rows) into their slots
-    auto dma_group = [&](int i, auto G) {
+    auto dma_group = [&](int i, auto G) __attribute__((always_inline)) {
         constexpr int g = decltype(G)::value;
         bf16 *BG = g == 0 ? BG0 : BG1;
         const int lz = opaque_lane();
@@ -1178,7 +1217,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p, int ro
         }
     };
     // chunk i's A rows of this wave's row tile, as MFMA operand fragments
-    auto load_a = [&](int i, bf16x8_t *dst) {
+    auto load_a = [&](int i, bf16x8_t *dst) __attribute__((always_inline)) {
         if (rt >= 0) {
             const int lz = opaque_lane();
             const int t = chunk_t(i);
@@ -1190,9 +1229,9 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p, int ro
     };
 
     // ---- prologue: first chunk's A rows and first group, incoming state ----
-    bf16x8_t af[KS], afn[KS];
+    bf16x8_t af[KS];
     dma_group(0, IC<0>());
-    load_a(0, afn);
+    load_a(0, af);
 
     f32x16 sacc[STW];
 #pragma unroll
@@ -1209,7 +1248,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p, int ro
             }
         }
     }
-    auto write_state = [&]() {   // XS[col feature][row feature] = bf16(state)
+    auto write_state = [&]() __attribute__((always_inline)) {   // XS[col feature][row feature] = bf16(state)
         const int lz = opaque_lane();
         const int lc = lz & 31, lg = lz >> 5;
 #pragma unroll
@@ -1229,41 +1268,54 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p, int ro
     // acc[nt]: output tile transposed, [feature nt*32 + crow(e)][row rt*32 + lane%32]
     f32x16 acc[NDT];
 
-    // pair product of row tile rt with column tile ct (both in range, causal),
-    // whose B and Cv rows are at Bt
-    auto pair = [&](const bf16 *Bt, int ct, int Ct) {
+    // pair products of row tile rt with NP column tiles ct[] (in range,
+    // causal) whose B and Cv rows are at Bt[]; the NP score tiles are
+    // independent MFMA chains until they meet in acc
+    auto pair = [&](auto NPC, const bf16 *const *Bt, const int *ct, int Ct) __attribute__((always_inline)) {
+        constexpr int NP = decltype(NPC)::value;
+        const FragOffs<D> fo = opaque(fo0);
         const int lz = opaque_lane();
         const int lc = lz & 31;
-        const bf16 *Vt = Bt + TILE;
-        f32x16 st;                     // S^T: [column token ct*32 + crow(e)][row rt*32 + lane%32]
-        zero(st);
+        f32x16 st[NP];                 // S^T: [column token ct*32 + crow(e)][row rt*32 + lane%32]
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mma(st, frag_rows_sw<D>(Bt, 0, ks * 16, lz), af[ks]);
-        if (ct == rt || decay || (ct + 1) * 32 > Ct) {
-            const int r = rt * 32 + lc;
+        for (int u = 0; u < NP; ++u) zero(st[u]);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int c = ct * 32 + crow(e, lz);
-                const int dist = rev ? (c - r) : (r - c);
-                const bool ok = dist >= 0 && c < Ct;
-                st[e] = ok ? (decay ? st[e] * dpow(l2, (float)dist) : st[e]) : 0.f;
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int u = 0; u < NP; ++u) mma(st[u], frag_rows_sw<D>(Bt[u], fo, 0, ks * 16), af[ks]);
+        bf16x8_t s0[NP], s1[NP];
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            if (ct[u] == rt || decay || (ct[u] + 1) * 32 > Ct) {
+                const int r = rt * 32 + lc;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int c = ct[u] * 32 + crow(e, lz);
+                    const int dist = rev ? (c - r) : (r - c);
+                    const float f = decay ? dpow(l2, (float)max(dist, 0)) : 1.f;
+                    st[u][e] = (dist >= 0 && c < Ct) ? st[u][e] * f : 0.f;
+                }
             }
+            // as an operand, S^T's k order is permuted; the Cv fragment follows it
+            s0[u] = pack8(st[u][0], st[u][1], st[u][2], st[u][3], st[u][4], st[u][5], st[u][6], st[u][7]);
+            s1[u] = pack8(st[u][8], st[u][9], st[u][10], st[u][11], st[u][12], st[u][13], st[u][14],
+                          st[u][15]);
         }
-        // as an operand, S^T's k order is permuted; the Cv fragment follows it
-        const bf16x8_t s0 = pack8(st[0], st[1], st[2], st[3], st[4], st[5], st[6], st[7]);
-        const bf16x8_t s1 = pack8(st[8], st[9], st[10], st[11], st[12], st[13], st[14], st[15]);
 #pragma unroll
         for (int nt = 0; nt < NDT; ++nt) {
-            mma(acc[nt], frag_cols_sw<D, true>(Vt, 0, nt * 32, lz), s0);
-            mma(acc[nt], frag_cols_sw<D, true>(Vt, 16, nt * 32, lz), s1);
+#pragma unroll
+            for (int u = 0; u < NP; ++u) {
+                const bf16 *Vt = Bt[u] + TILE;
+                mma(acc[nt], frag_cols_sw<D, true>(Vt, fo, 0, nt * 32), s0[u]);
+                mma(acc[nt], frag_cols_sw<D, true>(Vt, fo, 16, nt * 32), s1[u]);
+            }
         }
     };
     // state += (scaled U)^T W over the tokens of column tile ct
-    auto state_update = [&](const bf16 *Bt, int ct, int Ct) {
+    auto state_update = [&](const bf16 *Bt, int ct, int Ct) __attribute__((always_inline)) {
+        const FragOffs<D> fo = opaque(fo0);
         const int lz = opaque_lane();
         const int lg = lz >> 5;
-        // (offsets, not a choice between pointers: the compiler keeps track
-        // of which LDS array a pointer reads only through offsets)
         const bf16 *Ut = Bt + (u_is_b ? 0 : TILE), *Wt = Bt + (u_is_b ? TILE : 0);
         const bool scale = decay || (ct + 1) * 32 > Ct;
 #pragma unroll
@@ -1273,33 +1325,60 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p, int ro
                 const int mi = tl / NDT, ni = tl % NDT;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    bf16x8_t ua = frag_cols_sw<D, false>(Ut, kk * 16, mi * 32, lz);
+                    bf16x8_t ua = frag_cols_sw<D, false>(Ut, fo, kk * 16, mi * 32);
                     if (scale) {
                         float f[8];
                         load16((const bf16 *)&ua, f);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int tk = ct * 32 + kk * 16 + lg * 8 + e;
-                            f[e] *= tk >= Ct ? 0.f : dpow(l2, (float)(rev ? tk + 1 : Ct - 1 - tk));
+                            const float sc = dpow(l2, (float)max(rev ? tk + 1 : Ct - 1 - tk, 0));
+                            f[e] = tk < Ct ? f[e] * sc : 0.f;
                         }
                         ua = pack8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
                     }
-                    mma(sacc[k], ua, frag_cols_sw<D, false>(Wt, kk * 16, ni * 32, lz));
+                    mma(sacc[k], ua, frag_cols_sw<D, false>(Wt, fo, kk * 16, ni * 32));
                 }
             }
         }
     };
-    // one group of column tiles
-    auto run_group = [&](auto G, int Ct, bool upd) {
+    // one group of column tiles: pair products, then after_pairs(), then the
+    // state updates
+    auto run_group = [&](auto G, int Ct, bool upd, auto after_pairs) __attribute__((always_inline)) {
         constexpr int g = decltype(G)::value;
         const bf16 *BG = g == 0 ? BG0 : BG1;
+        if (rt >= 0 && rt * 32 < Ct) {
+            // the group's causal tiles, two at a time
+            int need = 0;
+#pragma unroll
+            for (int k = 0; k < NG; ++k) {
+                const int ct = Cfg::group_tile(g, k);
+                if (ct * 32 < Ct && (ct == rt || (rev ? ct > rt : ct < rt))) need |= 1 << k;
+            }
 #pragma unroll 1
-        for (int k = 0; k < NG; ++k) {
-            const int ct = Cfg::group_tile(g, k);
-            if (ct * 32 >= Ct) continue;
-            const bf16 *Bt = BG + k * 2 * TILE;
-            if (rt >= 0 && rt * 32 < Ct && (ct == rt || (rev ? ct > rt : ct < rt))) pair(Bt, ct, Ct);
-            if (upd) state_update(Bt, ct, Ct);
+            while (need) {
+                const int ka = __builtin_ctz(need);
+                need &= need - 1;
+                if (need) {
+                    const int kb = __builtin_ctz(need);
+                    need &= need - 1;
+                    const bf16 *bt[2] = {BG + ka * 2 * TILE, BG + kb * 2 * TILE};
+                    const int cts[2] = {Cfg::group_tile(g, ka), Cfg::group_tile(g, kb)};
+                    pair(IC<2>(), bt, cts, Ct);
+                } else {
+                    const bf16 *bt[1] = {BG + ka * 2 * TILE};
+                    const int cts[1] = {Cfg::group_tile(g, ka)};
+                    pair(IC<1>(), bt, cts, Ct);
+                }
+            }
+        }
+        after_pairs();
+        if (upd) {
+#pragma unroll 1
+            for (int k = 0; k < NG; ++k) {
+                const int ct = Cfg::group_tile(g, k);
+                if (ct * 32 < Ct) state_update(BG + k * 2 * TILE, ct, Ct);
+            }
         }
     };
 
@@ -1307,28 +1386,35 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p, int ro
     for (int i = 0; i < nch; ++i) {
         const int t = chunk_t(i), Ct = chunk_len(t);
         const bool upd = i + 1 < nch;  // the state after the segment's last chunk is not needed
-        // chunk start: this chunk's first group and A rows have landed (nothing
-        // newer is outstanding), every wave has published the state into XS
+        // chunk start: this chunk's first group and A rows have landed, every
+        // wave has published the state into XS
         LASP_WAIT_VM(0);
         lds_barrier();
         dma_group(i, IC<1>());         // slots of the second group are free now
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) af[ks] = afn[ks];
         // inter-chunk term: acc = (A X)^T, rows scaled by lambda^e(r)
         {
-            const int lz = opaque_lane();
 #pragma unroll
-            for (int nt = 0; nt < NDT; ++nt) {
-                zero(acc[nt]);
-                if (rt >= 0 && rt * 32 < Ct) {
+            for (int nt = 0; nt < NDT; ++nt) zero(acc[nt]);
+            auto inter = [&](auto XT) __attribute__((always_inline)) {
+                const FragOffs<D> fo = opaque(fo0);
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const bf16x8_t xf = xt ? frag_cols_sw<D, false>(XS, ks * 16, nt * 32, lz)
-                                               : frag_rows_sw<D>(XS, nt * 32, ks * 16, lz);
-                        mma(acc[nt], xf, af[ks]);
-                    }
+                for (int nt = 0; nt < NDT; ++nt) {
+                    bf16x8_t xf[KS];
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        xf[ks] = decltype(XT)::value ? frag_cols_sw<D, false>(XS, fo, ks * 16, nt * 32)
+                                                     : frag_rows_sw<D>(XS, fo, nt * 32, ks * 16);
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) mma(acc[nt], xf[ks], af[ks]);
                 }
+            };
+            if (rt >= 0 && rt * 32 < Ct) {
+                if (xt)
+                    inter(IC<1>());
+                else
+                    inter(IC<0>());
             }
+            const int lz = opaque_lane();
             if (decay && rt >= 0) {
                 const int r = rt * 32 + (lz & 31);
                 const float sc = dpow(l2, (float)(rev ? (Ct - 1 - r) : (r + 1)));
@@ -1341,16 +1427,17 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p, int ro
 #pragma unroll
             for (int k = 0; k < STW; ++k) sacc[k] *= dc;
         }
-        run_group(IC<0>(), Ct, upd);
+        run_group(IC<0>(), Ct, upd, [] {});
         // mid-chunk: the second group has landed; the first group's slots and
         // XS are no longer read by any wave
         LASP_WAIT_VM(0);
         lds_barrier();
-        if (i + 1 < nch) {
-            dma_group(i + 1, IC<0>());
-            load_a(i + 1, afn);
-        }
-        run_group(IC<1>(), Ct, upd);
+        if (i + 1 < nch) dma_group(i + 1, IC<0>());
+        // the next chunk's A rows go into af once this chunk's pair products
+        // have read it; the state updates and stores hide their latency
+        run_group(IC<1>(), Ct, upd, [&]() __attribute__((always_inline)) {
+            if (i + 1 < nch) load_a(i + 1, af);
+        });
         // rows out: lane holds row rt*32 + lane%32, features nt*32 + 8j + 4*(lane/32) + [0,4)
         if (rt >= 0 && rt * 32 < Ct) {
             const int lz = opaque_lane();
@@ -1601,3 +1688,4 @@ hipError_t launch_bwd(const Params &p, bool bf, hipStream_t st, hipEvent_t *ev) 
 }
 
 }  // namespace lasp
+
