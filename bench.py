@@ -57,20 +57,30 @@ def elapsed(L, a, b):
 
 def kernel_work(sh, local_b, seg_b):
     """Algorithmic HBM bytes and flops per launch of every kernel of a step.
-    U = token-heads; local_b / seg_b: bytes of the per-chunk (element type) and
-    per-segment (float32) state arrays, from the library's size queries."""
+
+    U = token-heads, e = element bytes; local_b / seg_b: bytes of the per-chunk
+    (element type, none for bf16) and per-segment (float32) state arrays, from
+    the library's size queries.  Bytes count every distinct array once:
+      local  : reads 2 token arrays (K,V resp. Q,dO), writes the local states
+      scan   : reads and writes the segment states, M_in/M_out (dM_out/dM_in)
+      out    : reads Q,K,V and the segment states, writes O
+      grads  : reads Q,K,V,dO and both segment-state arrays, writes dQ,dK,dV
+    Flops count the useful causal work per token-head and output role: the
+    intra-chunk products over c <= r (2d(C+1) on average: QK^T and SV), the
+    inter-chunk product A.X (2d^2) and the state update (2d^2)."""
     B, H, N, d, C = sh["B"], sh["H"], sh["N"], sh["d"], sh["chunk"]
     e = 2 if sh["dtype"] == "bf16" else 4
     U = B * H * N
     nS = sh["nseq"] or B
     st_io = nS * H * d * d * 4                    # M_in / M_out, dM_out / dM_in
+    role = U * (2 * d * (C + 1) + 4 * d * d)      # one output role (O, dQ, dK or dV)
     return {
         "fwd_local": (2 * U * d * e + local_b + seg_b, 2 * U * d * d),
         "fwd_scan": (2 * seg_b + 2 * st_io, seg_b // 2),
-        "fwd_out": (4 * U * d * e + local_b + seg_b, U * (4 * C * d + 2 * d * d)),
+        "fwd_out": (4 * U * d * e + local_b + seg_b, role),
         "bwd_local": (2 * U * d * e + local_b + seg_b, 2 * U * d * d),
         "bwd_scan": (2 * seg_b + 2 * st_io, seg_b // 2),
-        "bwd_grads": (7 * U * d * e + 2 * local_b + 2 * seg_b, U * (10 * C * d + 6 * d * d)),
+        "bwd_grads": (7 * U * d * e + 2 * local_b + 2 * seg_b, 3 * role),
     }
 
 
@@ -93,10 +103,10 @@ def measured_traffic(kernel):
 
 def cpu_baseline(inp, H, tokens):
     """The float64 C oracle over a bounded sample: the first `tokens` tokens of
-    `threads` heads (one head per host thread), forward + backward."""
+    every head (OpenMP over heads), forward + backward."""
     from oracle import crecurrent
     threads = crecurrent.threads()
-    nh = min(H, threads)
+    nh = H
     take = lambda x: x[:, :nh, :tokens].float().cpu().numpy()
     Q, K, V, dO = (take(inp[k]) for k in ("Q", "K", "V", "dO"))
     M_in = None if inp["M_in"] is None else inp["M_in"][:, :nh].double().cpu().numpy()
@@ -104,7 +114,14 @@ def cpu_baseline(inp, H, tokens):
     crecurrent.run(Q, K, V, dO, None, M_in, None)
     dt = time.perf_counter() - t0
     th = Q.shape[0] * nh * Q.shape[2]            # token-heads processed
-    return {"value": th / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    cpu = "?"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": th / H / dt, "unit": "tokens/s", "cores": min(threads, nh), "kind": "oracle",
+            "cpu": cpu,
             "sample": "%d of %d heads x first %d tokens, fwd+bwd float64 token recurrence "
                       "(C, OpenMP over heads), %.2f s; tokens/s counts all %d heads per token"
                       % (nh, H, Q.shape[2], dt, H)}
@@ -116,7 +133,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--cpu-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate "
@@ -182,10 +199,13 @@ def main():
 
     names = ["fwd_local", "fwd_scan", "fwd_out", "bwd_local", "bwd_scan", "bwd_grads"]
     kms = {k: 0.0 for k in names}
+    step_ms = []
     for i in range(a.warmup, n):
         for j in range(3):
             kms[names[j]] += elapsed(L, evf[i][j], evf[i][j + 1]) / a.steps
             kms[names[3 + j]] += elapsed(L, evb[i][j], evb[i][j + 1]) / a.steps
+        step_ms.append(elapsed(L, evf[i][0], evb[i][3]))
+    step_ms.sort()
 
     # state array sizes (fwd workspace with a cache = tables + per-segment states)
     table_b = 0 if not sh["nseq"] else -(-8 * (sh["nseq"] + 1) // 256) * 256
@@ -227,6 +247,7 @@ def main():
         "mfma_peak_frac_dense": f_dense / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "compulsory_io_GBs": (U * d * (8 + 14) * (2 if w.dtype == "bf16" else 4) / 2)
                              / (ms * 1e-3) / 1e9,
+        "ms_per_step_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
         "kernels_ms": kms,
         "roofline": roof,
         "gpu": torch.cuda.get_device_name(dev),

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <string>
+#include <vector>
 
 #include "lasp_internal.h"
 
@@ -156,6 +157,23 @@ size_t lasp_bwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype, int w
     return make_plan(shape, dtype, pl) == LASP_OK ? bwd_ws(pl, with_state_cache != 0) : 0;
 }
 
+// With LASP_DEBUG=1 in the environment, a packed batch's cu_seqlens is copied
+// to the host (after the work already on the stream) and checked: cu[0] = 0,
+// non-decreasing, cu[nseq] = N.  Otherwise its contents are trusted.
+static int debug_check_cu(const lasp_shape *shape, const int32_t *cu, hipStream_t stream) {
+    const char *e = getenv("LASP_DEBUG");
+    if (!cu || !e || strcmp(e, "1") != 0) return LASP_OK;
+    std::vector<int32_t> h((size_t)shape->nseq + 1);
+    hipError_t err = hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t),
+                                    hipMemcpyDeviceToHost, stream);
+    if (err == hipSuccess) err = hipStreamSynchronize(stream);
+    if (err != hipSuccess) return hip_status(err);
+    if (h[0] != 0 || h.back() != shape->N) return LASP_EINVAL;
+    for (size_t i = 1; i < h.size(); ++i)
+        if (h[i] < h[i - 1]) return LASP_EINVAL;
+    return LASP_OK;
+}
+
 int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
                 const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
                 void *O, float *M_out, void *state_cache, void *workspace,
@@ -181,6 +199,7 @@ int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
     const Range outs[] = {{O, tens}, {M_out, st}, {state_cache, cache ? pl.cache_b : 0},
                           {workspace, need}};
     if (any_overlap(outs, 4, ins, 6)) return LASP_EINVAL;
+    if ((rc = debug_check_cu(shape, cu_seqlens, (hipStream_t)stream)) != LASP_OK) return rc;
 
     lasp::Params p;
     fill_common(p, shape, pl, cu_seqlens, decay);
@@ -239,6 +258,7 @@ int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
                          {cu_seqlens, cu_seqlens ? ((size_t)pl.nseq + 1) * 4 : 0}};
     const Range outs[] = {{dQ, tens}, {dK, tens}, {dV, tens}, {dM_in, st}, {workspace, need}};
     if (any_overlap(outs, 5, ins, 9)) return LASP_EINVAL;
+    if ((rc = debug_check_cu(shape, cu_seqlens, (hipStream_t)stream)) != LASP_OK) return rc;
 
     lasp::Params p;
     fill_common(p, shape, pl, cu_seqlens, decay);

@@ -1134,8 +1134,12 @@ template <int C> struct SweepCfg {
     }
 };
 
-template <int D, int C>
-__global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p, int role0, int nroles) {
+// BWD = false: role 0 (O); BWD = true: roles 1-3 (dQ, dV, dK), neighbours in
+// launch order so that the roles of one segment run at the same time and share
+// their reads of Q, K, V, dO in L2.
+template <int D, int C, bool BWD>
+__global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
+    constexpr int role0 = BWD ? 1 : 0, nroles = BWD ? 3 : 1;
     using Cfg = SweepCfg<C>;
     constexpr int NCT = Cfg::NCT, NW = Cfg::NW, NG = Cfg::NG;
     constexpr int PR = D / 8, KS = D / 16, NDT = D / 32;
@@ -1626,18 +1630,18 @@ static hipError_t bwd_impl(const Params &p, hipStream_t st, hipEvent_t *ev) {
 }
 
 // bf16: segment totals (transpose-read local kernel), segment scan, sweep.
-template <int D, int C>
-static void sweep_launch(const Params &p, int role0, int nroles, hipStream_t st) {
-    hipLaunchKernelGGL((k_sweep_bf16<D, C>), dim3(round8(p.n_segs_ub * p.H * nroles)),
-                       dim3(SweepCfg<C>::NT), 0, st, p, role0, nroles);
+template <int D, int C, bool BWD>
+static void sweep_launch(const Params &p, hipStream_t st) {
+    hipLaunchKernelGGL((k_sweep_bf16<D, C, BWD>), dim3(round8(p.n_segs_ub * p.H * (BWD ? 3 : 1))),
+                       dim3(SweepCfg<C>::NT), 0, st, p);
 }
 
-template <int D>
-static void sweep_dispatch(const Params &p, int role0, int nroles, hipStream_t st) {
+template <int D, bool BWD>
+static void sweep_dispatch(const Params &p, hipStream_t st) {
     switch (p.C) {
-    case 64: sweep_launch<D, 64>(p, role0, nroles, st); break;
-    case 128: sweep_launch<D, 128>(p, role0, nroles, st); break;
-    default: sweep_launch<D, 256>(p, role0, nroles, st); break;
+    case 64: sweep_launch<D, 64, BWD>(p, st); break;
+    case 128: sweep_launch<D, 128, BWD>(p, st); break;
+    default: sweep_launch<D, 256, BWD>(p, st); break;
     }
 }
 
@@ -1650,7 +1654,7 @@ static hipError_t fwd_bf16(const Params &p, bool with_output, hipStream_t st, hi
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     hipLaunchKernelGGL((k_fwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
     rec(ev, 2, st);
-    if (with_output) sweep_dispatch<D>(p, 0, 1, st);
+    if (with_output) sweep_dispatch<D, false>(p, st);
     rec(ev, 3, st);
     return hipGetLastError();
 }
@@ -1664,7 +1668,7 @@ static hipError_t bwd_bf16(const Params &p, hipStream_t st, hipEvent_t *ev) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     hipLaunchKernelGGL((k_bwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
     rec(ev, 2, st);
-    sweep_dispatch<D>(p, 1, 3, st);   // dQ, dV, dK of a segment are neighbours in launch order
+    sweep_dispatch<D, true>(p, st);
     rec(ev, 3, st);
     return hipGetLastError();
 }

@@ -41,7 +41,12 @@
  *
  * Errors: every argument is checked before anything is enqueued; on error
  * nothing runs and a lasp_status code is returned.  cu_seqlens contents are
- * trusted (monotone, cu[0] = 0, cu[nseq] = N); NaN/Inf inputs propagate.
+ * trusted (monotone, cu[0] = 0, cu[nseq] = N) unless the environment has
+ * LASP_DEBUG=1: then each call copies cu_seqlens to the host (synchronizing
+ * the stream) and returns LASP_EINVAL if it is malformed.  Even unchecked, a
+ * malformed cu_seqlens cannot make the kernels access memory outside the
+ * [B, H, N, d] tensors (sequence bounds are clamped to [0, N]); the results
+ * are then meaningless.  NaN/Inf inputs propagate.
  * Numbers: bf16 inputs are multiplied on bf16 MFMA with float32 accumulation;
  * states are float32 in HBM between kernels and rounded to bf16 where they are
  * MFMA operands.  float32 inputs use float32 MFMA throughout.

@@ -245,6 +245,41 @@ def test_full_config_sampled(cfg):
     full_config_check(CONFIGS[cfg], seed=100 + cfg)
 
 
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_full_config_all_elements(cfg):
+    """Every element of O, dQ, dK, dV, M_out, dM_in at full size (the launch
+    configuration the benchmark times) against the C float64 recurrence."""
+    w = CONFIGS[cfg]
+    say("case: config %d, all elements" % cfg)
+    inp = make_inputs(w)
+    out = run_gpu(inp)
+    a = {k: inp[k].float().numpy() for k in ("Q", "K", "V", "dO")}
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy()
+    ref = crecurrent.run(a["Q"], a["K"], a["V"], a["dO"], np64(inp["decay"]), np64(inp["M_in"]),
+                         np64(inp["dM_out"]), cu_seqlens=cu)
+    del a
+    check("config%d" % cfg, out, ref, TOL[w.dtype], ["O", "dQ", "dK", "dV", "M_out", "dM_in"])
+
+
+def test_debug_rejects_bad_cu_seqlens(monkeypatch):
+    """LASP_DEBUG=1: a malformed cu_seqlens is rejected before anything runs."""
+    w = small("packed", lengths=[64, 100, 36], d=64, chunk=64)
+    inp = make_inputs(w)
+    Q, K, V = dev(inp["Q"]), dev(inp["K"]), dev(inp["V"])
+    N = Q.shape[2]
+    for bad in ([0, 100, 64, N], [1, 64, 164, N], [0, 64, 164, N + 1]):
+        cu = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        monkeypatch.setenv("LASP_DEBUG", "1")
+        with pytest.raises(cca.LaspError) as e:
+            cca.fwd(Q, K, V, 64, None, cu)
+        assert e.value.status == 1
+        monkeypatch.delenv("LASP_DEBUG")
+    good = dev(inp["cu_seqlens"])
+    monkeypatch.setenv("LASP_DEBUG", "1")
+    cca.fwd(Q, K, V, 64, None, good)
+    torch.cuda.synchronize()
+
+
 def test_config3_with_dm_out():
     """One device's share with both incoming state and incoming state gradient."""
     import dataclasses
