@@ -107,9 +107,9 @@ __device__ __forceinline__ void store4(float *p, float a, float b, float c, floa
     *(float4 *)p = make_float4(a, b, c, d);
 }
 __device__ __forceinline__ void store4(bf16 *p, float a, float b, float c, float d) {
-    const uint32_t lo = (uint32_t)fromf<bf16>(a).u | ((uint32_t)fromf<bf16>(b).u << 16);
-    const uint32_t hi = (uint32_t)fromf<bf16>(c).u | ((uint32_t)fromf<bf16>(d).u << 16);
-    *(uint2 *)p = make_uint2(lo, hi);
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    const bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};   // RNE, two packed cvts
+    *(bf16x4_t *)p = v;
 }
 
 // lambda^e with lambda = 2^l2; lambda^0 = 1 exactly (also for lambda = 0).
@@ -1283,10 +1283,24 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         f32x16 st[NP];                 // S^T: [column token ct*32 + crow(e)][row rt*32 + lane%32]
 #pragma unroll
         for (int u = 0; u < NP; ++u) zero(st[u]);
+        // The B fragments of k-step ks+1 are read while the MFMAs of step ks
+        // run (scheduling barriers keep the compiler from serializing each
+        // read with its MFMA to save registers).
+        bf16x8_t bf[2][NP];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int u = 0; u < NP; ++u) bf[0][u] = frag_rows_sw<D>(Bt[u], fo, 0, 0);
 #pragma unroll
-            for (int u = 0; u < NP; ++u) mma(st[u], frag_rows_sw<D>(Bt[u], fo, 0, ks * 16), af[ks]);
+        for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < KS) {
+#pragma unroll
+                for (int u = 0; u < NP; ++u)
+                    bf[(ks + 1) & 1][u] = frag_rows_sw<D>(Bt[u], fo, 0, (ks + 1) * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < NP; ++u) mma(st[u], bf[ks & 1][u], af[ks]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         bf16x8_t s0[NP], s1[NP];
 #pragma unroll
         for (int u = 0; u < NP; ++u) {
@@ -1390,9 +1404,13 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     for (int i = 0; i < nch; ++i) {
         const int t = chunk_t(i), Ct = chunk_len(t);
         const bool upd = i + 1 < nch;  // the state after the segment's last chunk is not needed
-        // chunk start: this chunk's first group and A rows have landed, every
-        // wave has published the state into XS
-        LASP_WAIT_VM(0);
+        // chunk start: this chunk's first group and A rows have landed (only the
+        // previous chunk's NDT*4 output stores, issued after them, may still be
+        // in flight), every wave has published the state into XS
+        if (i > 0)
+            LASP_WAIT_VM(NDT * 4);
+        else
+            LASP_WAIT_VM(0);
         lds_barrier();
         dma_group(i, IC<1>());         // slots of the second group are free now
         // inter-chunk term: acc = (A X)^T, rows scaled by lambda^e(r)
@@ -1442,19 +1460,27 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         run_group(IC<1>(), Ct, upd, [&]() __attribute__((always_inline)) {
             if (i + 1 < nch) load_a(i + 1, af);
         });
-        // rows out: lane holds row rt*32 + lane%32, features nt*32 + 8j + 4*(lane/32) + [0,4)
-        if (rt >= 0 && rt * 32 < Ct) {
+        // rows out: lane holds row rt*32 + lane%32, features nt*32 + 8j + 4*(lane/32) + [0,4).
+        // The stores go through a buffer descriptor that covers exactly this
+        // chunk's Ct rows (none for a wave without rows): the hardware drops
+        // stores past its end, so every wave issues the same NDT*4 stores and
+        // the count of memory operations in flight after them is known.
+        {
             const int lz = opaque_lane();
-            const int row = rt * 32 + (lz & 31);
-            bf16 *dst = Out + ((int64_t)t * p.C + row) * D + (lz >> 5) * 4;
-            if (row < Ct) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                Out + (int64_t)t * p.C * D, 0, rt >= 0 ? Ct * D * 2 : 0, 0x00020000);
+            const int off = ((rt * 32 + (lz & 31)) * D + (lz >> 5) * 4) * 2;   // negative: dropped
 #pragma unroll
-                for (int nt = 0; nt < NDT; ++nt)
+            for (int nt = 0; nt < NDT; ++nt)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        store4(dst + nt * 32 + j * 8, acc[nt][4 * j + 0], acc[nt][4 * j + 1],
-                               acc[nt][4 * j + 2], acc[nt][4 * j + 3]);
-            }
+                for (int j = 0; j < 4; ++j) {
+                    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                    typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+                    const bf16x4_t v = {(__bf16)acc[nt][4 * j + 0], (__bf16)acc[nt][4 * j + 1],
+                                        (__bf16)acc[nt][4 * j + 2], (__bf16)acc[nt][4 * j + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rs,
+                                                          off + (nt * 32 + j * 8) * 2, 0, 0);
+                }
         }
         if (upd) write_state();
     }
