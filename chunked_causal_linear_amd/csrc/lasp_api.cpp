@@ -49,9 +49,12 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl) {
     const int64_t per_seq_chunks = ((int64_t)s->N + s->chunk - 1) / s->chunk;
     int64_t chunks_ub = pl.varlen ? (int64_t)s->N / s->chunk + s->nseq
                                   : per_seq_chunks * (int64_t)s->B;
-    // Segments: enough (segment, head) workgroups to fill the GPU, few enough
-    // segment states to keep the cross-segment scan cheap.
-    int64_t g = chunks_ub * s->H / 2048;
+    // Segments: about 1024 (segment, head) workgroups per role (four per CU of
+    // the 256 on MI355X, one resident at a time), and as few segment states as
+    // that allows, which keeps the local-total and cross-segment-scan kernels
+    // cheap (measured at B1 H32 N131072 C256: G = 4, 8, 16 -> 5.28, 5.09,
+    // 4.99 ms per forward+backward).
+    int64_t g = chunks_ub * s->H / 1024;
     pl.G = (int)(g < 2 ? 2 : (g > 16 ? 16 : g));
     // Test hook: LASP_SEGMENT_CHUNKS overrides G (must be the same for the
     // forward and backward calls that share a state cache).

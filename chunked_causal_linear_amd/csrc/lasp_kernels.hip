@@ -945,14 +945,6 @@ __device__ __forceinline__ bf16x8_t pack8(float a0, float a1, float a2, float a3
     return r;
 }
 
-__device__ __forceinline__ uint4 scale8(uint4 v, float s) {
-    float f[8];
-    load16((const bf16 *)&v, f);
-    const bf16x8_t b = pack8(f[0] * s, f[1] * s, f[2] * s, f[3] * s, f[4] * s, f[5] * s,
-                             f[6] * s, f[7] * s);
-    return __builtin_bit_cast(uint4, b);
-}
-
 // ---------------------------------------------------------------------------
 // Unpadded LDS tiles.  global_load_lds_dwordx4 writes lane l's 16 bytes to
 // lds_base + 16*l, so token tiles are stored without padding and their 16-byte
@@ -1134,12 +1126,24 @@ template <int C> struct SweepCfg {
     }
 };
 
-// BWD = false: role 0 (O); BWD = true: roles 1-3 (dQ, dV, dK), neighbours in
-// launch order so that the roles of one segment run at the same time and share
-// their reads of Q, K, V, dO in L2.
-template <int D, int C, bool BWD>
+// What one launch computes:
+enum SweepKind {
+    SWEEP_OUT = 0,     // role 0 (O)
+    SWEEP_GRADS = 1,   // roles 1-3 (dQ, dV, dK), neighbours in launch order so
+                       // that the roles of one segment run at the same time and
+                       // share their reads of Q, K, V, dO in L2
+    SWEEP_TOT_F = 2,   // segment totals Z of the forward state recursion
+    SWEEP_TOT_B = 3    // segment totals W of the backward state recursion
+};
+// The totals are the state recursion alone, started from zero at the segment
+// boundary (LASP-2's chunk states M_t, resp. dM_t, accumulated with their decay
+// over the segment: Z = sum_t lambda^(tokens after chunk t) M_t); they feed the
+// cross-segment scan.  They use the same token-tile pipeline as the outputs.
+template <int D, int C, int KIND>
 __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
-    constexpr int role0 = BWD ? 1 : 0, nroles = BWD ? 3 : 1;
+    constexpr bool TOT = KIND >= SWEEP_TOT_F;
+    constexpr int role0 = KIND == SWEEP_GRADS ? 1 : (KIND == SWEEP_TOT_B ? 2 : 0);
+    constexpr int nroles = KIND == SWEEP_GRADS ? 3 : 1;
     using Cfg = SweepCfg<C>;
     constexpr int NCT = Cfg::NCT, NW = Cfg::NW, NG = Cfg::NG;
     constexpr int PR = D / 8, KS = D / 16, NDT = D / 32;
@@ -1149,7 +1153,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     constexpr int CPW = (NIG + NW - 1) / NW;           // copies per wave per group (at most)
     constexpr int NSTT = NDT * NDT;                    // 32x32 state tiles
     constexpr int STW = (NSTT + NW - 1) / NW;
-    __shared__ __attribute__((aligned(16))) bf16 XS[D * D];
+    __shared__ __attribute__((aligned(16))) bf16 XS[TOT ? 8 : D * D];
     // B and Cv tiles of the two groups.  Two distinct arrays: the compiler
     // then sees that copies in flight into one group's slots do not alias
     // reads of the other's, and does not wait for them.
@@ -1183,7 +1187,8 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     case 2: A = Kg; Bm = Qg; Cv = Og; Out = (bf16 *)p.dV + rbase * D; break;
     default: A = Vg; Bm = Og; Cv = Qg; Out = (bf16 *)p.dK + rbase * D; break;
     }
-    const float *seg = (rev ? p.Rseg : p.Pseg) + ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
+    const int64_t seg_off = ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
+    const float *seg = (rev ? p.Rseg : p.Pseg) + seg_off;
 
     const int w = wave_id(), l = lane_id();
     const int rt = Cfg::tile(w);
@@ -1235,14 +1240,14 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     // ---- prologue: first chunk's A rows and first group, incoming state ----
     bf16x8_t af[KS];
     dma_group(0, IC<0>());
-    load_a(0, af);
+    if (!TOT) load_a(0, af);
 
     f32x16 sacc[STW];
 #pragma unroll
     for (int k = 0; k < STW; ++k) {
         const int tl = w + k * NW;
         zero(sacc[k]);
-        if (tl < NSTT) {
+        if (!TOT && tl < NSTT) {
             const int mi = tl / NDT, ni = tl % NDT, lc = l & 31, lg = l >> 5;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1253,6 +1258,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         }
     }
     auto write_state = [&]() __attribute__((always_inline)) {   // XS[col feature][row feature] = bf16(state)
+        if (TOT) return;
         const int lz = opaque_lane();
         const int lc = lz & 31, lg = lz >> 5;
 #pragma unroll
@@ -1365,7 +1371,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     auto run_group = [&](auto G, int Ct, bool upd, auto after_pairs) __attribute__((always_inline)) {
         constexpr int g = decltype(G)::value;
         const bf16 *BG = g == 0 ? BG0 : BG1;
-        if (rt >= 0 && rt * 32 < Ct) {
+        if (!TOT && rt >= 0 && rt * 32 < Ct) {
             // the group's causal tiles, two at a time
             int need = 0;
 #pragma unroll
@@ -1403,18 +1409,19 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
 #pragma unroll 1
     for (int i = 0; i < nch; ++i) {
         const int t = chunk_t(i), Ct = chunk_len(t);
-        const bool upd = i + 1 < nch;  // the state after the segment's last chunk is not needed
+        // (the state after the segment's last chunk is needed only as a total)
+        const bool upd = TOT || i + 1 < nch;
         // chunk start: this chunk's first group and A rows have landed (only the
         // previous chunk's NDT*4 output stores, issued after them, may still be
         // in flight), every wave has published the state into XS
-        if (i > 0)
+        if (!TOT && i > 0)
             LASP_WAIT_VM(NDT * 4);
         else
             LASP_WAIT_VM(0);
         lds_barrier();
         dma_group(i, IC<1>());         // slots of the second group are free now
         // inter-chunk term: acc = (A X)^T, rows scaled by lambda^e(r)
-        {
+        if constexpr (!TOT) {
 #pragma unroll
             for (int nt = 0; nt < NDT; ++nt) zero(acc[nt]);
             auto inter = [&](auto XT) __attribute__((always_inline)) {
@@ -1458,14 +1465,14 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         // the next chunk's A rows go into af once this chunk's pair products
         // have read it; the state updates and stores hide their latency
         run_group(IC<1>(), Ct, upd, [&]() __attribute__((always_inline)) {
-            if (i + 1 < nch) load_a(i + 1, af);
+            if (!TOT && i + 1 < nch) load_a(i + 1, af);
         });
         // rows out: lane holds row rt*32 + lane%32, features nt*32 + 8j + 4*(lane/32) + [0,4).
         // The stores go through a buffer descriptor that covers exactly this
         // chunk's Ct rows (none for a wave without rows): the hardware drops
         // stores past its end, so every wave issues the same NDT*4 stores and
         // the count of memory operations in flight after them is known.
-        {
+        if constexpr (!TOT) {
             const int lz = opaque_lane();
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 Out + (int64_t)t * p.C * D, 0, rt >= 0 ? Ct * D * 2 : 0, 0x00020000);
@@ -1484,129 +1491,23 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         }
         if (upd) write_state();
     }
-}
-
-// ---------------------------------------------------------------------------
-// Local chunk states (bf16): one workgroup per (segment, head).
-//   which = 0: L_t = state entering chunk t from the segment start (chunks in
-//              order), L += (Gam_t K_t)^T V_t, stored to Lc, total to Z;
-//   which = 1: R_t = reverse state from the segment end (chunks in reverse),
-//              R += (Lam_t Q_t)^T dO_t, stored to Rc, total to W.
-// The K^T V (Q^T dO) products read both operands with the transpose read.
-template <int D>
-__global__ __launch_bounds__(256) void k_local_bf16(Params p, int which) {
-    constexpr int NT = 256, TT = 64, PX = D + 8;
-    constexpr int PIECES = TT * D / 8;
-    constexpr int PPT = (PIECES + NT - 1) / NT;
-    using TL = Tiles<D / 32, D / 32>;
-    __shared__ __attribute__((aligned(16))) bf16 A_s[2][TT * PX];
-    __shared__ __attribute__((aligned(16))) bf16 B_s[2][TT * PX];
-
-    const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
-    Seq s;
-    int sl;
-    if (!seg_seq(p, gs, s, sl)) return;
-    const float l2 = head_log2_decay(p, h);
-    const int64_t rb = row_base(p, s, h);
-    const bf16 *Ag = (const bf16 *)(which ? p.Q : p.K) + rb * D;
-    const bf16 *Bg = (const bf16 *)(which ? p.dO : p.V) + rb * D;
-    bf16 *Lout = (bf16 *)(which ? p.Rc : p.Lc);
-    float *Tot = which ? p.W : p.Z;
-    const bool store_local = p.G > 1 && Lout != nullptr;
-    const int tid = threadIdx.x;
-
-    f32x16 acc[TL::PER_WAVE];
+    if constexpr (TOT) {   // the segment total, [dv][dk] like the scanned states
+        float *tot = (KIND == SWEEP_TOT_F ? p.Z : p.W) + seg_off;
 #pragma unroll
-    for (int k = 0; k < TL::PER_WAVE; ++k) zero(acc[k]);
-
-    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
-    const int nchunks = t1 - t0;
-    // flattened (chunk, 64-token tile) steps in sweep order
-    auto chunk_of = [&](int i) { return which ? (t1 - 1 - i) : (t0 + i); };
-    auto tiles_of = [&](int t) { return (min(p.C, s.len - t * p.C) + TT - 1) / TT; };
-    uint4 pa[PPT], pb[PPT];
-    auto fetch = [&](int t, int tl) {
-        const int Ct = min(p.C, s.len - t * p.C);
+        for (int k = 0; k < STW; ++k) {
+            const int tl = w + k * NW;
+            if (tl < NSTT) {
+                const int mi = tl / NDT, ni = tl % NDT, lc = l & 31, lg = l >> 5;
 #pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const int i = tid + k * NT;
-            const int r = i / (D / 8), c = (i % (D / 8)) * 8;
-            const int row = tl * TT + r;      // token within chunk
-            pa[k] = pb[k] = make_uint4(0u, 0u, 0u, 0u);
-            if (i < PIECES && row < Ct) {
-                const int64_t off = (int64_t)(t * p.C + row) * D + c;
-                const float sc = dpow(l2, (float)(which ? row + 1 : Ct - 1 - row));
-                pa[k] = *(const uint4 *)(Ag + off);
-                if (sc != 1.f) pa[k] = scale8(pa[k], sc);
-                pb[k] = *(const uint4 *)(Bg + off);
+                for (int q = 0; q < 4; ++q)
+                    *(float4 *)(tot + (int64_t)(ni * 32 + lc) * D + mi * 32 + q * 8 + lg * 4) =
+                        make_float4(sacc[k][q * 4 + 0], sacc[k][q * 4 + 1], sacc[k][q * 4 + 2],
+                                    sacc[k][q * 4 + 3]);
             }
         }
-    };
-    auto deposit = [&](int buf) {
-#pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const int i = tid + k * NT;
-            if (i < PIECES) {
-                const int r = i / (D / 8), c = (i % (D / 8)) * 8;
-                *(uint4 *)(&A_s[buf][r * PX + c]) = pa[k];
-                *(uint4 *)(&B_s[buf][r * PX + c]) = pb[k];
-            }
-        }
-    };
-    if (nchunks <= 0) return;
-    int ci = 0, tl = 0, buf = 0;
-    int t = chunk_of(0);
-    fetch(t, 0);
-    deposit(0);
-    __syncthreads();
-    // state written before each chunk's contribution is added
-    bool first_tile = true;
-    while (true) {
-        const int ntl = tiles_of(t);
-        if (first_tile) {
-            if (store_local) {
-                bf16 *Lt = Lout + ((int64_t)(s.c0 + t) * p.H + h) * D * D;
-#pragma unroll
-                for (int k = 0; k < TL::PER_WAVE; ++k) {
-                    int mi, ni;
-                    if (TL::get(k, mi, ni)) store_T(acc[k], Lt, D, mi * 32, ni * 32, Ident());
-                }
-            }
-            const float dc = dpow(l2, (float)min(p.C, s.len - t * p.C));
-#pragma unroll
-            for (int k = 0; k < TL::PER_WAVE; ++k) acc[k] *= dc;
-        }
-        // next step
-        int nci = ci, ntl2 = tl + 1, nt_ = t;
-        if (ntl2 >= ntl) { nci = ci + 1; ntl2 = 0; nt_ = nci < nchunks ? chunk_of(nci) : -1; }
-        const bool more = nci < nchunks;
-        if (more) fetch(nt_, ntl2);
-#pragma unroll
-        for (int k = 0; k < TL::PER_WAVE; ++k) {
-            int mi, ni;
-            if (TL::get(k, mi, ni)) {
-#pragma unroll
-                for (int k0 = 0; k0 < TT; k0 += 16)
-                    mma(acc[k], frag_cols<false>(A_s[buf], PX, k0, mi * 32),
-                        frag_cols<false>(B_s[buf], PX, k0, ni * 32));
-            }
-        }
-        if (!more) break;
-        deposit(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
-        first_tile = nci != ci;
-        ci = nci;
-        tl = ntl2;
-        t = nt_;
-    }
-    float *Ts = Tot + ((int64_t)gs * p.H + h) * D * D;
-#pragma unroll
-    for (int k = 0; k < TL::PER_WAVE; ++k) {
-        int mi, ni;
-        if (TL::get(k, mi, ni)) store_T(acc[k], Ts, D, mi * 32, ni * 32, Ident());
     }
 }
+
 
 // ---------------------------------------------------------------------------
 // Launchers
@@ -1656,18 +1557,19 @@ static hipError_t bwd_impl(const Params &p, hipStream_t st, hipEvent_t *ev) {
 }
 
 // bf16: segment totals (transpose-read local kernel), segment scan, sweep.
-template <int D, int C, bool BWD>
+template <int D, int C, int KIND>
 static void sweep_launch(const Params &p, hipStream_t st) {
-    hipLaunchKernelGGL((k_sweep_bf16<D, C, BWD>), dim3(round8(p.n_segs_ub * p.H * (BWD ? 3 : 1))),
+    const int roles = KIND == SWEEP_GRADS ? 3 : 1;
+    hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND>), dim3(round8(p.n_segs_ub * p.H * roles)),
                        dim3(SweepCfg<C>::NT), 0, st, p);
 }
 
-template <int D, bool BWD>
+template <int D, int KIND>
 static void sweep_dispatch(const Params &p, hipStream_t st) {
     switch (p.C) {
-    case 64: sweep_launch<D, 64, BWD>(p, st); break;
-    case 128: sweep_launch<D, 128, BWD>(p, st); break;
-    default: sweep_launch<D, 256, BWD>(p, st); break;
+    case 64: sweep_launch<D, 64, KIND>(p, st); break;
+    case 128: sweep_launch<D, 128, KIND>(p, st); break;
+    default: sweep_launch<D, 256, KIND>(p, st); break;
     }
 }
 
@@ -1675,12 +1577,12 @@ template <int D>
 static hipError_t fwd_bf16(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
     if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
     rec(ev, 0, st);
-    hipLaunchKernelGGL((k_local_bf16<D>), dim3(p.n_segs_ub * p.H), dim3(256), 0, st, p, 0);
+    sweep_dispatch<D, SWEEP_TOT_F>(p, st);
     rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     hipLaunchKernelGGL((k_fwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
     rec(ev, 2, st);
-    if (with_output) sweep_dispatch<D, false>(p, st);
+    if (with_output) sweep_dispatch<D, SWEEP_OUT>(p, st);
     rec(ev, 3, st);
     return hipGetLastError();
 }
@@ -1689,12 +1591,12 @@ template <int D>
 static hipError_t bwd_bf16(const Params &p, hipStream_t st, hipEvent_t *ev) {
     if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
     rec(ev, 0, st);
-    hipLaunchKernelGGL((k_local_bf16<D>), dim3(p.n_segs_ub * p.H), dim3(256), 0, st, p, 1);
+    sweep_dispatch<D, SWEEP_TOT_B>(p, st);
     rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     hipLaunchKernelGGL((k_bwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
     rec(ev, 2, st);
-    sweep_dispatch<D, true>(p, st);
+    sweep_dispatch<D, SWEEP_GRADS>(p, st);
     rec(ev, 3, st);
     return hipGetLastError();
 }
