@@ -1412,10 +1412,10 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         // (the state after the segment's last chunk is needed only as a total)
         const bool upd = TOT || i + 1 < nch;
         // chunk start: this chunk's first group and A rows have landed (only the
-        // previous chunk's NDT*4 output stores, issued after them, may still be
+        // previous chunk's NDT*2 output stores, issued after them, may still be
         // in flight), every wave has published the state into XS
         if (!TOT && i > 0)
-            LASP_WAIT_VM(NDT * 4);
+            LASP_WAIT_VM(NDT * 2);
         else
             LASP_WAIT_VM(0);
         lds_barrier();
@@ -1468,26 +1468,42 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
             if (!TOT && i + 1 < nch) load_a(i + 1, af);
         });
         // rows out: lane holds row rt*32 + lane%32, features nt*32 + 8j + 4*(lane/32) + [0,4).
-        // The stores go through a buffer descriptor that covers exactly this
-        // chunk's Ct rows (none for a wave without rows): the hardware drops
-        // stores past its end, so every wave issues the same NDT*4 stores and
-        // the count of memory operations in flight after them is known.
+        // Lanes l and l+32 exchange halves (permlane32 swap) so that each lane
+        // holds two 8-feature pieces of its row, stored with 16-byte stores:
+        // lanes < 32 features 0-7 and 16-23 of a 32-feature block, lanes >= 32
+        // features 8-15 and 24-31.  The stores go through a buffer descriptor
+        // that covers exactly this chunk's Ct rows (none for a wave without
+        // rows): the hardware drops stores past its end, so every wave issues
+        // the same NDT*2 stores and the count of memory operations in flight
+        // after them is known.
         if constexpr (!TOT) {
             const int lz = opaque_lane();
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 Out + (int64_t)t * p.C * D, 0, rt >= 0 ? Ct * D * 2 : 0, 0x00020000);
-            const int off = ((rt * 32 + (lz & 31)) * D + (lz >> 5) * 4) * 2;   // negative: dropped
+            const int off = ((rt * 32 + (lz & 31)) * D + (lz >> 5) * 8) * 2;   // negative: dropped
 #pragma unroll
-            for (int nt = 0; nt < NDT; ++nt)
+            for (int nt = 0; nt < NDT; ++nt) {
+                typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+                typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+                unsigned r[8];   // r[2j], r[2j+1]: features 8j + 4*(lane/32) + [0,4), packed
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-                    typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-                    const bf16x4_t v = {(__bf16)acc[nt][4 * j + 0], (__bf16)acc[nt][4 * j + 1],
-                                        (__bf16)acc[nt][4 * j + 2], (__bf16)acc[nt][4 * j + 3]};
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rs,
-                                                          off + (nt * 32 + j * 8) * 2, 0, 0);
+                for (int q = 0; q < 8; ++q) {
+                    const bf16x2_t v = {(__bf16)acc[nt][2 * q], (__bf16)acc[nt][2 * q + 1]};
+                    r[q] = __builtin_bit_cast(unsigned, v);
                 }
+#pragma unroll
+                for (int q = 0; q < 8; q += 4) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const auto x = __builtin_amdgcn_permlane32_swap(r[q + e], r[q + 2 + e], false, false);
+                        r[q + e] = x[0];
+                        r[q + 2 + e] = x[1];
+                    }
+                }
+                const u32x4_t v0 = {r[0], r[1], r[2], r[3]}, v1 = {r[4], r[5], r[6], r[7]};
+                __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off + nt * 64, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off + nt * 64 + 32, 0, 0);
+            }
         }
         if (upd) write_state();
     }
