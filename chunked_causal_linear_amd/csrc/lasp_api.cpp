@@ -29,7 +29,8 @@ struct Plan {
     size_t table_b;      // packed-batch tables
     size_t local_b;      // per-chunk local states (Lc or Rc)
     size_t seg_b;        // per-segment f32 states (Pseg, Z, Rseg or W)
-    size_t cache_b;      // state cache = [Lc][Pseg]
+    size_t fin_b;        // per-sequence f32 final states (Pfin)
+    size_t cache_b;      // state cache = [Lc][Pseg][Pfin]
 };
 
 int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl) {
@@ -82,7 +83,9 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl) {
     // recomputes chunk states inside its segment sweep)
     pl.local_b = dt == LASP_BF16 ? 0 : align_up((size_t)pl.n_chunks_ub * pl.H * dd * pl.esz);
     pl.seg_b = align_up((size_t)pl.n_segs_ub * pl.H * dd * sizeof(float));
-    pl.cache_b = pl.local_b + pl.seg_b;
+    // final states: the bf16 backward starts its subtraction walk of dQ from them
+    pl.fin_b = dt == LASP_BF16 ? align_up((size_t)pl.nseq * pl.H * dd * sizeof(float)) : 0;
+    pl.cache_b = pl.local_b + pl.seg_b + pl.fin_b;
     return LASP_OK;
 }
 
@@ -223,6 +226,7 @@ int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
     char *c = cache ? (char *)state_cache : w;
     p.Lc = pl.local_b ? c : nullptr;
     p.Pseg = (float *)(c + pl.local_b);
+    p.Pfin = pl.fin_b ? (float *)(c + pl.local_b + pl.seg_b) : nullptr;
     return hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, true, (hipStream_t)stream,
                                        (hipEvent_t *)events));
 }
@@ -291,9 +295,11 @@ int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
     if (cache) {
         p.Lc = pl.local_b ? const_cast<void *>(state_cache) : nullptr;
         p.Pseg = (float *)((char *)state_cache + pl.local_b);
+        p.Pfin = pl.fin_b ? (float *)((char *)state_cache + pl.local_b + pl.seg_b) : nullptr;
     } else {   // recompute the forward states (no output, no M_out)
         p.Lc = pl.local_b ? w : nullptr;
         p.Pseg = (float *)(w + pl.local_b);
+        p.Pfin = pl.fin_b ? (float *)(w + pl.local_b + pl.seg_b) : nullptr;
         p.Z = (float *)(w + pl.cache_b);
         rc = hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, false, hs));
         if (rc != LASP_OK) return rc;

@@ -30,6 +30,7 @@ struct Params {
     float *M_out, *dM_in;          // [nseq][H][D][D] or null
     void *Lc;      // [chunks][H][D][D] elem: local prefix state entering each chunk, [dv][dk]
     float *Pseg;   // [segs][H][D][D] f32: state entering each segment, [dv][dk]
+    float *Pfin;   // [nseq][H][D][D] f32 or null: state after each sequence's last token, [dv][dk]
     float *Z;      // [segs][H][D][D] f32: local state at each segment end, [dv][dk]
     void *Rc;      // [chunks][H][D][D] elem: local reverse state of each chunk, [dv][dk]
     float *Rseg;   // [segs][H][D][D] f32: reverse state entering each segment's last chunk

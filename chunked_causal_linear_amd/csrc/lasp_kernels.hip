@@ -440,7 +440,7 @@ __global__ __launch_bounds__(NTHR) void k_fwd_local(Params p) {
 
 // ---------------------------------------------------------------------------
 // Forward 2: scan over segments, one thread per state element.
-//   Pseg[0] = M_in;  Pseg[s+1] = lambda^len_s Pseg[s] + Z[s];  M_out = last.
+//   Pseg[0] = M_in;  Pseg[s+1] = lambda^len_s Pseg[s] + Z[s];  M_out = Pfin = last.
 // (LASP-2 prefix sum of gathered states; LASP Alg. 2 receive/send as a scan.)
 // ---------------------------------------------------------------------------
 template <int D, typename T>
@@ -465,6 +465,7 @@ __global__ __launch_bounds__(NTHR) void k_fwd_segscan(Params p) {
         P = dpow(l2, (float)len_s) * P + p.Z[idx];
     }
     if (p.M_out) p.M_out[mo] = P;
+    if (p.Pfin) p.Pfin[(int64_t)ih * D * D + e] = P;
 }
 
 // ---------------------------------------------------------------------------
@@ -1097,6 +1098,17 @@ template <int N> struct IC { static constexpr int value = N; };
 // Roles 0 and 1 carry P forward, roles 2 and 3 carry R backward; the state
 // update takes its token rows from B (roles 0, 2) or from Cv (roles 1, 3).
 //
+// dQ of a head without decay walks backwards too, so that the three gradient
+// roles of a segment read the same chunks at the same time (one HBM read of
+// Q, K, V, dO, shared in L2).  With lambda = 1 the state before chunk t is the
+// state after it minus the chunk's own term, P_t = P_(t+1) - K_t^T V_t, hence
+//   dQ[r] = dO_r P_(t+1)^T - sum_{c > r} (dO_r . V_c) K_c,
+// the role-1 computation with the strict reverse causal range, a state that
+// starts at minus the state after the segment (the next segment's entering
+// state, or the sequence's final state) and accumulates as usual, and the
+// output negated.  (With decay the subtraction would divide by lambda^Ct,
+// which is not stable; those heads keep the forward walk.)
+//
 // Work split.  Wave w owns one 32-row tile of every chunk (its A rows live in
 // registers, loaded one chunk ahead) and a fixed share of the 32x32 state
 // tiles.  The chunk's B and Cv rows are all resident in LDS, so the waves run
@@ -1170,11 +1182,13 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
     const int nch = t1 - t0;
     if (nch <= 0) return;
-    const bool rev = role >= 2;                // c >= r, chunks swept backwards
-    const bool xt = role & 1;                  // state operand read transposed
-    const bool u_is_b = !(role & 1);           // state rows from B (else from Cv)
     const float l2 = head_log2_decay(p, h);
     const bool decay = l2 != 0.f;
+    const bool sub = role == 1 && !decay;      // dQ by subtraction, walked backwards
+    const bool rev = role >= 2 || sub;         // chunks swept backwards
+    const int dmin = sub ? 1 : 0;              // causal range: dist(r, c) >= dmin
+    const bool xt = role & 1;                  // state operand read transposed
+    const bool u_is_b = !(role & 1);           // state rows from B (else from Cv)
     const int64_t rbase = row_base(p, s, h);
     const bf16 *Qg = (const bf16 *)p.Q + rbase * D, *Kg = (const bf16 *)p.K + rbase * D;
     const bf16 *Vg = (const bf16 *)p.V + rbase * D;
@@ -1188,7 +1202,11 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     default: A = Vg; Bm = Og; Cv = Qg; Out = (bf16 *)p.dK + rbase * D; break;
     }
     const int64_t seg_off = ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
-    const float *seg = (rev ? p.Rseg : p.Pseg) + seg_off;
+    const float *seg = role >= 2 ? p.Rseg + seg_off : p.Pseg + seg_off;
+    if (sub)   // the state after this segment
+        seg = sl + 1 < min(s.S, p.n_segs_ub - s.s0) ? seg + (int64_t)p.H * D * D
+                                                    : p.Pfin + ((int64_t)s.i * p.H + h) * D * D;
+    const float sgn = sub ? -1.f : 1.f;
 
     const int w = wave_id(), l = lane_id();
     const int rt = Cfg::tile(w);
@@ -1252,8 +1270,8 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 v = *(const float4 *)(seg + (int64_t)(ni * 32 + lc) * D + mi * 32 + q * 8 + lg * 4);
-                sacc[k][q * 4 + 0] = v.x; sacc[k][q * 4 + 1] = v.y;
-                sacc[k][q * 4 + 2] = v.z; sacc[k][q * 4 + 3] = v.w;
+                sacc[k][q * 4 + 0] = sgn * v.x; sacc[k][q * 4 + 1] = sgn * v.y;
+                sacc[k][q * 4 + 2] = sgn * v.z; sacc[k][q * 4 + 3] = sgn * v.w;
             }
         }
     }
@@ -1317,7 +1335,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
                     const int c = ct[u] * 32 + crow(e, lz);
                     const int dist = rev ? (c - r) : (r - c);
                     const float f = decay ? dpow(l2, (float)max(dist, 0)) : 1.f;
-                    st[u][e] = (dist >= 0 && c < Ct) ? st[u][e] * f : 0.f;
+                    st[u][e] = (dist >= dmin && c < Ct) ? st[u][e] * f : 0.f;
                 }
             }
             // as an operand, S^T's k order is permuted; the Cv fragment follows it
@@ -1481,6 +1499,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 Out + (int64_t)t * p.C * D, 0, rt >= 0 ? Ct * D * 2 : 0, 0x00020000);
             const int off = ((rt * 32 + (lz & 31)) * D + (lz >> 5) * 8) * 2;   // negative: dropped
+            const unsigned neg = sub ? 0x80008000u : 0u;                          // bf16 sign bits
 #pragma unroll
             for (int nt = 0; nt < NDT; ++nt) {
                 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -1489,7 +1508,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     const bf16x2_t v = {(__bf16)acc[nt][2 * q], (__bf16)acc[nt][2 * q + 1]};
-                    r[q] = __builtin_bit_cast(unsigned, v);
+                    r[q] = __builtin_bit_cast(unsigned, v) ^ neg;
                 }
 #pragma unroll
                 for (int q = 0; q < 8; q += 4) {

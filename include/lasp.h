@@ -79,8 +79,9 @@ typedef struct {
 } lasp_shape;
 
 /* Size in bytes of the state cache written by lasp_fwd and read by lasp_bwd:
- * the per-chunk states the backward pass reuses (LASP Sec. 3.2, the cached
- * KV_{t-1}).  Depends only on the shape and dtype. */
+ * the states the backward pass reuses (LASP Sec. 3.2, the cached KV_{t-1}):
+ * per-chunk states (fp32) or the states entering each segment of chunks, and
+ * (bf16) each sequence's final state.  Depends only on the shape and dtype. */
 size_t lasp_state_cache_bytes(const lasp_shape *shape, lasp_dtype dtype);
 
 /* Workspace needed by lasp_fwd / lasp_bwd.  with_state_cache != 0 means the

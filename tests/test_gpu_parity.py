@@ -110,6 +110,8 @@ SMALL = [
           m_in_scale=0.1, dm_out_scale=0.1),
     small("bf16 one token", "bf16", B=1, H=1, N=1, d=64, chunk=64, seed=19, m_in_scale=0.1,
           dm_out_scale=0.1),
+    small("bf16 packed d128 C64 no decay Min dMout", "bf16", H=2, d=128, chunk=64, seed=24,
+          lengths=[1, 127, 128, 129, 0, 300, 64, 1000], m_in_scale=0.1, dm_out_scale=0.1),
 ]
 
 
@@ -122,15 +124,29 @@ def test_small_parity(w):
     check(w.name, out, ref, TOL[w.dtype])
 
 
+@pytest.mark.parametrize("decay", ["lightning", "none"])
 @pytest.mark.parametrize("G", ["1", "3", "16"])
-def test_segment_sizes(G, monkeypatch):
-    """The two-level scan gives the same result for any segment length."""
+def test_segment_sizes(G, decay, monkeypatch):
+    """The two-level scan gives the same result for any segment length (without
+    decay the dQ walk starts from the next segment's state or the final one)."""
     monkeypatch.setenv("LASP_SEGMENT_CHUNKS", G)
     w = small("bf16 d64 C64 many chunks", "bf16", B=2, H=2, N=64 * 11 + 17, d=64, chunk=64,
-              seed=20, decay="lightning", m_in_scale=0.1, dm_out_scale=0.1)
-    say("case: segment chunks", G)
+              seed=20, decay=decay, m_in_scale=0.1, dm_out_scale=0.1)
+    say("case: segment chunks", G, decay)
     inp = make_inputs(w)
     check("G=" + G, run_gpu(inp), oracle_full(inp), TOL["bf16"])
+
+
+def test_mixed_decay_heads(monkeypatch):
+    """Heads with and without decay in one launch (their dQ walks run in
+    opposite directions), packed sequences spanning several segments."""
+    monkeypatch.setenv("LASP_SEGMENT_CHUNKS", "3")
+    w = small("bf16 packed d128 C128", "bf16", H=4, d=128, chunk=128, seed=25,
+              lengths=[700, 129, 1, 2000], m_in_scale=0.1, dm_out_scale=0.1)
+    inp = make_inputs(w)
+    inp["decay"] = torch.tensor([1.0, 0.995, 1.0, 0.0], dtype=torch.float32)
+    say("case: mixed decay heads")
+    check("mixed decay", run_gpu(inp), oracle_full(inp), TOL["bf16"])
 
 
 def test_zero_decay():
