@@ -1307,24 +1307,40 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         f32x16 st[NP];                 // S^T: [column token ct*32 + crow(e)][row rt*32 + lane%32]
 #pragma unroll
         for (int u = 0; u < NP; ++u) zero(st[u]);
-        // The B fragments of k-step ks+1 are read while the MFMAs of step ks
+        // The B fragments of k-step ks+BPD are read while the MFMAs of step ks
         // run (scheduling barriers keep the compiler from serializing each
         // read with its MFMA to save registers).
-        bf16x8_t bf[2][NP];
+        constexpr int BPD = 1;
+        bf16x8_t bf[BPD + 1][NP];
 #pragma unroll
-        for (int u = 0; u < NP; ++u) bf[0][u] = frag_rows_sw<D>(Bt[u], fo, 0, 0);
+        for (int ks = 0; ks < BPD; ++ks)
+#pragma unroll
+            for (int u = 0; u < NP; ++u) bf[ks][u] = frag_rows_sw<D>(Bt[u], fo, 0, ks * 16);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             __builtin_amdgcn_sched_barrier(0);
-            if (ks + 1 < KS) {
+            if (ks + BPD < KS) {
 #pragma unroll
                 for (int u = 0; u < NP; ++u)
-                    bf[(ks + 1) & 1][u] = frag_rows_sw<D>(Bt[u], fo, 0, (ks + 1) * 16);
+                    bf[(ks + BPD) % (BPD + 1)][u] = frag_rows_sw<D>(Bt[u], fo, 0, (ks + BPD) * 16);
             }
 #pragma unroll
-            for (int u = 0; u < NP; ++u) mma(st[u], bf[ks & 1][u], af[ks]);
+            for (int u = 0; u < NP; ++u) mma(st[u], bf[ks % (BPD + 1)][u], af[ks]);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // S^T Cv: NJ MFMAs, each with its own Cv fragment (two transpose
+        // reads); the fragments are read CPD MFMAs ahead of their use, the
+        // first ones while the score tiles are masked and converted.
+        constexpr int NJ = NDT * NP * 2, CPD = 4;
+        // (MFMA j: feature tile j % NDT, score tile and half q = j / NDT, so
+        // that consecutive MFMAs accumulate into different tiles)
+        auto cv_frag = [&](int j) __attribute__((always_inline)) {
+            const int nt = j / (NP * 2), u = (j >> 1) % NP, kh = j & 1;
+            return frag_cols_sw<D, true>(Bt[u] + TILE, fo, kh * 16, nt * 32);
+        };
+        bf16x8_t cf[CPD];
+#pragma unroll
+        for (int j = 0; j < CPD; ++j) cf[j] = cv_frag(j);
         bf16x8_t s0[NP], s1[NP];
 #pragma unroll
         for (int u = 0; u < NP; ++u) {
@@ -1344,30 +1360,49 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
                           st[u][15]);
         }
 #pragma unroll
-        for (int nt = 0; nt < NDT; ++nt) {
-#pragma unroll
-            for (int u = 0; u < NP; ++u) {
-                const bf16 *Vt = Bt[u] + TILE;
-                mma(acc[nt], frag_cols_sw<D, true>(Vt, fo, 0, nt * 32), s0[u]);
-                mma(acc[nt], frag_cols_sw<D, true>(Vt, fo, 16, nt * 32), s1[u]);
-            }
+        for (int j = 0; j < NJ; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int nt = j / (NP * 2), u = (j >> 1) % NP;
+            mma(acc[nt], cf[j % CPD], (j & 1) ? s1[u] : s0[u]);
+            if (j + CPD < NJ) cf[j % CPD] = cv_frag(j + CPD);
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
-    // state += (scaled U)^T W over the tokens of column tile ct
-    auto state_update = [&](const bf16 *Bt, int ct, int Ct) __attribute__((always_inline)) {
+    // state += (scaled U)^T W over the tokens of the group's column tiles.
+    // Steps (column tile, 16-token half): the W fragment is shared by the
+    // wave's state tiles (they have the same column block ni), each tile reads
+    // its own U fragment; the fragments of step j+1 are read while the MFMAs
+    // of step j run.  Tiles past the chunk end are masked to zero by the
+    // scaling path (their LDS slots hold clamped, valid rows).
+    static_assert(NW % NDT == 0, "state tiles of one wave must share their column block");
+    auto state_updates = [&](const bf16 *BG, auto G, int Ct) __attribute__((always_inline)) {
+        constexpr int g = decltype(G)::value;
+        constexpr int NSU = NG * 2;
         const FragOffs<D> fo = opaque(fo0);
         const int lz = opaque_lane();
         const int lg = lz >> 5;
-        const bf16 *Ut = Bt + (u_is_b ? 0 : TILE), *Wt = Bt + (u_is_b ? TILE : 0);
-        const bool scale = decay || (ct + 1) * 32 > Ct;
+        const int ni = w % NDT;
+        bf16x8_t wf[2], uf[2][STW];
+        auto fetch = [&](int j, bf16x8_t &wd, bf16x8_t *ud) __attribute__((always_inline)) {
+            const bf16 *Bt = BG + (j >> 1) * 2 * TILE;
+            const bf16 *Ut = Bt + (u_is_b ? 0 : TILE), *Wt = Bt + (u_is_b ? TILE : 0);
+            const int kk = j & 1;
+            wd = frag_cols_sw<D, false>(Wt, fo, kk * 16, ni * 32);
 #pragma unroll
-        for (int k = 0; k < STW; ++k) {
-            const int tl = w + k * NW;
-            if (tl < NSTT) {
-                const int mi = tl / NDT, ni = tl % NDT;
+            for (int k = 0; k < STW; ++k)
+                if (w + k * NW < NSTT) ud[k] = frag_cols_sw<D, false>(Ut, fo, kk * 16, ((w + k * NW) / NDT) * 32);
+        };
+        fetch(0, wf[0], uf[0]);
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    bf16x8_t ua = frag_cols_sw<D, false>(Ut, fo, kk * 16, mi * 32);
+        for (int j = 0; j < NSU; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (j + 1 < NSU) fetch(j + 1, wf[(j + 1) & 1], uf[(j + 1) & 1]);
+            const int ct = Cfg::group_tile(g, j >> 1), kk = j & 1;
+            const bool scale = decay || (ct + 1) * 32 > Ct;
+#pragma unroll
+            for (int k = 0; k < STW; ++k) {
+                if (w + k * NW < NSTT) {
+                    bf16x8_t ua = uf[j & 1][k];
                     if (scale) {
                         float f[8];
                         load16((const bf16 *)&ua, f);
@@ -1379,10 +1414,11 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
                         }
                         ua = pack8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
                     }
-                    mma(sacc[k], ua, frag_cols_sw<D, false>(Wt, fo, kk * 16, ni * 32));
+                    mma(sacc[k], ua, wf[j & 1]);
                 }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
     // one group of column tiles: pair products, then after_pairs(), then the
     // state updates
@@ -1415,13 +1451,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
             }
         }
         after_pairs();
-        if (upd) {
-#pragma unroll 1
-            for (int k = 0; k < NG; ++k) {
-                const int ct = Cfg::group_tile(g, k);
-                if (ct * 32 < Ct) state_update(BG + k * 2 * TILE, ct, Ct);
-            }
-        }
+        if (upd) state_updates(BG, G, Ct);
     };
 
 #pragma unroll 1
@@ -1442,18 +1472,26 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         if constexpr (!TOT) {
 #pragma unroll
             for (int nt = 0; nt < NDT; ++nt) zero(acc[nt]);
+            // MFMA j = (k-step j / NDT, feature tile j % NDT): consecutive MFMAs
+            // accumulate into different tiles; fragments are read XPD ahead
             auto inter = [&](auto XT) __attribute__((always_inline)) {
                 const FragOffs<D> fo = opaque(fo0);
+                constexpr int NJ = NDT * KS, XPD = 4;
+                auto x_frag = [&](int j) __attribute__((always_inline)) {
+                    const int ks = j / NDT, nt = j % NDT;
+                    return decltype(XT)::value ? frag_cols_sw<D, false>(XS, fo, ks * 16, nt * 32)
+                                               : frag_rows_sw<D>(XS, fo, nt * 32, ks * 16);
+                };
+                bf16x8_t xf[XPD];
 #pragma unroll
-                for (int nt = 0; nt < NDT; ++nt) {
-                    bf16x8_t xf[KS];
+                for (int j = 0; j < XPD; ++j) xf[j] = x_frag(j);
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        xf[ks] = decltype(XT)::value ? frag_cols_sw<D, false>(XS, fo, ks * 16, nt * 32)
-                                                     : frag_rows_sw<D>(XS, fo, nt * 32, ks * 16);
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) mma(acc[nt], xf[ks], af[ks]);
+                for (int j = 0; j < NJ; ++j) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma(acc[j % NDT], xf[j % XPD], af[j / NDT]);
+                    if (j + XPD < NJ) xf[j % XPD] = x_frag(j + XPD);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             };
             if (rt >= 0 && rt * 32 < Ct) {
                 if (xt)
@@ -1496,8 +1534,11 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         // after them is known.
         if constexpr (!TOT) {
             const int lz = opaque_lane();
+            // (rt is wave-uniform: read it as a scalar, so that the descriptor
+            // lives in scalar registers as buffer stores require)
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                Out + (int64_t)t * p.C * D, 0, rt >= 0 ? Ct * D * 2 : 0, 0x00020000);
+                Out + (int64_t)t * p.C * D, 0,
+                __builtin_amdgcn_readfirstlane(rt >= 0 ? Ct * D * 2 : 0), 0x00020000);
             const int off = ((rt * 32 + (lz & 31)) * D + (lz >> 5) * 8) * 2;   // negative: dropped
             const unsigned neg = sub ? 0x80008000u : 0u;                          // bf16 sign bits
 #pragma unroll
