@@ -1151,7 +1151,9 @@ enum SweepKind {
 // boundary (LASP-2's chunk states M_t, resp. dM_t, accumulated with their decay
 // over the segment: Z = sum_t lambda^(tokens after chunk t) M_t); they feed the
 // cross-segment scan.  They use the same token-tile pipeline as the outputs.
-template <int D, int C, int KIND>
+// DEC = false: the call has no decay array (every lambda is 1); the decay
+// arithmetic is compiled out.
+template <int D, int C, int KIND, bool DEC>
 __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     constexpr bool TOT = KIND >= SWEEP_TOT_F;
     constexpr int role0 = KIND == SWEEP_GRADS ? 1 : (KIND == SWEEP_TOT_B ? 2 : 0);
@@ -1182,8 +1184,8 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
     const int nch = t1 - t0;
     if (nch <= 0) return;
-    const float l2 = head_log2_decay(p, h);
-    const bool decay = l2 != 0.f;
+    const float l2 = DEC ? head_log2_decay(p, h) : 0.f;
+    const bool decay = DEC && l2 != 0.f;
     const bool sub = role == 1 && !decay;      // dQ by subtraction, walked backwards
     const bool rev = role >= 2 || sub;         // chunks swept backwards
     const int dmin = sub ? 1 : 0;              // causal range: dist(r, c) >= dmin
@@ -1507,7 +1509,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
                 for (int nt = 0; nt < NDT; ++nt) acc[nt] *= sc;
             }
         }
-        if (upd) {
+        if (upd && decay) {
             const float dc = dpow(l2, (float)Ct);
 #pragma unroll
             for (int k = 0; k < STW; ++k) sacc[k] *= dc;
@@ -1636,8 +1638,11 @@ static hipError_t bwd_impl(const Params &p, hipStream_t st, hipEvent_t *ev) {
 template <int D, int C, int KIND>
 static void sweep_launch(const Params &p, hipStream_t st) {
     const int roles = KIND == SWEEP_GRADS ? 3 : 1;
-    hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND>), dim3(round8(p.n_segs_ub * p.H * roles)),
-                       dim3(SweepCfg<C>::NT), 0, st, p);
+    const dim3 grid(round8(p.n_segs_ub * p.H * roles)), block(SweepCfg<C>::NT);
+    if (p.decay)
+        hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND, true>), grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND, false>), grid, block, 0, st, p);
 }
 
 template <int D, int KIND>
