@@ -1141,22 +1141,15 @@ template <int C> struct SweepCfg {
 // What one launch computes:
 enum SweepKind {
     SWEEP_OUT = 0,     // role 0 (O)
-    SWEEP_GRADS = 1,   // roles 1-3 (dQ, dV, dK), neighbours in launch order so
+    SWEEP_GRADS = 1    // roles 1-3 (dQ, dV, dK), neighbours in launch order so
                        // that the roles of one segment run at the same time and
                        // share their reads of Q, K, V, dO in L2
-    SWEEP_TOT_F = 2,   // segment totals Z of the forward state recursion
-    SWEEP_TOT_B = 3    // segment totals W of the backward state recursion
 };
-// The totals are the state recursion alone, started from zero at the segment
-// boundary (LASP-2's chunk states M_t, resp. dM_t, accumulated with their decay
-// over the segment: Z = sum_t lambda^(tokens after chunk t) M_t); they feed the
-// cross-segment scan.  They use the same token-tile pipeline as the outputs.
 // DEC = false: the call has no decay array (every lambda is 1); the decay
 // arithmetic is compiled out.
 template <int D, int C, int KIND, bool DEC>
 __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
-    constexpr bool TOT = KIND >= SWEEP_TOT_F;
-    constexpr int role0 = KIND == SWEEP_GRADS ? 1 : (KIND == SWEEP_TOT_B ? 2 : 0);
+    constexpr int role0 = KIND == SWEEP_GRADS ? 1 : 0;
     constexpr int nroles = KIND == SWEEP_GRADS ? 3 : 1;
     using Cfg = SweepCfg<C>;
     constexpr int NCT = Cfg::NCT, NW = Cfg::NW, NG = Cfg::NG;
@@ -1167,7 +1160,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     constexpr int CPW = (NIG + NW - 1) / NW;           // copies per wave per group (at most)
     constexpr int NSTT = NDT * NDT;                    // 32x32 state tiles
     constexpr int STW = (NSTT + NW - 1) / NW;
-    __shared__ __attribute__((aligned(16))) bf16 XS[TOT ? 8 : D * D];
+    __shared__ __attribute__((aligned(16))) bf16 XS[D * D];
     // B and Cv tiles of the two groups.  Two distinct arrays: the compiler
     // then sees that copies in flight into one group's slots do not alias
     // reads of the other's, and does not wait for them.
@@ -1260,14 +1253,14 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     // ---- prologue: first chunk's A rows and first group, incoming state ----
     bf16x8_t af[KS];
     dma_group(0, IC<0>());
-    if (!TOT) load_a(0, af);
+    load_a(0, af);
 
     f32x16 sacc[STW];
 #pragma unroll
     for (int k = 0; k < STW; ++k) {
         const int tl = w + k * NW;
         zero(sacc[k]);
-        if (!TOT && tl < NSTT) {
+        if (tl < NSTT) {
             const int mi = tl / NDT, ni = tl % NDT, lc = l & 31, lg = l >> 5;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1278,7 +1271,6 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         }
     }
     auto write_state = [&]() __attribute__((always_inline)) {   // XS[col feature][row feature] = bf16(state)
-        if (TOT) return;
         const int lz = opaque_lane();
         const int lc = lz & 31, lg = lz >> 5;
 #pragma unroll
@@ -1427,7 +1419,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     auto run_group = [&](auto G, int Ct, bool upd, auto after_pairs) __attribute__((always_inline)) {
         constexpr int g = decltype(G)::value;
         const bf16 *BG = g == 0 ? BG0 : BG1;
-        if (!TOT && rt >= 0 && rt * 32 < Ct) {
+        if (rt >= 0 && rt * 32 < Ct) {
             // the group's causal tiles, two at a time
             int need = 0;
 #pragma unroll
@@ -1459,19 +1451,20 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
 #pragma unroll 1
     for (int i = 0; i < nch; ++i) {
         const int t = chunk_t(i), Ct = chunk_len(t);
-        // (the state after the segment's last chunk is needed only as a total)
-        const bool upd = TOT || i + 1 < nch;
+        // (the state after the segment's last chunk is not needed: the segment
+        // totals come from their own kernel)
+        const bool upd = i + 1 < nch;
         // chunk start: this chunk's first group and A rows have landed (only the
         // previous chunk's NDT*2 output stores, issued after them, may still be
         // in flight), every wave has published the state into XS
-        if (!TOT && i > 0)
+        if (i > 0)
             LASP_WAIT_VM(NDT * 2);
         else
             LASP_WAIT_VM(0);
         lds_barrier();
         dma_group(i, IC<1>());         // slots of the second group are free now
         // inter-chunk term: acc = (A X)^T, rows scaled by lambda^e(r)
-        if constexpr (!TOT) {
+        {
 #pragma unroll
             for (int nt = 0; nt < NDT; ++nt) zero(acc[nt]);
             // MFMA j = (k-step j / NDT, feature tile j % NDT): consecutive MFMAs
@@ -1523,7 +1516,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         // the next chunk's A rows go into af once this chunk's pair products
         // have read it; the state updates and stores hide their latency
         run_group(IC<1>(), Ct, upd, [&]() __attribute__((always_inline)) {
-            if (!TOT && i + 1 < nch) load_a(i + 1, af);
+            if (i + 1 < nch) load_a(i + 1, af);
         });
         // rows out: lane holds row rt*32 + lane%32, features nt*32 + 8j + 4*(lane/32) + [0,4).
         // Lanes l and l+32 exchange halves (permlane32 swap) so that each lane
@@ -1534,7 +1527,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         // rows): the hardware drops stores past its end, so every wave issues
         // the same NDT*2 stores and the count of memory operations in flight
         // after them is known.
-        if constexpr (!TOT) {
+        {
             const int lz = opaque_lane();
             // (rt is wave-uniform: read it as a scalar, so that the descriptor
             // lives in scalar registers as buffer stores require)
@@ -1569,19 +1562,148 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         }
         if (upd) write_state();
     }
-    if constexpr (TOT) {   // the segment total, [dv][dk] like the scanned states
-        float *tot = (KIND == SWEEP_TOT_F ? p.Z : p.W) + seg_off;
+}
+
+
+// ---------------------------------------------------------------------------
+// Segment totals (bf16): per (segment, head), the state recursion of the
+// segment started from zero, which collapses to one weighted contraction over
+// the segment's tokens tau = 0 .. L-1:
+//   forward  Z = sum_tau lambda^(L-1-tau) k_tau^T v_tau      (LASP-2's M_t, Eq. 10)
+//   backward W = sum_tau lambda^(tau+1)   q_tau^T dO_tau     (LASP Eq. 20)
+// stored [dv][dk] like the scanned states.  The chunking does not enter, so
+// the kernel streams steps of TPS 32-token tiles of U (K or Q) and W (V or dO)
+// through a ring of LDS slots, NSLOT-1 steps in flight: the work per tile is
+// small and the kernel lives on memory parallelism.  Each wave owns the same
+// 32x32 state tiles as in the sweep and accumulates (scaled U)^T W with the
+// same fragment reads.
+// ---------------------------------------------------------------------------
+template <int D> struct SegTotCfg {
+    static constexpr int NW = 8, NT = 64 * NW;
+    static constexpr int TILE = 32 * D;                            // elements of one 32-token tile
+    static constexpr int TPS = 2;                                  // tiles per step (one barrier each)
+    static constexpr int SLOT = 2 * TILE * TPS;                    // U tiles, W tiles of one step
+    static constexpr int NSLOT = (160 * 1024) / (SLOT * 2);        // slots in 160 KiB of LDS
+    static constexpr int CPT = TILE / 512;                         // 1 KiB wave copies per tile
+    static constexpr int CPS = 2 * CPT * TPS;                      // copies per slot
+    static constexpr int CPW = (CPS + NW - 1) / NW;                // copies per wave per slot (at most)
+};
+
+enum TotKind { TOT_F = 0, TOT_B = 1 };   // forward Z, backward W
+
+template <int D, int KIND, bool DEC>
+__global__ __launch_bounds__(SegTotCfg<D>::NT) void k_segtot_bf16(Params p) {
+    using Cfg = SegTotCfg<D>;
+    constexpr int NW = Cfg::NW, TILE = Cfg::TILE, TPS = Cfg::TPS, SLOT = Cfg::SLOT;
+    constexpr int NSLOT = Cfg::NSLOT, CPT = Cfg::CPT, CPS = Cfg::CPS, CPW = Cfg::CPW;
+    constexpr int PR = D / 8, NDT = D / 32, NSTT = NDT * NDT, STW = (NSTT + NW - 1) / NW;
+    constexpr bool BWD = KIND == TOT_B;
+    static_assert(NW % NDT == 0, "state tiles of one wave must share their column block");
+    // the wait below keeps (NSLOT - 2) slots of copies of this wave in flight
+    static_assert((NSLOT - 2) * CPW <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) bf16 ring[NSLOT * SLOT];
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = lid % p.H, gs = lid / p.H;
+    Seq s;
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    if (t1 <= t0) return;
+    const int tok0 = t0 * p.C;                                     // first token of the segment
+    const int L = min(t1 * p.C, s.len) - tok0;                     // tokens in the segment
+    const int nsteps = (L + 32 * TPS - 1) / (32 * TPS);
+    const float l2 = DEC ? head_log2_decay(p, h) : 0.f;
+    const bool decay = DEC && l2 != 0.f;
+    const int64_t rbase = row_base(p, s, h) + tok0;
+    const bf16 *U = (const bf16 *)(BWD ? p.Q : p.K) + rbase * D;
+    const bf16 *Wm = (const bf16 *)(BWD ? p.dO : p.V) + rbase * D;
+
+    const int w = wave_id(), l = lane_id();
+    const FragOffs<D> fo0 = frag_offs<D>(l);
+    f32x16 sacc[STW];
 #pragma unroll
-        for (int k = 0; k < STW; ++k) {
-            const int tl = w + k * NW;
-            if (tl < NSTT) {
-                const int mi = tl / NDT, ni = tl % NDT, lc = l & 31, lg = l >> 5;
+    for (int k = 0; k < STW; ++k) zero(sacc[k]);
+
+    // step j: tiles TPS j .. TPS j + TPS - 1 (swizzled rows, rows past L
+    // clamped to a valid row) into ring slot j % NSLOT, as [tile][U, W]
+    auto issue = [&](int j) __attribute__((always_inline)) {
+        int lz = l;
+        asm volatile("" : "+v"(lz));
+        bf16 *dst = ring + (j % NSLOT) * SLOT;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(float4 *)(tot + (int64_t)(ni * 32 + lc) * D + mi * 32 + q * 8 + lg * 4) =
-                        make_float4(sacc[k][q * 4 + 0], sacc[k][q * 4 + 1], sacc[k][q * 4 + 2],
-                                    sacc[k][q * 4 + 3]);
+        for (int k = 0; k < CPW; ++k) {
+            const int jj = w + k * NW;
+            if (CPS % NW == 0 || jj < CPS) {
+                const int q = jj / (2 * CPT), half = (jj / CPT) & 1, pc0 = jj % CPT;
+                const int slot = pc0 * 64 + lz;
+                const int r = slot / PR, pc = (slot % PR) ^ sw_key<D>(r);
+                const int row = min((j * TPS + q) * 32 + r, L - 1);
+                dma16((half ? Wm : U) + (int64_t)row * D + pc * 8,
+                      dst + q * 2 * TILE + half * TILE + pc0 * 512);
             }
+        }
+    };
+    // state += (scaled U)^T W over 32-token tile tq of the segment, at Ut, Wt
+    auto update = [&](const bf16 *Ut, const bf16 *Wt, int tq) __attribute__((always_inline)) {
+        const FragOffs<D> fo = opaque(fo0);
+        int lz = l;
+        asm volatile("" : "+v"(lz));
+        const int lg = lz >> 5, ni = w % NDT;
+        const bool scale = decay || (tq + 1) * 32 > L;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8_t wf = frag_cols_sw<D, false>(Wt, fo, kk * 16, ni * 32);
+#pragma unroll
+            for (int k = 0; k < STW; ++k) {
+                if (w + k * NW < NSTT) {
+                    bf16x8_t ua = frag_cols_sw<D, false>(Ut, fo, kk * 16, ((w + k * NW) / NDT) * 32);
+                    if (scale) {
+                        float f[8];
+                        load16((const bf16 *)&ua, f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int tau = tq * 32 + kk * 16 + lg * 8 + e;
+                            const float sc = decay ? dpow(l2, (float)(BWD ? tau + 1 : L - 1 - tau)) : 1.f;
+                            f[e] = tau < L ? f[e] * sc : 0.f;
+                        }
+                        ua = pack8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+                    }
+                    mma(sacc[k], ua, wf);
+                }
+            }
+        }
+    };
+
+#pragma unroll 1
+    for (int j = 0; j < NSLOT - 1 && j < nsteps; ++j) issue(j);
+
+#pragma unroll 1
+    for (int j = 0; j < nsteps; ++j) {
+        // step j has landed: this wave's copies of later steps may still be in flight
+        if (j + NSLOT - 2 < nsteps)
+            LASP_WAIT_VM((NSLOT - 2) * CPW);
+        else
+            LASP_WAIT_VM(0);
+        lds_barrier();
+        // every wave is done with step j-1: its slot takes step j + NSLOT - 1
+        if (j + NSLOT - 1 < nsteps) issue(j + NSLOT - 1);
+        const bf16 *Sl = ring + (j % NSLOT) * SLOT;
+#pragma unroll
+        for (int q = 0; q < TPS; ++q) update(Sl + q * 2 * TILE, Sl + q * 2 * TILE + TILE, j * TPS + q);
+    }
+
+    float *tot = (BWD ? p.W : p.Z) + ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
+#pragma unroll
+    for (int k = 0; k < STW; ++k) {
+        const int tl = w + k * NW;
+        if (tl < NSTT) {
+            const int mi = tl / NDT, ni = tl % NDT, lc = l & 31, lg = l >> 5;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *(float4 *)(tot + (int64_t)(ni * 32 + lc) * D + mi * 32 + q * 8 + lg * 4) =
+                    make_float4(sacc[k][q * 4 + 0], sacc[k][q * 4 + 1], sacc[k][q * 4 + 2],
+                                sacc[k][q * 4 + 3]);
         }
     }
 }
@@ -1634,7 +1756,7 @@ static hipError_t bwd_impl(const Params &p, hipStream_t st, hipEvent_t *ev) {
     return hipGetLastError();
 }
 
-// bf16: segment totals (transpose-read local kernel), segment scan, sweep.
+// bf16: segment totals, segment scan, sweep.
 template <int D, int C, int KIND>
 static void sweep_launch(const Params &p, hipStream_t st) {
     const int roles = KIND == SWEEP_GRADS ? 3 : 1;
@@ -1643,6 +1765,15 @@ static void sweep_launch(const Params &p, hipStream_t st) {
         hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND, true>), grid, block, 0, st, p);
     else
         hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND, false>), grid, block, 0, st, p);
+}
+
+template <int D, int KIND>
+static void segtot_launch(const Params &p, hipStream_t st) {
+    const dim3 grid(round8(p.n_segs_ub * p.H)), block(SegTotCfg<D>::NT);
+    if (p.decay)
+        hipLaunchKernelGGL((k_segtot_bf16<D, KIND, true>), grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL((k_segtot_bf16<D, KIND, false>), grid, block, 0, st, p);
 }
 
 template <int D, int KIND>
@@ -1658,7 +1789,7 @@ template <int D>
 static hipError_t fwd_bf16(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
     if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
     rec(ev, 0, st);
-    sweep_dispatch<D, SWEEP_TOT_F>(p, st);
+    segtot_launch<D, TOT_F>(p, st);
     rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     hipLaunchKernelGGL((k_fwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
@@ -1672,7 +1803,7 @@ template <int D>
 static hipError_t bwd_bf16(const Params &p, hipStream_t st, hipEvent_t *ev) {
     if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
     rec(ev, 0, st);
-    sweep_dispatch<D, SWEEP_TOT_B>(p, st);
+    segtot_launch<D, TOT_B>(p, st);
     rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     hipLaunchKernelGGL((k_bwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
