@@ -50,13 +50,28 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl) {
     const int64_t per_seq_chunks = ((int64_t)s->N + s->chunk - 1) / s->chunk;
     int64_t chunks_ub = pl.varlen ? (int64_t)s->N / s->chunk + s->nseq
                                   : per_seq_chunks * (int64_t)s->B;
-    // Segments: about 1024 (segment, head) workgroups per role (four per CU of
-    // the 256 on MI355X, one resident at a time), and as few segment states as
-    // that allows, which keeps the local-total and cross-segment-scan kernels
-    // cheap (measured at B1 H32 N131072 C256: G = 4, 8, 16 -> 5.28, 5.09,
-    // 4.99 ms per forward+backward).
-    int64_t g = chunks_ub * s->H / 1024;
-    pl.G = (int)(g < 2 ? 2 : (g > 16 ? 16 : g));
+    // Segments of G chunks: one sweep workgroup each per (segment, head, role),
+    // one resident per CU (256 CUs on MI355X), each taking a time about
+    // G + 2 chunks (the 2: its start-up).  G minimizes (G + 2) x (rounds of the
+    // one-role launches + rounds of the three-role backward launch), the
+    // larger G on ties (fewer segment states, cheaper scans).  Packed batches
+    // count one extra partial segment per sequence.  Measured at B1 H32 N131072 C256:
+    // G = 16, 32, 48, 64 -> 4.30, 4.24, 5.09, 4.25 ms per forward+backward
+    // (48 leaves the second round nearly empty).
+    {
+        const int64_t seqs = pl.varlen ? 1 : s->B;
+        const int64_t T = pl.varlen ? chunks_ub : per_seq_chunks;   // chunks per sequence (packed: all)
+        const int64_t extra = pl.varlen ? s->nseq : 0;              // packed: one partial segment per sequence
+        int64_t best_cost = -1;
+        for (int g = 1; g <= 256; ++g) {
+            const int64_t wg = seqs * s->H * ((T + g - 1) / g + extra);
+            const int64_t cost = (int64_t)(g + 2) * ((wg + 255) / 256 + (3 * wg + 255) / 256);
+            if (best_cost < 0 || cost <= best_cost) {
+                best_cost = cost;
+                pl.G = g;
+            }
+        }
+    }
     // Test hook: LASP_SEGMENT_CHUNKS overrides G (must be the same for the
     // forward and backward calls that share a state cache).
     if (const char *e = getenv("LASP_SEGMENT_CHUNKS")) {
