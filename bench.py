@@ -55,16 +55,19 @@ def elapsed(L, a, b):
     return ms.value
 
 
-def kernel_work(sh, local_b, seg_b):
+def kernel_work(sh, local_b, seg_b, fin_b):
     """Algorithmic HBM bytes and flops per launch of every kernel of a step.
 
-    U = token-heads, e = element bytes; local_b / seg_b: bytes of the per-chunk
-    (element type, none for bf16) and per-segment (float32) state arrays, from
-    the library's size queries.  Bytes count every distinct array once:
+    U = token-heads, e = element bytes; local_b / seg_b / fin_b: bytes of the
+    per-chunk (element type, none for bf16), per-segment (float32) and
+    per-sequence final (float32, bf16 only) state arrays, from the library's
+    size queries.  Bytes count every distinct array once:
       local  : reads 2 token arrays (K,V resp. Q,dO), writes the local states
-      scan   : reads and writes the segment states, M_in/M_out (dM_out/dM_in)
+      scan   : reads and writes the segment states, M_in/M_out (dM_out/dM_in),
+               writes the final states
       out    : reads Q,K,V and the segment states, writes O
-      grads  : reads Q,K,V,dO and both segment-state arrays, writes dQ,dK,dV
+      grads  : reads Q,K,V,dO, both segment-state arrays and the final states,
+               writes dQ,dK,dV
     Flops count the useful causal work per token-head and output role: the
     intra-chunk products over c <= r (2d(C+1) on average: QK^T and SV), the
     inter-chunk product A.X (2d^2) and the state update (2d^2)."""
@@ -76,11 +79,11 @@ def kernel_work(sh, local_b, seg_b):
     role = U * (2 * d * (C + 1) + 4 * d * d)      # one output role (O, dQ, dK or dV)
     return {
         "fwd_local": (2 * U * d * e + local_b + seg_b, 2 * U * d * d),
-        "fwd_scan": (2 * seg_b + 2 * st_io, seg_b // 2),
+        "fwd_scan": (2 * seg_b + 2 * st_io + fin_b, seg_b // 2),
         "fwd_out": (4 * U * d * e + local_b + seg_b, role),
         "bwd_local": (2 * U * d * e + local_b + seg_b, 2 * U * d * d),
         "bwd_scan": (2 * seg_b + 2 * st_io, seg_b // 2),
-        "bwd_grads": (7 * U * d * e + 2 * local_b + 2 * seg_b, 3 * role),
+        "bwd_grads": (7 * U * d * e + 2 * local_b + 2 * seg_b + fin_b, 3 * role),
     }
 
 
@@ -207,11 +210,13 @@ def main():
         step_ms.append(elapsed(L, evf[i][0], evb[i][3]))
     step_ms.sort()
 
-    # state array sizes (fwd workspace with a cache = tables + per-segment states)
+    # state array sizes (fwd workspace with a cache = tables + per-segment states;
+    # state cache = per-chunk states + per-segment states + final states)
     table_b = 0 if not sh["nseq"] else -(-8 * (sh["nseq"] + 1) // 256) * 256
     seg_b = cca.fwd_workspace_bytes(S, dt_code, True) - table_b
-    local_b = cca.state_cache_bytes(S, dt_code) - seg_b
-    work = kernel_work(sh, local_b, seg_b)
+    fin_b = 0 if sh["dtype"] != "bf16" else -(-(sh["nseq"] or sh["B"]) * sh["H"] * sh["d"] ** 2 * 4 // 256) * 256
+    local_b = cca.state_cache_bytes(S, dt_code) - seg_b - fin_b
+    work = kernel_work(sh, local_b, seg_b, fin_b)
     dom = max(names, key=lambda k: kms[k])
     bytes_, flops = work[dom]
     t_dom = kms[dom] * 1e-3
