@@ -1182,7 +1182,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     const bool sub = role == 1 && !decay;      // dQ by subtraction, walked backwards
     const bool rev = role >= 2 || sub;         // chunks swept backwards
     const int dmin = sub ? 1 : 0;              // causal range: dist(r, c) >= dmin
-    const bool xt = role & 1;                  // state operand read transposed
+    const bool xt = role & 1;                  // the role uses X^T: state tiles accumulated transposed
     const bool u_is_b = !(role & 1);           // state rows from B (else from Cv)
     const int64_t rbase = row_base(p, s, h);
     const bf16 *Qg = (const bf16 *)p.Q + rbase * D, *Kg = (const bf16 *)p.K + rbase * D;
@@ -1262,25 +1262,35 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         zero(sacc[k]);
         if (tl < NSTT) {
             const int mi = tl / NDT, ni = tl % NDT, lc = l & 31, lg = l >> 5;
+            if (xt) {   // transposed tile: rows W features, lanes U features
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 v = *(const float4 *)(seg + (int64_t)(ni * 32 + lc) * D + mi * 32 + q * 8 + lg * 4);
-                sacc[k][q * 4 + 0] = sgn * v.x; sacc[k][q * 4 + 1] = sgn * v.y;
-                sacc[k][q * 4 + 2] = sgn * v.z; sacc[k][q * 4 + 3] = sgn * v.w;
+                for (int e = 0; e < 16; ++e)
+                    sacc[k][e] = sgn * seg[(int64_t)(ni * 32 + crow(e, l)) * D + mi * 32 + lc];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *(const float4 *)(seg + (int64_t)(ni * 32 + lc) * D + mi * 32 + q * 8 + lg * 4);
+                    sacc[k][q * 4 + 0] = sgn * v.x; sacc[k][q * 4 + 1] = sgn * v.y;
+                    sacc[k][q * 4 + 2] = sgn * v.z; sacc[k][q * 4 + 3] = sgn * v.w;
+                }
             }
         }
     }
-    auto write_state = [&]() __attribute__((always_inline)) {   // XS[col feature][row feature] = bf16(state)
+    // XS = bf16(state) as the inter-chunk product's row operand: [W feature][U
+    // feature] (the state's memory layout), or its transpose for the roles that
+    // use X^T (their state tiles are accumulated transposed, so the same lane
+    // pattern writes the transpose)
+    auto write_state = [&]() __attribute__((always_inline)) {
         const int lz = opaque_lane();
         const int lc = lz & 31, lg = lz >> 5;
 #pragma unroll
         for (int k = 0; k < STW; ++k) {
             const int tl = w + k * NW;
             if (tl < NSTT) {
-                const int mi = tl / NDT, ni = tl % NDT;
+                const int rb = xt ? tl / NDT : tl % NDT, cb = xt ? tl % NDT : tl / NDT;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    store4(XS + sw_off<D>(ni * 32 + lc, mi * 32 + q * 8 + lg * 4), sacc[k][q * 4 + 0],
+                    store4(XS + sw_off<D>(rb * 32 + lc, cb * 32 + q * 8 + lg * 4), sacc[k][q * 4 + 0],
                            sacc[k][q * 4 + 1], sacc[k][q * 4 + 2], sacc[k][q * 4 + 3]);
             }
         }
@@ -1369,8 +1379,9 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     // of step j run.  Tiles past the chunk end are masked to zero by the
     // scaling path (their LDS slots hold clamped, valid rows).
     static_assert(NW % NDT == 0, "state tiles of one wave must share their column block");
-    auto state_updates = [&](const bf16 *BG, auto G, int Ct) __attribute__((always_inline)) {
+    auto state_updates = [&](const bf16 *BG, auto G, int Ct, auto XTC) __attribute__((always_inline)) {
         constexpr int g = decltype(G)::value;
+        constexpr bool XT = decltype(XTC)::value;   // accumulate the tiles transposed
         constexpr int NSU = NG * 2;
         const FragOffs<D> fo = opaque(fo0);
         const int lz = opaque_lane();
@@ -1408,7 +1419,10 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
                         }
                         ua = pack8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
                     }
-                    mma(sacc[k], ua, wf[j & 1]);
+                    if (XT)
+                        mma(sacc[k], wf[j & 1], ua);
+                    else
+                        mma(sacc[k], ua, wf[j & 1]);
                 }
             }
         }
@@ -1445,7 +1459,12 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
             }
         }
         after_pairs();
-        if (upd) state_updates(BG, G, Ct);
+        if (upd) {
+            if (xt)
+                state_updates(BG, G, Ct, IC<1>());
+            else
+                state_updates(BG, G, Ct, IC<0>());
+        }
     };
 
 #pragma unroll 1
@@ -1469,13 +1488,13 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
             for (int nt = 0; nt < NDT; ++nt) zero(acc[nt]);
             // MFMA j = (k-step j / NDT, feature tile j % NDT): consecutive MFMAs
             // accumulate into different tiles; fragments are read XPD ahead
-            auto inter = [&](auto XT) __attribute__((always_inline)) {
+            // (XS holds the operand in row form for every role: X, or X^T for
+            // the roles whose state tiles are accumulated transposed)
+            auto inter = [&]() __attribute__((always_inline)) {
                 const FragOffs<D> fo = opaque(fo0);
                 constexpr int NJ = NDT * KS, XPD = 4;
                 auto x_frag = [&](int j) __attribute__((always_inline)) {
-                    const int ks = j / NDT, nt = j % NDT;
-                    return decltype(XT)::value ? frag_cols_sw<D, false>(XS, fo, ks * 16, nt * 32)
-                                               : frag_rows_sw<D>(XS, fo, nt * 32, ks * 16);
+                    return frag_rows_sw<D>(XS, fo, (j % NDT) * 32, (j / NDT) * 16);
                 };
                 bf16x8_t xf[XPD];
 #pragma unroll
@@ -1488,12 +1507,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             };
-            if (rt >= 0 && rt * 32 < Ct) {
-                if (xt)
-                    inter(IC<1>());
-                else
-                    inter(IC<0>());
-            }
+            if (rt >= 0 && rt * 32 < Ct) inter();
             const int lz = opaque_lane();
             if (decay && rt >= 0) {
                 const int r = rt * 32 + (lz & 31);
