@@ -29,6 +29,7 @@ __all__ = [
     "sampled_o", "sampled_dq", "sampled_dk", "sampled_dv",
     "closed_m_out", "closed_dm_in",
     "batched_fwd", "batched_bwd",
+    "bidir_fwd", "bidir_bwd", "batched_bidir_fwd", "batched_bidir_bwd",
 ]
 
 
@@ -338,4 +339,72 @@ def batched_bwd(Q, K, V, dO, decay=None, m_in=None, dm_out=None, cu_seqlens=None
             else:
                 raise ValueError(form)
             dQ[b, h, s:e], dK[b, h, s:e], dV[b, h, s:e], dMin[si, h] = r
+    return dQ, dK, dV, dMin
+
+
+# ---------------------------------------------------------------------------
+# 6. The unmasked (bidirectional) form: [LASP] Eq. 3 without Norm, i.e. every
+#    token attends to every token of its sequence; with sequence parallelism
+#    each rank sums all chunk states (LASP-2's M_(1:T), one AllGather and a
+#    sum).  M_in stands for the states of the other ranks' chunks; there is
+#    no decay in this form.
+# ---------------------------------------------------------------------------
+def bidir_fwd(q, k, v, m_in=None):
+    """o_p = sum_i (q_p . k_i) v_i + q_p M_in   over all tokens i    [LASP Eq. 3, left product]
+    M_out = M_in + sum_i k_i^T v_i                                    (the summed state)
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    m = _zeros_state(q.shape[1], m_in)
+    o = (q @ k.T) @ v + q @ m
+    return o, m + k.T @ v
+
+
+def bidir_bwd(q, k, v, do, m_in=None, dm_out=None):
+    """Gradients of l = <dO, O> + <dM_out, M_out> through bidir_fwd, written
+    out from the definition:
+      dq_p  = sum_j (do_p . v_j) k_j + do_p M_in^T
+      dk_j  = sum_p (do_p . v_j) q_p + v_j dM_out^T
+      dv_j  = sum_p (q_p . k_j) do_p + k_j dM_out
+      dM_in = sum_p q_p^T do_p + dM_out
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    d = q.shape[1]
+    m = _zeros_state(d, m_in)
+    dm = _zeros_state(d, dm_out)
+    A = q @ k.T                # A[p, j] = q_p . k_j
+    E = do @ v.T               # E[p, j] = do_p . v_j
+    dq = E @ k + do @ m.T
+    dk = E.T @ q + v @ dm.T
+    dv = A.T @ do + k @ dm
+    dm_in = q.T @ do + dm
+    return dq, dk, dv, dm_in
+
+
+def batched_bidir_fwd(Q, K, V, m_in=None, cu_seqlens=None):
+    """[B, H, N, d] (or packed) driver of bidir_fwd.  Returns (O, M_out [S,H,d,d])."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    B, H, N, d = Q.shape
+    segs = _segments(B, N, cu_seqlens)
+    O = np.zeros(Q.shape[:3] + (V.shape[3],))
+    Mout = np.zeros((len(segs), H, d, V.shape[3]))
+    for si, (b, s, e) in enumerate(segs):
+        for h in range(H):
+            mi = None if m_in is None else m_in[si, h]
+            O[b, h, s:e], Mout[si, h] = bidir_fwd(Q[b, h, s:e], K[b, h, s:e], V[b, h, s:e], mi)
+    return O, Mout
+
+
+def batched_bidir_bwd(Q, K, V, dO, m_in=None, dm_out=None, cu_seqlens=None):
+    """Returns (dQ, dK, dV [B,H,N,d], dM_in [S,H,d,d])."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    B, H, N, d = Q.shape
+    segs = _segments(B, N, cu_seqlens)
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    dMin = np.zeros((len(segs), H, d, V.shape[3]))
+    for si, (b, s, e) in enumerate(segs):
+        for h in range(H):
+            mi = None if m_in is None else m_in[si, h]
+            dmo = None if dm_out is None else dm_out[si, h]
+            dQ[b, h, s:e], dK[b, h, s:e], dV[b, h, s:e], dMin[si, h] = bidir_bwd(
+                Q[b, h, s:e], K[b, h, s:e], V[b, h, s:e], dO[b, h, s:e], mi, dmo)
     return dQ, dK, dV, dMin

@@ -303,3 +303,73 @@ def test_planted_mistakes_fail_the_pins():
     assert ok(good())
     for bad in (transposed_state, dropped_dm_out_term, off_by_one_decay):
         assert not ok(bad()), bad.__name__
+
+
+# --- the unmasked (bidirectional) form ---------------------------------------
+def _bidir_loss(q, k, v, do, m, dm):
+    o, mo = lo.bidir_fwd(q, k, v, m)
+    return float(np.sum(do * o) + np.sum(dm * mo))
+
+
+def test_bidir_is_causal_plus_reversed_causal():
+    """Without a mask every token sees the tokens up to it (the causal oracle,
+    lambda = 1) and the tokens from it on (the causal oracle on the reversed
+    sequence), the diagonal counted once; M_in enters once, M_out is the causal
+    M_out."""
+    q, k, v, do, m, dm = rand_case(23, 5, 31)
+    o, mo = lo.bidir_fwd(q, k, v, m)
+    oc, moc = lo.quadratic_fwd(q, k, v, 1.0, m)
+    orr, _ = lo.quadratic_fwd(q[::-1], k[::-1], v[::-1], 1.0, None)
+    diag = np.sum(q * k, axis=1)[:, None] * v
+    np.testing.assert_allclose(o, oc + orr[::-1] - diag, atol=1e-11)
+    np.testing.assert_allclose(mo, moc, atol=1e-11)
+
+
+def test_bidir_loops_tiny():
+    """Pure-Python double loop over token pairs and features (no matrix products)."""
+    q, k, v, do, m, dm = rand_case(4, 3, 37)
+    L, d = q.shape
+    ref = [[sum(sum(q[p][a] * k[i][a] for a in range(d)) * v[i][n] for i in range(L)) +
+            sum(q[p][a] * m[a][n] for a in range(d)) for n in range(d)] for p in range(L)]
+    o, _ = lo.bidir_fwd(q, k, v, m)
+    np.testing.assert_allclose(o, np.array(ref), atol=1e-12)
+
+
+def test_bidir_finite_differences():
+    q, k, v, do, m, dm = rand_case(8, 3, 41)
+    f = lambda: _bidir_loss(q, k, v, do, m, dm)
+    dq, dk, dv, dmi = lo.bidir_bwd(q, k, v, do, m, dm)
+    for x, g in [(q, dq), (k, dk), (v, dv), (m, dmi)]:
+        np.testing.assert_allclose(g, _fd(f, x), atol=2e-7)
+    # planted mistakes fail the same pin: M_in untransposed in dq, dM_out^T in dv
+    assert not np.allclose(dq - do @ m.T + do @ m, _fd(f, q), atol=2e-7)
+    assert not np.allclose(dv - k @ dm + k @ dm.T, _fd(f, v), atol=2e-7)
+
+
+def test_bidir_permutation_invariance():
+    """Reordering the tokens permutes O's rows and leaves M_out unchanged."""
+    q, k, v, do, m, dm = rand_case(17, 4, 43)
+    perm = np.random.default_rng(5).permutation(17)
+    o, mo = lo.bidir_fwd(q, k, v, m)
+    op, mop = lo.bidir_fwd(q[perm], k[perm], v[perm], m)
+    np.testing.assert_allclose(op, o[perm], atol=1e-11)
+    np.testing.assert_allclose(mop, mo, atol=1e-11)
+
+
+def test_bidir_batched_varlen():
+    rng = np.random.default_rng(7)
+    H, d, lens = 2, 4, [5, 0, 9, 1]
+    cu = np.cumsum([0] + lens)
+    N = int(cu[-1])
+    Q, K, V, dO = (rng.standard_normal((1, H, N, d)) for _ in range(4))
+    Mi, dMo = (rng.standard_normal((len(lens), H, d, d)) for _ in range(2))
+    O, Mo = lo.batched_bidir_fwd(Q, K, V, Mi, cu)
+    dQ, dK, dV, dMi = lo.batched_bidir_bwd(Q, K, V, dO, Mi, dMo, cu)
+    for i, (s, e) in enumerate(zip(cu[:-1], cu[1:])):
+        for h in range(H):
+            o, mo = lo.bidir_fwd(Q[0, h, s:e], K[0, h, s:e], V[0, h, s:e], Mi[i, h])
+            np.testing.assert_allclose(O[0, h, s:e], o)
+            np.testing.assert_allclose(Mo[i, h], mo)
+            g = lo.bidir_bwd(Q[0, h, s:e], K[0, h, s:e], V[0, h, s:e], dO[0, h, s:e], Mi[i, h], dMo[i, h])
+            for a, b in zip((dQ[0, h, s:e], dK[0, h, s:e], dV[0, h, s:e], dMi[i, h]), g):
+                np.testing.assert_allclose(a, b)
