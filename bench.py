@@ -12,7 +12,9 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   cpu_baseline  the float64 C oracle (token recurrence) timed on the host cores
                 over a bounded sample of the same workload;
   kernels_ms    average duration of every kernel of the step.
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3] [--bidir]
+--bidir times the unmasked (bidirectional) form instead (lasp_fwd_bidir +
+lasp_bwd_bidir on the same inputs, no decay) and prints its own line.
 """
 import argparse
 import ctypes
@@ -138,6 +140,8 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--cpu-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bidir", action="store_true",
+                    help="time the unmasked (bidirectional) form instead")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate "
                          "the HBM byte counters of a profiler against known traffic")
@@ -172,6 +176,8 @@ def main():
     decay, cu, M_in, dM_out = inp["decay"], inp["cu_seqlens"], inp["M_in"], inp["dM_out"]
     C = sh["chunk"]
 
+    if a.bidir:
+        return bench_bidir(a, w, sh, inp, torch, cca)
     S = cca.Shape(sh["B"], sh["H"], sh["N"], sh["d"], C, sh["nseq"])
     dt_code = cca.LASP_BF16 if w.dtype == "bf16" else cca.LASP_FP32
     wsf = torch.empty(max(1, cca.fwd_workspace_bytes(S, dt_code, True)), dtype=torch.uint8,
@@ -259,6 +265,61 @@ def main():
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, sh["H"], min(a.cpu_tokens, sh["N"]))
+    print(json.dumps(out), flush=True)
+
+
+def bench_bidir(a, w, sh, inp, torch, cca):
+    """One step = lasp_fwd_bidir + lasp_bwd_bidir (segment totals, scan, row-block
+    products) on the workload's inputs; timed with events on the launch stream
+    around each call.  Roofline: the whole step against HBM (every kernel of
+    this form streams its rows once)."""
+    if w.dtype != "bf16":
+        sys.exit("--bidir needs a bf16 workload")
+    Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
+    cu, M_in, dM_out = inp["cu_seqlens"], inp["M_in"], inp["dM_out"]
+    C = sh["chunk"]
+    n = a.warmup + a.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+
+    def step(i):
+        ev[i][0].record()
+        O, M_out, cache = cca.fwd_bidir(Q, K, V, C, cu, M_in)
+        ev[i][1].record()
+        g = cca.bwd_bidir(Q, K, V, dO, C, cu, M_in, dM_out, cache)
+        ev[i][2].record()
+        return O, g
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.warmup, n):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    fwd_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(a.warmup, n))
+    bwd_ms = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(a.warmup, n))
+    tokens = sh["B"] * sh["N"]
+    U, d = tokens * sh["H"], sh["d"]
+    bytes_ = 12 * U * d * 2          # fwd: K, V, Q in, O out; bwd: Q, dO, dO, K, V in, dQ, dK, dV out
+    flops = 12 * U * d * d           # six d x d contractions per token-head
+    med = fwd_ms[len(fwd_ms) // 2] + bwd_ms[len(bwd_ms) // 2]
+    out = {
+        "metric": "unmasked linear-attn fwd+bwd tokens/s, d=128, N=131072",
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name + ", unmasked", "B": sh["B"], "H": sh["H"], "N": sh["N"],
+                   "d": d, "chunk": C, "nseq": sh["nseq"], "m_in": M_in is not None,
+                   "parallelism": "single GPU"},
+        "calls_ms": {"fwd_bidir": fwd_ms[len(fwd_ms) // 2], "bwd_bidir": bwd_ms[len(bwd_ms) // 2]},
+        "roofline": {"bound": "hbm", "achieved": bytes_ / (med * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": bytes_ / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "whole step", "algorithmic_bytes": bytes_,
+                     "algorithmic_flops": flops},
+        "gpu": torch.cuda.get_device_name(torch.device("cuda:0")),
+    }
     print(json.dumps(out), flush=True)
 
 

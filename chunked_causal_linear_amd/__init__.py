@@ -6,6 +6,7 @@ The binding raises if the library is missing: there is no fallback path.
 
   fwd(Q, K, V, chunk, ...) -> (O, M_out, state_cache)
   bwd(Q, K, V, dO, chunk, ...) -> (dQ, dK, dV, dM_in)
+  fwd_bidir / bwd_bidir: the unmasked (bidirectional) form, bf16, no decay
 
 Semantics, layouts and error codes are those of include/lasp.h ("Linear Attention
 Sequence Parallelism", arXiv 2404.02882, Sec. 3.2, Algorithms 2 and 3).
@@ -15,7 +16,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "bwd", "LaspError", "lib", "Shape", "LASP_FP32", "LASP_BF16",
+__all__ = ["fwd", "bwd", "fwd_bidir", "bwd_bidir", "LaspError", "lib", "Shape", "LASP_FP32", "LASP_BF16",
            "state_cache_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +58,10 @@ def lib():
         L.lasp_fwd_ex.restype = ctypes.c_int
         L.lasp_bwd_ex.argtypes = L.lasp_bwd.argtypes + [P]
         L.lasp_bwd_ex.restype = ctypes.c_int
+        L.lasp_fwd_bidir.argtypes = [SP, ctypes.c_int, P, P, P, P, P, P, P, P, P, S, P]
+        L.lasp_fwd_bidir.restype = ctypes.c_int
+        L.lasp_bwd_bidir.argtypes = [SP, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.lasp_bwd_bidir.restype = ctypes.c_int
         L.lasp_status_string.argtypes = [ctypes.c_int]
         L.lasp_status_string.restype = ctypes.c_char_p
         L.lasp_version.restype = ctypes.c_int
@@ -186,4 +191,68 @@ def bwd(Q, K, V, dO, chunk, decay=None, cu_seqlens=None, M_in=None, dM_out=None,
                            _ptr(workspace), nws, _stream(dev), events)
     if rc != 0:
         raise LaspError(rc, "lasp_bwd")
+    return dQ, dK, dV, dM_in
+
+
+def fwd_bidir(Q, K, V, chunk=256, cu_seqlens=None, M_in=None, *, want_m_out=True,
+              want_state_cache=True, workspace=None):
+    """Unmasked (bidirectional) forward, bf16: O = Q (M_in + sum_i k_i^T v_i) per
+    sequence and head (lasp_fwd_bidir).  chunk only sets the work split.
+    Returns (O, M_out, state_cache)."""
+    import torch
+    dev = Q.device
+    S_ = _shape(Q, chunk, cu_seqlens)
+    dt = _dtype_code(Q)
+    nS = S_.nseq if S_.nseq else S_.B
+    st_shape = (nS, S_.H, S_.d, S_.d)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_dev(n, t, dev, Q.dtype, Q.shape)
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    _check_dev("M_in", M_in, dev, torch.float32, st_shape)
+    O = torch.empty_like(Q)
+    M_out = torch.empty(st_shape, dtype=torch.float32, device=dev) if want_m_out else None
+    cache = None
+    if want_state_cache:
+        cache = torch.empty(max(1, state_cache_bytes(S_, dt)), dtype=torch.uint8, device=dev)
+    nws = fwd_workspace_bytes(S_, dt, cache is not None)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
+    rc = lib().lasp_fwd_bidir(ctypes.byref(S_), dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(cu_seqlens),
+                              _ptr(M_in), _ptr(O), _ptr(M_out), _ptr(cache), _ptr(workspace), nws,
+                              _stream(dev))
+    if rc != 0:
+        raise LaspError(rc, "lasp_fwd_bidir")
+    return O, M_out, cache
+
+
+def bwd_bidir(Q, K, V, dO, chunk=256, cu_seqlens=None, M_in=None, dM_out=None,
+              state_cache=None, *, want_dm_in=True, workspace=None):
+    """Unmasked (bidirectional) backward for l = <dO, O> + <dM_out, M_out>
+    (lasp_bwd_bidir).  Returns (dQ, dK, dV, dM_in)."""
+    import torch
+    dev = Q.device
+    S_ = _shape(Q, chunk, cu_seqlens)
+    dt = _dtype_code(Q)
+    nS = S_.nseq if S_.nseq else S_.B
+    st_shape = (nS, S_.H, S_.d, S_.d)
+    for n, t in (("Q", Q), ("K", K), ("V", V), ("dO", dO)):
+        _check_dev(n, t, dev, Q.dtype, Q.shape)
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    _check_dev("M_in", M_in, dev, torch.float32, st_shape)
+    _check_dev("dM_out", dM_out, dev, torch.float32, st_shape)
+    if state_cache is not None:
+        _check_dev("state_cache", state_cache, dev, torch.uint8)
+        if state_cache.numel() < state_cache_bytes(S_, dt):
+            raise ValueError("state_cache is smaller than lasp_state_cache_bytes()")
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    dM_in = torch.empty(st_shape, dtype=torch.float32, device=dev) if want_dm_in else None
+    nws = bwd_workspace_bytes(S_, dt, state_cache is not None)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
+    rc = lib().lasp_bwd_bidir(ctypes.byref(S_), dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(dO),
+                              _ptr(cu_seqlens), _ptr(M_in), _ptr(dM_out), _ptr(state_cache),
+                              _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dM_in), _ptr(workspace), nws,
+                              _stream(dev))
+    if rc != 0:
+        raise LaspError(rc, "lasp_bwd_bidir")
     return dQ, dK, dV, dM_in

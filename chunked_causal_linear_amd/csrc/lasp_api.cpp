@@ -108,8 +108,8 @@ size_t fwd_ws(const Plan &pl, bool cache) {
     return pl.table_b + pl.seg_b /*Z*/ + (cache ? 0 : pl.cache_b);
 }
 size_t bwd_ws(const Plan &pl, bool cache) {
-    return pl.table_b + pl.local_b /*Rc*/ + 2 * pl.seg_b /*Rseg, W*/ +
-           (cache ? 0 : pl.cache_b + pl.seg_b /*Lc, Pseg, Z*/);
+    return pl.table_b + pl.local_b /*Rc*/ + 2 * pl.seg_b /*Rseg, W*/ + pl.fin_b /*Rfin*/ +
+           (cache ? 0 : pl.cache_b + pl.seg_b /*Lc, Pseg, Pfin, Z*/);
 }
 
 bool misaligned(const void *p, size_t a) { return p && ((uintptr_t)p % a) != 0; }
@@ -195,13 +195,18 @@ static int debug_check_cu(const lasp_shape *shape, const int32_t *cu, hipStream_
     return LASP_OK;
 }
 
-int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
-                const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
-                void *O, float *M_out, void *state_cache, void *workspace,
-                size_t workspace_bytes, void *stream, void **events) {
+}  // extern "C"
+
+namespace {
+
+int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+               const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
+               void *O, float *M_out, void *state_cache, void *workspace,
+               size_t workspace_bytes, void *stream, void **events, bool bidir) {
     Plan pl;
     int rc = make_plan(shape, dtype, pl);
     if (rc != LASP_OK) return rc;
+    if (bidir && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
     if (!Q || !K || !V || !O) return LASP_EINVAL;
     if ((shape->nseq > 0) != (cu_seqlens != nullptr)) return LASP_EINVAL;
     const void *a16[] = {Q, K, V, O, M_in, M_out, state_cache, workspace};
@@ -242,8 +247,29 @@ int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
     p.Lc = pl.local_b ? c : nullptr;
     p.Pseg = (float *)(c + pl.local_b);
     p.Pfin = pl.fin_b ? (float *)(c + pl.local_b + pl.seg_b) : nullptr;
+    if (bidir) return hip_status(lasp::launch_fwd_bidir(p, true, (hipStream_t)stream));
     return hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, true, (hipStream_t)stream,
                                        (hipEvent_t *)events));
+}
+
+}  // namespace
+
+extern "C" {
+
+int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
+                void *O, float *M_out, void *state_cache, void *workspace,
+                size_t workspace_bytes, void *stream, void **events) {
+    return fwd_common(shape, dtype, Q, K, V, decay, cu_seqlens, M_in, O, M_out, state_cache,
+                      workspace, workspace_bytes, stream, events, false);
+}
+
+int lasp_fwd_bidir(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                   const void *V, const int32_t *cu_seqlens, const float *M_in, void *O,
+                   float *M_out, void *state_cache, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    return fwd_common(shape, dtype, Q, K, V, nullptr, cu_seqlens, M_in, O, M_out, state_cache,
+                      workspace, workspace_bytes, stream, nullptr, true);
 }
 
 int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
@@ -254,14 +280,19 @@ int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const voi
                        workspace, workspace_bytes, stream, nullptr);
 }
 
-int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
-                const void *V, const void *dO, const float *decay, const int32_t *cu_seqlens,
-                const float *M_in, const float *dM_out, const void *state_cache, void *dQ,
-                void *dK, void *dV, float *dM_in, void *workspace, size_t workspace_bytes,
-                void *stream, void **events) {
+}  // extern "C"
+
+namespace {
+
+int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+               const void *V, const void *dO, const float *decay, const int32_t *cu_seqlens,
+               const float *M_in, const float *dM_out, const void *state_cache, void *dQ,
+               void *dK, void *dV, float *dM_in, void *workspace, size_t workspace_bytes,
+               void *stream, void **events, bool bidir) {
     Plan pl;
     int rc = make_plan(shape, dtype, pl);
     if (rc != LASP_OK) return rc;
+    if (bidir && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
     if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return LASP_EINVAL;
     if ((shape->nseq > 0) != (cu_seqlens != nullptr)) return LASP_EINVAL;
     const void *a16[] = {Q, K, V, dO, M_in, dM_out, state_cache, dQ, dK, dV, dM_in, workspace};
@@ -306,6 +337,8 @@ int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
     w += pl.seg_b;
     p.W = (float *)w;
     w += pl.seg_b;
+    p.Rfin = pl.fin_b ? (float *)w : nullptr;
+    w += pl.fin_b;
     const hipStream_t hs = (hipStream_t)stream;
     if (cache) {
         p.Lc = pl.local_b ? const_cast<void *>(state_cache) : nullptr;
@@ -316,10 +349,33 @@ int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
         p.Pseg = (float *)(w + pl.local_b);
         p.Pfin = pl.fin_b ? (float *)(w + pl.local_b + pl.seg_b) : nullptr;
         p.Z = (float *)(w + pl.cache_b);
-        rc = hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, false, hs));
+        rc = hip_status(bidir ? lasp::launch_fwd_bidir(p, false, hs)
+                              : lasp::launch_fwd(p, dtype == LASP_BF16, false, hs));
         if (rc != LASP_OK) return rc;
     }
+    if (bidir) return hip_status(lasp::launch_bwd_bidir(p, hs));
     return hip_status(lasp::launch_bwd(p, dtype == LASP_BF16, hs, (hipEvent_t *)events));
+}
+
+}  // namespace
+
+extern "C" {
+
+int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                const void *V, const void *dO, const float *decay, const int32_t *cu_seqlens,
+                const float *M_in, const float *dM_out, const void *state_cache, void *dQ,
+                void *dK, void *dV, float *dM_in, void *workspace, size_t workspace_bytes,
+                void *stream, void **events) {
+    return bwd_common(shape, dtype, Q, K, V, dO, decay, cu_seqlens, M_in, dM_out, state_cache, dQ,
+                      dK, dV, dM_in, workspace, workspace_bytes, stream, events, false);
+}
+
+int lasp_bwd_bidir(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                   const void *V, const void *dO, const int32_t *cu_seqlens, const float *M_in,
+                   const float *dM_out, const void *state_cache, void *dQ, void *dK, void *dV,
+                   float *dM_in, void *workspace, size_t workspace_bytes, void *stream) {
+    return bwd_common(shape, dtype, Q, K, V, dO, nullptr, cu_seqlens, M_in, dM_out, state_cache, dQ,
+                      dK, dV, dM_in, workspace, workspace_bytes, stream, nullptr, true);
 }
 
 int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,

@@ -35,6 +35,8 @@ struct Params {
     void *Rc;      // [chunks][H][D][D] elem: local reverse state of each chunk, [dv][dk]
     float *Rseg;   // [segs][H][D][D] f32: reverse state entering each segment's last chunk
     float *W;      // [segs][H][D][D] f32: local reverse state at each segment start
+    float *Rfin;   // [nseq][H][D][D] f32 or null: reverse state before each sequence's first token, [dv][dk]
+    int parts;     // row-block products: workgroups per (segment, head, product)
 };
 
 // Enqueue the forward kernels: (packed-batch tables), local chunk states,
@@ -46,5 +48,12 @@ hipError_t launch_fwd(const Params &p, bool bf16, bool with_output, hipStream_t 
 // Enqueue the backward kernels: (tables), reverse local states, reverse
 // segment scan, gradient kernel.  The forward states (Lc, Pseg) must be valid.
 hipError_t launch_bwd(const Params &p, bool bf16, hipStream_t stream, hipEvent_t *ev = nullptr);
+
+// Unmasked (bidirectional) form, bf16, no decay.  Forward: (tables), segment
+// totals, segment scan (Pfin = the summed state), O = Q M.  Backward: (tables),
+// reverse totals, reverse scan (Rfin = the summed gradient state), then
+// dQ = dO M^T, dV = K dM, dK = V dM^T; Pfin must be valid.
+hipError_t launch_fwd_bidir(const Params &p, bool with_output, hipStream_t stream);
+hipError_t launch_bwd_bidir(const Params &p, hipStream_t stream);
 
 }  // namespace lasp

@@ -644,7 +644,7 @@ __global__ __launch_bounds__(NTHR) void k_bwd_local(Params p) {
 
 // ---------------------------------------------------------------------------
 // Backward 2: reverse scan over segments, one thread per state element.
-//   Rseg[S-1] = dM_out;  Rseg[s-1] = lambda^len_s Rseg[s] + W[s];  dM_in = last.
+//   Rseg[S-1] = dM_out;  Rseg[s-1] = lambda^len_s Rseg[s] + W[s];  dM_in = Rfin = last.
 // ---------------------------------------------------------------------------
 template <int D, typename T>
 __global__ __launch_bounds__(NTHR) void k_bwd_segscan(Params p) {
@@ -668,6 +668,7 @@ __global__ __launch_bounds__(NTHR) void k_bwd_segscan(Params p) {
         R = dpow(l2, (float)len_s) * R + p.W[idx];
     }
     if (p.dM_in) p.dM_in[mo] = R;
+    if (p.Rfin) p.Rfin[(int64_t)ih * D * D + e] = R;
 }
 
 // Combine a segment state and a local state into LDS:
@@ -1076,6 +1077,47 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int N> struct IC { static constexpr int value = N; };
+
+// Rows out of a 32-row output tile accumulated transposed: acc[nt] holds
+// [feature nt*32 + crow(e)][row lane%32], i.e. each lane holds 4-feature
+// pieces of one row.  Lanes l and l+32 exchange halves (permlane32 swap) so
+// that each lane holds two 8-feature pieces of its row, stored with 16-byte
+// stores: lanes < 32 features 0-7 and 16-23 of a 32-feature block, lanes >= 32
+// features 8-15 and 24-31.  The stores go through a buffer descriptor that
+// covers exactly the tile's `rows` valid rows (none when rows <= 0): the
+// hardware drops stores past its end, so every wave issues the same NDT*2
+// stores and the count of memory operations in flight after them is known.
+// neg = 0x80008000 flips the sign of every packed bf16 pair.
+template <int D>
+__device__ __forceinline__ void store_tile_t(const f32x16 *acc, bf16 *tile, int rows, int lz, unsigned neg) {
+    constexpr int NDT = D / 32;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        tile, 0, __builtin_amdgcn_readfirstlane(rows > 0 ? rows * D * 2 : 0), 0x00020000);
+    const int off = ((lz & 31) * D + (lz >> 5) * 8) * 2;
+#pragma unroll
+    for (int nt = 0; nt < NDT; ++nt) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+        unsigned r[8];   // r[2j], r[2j+1]: features 8j + 4*(lane/32) + [0,4), packed
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const bf16x2_t v = {(__bf16)acc[nt][2 * q], (__bf16)acc[nt][2 * q + 1]};
+            r[q] = __builtin_bit_cast(unsigned, v) ^ neg;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; q += 4) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const auto x = __builtin_amdgcn_permlane32_swap(r[q + e], r[q + 2 + e], false, false);
+                r[q + e] = x[0];
+                r[q + 2 + e] = x[1];
+            }
+        }
+        const u32x4_t v0 = {r[0], r[1], r[2], r[3]}, v1 = {r[4], r[5], r[6], r[7]};
+        __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off + nt * 64, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off + nt * 64 + 32, 0, 0);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Segment sweep (bf16).  One workgroup per (segment, head, role) walks the
@@ -1532,48 +1574,9 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         run_group(IC<1>(), Ct, upd, [&]() __attribute__((always_inline)) {
             if (i + 1 < nch) load_a(i + 1, af);
         });
-        // rows out: lane holds row rt*32 + lane%32, features nt*32 + 8j + 4*(lane/32) + [0,4).
-        // Lanes l and l+32 exchange halves (permlane32 swap) so that each lane
-        // holds two 8-feature pieces of its row, stored with 16-byte stores:
-        // lanes < 32 features 0-7 and 16-23 of a 32-feature block, lanes >= 32
-        // features 8-15 and 24-31.  The stores go through a buffer descriptor
-        // that covers exactly this chunk's Ct rows (none for a wave without
-        // rows): the hardware drops stores past its end, so every wave issues
-        // the same NDT*2 stores and the count of memory operations in flight
-        // after them is known.
-        {
-            const int lz = opaque_lane();
-            // (rt is wave-uniform: read it as a scalar, so that the descriptor
-            // lives in scalar registers as buffer stores require)
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                Out + (int64_t)t * p.C * D, 0,
-                __builtin_amdgcn_readfirstlane(rt >= 0 ? Ct * D * 2 : 0), 0x00020000);
-            const int off = ((rt * 32 + (lz & 31)) * D + (lz >> 5) * 8) * 2;   // negative: dropped
-            const unsigned neg = sub ? 0x80008000u : 0u;                          // bf16 sign bits
-#pragma unroll
-            for (int nt = 0; nt < NDT; ++nt) {
-                typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-                typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-                unsigned r[8];   // r[2j], r[2j+1]: features 8j + 4*(lane/32) + [0,4), packed
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const bf16x2_t v = {(__bf16)acc[nt][2 * q], (__bf16)acc[nt][2 * q + 1]};
-                    r[q] = __builtin_bit_cast(unsigned, v) ^ neg;
-                }
-#pragma unroll
-                for (int q = 0; q < 8; q += 4) {
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const auto x = __builtin_amdgcn_permlane32_swap(r[q + e], r[q + 2 + e], false, false);
-                        r[q + e] = x[0];
-                        r[q + 2 + e] = x[1];
-                    }
-                }
-                const u32x4_t v0 = {r[0], r[1], r[2], r[3]}, v1 = {r[4], r[5], r[6], r[7]};
-                __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off + nt * 64, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off + nt * 64 + 32, 0, 0);
-            }
-        }
+        // rows out (the tile's rows past the chunk end are dropped)
+        store_tile_t<D>(acc, Out + ((int64_t)t * p.C + rt * 32) * D, rt >= 0 ? Ct - rt * 32 : 0,
+                        opaque_lane(), sub ? 0x80008000u : 0u);
         if (upd) write_state();
     }
 }
@@ -1724,6 +1727,126 @@ __global__ __launch_bounds__(SegTotCfg<D>::NT) void k_segtot_bf16(Params p) {
 
 
 // ---------------------------------------------------------------------------
+// Row-block products of the unmasked (bidirectional) form ([LASP] Eq. 3, the
+// right-product version; LASP-2's O_t = Q_t M_(1:T)): Out = A X over every row
+// of a segment, with one d x d matrix X per (sequence, head):
+//   forward  O  = Q  M       (X = M,     the summed state Pfin)
+//   backward dQ = dO M^T,  dV = K dM,  dK = V dM^T   (dM: Rfin)
+// Pfin and Rfin are [dv][dk]: M[dk][dv] = Pfin[dv][dk].  One workgroup per
+// (segment, head, product); it converts X once into a bf16 LDS operand
+// XS[n][k] (n output feature, k contracted feature), then its waves take
+// 32-row tiles in turn: A rows into registers (the next tile's loaded while
+// the current one's MFMAs run), (XS A^T) accumulated transposed as in the
+// sweep, rows out through store_tile_t.  A segment's rows are split into
+// p.parts contiguous ranges of whole tiles, one workgroup each, so that the
+// launch has several workgroups per CU.
+// ---------------------------------------------------------------------------
+enum RowMatKind { RM_FWD = 0, RM_BWD = 1 };
+constexpr int RM_NW = 8;   // waves per workgroup
+
+template <int D, int KIND>
+__global__ __launch_bounds__(64 * RM_NW) void k_rowmat_bf16(Params p) {
+    constexpr int NW = RM_NW, NDT = D / 32, KS = D / 16;
+    constexpr int nprod = KIND == RM_BWD ? 3 : 1;
+    __shared__ __attribute__((aligned(16))) bf16 XS[D * D];
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int prod = lid % nprod, rest0 = lid / nprod;
+    const int part = rest0 % p.parts, rest = rest0 / p.parts;
+    const int h = rest % p.H, gs = rest / p.H;
+    Seq s;
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    if (t1 <= t0) return;
+    const int seg_rows = min(t1 * p.C, s.len) - t0 * p.C;
+    const int tpp = ((seg_rows + 31) / 32 + p.parts - 1) / p.parts;   // tiles per part
+    const int row0 = t0 * p.C + part * tpp * 32;               // first row of this part
+    const int nrows = min(seg_rows - part * tpp * 32, tpp * 32);
+    if (nrows <= 0) return;
+    const int64_t rbase = (row_base(p, s, h) + row0) * D;
+    const float *X = (KIND == RM_FWD || prod == 0 ? p.Pfin : p.Rfin) + ((int64_t)s.i * p.H + h) * D * D;
+    const bool trans = KIND == RM_BWD && prod != 1;            // dQ, dK use the transpose
+    const bf16 *A;
+    bf16 *Out;
+    if (KIND == RM_FWD) {
+        A = (const bf16 *)p.Q + rbase; Out = (bf16 *)p.O + rbase;
+    } else if (prod == 0) {
+        A = (const bf16 *)p.dO + rbase; Out = (bf16 *)p.dQ + rbase;
+    } else if (prod == 1) {
+        A = (const bf16 *)p.K + rbase; Out = (bf16 *)p.dV + rbase;
+    } else {
+        A = (const bf16 *)p.V + rbase; Out = (bf16 *)p.dK + rbase;
+    }
+
+    // XS[n][k] = bf16(X[n][k]), or bf16(X[k][n]) for the transpose
+    for (int c = threadIdx.x; c < D * D / 4; c += NW * 64) {
+        int n, k0;
+        float f[4];
+        if (trans) {   // lanes take consecutive n: coalesced reads of X rows
+            n = c % D;
+            k0 = (c / D) * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f[j] = X[(int64_t)(k0 + j) * D + n];
+        } else {
+            n = c / (D / 4);
+            k0 = (c % (D / 4)) * 4;
+            const float4 v = *(const float4 *)(X + (int64_t)n * D + k0);
+            f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+        }
+        store4(XS + sw_off<D>(n, k0), f[0], f[1], f[2], f[3]);
+    }
+    __syncthreads();
+
+    const int w = wave_id(), l = lane_id();
+    const FragOffs<D> fo0 = frag_offs<D>(l);
+    const int ntiles = (nrows + 31) / 32;
+    // A rows of tile `tile` (rows past the segment end: a valid row)
+    auto load_rows = [&](int tile, bf16x8_t *dst) __attribute__((always_inline)) {
+        int lz = l;
+        asm volatile("" : "+v"(lz));
+        const int row = min(tile * 32 + (lz & 31), nrows - 1);
+        const bf16 *src = A + (int64_t)row * D + (lz >> 5) * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dst[ks] = *(const bf16x8_t *)(src + ks * 16);
+    };
+    // one tile: acc = (XS A^T), the XS fragments read XPD MFMAs ahead, rows out
+    auto process = [&](int tile, const bf16x8_t *a) __attribute__((always_inline)) {
+        f32x16 acc[NDT];
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt) zero(acc[nt]);
+        const FragOffs<D> fo = opaque(fo0);
+        constexpr int NJ = NDT * KS, XPD = 4;
+        bf16x8_t xf[XPD];
+#pragma unroll
+        for (int j = 0; j < XPD; ++j) xf[j] = frag_rows_sw<D>(XS, fo, (j % NDT) * 32, (j / NDT) * 16);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            mma(acc[j % NDT], xf[j % XPD], a[j / NDT]);
+            if (j + XPD < NJ)
+                xf[j % XPD] = frag_rows_sw<D>(XS, fo, ((j + XPD) % NDT) * 32, ((j + XPD) / NDT) * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        int lz = l;
+        asm volatile("" : "+v"(lz));
+        store_tile_t<D>(acc, Out + (int64_t)tile * 32 * D, nrows - tile * 32, lz, 0u);
+    };
+    // tiles w, w + NW, ... in pairs, each tile's A rows loaded while the one
+    // before it is computed (two named buffers: no indexed register arrays)
+    bf16x8_t a0[KS], a1[KS];
+    if (w < ntiles) load_rows(w, a0);
+#pragma unroll 1
+    for (int tile = w; tile < ntiles; tile += 2 * NW) {
+        if (tile + NW < ntiles) load_rows(tile + NW, a1);
+        process(tile, a0);
+        if (tile + NW >= ntiles) break;
+        if (tile + 2 * NW < ntiles) load_rows(tile + 2 * NW, a0);
+        process(tile + NW, a1);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 static inline int round8(int n) { return (n + 7) & ~7; }
@@ -1825,6 +1948,58 @@ static hipError_t bwd_bf16(const Params &p, hipStream_t st, hipEvent_t *ev) {
     sweep_dispatch<D, SWEEP_GRADS>(p, st);
     rec(ev, 3, st);
     return hipGetLastError();
+}
+
+template <int D, int KIND>
+static void rowmat_launch(const Params &p0, hipStream_t st) {
+    const int prods = KIND == RM_BWD ? 3 : 1;
+    // about 1024 workgroups (four per CU), parts of at least 8 tiles
+    Params p = p0;
+    const int64_t wg = (int64_t)p.n_segs_ub * p.H * prods;
+    const int by_wg = (int)((1024 + wg - 1) / wg);
+    const int by_rows = (p.G * p.C / 32) / 8;
+    p.parts = by_wg < 1 ? 1 : (by_wg < by_rows ? by_wg : (by_rows < 1 ? 1 : by_rows));
+    hipLaunchKernelGGL((k_rowmat_bf16<D, KIND>), dim3(round8(wg * p.parts)), dim3(64 * RM_NW), 0, st, p);
+}
+
+template <int D>
+static hipError_t fwd_bidir(const Params &p, bool with_output, hipStream_t st) {
+    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
+    segtot_launch<D, TOT_F>(p, st);
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    hipLaunchKernelGGL((k_fwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    if (with_output) rowmat_launch<D, RM_FWD>(p, st);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t bwd_bidir(const Params &p, hipStream_t st) {
+    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
+    segtot_launch<D, TOT_B>(p, st);
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    hipLaunchKernelGGL((k_bwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    rowmat_launch<D, RM_BWD>(p, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_bidir(const Params &p, bool with_output, hipStream_t st) {
+    if (p.decay || !p.Pfin) return hipErrorInvalidValue;
+    switch (p.D) {
+    case 32: return fwd_bidir<32>(p, with_output, st);
+    case 64: return fwd_bidir<64>(p, with_output, st);
+    case 128: return fwd_bidir<128>(p, with_output, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_bidir(const Params &p, hipStream_t st) {
+    if (p.decay || !p.Pfin || !p.Rfin) return hipErrorInvalidValue;
+    switch (p.D) {
+    case 32: return bwd_bidir<32>(p, st);
+    case 64: return bwd_bidir<64>(p, st);
+    case 128: return bwd_bidir<128>(p, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd(const Params &p, bool bf, bool with_output, hipStream_t st, hipEvent_t *ev) {

@@ -141,6 +141,35 @@ int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype,
                 void *dQ, void *dK, void *dV, float *dM_in,
                 void *workspace, size_t workspace_bytes, void *stream, void **events);
 
+/* Unmasked (bidirectional) form: LASP Eq. 3 without Norm, every token attends
+ * to every token of its sequence, no decay; with sequence parallelism each
+ * device sums all chunk states (LASP-2 review page: one AllGather of the M_t,
+ * then their sum M_(1:T)):
+ *
+ *   M = M_in + sum_i k_i^T v_i,   o_p = q_p M   (= sum_i (q_p . k_i) v_i + q_p M_in)
+ *   M_out = M
+ *
+ * M_in stands for the summed states of the other devices' chunks.  The
+ * backward, for l = <dO, O> + <dM_out, M_out>, returns
+ *   dM = sum_p q_p^T do_p + dM_out,  dq_p = do_p M^T,  dk_j = v_j dM^T,
+ *   dv_j = k_j dM,  dM_in = dM.
+ * Arguments, layouts, size queries (the same shape gives the same workspace
+ * and state-cache sizes as lasp_fwd / lasp_bwd; shape->chunk only sets the
+ * work split) and errors as for lasp_fwd / lasp_bwd; there is no decay
+ * argument.  dtype must be LASP_BF16 (else LASP_EUNSUPPORTED).  The state
+ * cache carries M from lasp_fwd_bidir to lasp_bwd_bidir. */
+int lasp_fwd_bidir(const lasp_shape *shape, lasp_dtype dtype,
+                   const void *Q, const void *K, const void *V,
+                   const int32_t *cu_seqlens, const float *M_in,
+                   void *O, float *M_out, void *state_cache,
+                   void *workspace, size_t workspace_bytes, void *stream);
+int lasp_bwd_bidir(const lasp_shape *shape, lasp_dtype dtype,
+                   const void *Q, const void *K, const void *V, const void *dO,
+                   const int32_t *cu_seqlens, const float *M_in,
+                   const float *dM_out, const void *state_cache,
+                   void *dQ, void *dK, void *dV, float *dM_in,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable text for a status code (for LASP_EHIP: the last HIP error of
  * the calling thread). */
 const char *lasp_status_string(int status);

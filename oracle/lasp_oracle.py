@@ -29,7 +29,7 @@ __all__ = [
     "sampled_o", "sampled_dq", "sampled_dk", "sampled_dv",
     "closed_m_out", "closed_dm_in",
     "batched_fwd", "batched_bwd",
-    "bidir_fwd", "bidir_bwd", "batched_bidir_fwd", "batched_bidir_bwd",
+    "bidir_fwd", "bidir_bwd", "batched_bidir_fwd", "batched_bidir_bwd", "bidir_sampled",
 ]
 
 
@@ -408,3 +408,22 @@ def batched_bidir_bwd(Q, K, V, dO, m_in=None, dm_out=None, cu_seqlens=None):
             dQ[b, h, s:e], dK[b, h, s:e], dV[b, h, s:e], dMin[si, h] = bidir_bwd(
                 Q[b, h, s:e], K[b, h, s:e], V[b, h, s:e], dO[b, h, s:e], mi, dmo)
     return dQ, dK, dV, dMin
+
+
+def bidir_sampled(q, k, v, do, rows, m_in=None, dm_out=None):
+    """Rows `rows` of O, dQ, dK, dV of the unmasked form, each a direct sum over
+    all tokens (left products restricted to the sampled rows), and the full
+    M_out and dM_in.  For sequences too long for the L x L products."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    d = q.shape[1]
+    m = _zeros_state(d, m_in)
+    dm = _zeros_state(d, dm_out)
+    r = np.asarray(rows)
+    return {
+        "O": (q[r] @ k.T) @ v + q[r] @ m,
+        "dQ": (do[r] @ v.T) @ k + do[r] @ m.T,
+        "dK": (v[r] @ do.T) @ q + v[r] @ dm.T,
+        "dV": (k[r] @ q.T) @ do + k[r] @ dm,
+        "M_out": m + k.T @ v,
+        "dM_in": q.T @ do + dm,
+    }

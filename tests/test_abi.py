@@ -140,3 +140,33 @@ def test_sizes_follow_the_shape(L):
     # invalid shapes report 0
     assert L.lasp_state_cache_bytes(ctypes.byref(Shape(1, 1, 1, 33, 64, 0)), 1) == 0
     assert L.lasp_fwd_workspace_bytes(None, 1, 0) == 0
+
+
+def test_bidir_rejects_bad_arguments(L):
+    """The unmasked entry points share the checks of lasp_fwd / lasp_bwd and take
+    bf16 only (every case here fails before anything is enqueued)."""
+    s = Shape(1, 2, 300, 64, 128, 0)
+    p = [fake(i) for i in range(12)]
+    nf = L.lasp_fwd_workspace_bytes(ctypes.byref(s), 1, 0)
+    nb = L.lasp_bwd_workspace_bytes(ctypes.byref(s), 1, 0)
+
+    def fwd(shape=s, dt=1, ws_bytes=nf, **kw):
+        a = dict(Q=p[0], K=p[1], V=p[2], cu=None, M_in=None, O=p[3], M_out=None, cache=None, ws=p[5])
+        a.update(kw)
+        return L.lasp_fwd_bidir(ctypes.byref(shape), dt, a["Q"], a["K"], a["V"], a["cu"], a["M_in"],
+                                a["O"], a["M_out"], a["cache"], a["ws"], ws_bytes, None)
+
+    def bwd(shape=s, dt=1, ws_bytes=nb, **kw):
+        a = dict(Q=p[0], K=p[1], V=p[2], dO=p[3], cu=None, M_in=None, dM_out=None, cache=None,
+                 dQ=p[4], dK=p[5], dV=p[6], dM_in=None, ws=p[7])
+        a.update(kw)
+        return L.lasp_bwd_bidir(ctypes.byref(shape), dt, a["Q"], a["K"], a["V"], a["dO"], a["cu"],
+                                a["M_in"], a["dM_out"], a["cache"], a["dQ"], a["dK"], a["dV"],
+                                a["dM_in"], a["ws"], ws_bytes, None)
+
+    assert fwd(dt=0) == EUNSUP and bwd(dt=0) == EUNSUP          # float32: not in this form
+    assert fwd(shape=Shape(1, 2, 300, 48, 128, 0)) == EUNSUP
+    assert fwd(O=None) == EINVAL and bwd(dV=None) == EINVAL
+    assert fwd(O=p[1]) == EINVAL and bwd(dK=p[0]) == EINVAL    # output aliases an input
+    assert fwd(ws_bytes=nf - 1) == EWS and bwd(ws_bytes=nb - 1) == EWS
+    assert fwd(cu=p[8]) == EINVAL                               # cu_seqlens without nseq

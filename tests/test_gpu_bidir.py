@@ -1,0 +1,119 @@
+"""GPU parity of the unmasked (bidirectional) form: lasp_fwd_bidir /
+lasp_bwd_bidir through the C ABI against the oracle's bidir_* functions
+("Linear Attention Sequence Parallelism", Eq. 3 without Norm; LASP-2's sum of
+all chunk states).  Same metric and bar as the causal parity tests:
+max|gpu - ref| / max|ref| per tensor <= 2e-2 for bf16 inputs."""
+import numpy as np
+import pytest
+import torch
+
+import chunked_causal_linear_amd as cca
+from chunked_causal_linear_amd.workloads import CONFIGS, make_inputs, small
+from oracle import lasp_oracle as lo
+from test_gpu_parity import TOL, check, dev, np64, rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    cca.lib()       # raises if the HIP library is missing: no fallback
+    yield
+
+
+def run_bidir(inp, use_cache=True):
+    sh = inp["shape"]
+    Q, K, V = dev(inp["Q"]), dev(inp["K"]), dev(inp["V"])
+    cu, M_in = dev(inp["cu_seqlens"]), dev(inp["M_in"])
+    O, M_out, cache = cca.fwd_bidir(Q, K, V, sh["chunk"], cu, M_in, want_state_cache=use_cache)
+    dQ, dK, dV, dM_in = cca.bwd_bidir(Q, K, V, dev(inp["dO"]), sh["chunk"], cu, M_in,
+                                      dev(inp["dM_out"]), cache)
+    torch.cuda.synchronize()
+    return dict(O=O, M_out=M_out, dQ=dQ, dK=dK, dV=dV, dM_in=dM_in)
+
+
+def oracle_bidir(inp):
+    a = {k: np64(inp[k]) for k in ("Q", "K", "V", "dO", "M_in", "dM_out")}
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy()
+    O, Mo = lo.batched_bidir_fwd(a["Q"], a["K"], a["V"], a["M_in"], cu)
+    dQ, dK, dV, dMi = lo.batched_bidir_bwd(a["Q"], a["K"], a["V"], a["dO"], a["M_in"], a["dM_out"], cu)
+    return dict(O=O, M_out=Mo, dQ=dQ, dK=dK, dV=dV, dM_in=dMi)
+
+
+SMALL = [
+    small("bidir bf16 d64 C64 B2 H2 Min dMout", "bf16", B=2, H=2, N=300, d=64, chunk=64, seed=50,
+          m_in_scale=0.1, dm_out_scale=0.1),
+    small("bidir bf16 d128 C256 ragged", "bf16", B=1, H=2, N=700, d=128, chunk=256, seed=51),
+    small("bidir bf16 d32 C64 B3 H1 Min dMout", "bf16", B=3, H=1, N=200, d=32, chunk=64, seed=52,
+          m_in_scale=0.1, dm_out_scale=0.1),
+    small("bidir bf16 packed d128 C128 edge lengths", "bf16", H=2, d=128, chunk=128, seed=53,
+          lengths=[1, 127, 128, 129, 0, 300, 64, 1000], m_in_scale=0.1, dm_out_scale=0.1),
+    small("bidir bf16 one token", "bf16", B=1, H=1, N=1, d=64, chunk=64, seed=54, m_in_scale=0.1,
+          dm_out_scale=0.1),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_bidir_small(w):
+    say("case:", w.name)
+    inp = make_inputs(w)
+    check(w.name, run_bidir(inp), oracle_bidir(inp), TOL["bf16"])
+
+
+@pytest.mark.parametrize("G", ["1", "3"])
+def test_bidir_segment_sizes(G, monkeypatch):
+    monkeypatch.setenv("LASP_SEGMENT_CHUNKS", G)
+    w = small("bidir bf16 d64 C64 many chunks", "bf16", B=2, H=2, N=64 * 11 + 17, d=64, chunk=64,
+              seed=55, m_in_scale=0.1, dm_out_scale=0.1)
+    say("case: bidir segment chunks", G)
+    inp = make_inputs(w)
+    check("bidir G=" + G, run_bidir(inp), oracle_bidir(inp), TOL["bf16"])
+
+
+def test_bidir_recompute_equals_cache():
+    w = small("bidir bf16 d128 C128", "bf16", B=1, H=2, N=900, d=128, chunk=128, seed=56,
+              m_in_scale=0.1, dm_out_scale=0.1)
+    inp = make_inputs(w)
+    say("case: bidir recompute vs cache")
+    a = run_bidir(inp, use_cache=True)
+    b = run_bidir(inp, use_cache=False)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_bidir_rejects_fp32():
+    inp = make_inputs(small("fp32", "fp32", B=1, H=1, N=64, d=32, chunk=64, seed=57))
+    with pytest.raises(cca.LaspError) as e:
+        cca.fwd_bidir(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), 64)
+    assert e.value.status == 2
+
+
+def test_bidir_full_size_sampled():
+    """bf16 B1 H32 N131072 d128 (the benchmark's shape, with M_in and dM_out):
+    sampled rows of O, dQ, dK, dV as direct sums over all tokens, full M_out and
+    dM_in, one head at a time."""
+    import dataclasses
+    w = dataclasses.replace(CONFIGS[3], name="bidir " + CONFIGS[3].name, dm_out_scale=0.01, seed=58)
+    say("case:", w.name)
+    inp = make_inputs(w)
+    out = run_bidir(inp)
+    r = np.random.default_rng(158)
+    L = w.N
+    rows = np.unique(np.concatenate([[0, L - 1], r.integers(0, L, 32)]))
+    idx = torch.as_tensor(rows)
+    acc = {k: ([], []) for k in ("O", "dQ", "dK", "dV", "M_out", "dM_in")}
+    for h in range(w.H):
+        q, k, v, do = (np64(inp[x][0, h]) for x in ("Q", "K", "V", "dO"))
+        ref = lo.bidir_sampled(q, k, v, do, rows, np64(inp["M_in"][0, h]), np64(inp["dM_out"][0, h]))
+        for name in ("O", "dQ", "dK", "dV"):
+            acc[name][0].append(np64(out[name][0, h].index_select(0, idx.to(out[name].device))))
+            acc[name][1].append(ref[name])
+        acc["M_out"][0].append(np64(out["M_out"][0, h]))
+        acc["M_out"][1].append(ref["M_out"])
+        acc["dM_in"][0].append(np64(out["dM_in"][0, h]))
+        acc["dM_in"][1].append(ref["dM_in"])
+    errs = {k: rel(np.concatenate(g), np.concatenate(rv)) for k, (g, rv) in acc.items()}
+    say(w.name, " ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {k: e for k, e in errs.items() if not e <= TOL["bf16"]}
+    assert not bad, bad

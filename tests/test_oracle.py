@@ -373,3 +373,14 @@ def test_bidir_batched_varlen():
             g = lo.bidir_bwd(Q[0, h, s:e], K[0, h, s:e], V[0, h, s:e], dO[0, h, s:e], Mi[i, h], dMo[i, h])
             for a, b in zip((dQ[0, h, s:e], dK[0, h, s:e], dV[0, h, s:e], dMi[i, h]), g):
                 np.testing.assert_allclose(a, b)
+
+
+def test_bidir_sampled_rows_match_full():
+    q, k, v, do, m, dm = rand_case(31, 4, 47)
+    rows = [0, 5, 30]
+    got = lo.bidir_sampled(q, k, v, do, rows, m, dm)
+    o, mo = lo.bidir_fwd(q, k, v, m)
+    dq, dk, dv, dmi = lo.bidir_bwd(q, k, v, do, m, dm)
+    for name, full in (("O", o[rows]), ("dQ", dq[rows]), ("dK", dk[rows]), ("dV", dv[rows]),
+                       ("M_out", mo), ("dM_in", dmi)):
+        np.testing.assert_allclose(got[name], full, atol=1e-10)
