@@ -138,6 +138,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="override the workload's chunk length (64, 128 or 256)")
     ap.add_argument("--cpu-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bidir", action="store_true",
@@ -168,6 +170,9 @@ def main():
     from chunked_causal_linear_amd.workloads import CONFIGS, make_inputs
 
     w = CONFIGS[a.config]
+    if a.chunk:
+        import dataclasses
+        w = dataclasses.replace(w, chunk=a.chunk, name=w.name.replace("C%d" % w.chunk, "C%d" % a.chunk))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = make_inputs(w, device="cuda")
