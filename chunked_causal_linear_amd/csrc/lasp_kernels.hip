@@ -1345,7 +1345,8 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     // pair products of row tile rt with NP column tiles ct[] (in range,
     // causal) whose B and Cv rows are at Bt[]; the NP score tiles are
     // independent MFMA chains until they meet in acc
-    auto pair = [&](auto NPC, const bf16 *const *Bt, const int *ct, int Ct) __attribute__((always_inline)) {
+    auto pair = [&](auto NPC, const bf16 *const *Bt, const int *ct, int Ct, auto after_scores)
+                    __attribute__((always_inline)) {
         constexpr int NP = decltype(NPC)::value;
         const FragOffs<D> fo = opaque(fo0);
         const int lz = opaque_lane();
@@ -1374,6 +1375,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
             for (int u = 0; u < NP; ++u) mma(st[u], bf[ks % (BPD + 1)][u], af[ks]);
         }
         __builtin_amdgcn_sched_barrier(0);
+        after_scores();   // af has been read
         // S^T Cv: NJ MFMAs, each with its own Cv fragment (two transpose
         // reads); the fragments are read CPD MFMAs ahead of their use, the
         // first ones while the score tiles are masked and converted.
@@ -1470,11 +1472,14 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // one group of column tiles: pair products, then after_pairs(), then the
-    // state updates
-    auto run_group = [&](auto G, int Ct, bool upd, auto after_pairs) __attribute__((always_inline)) {
+    // one group of column tiles: pair products, then the state updates.
+    // after_a() runs once the pair products have read af: right after the
+    // score products of the group's last pair (its S^T Cv products and the
+    // state updates then hide the latency), or at once without pairs
+    auto run_group = [&](auto G, int Ct, bool upd, auto after_a) __attribute__((always_inline)) {
         constexpr int g = decltype(G)::value;
         const bf16 *BG = g == 0 ? BG0 : BG1;
+        bool a_done = false;
         if (rt >= 0 && rt * 32 < Ct) {
             // the group's causal tiles, two at a time
             int need = 0;
@@ -1492,15 +1497,21 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
                     need &= need - 1;
                     const bf16 *bt[2] = {BG + ka * 2 * TILE, BG + kb * 2 * TILE};
                     const int cts[2] = {Cfg::group_tile(g, ka), Cfg::group_tile(g, kb)};
-                    pair(IC<2>(), bt, cts, Ct);
+                    const bool last = need == 0;
+                    pair(IC<2>(), bt, cts, Ct, [&]() __attribute__((always_inline)) {
+                        if (last) { after_a(); a_done = true; }
+                    });
                 } else {
                     const bf16 *bt[1] = {BG + ka * 2 * TILE};
                     const int cts[1] = {Cfg::group_tile(g, ka)};
-                    pair(IC<1>(), bt, cts, Ct);
+                    pair(IC<1>(), bt, cts, Ct, [&]() __attribute__((always_inline)) {
+                        after_a();
+                        a_done = true;
+                    });
                 }
             }
         }
-        after_pairs();
+        if (!a_done) after_a();
         if (upd) {
             if (xt)
                 state_updates(BG, G, Ct, IC<1>());
