@@ -13,6 +13,11 @@ Recipe (all configurations):
   * per-head decay (the lightning-attention style workload):
     lambda_h = 1 - 2^-(5 + 8 h / H), h = 0..H-1, computed in float64 and rounded
     to float32 (the decay is a fixed hyperparameter, never learned).
+  * gated workloads draw, after everything above, x ~ N(0, 1) of shape
+    [B, H, N, d] and take float32 log-gates from it:
+      "gla"    log g = logsigmoid(x) / 16   (GLA-style gates near 1)
+      "strong" log g = 4 logsigmoid(x) - 1  (gates from e^-1 down to ~0)
+      "mixed"  "gla", except "strong" for tokens n with (n // 32) % 3 == 1
 """
 from __future__ import annotations
 
@@ -36,6 +41,7 @@ class Workload:
     lengths: Optional[tuple] = None      # packed batch: drawn lengths are stored here
     len_range: Optional[tuple] = None    # packed batch: (nseq, lo, hi) to draw from
     decay: str = "none"                  # "none" | "lightning"
+    gates: str = "none"                  # "none" | "gla" | "strong" | "mixed"
     m_in_scale: Optional[float] = None
     dm_out_scale: Optional[float] = None
     backward: bool = True
@@ -65,7 +71,7 @@ def make_inputs(w: Workload, backward: Optional[bool] = None, device: str = "cpu
     seeded with w.seed; draws on the GPU give other values than on the CPU, with
     the same recipe).  Returns a dict with
     Q, K, V (and dO when backward) in w's dtype [B, H, N, d]; decay float32 [H]
-    or None; cu_seqlens int32 [nseq+1] or None; M_in / dM_out float32
+    or None; log_g float32 [B, H, N, d] or None (gated workloads); cu_seqlens int32 [nseq+1] or None; M_in / dM_out float32
     [S, H, d, d] or None; and the resolved shape (B, H, N, d, chunk, nseq)."""
     backward = w.backward if backward is None else backward
     g = torch.Generator("cpu").manual_seed(w.seed)
@@ -93,9 +99,23 @@ def make_inputs(w: Workload, backward: Optional[bool] = None, device: str = "cpu
     dM_out = (draw((S, H, d, d), w.dm_out_scale)
               if (backward and w.dm_out_scale is not None) else None)
     decay = lightning_decay(H).to(device) if w.decay == "lightning" else None
+    log_g = None
+    if w.gates != "none":
+        x = draw((B, H, N, d), 1.0)
+        gla = torch.nn.functional.logsigmoid(x) / 16.0
+        strong = 4.0 * torch.nn.functional.logsigmoid(x) - 1.0
+        if w.gates == "gla":
+            log_g = gla
+        elif w.gates == "strong":
+            log_g = strong
+        elif w.gates == "mixed":
+            n = torch.arange(N, device=device)
+            log_g = torch.where(((n // 32) % 3 == 1)[:, None], strong, gla)
+        else:
+            raise ValueError(w.gates)
     if cu is not None:
         cu = cu.to(device)
-    return dict(Q=Q, K=K, V=V, dO=dO, M_in=M_in, dM_out=dM_out, decay=decay,
+    return dict(Q=Q, K=K, V=V, dO=dO, M_in=M_in, dM_out=dM_out, decay=decay, log_g=log_g,
                 cu_seqlens=cu, lengths=lens,
                 shape=dict(B=B, H=H, N=N, d=d, chunk=w.chunk,
                            nseq=(len(lens) if lens is not None else 0)))
@@ -115,10 +135,17 @@ CONFIGS = {
                 seed=5, len_range=(8, 1024, 16384)),
 }
 
+# The gated (GLA-style) form at the long-sequence shape, with the chunk length
+# the gated kernels use.
+GATED = Workload("bf16 B1 H32 N131072 d128 C64, GLA gates, M_in and M_out", "bf16", 1, 32,
+                 131072, 128, 64, seed=6, gates="gla", m_in_scale=0.01)
+
 
 def small(name, dtype="bf16", B=1, H=2, N=300, d=64, chunk=64, seed=0, lengths=None,
-          decay="none", m_in_scale=None, dm_out_scale=None, backward=True) -> Workload:
+          decay="none", m_in_scale=None, dm_out_scale=None, backward=True,
+          gates="none") -> Workload:
     """A reduced workload for parity tests."""
     return Workload(name, dtype, B, H, N, d, chunk, seed,
                     lengths=None if lengths is None else tuple(lengths), decay=decay,
-                    m_in_scale=m_in_scale, dm_out_scale=dm_out_scale, backward=backward)
+                    gates=gates, m_in_scale=m_in_scale, dm_out_scale=dm_out_scale,
+                    backward=backward)
