@@ -7,6 +7,8 @@ The binding raises if the library is missing: there is no fallback path.
   fwd(Q, K, V, chunk, ...) -> (O, M_out, state_cache)
   bwd(Q, K, V, dO, chunk, ...) -> (dQ, dK, dV, dM_in)
   fwd_bidir / bwd_bidir: the unmasked (bidirectional) form, bf16, no decay
+  fwd_gated / bwd_gated: per-token, per-key-channel gates (log-gates in, their
+                         gradient out), chunk 64
 
 Semantics, layouts and error codes are those of include/lasp.h ("Linear Attention
 Sequence Parallelism", arXiv 2404.02882, Sec. 3.2, Algorithms 2 and 3).
@@ -16,8 +18,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "bwd", "fwd_bidir", "bwd_bidir", "LaspError", "lib", "Shape", "LASP_FP32", "LASP_BF16",
-           "state_cache_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes"]
+__all__ = ["fwd", "bwd", "fwd_bidir", "bwd_bidir", "fwd_gated", "bwd_gated", "LaspError", "lib",
+           "Shape", "LASP_FP32", "LASP_BF16", "state_cache_bytes", "fwd_workspace_bytes",
+           "bwd_workspace_bytes", "gated_state_cache_bytes", "gated_fwd_workspace_bytes",
+           "gated_bwd_workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblasp.so")
@@ -62,6 +66,19 @@ def lib():
         L.lasp_fwd_bidir.restype = ctypes.c_int
         L.lasp_bwd_bidir.argtypes = [SP, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
         L.lasp_bwd_bidir.restype = ctypes.c_int
+        L.lasp_gated_state_cache_bytes.argtypes = [SP, ctypes.c_int]
+        L.lasp_gated_state_cache_bytes.restype = S
+        for f in (L.lasp_gated_fwd_workspace_bytes, L.lasp_gated_bwd_workspace_bytes):
+            f.argtypes = [SP, ctypes.c_int, ctypes.c_int]
+            f.restype = S
+        L.lasp_fwd_gated.argtypes = [SP, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.lasp_fwd_gated.restype = ctypes.c_int
+        L.lasp_bwd_gated.argtypes = [SP, ctypes.c_int] + [P] * 15 + [S, P]
+        L.lasp_bwd_gated.restype = ctypes.c_int
+        L.lasp_fwd_gated_ex.argtypes = L.lasp_fwd_gated.argtypes + [P]
+        L.lasp_fwd_gated_ex.restype = ctypes.c_int
+        L.lasp_bwd_gated_ex.argtypes = L.lasp_bwd_gated.argtypes + [P]
+        L.lasp_bwd_gated_ex.restype = ctypes.c_int
         L.lasp_status_string.argtypes = [ctypes.c_int]
         L.lasp_status_string.restype = ctypes.c_char_p
         L.lasp_version.restype = ctypes.c_int
@@ -256,3 +273,82 @@ def bwd_bidir(Q, K, V, dO, chunk=256, cu_seqlens=None, M_in=None, dM_out=None,
     if rc != 0:
         raise LaspError(rc, "lasp_bwd_bidir")
     return dQ, dK, dV, dM_in
+
+
+def gated_state_cache_bytes(shape: Shape, dtype: int) -> int:
+    return int(lib().lasp_gated_state_cache_bytes(ctypes.byref(shape), dtype))
+
+
+def gated_fwd_workspace_bytes(shape: Shape, dtype: int, with_cache: bool) -> int:
+    return int(lib().lasp_gated_fwd_workspace_bytes(ctypes.byref(shape), dtype, int(with_cache)))
+
+
+def gated_bwd_workspace_bytes(shape: Shape, dtype: int, with_cache: bool) -> int:
+    return int(lib().lasp_gated_bwd_workspace_bytes(ctypes.byref(shape), dtype, int(with_cache)))
+
+
+def fwd_gated(Q, K, V, log_g, chunk=64, cu_seqlens=None, M_in=None, *, want_m_out=True,
+              want_state_cache=True, workspace=None, events=None):
+    """Gated forward (lasp_fwd_gated): kv_p = Diag(g_p) kv_{p-1} + k_p^T v_p,
+    o_p = q_p kv_p, with log_g = log g as a float32 [B, H, N, d] tensor.
+    Returns (O, M_out, state_cache)."""
+    import torch
+    dev = Q.device
+    S_ = _shape(Q, chunk, cu_seqlens)
+    dt = _dtype_code(Q)
+    nS = S_.nseq if S_.nseq else S_.B
+    st_shape = (nS, S_.H, S_.d, S_.d)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_dev(n, t, dev, Q.dtype, Q.shape)
+    _check_dev("log_g", log_g, dev, torch.float32, Q.shape)
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    _check_dev("M_in", M_in, dev, torch.float32, st_shape)
+    O = torch.empty_like(Q)
+    M_out = torch.empty(st_shape, dtype=torch.float32, device=dev) if want_m_out else None
+    cache = None
+    if want_state_cache:
+        cache = torch.empty(max(1, gated_state_cache_bytes(S_, dt)), dtype=torch.uint8, device=dev)
+    nws = gated_fwd_workspace_bytes(S_, dt, cache is not None)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
+    rc = lib().lasp_fwd_gated_ex(ctypes.byref(S_), dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(log_g),
+                                 _ptr(cu_seqlens), _ptr(M_in), _ptr(O), _ptr(M_out), _ptr(cache),
+                                 _ptr(workspace), nws, _stream(dev), events)
+    if rc != 0:
+        raise LaspError(rc, "lasp_fwd_gated")
+    return O, M_out, cache
+
+
+def bwd_gated(Q, K, V, log_g, dO, chunk=64, cu_seqlens=None, M_in=None, dM_out=None,
+              state_cache=None, *, want_dm_in=True, workspace=None, events=None):
+    """Gated backward for l = <dO, O> + <dM_out, M_out> (lasp_bwd_gated).
+    Returns (dQ, dK, dV, dlog_g, dM_in)."""
+    import torch
+    dev = Q.device
+    S_ = _shape(Q, chunk, cu_seqlens)
+    dt = _dtype_code(Q)
+    nS = S_.nseq if S_.nseq else S_.B
+    st_shape = (nS, S_.H, S_.d, S_.d)
+    for n, t in (("Q", Q), ("K", K), ("V", V), ("dO", dO)):
+        _check_dev(n, t, dev, Q.dtype, Q.shape)
+    _check_dev("log_g", log_g, dev, torch.float32, Q.shape)
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    _check_dev("M_in", M_in, dev, torch.float32, st_shape)
+    _check_dev("dM_out", dM_out, dev, torch.float32, st_shape)
+    if state_cache is not None:
+        _check_dev("state_cache", state_cache, dev, torch.uint8)
+        if state_cache.numel() < gated_state_cache_bytes(S_, dt):
+            raise ValueError("state_cache is smaller than lasp_gated_state_cache_bytes()")
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    dLG = torch.empty_like(log_g)
+    dM_in = torch.empty(st_shape, dtype=torch.float32, device=dev) if want_dm_in else None
+    nws = gated_bwd_workspace_bytes(S_, dt, state_cache is not None)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
+    rc = lib().lasp_bwd_gated_ex(ctypes.byref(S_), dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(log_g),
+                                 _ptr(dO), _ptr(cu_seqlens), _ptr(M_in), _ptr(dM_out),
+                                 _ptr(state_cache), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dLG),
+                                 _ptr(dM_in), _ptr(workspace), nws, _stream(dev), events)
+    if rc != 0:
+        raise LaspError(rc, "lasp_bwd_gated")
+    return dQ, dK, dV, dLG, dM_in

@@ -5,7 +5,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = [os.path.join(HERE, "csrc", "lasp_kernels.hip"), os.path.join(HERE, "csrc", "lasp_api.cpp")]
+SRC = [os.path.join(HERE, "csrc", n) for n in ("lasp_kernels.hip", "lasp_gated.hip", "lasp_api.cpp")]
 LIB = os.path.join(HERE, "liblasp.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -30,10 +30,13 @@ struct Plan {
     size_t local_b;      // per-chunk local states (Lc or Rc)
     size_t seg_b;        // per-segment f32 states (Pseg, Z, Rseg or W)
     size_t fin_b;        // per-sequence f32 final states (Pfin)
-    size_t cache_b;      // state cache = [Lc][Pseg][Pfin]
+    size_t gate_c;       // gated form: per-chunk f32 gate products (Gc, Hc)
+    size_t gate_s;       // gated form: per-segment f32 gate products (Gs)
+    size_t cache_b;      // state cache = [Lc][Pseg][Pfin][Gc][Gs]
 };
 
-int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl) {
+// gated: the per-channel gated form (chunk 64; f32 only with d <= 64).
+int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false) {
     if (!s) return LASP_EINVAL;
     if (s->B <= 0 || s->H <= 0 || s->N <= 0 || s->d <= 0 || s->chunk <= 0 || s->nseq < 0)
         return LASP_EINVAL;
@@ -41,6 +44,7 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl) {
     if (dt != LASP_FP32 && dt != LASP_BF16) return LASP_EUNSUPPORTED;
     if (s->d != 32 && s->d != 64 && s->d != 128) return LASP_EUNSUPPORTED;
     if (s->chunk != 64 && s->chunk != 128 && s->chunk != 256) return LASP_EUNSUPPORTED;
+    if (gated && (s->chunk != 64 || (dt == LASP_FP32 && s->d > 64))) return LASP_EUNSUPPORTED;
     pl.D = s->d;
     pl.C = s->chunk;
     pl.H = s->H;
@@ -58,7 +62,12 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl) {
     // count one extra partial segment per sequence.  Measured at B1 H32 N131072 C256:
     // G = 16, 32, 48, 64 -> 4.30, 4.24, 5.09, 4.25 ms per forward+backward
     // (48 leaves the second round nearly empty).
-    {
+    if (gated) {
+        // the gated local-state kernels walk G chunks per (segment, head):
+        // about 2048 of them, segments of 1 to 64 chunks
+        const int64_t g = chunks_ub * s->H / 2048;
+        pl.G = (int)(g < 1 ? 1 : (g > 64 ? 64 : g));
+    } else {
         const int64_t seqs = pl.varlen ? 1 : s->B;
         const int64_t T = pl.varlen ? chunks_ub : per_seq_chunks;   // chunks per sequence (packed: all)
         const int64_t extra = pl.varlen ? s->nseq : 0;              // packed: one partial segment per sequence
@@ -94,13 +103,17 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl) {
     pl.n_segs_ub = (int)segs_ub;
     const size_t dd = (size_t)pl.D * pl.D;
     pl.table_b = pl.varlen ? align_up(2 * sizeof(int32_t) * ((size_t)pl.nseq + 1)) : 0;
-    // per-chunk local states: only the float32 path keeps them (the bf16 path
-    // recomputes chunk states inside its segment sweep)
-    pl.local_b = dt == LASP_BF16 ? 0 : align_up((size_t)pl.n_chunks_ub * pl.H * dd * pl.esz);
+    // per-chunk local states: only the float32 and gated paths keep them (the
+    // bf16 path recomputes chunk states inside its segment sweep)
+    pl.local_b = (dt == LASP_BF16 && !gated)
+                     ? 0 : align_up((size_t)pl.n_chunks_ub * pl.H * dd * pl.esz);
     pl.seg_b = align_up((size_t)pl.n_segs_ub * pl.H * dd * sizeof(float));
     // final states: the bf16 backward starts its subtraction walk of dQ from them
-    pl.fin_b = dt == LASP_BF16 ? align_up((size_t)pl.nseq * pl.H * dd * sizeof(float)) : 0;
-    pl.cache_b = pl.local_b + pl.seg_b + pl.fin_b;
+    pl.fin_b = (dt == LASP_BF16 && !gated)
+                   ? align_up((size_t)pl.nseq * pl.H * dd * sizeof(float)) : 0;
+    pl.gate_c = gated ? align_up((size_t)pl.n_chunks_ub * pl.H * pl.D * sizeof(float)) : 0;
+    pl.gate_s = gated ? align_up((size_t)pl.n_segs_ub * pl.H * pl.D * sizeof(float)) : 0;
+    pl.cache_b = pl.local_b + pl.seg_b + pl.fin_b + pl.gate_c + pl.gate_s;
     return LASP_OK;
 }
 
@@ -109,6 +122,7 @@ size_t fwd_ws(const Plan &pl, bool cache) {
 }
 size_t bwd_ws(const Plan &pl, bool cache) {
     return pl.table_b + pl.local_b /*Rc*/ + 2 * pl.seg_b /*Rseg, W*/ + pl.fin_b /*Rfin*/ +
+           pl.gate_c /*Hc*/ +
            (cache ? 0 : pl.cache_b + pl.seg_b /*Lc, Pseg, Pfin, Z*/);
 }
 
@@ -168,6 +182,23 @@ size_t lasp_state_cache_bytes(const lasp_shape *shape, lasp_dtype dtype) {
     return make_plan(shape, dtype, pl) == LASP_OK ? pl.cache_b : 0;
 }
 
+size_t lasp_gated_state_cache_bytes(const lasp_shape *shape, lasp_dtype dtype) {
+    Plan pl;
+    return make_plan(shape, dtype, pl, true) == LASP_OK ? pl.cache_b : 0;
+}
+
+size_t lasp_gated_fwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype,
+                                      int with_state_cache) {
+    Plan pl;
+    return make_plan(shape, dtype, pl, true) == LASP_OK ? fwd_ws(pl, with_state_cache != 0) : 0;
+}
+
+size_t lasp_gated_bwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype,
+                                      int with_state_cache) {
+    Plan pl;
+    return make_plan(shape, dtype, pl, true) == LASP_OK ? bwd_ws(pl, with_state_cache != 0) : 0;
+}
+
 size_t lasp_fwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype, int with_state_cache) {
     Plan pl;
     return make_plan(shape, dtype, pl) == LASP_OK ? fwd_ws(pl, with_state_cache != 0) : 0;
@@ -199,17 +230,20 @@ static int debug_check_cu(const lasp_shape *shape, const int32_t *cu, hipStream_
 
 namespace {
 
+enum Mode { CAUSAL, BIDIR, GATED };
+
 int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
-               const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
-               void *O, float *M_out, void *state_cache, void *workspace,
-               size_t workspace_bytes, void *stream, void **events, bool bidir) {
+               const void *V, const float *decay, const float *log_g,
+               const int32_t *cu_seqlens, const float *M_in, void *O, float *M_out,
+               void *state_cache, void *workspace, size_t workspace_bytes, void *stream,
+               void **events, Mode mode) {
     Plan pl;
-    int rc = make_plan(shape, dtype, pl);
+    int rc = make_plan(shape, dtype, pl, mode == GATED);
     if (rc != LASP_OK) return rc;
-    if (bidir && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
-    if (!Q || !K || !V || !O) return LASP_EINVAL;
+    if (mode == BIDIR && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
+    if (!Q || !K || !V || !O || (mode == GATED && !log_g)) return LASP_EINVAL;
     if ((shape->nseq > 0) != (cu_seqlens != nullptr)) return LASP_EINVAL;
-    const void *a16[] = {Q, K, V, O, M_in, M_out, state_cache, workspace};
+    const void *a16[] = {Q, K, V, O, M_in, M_out, state_cache, workspace, log_g};
     for (const void *ptr : a16)
         if (misaligned(ptr, 16)) return LASP_EINVAL;
     if (misaligned(decay, 4) || misaligned(cu_seqlens, 4)) return LASP_EINVAL;
@@ -218,13 +252,15 @@ int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     if (workspace_bytes < need || (need && !workspace)) return LASP_EWORKSPACE;
 
     const size_t tens = (size_t)shape->B * shape->H * shape->N * shape->d * pl.esz;
+    const size_t gates = (size_t)shape->B * shape->H * shape->N * shape->d * sizeof(float);
     const size_t st = (size_t)pl.nseq * pl.H * pl.D * pl.D * sizeof(float);
     const Range ins[] = {{Q, tens}, {K, tens}, {V, tens}, {M_in, st},
                          {decay, (size_t)pl.H * 4},
-                         {cu_seqlens, cu_seqlens ? ((size_t)pl.nseq + 1) * 4 : 0}};
+                         {cu_seqlens, cu_seqlens ? ((size_t)pl.nseq + 1) * 4 : 0},
+                         {log_g, log_g ? gates : 0}};
     const Range outs[] = {{O, tens}, {M_out, st}, {state_cache, cache ? pl.cache_b : 0},
                           {workspace, need}};
-    if (any_overlap(outs, 4, ins, 6)) return LASP_EINVAL;
+    if (any_overlap(outs, 4, ins, 7)) return LASP_EINVAL;
     if ((rc = debug_check_cu(shape, cu_seqlens, (hipStream_t)stream)) != LASP_OK) return rc;
 
     lasp::Params p;
@@ -247,7 +283,14 @@ int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     p.Lc = pl.local_b ? c : nullptr;
     p.Pseg = (float *)(c + pl.local_b);
     p.Pfin = pl.fin_b ? (float *)(c + pl.local_b + pl.seg_b) : nullptr;
-    if (bidir) return hip_status(lasp::launch_fwd_bidir(p, true, (hipStream_t)stream));
+    if (mode == BIDIR) return hip_status(lasp::launch_fwd_bidir(p, true, (hipStream_t)stream));
+    if (mode == GATED) {
+        p.LG = log_g;
+        p.Gc = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b);
+        p.Gs = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b + pl.gate_c);
+        return hip_status(lasp::launch_fwd_gated(p, dtype == LASP_BF16, true, (hipStream_t)stream,
+                                                 (hipEvent_t *)events));
+    }
     return hip_status(lasp::launch_fwd(p, dtype == LASP_BF16, true, (hipStream_t)stream,
                                        (hipEvent_t *)events));
 }
@@ -260,16 +303,32 @@ int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
                 const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
                 void *O, float *M_out, void *state_cache, void *workspace,
                 size_t workspace_bytes, void *stream, void **events) {
-    return fwd_common(shape, dtype, Q, K, V, decay, cu_seqlens, M_in, O, M_out, state_cache,
-                      workspace, workspace_bytes, stream, events, false);
+    return fwd_common(shape, dtype, Q, K, V, decay, nullptr, cu_seqlens, M_in, O, M_out,
+                      state_cache, workspace, workspace_bytes, stream, events, CAUSAL);
 }
 
 int lasp_fwd_bidir(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
                    const void *V, const int32_t *cu_seqlens, const float *M_in, void *O,
                    float *M_out, void *state_cache, void *workspace, size_t workspace_bytes,
                    void *stream) {
-    return fwd_common(shape, dtype, Q, K, V, nullptr, cu_seqlens, M_in, O, M_out, state_cache,
-                      workspace, workspace_bytes, stream, nullptr, true);
+    return fwd_common(shape, dtype, Q, K, V, nullptr, nullptr, cu_seqlens, M_in, O, M_out,
+                      state_cache, workspace, workspace_bytes, stream, nullptr, BIDIR);
+}
+
+int lasp_fwd_gated_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                      const void *V, const float *log_g, const int32_t *cu_seqlens,
+                      const float *M_in, void *O, float *M_out, void *state_cache,
+                      void *workspace, size_t workspace_bytes, void *stream, void **events) {
+    return fwd_common(shape, dtype, Q, K, V, nullptr, log_g, cu_seqlens, M_in, O, M_out,
+                      state_cache, workspace, workspace_bytes, stream, events, GATED);
+}
+
+int lasp_fwd_gated(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                   const void *V, const float *log_g, const int32_t *cu_seqlens,
+                   const float *M_in, void *O, float *M_out, void *state_cache, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    return lasp_fwd_gated_ex(shape, dtype, Q, K, V, log_g, cu_seqlens, M_in, O, M_out,
+                             state_cache, workspace, workspace_bytes, stream, nullptr);
 }
 
 int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
@@ -285,17 +344,20 @@ int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const voi
 namespace {
 
 int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
-               const void *V, const void *dO, const float *decay, const int32_t *cu_seqlens,
-               const float *M_in, const float *dM_out, const void *state_cache, void *dQ,
-               void *dK, void *dV, float *dM_in, void *workspace, size_t workspace_bytes,
-               void *stream, void **events, bool bidir) {
+               const void *V, const void *dO, const float *decay, const float *log_g,
+               const int32_t *cu_seqlens, const float *M_in, const float *dM_out,
+               const void *state_cache, void *dQ, void *dK, void *dV, float *dlog_g,
+               float *dM_in, void *workspace, size_t workspace_bytes, void *stream,
+               void **events, Mode mode) {
     Plan pl;
-    int rc = make_plan(shape, dtype, pl);
+    int rc = make_plan(shape, dtype, pl, mode == GATED);
     if (rc != LASP_OK) return rc;
-    if (bidir && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
+    if (mode == BIDIR && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
     if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return LASP_EINVAL;
+    if (mode == GATED && (!log_g || !dlog_g)) return LASP_EINVAL;
     if ((shape->nseq > 0) != (cu_seqlens != nullptr)) return LASP_EINVAL;
-    const void *a16[] = {Q, K, V, dO, M_in, dM_out, state_cache, dQ, dK, dV, dM_in, workspace};
+    const void *a16[] = {Q,  K,  V,  dO,    M_in,      dM_out, state_cache,
+                         dQ, dK, dV, dM_in, workspace, log_g,  dlog_g};
     for (const void *ptr : a16)
         if (misaligned(ptr, 16)) return LASP_EINVAL;
     if (misaligned(decay, 4) || misaligned(cu_seqlens, 4)) return LASP_EINVAL;
@@ -304,13 +366,16 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     if (workspace_bytes < need || (need && !workspace)) return LASP_EWORKSPACE;
 
     const size_t tens = (size_t)shape->B * shape->H * shape->N * shape->d * pl.esz;
+    const size_t gates = (size_t)shape->B * shape->H * shape->N * shape->d * sizeof(float);
     const size_t st = (size_t)pl.nseq * pl.H * pl.D * pl.D * sizeof(float);
     const Range ins[] = {{Q, tens}, {K, tens}, {V, tens}, {dO, tens}, {M_in, st}, {dM_out, st},
                          {state_cache, cache ? pl.cache_b : 0},
                          {decay, (size_t)pl.H * 4},
-                         {cu_seqlens, cu_seqlens ? ((size_t)pl.nseq + 1) * 4 : 0}};
-    const Range outs[] = {{dQ, tens}, {dK, tens}, {dV, tens}, {dM_in, st}, {workspace, need}};
-    if (any_overlap(outs, 5, ins, 9)) return LASP_EINVAL;
+                         {cu_seqlens, cu_seqlens ? ((size_t)pl.nseq + 1) * 4 : 0},
+                         {log_g, log_g ? gates : 0}};
+    const Range outs[] = {{dQ, tens}, {dK, tens}, {dV, tens}, {dM_in, st}, {workspace, need},
+                          {dlog_g, mode == GATED ? gates : 0}};
+    if (any_overlap(outs, 6, ins, 10)) return LASP_EINVAL;
     if ((rc = debug_check_cu(shape, cu_seqlens, (hipStream_t)stream)) != LASP_OK) return rc;
 
     lasp::Params p;
@@ -339,21 +404,30 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     w += pl.seg_b;
     p.Rfin = pl.fin_b ? (float *)w : nullptr;
     w += pl.fin_b;
+    p.Hc = pl.gate_c ? (float *)w : nullptr;
+    w += pl.gate_c;
+    p.LG = log_g;
+    p.dLG = dlog_g;
     const hipStream_t hs = (hipStream_t)stream;
-    if (cache) {
-        p.Lc = pl.local_b ? const_cast<void *>(state_cache) : nullptr;
-        p.Pseg = (float *)((char *)state_cache + pl.local_b);
-        p.Pfin = pl.fin_b ? (float *)((char *)state_cache + pl.local_b + pl.seg_b) : nullptr;
-    } else {   // recompute the forward states (no output, no M_out)
-        p.Lc = pl.local_b ? w : nullptr;
-        p.Pseg = (float *)(w + pl.local_b);
-        p.Pfin = pl.fin_b ? (float *)(w + pl.local_b + pl.seg_b) : nullptr;
+    char *c = cache ? (char *)const_cast<void *>(state_cache) : w;
+    p.Lc = pl.local_b ? c : nullptr;
+    p.Pseg = (float *)(c + pl.local_b);
+    p.Pfin = pl.fin_b ? (float *)(c + pl.local_b + pl.seg_b) : nullptr;
+    if (mode == GATED) {
+        p.Gc = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b);
+        p.Gs = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b + pl.gate_c);
+    }
+    if (!cache) {   // recompute the forward states (no output, no M_out)
         p.Z = (float *)(w + pl.cache_b);
-        rc = hip_status(bidir ? lasp::launch_fwd_bidir(p, false, hs)
-                              : lasp::launch_fwd(p, dtype == LASP_BF16, false, hs));
+        const bool bf = dtype == LASP_BF16;
+        rc = hip_status(mode == BIDIR   ? lasp::launch_fwd_bidir(p, false, hs)
+                        : mode == GATED ? lasp::launch_fwd_gated(p, bf, false, hs)
+                                        : lasp::launch_fwd(p, bf, false, hs));
         if (rc != LASP_OK) return rc;
     }
-    if (bidir) return hip_status(lasp::launch_bwd_bidir(p, hs));
+    if (mode == BIDIR) return hip_status(lasp::launch_bwd_bidir(p, hs));
+    if (mode == GATED)
+        return hip_status(lasp::launch_bwd_gated(p, dtype == LASP_BF16, hs, (hipEvent_t *)events));
     return hip_status(lasp::launch_bwd(p, dtype == LASP_BF16, hs, (hipEvent_t *)events));
 }
 
@@ -366,16 +440,39 @@ int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
                 const float *M_in, const float *dM_out, const void *state_cache, void *dQ,
                 void *dK, void *dV, float *dM_in, void *workspace, size_t workspace_bytes,
                 void *stream, void **events) {
-    return bwd_common(shape, dtype, Q, K, V, dO, decay, cu_seqlens, M_in, dM_out, state_cache, dQ,
-                      dK, dV, dM_in, workspace, workspace_bytes, stream, events, false);
+    return bwd_common(shape, dtype, Q, K, V, dO, decay, nullptr, cu_seqlens, M_in, dM_out,
+                      state_cache, dQ, dK, dV, nullptr, dM_in, workspace, workspace_bytes, stream,
+                      events, CAUSAL);
 }
 
 int lasp_bwd_bidir(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
                    const void *V, const void *dO, const int32_t *cu_seqlens, const float *M_in,
                    const float *dM_out, const void *state_cache, void *dQ, void *dK, void *dV,
                    float *dM_in, void *workspace, size_t workspace_bytes, void *stream) {
-    return bwd_common(shape, dtype, Q, K, V, dO, nullptr, cu_seqlens, M_in, dM_out, state_cache, dQ,
-                      dK, dV, dM_in, workspace, workspace_bytes, stream, nullptr, true);
+    return bwd_common(shape, dtype, Q, K, V, dO, nullptr, nullptr, cu_seqlens, M_in, dM_out,
+                      state_cache, dQ, dK, dV, nullptr, dM_in, workspace, workspace_bytes, stream,
+                      nullptr, BIDIR);
+}
+
+int lasp_bwd_gated_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                      const void *V, const float *log_g, const void *dO,
+                      const int32_t *cu_seqlens, const float *M_in, const float *dM_out,
+                      const void *state_cache, void *dQ, void *dK, void *dV, float *dlog_g,
+                      float *dM_in, void *workspace, size_t workspace_bytes, void *stream,
+                      void **events) {
+    return bwd_common(shape, dtype, Q, K, V, dO, nullptr, log_g, cu_seqlens, M_in, dM_out,
+                      state_cache, dQ, dK, dV, dlog_g, dM_in, workspace, workspace_bytes, stream,
+                      events, GATED);
+}
+
+int lasp_bwd_gated(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                   const void *V, const float *log_g, const void *dO, const int32_t *cu_seqlens,
+                   const float *M_in, const float *dM_out, const void *state_cache, void *dQ,
+                   void *dK, void *dV, float *dlog_g, float *dM_in, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    return lasp_bwd_gated_ex(shape, dtype, Q, K, V, log_g, dO, cu_seqlens, M_in, dM_out,
+                             state_cache, dQ, dK, dV, dlog_g, dM_in, workspace, workspace_bytes,
+                             stream, nullptr);
 }
 
 int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
@@ -390,7 +487,9 @@ const char *lasp_status_string(int status) {
     switch (status) {
     case LASP_OK: return "ok";
     case LASP_EINVAL: return "invalid argument";
-    case LASP_EUNSUPPORTED: return "unsupported configuration (d in {32,64,128}, chunk in {64,128,256}, dtype fp32/bf16)";
+    case LASP_EUNSUPPORTED:
+        return "unsupported configuration (d in {32,64,128}, chunk in {64,128,256}, dtype fp32/bf16; "
+               "gated form: chunk 64, fp32 only with d <= 64; unmasked form: bf16)";
     case LASP_EWORKSPACE: return "workspace too small";
     case LASP_EHIP: return g_hip_error.empty() ? "HIP error" : g_hip_error.c_str();
     }

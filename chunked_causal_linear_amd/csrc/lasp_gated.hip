@@ -1,0 +1,771 @@
+// HIP kernels (gfx950 / MI355X) for the gated form: a per-token, per-key-channel
+// decay (LASP Appendix A.4, Eq. 24 with the GLA / GateLoop row of Table 5):
+//   kv_p = Diag(g_p) kv_{p-1} + k_p^T v_p,   o_p = q_p kv_p.
+//
+// The gates arrive as log-gates.  Inside a chunk of C = 64 tokens every kernel
+// works with b, the inclusive running sum of the chunk's log-gates in base-2
+// units (b_r = log2(g_0 ... g_r) per channel).  With m a reference row,
+//   o_s = sum_{i<=s} (q_s 2^(b_s - b_m)) . (k_i 2^(b_m - b_i)) v_i + (q_s 2^(b_s)) P_t
+// where P_t is the state entering the chunk.  The intra-chunk score products
+// run on MFMA over 32x32 tiles with m the first row of the query tile: for a
+// key tile left of the query tile both factors are at most 1, so nothing
+// overflows whatever the gates.  On a diagonal tile the key factor grows up to
+// 2^(b_m - b_(m+31)); a tile whose log-gate drop stays within SPAN2 bits uses
+// the same products, any other tile sums its pairs one by one with the exact
+// factor 2^(b_s - b_i) <= 1.  The chunk state and its reverse are
+//   P_{t+1} = Diag(gam_t) P_t + (K_t 2^(b_last - b))^T V_t,   gam_t = 2^(b_last)
+//   R_{t-1} = Diag(gam_t) R_t + (Q_t 2^b)^T dO_t
+// carried over segments of G chunks (local kernels) and across segments by a
+// scan, as in the decayed form.  The log-gate gradient uses that the map
+// depends on the running log-gate B through 2^(B_s - B_i) and 2^(B_s) only:
+// dl/dB_u = q_u dq_u - k_u dk_u per channel, and the log-gate of token p enters
+// every B_u with u >= p, so dlog_g_p is a suffix sum of these; the part of the
+// suffix beyond the chunk is rowsum(R_t . P_{t+1}).
+#include "lasp_device.h"
+
+namespace lasp {
+
+constexpr int GC = 64;            // chunk length of the gated kernels
+constexpr float SPAN2 = 80.f;     // largest log2-gate drop inside a factorised diagonal tile
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bS[r][c] = log2(g_0 ... g_r) for channel c of the chunk whose first log-gate
+// row is lg; rows at or past Ct repeat the last valid one (gate 1).
+template <int D>
+__device__ __forceinline__ void chunk_cumlog(float *bS, const float *lg, int Ct) {
+    constexpr float LOG2E = 1.4426950408889634f;
+    for (int c = threadIdx.x; c < D; c += NTHR) {
+        float run = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < GC; ++r) {
+            if (r < Ct) run += lg[(int64_t)r * D + c] * LOG2E;
+            bS[r * D + c] = run;
+        }
+    }
+}
+
+// 16 bytes of V converted values at p.
+template <typename T>
+__device__ __forceinline__ void store_vec(T *p, const float *f) {
+#pragma unroll
+    for (int j = 0; j < Tr<T>::VEC; j += 4) store4(p + j, f[j], f[j + 1], f[j + 2], f[j + 3]);
+}
+
+// dst[j][c] = src[row(j)][c] * 2^(bS[ref(j)][c] - bS[row(j)][c]) for j < R
+// (zero where row(j) >= Ct): gate-scaled rows, feature index contiguous.
+// ref(j) < 0 means the plain factor 2^(bS[row][c]) (the state side).
+template <typename T, int D, int R, typename RowF, typename RefF>
+__device__ __forceinline__ void stage_gated(T *dst, int pitch, const T *src, const float *bS,
+                                            int Ct, RowF row, RefF ref, bool invert = false) {
+    constexpr int V = Tr<T>::VEC, PR = D / V;
+    for (int i = threadIdx.x; i < R * PR; i += NTHR) {
+        const int j = i / PR, c = (i % PR) * V;
+        const int r = row(j), m = ref(j);
+        float f[V];
+        if (r < Ct) {
+            load16(src + (int64_t)r * D + c, f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float br = bS[r * D + c + e];
+                const float x = m < 0 ? br : (invert ? br - bS[m * D + c + e] : bS[m * D + c + e] - br);
+                f[e] *= ex2(x);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) f[e] = 0.f;
+        }
+        store_vec(dst + j * pitch + c, f);
+    }
+}
+
+// Transposed form: dst[c][j] = (same value), token index contiguous.
+template <typename T, int D, int R, typename RowF, typename RefF>
+__device__ __forceinline__ void stage_gated_T(T *dst, int pitch, const T *src, const float *bS,
+                                              int Ct, RowF row, RefF ref, bool invert = false) {
+    constexpr int V = Tr<T>::VEC;
+    for (int i = threadIdx.x; i < R * (D / V); i += NTHR) {
+        const int j = i % R, c = (i / R) * V;
+        const int r = row(j), m = ref(j);
+        float f[V];
+        if (r < Ct) {
+            load16(src + (int64_t)r * D + c, f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float br = bS[r * D + c + e];
+                const float x = m < 0 ? br : (invert ? br - bS[m * D + c + e] : bS[m * D + c + e] - br);
+                f[e] *= ex2(x);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) f[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) dst[(c + e) * pitch + j] = fromf<T>(f[e]);
+    }
+}
+
+// Span test of the two 32-row tiles of a chunk (uniform over the workgroup).
+template <int D>
+__device__ __forceinline__ void tile_spans(const float *bS, bool &slow0, bool &slow1) {
+    bool s0 = false, s1 = false;
+    for (int c = threadIdx.x; c < D; c += NTHR) {
+        s0 |= bS[c] - bS[31 * D + c] > SPAN2;
+        s1 |= bS[32 * D + c] - bS[63 * D + c] > SPAN2;
+    }
+    slow0 = __syncthreads_or(s0);
+    slow1 = __syncthreads_or(s1);
+}
+
+// Exact gated score of query row s and key row i (i <= s, both in the chunk):
+// sum_c q_s[c] k_i[c] 2^(b_s[c] - b_i[c]), inputs read from global memory.
+template <typename T, int D>
+__device__ float exact_score(const T *Q, const T *K, const float *bS, int s, int i) {
+    float acc = 0.f;
+    for (int c = 0; c < D; ++c)
+        acc += tof(Q[(int64_t)s * D + c]) * tof(K[(int64_t)i * D + c]) *
+               ex2(bS[s * D + c] - bS[i * D + c]);
+    return acc;
+}
+
+// The state entering chunk t (or the reverse state leaving it), combined from
+// the segment state and the local one:  X[dv][dk] = g[dk] seg[dv][dk] + loc[dv][dk].
+__device__ __forceinline__ float comb(const float *seg, const void *loc, bool bf, const float *g,
+                                      int e, int dk) {
+    float l = 0.f;
+    if (loc) l = bf ? tof(((const bf16 *)loc)[e]) : ((const float *)loc)[e];
+    return g[dk] * seg[e] + l;
+}
+
+// ---------------------------------------------------------------------------
+// Forward 1: local states, one workgroup per (segment, head), chunks in order
+// from a zero state at the segment start:
+//   Lc[t] = L, Gc[t] = gate product of the segment's chunks before t;
+//   L = Diag(gam_t) L + (K_t 2^(b_last - b))^T V_t;   Z = L, Gs = all gates.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR) void k_gfwd_local(Params p) {
+    constexpr int PT = GC + Tr<T>::VEC;
+    __shared__ float bS[GC * D];
+    __shared__ __attribute__((aligned(16))) T KT_s[D * PT];
+    __shared__ __attribute__((aligned(16))) T VT_s[D * PT];
+    using TL = Tiles<D / 32, D / 32>;
+
+    const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
+    Seq s;
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const int64_t rb = row_base(p, s, h);
+    const T *K = (const T *)p.K + rb * D;
+    const T *Vg = (const T *)p.V + rb * D;
+    const float *LG = p.LG + rb * D;
+    const bool store_local = p.G > 1;
+
+    f32x16 acc[TL::PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) zero(acc[k]);
+    float gcum = 1.f;   // thread c < D: gate product of channel c
+
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    for (int t = t0; t < t1; ++t) {
+        const int tok = t * GC;
+        const int Ct = min(GC, s.len - tok);
+        const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
+        if (store_local) {
+            T *Lt = (T *)p.Lc + ch * D * D;
+#pragma unroll
+            for (int k = 0; k < TL::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TL::get(k, mi, ni)) store_T(acc[k], Lt, D, mi * 32, ni * 32, Ident());
+            }
+        }
+        if (threadIdx.x < D) p.Gc[ch * D + threadIdx.x] = gcum;
+        __syncthreads();
+        chunk_cumlog<D>(bS, LG + (int64_t)tok * D, Ct);
+        __syncthreads();
+        stage_gated_T<T, D, GC>(KT_s, PT, K + (int64_t)tok * D, bS, Ct, [](int j) { return j; },
+                                [](int) { return GC - 1; });
+        stage_rows_T<T, GC, D>(VT_s, PT, Vg + (int64_t)tok * D, Ct, One());
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TL::PER_WAVE; ++k) {
+            int mi, ni;
+            if (TL::get(k, mi, ni)) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[k][r] *= ex2(bS[(GC - 1) * D + mi * 32 + crow(r)]);
+                gemm<T, GC>(acc[k], KT_s, PT, mi * 32, VT_s, PT, ni * 32);
+            }
+        }
+        if (threadIdx.x < D) gcum *= ex2(bS[(GC - 1) * D + threadIdx.x]);
+    }
+    const int64_t sh = (int64_t)gs * p.H + h;
+    float *Zs = p.Z + sh * D * D;
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) {
+        int mi, ni;
+        if (TL::get(k, mi, ni)) store_T(acc[k], Zs, D, mi * 32, ni * 32, Ident());
+    }
+    if (threadIdx.x < D) p.Gs[sh * D + threadIdx.x] = gcum;
+}
+
+// ---------------------------------------------------------------------------
+// Forward 2: scan over segments, one thread per state element:
+//   Pseg[0] = M_in;  Pseg[s+1] = Diag(Gs[s]) Pseg[s] + Z[s];  M_out = last.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NTHR) void k_gfwd_segscan(Params p) {
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    const int ih = blockIdx.x / NB;
+    const int e = (blockIdx.x % NB) * NTHR + threadIdx.x;
+    if (e >= D * D) return;
+    const int i = ih / p.H, h = ih % p.H;
+    Seq s;
+    seq_fill(p, i, s);
+    const int dv = e / D, dk = e % D;
+    const int64_t mo = ((int64_t)ih * D + dk) * D + dv;   // [dk][dv] of the API states
+    float P = p.M_in ? p.M_in[mo] : 0.f;
+    const int nS = min(s.S, p.n_segs_ub - s.s0);
+    for (int sl = 0; sl < nS; ++sl) {
+        const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
+        p.Pseg[sh * D * D + e] = P;
+        P = p.Gs[sh * D + dk] * P + p.Z[sh * D * D + e];
+    }
+    if (p.M_out) p.M_out[mo] = P;
+}
+
+// ---------------------------------------------------------------------------
+// Forward 3: output, one workgroup per (chunk, head).
+//   O = (Q 2^b) P_t + sum over tile pairs J <= I of
+//       [(Q_I 2^(b - b_mI)) (K_J 2^(b_mI - b))^T masked] V_J
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR) void k_gfwd_out(Params p) {
+    constexpr int V = Tr<T>::VEC;
+    constexpr int PD = D + V, PS = GC + V, PX = PD > PS ? PD : PS;
+    __shared__ float bS[GC * D];
+    __shared__ __attribute__((aligned(16))) T QA[GC * PD];
+    __shared__ __attribute__((aligned(16))) T KA[96 * PD];
+    __shared__ __attribute__((aligned(16))) T XT[D * PX];   // P_t^T (pitch PD), then V^T (pitch PS)
+    __shared__ __attribute__((aligned(16))) T S_s[GC * PS];
+    using TO = Tiles<GC / 32, D / 32>;
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = lid % p.H, gc = lid / p.H;
+    Seq s;
+    int t;
+    if (!chunk_seq(p, gc, s, t)) return;
+    const int tok = t * GC;
+    const int Ct = min(GC, s.len - tok);
+    const int sl = t / p.G;
+    if (s.s0 + sl >= p.n_segs_ub) return;   // only with malformed cu_seqlens
+    const int64_t rb = row_base(p, s, h) + tok;
+    const T *Q = (const T *)p.Q + rb * D;
+    const T *K = (const T *)p.K + rb * D;
+    const T *Vg = (const T *)p.V + rb * D;
+    T *O = (T *)p.O + rb * D;
+    const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
+    const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
+
+    chunk_cumlog<D>(bS, p.LG + rb * D, Ct);
+    {   // P_t^T [dv][dk] into XT
+        const float *Ps = p.Pseg + sh * D * D;
+        const void *Lt = p.G > 1 ? (const void *)((const char *)p.Lc + ch * D * D * sizeof(T)) : nullptr;
+        const float *g = p.Gc + ch * D;
+        for (int e = threadIdx.x; e < D * D; e += NTHR) {
+            const int dv = e / D, dk = e % D;
+            XT[dv * PD + dk] = fromf<T>(comb(Ps, Lt, sizeof(T) == 2, g, e, dk));
+        }
+    }
+    __syncthreads();
+    stage_gated<T, D, GC>(QA, PD, Q, bS, Ct, [](int j) { return j; }, [](int) { return -1; });
+    __syncthreads();
+    f32x16 o[TO::PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < TO::PER_WAVE; ++k) {
+        zero(o[k]);
+        int mi, ni;
+        if (TO::get(k, mi, ni)) gemm<T, D>(o[k], QA, PD, mi * 32, XT, PD, ni * 32);
+    }
+    __syncthreads();
+    // Q_I 2^(b - b_mI);  K rows: (J=0 | ref 0), (J=0 | ref 32), (J=1 | ref 32)
+    stage_gated<T, D, GC>(QA, PD, Q, bS, Ct, [](int j) { return j; },
+                          [](int j) { return j & ~31; }, true);
+    stage_gated<T, D, 96>(KA, PD, K, bS, Ct, [](int j) { return j < 64 ? (j & 31) : j - 32; },
+                          [](int j) { return j < 32 ? 0 : 32; });
+    stage_rows_T<T, GC, D>(XT, PS, Vg, Ct, One());
+    bool slow0, slow1;
+    tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
+    {
+        const int w = wave_id(), l = lane_id();
+        if (w < 3) {
+            const int I = w == 0 ? 0 : 1, J = w == 2 ? 1 : 0;
+            const bool diag = I == J, slow = diag && (I == 0 ? slow0 : slow1);
+            f32x16 st;
+            zero(st);
+            if (!slow) gemm<T, D>(st, QA, PD, 32 * I, KA, PD, 32 * w);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qs = 32 * I + crow(r), ki = 32 * J + (l & 31);
+                float x = 0.f;
+                if (qs < Ct && ki < Ct && ki <= qs)
+                    x = slow ? exact_score<T, D>(Q, K, bS, qs, ki) : st[r];
+                S_s[qs * PS + ki] = fromf<T>(x);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S_s[crow(r) * PS + 32 + (l & 31)] = fromf<T>(0.f);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < TO::PER_WAVE; ++k) {
+        int mi, ni;
+        if (TO::get(k, mi, ni)) {
+            gemm<T, GC>(o[k], S_s, PS, mi * 32, XT, PS, ni * 32);
+            store_rows(o[k], O, D, mi * 32, ni * 32, Ct);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward 1: local reverse states, one workgroup per (segment, head), chunks
+// last to first from a zero state at the segment end:
+//   Rc[t] = R, Hc[t] = gate product of the segment's chunks after t;
+//   R = Diag(gam_t) R + (Q_t 2^b)^T dO_t;   W = R.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR) void k_gbwd_local(Params p) {
+    constexpr int PT = GC + Tr<T>::VEC;
+    __shared__ float bS[GC * D];
+    __shared__ __attribute__((aligned(16))) T QT_s[D * PT];
+    __shared__ __attribute__((aligned(16))) T OT_s[D * PT];
+    using TL = Tiles<D / 32, D / 32>;
+
+    const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
+    Seq s;
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const int64_t rb = row_base(p, s, h);
+    const T *Q = (const T *)p.Q + rb * D;
+    const T *dO = (const T *)p.dO + rb * D;
+    const float *LG = p.LG + rb * D;
+    const bool store_local = p.G > 1;
+
+    f32x16 acc[TL::PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) zero(acc[k]);
+    float hcum = 1.f;
+
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    for (int t = t1 - 1; t >= t0; --t) {
+        const int tok = t * GC;
+        const int Ct = min(GC, s.len - tok);
+        const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
+        if (store_local) {
+            T *Rt = (T *)p.Rc + ch * D * D;
+#pragma unroll
+            for (int k = 0; k < TL::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TL::get(k, mi, ni)) store_T(acc[k], Rt, D, mi * 32, ni * 32, Ident());
+            }
+        }
+        if (threadIdx.x < D) p.Hc[ch * D + threadIdx.x] = hcum;
+        __syncthreads();
+        chunk_cumlog<D>(bS, LG + (int64_t)tok * D, Ct);
+        __syncthreads();
+        stage_gated_T<T, D, GC>(QT_s, PT, Q + (int64_t)tok * D, bS, Ct, [](int j) { return j; },
+                                [](int) { return -1; });
+        stage_rows_T<T, GC, D>(OT_s, PT, dO + (int64_t)tok * D, Ct, One());
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TL::PER_WAVE; ++k) {
+            int mi, ni;
+            if (TL::get(k, mi, ni)) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[k][r] *= ex2(bS[(GC - 1) * D + mi * 32 + crow(r)]);
+                gemm<T, GC>(acc[k], QT_s, PT, mi * 32, OT_s, PT, ni * 32);
+            }
+        }
+        if (threadIdx.x < D) hcum *= ex2(bS[(GC - 1) * D + threadIdx.x]);
+    }
+    float *Ws = p.W + ((int64_t)gs * p.H + h) * D * D;
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) {
+        int mi, ni;
+        if (TL::get(k, mi, ni)) store_T(acc[k], Ws, D, mi * 32, ni * 32, Ident());
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward 2: reverse scan over segments, one thread per state element:
+//   Rseg[S-1] = dM_out;  Rseg[s-1] = Diag(Gs[s]) Rseg[s] + W[s];  dM_in = last.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NTHR) void k_gbwd_segscan(Params p) {
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    const int ih = blockIdx.x / NB;
+    const int e = (blockIdx.x % NB) * NTHR + threadIdx.x;
+    if (e >= D * D) return;
+    const int i = ih / p.H, h = ih % p.H;
+    Seq s;
+    seq_fill(p, i, s);
+    const int dv = e / D, dk = e % D;
+    const int64_t mo = ((int64_t)ih * D + dk) * D + dv;
+    float R = p.dM_out ? p.dM_out[mo] : 0.f;
+    const int nS = min(s.S, p.n_segs_ub - s.s0);
+    for (int sl = nS - 1; sl >= 0; --sl) {
+        const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
+        p.Rseg[sh * D * D + e] = R;
+        R = p.Gs[sh * D + dk] * R + p.W[sh * D * D + e];
+    }
+    if (p.dM_in) p.dM_in[mo] = R;
+}
+
+// ---------------------------------------------------------------------------
+// Backward 3: gradients, one workgroup per (chunk, head), with D_ = dO V^T:
+//   dQ = 2^b . (dO P_t^T) + sum_{J<=I} 2^(b - b_mI) . ([D_ masked]_IJ (K_J 2^(b_mI - b)))
+//   dV = (K 2^(b_last - b)) R_t + sum_{I>=J} [A masked]_IJ^T dO_I   (A: the gated scores)
+//   dK = 2^(b_last - b) . (V R_t^T)
+//        + sum_{I>=J} 2^(b_mJ' - b) . ([D_ masked]_IJ^T (Q_I 2^(b - b_mJ')))
+//   dlog_g[s] = sum_{u>=s in chunk} (q_u dq_u - k_u dk_u) + rowsum(R_t . P_{t+1})
+// with m_I the first row of query tile I and m'_J the last row of key tile J.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct GradLds {
+    static constexpr int V = Tr<T>::VEC, PD = D + V, PS = GC + V, PK = 96 + V;
+    // phase buffers (element offsets into one T array)
+    static constexpr int ROWS = GC * PD, STATE = D * PD, KT3 = D * PK, SC = GC * PS, TT = D * PS;
+    static constexpr int A1 = ROWS + STATE;               // dO, P
+    static constexpr int A2 = 2 * ROWS + KT3 + SC;        // dO, V, K^T x3, scores
+    static constexpr int B2 = ROWS + 96 * PD + TT + SC;   // Q, K x3, dO^T, scores
+    static constexpr int C2 = 2 * ROWS + KT3 + SC;        // V, dO, Q^T x3, scores
+    static constexpr int M1 = A1 > A2 ? A1 : A2, M2 = B2 > C2 ? B2 : C2;
+    static constexpr int ELEMS = M1 > M2 ? M1 : M2;
+    static constexpr int BYTES = ELEMS * (int)sizeof(T) > GC * D * 4 ? ELEMS * (int)sizeof(T) : GC * D * 4;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
+    using L = GradLds<T, D>;
+    constexpr int PD = L::PD, PS = L::PS, PK = L::PK;
+    __shared__ float bS[GC * D];
+    __shared__ float rho[D], Ep[D];
+    __shared__ __attribute__((aligned(16))) char U_raw[L::BYTES];
+    T *U = (T *)U_raw;
+    using TO = Tiles<GC / 32, D / 32>;
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = lid % p.H, gc = lid / p.H;
+    Seq s;
+    int t;
+    if (!chunk_seq(p, gc, s, t)) return;
+    const int tok = t * GC;
+    const int Ct = min(GC, s.len - tok);
+    const int sl = t / p.G;
+    if (s.s0 + sl >= p.n_segs_ub) return;
+    const int64_t rb = row_base(p, s, h) + tok;
+    const T *Q = (const T *)p.Q + rb * D;
+    const T *K = (const T *)p.K + rb * D;
+    const T *Vg = (const T *)p.V + rb * D;
+    const T *dO = (const T *)p.dO + rb * D;
+    const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
+    const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
+    const bool bf = sizeof(T) == 2;
+    const float *Ps = p.Pseg + sh * D * D, *Rs = p.Rseg + sh * D * D;
+    const void *Lt = p.G > 1 ? (const void *)((const char *)p.Lc + ch * D * D * sizeof(T)) : nullptr;
+    const void *Rt = p.G > 1 ? (const void *)((const char *)p.Rc + ch * D * D * sizeof(T)) : nullptr;
+    const float *gP = p.Gc + ch * D, *gR = p.Hc + ch * D;
+    const int w = wave_id(), l = lane_id();
+
+    chunk_cumlog<D>(bS, p.LG + rb * D, Ct);
+    if (threadIdx.x < D) {
+        Ep[threadIdx.x] = 0.f;
+        rho[threadIdx.x] = 0.f;
+    }
+    bool slow0 = false, slow1 = false;
+    T *Sc = nullptr;
+    // Masked 32x32 score tiles A_a . B_b^T into Sc, on waves 0..2: tiles
+    // (a, b) = (0,0), (1,0), (1,1) (lower: b <= a kept) or (0,0), (0,1), (1,1)
+    // (upper: b >= a kept); wave 3 zeroes the remaining block.  B's rows for
+    // wave w start at brow(w).  Gated diagonal tiles over the span limit take
+    // exact(a, b) instead of the product.  tr stores Sc[b][a].
+    auto scores = [&](const T *A, const T *B, auto brow, bool upper, bool tr, bool gated,
+                      auto exact) __attribute__((always_inline)) {
+        if (w < 3) {
+            const int ta = upper ? (w == 2 ? 1 : 0) : (w == 0 ? 0 : 1);
+            const int tb = upper ? (w == 0 ? 0 : 1) : (w == 2 ? 1 : 0);
+            const bool slow = gated && ta == tb && (ta == 0 ? slow0 : slow1);
+            f32x16 st;
+            zero(st);
+            if (!slow) gemm<T, D>(st, A, PD, 32 * ta, B, PD, brow(w));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int a = 32 * ta + crow(r), b = 32 * tb + (l & 31);
+                float x = 0.f;
+                if (a < Ct && b < Ct && (upper ? b >= a : b <= a)) x = slow ? exact(a, b) : st[r];
+                Sc[tr ? b * PS + a : a * PS + b] = fromf<T>(x);
+            }
+        } else {
+            const int ta = upper ? 1 : 0, tb = upper ? 0 : 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int a = 32 * ta + crow(r), b = 32 * tb + (l & 31);
+                Sc[tr ? b * PS + a : a * PS + b] = fromf<T>(0.f);
+            }
+        }
+    };
+    auto no_exact = [](int, int) { return 0.f; };
+
+    // ---- A: dQ -------------------------------------------------------------
+    f32x16 dq[TO::PER_WAVE];
+    {
+        T *dOr = U, *Pk = U + L::ROWS;   // dO rows [GC][PD]; P_t as [dk][dv]
+        stage_rows<T, GC, D>(dOr, PD, dO, Ct);
+        float racc = 0.f;                 // rho[dk] = sum_dv R_t[dk][dv] P_t[dk][dv]
+        const int dk = threadIdx.x % D;   // D divides NTHR: fixed per thread
+        for (int e = threadIdx.x; e < D * D; e += NTHR) {
+            const int dv = e / D;
+            const float pv = comb(Ps, Lt, bf, gP, e, dk), rv = comb(Rs, Rt, bf, gR, e, dk);
+            Pk[dk * PD + dv] = fromf<T>(pv);
+            racc += pv * rv;
+        }
+        __syncthreads();
+        atomicAdd(&rho[dk], racc);
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            zero(dq[k]);
+            int mi, ni;
+            if (TO::get(k, mi, ni)) {
+                gemm<T, D>(dq[k], dOr, PD, mi * 32, Pk, PD, ni * 32);
+                const float sc = ex2(bS[mi * 32 * D + ni * 32 + (l & 31)]);   // 2^(b_mI) of column c
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dq[k][r] *= sc;
+            }
+        }
+        __syncthreads();
+        T *Vr = U + L::ROWS, *KT3 = U + 2 * L::ROWS;
+        Sc = KT3 + L::KT3;
+        stage_rows<T, GC, D>(Vr, PD, Vg, Ct);
+        // K^T in three versions: (J=0 | ref row 0), (J=0 | ref 32), (J=1 | ref 32)
+        stage_gated_T<T, D, 96>(KT3, PK, K, bS, Ct,
+                                [](int j) { return j < 64 ? (j & 31) : j - 32; },
+                                [](int j) { return j < 32 ? 0 : 32; });
+        tile_spans<D>(bS, slow0, slow1);
+        scores(dOr, Vr, [](int ww) { return ww == 2 ? 32 : 0; }, false, false, false, no_exact);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (!TO::get(k, mi, ni)) continue;
+            const bool slow = mi == 0 ? slow0 : slow1;
+            if (mi == 1) gemm<T, 32>(dq[k], Sc, PS, 32, KT3 + 32, PK, ni * 32);
+            if (!slow) gemm<T, 32>(dq[k], Sc + 32 * mi, PS, 32 * mi, KT3 + (mi ? 64 : 0), PK, ni * 32);
+            const int c = ni * 32 + (l & 31), m = mi * 32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qs = m + crow(r);
+                dq[k][r] *= ex2(bS[qs * D + c] - bS[m * D + c]);
+                if (slow && qs < Ct) {
+                    float acc = 0.f;
+                    for (int i = m; i <= qs; ++i)
+                        acc += tof(Sc[qs * PS + i]) * tof(K[(int64_t)i * D + c]) *
+                               ex2(bS[qs * D + c] - bS[i * D + c]);
+                    dq[k][r] += acc;
+                }
+            }
+            store_rows(dq[k], (T *)p.dQ + rb * D, D, mi * 32, ni * 32, Ct);
+        }
+        __syncthreads();
+    }
+
+    // ---- B: dV -------------------------------------------------------------
+    {
+        T *Rv = U, *Kl = U + L::STATE;   // R_t [dv][dk]; K 2^(b_last - b) rows
+        for (int e = threadIdx.x; e < D * D; e += NTHR) {
+            const int dv = e / D, dk = e % D;
+            Rv[dv * PD + dk] = fromf<T>(comb(Rs, Rt, bf, gR, e, dk));
+        }
+        stage_gated<T, D, GC>(Kl, PD, K, bS, Ct, [](int j) { return j; }, [](int) { return GC - 1; });
+        __syncthreads();
+        f32x16 dv[TO::PER_WAVE];
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            zero(dv[k]);
+            int mi, ni;
+            if (TO::get(k, mi, ni)) gemm<T, D>(dv[k], Kl, PD, mi * 32, Rv, PD, ni * 32);
+        }
+        __syncthreads();
+        T *Qg = U, *K3 = U + L::ROWS, *OT = K3 + 96 * PD;
+        Sc = OT + L::TT;
+        stage_gated<T, D, GC>(Qg, PD, Q, bS, Ct, [](int j) { return j; }, [](int j) { return j & ~31; },
+                              true);
+        stage_gated<T, D, 96>(K3, PD, K, bS, Ct, [](int j) { return j < 64 ? (j & 31) : j - 32; },
+                              [](int j) { return j < 32 ? 0 : 32; });
+        stage_rows_T<T, GC, D>(OT, PS, dO, Ct, One());
+        __syncthreads();
+        scores(Qg, K3, [](int ww) { return 32 * ww; }, false, true, true,
+               [&](int a, int b) { return exact_score<T, D>(Q, K, bS, a, b); });
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (!TO::get(k, mi, ni)) continue;
+            gemm<T, GC>(dv[k], Sc, PS, mi * 32, OT, PS, ni * 32);
+            store_rows(dv[k], (T *)p.dV + rb * D, D, mi * 32, ni * 32, Ct);
+        }
+        __syncthreads();
+    }
+
+    // ---- C: dK -------------------------------------------------------------
+    f32x16 dk[TO::PER_WAVE];
+    {
+        T *Vr = U, *RT = U + L::ROWS;   // V rows; R_t as [dk][dv]
+        stage_rows<T, GC, D>(Vr, PD, Vg, Ct);
+        for (int e = threadIdx.x; e < D * D; e += NTHR) {
+            const int dv = e / D, dkk = e % D;
+            RT[dkk * PD + dv] = fromf<T>(comb(Rs, Rt, bf, gR, e, dkk));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            zero(dk[k]);
+            int mi, ni;
+            if (!TO::get(k, mi, ni)) continue;
+            gemm<T, D>(dk[k], Vr, PD, mi * 32, RT, PD, ni * 32);   // X = V R^T
+            // rowsum(R_t . P_{t+1}) gets sum_i k_i 2^(b_last - b_i) X_i
+            const int c = ni * 32 + (l & 31), mJ = mi * 32 + 31;
+            const float bl = bS[(GC - 1) * D + c];
+            float ep = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = mi * 32 + crow(r);
+                if (i < Ct) ep += tof(K[(int64_t)i * D + c]) * ex2(bl - bS[i * D + c]) * dk[k][r];
+            }
+            ep += __shfl_xor(ep, 32);
+            if (l < 32) atomicAdd(&Ep[c], ep);
+            const float sc = ex2(bl - bS[mJ * D + c]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dk[k][r] *= sc;
+        }
+        __syncthreads();
+        T *dOr = U + L::ROWS, *QT3 = U + 2 * L::ROWS;
+        Sc = QT3 + L::KT3;
+        stage_rows<T, GC, D>(dOr, PD, dO, Ct);
+        // Q^T in three versions: (I=0 | ref row 31), (I=1 | ref 31), (I=1 | ref 63)
+        stage_gated_T<T, D, 96>(QT3, PK, Q, bS, Ct, [](int j) { return j < 64 ? j : j - 32; },
+                                [](int j) { return j < 64 ? 31 : 63; }, true);
+        __syncthreads();
+        scores(Vr, dOr, [](int ww) { return ww == 0 ? 0 : 32; }, true, false, false, no_exact);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (!TO::get(k, mi, ni)) continue;
+            const bool slow = mi == 0 ? slow0 : slow1;
+            if (mi == 0) gemm<T, 32>(dk[k], Sc + 32, PS, 0, QT3 + 32, PK, ni * 32);
+            if (!slow) gemm<T, 32>(dk[k], Sc + 32 * mi, PS, 32 * mi, QT3 + (mi ? 64 : 0), PK, ni * 32);
+            const int c = ni * 32 + (l & 31), mJ = mi * 32 + 31;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = mi * 32 + crow(r);
+                dk[k][r] *= ex2(bS[mJ * D + c] - bS[i * D + c]);
+                if (slow && i < Ct) {
+                    float acc = 0.f;
+                    const int se = min(mi * 32 + 32, Ct);
+                    for (int sq = i; sq < se; ++sq)
+                        acc += tof(Sc[i * PS + sq]) * tof(Q[(int64_t)sq * D + c]) *
+                               ex2(bS[sq * D + c] - bS[i * D + c]);
+                    dk[k][r] += acc;
+                }
+            }
+            store_rows(dk[k], (T *)p.dK + rb * D, D, mi * 32, ni * 32, Ct);
+        }
+        __syncthreads();
+    }
+
+    // ---- D: log-gate gradient ------------------------------------------------
+    float *dBs = (float *)U_raw;   // [GC][D]: q dq - k dk
+#pragma unroll
+    for (int k = 0; k < TO::PER_WAVE; ++k) {
+        int mi, ni;
+        if (!TO::get(k, mi, ni)) continue;
+        const int c = ni * 32 + (l & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int su = mi * 32 + crow(r);
+            float x = 0.f;
+            if (su < Ct)
+                x = tof(Q[(int64_t)su * D + c]) * dq[k][r] - tof(K[(int64_t)su * D + c]) * dk[k][r];
+            dBs[su * D + c] = x;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+        const int c = threadIdx.x;
+        float run = ex2(bS[(GC - 1) * D + c]) * rho[c] + Ep[c];
+        float *out = p.dLG + rb * D;
+        for (int su = Ct - 1; su >= 0; --su) {
+            run += dBs[su * D + c];
+            out[(int64_t)su * D + c] = run;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+static inline int round8g(int n) { return (n + 7) & ~7; }
+static inline void grec(hipEvent_t *ev, int i, hipStream_t st) {
+    if (ev) (void)hipEventRecord(ev[i], st);
+}
+
+template <typename T, int D>
+static hipError_t gfwd(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
+    if (p.varlen) launch_setup(p, st);
+    grec(ev, 0, st);
+    hipLaunchKernelGGL((k_gfwd_local<T, D>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
+    grec(ev, 1, st);
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    hipLaunchKernelGGL((k_gfwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    grec(ev, 2, st);
+    if (with_output)
+        hipLaunchKernelGGL((k_gfwd_out<T, D>), dim3(round8g(p.n_chunks_ub * p.H)), dim3(NTHR), 0, st, p);
+    grec(ev, 3, st);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t gbwd(const Params &p, hipStream_t st, hipEvent_t *ev) {
+    if (p.varlen) launch_setup(p, st);
+    grec(ev, 0, st);
+    hipLaunchKernelGGL((k_gbwd_local<T, D>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
+    grec(ev, 1, st);
+    constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    hipLaunchKernelGGL((k_gbwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
+    grec(ev, 2, st);
+    hipLaunchKernelGGL((k_gbwd_grads<T, D>), dim3(round8g(p.n_chunks_ub * p.H)), dim3(NTHR), 0, st, p);
+    grec(ev, 3, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_gated(const Params &p, bool bf, bool with_output, hipStream_t st, hipEvent_t *ev) {
+    if (p.C != GC || !p.LG || !p.Gc || !p.Gs) return hipErrorInvalidValue;
+    switch (p.D) {
+    case 32: return bf ? gfwd<bf16, 32>(p, with_output, st, ev) : gfwd<float, 32>(p, with_output, st, ev);
+    case 64: return bf ? gfwd<bf16, 64>(p, with_output, st, ev) : gfwd<float, 64>(p, with_output, st, ev);
+    case 128: return bf ? gfwd<bf16, 128>(p, with_output, st, ev) : hipErrorInvalidValue;
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_gated(const Params &p, bool bf, hipStream_t st, hipEvent_t *ev) {
+    if (p.C != GC || !p.LG || !p.dLG || !p.Gc || !p.Gs || !p.Hc) return hipErrorInvalidValue;
+    switch (p.D) {
+    case 32: return bf ? gbwd<bf16, 32>(p, st, ev) : gbwd<float, 32>(p, st, ev);
+    case 64: return bf ? gbwd<bf16, 64>(p, st, ev) : gbwd<float, 64>(p, st, ev);
+    case 128: return bf ? gbwd<bf16, 128>(p, st, ev) : hipErrorInvalidValue;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lasp

@@ -37,6 +37,12 @@ struct Params {
     float *W;      // [segs][H][D][D] f32: local reverse state at each segment start
     float *Rfin;   // [nseq][H][D][D] f32 or null: reverse state before each sequence's first token, [dv][dk]
     int parts;     // row-block products: workgroups per (segment, head, product)
+    // gated form
+    const float *LG;   // [B, H, N, D] f32 log-gates (key channels)
+    float *dLG;        // [B, H, N, D] f32 log-gate gradient
+    float *Gc;         // [chunks][H][D] f32: gate product of the segment's chunks before each chunk
+    float *Gs;         // [segs][H][D] f32: gate product of each segment
+    float *Hc;         // [chunks][H][D] f32: gate product of the segment's chunks after each chunk
 };
 
 // Enqueue the forward kernels: (packed-batch tables), local chunk states,
@@ -53,6 +59,16 @@ hipError_t launch_bwd(const Params &p, bool bf16, hipStream_t stream, hipEvent_t
 // totals, segment scan (Pfin = the summed state), O = Q M.  Backward: (tables),
 // reverse totals, reverse scan (Rfin = the summed gradient state), then
 // dQ = dO M^T, dV = K dM, dK = V dM^T; Pfin must be valid.
+// Gated form (per-token, per-key-channel gates given as logs; chunk 64; f32
+// with D <= 64 or bf16).  Same kernel sequence and events as launch_fwd /
+// launch_bwd; the forward also fills Gc and Gs, the backward Hc.
+hipError_t launch_fwd_gated(const Params &p, bool bf16, bool with_output, hipStream_t stream,
+                            hipEvent_t *ev = nullptr);
+hipError_t launch_bwd_gated(const Params &p, bool bf16, hipStream_t stream, hipEvent_t *ev = nullptr);
+
+// Packed-batch tables (chunk_prefix, seg_prefix) on the stream.
+void launch_setup(const Params &p, hipStream_t stream);
+
 hipError_t launch_fwd_bidir(const Params &p, bool with_output, hipStream_t stream);
 hipError_t launch_bwd_bidir(const Params &p, hipStream_t stream);
 

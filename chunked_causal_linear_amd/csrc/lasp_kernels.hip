@@ -26,302 +26,9 @@
 // one workgroup per (chunk, head), combining the segment state with the local
 // one.  All products run on MFMA (32x32x16 bf16 or 32x32x2 f32) with operands
 // staged in LDS so that the contraction index is contiguous for every operand.
-#include "lasp_internal.h"
+#include "lasp_device.h"
 
 namespace lasp {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-struct bf16 {
-    uint16_t u;
-};
-
-template <typename T> struct Tr;
-template <> struct Tr<float> {
-    using frag = f32x4;
-    static constexpr int VEC = 4;   // elements per 16 bytes
-};
-template <> struct Tr<bf16> {
-    using frag = bf16x8_t;
-    static constexpr int VEC = 8;
-};
-
-constexpr int NTHR = 256;   // 4 waves of 64
-constexpr int NWAVE = 4;
-
-// ---------------------------------------------------------------------------
-// MFMA micro-kernel.  32x32 output tile, fp32 accumulate.  Lane l holds, for
-// both element types, output rows (r/4)*8 + (l/32)*4 + r%4 (r = 0..15) of
-// column l%32.  An operand fragment is 16 bytes per lane: row (l%32) of A (or
-// column of B), contraction elements [(l/32)*VEC, (l/32)*VEC + VEC) of a
-// 2*VEC-wide k-step.  bf16: one 32x32x16 MFMA; f32: four 32x32x2 MFMAs where
-// step s pairs element s of both lane halves (A and B agree on the pairing).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void mma(f32x16 &c, const bf16x8_t &a, const bf16x8_t &b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ void mma(f32x16 &c, const f32x4 &a, const f32x4 &b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], b[1], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], b[2], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], b[3], c, 0, 0, 0);
-}
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
-// Row (within the 32x32 tile) of accumulator element r for this lane.
-__device__ __forceinline__ int crow(int r, int l = threadIdx.x & 63) {
-    return (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
-}
-
-__device__ __forceinline__ float tof(float x) { return x; }
-__device__ __forceinline__ float tof(bf16 x) { return __uint_as_float(((uint32_t)x.u) << 16); }
-template <typename T> __device__ __forceinline__ T fromf(float x);
-template <> __device__ __forceinline__ float fromf<float>(float x) { return x; }
-template <> __device__ __forceinline__ bf16 fromf<bf16>(float x) {
-    __bf16 h = (__bf16)x;   // round to nearest even (v_cvt_pk_bf16_f32)
-    bf16 r;
-    r.u = __builtin_bit_cast(uint16_t, h);
-    return r;
-}
-
-// 16-byte load of VEC elements, widened to float.
-__device__ __forceinline__ void load16(const float *p, float *f) {
-    float4 v = *(const float4 *)p;
-    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
-}
-__device__ __forceinline__ void load16(const bf16 *p, float *f) {
-    uint4 v = *(const uint4 *)p;
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(w[i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-}
-
-// Store 4 consecutive values (converted) at p.
-__device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
-    *(float4 *)p = make_float4(a, b, c, d);
-}
-__device__ __forceinline__ void store4(bf16 *p, float a, float b, float c, float d) {
-    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-    const bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};   // RNE, two packed cvts
-    *(bf16x4_t *)p = v;
-}
-
-// lambda^e with lambda = 2^l2; lambda^0 = 1 exactly (also for lambda = 0).
-__device__ __forceinline__ float dpow(float l2, float e) {
-    return e == 0.f ? 1.f : __builtin_amdgcn_exp2f(e * l2);
-}
-__device__ __forceinline__ float head_log2_decay(const Params &p, int h) {
-    return p.decay ? log2f(p.decay[h]) : 0.f;
-}
-
-// ---------------------------------------------------------------------------
-// Sequence bookkeeping
-// ---------------------------------------------------------------------------
-struct Seq {
-    int i;          // sequence index
-    int64_t tok0;   // first token (packed batch: offset inside N)
-    int len;        // tokens
-    int T, S;       // chunks, segments
-    int c0, s0;     // first global chunk / segment
-};
-
-__device__ __forceinline__ int last_le(const int32_t *pre, int n, int x) {
-    // largest i in [0, n) with pre[i] <= x (pre non-decreasing, pre[0] = 0)
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= x) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
-// Token range of packed sequence i, clamped into [0, N] so that malformed
-// cu_seqlens can never address outside the tensors.
-__device__ __forceinline__ void packed_bounds(const Params &p, int i, int &tok0, int &len) {
-    const int a = min(max(p.cu[i], 0), p.N);
-    const int b = min(max(p.cu[i + 1], a), p.N);
-    tok0 = a;
-    len = b - a;
-}
-
-__device__ __forceinline__ void seq_fill(const Params &p, int i, Seq &s) {
-    s.i = i;
-    if (!p.varlen) {
-        s.tok0 = 0;
-        s.len = p.N;
-        s.T = p.T_fixed;
-        s.S = p.S_fixed;
-        s.c0 = i * p.T_fixed;
-        s.s0 = i * p.S_fixed;
-    } else {
-        int tok0, len;
-        packed_bounds(p, i, tok0, len);
-        s.tok0 = tok0;
-        s.len = len;
-        s.c0 = p.chunk_prefix[i];
-        s.T = p.chunk_prefix[i + 1] - s.c0;
-        s.s0 = p.seg_prefix[i];
-        s.S = p.seg_prefix[i + 1] - s.s0;
-    }
-}
-
-// Global chunk gc -> (sequence, local chunk t).  False if gc is past the end.
-__device__ __forceinline__ bool chunk_seq(const Params &p, int gc, Seq &s, int &t) {
-    int i;
-    if (!p.varlen) {
-        if (gc >= p.nseq * p.T_fixed) return false;
-        i = gc / p.T_fixed;
-    } else {
-        if (gc >= p.chunk_prefix[p.nseq]) return false;
-        i = last_le(p.chunk_prefix, p.nseq, gc);
-    }
-    seq_fill(p, i, s);
-    t = gc - s.c0;
-    return gc < p.n_chunks_ub;
-}
-
-__device__ __forceinline__ bool seg_seq(const Params &p, int gs, Seq &s, int &sl) {
-    int i;
-    if (!p.varlen) {
-        if (gs >= p.nseq * p.S_fixed) return false;
-        i = gs / p.S_fixed;
-    } else {
-        if (gs >= p.seg_prefix[p.nseq]) return false;
-        i = last_le(p.seg_prefix, p.nseq, gs);
-    }
-    seq_fill(p, i, s);
-    sl = gs - s.s0;
-    return gs < p.n_segs_ub;
-}
-
-// First row (token) of sequence s, head h, in the [B, H, N, d] layout.
-__device__ __forceinline__ int64_t row_base(const Params &p, const Seq &s, int h) {
-    return p.varlen ? ((int64_t)h * p.N + s.tok0) : (((int64_t)s.i * p.H + h) * p.N);
-}
-
-// Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Map ids so
-// that each XCD gets a contiguous range of logical work items: neighbouring
-// chunks of one head then share that XCD's L2.  n is a multiple of 8.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-    return (bid & 7) * (n >> 3) + (bid >> 3);
-}
-
-// ---------------------------------------------------------------------------
-// LDS staging and tile GEMM helpers (all 256 threads take part in staging)
-// ---------------------------------------------------------------------------
-// dst[r][c] = src[r][c] for a R x W tile; rows >= nvalid become zero.
-template <typename T, int R, int W>
-__device__ __forceinline__ void stage_rows(T *dst, int pitch, const T *src, int nvalid) {
-    constexpr int V = Tr<T>::VEC;
-    constexpr int PR = W / V;
-    for (int i = threadIdx.x; i < R * PR; i += NTHR) {
-        const int r = i / PR, c = (i % PR) * V;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r < nvalid) v = *(const uint4 *)(src + (int64_t)r * W + c);
-        *(uint4 *)(dst + r * pitch + c) = v;
-    }
-}
-
-// dst[c][r] = scale(r) * src[r][c] (transposed, token index contiguous);
-// rows >= nvalid become zero.
-template <typename T, int R, int W, typename F>
-__device__ __forceinline__ void stage_rows_T(T *dst, int pitch, const T *src, int nvalid,
-                                             F scale) {
-    constexpr int V = Tr<T>::VEC;
-    for (int i = threadIdx.x; i < R * (W / V); i += NTHR) {
-        const int r = i % R, c = (i / R) * V;
-        float f[V];
-        if (r < nvalid) {
-            load16(src + (int64_t)r * W + c, f);
-            const float s = scale(r);
-#pragma unroll
-            for (int e = 0; e < V; ++e) f[e] *= s;
-        } else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) f[e] = 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < V; ++e) dst[(c + e) * pitch + r] = fromf<T>(f[e]);
-    }
-}
-
-struct One {
-    __device__ float operator()(int) const { return 1.f; }
-};
-
-// acc += A[m0..m0+32)[0..K) * B[n0..n0+32)[0..K)^T, A and B in LDS with the
-// contraction index contiguous (pitches pa, pb in elements).
-template <typename T, int K>
-__device__ __forceinline__ void gemm(f32x16 &acc, const T *As, int pa, int m0, const T *Bs,
-                                     int pb, int n0) {
-    constexpr int V = Tr<T>::VEC;
-    using Fr = typename Tr<T>::frag;
-    const int l = lane_id();
-    const T *ap = As + (m0 + (l & 31)) * pa + (l >> 5) * V;
-    const T *bp = Bs + (n0 + (l & 31)) * pb + (l >> 5) * V;
-#pragma unroll
-    for (int k = 0; k < K; k += 2 * V) {
-        const Fr a = *(const Fr *)(ap + k);
-        const Fr b = *(const Fr *)(bp + k);
-        mma(acc, a, b);
-    }
-}
-
-// Y[n0 + col][m0 + row] = f(acc, m0 + row, n0 + col): transposed store of a
-// 32x32 tile (4 consecutive rows per lane per store).  Y in LDS or global.
-template <typename T, typename F>
-__device__ __forceinline__ void store_T(const f32x16 &acc, T *Y, int64_t py, int m0, int n0,
-                                        F f) {
-    const int l = lane_id(), col = l & 31, g = l >> 5;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int m = m0 + q * 8 + g * 4;
-        store4(Y + (int64_t)(n0 + col) * py + m, f(acc[q * 4 + 0], m + 0, n0 + col),
-               f(acc[q * 4 + 1], m + 1, n0 + col), f(acc[q * 4 + 2], m + 2, n0 + col),
-               f(acc[q * 4 + 3], m + 3, n0 + col));
-    }
-}
-
-struct Ident {
-    __device__ float operator()(float x, int, int) const { return x; }
-};
-
-// G[(m0+row)][n0+col] = acc for rows < nvalid (row-major global store).
-template <typename T>
-__device__ __forceinline__ void store_rows(const f32x16 &acc, T *G, int64_t ld, int m0, int n0,
-                                           int nvalid) {
-    const int col = lane_id() & 31;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = m0 + crow(r);
-        if (row < nvalid) G[(int64_t)row * ld + n0 + col] = fromf<T>(acc[r]);
-    }
-}
-
-// Tiles of a (MT*32) x (NT*32) output are dealt to the 4 waves round-robin.
-template <int MT, int NT>
-struct Tiles {
-    static constexpr int N = MT * NT;
-    static constexpr int PER_WAVE = (N + NWAVE - 1) / NWAVE;
-    __device__ static bool get(int k, int &mi, int &ni) {
-        const int tile = wave_id() + k * NWAVE;
-        mi = tile / NT;
-        ni = tile % NT;
-        return tile < N;
-    }
-};
-
-__device__ __forceinline__ void zero(f32x16 &a) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) a[r] = 0.f;
-}
 
 // ---------------------------------------------------------------------------
 // Packed-batch tables: chunk_prefix[i] = sum_{i'<i} ceil(L_i'/C),
@@ -1866,6 +1573,10 @@ static inline int round8(int n) { return (n + 7) & ~7; }
 template <typename T, int D> struct Block {
     static constexpr int BT = (sizeof(T) == 4 && D == 128) ? 32 : 64;
 };
+
+void launch_setup(const Params &p, hipStream_t st) {
+    hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
+}
 
 static inline void rec(hipEvent_t *ev, int i, hipStream_t st) {
     if (ev) (void)hipEventRecord(ev[i], st);

@@ -66,7 +66,8 @@ typedef enum { LASP_FP32 = 0, LASP_BF16 = 1 } lasp_dtype;
 typedef enum {
     LASP_OK = 0,
     LASP_EINVAL = 1,        /* bad argument: dims, NULL, alignment, overlap, nseq/B */
-    LASP_EUNSUPPORTED = 2,  /* d not in {32,64,128}, chunk not in {64,128,256}, dtype */
+    LASP_EUNSUPPORTED = 2,  /* d not in {32,64,128}, chunk not in {64,128,256}, dtype;
+                               the gated and unmasked forms' own limits */
     LASP_EWORKSPACE = 3,    /* workspace_bytes smaller than the size query returns */
     LASP_EHIP = 4           /* a HIP call or kernel launch failed */
 } lasp_status;
@@ -169,6 +170,58 @@ int lasp_bwd_bidir(const lasp_shape *shape, lasp_dtype dtype,
                    const float *dM_out, const void *state_cache,
                    void *dQ, void *dK, void *dV, float *dM_in,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Gated form: a per-token, per-key-channel gate g_p in (0, 1]^d (LASP
+ * Appendix A.4: the general recurrence of Eq. 24 with the GLA / GateLoop row
+ * of Table 5):
+ *
+ *   kv_p = Diag(g_p) kv_{p-1} + k_p^T v_p,   kv_{-1} = M_in,   o_p = q_p kv_p
+ *   M_out = kv_{L-1}
+ *
+ * i.e. o_p = sum_{i<=p} (q_p . (k_i * G_(i,p))) v_i + (q_p * G_(-1,p)) M_in with
+ * G_(i,p) = g_(i+1) * ... * g_p per channel.  The gate scales the key rows of
+ * the d x d state.  With every g_p = lambda this is lasp_fwd with decay lambda.
+ *   log_g   device float32 [B, H, N, d] (the layout of Q): log g_p, finite and
+ *           <= 0.  Larger values are accepted but products of gates above 1 may
+ *           overflow.
+ * The backward, for l = <dO, O> + <dM_out, M_out>, also returns
+ *   dlog_g  device float32 [B, H, N, d]: dl/d(log g_p).
+ * Restrictions: shape->chunk must be 64 (the kernels' chunk length), and
+ * LASP_FP32 needs d <= 64 (else LASP_EUNSUPPORTED).  Numbers: inside a chunk
+ * the gates enter the bf16 MFMA operands as factors 2^(b_s - b_m) and
+ * 2^(b_m - b_i) (b: running log2 of the gates; m: the first row of a 32-row
+ * query tile), each at most 1 off the diagonal tiles; a diagonal tile whose
+ * gates fall by more than 2^80 is summed pair by pair in float32 instead.
+ * Sizes come from the lasp_gated_* queries (the gated state cache also holds
+ * per-chunk gate products); buffers, pointers, alignment, errors and the events
+ * of the _ex variants are as for lasp_fwd / lasp_bwd (no decay argument). */
+size_t lasp_gated_state_cache_bytes(const lasp_shape *shape, lasp_dtype dtype);
+size_t lasp_gated_fwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype,
+                                      int with_state_cache);
+size_t lasp_gated_bwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype,
+                                      int with_state_cache);
+int lasp_fwd_gated(const lasp_shape *shape, lasp_dtype dtype,
+                   const void *Q, const void *K, const void *V, const float *log_g,
+                   const int32_t *cu_seqlens, const float *M_in,
+                   void *O, float *M_out, void *state_cache,
+                   void *workspace, size_t workspace_bytes, void *stream);
+int lasp_bwd_gated(const lasp_shape *shape, lasp_dtype dtype,
+                   const void *Q, const void *K, const void *V, const float *log_g,
+                   const void *dO, const int32_t *cu_seqlens, const float *M_in,
+                   const float *dM_out, const void *state_cache,
+                   void *dQ, void *dK, void *dV, float *dlog_g, float *dM_in,
+                   void *workspace, size_t workspace_bytes, void *stream);
+int lasp_fwd_gated_ex(const lasp_shape *shape, lasp_dtype dtype,
+                      const void *Q, const void *K, const void *V, const float *log_g,
+                      const int32_t *cu_seqlens, const float *M_in,
+                      void *O, float *M_out, void *state_cache,
+                      void *workspace, size_t workspace_bytes, void *stream, void **events);
+int lasp_bwd_gated_ex(const lasp_shape *shape, lasp_dtype dtype,
+                      const void *Q, const void *K, const void *V, const float *log_g,
+                      const void *dO, const int32_t *cu_seqlens, const float *M_in,
+                      const float *dM_out, const void *state_cache,
+                      void *dQ, void *dK, void *dV, float *dlog_g, float *dM_in,
+                      void *workspace, size_t workspace_bytes, void *stream, void **events);
 
 /* Human-readable text for a status code (for LASP_EHIP: the last HIP error of
  * the calling thread). */

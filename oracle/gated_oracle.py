@@ -27,7 +27,7 @@ import numpy as np
 
 __all__ = [
     "gated_recurrent_fwd", "gated_recurrent_bwd", "gated_unrolled_fwd",
-    "batched_gated_fwd", "batched_gated_bwd", "gated_sampled",
+    "batched_gated_fwd", "batched_gated_bwd", "gated_sampled", "gated_closed_states",
 ]
 
 
@@ -181,3 +181,19 @@ def gated_sampled(q, k, v, log_g, do, rows, m_in=None, dm_out=None):
         out["dV"][n] = k[p] @ G
         out["dLG"][n] = np.exp(lg[p]) * np.sum(G * kv_prev, axis=1)
     return out
+
+
+def gated_closed_states(q, k, v, log_g, do, m_in=None, dm_out=None):
+    """M_out and dM_in of a long sequence in closed form (section 4 at the ends):
+        M_out = sum_i Diag(exp(B_{L-1} - B_i)) k_i^T v_i + Diag(exp(B_{L-1})) M_in
+        dM_in = sum_u Diag(exp(B_u)) q_u^T do_u + Diag(exp(B_{L-1})) dM_out"""
+    q, k, v, lg, do = _f64(q), _f64(k), _f64(v), _f64(log_g), _f64(do)
+    L, d = q.shape
+    m = _state(d, m_in)
+    dm = _state(d, dm_out)
+    if L == 0:
+        return m, dm
+    B = np.cumsum(lg, axis=0)
+    m_out = (k * np.exp(B[L - 1][None, :] - B)).T @ v + np.exp(B[L - 1])[:, None] * m
+    dm_in = (q * np.exp(B)).T @ do + np.exp(B[L - 1])[:, None] * dm
+    return m_out, dm_in

@@ -170,3 +170,44 @@ def test_bidir_rejects_bad_arguments(L):
     assert fwd(O=p[1]) == EINVAL and bwd(dK=p[0]) == EINVAL    # output aliases an input
     assert fwd(ws_bytes=nf - 1) == EWS and bwd(ws_bytes=nb - 1) == EWS
     assert fwd(cu=p[8]) == EINVAL                               # cu_seqlens without nseq
+
+
+def test_gated_rejects_bad_arguments(L):
+    """The gated entry points: chunk 64 only, float32 only with d <= 64, log_g
+    (and dlog_g) required, aligned and disjoint from the outputs."""
+    s = Shape(1, 2, 300, 64, 64, 0)
+    p = [fake(i) for i in range(14)]
+    nf = L.lasp_gated_fwd_workspace_bytes(ctypes.byref(s), 1, 0)
+    nb = L.lasp_gated_bwd_workspace_bytes(ctypes.byref(s), 1, 0)
+    assert nf > 0 and nb > 0
+
+    def fwd(shape=s, dt=1, ws_bytes=nf, **kw):
+        a = dict(Q=p[0], K=p[1], V=p[2], LG=p[9], cu=None, M_in=None, O=p[3], M_out=None,
+                 cache=None, ws=p[5])
+        a.update(kw)
+        return L.lasp_fwd_gated(ctypes.byref(shape), dt, a["Q"], a["K"], a["V"], a["LG"], a["cu"],
+                                a["M_in"], a["O"], a["M_out"], a["cache"], a["ws"], ws_bytes, None)
+
+    def bwd(shape=s, dt=1, ws_bytes=nb, **kw):
+        a = dict(Q=p[0], K=p[1], V=p[2], LG=p[9], dO=p[3], cu=None, M_in=None, dM_out=None,
+                 cache=None, dQ=p[4], dK=p[5], dV=p[6], dLG=p[10], dM_in=None, ws=p[7])
+        a.update(kw)
+        return L.lasp_bwd_gated(ctypes.byref(shape), dt, a["Q"], a["K"], a["V"], a["LG"], a["dO"],
+                                a["cu"], a["M_in"], a["dM_out"], a["cache"], a["dQ"], a["dK"],
+                                a["dV"], a["dLG"], a["dM_in"], a["ws"], ws_bytes, None)
+
+    for c in (128, 256):
+        assert fwd(shape=Shape(1, 2, 300, 64, c, 0)) == EUNSUP
+        assert bwd(shape=Shape(1, 2, 300, 64, c, 0)) == EUNSUP
+    assert fwd(shape=Shape(1, 2, 300, 128, 64, 0), dt=0) == EUNSUP
+    assert L.lasp_gated_state_cache_bytes(ctypes.byref(Shape(1, 2, 300, 128, 64, 0)), 0) == 0
+    assert L.lasp_gated_state_cache_bytes(ctypes.byref(Shape(1, 2, 300, 128, 64, 0)), 1) > 0
+    assert fwd(LG=None) == EINVAL and bwd(LG=None) == EINVAL and bwd(dLG=None) == EINVAL
+    assert fwd(LG=ctypes.c_void_p(A + 9 * GAP + 4)) == EINVAL        # misaligned log_g
+    assert fwd(O=p[9]) == EINVAL                                      # O aliases log_g
+    assert bwd(dLG=p[9]) == EINVAL and bwd(dLG=p[4]) == EINVAL       # dlog_g aliases
+    assert fwd(ws_bytes=nf - 1) == EWS and bwd(ws_bytes=nb - 1) == EWS
+    assert fwd(cu=p[8]) == EINVAL
+    # the gated state cache also holds per-chunk states and gate products
+    assert (L.lasp_gated_state_cache_bytes(ctypes.byref(s), 1)
+            > L.lasp_state_cache_bytes(ctypes.byref(s), 1))

@@ -240,8 +240,11 @@ def test_batched_packed_equals_separate():
 def test_sampled_rows_match_full():
     L, d = 40, 4
     q, k, v, lg, do, m, dm = case(L, d, 17, strong=True)
-    o, _ = go.gated_recurrent_fwd(q, k, v, lg, m)
-    dq, dk, dv, dlg, _ = go.gated_recurrent_bwd(q, k, v, lg, do, m, dm)
+    o, mo = go.gated_recurrent_fwd(q, k, v, lg, m)
+    dq, dk, dv, dlg, dmi = go.gated_recurrent_bwd(q, k, v, lg, do, m, dm)
+    cm, cdm = go.gated_closed_states(q, k, v, lg, do, m, dm)
+    np.testing.assert_allclose(cm, mo, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(cdm, dmi, rtol=1e-10, atol=1e-12)
     rows = [0, 1, 17, 38, 39]
     s = go.gated_sampled(q, k, v, lg, do, rows, m, dm)
     for name, full in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv), ("dLG", dlg)):

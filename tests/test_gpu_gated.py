@@ -1,0 +1,159 @@
+"""GPU parity of the gated form: lasp_fwd_gated / lasp_bwd_gated through the C
+ABI against the oracle's gated recurrence ("Linear Attention Sequence
+Parallelism", Appendix A.4, Eq. 24 with the GLA / GateLoop row of Table 5).
+Metric: max|gpu - ref| / max|ref| per tensor, <= 1e-4 for float32 inputs and
+<= 2e-2 for bf16 inputs (the same bar as the causal parity tests).  Gate
+recipes: "gla" (every diagonal tile takes the factorised MFMA products),
+"strong" (every diagonal tile is summed pair by pair), "mixed" (both)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_causal_linear_amd as cca
+from chunked_causal_linear_amd.workloads import GATED, make_inputs, small
+from oracle import gated_oracle as go
+from test_gpu_parity import TOL, check, dev, np64, rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    cca.lib()       # raises if the HIP library is missing: no fallback
+    yield
+
+
+def run_gated(inp, use_cache=True):
+    sh = inp["shape"]
+    Q, K, V, LG = dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(inp["log_g"])
+    cu, M_in = dev(inp["cu_seqlens"]), dev(inp["M_in"])
+    O, M_out, cache = cca.fwd_gated(Q, K, V, LG, sh["chunk"], cu, M_in, want_state_cache=use_cache)
+    dQ, dK, dV, dLG, dM_in = cca.bwd_gated(Q, K, V, LG, dev(inp["dO"]), sh["chunk"], cu, M_in,
+                                           dev(inp["dM_out"]), cache)
+    torch.cuda.synchronize()
+    return dict(O=O, M_out=M_out, dQ=dQ, dK=dK, dV=dV, dLG=dLG, dM_in=dM_in)
+
+
+def oracle_gated(inp):
+    a = {k: np64(inp[k]) for k in ("Q", "K", "V", "dO", "log_g", "M_in", "dM_out")}
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy()
+    O, Mo = go.batched_gated_fwd(a["Q"], a["K"], a["V"], a["log_g"], a["M_in"], cu)
+    dQ, dK, dV, dLG, dMi = go.batched_gated_bwd(a["Q"], a["K"], a["V"], a["log_g"], a["dO"],
+                                                a["M_in"], a["dM_out"], cu)
+    return dict(O=O, M_out=Mo, dQ=dQ, dK=dK, dV=dV, dLG=dLG, dM_in=dMi)
+
+
+SMALL = [
+    small("gated fp32 d32 B2 H2 gla Min dMout ragged", "fp32", B=2, H=2, N=300, d=32, seed=60,
+          gates="gla", m_in_scale=0.1, dm_out_scale=0.1),
+    small("gated fp32 d64 strong Min dMout", "fp32", B=1, H=2, N=200, d=64, seed=61,
+          gates="strong", m_in_scale=0.1, dm_out_scale=0.1),
+    small("gated fp32 d64 mixed", "fp32", B=1, H=1, N=333, d=64, seed=62, gates="mixed"),
+    small("gated bf16 d64 B2 H2 gla", "bf16", B=2, H=2, N=300, d=64, seed=63, gates="gla"),
+    small("gated bf16 d128 mixed Min dMout", "bf16", B=1, H=2, N=700, d=128, seed=64,
+          gates="mixed", m_in_scale=0.1, dm_out_scale=0.1),
+    small("gated bf16 d128 strong", "bf16", B=1, H=1, N=257, d=128, seed=65, gates="strong"),
+    small("gated bf16 d32 B3 gla Min dMout", "bf16", B=3, H=1, N=150, d=32, seed=66, gates="gla",
+          m_in_scale=0.1, dm_out_scale=0.1),
+    small("gated bf16 packed d64 edge lengths", "bf16", H=2, d=64, seed=67, gates="mixed",
+          lengths=[1, 63, 64, 65, 0, 200, 33, 128], m_in_scale=0.1, dm_out_scale=0.1),
+    small("gated fp32 packed d32 edge lengths", "fp32", H=2, d=32, seed=68, gates="gla",
+          lengths=[0, 1, 64, 127, 31, 2], m_in_scale=0.1, dm_out_scale=0.1),
+    small("gated bf16 one token", "bf16", B=1, H=1, N=1, d=64, seed=69, gates="gla",
+          m_in_scale=0.1, dm_out_scale=0.1),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_gated_small(w):
+    say("case:", w.name)
+    inp = make_inputs(w)
+    check(w.name, run_gated(inp), oracle_gated(inp), TOL[w.dtype])
+
+
+@pytest.mark.parametrize("G", ["1", "3"])
+def test_gated_segment_sizes(G, monkeypatch):
+    monkeypatch.setenv("LASP_SEGMENT_CHUNKS", G)
+    w = small("gated fp32 d32 many chunks", "fp32", B=2, H=2, N=64 * 11 + 17, d=32, seed=70,
+              gates="mixed", m_in_scale=0.1, dm_out_scale=0.1)
+    say("case: gated segment chunks", G)
+    inp = make_inputs(w)
+    check("gated G=" + G, run_gated(inp), oracle_gated(inp), TOL["fp32"])
+
+
+def test_gated_recompute_equals_cache():
+    w = small("gated bf16 d128", "bf16", B=1, H=2, N=900, d=128, seed=71, gates="gla",
+              m_in_scale=0.1, dm_out_scale=0.1)
+    inp = make_inputs(w)
+    say("case: gated recompute vs cache")
+    a = run_gated(inp, use_cache=True)
+    b = run_gated(inp, use_cache=False)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_constant_gates_match_the_decayed_path():
+    """log g = log(lambda_h) everywhere: the gated kernels and the decayed ones
+    (lasp_fwd / lasp_bwd with decay) compute the same map."""
+    w = small("gated fp32 d64 constant", "fp32", B=1, H=2, N=500, d=64, seed=72,
+              m_in_scale=0.1, dm_out_scale=0.1)
+    inp = make_inputs(w)
+    lam = torch.tensor([0.97, 0.8])
+    inp["log_g"] = torch.log(lam)[None, :, None, None].expand(1, 2, 500, 64).contiguous()
+    say("case: constant gates vs decay")
+    g = run_gated(inp)
+    Q, K, V, dO = (dev(inp[x]) for x in ("Q", "K", "V", "dO"))
+    O, M_out, cache = cca.fwd(Q, K, V, 64, dev(lam), None, dev(inp["M_in"]))
+    dQ, dK, dV, dM_in = cca.bwd(Q, K, V, dO, 64, dev(lam), None, dev(inp["M_in"]),
+                                dev(inp["dM_out"]), cache)
+    ref = dict(O=O, M_out=M_out, dQ=dQ, dK=dK, dV=dV, dM_in=dM_in)
+    errs = {k: rel(np64(g[k]), np64(ref[k])) for k in ref}
+    say(" ".join("%s=%.2e" % kv for kv in errs.items()))
+    assert all(e <= TOL["fp32"] for e in errs.values()), errs
+
+
+def test_gated_rejects_bad_configurations():
+    inp = make_inputs(small("fp32 d128", "fp32", B=1, H=1, N=64, d=128, seed=73, gates="gla"))
+    with pytest.raises(cca.LaspError) as e:
+        cca.fwd_gated(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(inp["log_g"]))
+    assert e.value.status == 2
+    inp = make_inputs(small("bf16 C128", "bf16", B=1, H=1, N=64, d=64, seed=74, gates="gla"))
+    with pytest.raises(cca.LaspError) as e:
+        cca.fwd_gated(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(inp["log_g"]), 128)
+    assert e.value.status == 2
+
+
+def test_gated_full_size_sampled():
+    """bf16 B1 H32 N131072 d128 C64 with GLA gates, M_in and dM_out (the
+    benchmark's gated workload): sampled rows of O, dQ, dK, dV and dlog_g from
+    the oracle's prefix / suffix sums, and the full M_out and dM_in, on four
+    heads."""
+    w = dataclasses.replace(GATED, dm_out_scale=0.01, seed=75)
+    say("case:", w.name)
+    inp = make_inputs(w)
+    out = run_gated(inp)
+    r = np.random.default_rng(175)
+    L = w.N
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, L - 65, L - 1], r.integers(0, L, 10)]))
+    idx = torch.as_tensor(rows)
+    names = ("O", "dQ", "dK", "dV", "dLG")
+    acc = {k: ([], []) for k in names + ("M_out", "dM_in")}
+    for h in (0, 9, 22, 31):
+        q, k, v, lg, do = (np64(inp[x][0, h]) for x in ("Q", "K", "V", "log_g", "dO"))
+        mi, dmo = np64(inp["M_in"][0, h]), np64(inp["dM_out"][0, h])
+        ref = go.gated_sampled(q, k, v, lg, do, rows, mi, dmo)
+        mo, dmi = go.gated_closed_states(q, k, v, lg, do, mi, dmo)
+        for name in names:
+            acc[name][0].append(np64(out[name][0, h].index_select(0, idx.to(out[name].device))))
+            acc[name][1].append(ref[name])
+        acc["M_out"][0].append(np64(out["M_out"][0, h]))
+        acc["M_out"][1].append(mo)
+        acc["dM_in"][0].append(np64(out["dM_in"][0, h]))
+        acc["dM_in"][1].append(dmi)
+    errs = {k: rel(np.concatenate(g), np.concatenate(rv)) for k, (g, rv) in acc.items()}
+    say(w.name, " ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {k: e for k, e in errs.items() if not e <= TOL["bf16"]}
+    assert not bad, bad
