@@ -12,9 +12,11 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   cpu_baseline  the float64 C oracle (token recurrence) timed on the host cores
                 over a bounded sample of the same workload;
   kernels_ms    average duration of every kernel of the step.
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3] [--bidir]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3] [--bidir | --gated]
 --bidir times the unmasked (bidirectional) form instead (lasp_fwd_bidir +
 lasp_bwd_bidir on the same inputs, no decay) and prints its own line.
+--gated times the gated form (lasp_fwd_gated + lasp_bwd_gated) on its own
+workload: bf16 B1 H32 N131072 d128 C64 with GLA-style gates, M_in and M_out.
 """
 import argparse
 import ctypes
@@ -144,6 +146,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bidir", action="store_true",
                     help="time the unmasked (bidirectional) form instead")
+    ap.add_argument("--gated", action="store_true",
+                    help="time the gated (per-channel decay) form on its own workload")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate "
                          "the HBM byte counters of a profiler against known traffic")
@@ -167,9 +171,9 @@ def main():
         print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n}), flush=True)
         return
     import chunked_causal_linear_amd as cca
-    from chunked_causal_linear_amd.workloads import CONFIGS, make_inputs
+    from chunked_causal_linear_amd.workloads import CONFIGS, GATED, make_inputs
 
-    w = CONFIGS[a.config]
+    w = GATED if a.gated else CONFIGS[a.config]
     if a.chunk:
         import dataclasses
         w = dataclasses.replace(w, chunk=a.chunk, name=w.name.replace("C%d" % w.chunk, "C%d" % a.chunk))
@@ -183,6 +187,8 @@ def main():
 
     if a.bidir:
         return bench_bidir(a, w, sh, inp, torch, cca)
+    if a.gated:
+        return bench_gated(a, w, sh, inp, torch, cca)
     S = cca.Shape(sh["B"], sh["H"], sh["N"], sh["d"], C, sh["nseq"])
     dt_code = cca.LASP_BF16 if w.dtype == "bf16" else cca.LASP_FP32
     wsf = torch.empty(max(1, cca.fwd_workspace_bytes(S, dt_code, True)), dtype=torch.uint8,
@@ -324,6 +330,115 @@ def bench_bidir(a, w, sh, inp, torch, cca):
                      "traffic": None, "kernel": "whole step", "algorithmic_bytes": bytes_,
                      "algorithmic_flops": flops},
         "gpu": torch.cuda.get_device_name(torch.device("cuda:0")),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def gated_work(sh, P):
+    """Algorithmic HBM bytes and flops per launch of the gated kernels (U token-
+    heads, e element bytes, log-gates and their gradient float32).  P: the
+    library's array sizes (local_b per-chunk states, seg_b per-segment float32
+    states, gate_c / gate_s per-chunk / per-segment gate products).  Flops count
+    useful causal work: intra-chunk products over c <= r (2d(C+1) per output
+    role) and the d x d state products (2d^2 each)."""
+    B, H, N, d, C = sh["B"], sh["H"], sh["N"], sh["d"], sh["chunk"]
+    e = 2 if sh["dtype"] == "bf16" else 4
+    U = B * H * N
+    nS = sh["nseq"] or B
+    st_io = nS * H * d * d * 4
+    T, G = U * d * e, U * d * 4                  # one token array, the log-gate array
+    lb, sb, gc, gs = P["local_b"], P["seg_b"], P["gate_c"], P["gate_s"]
+    intra = 2 * d * (C + 1)
+    return {
+        "fwd_local": (2 * T + G + lb + sb + gc + gs, 2 * U * d * d),
+        "fwd_scan": (2 * sb + gs + 2 * st_io, sb // 2),
+        "fwd_out": (4 * T + G + lb + sb + gc, U * (intra + 2 * d * d)),
+        "bwd_local": (2 * T + G + lb + sb + gc, 2 * U * d * d),
+        "bwd_scan": (2 * sb + gs + 2 * st_io, sb // 2),
+        "bwd_grads": (7 * T + 2 * G + 2 * lb + 2 * sb + 2 * gc, U * (3 * intra + 8 * d * d)),
+    }
+
+
+def bench_gated(a, w, sh, inp, torch, cca):
+    """One step = lasp_fwd_gated + lasp_bwd_gated (local states, scan, output;
+    reverse local states, reverse scan, gradients incl. the log-gate gradient),
+    with per-kernel HIP events recorded on the launch stream inside the library."""
+    Q, K, V, dO, LG = inp["Q"], inp["K"], inp["V"], inp["dO"], inp["log_g"]
+    cu, M_in, dM_out = inp["cu_seqlens"], inp["M_in"], inp["dM_out"]
+    C = sh["chunk"]
+    dev = torch.device("cuda:0")
+    S = cca.Shape(sh["B"], sh["H"], sh["N"], sh["d"], C, sh["nseq"])
+    dt_code = cca.LASP_BF16 if w.dtype == "bf16" else cca.LASP_FP32
+    wsf = torch.empty(max(1, cca.gated_fwd_workspace_bytes(S, dt_code, True)), dtype=torch.uint8,
+                      device=dev)
+    wsb = torch.empty(max(1, cca.gated_bwd_workspace_bytes(S, dt_code, True)), dtype=torch.uint8,
+                      device=dev)
+    L = hip()
+    n = a.warmup + a.steps
+    evf = [make_events(L, 4) for _ in range(n)]
+    evb = [make_events(L, 4) for _ in range(n)]
+
+    def step(i):
+        O, M_out, cache = cca.fwd_gated(Q, K, V, LG, C, cu, M_in, workspace=wsf, events=evf[i])
+        g = cca.bwd_gated(Q, K, V, LG, dO, C, cu, M_in, dM_out, cache, workspace=wsb,
+                          events=evb[i])
+        return O, g
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.warmup, n):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    names = ["fwd_local", "fwd_scan", "fwd_out", "bwd_local", "bwd_scan", "bwd_grads"]
+    kms = {k: 0.0 for k in names}
+    for i in range(a.warmup, n):
+        for j in range(3):
+            kms[names[j]] += elapsed(L, evf[i][j], evf[i][j + 1]) / a.steps
+            kms[names[3 + j]] += elapsed(L, evb[i][j], evb[i][j + 1]) / a.steps
+    # array sizes from the size queries: fwd workspace with a cache = tables + Z;
+    # cache = Lc + Pseg + Gc + Gs; bwd workspace adds Rc, Rseg, W, Hc
+    U, d = sh["B"] * sh["H"] * sh["N"], sh["d"]
+    e = 2 if w.dtype == "bf16" else 4
+    table_b = 0 if not sh["nseq"] else -(-8 * (sh["nseq"] + 1) // 256) * 256
+    seg_b = cca.gated_fwd_workspace_bytes(S, dt_code, True) - table_b
+    cache_b = cca.gated_state_cache_bytes(S, dt_code)
+    bws = cca.gated_bwd_workspace_bytes(S, dt_code, True) - table_b
+    # bws = local_b + 2 seg_b + gate_c;  cache_b = local_b + seg_b + gate_c + gate_s
+    chunks = (sh["N"] + C - 1) // C * sh["B"] if not sh["nseq"] else sh["N"] // C + sh["nseq"]
+    gate_c = -(-chunks * sh["H"] * d * 4 // 256) * 256
+    local_b = bws - 2 * seg_b - gate_c
+    gate_s = cache_b - local_b - seg_b - gate_c
+    work = gated_work(sh, dict(local_b=local_b, seg_b=seg_b, gate_c=gate_c, gate_s=gate_s))
+    dom = max(names, key=lambda k: kms[k])
+    bytes_, flops = work[dom]
+    t_dom = kms[dom] * 1e-3
+    if bytes_ / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": bytes_ / t_dom / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof.update(kernel="gated " + dom, ms=kms[dom], algorithmic_bytes=bytes_,
+                algorithmic_flops=flops)
+    tokens = sh["B"] * sh["N"]
+    step_bytes = sum(b for b, _ in work.values())
+    out = {
+        "metric": "gated (per-channel decay) linear-attn fwd+bwd tokens/s, d=128, N=131072",
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": sh["B"], "H": sh["H"], "N": sh["N"], "d": d,
+                   "chunk": C, "nseq": sh["nseq"], "gates": w.gates, "m_in": M_in is not None,
+                   "parallelism": "single GPU"},
+        "kernels_ms": kms,
+        "step_algorithmic_GBs": step_bytes / (ms * 1e-3) / 1e9,
+        "roofline": roof,
+        "gpu": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(out), flush=True)
 

@@ -31,18 +31,27 @@ constexpr float SPAN2 = 80.f;     // largest log2-gate drop inside a factorised 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // bS[r][c] = log2(g_0 ... g_r) for channel c of the chunk whose first log-gate
-// row is lg; rows at or past Ct repeat the last valid one (gate 1).
+// row is lg; rows at or past Ct repeat the last valid one (gate 1).  All
+// threads take part: NTHR / D parts of the rows per channel, each summed in
+// registers, then offset by the totals of the parts before it.  The caller
+// synchronizes before anyone reads bS and after anyone last read it.
 template <int D>
 __device__ __forceinline__ void chunk_cumlog(float *bS, const float *lg, int Ct) {
     constexpr float LOG2E = 1.4426950408889634f;
-    for (int c = threadIdx.x; c < D; c += NTHR) {
-        float run = 0.f;
-#pragma unroll 8
-        for (int r = 0; r < GC; ++r) {
-            if (r < Ct) run += lg[(int64_t)r * D + c] * LOG2E;
-            bS[r * D + c] = run;
-        }
-    }
+    constexpr int NP = NTHR / D, RP = GC / NP;
+    const int c = threadIdx.x % D, r0 = (threadIdx.x / D) * RP;
+    float x[RP];
+#pragma unroll
+    for (int j = 0; j < RP; ++j) x[j] = r0 + j < Ct ? lg[(int64_t)(r0 + j) * D + c] * LOG2E : 0.f;
+#pragma unroll
+    for (int j = 1; j < RP; ++j) x[j] += x[j - 1];
+    bS[(r0 + RP - 1) * D + c] = x[RP - 1];
+    __syncthreads();
+    float off = 0.f;
+    for (int q = RP - 1; q < r0; q += RP) off += bS[q * D + c];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < RP; ++j) bS[(r0 + j) * D + c] = x[j] + off;
 }
 
 // 16 bytes of V converted values at p.
@@ -52,56 +61,124 @@ __device__ __forceinline__ void store_vec(T *p, const float *f) {
     for (int j = 0; j < Tr<T>::VEC; j += 4) store4(p + j, f[j], f[j + 1], f[j + 2], f[j + 3]);
 }
 
-// dst[j][c] = src[row(j)][c] * 2^(bS[ref(j)][c] - bS[row(j)][c]) for j < R
-// (zero where row(j) >= Ct): gate-scaled rows, feature index contiguous.
-// ref(j) < 0 means the plain factor 2^(bS[row][c]) (the state side).
-template <typename T, int D, int R, typename RowF, typename RefF>
-__device__ __forceinline__ void stage_gated(T *dst, int pitch, const T *src, const float *bS,
-                                            int Ct, RowF row, RefF ref, bool invert = false) {
-    constexpr int V = Tr<T>::VEC, PR = D / V;
-    for (int i = threadIdx.x; i < R * PR; i += NTHR) {
-        const int j = i / PR, c = (i % PR) * V;
-        const int r = row(j), m = ref(j);
-        float f[V];
-        if (r < Ct) {
-            load16(src + (int64_t)r * D + c, f);
+// Stage R rows of a [*, D] token array into LDS: row j of the tile is token
+// row(j) (zero at or past Ct), scaled in place by scale(j, r, c, f[V]) for the
+// V features c.. of token r.  Row form: dst[j][c]; transposed: dst[c][j].
+// Every load of a thread is issued before the first store.
+template <typename T, int D, int R, bool TRANS, typename RowF, typename ScaleF>
+__device__ __forceinline__ void stage(T *dst, int pitch, const T *src, int Ct, RowF row,
+                                      ScaleF scale) {
+    constexpr int V = Tr<T>::VEC, PR = D / V, N = R * PR, IT = (N + NTHR - 1) / NTHR;
+    float f[IT][V];
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-                const float br = bS[r * D + c + e];
-                const float x = m < 0 ? br : (invert ? br - bS[m * D + c + e] : bS[m * D + c + e] - br);
-                f[e] *= ex2(x);
-            }
+    for (int u = 0; u < IT; ++u) {
+        const int i = u * NTHR + threadIdx.x;
+        const int j = TRANS ? i % R : i / PR, c = TRANS ? (i / R) * V : (i % PR) * V;
+        const int r = row(j);
+        if (i < N && r < Ct) {
+            load16(src + (int64_t)r * D + c, f[u]);
         } else {
 #pragma unroll
-            for (int e = 0; e < V; ++e) f[e] = 0.f;
+            for (int e = 0; e < V; ++e) f[u][e] = 0.f;
         }
-        store_vec(dst + j * pitch + c, f);
+    }
+#pragma unroll
+    for (int u = 0; u < IT; ++u) {
+        const int i = u * NTHR + threadIdx.x;
+        if (i >= N) continue;
+        const int j = TRANS ? i % R : i / PR, c = TRANS ? (i / R) * V : (i % PR) * V;
+        const int r = row(j);
+        if (r < Ct) scale(j, r, c, f[u]);
+        if (TRANS) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) dst[(c + e) * pitch + j] = fromf<T>(f[u][e]);
+        } else {
+            store_vec(dst + j * pitch + c, f[u]);
+        }
     }
 }
 
-// Transposed form: dst[c][j] = (same value), token index contiguous.
+struct RowId {
+    __device__ int operator()(int j) const { return j; }
+};
+struct NoScale {
+    template <typename F> __device__ void operator()(int, int, int, F) const {}
+};
+
+// Gate factors for stage(): f *= 2^(b[ref] - b[r]) (invert: 2^(b[r] - b[ref]));
+// ref < 0: f *= 2^(b[r]).
+template <int V, typename RefF>
+struct GateScale {
+    const float *bS;
+    RefF ref;
+    bool invert;
+    int D;
+    __device__ void operator()(int j, int r, int c, float *f) const {
+        const int m = ref(j);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float br = bS[r * D + c + e];
+            const float x = m < 0 ? br : (invert ? br - bS[m * D + c + e] : bS[m * D + c + e] - br);
+            f[e] *= ex2(x);
+        }
+    }
+};
+
+template <typename T, int D, int R, typename RowF, typename RefF>
+__device__ __forceinline__ void stage_gated(T *dst, int pitch, const T *src, const float *bS,
+                                            int Ct, RowF row, RefF ref, bool invert = false) {
+    stage<T, D, R, false>(dst, pitch, src, Ct, row,
+                          GateScale<Tr<T>::VEC, RefF>{bS, ref, invert, D});
+}
+
 template <typename T, int D, int R, typename RowF, typename RefF>
 __device__ __forceinline__ void stage_gated_T(T *dst, int pitch, const T *src, const float *bS,
                                               int Ct, RowF row, RefF ref, bool invert = false) {
-    constexpr int V = Tr<T>::VEC;
-    for (int i = threadIdx.x; i < R * (D / V); i += NTHR) {
-        const int j = i % R, c = (i / R) * V;
-        const int r = row(j), m = ref(j);
-        float f[V];
-        if (r < Ct) {
-            load16(src + (int64_t)r * D + c, f);
+    stage<T, D, R, true>(dst, pitch, src, Ct, row,
+                         GateScale<Tr<T>::VEC, RefF>{bS, ref, invert, D});
+}
+
+// The D x D states entering (or leaving) a chunk, combined from the segment
+// state and the local one, NS of them side by side:
+//   x_s[dv][dk] = g_s[dk] seg_s[dv][dk] + loc_s[dv][dk]    (loc_s null: 0)
+// in the [dv][dk] layout of the state arrays.  f(dv, dk0, x) receives V
+// consecutive dk of every state; loads are issued in batches of IB groups.
+template <typename T, int D, int NS, typename F>
+__device__ __forceinline__ void for_states(const float *const *seg, const void *const *loc,
+                                           const float *const *g, F f) {
+    constexpr int V = Tr<T>::VEC, IT = (D * D + NTHR * V - 1) / (NTHR * V);
+    constexpr int IB = IT < 4 ? IT : 4;
+    static_assert(IT % IB == 0, "batches");
+    for (int b = 0; b < IT; b += IB) {
+        float x[IB][NS][V];
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-                const float br = bS[r * D + c + e];
-                const float x = m < 0 ? br : (invert ? br - bS[m * D + c + e] : bS[m * D + c + e] - br);
-                f[e] *= ex2(x);
+        for (int u = 0; u < IB; ++u) {
+            const int e = ((b + u) * NTHR + threadIdx.x) * V;
+            if (e >= D * D) continue;
+            const int dk = e % D;
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                float sg[V], gg[V], lc[V];
+#pragma unroll
+                for (int j = 0; j < V; j += 4) {
+                    load16(seg[q] + e + j, sg + j);
+                    load16(g[q] + dk + j, gg + j);
+                }
+                if (loc[q]) {
+                    load16((const T *)loc[q] + e, lc);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < V; ++j) lc[j] = 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < V; ++j) x[u][q][j] = gg[j] * sg[j] + lc[j];
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) f[e] = 0.f;
         }
 #pragma unroll
-        for (int e = 0; e < V; ++e) dst[(c + e) * pitch + j] = fromf<T>(f[e]);
+        for (int u = 0; u < IB; ++u) {
+            const int e = ((b + u) * NTHR + threadIdx.x) * V;
+            if (e < D * D) f(e / D, e % D, x[u]);
+        }
     }
 }
 
@@ -126,15 +203,6 @@ __device__ float exact_score(const T *Q, const T *K, const float *bS, int s, int
         acc += tof(Q[(int64_t)s * D + c]) * tof(K[(int64_t)i * D + c]) *
                ex2(bS[s * D + c] - bS[i * D + c]);
     return acc;
-}
-
-// The state entering chunk t (or the reverse state leaving it), combined from
-// the segment state and the local one:  X[dv][dk] = g[dk] seg[dv][dk] + loc[dv][dk].
-__device__ __forceinline__ float comb(const float *seg, const void *loc, bool bf, const float *g,
-                                      int e, int dk) {
-    float l = 0.f;
-    if (loc) l = bf ? tof(((const bf16 *)loc)[e]) : ((const float *)loc)[e];
-    return g[dk] * seg[e] + l;
 }
 
 // ---------------------------------------------------------------------------
@@ -185,7 +253,7 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_local(Params p) {
         __syncthreads();
         stage_gated_T<T, D, GC>(KT_s, PT, K + (int64_t)tok * D, bS, Ct, [](int j) { return j; },
                                 [](int) { return GC - 1; });
-        stage_rows_T<T, GC, D>(VT_s, PT, Vg + (int64_t)tok * D, Ct, One());
+        stage<T, D, GC, true>(VT_s, PT, Vg + (int64_t)tok * D, Ct, RowId(), NoScale());
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TL::PER_WAVE; ++k) {
@@ -268,13 +336,12 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_out(Params p) {
 
     chunk_cumlog<D>(bS, p.LG + rb * D, Ct);
     {   // P_t^T [dv][dk] into XT
-        const float *Ps = p.Pseg + sh * D * D;
-        const void *Lt = p.G > 1 ? (const void *)((const char *)p.Lc + ch * D * D * sizeof(T)) : nullptr;
-        const float *g = p.Gc + ch * D;
-        for (int e = threadIdx.x; e < D * D; e += NTHR) {
-            const int dv = e / D, dk = e % D;
-            XT[dv * PD + dk] = fromf<T>(comb(Ps, Lt, sizeof(T) == 2, g, e, dk));
-        }
+        const float *seg[1] = {p.Pseg + sh * D * D};
+        const void *loc[1] = {p.G > 1 ? (const void *)((const T *)p.Lc + ch * D * D) : nullptr};
+        const float *g[1] = {p.Gc + ch * D};
+        for_states<T, D, 1>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
+            store_vec(XT + dv * PD + dk, x[0]);
+        });
     }
     __syncthreads();
     stage_gated<T, D, GC>(QA, PD, Q, bS, Ct, [](int j) { return j; }, [](int) { return -1; });
@@ -292,7 +359,7 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_out(Params p) {
                           [](int j) { return j & ~31; }, true);
     stage_gated<T, D, 96>(KA, PD, K, bS, Ct, [](int j) { return j < 64 ? (j & 31) : j - 32; },
                           [](int j) { return j < 32 ? 0 : 32; });
-    stage_rows_T<T, GC, D>(XT, PS, Vg, Ct, One());
+    stage<T, D, GC, true>(XT, PS, Vg, Ct, RowId(), NoScale());
     bool slow0, slow1;
     tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
     {
@@ -375,7 +442,7 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_local(Params p) {
         __syncthreads();
         stage_gated_T<T, D, GC>(QT_s, PT, Q + (int64_t)tok * D, bS, Ct, [](int j) { return j; },
                                 [](int) { return -1; });
-        stage_rows_T<T, GC, D>(OT_s, PT, dO + (int64_t)tok * D, Ct, One());
+        stage<T, D, GC, true>(OT_s, PT, dO + (int64_t)tok * D, Ct, RowId(), NoScale());
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TL::PER_WAVE; ++k) {
@@ -450,6 +517,7 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     constexpr int PD = L::PD, PS = L::PS, PK = L::PK;
     __shared__ float bS[GC * D];
     __shared__ float rho[D], Ep[D];
+    __shared__ float rpart[NTHR * Tr<T>::VEC];   // rho partial sums, [slot][dk]
     __shared__ __attribute__((aligned(16))) char U_raw[L::BYTES];
     T *U = (T *)U_raw;
     using TO = Tiles<GC / 32, D / 32>;
@@ -470,7 +538,6 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     const T *dO = (const T *)p.dO + rb * D;
     const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
     const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
-    const bool bf = sizeof(T) == 2;
     const float *Ps = p.Pseg + sh * D * D, *Rs = p.Rseg + sh * D * D;
     const void *Lt = p.G > 1 ? (const void *)((const char *)p.Lc + ch * D * D * sizeof(T)) : nullptr;
     const void *Rt = p.G > 1 ? (const void *)((const char *)p.Rc + ch * D * D * sizeof(T)) : nullptr;
@@ -520,17 +587,36 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     f32x16 dq[TO::PER_WAVE];
     {
         T *dOr = U, *Pk = U + L::ROWS;   // dO rows [GC][PD]; P_t as [dk][dv]
-        stage_rows<T, GC, D>(dOr, PD, dO, Ct);
-        float racc = 0.f;                 // rho[dk] = sum_dv R_t[dk][dv] P_t[dk][dv]
-        const int dk = threadIdx.x % D;   // D divides NTHR: fixed per thread
-        for (int e = threadIdx.x; e < D * D; e += NTHR) {
-            const int dv = e / D;
-            const float pv = comb(Ps, Lt, bf, gP, e, dk), rv = comb(Rs, Rt, bf, gR, e, dk);
-            Pk[dk * PD + dv] = fromf<T>(pv);
-            racc += pv * rv;
+        stage<T, D, GC, false>(dOr, PD, dO, Ct, RowId(), NoScale());
+        // rho[dk] = sum_dv R_t[dk][dv] P_t[dk][dv]; each thread keeps one group
+        // of V consecutive dk (NTHR * V is a multiple of D)
+        constexpr int V = Tr<T>::VEC;
+        float racc[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) racc[j] = 0.f;
+        const float *seg[2] = {Ps, Rs};
+        const void *loc[2] = {Lt, Rt};
+        const float *g[2] = {gP, gR};
+        for_states<T, D, 2>(seg, loc, g, [&](int dv, int dk, const float (*x)[V]) {
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                Pk[(dk + j) * PD + dv] = fromf<T>(x[0][j]);
+                racc[j] += x[0][j] * x[1][j];
+            }
+        });
+        // the threads sharing a dk group sum in a fixed order (no atomics:
+        // the result must not depend on timing)
+        constexpr int SLOTS = (NTHR * V < D * D ? NTHR * V : D * D) / D;
+        if (threadIdx.x * V < D * D) {
+#pragma unroll
+            for (int j = 0; j < V; ++j) rpart[threadIdx.x * V + j] = racc[j];
         }
         __syncthreads();
-        atomicAdd(&rho[dk], racc);
+        if (threadIdx.x < D) {
+            float r = 0.f;
+            for (int q = 0; q < SLOTS; ++q) r += rpart[q * D + threadIdx.x];
+            rho[threadIdx.x] = r;
+        }
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             zero(dq[k]);
@@ -545,7 +631,7 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
         __syncthreads();
         T *Vr = U + L::ROWS, *KT3 = U + 2 * L::ROWS;
         Sc = KT3 + L::KT3;
-        stage_rows<T, GC, D>(Vr, PD, Vg, Ct);
+        stage<T, D, GC, false>(Vr, PD, Vg, Ct, RowId(), NoScale());
         // K^T in three versions: (J=0 | ref row 0), (J=0 | ref 32), (J=1 | ref 32)
         stage_gated_T<T, D, 96>(KT3, PK, K, bS, Ct,
                                 [](int j) { return j < 64 ? (j & 31) : j - 32; },
@@ -581,9 +667,13 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     // ---- B: dV -------------------------------------------------------------
     {
         T *Rv = U, *Kl = U + L::STATE;   // R_t [dv][dk]; K 2^(b_last - b) rows
-        for (int e = threadIdx.x; e < D * D; e += NTHR) {
-            const int dv = e / D, dk = e % D;
-            Rv[dv * PD + dk] = fromf<T>(comb(Rs, Rt, bf, gR, e, dk));
+        {
+            const float *seg[1] = {Rs};
+            const void *loc[1] = {Rt};
+            const float *g[1] = {gR};
+            for_states<T, D, 1>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
+                store_vec(Rv + dv * PD + dk, x[0]);
+            });
         }
         stage_gated<T, D, GC>(Kl, PD, K, bS, Ct, [](int j) { return j; }, [](int) { return GC - 1; });
         __syncthreads();
@@ -601,7 +691,7 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
                               true);
         stage_gated<T, D, 96>(K3, PD, K, bS, Ct, [](int j) { return j < 64 ? (j & 31) : j - 32; },
                               [](int j) { return j < 32 ? 0 : 32; });
-        stage_rows_T<T, GC, D>(OT, PS, dO, Ct, One());
+        stage<T, D, GC, true>(OT, PS, dO, Ct, RowId(), NoScale());
         __syncthreads();
         scores(Qg, K3, [](int ww) { return 32 * ww; }, false, true, true,
                [&](int a, int b) { return exact_score<T, D>(Q, K, bS, a, b); });
@@ -620,10 +710,15 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     f32x16 dk[TO::PER_WAVE];
     {
         T *Vr = U, *RT = U + L::ROWS;   // V rows; R_t as [dk][dv]
-        stage_rows<T, GC, D>(Vr, PD, Vg, Ct);
-        for (int e = threadIdx.x; e < D * D; e += NTHR) {
-            const int dv = e / D, dkk = e % D;
-            RT[dkk * PD + dv] = fromf<T>(comb(Rs, Rt, bf, gR, e, dkk));
+        stage<T, D, GC, false>(Vr, PD, Vg, Ct, RowId(), NoScale());
+        {
+            const float *seg[1] = {Rs};
+            const void *loc[1] = {Rt};
+            const float *g[1] = {gR};
+            for_states<T, D, 1>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
+#pragma unroll
+                for (int j = 0; j < Tr<T>::VEC; ++j) RT[(dk + j) * PD + dv] = fromf<T>(x[0][j]);
+            });
         }
         __syncthreads();
 #pragma unroll
@@ -650,7 +745,7 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
         __syncthreads();
         T *dOr = U + L::ROWS, *QT3 = U + 2 * L::ROWS;
         Sc = QT3 + L::KT3;
-        stage_rows<T, GC, D>(dOr, PD, dO, Ct);
+        stage<T, D, GC, false>(dOr, PD, dO, Ct, RowId(), NoScale());
         // Q^T in three versions: (I=0 | ref row 31), (I=1 | ref 31), (I=1 | ref 63)
         stage_gated_T<T, D, 96>(QT3, PK, Q, bS, Ct, [](int j) { return j < 64 ? j : j - 32; },
                                 [](int j) { return j < 64 ? 31 : 63; }, true);
@@ -700,14 +795,24 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
         }
     }
     __syncthreads();
-    if (threadIdx.x < D) {
-        const int c = threadIdx.x;
-        float run = ex2(bS[(GC - 1) * D + c]) * rho[c] + Ep[c];
+    {   // suffix sums over the chunk's rows, NTHR / D parts per channel, plus
+        // rowsum(R_t . P_{t+1}) = 2^(b_last) rho + Ep
+        constexpr int NP = NTHR / D, RP = GC / NP;
+        const int c = threadIdx.x % D, part = threadIdx.x / D, r0 = part * RP;
+        float x[RP];
+#pragma unroll
+        for (int j = 0; j < RP; ++j) x[j] = dBs[(r0 + j) * D + c];
+#pragma unroll
+        for (int j = RP - 2; j >= 0; --j) x[j] += x[j + 1];
+        __syncthreads();
+        dBs[part * D + c] = x[0];
+        __syncthreads();
+        float off = ex2(bS[(GC - 1) * D + c]) * rho[c] + Ep[c];
+        for (int q = part + 1; q < NP; ++q) off += dBs[q * D + c];
         float *out = p.dLG + rb * D;
-        for (int su = Ct - 1; su >= 0; --su) {
-            run += dBs[su * D + c];
-            out[(int64_t)su * D + c] = run;
-        }
+#pragma unroll
+        for (int j = 0; j < RP; ++j)
+            if (r0 + j < Ct) out[(int64_t)(r0 + j) * D + c] = x[j] + off;
     }
 }
 
