@@ -35,16 +35,28 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 // threads take part: NTHR / D parts of the rows per channel, each summed in
 // registers, then offset by the totals of the parts before it.  The caller
 // synchronizes before anyone reads bS and after anyone last read it.
+template <int D> struct LogRows {
+    static constexpr int NP = NTHR / D, RP = GC / NP;
+    float x[RP];
+};
+
 template <int D>
-__device__ __forceinline__ void chunk_cumlog(float *bS, const float *lg, int Ct) {
+__device__ __forceinline__ void cumlog_load(LogRows<D> &lr, const float *lg, int Ct) {
+    constexpr int RP = LogRows<D>::RP;
+    const int c = threadIdx.x % D, r0 = (threadIdx.x / D) * RP;
+#pragma unroll
+    for (int j = 0; j < RP; ++j) lr.x[j] = r0 + j < Ct ? lg[(int64_t)(r0 + j) * D + c] : 0.f;
+}
+
+template <int D>
+__device__ __forceinline__ void cumlog_scan(float *bS, const LogRows<D> &lr) {
     constexpr float LOG2E = 1.4426950408889634f;
-    constexpr int NP = NTHR / D, RP = GC / NP;
+    constexpr int RP = LogRows<D>::RP;
     const int c = threadIdx.x % D, r0 = (threadIdx.x / D) * RP;
     float x[RP];
+    x[0] = lr.x[0] * LOG2E;
 #pragma unroll
-    for (int j = 0; j < RP; ++j) x[j] = r0 + j < Ct ? lg[(int64_t)(r0 + j) * D + c] * LOG2E : 0.f;
-#pragma unroll
-    for (int j = 1; j < RP; ++j) x[j] += x[j - 1];
+    for (int j = 1; j < RP; ++j) x[j] = x[j - 1] + lr.x[j] * LOG2E;
     bS[(r0 + RP - 1) * D + c] = x[RP - 1];
     __syncthreads();
     float off = 0.f;
@@ -54,6 +66,13 @@ __device__ __forceinline__ void chunk_cumlog(float *bS, const float *lg, int Ct)
     for (int j = 0; j < RP; ++j) bS[(r0 + j) * D + c] = x[j] + off;
 }
 
+template <int D>
+__device__ __forceinline__ void chunk_cumlog(float *bS, const float *lg, int Ct) {
+    LogRows<D> lr;
+    cumlog_load<D>(lr, lg, Ct);
+    cumlog_scan<D>(bS, lr);
+}
+
 // 16 bytes of V converted values at p.
 template <typename T>
 __device__ __forceinline__ void store_vec(T *p, const float *f) {
@@ -61,39 +80,65 @@ __device__ __forceinline__ void store_vec(T *p, const float *f) {
     for (int j = 0; j < Tr<T>::VEC; j += 4) store4(p + j, f[j], f[j + 1], f[j + 2], f[j + 3]);
 }
 
-// Stage R rows of a [*, D] token array into LDS: row j of the tile is token
-// row(j) (zero at or past Ct), scaled in place by scale(j, r, c, f[V]) for the
-// V features c.. of token r.  Row form: dst[j][c]; transposed: dst[c][j].
-// Every load of a thread is issued before the first store.
-template <typename T, int D, int R, bool TRANS, typename RowF, typename ScaleF>
-__device__ __forceinline__ void stage(T *dst, int pitch, const T *src, int Ct, RowF row,
-                                      ScaleF scale) {
-    constexpr int V = Tr<T>::VEC, PR = D / V, N = R * PR, IT = (N + NTHR - 1) / NTHR;
-    float f[IT][V];
+// Staging of token tiles into LDS, split in two halves so that the loads of
+// several tiles (and of the states) are in flight together: raw_load issues a
+// thread's 16-byte loads into registers, raw_store scales and writes them.
+// Row j of an R-row tile is token row(j) (zero at or past Ct); row form
+// dst[j][c], transposed dst[c][j].  Consecutive threads take consecutive
+// feature groups of a row (coalesced loads, conflict-free reads of row-major
+// LDS tables in the scale functor, which multiplies the V features c.. of
+// token r in place: scale(j, r, c, f)).
+template <typename T, int D, int R>
+struct Raw {
+    static constexpr int V = Tr<T>::VEC, PR = D / V, N = R * PR, IT = (N + NTHR - 1) / NTHR;
+    uint4 v[IT];
+};
+
+__device__ __forceinline__ void unpack16(const uint4 &v, float *f, const float *) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ void unpack16(const uint4 &v, float *f, const bf16 *) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int u = 0; u < IT; ++u) {
-        const int i = u * NTHR + threadIdx.x;
-        const int j = TRANS ? i % R : i / PR, c = TRANS ? (i / R) * V : (i % PR) * V;
-        const int r = row(j);
-        if (i < N && r < Ct) {
-            load16(src + (int64_t)r * D + c, f[u]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) f[u][e] = 0.f;
-        }
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
+}
+
+template <typename T, int D, int R, typename RowF>
+__device__ __forceinline__ void raw_load(Raw<T, D, R> &raw, const T *src, int Ct, RowF row) {
+    using RW = Raw<T, D, R>;
 #pragma unroll
-    for (int u = 0; u < IT; ++u) {
+    for (int u = 0; u < RW::IT; ++u) {
         const int i = u * NTHR + threadIdx.x;
-        if (i >= N) continue;
-        const int j = TRANS ? i % R : i / PR, c = TRANS ? (i / R) * V : (i % PR) * V;
+        const int j = i / RW::PR, c = (i % RW::PR) * RW::V;
         const int r = row(j);
-        if (r < Ct) scale(j, r, c, f[u]);
+        raw.v[u] = (i < RW::N && r < Ct) ? *(const uint4 *)(src + (int64_t)r * D + c)
+                                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+template <typename T, int D, int R, bool TRANS, typename RowF, typename ScaleF>
+__device__ __forceinline__ void raw_store(const Raw<T, D, R> &raw, T *dst, int pitch, int Ct,
+                                          RowF row, ScaleF scale) {
+    using RW = Raw<T, D, R>;
+    constexpr int V = RW::V;
+#pragma unroll
+    for (int u = 0; u < RW::IT; ++u) {
+        const int i = u * NTHR + threadIdx.x;
+        if (i >= RW::N) continue;
+        const int j = i / RW::PR, c = (i % RW::PR) * V;
+        const int r = row(j);
+        float f[V];
+        unpack16(raw.v[u], f, (const T *)nullptr);
+        if (r < Ct) scale(j, r, c, f);
         if (TRANS) {
 #pragma unroll
-            for (int e = 0; e < V; ++e) dst[(c + e) * pitch + j] = fromf<T>(f[u][e]);
+            for (int e = 0; e < V; ++e) dst[(c + e) * pitch + j] = fromf<T>(f[e]);
         } else {
-            store_vec(dst + j * pitch + c, f[u]);
+            store_vec(dst + j * pitch + c, f);
         }
     }
 }
@@ -105,7 +150,7 @@ struct NoScale {
     template <typename F> __device__ void operator()(int, int, int, F) const {}
 };
 
-// Gate factors for stage(): f *= 2^(b[ref] - b[r]) (invert: 2^(b[r] - b[ref]));
+// Gate factors for raw_store(): f *= 2^(b[ref] - b[r]) (invert: 2^(b[r] - b[ref]));
 // ref < 0: f *= 2^(b[r]).
 template <int V, typename RefF>
 struct GateScale {
@@ -124,18 +169,10 @@ struct GateScale {
     }
 };
 
-template <typename T, int D, int R, typename RowF, typename RefF>
-__device__ __forceinline__ void stage_gated(T *dst, int pitch, const T *src, const float *bS,
-                                            int Ct, RowF row, RefF ref, bool invert = false) {
-    stage<T, D, R, false>(dst, pitch, src, Ct, row,
-                          GateScale<Tr<T>::VEC, RefF>{bS, ref, invert, D});
-}
-
-template <typename T, int D, int R, typename RowF, typename RefF>
-__device__ __forceinline__ void stage_gated_T(T *dst, int pitch, const T *src, const float *bS,
-                                              int Ct, RowF row, RefF ref, bool invert = false) {
-    stage<T, D, R, true>(dst, pitch, src, Ct, row,
-                         GateScale<Tr<T>::VEC, RefF>{bS, ref, invert, D});
+template <typename T, typename RefF>
+__device__ __forceinline__ GateScale<Tr<T>::VEC, RefF> gate_scale(const float *bS, int D, RefF ref,
+                                                                  bool invert = false) {
+    return GateScale<Tr<T>::VEC, RefF>{bS, ref, invert, D};
 }
 
 // The D x D states entering (or leaving) a chunk, combined from the segment
@@ -143,41 +180,49 @@ __device__ __forceinline__ void stage_gated_T(T *dst, int pitch, const T *src, c
 //   x_s[dv][dk] = g_s[dk] seg_s[dv][dk] + loc_s[dv][dk]    (loc_s null: 0)
 // in the [dv][dk] layout of the state arrays.  f(dv, dk0, x) receives V
 // consecutive dk of every state; loads are issued in batches of IB groups.
-template <typename T, int D, int NS, typename F>
+template <typename T, int D, int NS, int BUDGET = 8, typename F>
 __device__ __forceinline__ void for_states(const float *const *seg, const void *const *loc,
                                            const float *const *g, F f) {
     constexpr int V = Tr<T>::VEC, IT = (D * D + NTHR * V - 1) / (NTHR * V);
-    constexpr int IB = IT < 4 ? IT : 4;
+    constexpr int IB = IT < BUDGET / NS ? IT : BUDGET / NS;
     static_assert(IT % IB == 0, "batches");
+    // NTHR * V is a multiple of D: a thread's dk group is the same in every batch
+    const int dk0 = (threadIdx.x * V) % D;
+    float gg[NS][V];
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+        for (int j = 0; j < V; j += 4) load16(g[q] + dk0 + j, gg[q] + j);
     for (int b = 0; b < IT; b += IB) {
-        float x[IB][NS][V];
+        uint4 sr[IB][NS][V / 4], lr[IB][NS];
 #pragma unroll
         for (int u = 0; u < IB; ++u) {
             const int e = ((b + u) * NTHR + threadIdx.x) * V;
-            if (e >= D * D) continue;
-            const int dk = e % D;
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
-                float sg[V], gg[V], lc[V];
+                const bool in = e < D * D;
 #pragma unroll
-                for (int j = 0; j < V; j += 4) {
-                    load16(seg[q] + e + j, sg + j);
-                    load16(g[q] + dk + j, gg + j);
-                }
-                if (loc[q]) {
-                    load16((const T *)loc[q] + e, lc);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < V; ++j) lc[j] = 0.f;
-                }
-#pragma unroll
-                for (int j = 0; j < V; ++j) x[u][q][j] = gg[j] * sg[j] + lc[j];
+                for (int j = 0; j < V / 4; ++j)
+                    sr[u][q][j] = in ? *(const uint4 *)(seg[q] + e + 4 * j) : make_uint4(0u, 0u, 0u, 0u);
+                lr[u][q] = (in && loc[q]) ? *(const uint4 *)((const T *)loc[q] + e)
+                                          : make_uint4(0u, 0u, 0u, 0u);
             }
         }
 #pragma unroll
         for (int u = 0; u < IB; ++u) {
             const int e = ((b + u) * NTHR + threadIdx.x) * V;
-            if (e < D * D) f(e / D, e % D, x[u]);
+            if (e >= D * D) continue;
+            float x[NS][V];
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                float sg[V], lc[V];
+#pragma unroll
+                for (int j = 0; j < V / 4; ++j) unpack16(sr[u][q][j], sg + 4 * j, (const float *)nullptr);
+                unpack16(lr[u][q], lc, (const T *)nullptr);
+#pragma unroll
+                for (int j = 0; j < V; ++j) x[q][j] = gg[q][j] * sg[j] + lc[j];
+            }
+            f(e / D, dk0, x);
         }
     }
 }
@@ -235,6 +280,15 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_local(Params p) {
     float gcum = 1.f;   // thread c < D: gate product of channel c
 
     const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    // the next chunk's rows are loaded while the current one is multiplied
+    Raw<T, D, GC> rk, rv;
+    LogRows<D> rl;
+    if (t0 < t1) {
+        const int Ct0 = min(GC, s.len - t0 * GC);
+        raw_load(rk, K + (int64_t)t0 * GC * D, Ct0, RowId());
+        raw_load(rv, Vg + (int64_t)t0 * GC * D, Ct0, RowId());
+        cumlog_load<D>(rl, LG + (int64_t)t0 * GC * D, Ct0);
+    }
     for (int t = t0; t < t1; ++t) {
         const int tok = t * GC;
         const int Ct = min(GC, s.len - tok);
@@ -249,11 +303,17 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_local(Params p) {
         }
         if (threadIdx.x < D) p.Gc[ch * D + threadIdx.x] = gcum;
         __syncthreads();
-        chunk_cumlog<D>(bS, LG + (int64_t)tok * D, Ct);
+        cumlog_scan<D>(bS, rl);
         __syncthreads();
-        stage_gated_T<T, D, GC>(KT_s, PT, K + (int64_t)tok * D, bS, Ct, [](int j) { return j; },
-                                [](int) { return GC - 1; });
-        stage<T, D, GC, true>(VT_s, PT, Vg + (int64_t)tok * D, Ct, RowId(), NoScale());
+        raw_store<T, D, GC, true>(rk, KT_s, PT, Ct, RowId(),
+                                  gate_scale<T>(bS, D, [](int) { return GC - 1; }));
+        raw_store<T, D, GC, true>(rv, VT_s, PT, Ct, RowId(), NoScale());
+        if (t + 1 < t1) {
+            const int Cn = min(GC, s.len - tok - GC);
+            raw_load(rk, K + (int64_t)(tok + GC) * D, Cn, RowId());
+            raw_load(rv, Vg + (int64_t)(tok + GC) * D, Cn, RowId());
+            cumlog_load<D>(rl, LG + (int64_t)(tok + GC) * D, Cn);
+        }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TL::PER_WAVE; ++k) {
@@ -334,6 +394,13 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_out(Params p) {
     const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
     const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
 
+    // every token load of the kernel, issued up front
+    auto krow = [](int j) { return j < 64 ? (j & 31) : j - 32; };   // K rows of the 3 versions
+    Raw<T, D, GC> rq, rv;
+    Raw<T, D, 96> rk;
+    raw_load(rq, Q, Ct, RowId());
+    raw_load(rk, K, Ct, krow);
+    raw_load(rv, Vg, Ct, RowId());
     chunk_cumlog<D>(bS, p.LG + rb * D, Ct);
     {   // P_t^T [dv][dk] into XT
         const float *seg[1] = {p.Pseg + sh * D * D};
@@ -344,7 +411,7 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_out(Params p) {
         });
     }
     __syncthreads();
-    stage_gated<T, D, GC>(QA, PD, Q, bS, Ct, [](int j) { return j; }, [](int) { return -1; });
+    raw_store<T, D, GC, false>(rq, QA, PD, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return -1; }));
     __syncthreads();
     f32x16 o[TO::PER_WAVE];
 #pragma unroll
@@ -355,11 +422,11 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_out(Params p) {
     }
     __syncthreads();
     // Q_I 2^(b - b_mI);  K rows: (J=0 | ref 0), (J=0 | ref 32), (J=1 | ref 32)
-    stage_gated<T, D, GC>(QA, PD, Q, bS, Ct, [](int j) { return j; },
-                          [](int j) { return j & ~31; }, true);
-    stage_gated<T, D, 96>(KA, PD, K, bS, Ct, [](int j) { return j < 64 ? (j & 31) : j - 32; },
-                          [](int j) { return j < 32 ? 0 : 32; });
-    stage<T, D, GC, true>(XT, PS, Vg, Ct, RowId(), NoScale());
+    raw_store<T, D, GC, false>(rq, QA, PD, Ct, RowId(),
+                               gate_scale<T>(bS, D, [](int j) { return j & ~31; }, true));
+    raw_store<T, D, 96, false>(rk, KA, PD, Ct, krow,
+                               gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
+    raw_store<T, D, GC, true>(rv, XT, PS, Ct, RowId(), NoScale());
     bool slow0, slow1;
     tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
     {
@@ -424,6 +491,14 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_local(Params p) {
     float hcum = 1.f;
 
     const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    Raw<T, D, GC> rq, ro;   // the next (earlier) chunk's rows, loaded ahead
+    LogRows<D> rl;
+    if (t0 < t1) {
+        const int tl = (t1 - 1) * GC, Cl = min(GC, s.len - tl);
+        raw_load(rq, Q + (int64_t)tl * D, Cl, RowId());
+        raw_load(ro, dO + (int64_t)tl * D, Cl, RowId());
+        cumlog_load<D>(rl, LG + (int64_t)tl * D, Cl);
+    }
     for (int t = t1 - 1; t >= t0; --t) {
         const int tok = t * GC;
         const int Ct = min(GC, s.len - tok);
@@ -438,11 +513,15 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_local(Params p) {
         }
         if (threadIdx.x < D) p.Hc[ch * D + threadIdx.x] = hcum;
         __syncthreads();
-        chunk_cumlog<D>(bS, LG + (int64_t)tok * D, Ct);
+        cumlog_scan<D>(bS, rl);
         __syncthreads();
-        stage_gated_T<T, D, GC>(QT_s, PT, Q + (int64_t)tok * D, bS, Ct, [](int j) { return j; },
-                                [](int) { return -1; });
-        stage<T, D, GC, true>(OT_s, PT, dO + (int64_t)tok * D, Ct, RowId(), NoScale());
+        raw_store<T, D, GC, true>(rq, QT_s, PT, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return -1; }));
+        raw_store<T, D, GC, true>(ro, OT_s, PT, Ct, RowId(), NoScale());
+        if (t - 1 >= t0) {   // chunk t - 1 is full
+            raw_load(rq, Q + (int64_t)(tok - GC) * D, GC, RowId());
+            raw_load(ro, dO + (int64_t)(tok - GC) * D, GC, RowId());
+            cumlog_load<D>(rl, LG + (int64_t)(tok - GC) * D, GC);
+        }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TL::PER_WAVE; ++k) {
@@ -543,6 +622,14 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     const void *Rt = p.G > 1 ? (const void *)((const char *)p.Rc + ch * D * D * sizeof(T)) : nullptr;
     const float *gP = p.Gc + ch * D, *gR = p.Hc + ch * D;
     const int w = wave_id(), l = lane_id();
+    auto krow = [](int j) { return j < 64 ? (j & 31) : j - 32; };   // K rows of the 3 versions
+    auto qrow = [](int j) { return j < 64 ? j : j - 32; };          // Q rows of the 3 versions
+    // token rows kept in registers across phases (each loaded once)
+    Raw<T, D, GC> rdo, rv;
+    Raw<T, D, 96> rk96;
+    raw_load(rdo, dO, Ct, RowId());
+    raw_load(rv, Vg, Ct, RowId());
+    raw_load(rk96, K, Ct, krow);
 
     chunk_cumlog<D>(bS, p.LG + rb * D, Ct);
     if (threadIdx.x < D) {
@@ -585,9 +672,10 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
 
     // ---- A: dQ -------------------------------------------------------------
     f32x16 dq[TO::PER_WAVE];
+    Raw<T, D, GC> rk64, rq64;
     {
         T *dOr = U, *Pk = U + L::ROWS;   // dO rows [GC][PD]; P_t as [dk][dv]
-        stage<T, D, GC, false>(dOr, PD, dO, Ct, RowId(), NoScale());
+        raw_store<T, D, GC, false>(rdo, dOr, PD, Ct, RowId(), NoScale());
         // rho[dk] = sum_dv R_t[dk][dv] P_t[dk][dv]; each thread keeps one group
         // of V consecutive dk (NTHR * V is a multiple of D)
         constexpr int V = Tr<T>::VEC;
@@ -597,7 +685,7 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
         const float *seg[2] = {Ps, Rs};
         const void *loc[2] = {Lt, Rt};
         const float *g[2] = {gP, gR};
-        for_states<T, D, 2>(seg, loc, g, [&](int dv, int dk, const float (*x)[V]) {
+        for_states<T, D, 2, 4>(seg, loc, g, [&](int dv, int dk, const float (*x)[V]) {
 #pragma unroll
             for (int j = 0; j < V; ++j) {
                 Pk[(dk + j) * PD + dv] = fromf<T>(x[0][j]);
@@ -631,11 +719,12 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
         __syncthreads();
         T *Vr = U + L::ROWS, *KT3 = U + 2 * L::ROWS;
         Sc = KT3 + L::KT3;
-        stage<T, D, GC, false>(Vr, PD, Vg, Ct, RowId(), NoScale());
+        raw_store<T, D, GC, false>(rv, Vr, PD, Ct, RowId(), NoScale());
         // K^T in three versions: (J=0 | ref row 0), (J=0 | ref 32), (J=1 | ref 32)
-        stage_gated_T<T, D, 96>(KT3, PK, K, bS, Ct,
-                                [](int j) { return j < 64 ? (j & 31) : j - 32; },
-                                [](int j) { return j < 32 ? 0 : 32; });
+        raw_store<T, D, 96, true>(rk96, KT3, PK, Ct, krow,
+                                  gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
+        raw_load(rk64, K, Ct, RowId());   // for B, in flight during A
+        raw_load(rq64, Q, Ct, RowId());
         tile_spans<D>(bS, slow0, slow1);
         scores(dOr, Vr, [](int ww) { return ww == 2 ? 32 : 0; }, false, false, false, no_exact);
         __syncthreads();
@@ -665,17 +754,19 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     }
 
     // ---- B: dV -------------------------------------------------------------
+    Raw<T, D, 96> rq96;
     {
         T *Rv = U, *Kl = U + L::STATE;   // R_t [dv][dk]; K 2^(b_last - b) rows
         {
             const float *seg[1] = {Rs};
             const void *loc[1] = {Rt};
             const float *g[1] = {gR};
-            for_states<T, D, 1>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
+            for_states<T, D, 1, 4>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
                 store_vec(Rv + dv * PD + dk, x[0]);
             });
         }
-        stage_gated<T, D, GC>(Kl, PD, K, bS, Ct, [](int j) { return j; }, [](int) { return GC - 1; });
+        raw_store<T, D, GC, false>(rk64, Kl, PD, Ct, RowId(),
+                                   gate_scale<T>(bS, D, [](int) { return GC - 1; }));
         __syncthreads();
         f32x16 dv[TO::PER_WAVE];
 #pragma unroll
@@ -687,11 +778,12 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
         __syncthreads();
         T *Qg = U, *K3 = U + L::ROWS, *OT = K3 + 96 * PD;
         Sc = OT + L::TT;
-        stage_gated<T, D, GC>(Qg, PD, Q, bS, Ct, [](int j) { return j; }, [](int j) { return j & ~31; },
-                              true);
-        stage_gated<T, D, 96>(K3, PD, K, bS, Ct, [](int j) { return j < 64 ? (j & 31) : j - 32; },
-                              [](int j) { return j < 32 ? 0 : 32; });
-        stage<T, D, GC, true>(OT, PS, dO, Ct, RowId(), NoScale());
+        raw_store<T, D, GC, false>(rq64, Qg, PD, Ct, RowId(),
+                                   gate_scale<T>(bS, D, [](int j) { return j & ~31; }, true));
+        raw_store<T, D, 96, false>(rk96, K3, PD, Ct, krow,
+                                   gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
+        raw_store<T, D, GC, true>(rdo, OT, PS, Ct, RowId(), NoScale());
+        raw_load(rq96, Q, Ct, qrow);   // for C, in flight during B
         __syncthreads();
         scores(Qg, K3, [](int ww) { return 32 * ww; }, false, true, true,
                [&](int a, int b) { return exact_score<T, D>(Q, K, bS, a, b); });
@@ -710,12 +802,12 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     f32x16 dk[TO::PER_WAVE];
     {
         T *Vr = U, *RT = U + L::ROWS;   // V rows; R_t as [dk][dv]
-        stage<T, D, GC, false>(Vr, PD, Vg, Ct, RowId(), NoScale());
+        raw_store<T, D, GC, false>(rv, Vr, PD, Ct, RowId(), NoScale());
         {
             const float *seg[1] = {Rs};
             const void *loc[1] = {Rt};
             const float *g[1] = {gR};
-            for_states<T, D, 1>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
+            for_states<T, D, 1, 4>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
 #pragma unroll
                 for (int j = 0; j < Tr<T>::VEC; ++j) RT[(dk + j) * PD + dv] = fromf<T>(x[0][j]);
             });
@@ -745,10 +837,10 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
         __syncthreads();
         T *dOr = U + L::ROWS, *QT3 = U + 2 * L::ROWS;
         Sc = QT3 + L::KT3;
-        stage<T, D, GC, false>(dOr, PD, dO, Ct, RowId(), NoScale());
+        raw_store<T, D, GC, false>(rdo, dOr, PD, Ct, RowId(), NoScale());
         // Q^T in three versions: (I=0 | ref row 31), (I=1 | ref 31), (I=1 | ref 63)
-        stage_gated_T<T, D, 96>(QT3, PK, Q, bS, Ct, [](int j) { return j < 64 ? j : j - 32; },
-                                [](int j) { return j < 64 ? 31 : 63; }, true);
+        raw_store<T, D, 96, true>(rq96, QT3, PK, Ct, qrow,
+                                  gate_scale<T>(bS, D, [](int j) { return j < 64 ? 31 : 63; }, true));
         __syncthreads();
         scores(Vr, dOr, [](int ww) { return ww == 0 ? 0 : 32; }, true, false, false, no_exact);
         __syncthreads();
