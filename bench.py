@@ -31,8 +31,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-KERNEL_SRC = os.path.join(ROOT, "chunked_causal_linear_amd", "csrc", "lasp_kernels.hip")
+CSRC = os.path.join(ROOT, "chunked_causal_linear_amd", "csrc")
+KERNEL_SRC = [os.path.join(CSRC, "lasp_kernels.hip"), os.path.join(CSRC, "lasp_device.h")]
+GATED_SRC = [os.path.join(CSRC, "lasp_gated.hip"), os.path.join(CSRC, "lasp_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+GATED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters_gated.json")
 
 
 def hip():
@@ -91,18 +94,22 @@ def kernel_work(sh, local_b, seg_b, fin_b):
     }
 
 
-def src_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+def src_sha(files=None):
+    """sha256 over the kernel sources (the kernel file and the shared device header)."""
+    h = hashlib.sha256()
+    for f in files or KERNEL_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, traffic_file=None, files=None):
     """HBM bytes per launch from committed rocprofv3 counters, if they were taken
     on the current kernel source; else None."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(traffic_file or TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != src_sha():
+    if t.get("source_sha256") != src_sha(files):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -421,7 +428,7 @@ def bench_gated(a, w, sh, inp, torch, cca):
         roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom, GATED_TRAFFIC_FILE, GATED_SRC)
     roof.update(kernel="gated " + dom, ms=kms[dom], algorithmic_bytes=bytes_,
                 algorithmic_flops=flops)
     tokens = sh["B"] * sh["N"]

@@ -377,8 +377,11 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_out(Params p) {
     __shared__ __attribute__((aligned(16))) T S_s[GC * PS];
     using TO = Tiles<GC / 32, D / 32>;
 
+    // consecutive workgroups (on one XCD) take consecutive chunks of one head:
+    // the chunks of a segment then read its segment states from that XCD's L2
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = lid % p.H, gc = lid / p.H;
+    const int h = lid / p.n_chunks_ub, gc = lid % p.n_chunks_ub;
+    if (h >= p.H) return;
     Seq s;
     int t;
     if (!chunk_seq(p, gc, s, t)) return;
@@ -601,8 +604,11 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     T *U = (T *)U_raw;
     using TO = Tiles<GC / 32, D / 32>;
 
+    // consecutive workgroups (on one XCD) take consecutive chunks of one head:
+    // the chunks of a segment then read its segment states from that XCD's L2
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = lid % p.H, gc = lid / p.H;
+    const int h = lid / p.n_chunks_ub, gc = lid % p.n_chunks_ub;
+    if (h >= p.H) return;
     Seq s;
     int t;
     if (!chunk_seq(p, gc, s, t)) return;
