@@ -80,6 +80,10 @@ __device__ __forceinline__ void store_vec(T *p, const float *f) {
     for (int j = 0; j < Tr<T>::VEC; j += 4) store4(p + j, f[j], f[j + 1], f[j + 2], f[j + 3]);
 }
 
+struct RowId {
+    __device__ int operator()(int j) const { return j; }
+};
+
 // Staging of token tiles into LDS, split in two halves so that the loads of
 // several tiles (and of the states) are in flight together: raw_load issues a
 // thread's 16-byte loads into registers, raw_store scales and writes them.
@@ -120,9 +124,10 @@ __device__ __forceinline__ void raw_load(Raw<T, D, R> &raw, const T *src, int Ct
     }
 }
 
-template <typename T, int D, int R, bool TRANS, typename RowF, typename ScaleF>
-__device__ __forceinline__ void raw_store(const Raw<T, D, R> &raw, T *dst, int pitch, int Ct,
-                                          RowF row, ScaleF scale) {
+// dst_row(j) < 0 skips tile row j; otherwise it is written as row dst_row(j).
+template <typename T, int D, int R, bool TRANS, typename RowF, typename ScaleF, typename DstF>
+__device__ __forceinline__ void raw_store_map(const Raw<T, D, R> &raw, T *dst, int pitch, int Ct,
+                                              RowF row, ScaleF scale, DstF dst_row) {
     using RW = Raw<T, D, R>;
     constexpr int V = RW::V;
 #pragma unroll
@@ -130,22 +135,27 @@ __device__ __forceinline__ void raw_store(const Raw<T, D, R> &raw, T *dst, int p
         const int i = u * NTHR + threadIdx.x;
         if (i >= RW::N) continue;
         const int j = i / RW::PR, c = (i % RW::PR) * V;
+        const int dj = dst_row(j);
+        if (dj < 0) continue;
         const int r = row(j);
         float f[V];
         unpack16(raw.v[u], f, (const T *)nullptr);
         if (r < Ct) scale(j, r, c, f);
         if (TRANS) {
 #pragma unroll
-            for (int e = 0; e < V; ++e) dst[(c + e) * pitch + j] = fromf<T>(f[e]);
+            for (int e = 0; e < V; ++e) dst[(c + e) * pitch + dj] = fromf<T>(f[e]);
         } else {
-            store_vec(dst + j * pitch + c, f);
+            store_vec(dst + dj * pitch + c, f);
         }
     }
 }
 
-struct RowId {
-    __device__ int operator()(int j) const { return j; }
-};
+template <typename T, int D, int R, bool TRANS, typename RowF, typename ScaleF>
+__device__ __forceinline__ void raw_store(const Raw<T, D, R> &raw, T *dst, int pitch, int Ct,
+                                          RowF row, ScaleF scale) {
+    raw_store_map<T, D, R, TRANS>(raw, dst, pitch, Ct, row, scale, RowId());
+}
+
 struct NoScale {
     template <typename F> __device__ void operator()(int, int, int, F) const {}
 };
@@ -180,10 +190,11 @@ __device__ __forceinline__ GateScale<Tr<T>::VEC, RefF> gate_scale(const float *b
 //   x_s[dv][dk] = g_s[dk] seg_s[dv][dk] + loc_s[dv][dk]    (loc_s null: 0)
 // in the [dv][dk] layout of the state arrays.  f(dv, dk0, x) receives V
 // consecutive dk of every state; loads are issued in batches of IB groups.
-template <typename T, int D, int NS, int BUDGET = 8, typename F>
+template <typename T, int D, int NS, int BUDGET = 8, int NDV = D, typename F>
 __device__ __forceinline__ void for_states(const float *const *seg, const void *const *loc,
-                                           const float *const *g, F f) {
-    constexpr int V = Tr<T>::VEC, IT = (D * D + NTHR * V - 1) / (NTHR * V);
+                                           const float *const *g, F f, int dv0 = 0) {
+    // rows dv0 .. dv0 + NDV - 1 of the [dv][dk] states
+    constexpr int V = Tr<T>::VEC, IT = (NDV * D + NTHR * V - 1) / (NTHR * V);
     constexpr int IB = IT < BUDGET / NS ? IT : BUDGET / NS;
     static_assert(IT % IB == 0, "batches");
     // NTHR * V is a multiple of D: a thread's dk group is the same in every batch
@@ -197,10 +208,10 @@ __device__ __forceinline__ void for_states(const float *const *seg, const void *
         uint4 sr[IB][NS][V / 4], lr[IB][NS];
 #pragma unroll
         for (int u = 0; u < IB; ++u) {
-            const int e = ((b + u) * NTHR + threadIdx.x) * V;
+            const int e = dv0 * D + ((b + u) * NTHR + threadIdx.x) * V;
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
-                const bool in = e < D * D;
+                const bool in = e < (dv0 + NDV) * D;
 #pragma unroll
                 for (int j = 0; j < V / 4; ++j)
                     sr[u][q][j] = in ? *(const uint4 *)(seg[q] + e + 4 * j) : make_uint4(0u, 0u, 0u, 0u);
@@ -210,8 +221,8 @@ __device__ __forceinline__ void for_states(const float *const *seg, const void *
         }
 #pragma unroll
         for (int u = 0; u < IB; ++u) {
-            const int e = ((b + u) * NTHR + threadIdx.x) * V;
-            if (e >= D * D) continue;
+            const int e = dv0 * D + ((b + u) * NTHR + threadIdx.x) * V;
+            if (e >= (dv0 + NDV) * D) continue;
             float x[NS][V];
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
@@ -366,15 +377,26 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_segscan(Params p) {
 //   O = (Q 2^b) P_t + sum over tile pairs J <= I of
 //       [(Q_I 2^(b - b_mI)) (K_J 2^(b_mI - b))^T masked] V_J
 // ---------------------------------------------------------------------------
+// LDS plan of the output kernel: the running log-gates (float32) and one
+// scratch area reused by three phases, small enough for two workgroups per CU:
+//   1  Q 2^b rows | P_t^T rows (half of them at a time when d = 128)
+//   2  Q_I 2^(b - b_mI) rows | K rows 0..63 (ref 32; then rows 0..31 with ref 0) | scores
+//   3  V^T | (scores)
+template <typename T, int D> struct OutLds {
+    static constexpr int V = Tr<T>::VEC, PD = D + V, PS = GC + V;
+    static constexpr int NHALF = D * PD * (int)sizeof(T) > 20000 ? 2 : 1, DH = D / NHALF;
+    static constexpr int ROWS = GC * PD, SOFF = 2 * ROWS;
+    static constexpr int P1 = ROWS + DH * PD, P2 = SOFF + GC * PS;
+    static constexpr int ELEMS = P1 > P2 ? P1 : P2;
+    static_assert(D * PS <= SOFF, "V^T must not reach the scores");
+};
+
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR) void k_gfwd_out(Params p) {
-    constexpr int V = Tr<T>::VEC;
-    constexpr int PD = D + V, PS = GC + V, PX = PD > PS ? PD : PS;
+__global__ __launch_bounds__(NTHR, 2) void k_gfwd_out(Params p) {
+    using L = OutLds<T, D>;
+    constexpr int PD = L::PD, PS = L::PS, DH = L::DH;
     __shared__ float bS[GC * D];
-    __shared__ __attribute__((aligned(16))) T QA[GC * PD];
-    __shared__ __attribute__((aligned(16))) T KA[96 * PD];
-    __shared__ __attribute__((aligned(16))) T XT[D * PX];   // P_t^T (pitch PD), then V^T (pitch PS)
-    __shared__ __attribute__((aligned(16))) T S_s[GC * PS];
+    __shared__ __attribute__((aligned(16))) T U[L::ELEMS];
     using TO = Tiles<GC / 32, D / 32>;
 
     // consecutive workgroups (on one XCD) take consecutive chunks of one head:
@@ -396,69 +418,90 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_out(Params p) {
     T *O = (T *)p.O + rb * D;
     const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
     const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
+    const int w = wave_id(), l = lane_id();
 
     // every token load of the kernel, issued up front
-    auto krow = [](int j) { return j < 64 ? (j & 31) : j - 32; };   // K rows of the 3 versions
+    auto krow = [](int j) { return j < 64 ? (j & 31) : j - 32; };   // K rows: (0|ref 0), (0|32), (1|32)
     Raw<T, D, GC> rq, rv;
     Raw<T, D, 96> rk;
     raw_load(rq, Q, Ct, RowId());
     raw_load(rk, K, Ct, krow);
     raw_load(rv, Vg, Ct, RowId());
     chunk_cumlog<D>(bS, p.LG + rb * D, Ct);
-    {   // P_t^T [dv][dk] into XT
+
+    // 1: o = (Q 2^b) P_t
+    T *Qh = U, *Ph = U + L::ROWS;
+    f32x16 o[TO::PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < TO::PER_WAVE; ++k) zero(o[k]);
+    {
         const float *seg[1] = {p.Pseg + sh * D * D};
         const void *loc[1] = {p.G > 1 ? (const void *)((const T *)p.Lc + ch * D * D) : nullptr};
         const float *g[1] = {p.Gc + ch * D};
-        for_states<T, D, 1>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
-            store_vec(XT + dv * PD + dk, x[0]);
-        });
-    }
-    __syncthreads();
-    raw_store<T, D, GC, false>(rq, QA, PD, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return -1; }));
-    __syncthreads();
-    f32x16 o[TO::PER_WAVE];
+        for (int hh = 0; hh < L::NHALF; ++hh) {
+            const int dv0 = hh * DH;
+            if (hh) __syncthreads();
+            for_states<T, D, 1, 8, DH>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
+                store_vec(Ph + (dv - dv0) * PD + dk, x[0]);
+            }, dv0);
+            if (!hh)
+                raw_store<T, D, GC, false>(rq, Qh, PD, Ct, RowId(),
+                                           gate_scale<T>(bS, D, [](int) { return -1; }));
+            __syncthreads();
 #pragma unroll
-    for (int k = 0; k < TO::PER_WAVE; ++k) {
-        zero(o[k]);
-        int mi, ni;
-        if (TO::get(k, mi, ni)) gemm<T, D>(o[k], QA, PD, mi * 32, XT, PD, ni * 32);
-    }
-    __syncthreads();
-    // Q_I 2^(b - b_mI);  K rows: (J=0 | ref 0), (J=0 | ref 32), (J=1 | ref 32)
-    raw_store<T, D, GC, false>(rq, QA, PD, Ct, RowId(),
-                               gate_scale<T>(bS, D, [](int j) { return j & ~31; }, true));
-    raw_store<T, D, 96, false>(rk, KA, PD, Ct, krow,
-                               gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
-    raw_store<T, D, GC, true>(rv, XT, PS, Ct, RowId(), NoScale());
-    bool slow0, slow1;
-    tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
-    {
-        const int w = wave_id(), l = lane_id();
-        if (w < 3) {
-            const int I = w == 0 ? 0 : 1, J = w == 2 ? 1 : 0;
-            const bool diag = I == J, slow = diag && (I == 0 ? slow0 : slow1);
-            f32x16 st;
-            zero(st);
-            if (!slow) gemm<T, D>(st, QA, PD, 32 * I, KA, PD, 32 * w);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qs = 32 * I + crow(r), ki = 32 * J + (l & 31);
-                float x = 0.f;
-                if (qs < Ct && ki < Ct && ki <= qs)
-                    x = slow ? exact_score<T, D>(Q, K, bS, qs, ki) : st[r];
-                S_s[qs * PS + ki] = fromf<T>(x);
+            for (int k = 0; k < TO::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TO::get(k, mi, ni) && ni * 32 >= dv0 && ni * 32 < dv0 + DH)
+                    gemm<T, D>(o[k], Qh, PD, mi * 32, Ph, PD, ni * 32 - dv0);
             }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S_s[crow(r) * PS + 32 + (l & 31)] = fromf<T>(0.f);
         }
     }
+    __syncthreads();
+
+    // 2: masked gated scores into Sc
+    T *Qt = U, *K64 = U + L::ROWS, *Sc = U + L::SOFF;
+    raw_store<T, D, GC, false>(rq, Qt, PD, Ct, RowId(),
+                               gate_scale<T>(bS, D, [](int j) { return j & ~31; }, true));
+    raw_store_map<T, D, 96, false>(rk, K64, PD, Ct, krow,
+                                   gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }),
+                                   [](int j) { return j - 32; });   // rows 0..63 with ref 32
+    bool slow0, slow1;
+    tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
+    auto score_tile = [&](int I, int J, int krow0, bool slow) __attribute__((always_inline)) {
+        f32x16 st;
+        zero(st);
+        if (!slow) gemm<T, D>(st, Qt, PD, 32 * I, K64, PD, krow0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int qs = 32 * I + crow(r), ki = 32 * J + (l & 31);
+            float x = 0.f;
+            if (qs < Ct && ki < Ct && ki <= qs) x = slow ? exact_score<T, D>(Q, K, bS, qs, ki) : st[r];
+            Sc[qs * PS + ki] = fromf<T>(x);
+        }
+    };
+    if (w == 1) score_tile(1, 0, 0, false);
+    if (w == 2) score_tile(1, 1, 32, slow1);
+    if (w == 3) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Sc[crow(r) * PS + 32 + (l & 31)] = fromf<T>(0.f);
+    }
+    __syncthreads();
+    raw_store_map<T, D, 96, false>(rk, K64, PD, Ct, krow,
+                                   gate_scale<T>(bS, D, [](int) { return 0; }),
+                                   [](int j) { return j < 32 ? j : -1; });   // rows 0..31 with ref 0
+    __syncthreads();
+    if (w == 0) score_tile(0, 0, 0, slow0);
+    __syncthreads();
+
+    // 3: o += Sc V
+    T *VT = U;
+    raw_store<T, D, GC, true>(rv, VT, PS, Ct, RowId(), NoScale());
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < TO::PER_WAVE; ++k) {
         int mi, ni;
         if (TO::get(k, mi, ni)) {
-            gemm<T, GC>(o[k], S_s, PS, mi * 32, XT, PS, ni * 32);
+            gemm<T, GC>(o[k], Sc, PS, mi * 32, VT, PS, ni * 32);
             store_rows(o[k], O, D, mi * 32, ni * 32, Ct);
         }
     }
