@@ -66,11 +66,56 @@ __device__ __forceinline__ void cumlog_scan(float *bS, const LogRows<D> &lr) {
     for (int j = 0; j < RP; ++j) bS[(r0 + j) * D + c] = x[j] + off;
 }
 
+// The same in blocks of 16 rows (fewer registers live; the kernels that use
+// it keep their other tiles in registers meanwhile).
 template <int D>
 __device__ __forceinline__ void chunk_cumlog(float *bS, const float *lg, int Ct) {
-    LogRows<D> lr;
-    cumlog_load<D>(lr, lg, Ct);
-    cumlog_scan<D>(bS, lr);
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr int RP = LogRows<D>::RP, B = RP < 16 ? RP : 16;
+    const int c = threadIdx.x % D, r0 = (threadIdx.x / D) * RP;
+    float run = 0.f;
+#pragma unroll
+    for (int b0 = 0; b0 < RP; b0 += B) {
+        float x[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int r = r0 + b0 + j;
+            x[j] = r < Ct ? lg[(int64_t)r * D + c] * LOG2E : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            run += x[j];
+            bS[(r0 + b0 + j) * D + c] = run;
+        }
+    }
+    __syncthreads();
+    float off = 0.f;
+    for (int q = RP - 1; q < r0; q += RP) off += bS[q * D + c];
+    __syncthreads();
+    if (off != 0.f) {
+#pragma unroll 8
+        for (int j = 0; j < RP; ++j) bS[(r0 + j) * D + c] += off;
+    }
+}
+
+// acc += A[m0..m0+32)[0..K) * B[n0..n0+32)[0..K)^T with LDS operands (the
+// contraction index contiguous), two k-steps of fragments in flight: fewer
+// registers than a fully unrolled product, for kernels that run two
+// workgroups per CU.
+template <typename T, int K>
+__device__ __forceinline__ void gemm2(f32x16 &acc, const T *As, int pa, int m0, const T *Bs,
+                                      int pb, int n0) {
+    constexpr int V = Tr<T>::VEC;
+    using Fr = typename Tr<T>::frag;
+    const int l = lane_id();
+    const T *ap = As + (m0 + (l & 31)) * pa + (l >> 5) * V;
+    const T *bp = Bs + (n0 + (l & 31)) * pb + (l >> 5) * V;
+#pragma unroll 2
+    for (int k = 0; k < K; k += 2 * V) {
+        const Fr a = *(const Fr *)(ap + k);
+        const Fr b = *(const Fr *)(bp + k);
+        mma(acc, a, b);
+    }
 }
 
 // 16 bytes of V converted values at p.
@@ -622,29 +667,40 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_segscan(Params p) {
 //   dlog_g[s] = sum_{u>=s in chunk} (q_u dq_u - k_u dk_u) + rowsum(R_t . P_{t+1})
 // with m_I the first row of query tile I and m'_J the last row of key tile J.
 // ---------------------------------------------------------------------------
+// LDS plan of the gradient kernel: the running log-gates (float32), two small
+// per-channel sums and one scratch area reused by every phase, small enough
+// for two workgroups per CU.  A d x d state operand is staged in NHALF parts
+// (d = 128): split along the contraction index where the product allows it
+// (dQ's dO P_t^T, dK's V R_t^T), along the output columns otherwise (dV's
+// K R_t).  Score tiles are formed before the next product's operands are
+// staged over the rows they came from.
 template <typename T, int D>
 struct GradLds {
     static constexpr int V = Tr<T>::VEC, PD = D + V, PS = GC + V, PK = 96 + V;
-    // phase buffers (element offsets into one T array)
-    static constexpr int ROWS = GC * PD, STATE = D * PD, KT3 = D * PK, SC = GC * PS, TT = D * PS;
-    static constexpr int A1 = ROWS + STATE;               // dO, P
-    static constexpr int A2 = 2 * ROWS + KT3 + SC;        // dO, V, K^T x3, scores
-    static constexpr int B2 = ROWS + 96 * PD + TT + SC;   // Q, K x3, dO^T, scores
-    static constexpr int C2 = 2 * ROWS + KT3 + SC;        // V, dO, Q^T x3, scores
-    static constexpr int M1 = A1 > A2 ? A1 : A2, M2 = B2 > C2 ? B2 : C2;
+    static constexpr int NHALF = D * PD * (int)sizeof(T) > 20000 ? 2 : 1, DH = D / NHALF;
+    static constexpr int PDH = DH + V;                    // pitch of a contraction-split part
+    static constexpr int ROWS = GC * PD, SC = GC * PS, SOFF = 2 * ROWS;
+    static constexpr int CPART = D * PDH, RPART = DH * PD;
+    static constexpr int RP = NTHR * V * 4 / (int)sizeof(T);   // float partial sums of rho
+    static constexpr int A1 = ROWS + CPART + RP;          // dO rows, P part, rho partials
+    static constexpr int B1 = RPART + ROWS;               // R part, K rows
+    static constexpr int C1 = ROWS + CPART;               // V rows, R^T part
+    static constexpr int S2 = SOFF + SC;                  // two row arrays + scores
+    static constexpr int M1 = A1 > B1 ? A1 : B1, M2 = C1 > S2 ? C1 : S2;
     static constexpr int ELEMS = M1 > M2 ? M1 : M2;
     static constexpr int BYTES = ELEMS * (int)sizeof(T) > GC * D * 4 ? ELEMS * (int)sizeof(T) : GC * D * 4;
+    static_assert(D * PK <= SOFF && D * PS <= SOFF, "K^T / Q^T / dO^T must not reach the scores");
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
+__global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
     using L = GradLds<T, D>;
-    constexpr int PD = L::PD, PS = L::PS, PK = L::PK;
+    constexpr int V = Tr<T>::VEC, PD = L::PD, PS = L::PS, PK = L::PK, DH = L::DH, PDH = L::PDH;
     __shared__ float bS[GC * D];
     __shared__ float rho[D], Ep[D];
-    __shared__ float rpart[NTHR * Tr<T>::VEC];   // rho partial sums, [slot][dk]
     __shared__ __attribute__((aligned(16))) char U_raw[L::BYTES];
     T *U = (T *)U_raw;
+    T *Sc = U + L::SOFF;   // score tiles (every phase)
     using TO = Tiles<GC / 32, D / 32>;
 
     // consecutive workgroups (on one XCD) take consecutive chunks of one head:
@@ -667,40 +723,38 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
     const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
     const float *Ps = p.Pseg + sh * D * D, *Rs = p.Rseg + sh * D * D;
-    const void *Lt = p.G > 1 ? (const void *)((const char *)p.Lc + ch * D * D * sizeof(T)) : nullptr;
-    const void *Rt = p.G > 1 ? (const void *)((const char *)p.Rc + ch * D * D * sizeof(T)) : nullptr;
+    const void *Lt = p.G > 1 ? (const void *)((const T *)p.Lc + ch * D * D) : nullptr;
+    const void *Rt = p.G > 1 ? (const void *)((const T *)p.Rc + ch * D * D) : nullptr;
     const float *gP = p.Gc + ch * D, *gR = p.Hc + ch * D;
     const int w = wave_id(), l = lane_id();
     auto krow = [](int j) { return j < 64 ? (j & 31) : j - 32; };   // K rows of the 3 versions
     auto qrow = [](int j) { return j < 64 ? j : j - 32; };          // Q rows of the 3 versions
-    // token rows kept in registers across phases (each loaded once)
-    Raw<T, D, GC> rdo, rv;
+    // token rows in registers, loaded a phase ahead of their use (reloaded
+    // from L2 rather than kept live across phases: registers bound the
+    // workgroups per CU)
+    chunk_cumlog<D>(bS, p.LG + rb * D, Ct);   // (its registers are free before the rows load)
+    if (threadIdx.x < D) Ep[threadIdx.x] = 0.f;
+    Raw<T, D, GC> rdo, rv, rkq;
     Raw<T, D, 96> rk96;
     raw_load(rdo, dO, Ct, RowId());
     raw_load(rv, Vg, Ct, RowId());
     raw_load(rk96, K, Ct, krow);
-
-    chunk_cumlog<D>(bS, p.LG + rb * D, Ct);
-    if (threadIdx.x < D) {
-        Ep[threadIdx.x] = 0.f;
-        rho[threadIdx.x] = 0.f;
-    }
     bool slow0 = false, slow1 = false;
-    T *Sc = nullptr;
-    // Masked 32x32 score tiles A_a . B_b^T into Sc, on waves 0..2: tiles
-    // (a, b) = (0,0), (1,0), (1,1) (lower: b <= a kept) or (0,0), (0,1), (1,1)
-    // (upper: b >= a kept); wave 3 zeroes the remaining block.  B's rows for
-    // wave w start at brow(w).  Gated diagonal tiles over the span limit take
-    // exact(a, b) instead of the product.  tr stores Sc[b][a].
+    // Masked 32x32 score tiles A_a . B_b^T into Sc: tiles (a, b) = (0,0), (1,0),
+    // (1,1) (lower: b <= a kept) or (0,0), (0,1), (1,1) (upper: b >= a kept),
+    // the tiles of mask bit w (bit i: tile i) on waves 0..2; wave 3 zeroes the
+    // remaining block when zero_block.  B's rows for tile i start at brow(i).
+    // Gated diagonal tiles over the span limit take exact(a, b) instead of the
+    // product.  tr stores Sc[b][a].
     auto scores = [&](const T *A, const T *B, auto brow, bool upper, bool tr, bool gated,
-                      auto exact) __attribute__((always_inline)) {
-        if (w < 3) {
+                      auto exact, int mask, bool zero_block) __attribute__((always_inline)) {
+        if (w < 3 && ((mask >> w) & 1)) {
             const int ta = upper ? (w == 2 ? 1 : 0) : (w == 0 ? 0 : 1);
             const int tb = upper ? (w == 0 ? 0 : 1) : (w == 2 ? 1 : 0);
             const bool slow = gated && ta == tb && (ta == 0 ? slow0 : slow1);
             f32x16 st;
             zero(st);
-            if (!slow) gemm<T, D>(st, A, PD, 32 * ta, B, PD, brow(w));
+            if (!slow) gemm2<T, D>(st, A, PD, 32 * ta, B, PD, brow(w));
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int a = 32 * ta + crow(r), b = 32 * tb + (l & 31);
@@ -708,7 +762,7 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
                 if (a < Ct && b < Ct && (upper ? b >= a : b <= a)) x = slow ? exact(a, b) : st[r];
                 Sc[tr ? b * PS + a : a * PS + b] = fromf<T>(x);
             }
-        } else {
+        } else if (w == 3 && zero_block) {
             const int ta = upper ? 1 : 0, tb = upper ? 0 : 1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -720,27 +774,38 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
     auto no_exact = [](int, int) { return 0.f; };
 
     // ---- A: dQ -------------------------------------------------------------
-    f32x16 dq[TO::PER_WAVE];
-    Raw<T, D, GC> rk64, rq64;
     {
-        T *dOr = U, *Pk = U + L::ROWS;   // dO rows [GC][PD]; P_t as [dk][dv]
+        f32x16 dq[TO::PER_WAVE];
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) zero(dq[k]);
+        T *dOr = U, *Pk = U + L::ROWS;   // dO rows; P_t as [dk][dv part]
+        float *rpart = (float *)(U + L::ROWS + L::CPART);
         raw_store<T, D, GC, false>(rdo, dOr, PD, Ct, RowId(), NoScale());
         // rho[dk] = sum_dv R_t[dk][dv] P_t[dk][dv]; each thread keeps one group
         // of V consecutive dk (NTHR * V is a multiple of D)
-        constexpr int V = Tr<T>::VEC;
         float racc[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) racc[j] = 0.f;
         const float *seg[2] = {Ps, Rs};
         const void *loc[2] = {Lt, Rt};
         const float *g[2] = {gP, gR};
-        for_states<T, D, 2, 4>(seg, loc, g, [&](int dv, int dk, const float (*x)[V]) {
+        for (int hh = 0; hh < L::NHALF; ++hh) {
+            const int dv0 = hh * DH;
+            if (hh) __syncthreads();
+            for_states<T, D, 2, 4, DH>(seg, loc, g, [&](int dv, int dk, const float (*x)[V]) {
 #pragma unroll
-            for (int j = 0; j < V; ++j) {
-                Pk[(dk + j) * PD + dv] = fromf<T>(x[0][j]);
-                racc[j] += x[0][j] * x[1][j];
+                for (int j = 0; j < V; ++j) {
+                    Pk[(dk + j) * PDH + dv - dv0] = fromf<T>(x[0][j]);
+                    racc[j] += x[0][j] * x[1][j];
+                }
+            }, dv0);
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < TO::PER_WAVE; ++k) {
+                int mi, ni;
+                if (TO::get(k, mi, ni)) gemm2<T, DH>(dq[k], dOr + dv0, PD, mi * 32, Pk, PDH, ni * 32);
             }
-        });
+        }
         // the threads sharing a dk group sum in a fixed order (no atomics:
         // the result must not depend on timing)
         constexpr int SLOTS = (NTHR * V < D * D ? NTHR * V : D * D) / D;
@@ -756,34 +821,32 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
         }
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
-            zero(dq[k]);
             int mi, ni;
             if (TO::get(k, mi, ni)) {
-                gemm<T, D>(dq[k], dOr, PD, mi * 32, Pk, PD, ni * 32);
                 const float sc = ex2(bS[mi * 32 * D + ni * 32 + (l & 31)]);   // 2^(b_mI) of column c
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dq[k][r] *= sc;
             }
         }
-        __syncthreads();
-        T *Vr = U + L::ROWS, *KT3 = U + 2 * L::ROWS;
-        Sc = KT3 + L::KT3;
+        // D_ = dO V^T (no gates), then K^T in three versions over the rows
+        __syncthreads();   // rho's partial sums are read before V's rows overwrite them
+        T *Vr = U + L::ROWS;
         raw_store<T, D, GC, false>(rv, Vr, PD, Ct, RowId(), NoScale());
-        // K^T in three versions: (J=0 | ref row 0), (J=0 | ref 32), (J=1 | ref 32)
+        tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
+        scores(dOr, Vr, [](int ww) { return ww == 2 ? 32 : 0; }, false, false, false, no_exact, 7, true);
+        __syncthreads();
+        T *KT3 = U;   // (J=0 | ref row 0), (J=0 | ref 32), (J=1 | ref 32)
         raw_store<T, D, 96, true>(rk96, KT3, PK, Ct, krow,
                                   gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
-        raw_load(rk64, K, Ct, RowId());   // for B, in flight during A
-        raw_load(rq64, Q, Ct, RowId());
-        tile_spans<D>(bS, slow0, slow1);
-        scores(dOr, Vr, [](int ww) { return ww == 2 ? 32 : 0; }, false, false, false, no_exact);
+        raw_load(rkq, K, Ct, RowId());   // K rows for B, in flight during A
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
             const bool slow = mi == 0 ? slow0 : slow1;
-            if (mi == 1) gemm<T, 32>(dq[k], Sc, PS, 32, KT3 + 32, PK, ni * 32);
-            if (!slow) gemm<T, 32>(dq[k], Sc + 32 * mi, PS, 32 * mi, KT3 + (mi ? 64 : 0), PK, ni * 32);
+            if (mi == 1) gemm2<T, 32>(dq[k], Sc, PS, 32, KT3 + 32, PK, ni * 32);
+            if (!slow) gemm2<T, 32>(dq[k], Sc + 32 * mi, PS, 32 * mi, KT3 + (mi ? 64 : 0), PK, ni * 32);
             const int c = ni * 32 + (l & 31), m = mi * 32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -798,50 +861,73 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
                 }
             }
             store_rows(dq[k], (T *)p.dQ + rb * D, D, mi * 32, ni * 32, Ct);
+            // q . dq goes to the log-gate gradient's rows for now (each element
+            // is read back by the lane that wrote it); dq's registers are then free
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qs = m + crow(r);
+                if (qs < Ct) p.dLG[(rb + qs) * D + c] = tof(Q[(int64_t)qs * D + c]) * dq[k][r];
+            }
         }
         __syncthreads();
     }
 
     // ---- B: dV -------------------------------------------------------------
-    Raw<T, D, 96> rq96;
     {
-        T *Rv = U, *Kl = U + L::STATE;   // R_t [dv][dk]; K 2^(b_last - b) rows
+        f32x16 dv[TO::PER_WAVE];
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) zero(dv[k]);
+        T *Rv = U, *Kl = U + L::RPART;   // R_t rows dv part [dv][dk]; K 2^(b_last - b) rows
+        raw_store<T, D, GC, false>(rkq, Kl, PD, Ct, RowId(),
+                                   gate_scale<T>(bS, D, [](int) { return GC - 1; }));
+        raw_load(rkq, Q, Ct, RowId());   // Q rows for B's scores
+        raw_load(rdo, dO, Ct, RowId());  // dO rows for dV, and for C
         {
             const float *seg[1] = {Rs};
             const void *loc[1] = {Rt};
             const float *g[1] = {gR};
-            for_states<T, D, 1, 4>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
-                store_vec(Rv + dv * PD + dk, x[0]);
-            });
-        }
-        raw_store<T, D, GC, false>(rk64, Kl, PD, Ct, RowId(),
-                                   gate_scale<T>(bS, D, [](int) { return GC - 1; }));
-        __syncthreads();
-        f32x16 dv[TO::PER_WAVE];
+            for (int hh = 0; hh < L::NHALF; ++hh) {
+                const int dv0 = hh * DH;
+                if (hh) __syncthreads();
+                for_states<T, D, 1, 4, DH>(seg, loc, g, [&](int dvv, int dk, const float (*x)[V]) {
+                    store_vec(Rv + (dvv - dv0) * PD + dk, x[0]);
+                }, dv0);
+                __syncthreads();
 #pragma unroll
-        for (int k = 0; k < TO::PER_WAVE; ++k) {
-            zero(dv[k]);
-            int mi, ni;
-            if (TO::get(k, mi, ni)) gemm<T, D>(dv[k], Kl, PD, mi * 32, Rv, PD, ni * 32);
+                for (int k = 0; k < TO::PER_WAVE; ++k) {
+                    int mi, ni;
+                    if (TO::get(k, mi, ni) && ni * 32 >= dv0 && ni * 32 < dv0 + DH)
+                        gemm2<T, D>(dv[k], Kl, PD, mi * 32, Rv, PD, ni * 32 - dv0);
+                }
+            }
         }
         __syncthreads();
-        T *Qg = U, *K3 = U + L::ROWS, *OT = K3 + 96 * PD;
-        Sc = OT + L::TT;
-        raw_store<T, D, GC, false>(rq64, Qg, PD, Ct, RowId(),
+        // gated scores A (stored transposed, [key][query]): tiles (1,0), (1,1)
+        // from K rows 0..63 with ref 32, then (0,0) from K rows 0..31 with ref 0
+        T *Qg = U, *K64 = U + L::ROWS;
+        raw_store<T, D, GC, false>(rkq, Qg, PD, Ct, RowId(),
                                    gate_scale<T>(bS, D, [](int j) { return j & ~31; }, true));
-        raw_store<T, D, 96, false>(rk96, K3, PD, Ct, krow,
-                                   gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
-        raw_store<T, D, GC, true>(rdo, OT, PS, Ct, RowId(), NoScale());
-        raw_load(rq96, Q, Ct, qrow);   // for C, in flight during B
+        raw_store_map<T, D, 96, false>(rk96, K64, PD, Ct, krow,
+                                       gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }),
+                                       [](int j) { return j - 32; });
         __syncthreads();
-        scores(Qg, K3, [](int ww) { return 32 * ww; }, false, true, true,
-               [&](int a, int b) { return exact_score<T, D>(Q, K, bS, a, b); });
+        auto exact = [&](int a, int b) { return exact_score<T, D>(Q, K, bS, a, b); };
+        scores(Qg, K64, [](int ww) { return ww == 2 ? 32 : 0; }, false, true, true, exact, 6, true);
+        __syncthreads();
+        raw_store_map<T, D, 96, false>(rk96, K64, PD, Ct, krow,
+                                       gate_scale<T>(bS, D, [](int) { return 0; }),
+                                       [](int j) { return j < 32 ? j : -1; });
+        __syncthreads();
+        scores(Qg, K64, [](int) { return 0; }, false, true, true, exact, 1, false);
+        __syncthreads();
+        T *OT = U;   // dO^T [dv][query]
+        raw_store<T, D, GC, true>(rdo, OT, PS, Ct, RowId(), NoScale());
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
-            gemm<T, GC>(dv[k], Sc, PS, mi * 32, OT, PS, ni * 32);
+            gemm2<T, GC>(dv[k], Sc, PS, mi * 32, OT, PS, ni * 32);
             store_rows(dv[k], (T *)p.dV + rb * D, D, mi * 32, ni * 32, Ct);
         }
         __syncthreads();
@@ -849,26 +935,37 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
 
     // ---- C: dK -------------------------------------------------------------
     f32x16 dk[TO::PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < TO::PER_WAVE; ++k) zero(dk[k]);
+    raw_load(rv, Vg, Ct, RowId());
+    raw_load(rk96, Q, Ct, qrow);   // Q rows of the three versions (the K registers are free)
     {
-        T *Vr = U, *RT = U + L::ROWS;   // V rows; R_t as [dk][dv]
+        T *Vr = U, *RT = U + L::ROWS;   // V rows; R_t as [dk][dv part]
         raw_store<T, D, GC, false>(rv, Vr, PD, Ct, RowId(), NoScale());
         {
             const float *seg[1] = {Rs};
             const void *loc[1] = {Rt};
             const float *g[1] = {gR};
-            for_states<T, D, 1, 4>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
+            for (int hh = 0; hh < L::NHALF; ++hh) {
+                const int dv0 = hh * DH;
+                if (hh) __syncthreads();
+                for_states<T, D, 1, 4, DH>(seg, loc, g, [&](int dvv, int dkk, const float (*x)[V]) {
 #pragma unroll
-                for (int j = 0; j < Tr<T>::VEC; ++j) RT[(dk + j) * PD + dv] = fromf<T>(x[0][j]);
-            });
+                    for (int j = 0; j < V; ++j) RT[(dkk + j) * PDH + dvv - dv0] = fromf<T>(x[0][j]);
+                }, dv0);
+                __syncthreads();
+#pragma unroll
+                for (int k = 0; k < TO::PER_WAVE; ++k) {
+                    int mi, ni;
+                    if (TO::get(k, mi, ni)) gemm2<T, DH>(dk[k], Vr + dv0, PD, mi * 32, RT, PDH, ni * 32);
+                }
+            }
         }
-        __syncthreads();
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
-            zero(dk[k]);
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
-            gemm<T, D>(dk[k], Vr, PD, mi * 32, RT, PD, ni * 32);   // X = V R^T
-            // rowsum(R_t . P_{t+1}) gets sum_i k_i 2^(b_last - b_i) X_i
+            // X = V R^T is in dk; rowsum(R_t . P_{t+1}) gets sum_i k_i 2^(b_last - b_i) X_i
             const int c = ni * 32 + (l & 31), mJ = mi * 32 + 31;
             const float bl = bS[(GC - 1) * D + c];
             float ep = 0.f;
@@ -884,22 +981,22 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
             for (int r = 0; r < 16; ++r) dk[k][r] *= sc;
         }
         __syncthreads();
-        T *dOr = U + L::ROWS, *QT3 = U + 2 * L::ROWS;
-        Sc = QT3 + L::KT3;
+        T *dOr = U + L::ROWS;   // D_^T = V dO^T (upper tiles), then Q^T in three versions
         raw_store<T, D, GC, false>(rdo, dOr, PD, Ct, RowId(), NoScale());
-        // Q^T in three versions: (I=0 | ref row 31), (I=1 | ref 31), (I=1 | ref 63)
-        raw_store<T, D, 96, true>(rq96, QT3, PK, Ct, qrow,
-                                  gate_scale<T>(bS, D, [](int j) { return j < 64 ? 31 : 63; }, true));
         __syncthreads();
-        scores(Vr, dOr, [](int ww) { return ww == 0 ? 0 : 32; }, true, false, false, no_exact);
+        scores(Vr, dOr, [](int ww) { return ww == 0 ? 0 : 32; }, true, false, false, no_exact, 7, true);
+        __syncthreads();
+        T *QT3 = U;   // (I=0 | ref row 31), (I=1 | ref 31), (I=1 | ref 63)
+        raw_store<T, D, 96, true>(rk96, QT3, PK, Ct, qrow,
+                                  gate_scale<T>(bS, D, [](int j) { return j < 64 ? 31 : 63; }, true));
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
             const bool slow = mi == 0 ? slow0 : slow1;
-            if (mi == 0) gemm<T, 32>(dk[k], Sc + 32, PS, 0, QT3 + 32, PK, ni * 32);
-            if (!slow) gemm<T, 32>(dk[k], Sc + 32 * mi, PS, 32 * mi, QT3 + (mi ? 64 : 0), PK, ni * 32);
+            if (mi == 0) gemm2<T, 32>(dk[k], Sc + 32, PS, 0, QT3 + 32, PK, ni * 32);
+            if (!slow) gemm2<T, 32>(dk[k], Sc + 32 * mi, PS, 32 * mi, QT3 + (mi ? 64 : 0), PK, ni * 32);
             const int c = ni * 32 + (l & 31), mJ = mi * 32 + 31;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -930,21 +1027,20 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
         for (int r = 0; r < 16; ++r) {
             const int su = mi * 32 + crow(r);
             float x = 0.f;
-            if (su < Ct)
-                x = tof(Q[(int64_t)su * D + c]) * dq[k][r] - tof(K[(int64_t)su * D + c]) * dk[k][r];
+            if (su < Ct) x = p.dLG[(rb + su) * D + c] - tof(K[(int64_t)su * D + c]) * dk[k][r];
             dBs[su * D + c] = x;
         }
     }
     __syncthreads();
     {   // suffix sums over the chunk's rows, NTHR / D parts per channel, plus
         // rowsum(R_t . P_{t+1}) = 2^(b_last) rho + Ep
-        constexpr int NP = NTHR / D, RP = GC / NP;
-        const int c = threadIdx.x % D, part = threadIdx.x / D, r0 = part * RP;
-        float x[RP];
+        constexpr int NP = NTHR / D, RPP = GC / NP;
+        const int c = threadIdx.x % D, part = threadIdx.x / D, r0 = part * RPP;
+        float x[RPP];
 #pragma unroll
-        for (int j = 0; j < RP; ++j) x[j] = dBs[(r0 + j) * D + c];
+        for (int j = 0; j < RPP; ++j) x[j] = dBs[(r0 + j) * D + c];
 #pragma unroll
-        for (int j = RP - 2; j >= 0; --j) x[j] += x[j + 1];
+        for (int j = RPP - 2; j >= 0; --j) x[j] += x[j + 1];
         __syncthreads();
         dBs[part * D + c] = x[0];
         __syncthreads();
@@ -952,7 +1048,7 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_grads(Params p) {
         for (int q = part + 1; q < NP; ++q) off += dBs[q * D + c];
         float *out = p.dLG + rb * D;
 #pragma unroll
-        for (int j = 0; j < RP; ++j)
+        for (int j = 0; j < RPP; ++j)
             if (r0 + j < Ct) out[(int64_t)(r0 + j) * D + c] = x[j] + off;
     }
 }
