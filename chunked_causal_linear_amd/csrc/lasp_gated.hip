@@ -98,26 +98,6 @@ __device__ __forceinline__ void chunk_cumlog(float *bS, const float *lg, int Ct)
     }
 }
 
-// acc += A[m0..m0+32)[0..K) * B[n0..n0+32)[0..K)^T with LDS operands (the
-// contraction index contiguous), two k-steps of fragments in flight: fewer
-// registers than a fully unrolled product, for kernels that run two
-// workgroups per CU.
-template <typename T, int K>
-__device__ __forceinline__ void gemm2(f32x16 &acc, const T *As, int pa, int m0, const T *Bs,
-                                      int pb, int n0) {
-    constexpr int V = Tr<T>::VEC;
-    using Fr = typename Tr<T>::frag;
-    const int l = lane_id();
-    const T *ap = As + (m0 + (l & 31)) * pa + (l >> 5) * V;
-    const T *bp = Bs + (n0 + (l & 31)) * pb + (l >> 5) * V;
-#pragma unroll 2
-    for (int k = 0; k < K; k += 2 * V) {
-        const Fr a = *(const Fr *)(ap + k);
-        const Fr b = *(const Fr *)(bp + k);
-        mma(acc, a, b);
-    }
-}
-
 // 16 bytes of V converted values at p.
 template <typename T>
 __device__ __forceinline__ void store_vec(T *p, const float *f) {
@@ -754,7 +734,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
             const bool slow = gated && ta == tb && (ta == 0 ? slow0 : slow1);
             f32x16 st;
             zero(st);
-            if (!slow) gemm2<T, D>(st, A, PD, 32 * ta, B, PD, brow(w));
+            if (!slow) gemm<T, D>(st, A, PD, 32 * ta, B, PD, brow(w));
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int a = 32 * ta + crow(r), b = 32 * tb + (l & 31);
@@ -803,7 +783,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
 #pragma unroll
             for (int k = 0; k < TO::PER_WAVE; ++k) {
                 int mi, ni;
-                if (TO::get(k, mi, ni)) gemm2<T, DH>(dq[k], dOr + dv0, PD, mi * 32, Pk, PDH, ni * 32);
+                if (TO::get(k, mi, ni)) gemm<T, DH>(dq[k], dOr + dv0, PD, mi * 32, Pk, PDH, ni * 32);
             }
         }
         // the threads sharing a dk group sum in a fixed order (no atomics:
@@ -845,8 +825,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
             const bool slow = mi == 0 ? slow0 : slow1;
-            if (mi == 1) gemm2<T, 32>(dq[k], Sc, PS, 32, KT3 + 32, PK, ni * 32);
-            if (!slow) gemm2<T, 32>(dq[k], Sc + 32 * mi, PS, 32 * mi, KT3 + (mi ? 64 : 0), PK, ni * 32);
+            if (mi == 1) gemm<T, 32>(dq[k], Sc, PS, 32, KT3 + 32, PK, ni * 32);
+            if (!slow) gemm<T, 32>(dq[k], Sc + 32 * mi, PS, 32 * mi, KT3 + (mi ? 64 : 0), PK, ni * 32);
             const int c = ni * 32 + (l & 31), m = mi * 32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -897,7 +877,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
                 for (int k = 0; k < TO::PER_WAVE; ++k) {
                     int mi, ni;
                     if (TO::get(k, mi, ni) && ni * 32 >= dv0 && ni * 32 < dv0 + DH)
-                        gemm2<T, D>(dv[k], Kl, PD, mi * 32, Rv, PD, ni * 32 - dv0);
+                        gemm<T, D>(dv[k], Kl, PD, mi * 32, Rv, PD, ni * 32 - dv0);
                 }
             }
         }
@@ -927,7 +907,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
-            gemm2<T, GC>(dv[k], Sc, PS, mi * 32, OT, PS, ni * 32);
+            gemm<T, GC>(dv[k], Sc, PS, mi * 32, OT, PS, ni * 32);
             store_rows(dv[k], (T *)p.dV + rb * D, D, mi * 32, ni * 32, Ct);
         }
         __syncthreads();
@@ -957,7 +937,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
 #pragma unroll
                 for (int k = 0; k < TO::PER_WAVE; ++k) {
                     int mi, ni;
-                    if (TO::get(k, mi, ni)) gemm2<T, DH>(dk[k], Vr + dv0, PD, mi * 32, RT, PDH, ni * 32);
+                    if (TO::get(k, mi, ni)) gemm<T, DH>(dk[k], Vr + dv0, PD, mi * 32, RT, PDH, ni * 32);
                 }
             }
         }
@@ -995,8 +975,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
             const bool slow = mi == 0 ? slow0 : slow1;
-            if (mi == 0) gemm2<T, 32>(dk[k], Sc + 32, PS, 0, QT3 + 32, PK, ni * 32);
-            if (!slow) gemm2<T, 32>(dk[k], Sc + 32 * mi, PS, 32 * mi, QT3 + (mi ? 64 : 0), PK, ni * 32);
+            if (mi == 0) gemm<T, 32>(dk[k], Sc + 32, PS, 0, QT3 + 32, PK, ni * 32);
+            if (!slow) gemm<T, 32>(dk[k], Sc + 32 * mi, PS, 32 * mi, QT3 + (mi ? 64 : 0), PK, ni * 32);
             const int c = ni * 32 + (l & 31), mJ = mi * 32 + 31;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
