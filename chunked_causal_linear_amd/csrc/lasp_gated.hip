@@ -772,7 +772,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
         for (int hh = 0; hh < L::NHALF; ++hh) {
             const int dv0 = hh * DH;
             if (hh) __syncthreads();
-            for_states<T, D, 2, 4, DH>(seg, loc, g, [&](int dv, int dk, const float (*x)[V]) {
+            for_states<T, D, 2, 2, DH>(seg, loc, g, [&](int dv, int dk, const float (*x)[V]) {
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
                     Pk[(dk + j) * PDH + dv - dv0] = fromf<T>(x[0][j]);
@@ -869,7 +869,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
             for (int hh = 0; hh < L::NHALF; ++hh) {
                 const int dv0 = hh * DH;
                 if (hh) __syncthreads();
-                for_states<T, D, 1, 4, DH>(seg, loc, g, [&](int dvv, int dk, const float (*x)[V]) {
+                for_states<T, D, 1, 2, DH>(seg, loc, g, [&](int dvv, int dk, const float (*x)[V]) {
                     store_vec(Rv + (dvv - dv0) * PD + dk, x[0]);
                 }, dv0);
                 __syncthreads();
@@ -929,7 +929,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
             for (int hh = 0; hh < L::NHALF; ++hh) {
                 const int dv0 = hh * DH;
                 if (hh) __syncthreads();
-                for_states<T, D, 1, 4, DH>(seg, loc, g, [&](int dvv, int dkk, const float (*x)[V]) {
+                for_states<T, D, 1, 2, DH>(seg, loc, g, [&](int dvv, int dkk, const float (*x)[V]) {
 #pragma unroll
                     for (int j = 0; j < V; ++j) RT[(dkk + j) * PDH + dvv - dv0] = fromf<T>(x[0][j]);
                 }, dv0);
