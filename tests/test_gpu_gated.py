@@ -84,6 +84,17 @@ def test_gated_segment_sizes(G, monkeypatch):
     check("gated G=" + G, run_gated(inp), oracle_gated(inp), TOL["fp32"])
 
 
+def test_gated_medium_multi_segment(monkeypatch):
+    """bf16 B2 H4 N4096 d128 (64 chunks per sequence) in segments of 8 chunks,
+    every element against the oracle's recurrence."""
+    monkeypatch.setenv("LASP_SEGMENT_CHUNKS", "8")
+    w = small("gated bf16 d128 B2 H4 N4096 G8", "bf16", B=2, H=4, N=4096, d=128, seed=76,
+              gates="mixed", m_in_scale=0.05, dm_out_scale=0.05)
+    say("case:", w.name)
+    inp = make_inputs(w)
+    check(w.name, run_gated(inp), oracle_gated(inp), TOL["bf16"])
+
+
 def test_gated_recompute_equals_cache():
     w = small("gated bf16 d128", "bf16", B=1, H=2, N=900, d=128, seed=71, gates="gla",
               m_in_scale=0.1, dm_out_scale=0.1)
