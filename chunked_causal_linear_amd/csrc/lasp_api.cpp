@@ -35,7 +35,7 @@ struct Plan {
     size_t cache_b;      // state cache = [Lc][Pseg][Pfin][Gc][Gs]
 };
 
-// gated: the per-channel gated form (chunk 64; f32 only with d <= 64).
+// gated: the per-channel gated form (chunk 64).
 int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false) {
     if (!s) return LASP_EINVAL;
     if (s->B <= 0 || s->H <= 0 || s->N <= 0 || s->d <= 0 || s->chunk <= 0 || s->nseq < 0)
@@ -44,7 +44,7 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false) 
     if (dt != LASP_FP32 && dt != LASP_BF16) return LASP_EUNSUPPORTED;
     if (s->d != 32 && s->d != 64 && s->d != 128) return LASP_EUNSUPPORTED;
     if (s->chunk != 64 && s->chunk != 128 && s->chunk != 256) return LASP_EUNSUPPORTED;
-    if (gated && (s->chunk != 64 || (dt == LASP_FP32 && s->d > 64))) return LASP_EUNSUPPORTED;
+    if (gated && s->chunk != 64) return LASP_EUNSUPPORTED;
     pl.D = s->d;
     pl.C = s->chunk;
     pl.H = s->H;
@@ -489,7 +489,7 @@ const char *lasp_status_string(int status) {
     case LASP_EINVAL: return "invalid argument";
     case LASP_EUNSUPPORTED:
         return "unsupported configuration (d in {32,64,128}, chunk in {64,128,256}, dtype fp32/bf16; "
-               "gated form: chunk 64, fp32 only with d <= 64; unmasked form: bf16)";
+               "gated form: chunk 64; unmasked form: bf16)";
     case LASP_EWORKSPACE: return "workspace too small";
     case LASP_EHIP: return g_hip_error.empty() ? "HIP error" : g_hip_error.c_str();
     }

@@ -26,6 +26,12 @@
 namespace lasp {
 
 constexpr int GC = 64;            // chunk length of the gated kernels
+
+// Workgroups per CU the local-state, output and gradient kernels are built
+// for (their LDS allows two, except for float32 at d = 128).
+template <typename T, int D> struct WgPerCu {
+    static constexpr int N = (sizeof(T) == 4 && D == 128) ? 1 : 2;
+};
 constexpr float SPAN2 = 80.f;     // largest log2-gate drop inside a factorised diagonal tile
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -293,7 +299,7 @@ __device__ float exact_score(const T *Q, const T *K, const float *bS, int s, int
 //   L = Diag(gam_t) L + (K_t 2^(b_last - b))^T V_t;   Z = L, Gs = all gates.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR) void k_gfwd_local(Params p) {
+__global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params p) {
     constexpr int PT = GC + Tr<T>::VEC;
     __shared__ float bS[GC * D];
     __shared__ __attribute__((aligned(16))) T KT_s[D * PT];
@@ -417,7 +423,7 @@ template <typename T, int D> struct OutLds {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR, 2) void k_gfwd_out(Params p) {
+__global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_out(Params p) {
     using L = OutLds<T, D>;
     constexpr int PD = L::PD, PS = L::PS, DH = L::DH;
     __shared__ float bS[GC * D];
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_gfwd_out(Params p) {
 //   R = Diag(gam_t) R + (Q_t 2^b)^T dO_t;   W = R.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR) void k_gbwd_local(Params p) {
+__global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params p) {
     constexpr int PT = GC + Tr<T>::VEC;
     __shared__ float bS[GC * D];
     __shared__ __attribute__((aligned(16))) T QT_s[D * PT];
@@ -673,7 +679,7 @@ struct GradLds {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR, 2) void k_gbwd_grads(Params p) {
+__global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params p) {
     using L = GradLds<T, D>;
     constexpr int V = Tr<T>::VEC, PD = L::PD, PS = L::PS, PK = L::PK, DH = L::DH, PDH = L::PDH;
     __shared__ float bS[GC * D];
@@ -1075,7 +1081,7 @@ hipError_t launch_fwd_gated(const Params &p, bool bf, bool with_output, hipStrea
     switch (p.D) {
     case 32: return bf ? gfwd<bf16, 32>(p, with_output, st, ev) : gfwd<float, 32>(p, with_output, st, ev);
     case 64: return bf ? gfwd<bf16, 64>(p, with_output, st, ev) : gfwd<float, 64>(p, with_output, st, ev);
-    case 128: return bf ? gfwd<bf16, 128>(p, with_output, st, ev) : hipErrorInvalidValue;
+    case 128: return bf ? gfwd<bf16, 128>(p, with_output, st, ev) : gfwd<float, 128>(p, with_output, st, ev);
     }
     return hipErrorInvalidValue;
 }
@@ -1085,7 +1091,7 @@ hipError_t launch_bwd_gated(const Params &p, bool bf, hipStream_t st, hipEvent_t
     switch (p.D) {
     case 32: return bf ? gbwd<bf16, 32>(p, st, ev) : gbwd<float, 32>(p, st, ev);
     case 64: return bf ? gbwd<bf16, 64>(p, st, ev) : gbwd<float, 64>(p, st, ev);
-    case 128: return bf ? gbwd<bf16, 128>(p, st, ev) : hipErrorInvalidValue;
+    case 128: return bf ? gbwd<bf16, 128>(p, st, ev) : gbwd<float, 128>(p, st, ev);
     }
     return hipErrorInvalidValue;
 }

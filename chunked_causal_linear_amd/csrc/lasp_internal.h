@@ -59,8 +59,7 @@ hipError_t launch_bwd(const Params &p, bool bf16, hipStream_t stream, hipEvent_t
 // totals, segment scan (Pfin = the summed state), O = Q M.  Backward: (tables),
 // reverse totals, reverse scan (Rfin = the summed gradient state), then
 // dQ = dO M^T, dV = K dM, dK = V dM^T; Pfin must be valid.
-// Gated form (per-token, per-key-channel gates given as logs; chunk 64; f32
-// with D <= 64 or bf16).  Same kernel sequence and events as launch_fwd /
+// Gated form (per-token, per-key-channel gates given as logs; chunk 64).  Same kernel sequence and events as launch_fwd /
 // launch_bwd; the forward also fills Gc and Gs, the backward Hc.
 hipError_t launch_fwd_gated(const Params &p, bool bf16, bool with_output, hipStream_t stream,
                             hipEvent_t *ev = nullptr);

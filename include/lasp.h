@@ -186,8 +186,8 @@ int lasp_bwd_bidir(const lasp_shape *shape, lasp_dtype dtype,
  *           overflow.
  * The backward, for l = <dO, O> + <dM_out, M_out>, also returns
  *   dlog_g  device float32 [B, H, N, d]: dl/d(log g_p).
- * Restrictions: shape->chunk must be 64 (the kernels' chunk length), and
- * LASP_FP32 needs d <= 64 (else LASP_EUNSUPPORTED).  Numbers: inside a chunk
+ * Restriction: shape->chunk must be 64, the kernels' chunk length (else
+ * LASP_EUNSUPPORTED).  Numbers: inside a chunk
  * the gates enter the bf16 MFMA operands as factors 2^(b_s - b_m) and
  * 2^(b_m - b_i) (b: running log2 of the gates; m: the first row of a 32-row
  * query tile), each at most 1 off the diagonal tiles; a diagonal tile whose

@@ -173,7 +173,7 @@ def test_bidir_rejects_bad_arguments(L):
 
 
 def test_gated_rejects_bad_arguments(L):
-    """The gated entry points: chunk 64 only, float32 only with d <= 64, log_g
+    """The gated entry points: chunk 64 only, log_g
     (and dlog_g) required, aligned and disjoint from the outputs."""
     s = Shape(1, 2, 300, 64, 64, 0)
     p = [fake(i) for i in range(14)]
@@ -199,9 +199,10 @@ def test_gated_rejects_bad_arguments(L):
     for c in (128, 256):
         assert fwd(shape=Shape(1, 2, 300, 64, c, 0)) == EUNSUP
         assert bwd(shape=Shape(1, 2, 300, 64, c, 0)) == EUNSUP
-    assert fwd(shape=Shape(1, 2, 300, 128, 64, 0), dt=0) == EUNSUP
-    assert L.lasp_gated_state_cache_bytes(ctypes.byref(Shape(1, 2, 300, 128, 64, 0)), 0) == 0
-    assert L.lasp_gated_state_cache_bytes(ctypes.byref(Shape(1, 2, 300, 128, 64, 0)), 1) > 0
+    assert fwd(shape=Shape(1, 2, 300, 48, 64, 0)) == EUNSUP
+    assert L.lasp_gated_state_cache_bytes(ctypes.byref(Shape(1, 2, 300, 128, 128, 0)), 1) == 0
+    for dt in (0, 1):
+        assert L.lasp_gated_state_cache_bytes(ctypes.byref(Shape(1, 2, 300, 128, 64, 0)), dt) > 0
     assert fwd(LG=None) == EINVAL and bwd(LG=None) == EINVAL and bwd(dLG=None) == EINVAL
     assert fwd(LG=ctypes.c_void_p(A + 9 * GAP + 4)) == EINVAL        # misaligned log_g
     assert fwd(O=p[9]) == EINVAL                                      # O aliases log_g
