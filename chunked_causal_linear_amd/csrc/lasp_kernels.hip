@@ -887,6 +887,41 @@ template <int C> struct SweepCfg {
     }
 };
 
+// f[e] *= b lambda^e (up) or b lambda^(7-e): the decay weights of 8
+// consecutive tokens from the weight b of the first (up) or last of them, by
+// successive products (the factors are at most 1, so no overflow).
+__device__ __forceinline__ void geo8(float *f, float b, float lam, bool up) {
+    if (up) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { f[e] *= b; b *= lam; }
+    } else {
+#pragma unroll
+        for (int e = 7; e >= 0; --e) { f[e] *= b; b *= lam; }
+    }
+}
+
+// The same over the 16 elements of a lane's 32x32 MFMA result tile, which sit
+// at offsets 8 (e >> 2) + (e & 3) along the tile's rows: s[e] *= b lambda^k(e),
+// k(e) = that offset (up), or 27 minus it.
+__device__ __forceinline__ void geo16(f32x16 &s, float b, float lam, bool up) {
+    const float lam4 = (lam * lam) * (lam * lam);
+    if (up) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { s[4 * g + i] *= b; b *= lam; }
+            b *= lam4;
+        }
+    } else {
+#pragma unroll
+        for (int g = 3; g >= 0; --g) {
+#pragma unroll
+            for (int i = 3; i >= 0; --i) { s[4 * g + i] *= b; b *= lam; }
+            b *= lam4;
+        }
+    }
+}
+
 // What one launch computes:
 enum SweepKind {
     SWEEP_OUT = 0,     // role 0 (O)
@@ -951,6 +986,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         seg = sl + 1 < min(s.S, p.n_segs_ub - s.s0) ? seg + (int64_t)p.H * D * D
                                                     : p.Pfin + ((int64_t)s.i * p.H + h) * D * D;
     const float sgn = sub ? -1.f : 1.f;
+    const float lam = dpow(l2, 1.f);
 
     const int w = wave_id(), l = lane_id();
     const int rt = Cfg::tile(w);
@@ -1099,7 +1135,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         bf16x8_t s0[NP], s1[NP];
 #pragma unroll
         for (int u = 0; u < NP; ++u) {
-            if (ct[u] == rt || decay || (ct[u] + 1) * 32 > Ct) {
+            if (ct[u] == rt || (ct[u] + 1) * 32 > Ct) {
                 const int r = rt * 32 + lc;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -1108,6 +1144,11 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
                     const float f = decay ? dpow(l2, (float)max(dist, 0)) : 1.f;
                     st[u][e] = (dist >= dmin && c < Ct) ? st[u][e] * f : 0.f;
                 }
+            } else if (decay) {
+                // off-diagonal tile inside the chunk: every distance is
+                // positive; one power for the lane's nearest column
+                const int r = rt * 32 + lc, c0 = ct[u] * 32 + crow(0, lz);
+                geo16(st[u], dpow(l2, (float)(rev ? c0 - r : r - c0 - 27)), lam, rev);
             }
             // as an operand, S^T's k order is permuted; the Cv fragment follows it
             s0[u] = pack8(st[u][0], st[u][1], st[u][2], st[u][3], st[u][4], st[u][5], st[u][6], st[u][7]);
@@ -1123,12 +1164,15 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // state += (scaled U)^T W over the tokens of the group's column tiles.
+    // state += U^T (scaled W) over the tokens of the group's column tiles.
     // Steps (column tile, 16-token half): the W fragment is shared by the
     // wave's state tiles (they have the same column block ni), each tile reads
     // its own U fragment; the fragments of step j+1 are read while the MFMAs
-    // of step j run.  Tiles past the chunk end are masked to zero by the
-    // scaling path (their LDS slots hold clamped, valid rows).
+    // of step j run.  The token weights (lambda^(Ct-1-tk), or lambda^(tk+1)
+    // when walking backwards) go on the shared W fragment, the token index
+    // being the contraction index: one power per fragment times the per-lane
+    // successive factors lambda (geo8).  Tokens past the chunk end are masked to zero there
+    // (their LDS slots hold clamped, valid rows).
     static_assert(NW % NDT == 0, "state tiles of one wave must share their column block");
     auto state_updates = [&](const bf16 *BG, auto G, int Ct, auto XTC) __attribute__((always_inline)) {
         constexpr int g = decltype(G)::value;
@@ -1155,25 +1199,30 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
             if (j + 1 < NSU) fetch(j + 1, wf[(j + 1) & 1], uf[(j + 1) & 1]);
             const int ct = Cfg::group_tile(g, j >> 1), kk = j & 1;
             const bool scale = decay || (ct + 1) * 32 > Ct;
+            bf16x8_t wa = wf[j & 1];
+            if (scale) {
+                float f[8];
+                load16((const bf16 *)&wa, f);
+                const int tk0 = ct * 32 + kk * 16 + lg * 8;
+                if (tk0 + 7 < Ct) {   // the 8 tokens are in the chunk
+                    if (decay) geo8(f, dpow(l2, (float)(rev ? tk0 + 1 : Ct - 1 - (tk0 + 7))), lam, rev);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int tk = tk0 + e;
+                        const float sc = decay ? dpow(l2, (float)max(rev ? tk + 1 : Ct - 1 - tk, 0)) : 1.f;
+                        f[e] = tk < Ct ? f[e] * sc : 0.f;
+                    }
+                }
+                wa = pack8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+            }
 #pragma unroll
             for (int k = 0; k < STW; ++k) {
                 if (w + k * NW < NSTT) {
-                    bf16x8_t ua = uf[j & 1][k];
-                    if (scale) {
-                        float f[8];
-                        load16((const bf16 *)&ua, f);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int tk = ct * 32 + kk * 16 + lg * 8 + e;
-                            const float sc = dpow(l2, (float)max(rev ? tk + 1 : Ct - 1 - tk, 0));
-                            f[e] = tk < Ct ? f[e] * sc : 0.f;
-                        }
-                        ua = pack8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
-                    }
                     if (XT)
-                        mma(sacc[k], wf[j & 1], ua);
+                        mma(sacc[k], wa, uf[j & 1][k]);
                     else
-                        mma(sacc[k], ua, wf[j & 1]);
+                        mma(sacc[k], uf[j & 1][k], wa);
                 }
             }
         }
@@ -1359,6 +1408,7 @@ __global__ __launch_bounds__(SegTotCfg<D>::NT) void k_segtot_bf16(Params p) {
     f32x16 sacc[STW];
 #pragma unroll
     for (int k = 0; k < STW; ++k) zero(sacc[k]);
+    const float lam = dpow(l2, 1.f);
 
     // step j: tiles TPS j .. TPS j + TPS - 1 (swizzled rows, rows past L
     // clamped to a valid row) into ring slot j % NSLOT, as [tile][U, W]
@@ -1388,24 +1438,29 @@ __global__ __launch_bounds__(SegTotCfg<D>::NT) void k_segtot_bf16(Params p) {
         const bool scale = decay || (tq + 1) * 32 > L;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8_t wf = frag_cols_sw<D, false>(Wt, fo, kk * 16, ni * 32);
+            // the token weights go on the shared W fragment (see the sweep's
+            // state updates)
+            bf16x8_t wf = frag_cols_sw<D, false>(Wt, fo, kk * 16, ni * 32);
+            if (scale) {
+                float f[8];
+                load16((const bf16 *)&wf, f);
+                const int tau0 = tq * 32 + kk * 16 + lg * 8;
+                if (tau0 + 7 < L) {
+                    if (decay) geo8(f, dpow(l2, (float)(BWD ? tau0 + 1 : L - 1 - (tau0 + 7))), lam, BWD);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int tau = tau0 + e;
+                        const float sc = decay ? dpow(l2, (float)(BWD ? tau + 1 : L - 1 - tau)) : 1.f;
+                        f[e] = tau < L ? f[e] * sc : 0.f;
+                    }
+                }
+                wf = pack8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+            }
 #pragma unroll
             for (int k = 0; k < STW; ++k) {
-                if (w + k * NW < NSTT) {
-                    bf16x8_t ua = frag_cols_sw<D, false>(Ut, fo, kk * 16, ((w + k * NW) / NDT) * 32);
-                    if (scale) {
-                        float f[8];
-                        load16((const bf16 *)&ua, f);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int tau = tq * 32 + kk * 16 + lg * 8 + e;
-                            const float sc = decay ? dpow(l2, (float)(BWD ? tau + 1 : L - 1 - tau)) : 1.f;
-                            f[e] = tau < L ? f[e] * sc : 0.f;
-                        }
-                        ua = pack8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
-                    }
-                    mma(sacc[k], ua, wf);
-                }
+                if (w + k * NW < NSTT)
+                    mma(sacc[k], frag_cols_sw<D, false>(Ut, fo, kk * 16, ((w + k * NW) / NDT) * 32), wf);
             }
         }
     };
