@@ -102,14 +102,14 @@ def src_sha(files=None):
     return h.hexdigest()
 
 
-def measured_traffic(kernel, traffic_file=None, files=None):
+def measured_traffic(kernel, workload, traffic_file=None, files=None):
     """HBM bytes per launch from committed rocprofv3 counters, if they were taken
-    on the current kernel source; else None."""
+    on the current kernel source and on this workload; else None."""
     try:
         t = json.load(open(traffic_file or TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != src_sha(files):
+    if t.get("source_sha256") != src_sha(files) or t.get("workload") != workload:
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -252,7 +252,7 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom)
+    roof["traffic"] = measured_traffic(dom, w.name)
     roof.update(kernel=dom, ms=kms[dom], algorithmic_bytes=bytes_, algorithmic_flops=flops)
 
     tokens = sh["B"] * sh["N"]
@@ -428,7 +428,7 @@ def bench_gated(a, w, sh, inp, torch, cca):
         roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom, GATED_TRAFFIC_FILE, GATED_SRC)
+    roof["traffic"] = measured_traffic(dom, w.name, GATED_TRAFFIC_FILE, GATED_SRC)
     roof.update(kernel="gated " + dom, ms=kms[dom], algorithmic_bytes=bytes_,
                 algorithmic_flops=flops)
     tokens = sh["B"] * sh["N"]

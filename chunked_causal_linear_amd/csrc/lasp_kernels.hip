@@ -925,16 +925,21 @@ __device__ __forceinline__ void geo16(f32x16 &s, float b, float lam, bool up) {
 // What one launch computes:
 enum SweepKind {
     SWEEP_OUT = 0,     // role 0 (O)
-    SWEEP_GRADS = 1    // roles 1-3 (dQ, dV, dK), neighbours in launch order so
+    SWEEP_GRADS = 1,   // roles 1-3 (dQ, dV, dK), neighbours in launch order so
                        // that the roles of one segment run at the same time and
                        // share their reads of Q, K, V, dO in L2
+    // With decay the dQ role walks forwards while dV and dK walk backwards,
+    // at other speeds: in one launch the three drift apart and share nothing.
+    // Such calls launch dV + dK together (they keep in step) and dQ after them.
+    SWEEP_DQ = 2,      // role 1
+    SWEEP_DVDK = 3     // roles 2-3
 };
 // DEC = false: the call has no decay array (every lambda is 1); the decay
 // arithmetic is compiled out.
 template <int D, int C, int KIND, bool DEC>
 __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
-    constexpr int role0 = KIND == SWEEP_GRADS ? 1 : 0;
-    constexpr int nroles = KIND == SWEEP_GRADS ? 3 : 1;
+    constexpr int role0 = KIND == SWEEP_GRADS || KIND == SWEEP_DQ ? 1 : KIND == SWEEP_DVDK ? 2 : 0;
+    constexpr int nroles = KIND == SWEEP_GRADS ? 3 : KIND == SWEEP_DVDK ? 2 : 1;
     using Cfg = SweepCfg<C>;
     constexpr int NCT = Cfg::NCT, NW = Cfg::NW, NG = Cfg::NG;
     constexpr int PR = D / 8, KS = D / 16, NDT = D / 32;
@@ -1675,10 +1680,18 @@ template <int D, int C, int KIND>
 static void sweep_launch(const Params &p, hipStream_t st) {
     const int roles = KIND == SWEEP_GRADS ? 3 : 1;
     const dim3 grid(round8(p.n_segs_ub * p.H * roles)), block(SweepCfg<C>::NT);
-    if (p.decay)
-        hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND, true>), grid, block, 0, st, p);
-    else
+    if (p.decay) {
+        if constexpr (KIND == SWEEP_GRADS) {
+            hipLaunchKernelGGL((k_sweep_bf16<D, C, SWEEP_DVDK, true>),
+                               dim3(round8(p.n_segs_ub * p.H * 2)), block, 0, st, p);
+            hipLaunchKernelGGL((k_sweep_bf16<D, C, SWEEP_DQ, true>), dim3(round8(p.n_segs_ub * p.H)),
+                               block, 0, st, p);
+        } else {
+            hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND, true>), grid, block, 0, st, p);
+        }
+    } else {
         hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND, false>), grid, block, 0, st, p);
+    }
 }
 
 template <int D, int KIND>
