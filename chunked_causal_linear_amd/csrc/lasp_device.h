@@ -299,4 +299,136 @@ __device__ __forceinline__ void zero(f32x16 &a) {
     for (int r = 0; r < 16; ++r) a[r] = 0.f;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 operand fragments for the 32x32x16 MFMA, read from LDS tiles.  Operands
+// whose contraction index is the token index come from row-major tiles via the
+// LDS transpose read (ds_read_b64_tr_b16), so no transposed copies are made.
+// ---------------------------------------------------------------------------
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// Operand fragment from an LDS tile stored X[k][n] (n contiguous), operand row
+// n0 + lane%32.  With g = lane/32 the 8 contraction elements are
+// k0 + 8g + [0, 8) (PERM = false) or k0 + 4g + {0..3, 8..11} (PERM = true).
+// ds_read_b64_tr_b16 works on groups of 16 lanes: when lane i of a group reads
+// the 4 elements at row rb + i/4, columns cb + 4*(i%4), lane j of the group
+// receives rows rb + 0..3 of column cb + j.
+template <bool PERM>
+__device__ __forceinline__ bf16x8_t frag_cols(const bf16 *X, int pitch, int k0, int n0,
+                                              int l = lane_id()) {
+    const int i = l & 15, h = l >> 4, g = h >> 1;
+    const int col = n0 + (h & 1) * 16 + 4 * (i & 3);
+    const int ra = k0 + (PERM ? 4 * g : 8 * g) + (i >> 2);
+    const int rb = ra + (PERM ? 8 : 4);
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(X + ra * pitch + col));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(X + rb * pitch + col));
+    const v8s c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, c);
+}
+
+__device__ __forceinline__ bf16x8_t pack8(float a0, float a1, float a2, float a3, float a4,
+                                          float a5, float a6, float a7) {
+    bf16x8_t r;
+    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+    r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Unpadded LDS tiles.  global_load_lds_dwordx4 writes lane l's 16 bytes to
+// lds_base + 16*l, so token tiles are stored without padding and their 16-byte
+// pieces are permuted within each row: piece p of row r sits in slot
+// r*PR + (p ^ key(r)), PR = pieces per row.  key(r) depends on r mod 16 and is
+// linear over GF(2) in its four bits; it is chosen (by exhaustive search over
+// such keys) so that the operand reads below touch every LDS bank once per
+// access group, both for 128-byte and for 256-byte bank rows:
+//   frag_rows_sw  ds_read_b128, 32 consecutive rows, one piece each;
+//   frag_cols_sw  ds_read_b64_tr_b16, 4 consecutive rows x 2 or 4 pieces.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D> struct SwKey {
+    // images of row bits 0..3; key(r) = XOR of the images of the set bits
+    static constexpr int m0 = D == 128 ? 4 : (D == 64 ? 2 : 0);
+    static constexpr int m1 = D == 128 ? 10 : (D == 64 ? 4 : 2);
+    static constexpr int m2 = 1, m3 = 2;
+    static constexpr unsigned long long table() {
+        unsigned long long t = 0;
+        for (int r = 0; r < 16; ++r) {
+            const int k = ((r & 1) ? m0 : 0) ^ ((r & 2) ? m1 : 0) ^ ((r & 4) ? m2 : 0) ^
+                          ((r & 8) ? m3 : 0);
+            t |= (unsigned long long)k << (4 * r);
+        }
+        return t;
+    }
+    static constexpr unsigned long long T = table();
+};
+
+template <int D>
+__device__ __forceinline__ int sw_key(int r) {
+    return (int)((SwKey<D>::T >> (4 * (r & 15))) & 15);
+}
+
+template <int D>
+__device__ __forceinline__ int sw_off(int r, int c) {
+    constexpr int PR = D / 8;
+    return (r * PR + ((c >> 3) ^ sw_key<D>(r))) * 8 + (c & 7);
+}
+
+// Operand fragments from swizzled tiles (the layout of frag_cols above, with
+// sw_off placement).  The lane-dependent part of every fragment address is a
+// per-lane byte offset computed once (FragOffs); a fragment address is then
+// that offset XOR a wave-uniform term, plus a wave-uniform base: one VALU
+// operation.  This holds for tiles whose first row is a multiple of 16: the
+// XOR only touches the piece bits of the offset.
+//   frag_rows: rows r0 + lane%32, k = k0 + (lane/32)*8 + [0, 8)   (k0 % 16 == 0)
+//   frag_cols: operand row n0 + lane%32 of a tile stored [k][n]      (n0 % 32 == 0)
+template <int D> struct FragOffs {
+    uint32_t rows;          // frag_rows: XOR 2*k0, add 2*r0*D
+    uint32_t cols[2][2];    // frag_cols [PERM][first/second read]: XOR 2*n0, add 2*k0*D
+};
+
+template <int D>
+__device__ __forceinline__ FragOffs<D> frag_offs(int l) {
+    FragOffs<D> o;
+    o.rows = 2u * sw_off<D>(l & 31, (l >> 5) * 8);
+    const int i = l & 15, h = l >> 4, g = h >> 1;
+    const int col = (h & 1) * 16 + 4 * (i & 3);
+#pragma unroll
+    for (int perm = 0; perm < 2; ++perm) {
+        const int ra = (perm ? 4 * g : 8 * g) + (i >> 2);
+        o.cols[perm][0] = 2u * sw_off<D>(ra, col);
+        o.cols[perm][1] = 2u * sw_off<D>(ra + (perm ? 8 : 4), col);
+    }
+    return o;
+}
+
+// A copy of o that the compiler cannot see through: address terms derived from
+// it are then computed where they are used rather than hoisted out of loops
+// into registers of their own.
+template <int D>
+__device__ __forceinline__ FragOffs<D> opaque(FragOffs<D> o) {
+    asm volatile("" : "+v"(o.rows), "+v"(o.cols[0][0]), "+v"(o.cols[0][1]), "+v"(o.cols[1][0]),
+                 "+v"(o.cols[1][1]));
+    return o;
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t frag_rows_sw(const bf16 *X, const FragOffs<D> &o, int r0, int k0) {
+    const char *b = (const char *)X + 2 * r0 * D;
+    return *(const bf16x8_t *)(b + (o.rows ^ (uint32_t)(2 * k0)));
+}
+
+template <int D, bool PERM>
+__device__ __forceinline__ bf16x8_t frag_cols_sw(const bf16 *X, const FragOffs<D> &o, int k0, int n0) {
+    const char *b = (const char *)X + 2 * k0 * D;
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s *)(b + (o.cols[PERM][0] ^ (uint32_t)(2 * n0))));
+    const v4s c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s *)(b + (o.cols[PERM][1] ^ (uint32_t)(2 * n0))));
+    const v8s r = __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
 }  // namespace lasp

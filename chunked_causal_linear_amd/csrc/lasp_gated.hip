@@ -187,6 +187,53 @@ __device__ __forceinline__ void raw_store(const Raw<T, D, R> &raw, T *dst, int p
     raw_store_map<T, D, R, TRANS>(raw, dst, pitch, Ct, row, scale, RowId());
 }
 
+// bf16: raw_store into an unpadded row-major tile in the swizzled placement
+// sw_off (tile rows 0 .. R-1; rows dst_row(j) < 0 skipped), read back with
+// frag_rows_sw / frag_cols_sw.
+template <int D, int R, typename RowF, typename ScaleF, typename DstF = RowId>
+__device__ __forceinline__ void raw_store_sw(const Raw<bf16, D, R> &raw, bf16 *dst, int Ct, RowF row,
+                                             ScaleF scale, DstF dst_row = DstF()) {
+    using RW = Raw<bf16, D, R>;
+    constexpr int V = RW::V;
+#pragma unroll
+    for (int u = 0; u < RW::IT; ++u) {
+        const int i = u * NTHR + threadIdx.x;
+        if (i >= RW::N) continue;
+        const int j = i / RW::PR, c = (i % RW::PR) * V;
+        const int dj = dst_row(j);
+        if (dj < 0) continue;
+        const int r = row(j);
+        float f[V];
+        unpack16(raw.v[u], f, (const bf16 *)nullptr);
+        if (r < Ct) scale(j, r, c, f);
+        store_vec(dst + sw_off<D>(dj, c), f);
+    }
+}
+
+// acc += X[k][m0 + i] Y[k][n0 + j] summed over k < K, X and Y swizzled bf16
+// tiles whose rows are the contraction index (transpose reads for both).
+template <int D, int K>
+__device__ __forceinline__ void gemm_cc(f32x16 &acc, const bf16 *X, int m0, const bf16 *Y, int n0,
+                                        const FragOffs<D> &fo) {
+#pragma unroll
+    for (int k = 0; k < K; k += 16)
+        mma(acc, frag_cols_sw<D, false>(X, fo, k, m0), frag_cols_sw<D, false>(Y, fo, k, n0));
+}
+
+// acc += A[m0 + i][k] Y[k][n0 + j] summed over k < K: A bf16 rows with the
+// contraction index contiguous (pitch pa), Y a swizzled bf16 tile whose rows
+// are the contraction index (transpose reads).
+template <int D, int K>
+__device__ __forceinline__ void gemm_rc(f32x16 &acc, const bf16 *A, int pa, int m0, const bf16 *Y,
+                                        int n0, const FragOffs<D> &fo, int y0 = 0) {
+    // (Y's rows y0 .. y0 + K - 1; y0 a multiple of 16)
+    const int l = lane_id();
+    const bf16 *ap = A + (m0 + (l & 31)) * pa + (l >> 5) * 8;
+#pragma unroll
+    for (int k = 0; k < K; k += 16)
+        mma(acc, *(const bf16x8_t *)(ap + k), frag_cols_sw<D, false>(Y, fo, y0 + k, n0));
+}
+
 struct NoScale {
     template <typename F> __device__ void operator()(int, int, int, F) const {}
 };
@@ -300,11 +347,15 @@ __device__ float exact_score(const T *Q, const T *K, const float *bS, int s, int
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params p) {
+    // bf16: K and V rows in swizzled row-major tiles, read transposed;
+    // float32: transposed copies
+    constexpr bool SW = sizeof(T) == 2;
     constexpr int PT = GC + Tr<T>::VEC;
     __shared__ float bS[GC * D];
-    __shared__ __attribute__((aligned(16))) T KT_s[D * PT];
-    __shared__ __attribute__((aligned(16))) T VT_s[D * PT];
+    __shared__ __attribute__((aligned(16))) T KT_s[SW ? GC * D : D * PT];
+    __shared__ __attribute__((aligned(16))) T VT_s[SW ? GC * D : D * PT];
     using TL = Tiles<D / 32, D / 32>;
+    const FragOffs<D> fo = frag_offs<D>(lane_id());
 
     const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
     Seq s;
@@ -347,9 +398,15 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params 
         __syncthreads();
         cumlog_scan<D>(bS, rl);
         __syncthreads();
-        raw_store<T, D, GC, true>(rk, KT_s, PT, Ct, RowId(),
-                                  gate_scale<T>(bS, D, [](int) { return GC - 1; }));
-        raw_store<T, D, GC, true>(rv, VT_s, PT, Ct, RowId(), NoScale());
+        if constexpr (SW) {
+            raw_store_sw<D, GC>(rk, (bf16 *)KT_s, Ct, RowId(),
+                                gate_scale<T>(bS, D, [](int) { return GC - 1; }));
+            raw_store_sw<D, GC>(rv, (bf16 *)VT_s, Ct, RowId(), NoScale());
+        } else {
+            raw_store<T, D, GC, true>(rk, KT_s, PT, Ct, RowId(),
+                                      gate_scale<T>(bS, D, [](int) { return GC - 1; }));
+            raw_store<T, D, GC, true>(rv, VT_s, PT, Ct, RowId(), NoScale());
+        }
         if (t + 1 < t1) {
             const int Cn = min(GC, s.len - tok - GC);
             raw_load(rk, K + (int64_t)(tok + GC) * D, Cn, RowId());
@@ -363,7 +420,10 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params 
             if (TL::get(k, mi, ni)) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[k][r] *= ex2(bS[(GC - 1) * D + mi * 32 + crow(r)]);
-                gemm<T, GC>(acc[k], KT_s, PT, mi * 32, VT_s, PT, ni * 32);
+                if constexpr (SW)
+                    gemm_cc<D, GC>(acc[k], (const bf16 *)KT_s, mi * 32, (const bf16 *)VT_s, ni * 32, fo);
+                else
+                    gemm<T, GC>(acc[k], KT_s, PT, mi * 32, VT_s, PT, ni * 32);
             }
         }
         if (threadIdx.x < D) gcum *= ex2(bS[(GC - 1) * D + threadIdx.x]);
@@ -524,15 +584,25 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_out(Params p)
     if (w == 0) score_tile(0, 0, 0, slow0);
     __syncthreads();
 
-    // 3: o += Sc V
+    // 3: o += Sc V (bf16: V rows in a swizzled tile, read transposed;
+    // float32: a transposed copy)
+    constexpr bool SW = sizeof(T) == 2;
+    static_assert(GC * D <= L::SOFF, "V must not reach the scores");
     T *VT = U;
-    raw_store<T, D, GC, true>(rv, VT, PS, Ct, RowId(), NoScale());
+    if constexpr (SW)
+        raw_store_sw<D, GC>(rv, (bf16 *)VT, Ct, RowId(), NoScale());
+    else
+        raw_store<T, D, GC, true>(rv, VT, PS, Ct, RowId(), NoScale());
     __syncthreads();
+    const FragOffs<D> fo = frag_offs<D>(l);
 #pragma unroll
     for (int k = 0; k < TO::PER_WAVE; ++k) {
         int mi, ni;
         if (TO::get(k, mi, ni)) {
-            gemm<T, GC>(o[k], Sc, PS, mi * 32, VT, PS, ni * 32);
+            if constexpr (SW)
+                gemm_rc<D, GC>(o[k], (const bf16 *)Sc, PS, mi * 32, (const bf16 *)VT, ni * 32, fo);
+            else
+                gemm<T, GC>(o[k], Sc, PS, mi * 32, VT, PS, ni * 32);
             store_rows(o[k], O, D, mi * 32, ni * 32, Ct);
         }
     }
@@ -546,11 +616,13 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_out(Params p)
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params p) {
+    constexpr bool SW = sizeof(T) == 2;   // as in k_gfwd_local
     constexpr int PT = GC + Tr<T>::VEC;
     __shared__ float bS[GC * D];
-    __shared__ __attribute__((aligned(16))) T QT_s[D * PT];
-    __shared__ __attribute__((aligned(16))) T OT_s[D * PT];
+    __shared__ __attribute__((aligned(16))) T QT_s[SW ? GC * D : D * PT];
+    __shared__ __attribute__((aligned(16))) T OT_s[SW ? GC * D : D * PT];
     using TL = Tiles<D / 32, D / 32>;
+    const FragOffs<D> fo = frag_offs<D>(lane_id());
 
     const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
     Seq s;
@@ -592,8 +664,15 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params 
         __syncthreads();
         cumlog_scan<D>(bS, rl);
         __syncthreads();
-        raw_store<T, D, GC, true>(rq, QT_s, PT, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return -1; }));
-        raw_store<T, D, GC, true>(ro, OT_s, PT, Ct, RowId(), NoScale());
+        if constexpr (SW) {
+            raw_store_sw<D, GC>(rq, (bf16 *)QT_s, Ct, RowId(),
+                                gate_scale<T>(bS, D, [](int) { return -1; }));
+            raw_store_sw<D, GC>(ro, (bf16 *)OT_s, Ct, RowId(), NoScale());
+        } else {
+            raw_store<T, D, GC, true>(rq, QT_s, PT, Ct, RowId(),
+                                      gate_scale<T>(bS, D, [](int) { return -1; }));
+            raw_store<T, D, GC, true>(ro, OT_s, PT, Ct, RowId(), NoScale());
+        }
         if (t - 1 >= t0) {   // chunk t - 1 is full
             raw_load(rq, Q + (int64_t)(tok - GC) * D, GC, RowId());
             raw_load(ro, dO + (int64_t)(tok - GC) * D, GC, RowId());
@@ -606,7 +685,10 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params 
             if (TL::get(k, mi, ni)) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[k][r] *= ex2(bS[(GC - 1) * D + mi * 32 + crow(r)]);
-                gemm<T, GC>(acc[k], QT_s, PT, mi * 32, OT_s, PT, ni * 32);
+                if constexpr (SW)
+                    gemm_cc<D, GC>(acc[k], (const bf16 *)QT_s, mi * 32, (const bf16 *)OT_s, ni * 32, fo);
+                else
+                    gemm<T, GC>(acc[k], QT_s, PT, mi * 32, OT_s, PT, ni * 32);
             }
         }
         if (threadIdx.x < D) hcum *= ex2(bS[(GC - 1) * D + threadIdx.x]);
@@ -682,6 +764,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params p) {
     using L = GradLds<T, D>;
     constexpr int V = Tr<T>::VEC, PD = L::PD, PS = L::PS, PK = L::PK, DH = L::DH, PDH = L::PDH;
+    constexpr bool SW = sizeof(T) == 2;   // bf16: transpose reads of row tiles
+    static_assert(96 * D <= L::SOFF, "K / Q rows must not reach the scores");
     __shared__ float bS[GC * D];
     __shared__ float rho[D], Ep[D];
     __shared__ __attribute__((aligned(16))) char U_raw[L::BYTES];
@@ -821,9 +905,15 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
         tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
         scores(dOr, Vr, [](int ww) { return ww == 2 ? 32 : 0; }, false, false, false, no_exact, 7, true);
         __syncthreads();
+        // (bf16: the three versions as rows of a swizzled tile, read
+        // transposed; float32: transposed copies)
         T *KT3 = U;   // (J=0 | ref row 0), (J=0 | ref 32), (J=1 | ref 32)
-        raw_store<T, D, 96, true>(rk96, KT3, PK, Ct, krow,
-                                  gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
+        if constexpr (SW)
+            raw_store_sw<D, 96>(rk96, (bf16 *)KT3, Ct, krow,
+                                gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
+        else
+            raw_store<T, D, 96, true>(rk96, KT3, PK, Ct, krow,
+                                      gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
         raw_load(rkq, K, Ct, RowId());   // K rows for B, in flight during A
         __syncthreads();
 #pragma unroll
@@ -831,8 +921,16 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
             const bool slow = mi == 0 ? slow0 : slow1;
-            if (mi == 1) gemm<T, 32>(dq[k], Sc, PS, 32, KT3 + 32, PK, ni * 32);
-            if (!slow) gemm<T, 32>(dq[k], Sc + 32 * mi, PS, 32 * mi, KT3 + (mi ? 64 : 0), PK, ni * 32);
+            if constexpr (SW) {
+                const FragOffs<D> fo = frag_offs<D>(l);
+                if (mi == 1) gemm_rc<D, 32>(dq[k], (const bf16 *)Sc, PS, 32, (const bf16 *)KT3, ni * 32, fo, 32);
+                if (!slow)
+                    gemm_rc<D, 32>(dq[k], (const bf16 *)Sc + 32 * mi, PS, 32 * mi, (const bf16 *)KT3, ni * 32,
+                                   fo, mi ? 64 : 0);
+            } else {
+                if (mi == 1) gemm<T, 32>(dq[k], Sc, PS, 32, KT3 + 32, PK, ni * 32);
+                if (!slow) gemm<T, 32>(dq[k], Sc + 32 * mi, PS, 32 * mi, KT3 + (mi ? 64 : 0), PK, ni * 32);
+            }
             const int c = ni * 32 + (l & 31), m = mi * 32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -906,14 +1004,20 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
         __syncthreads();
         scores(Qg, K64, [](int) { return 0; }, false, true, true, exact, 1, false);
         __syncthreads();
-        T *OT = U;   // dO^T [dv][query]
-        raw_store<T, D, GC, true>(rdo, OT, PS, Ct, RowId(), NoScale());
+        T *OT = U;   // dO^T [dv][query] (bf16: dO rows, swizzled, read transposed)
+        if constexpr (SW)
+            raw_store_sw<D, GC>(rdo, (bf16 *)OT, Ct, RowId(), NoScale());
+        else
+            raw_store<T, D, GC, true>(rdo, OT, PS, Ct, RowId(), NoScale());
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
-            gemm<T, GC>(dv[k], Sc, PS, mi * 32, OT, PS, ni * 32);
+            if constexpr (SW)
+                gemm_rc<D, GC>(dv[k], (const bf16 *)Sc, PS, mi * 32, (const bf16 *)OT, ni * 32, frag_offs<D>(l));
+            else
+                gemm<T, GC>(dv[k], Sc, PS, mi * 32, OT, PS, ni * 32);
             store_rows(dv[k], (T *)p.dV + rb * D, D, mi * 32, ni * 32, Ct);
         }
         __syncthreads();
@@ -972,17 +1076,29 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
         __syncthreads();
         scores(Vr, dOr, [](int ww) { return ww == 0 ? 0 : 32; }, true, false, false, no_exact, 7, true);
         __syncthreads();
-        T *QT3 = U;   // (I=0 | ref row 31), (I=1 | ref 31), (I=1 | ref 63)
-        raw_store<T, D, 96, true>(rk96, QT3, PK, Ct, qrow,
-                                  gate_scale<T>(bS, D, [](int j) { return j < 64 ? 31 : 63; }, true));
+        T *QT3 = U;   // (I=0 | ref row 31), (I=1 | ref 31), (I=1 | ref 63), stored as KT3
+        if constexpr (SW)
+            raw_store_sw<D, 96>(rk96, (bf16 *)QT3, Ct, qrow,
+                                gate_scale<T>(bS, D, [](int j) { return j < 64 ? 31 : 63; }, true));
+        else
+            raw_store<T, D, 96, true>(rk96, QT3, PK, Ct, qrow,
+                                      gate_scale<T>(bS, D, [](int j) { return j < 64 ? 31 : 63; }, true));
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
             const bool slow = mi == 0 ? slow0 : slow1;
-            if (mi == 0) gemm<T, 32>(dk[k], Sc + 32, PS, 0, QT3 + 32, PK, ni * 32);
-            if (!slow) gemm<T, 32>(dk[k], Sc + 32 * mi, PS, 32 * mi, QT3 + (mi ? 64 : 0), PK, ni * 32);
+            if constexpr (SW) {
+                const FragOffs<D> fo = frag_offs<D>(l);
+                if (mi == 0) gemm_rc<D, 32>(dk[k], (const bf16 *)Sc + 32, PS, 0, (const bf16 *)QT3, ni * 32, fo, 32);
+                if (!slow)
+                    gemm_rc<D, 32>(dk[k], (const bf16 *)Sc + 32 * mi, PS, 32 * mi, (const bf16 *)QT3, ni * 32,
+                                   fo, mi ? 64 : 0);
+            } else {
+                if (mi == 0) gemm<T, 32>(dk[k], Sc + 32, PS, 0, QT3 + 32, PK, ni * 32);
+                if (!slow) gemm<T, 32>(dk[k], Sc + 32 * mi, PS, 32 * mi, QT3 + (mi ? 64 : 0), PK, ni * 32);
+            }
             const int c = ni * 32 + (l & 31), mJ = mi * 32 + 31;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
