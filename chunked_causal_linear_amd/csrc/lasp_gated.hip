@@ -766,6 +766,7 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
     constexpr int V = Tr<T>::VEC, PD = L::PD, PS = L::PS, PK = L::PK, DH = L::DH, PDH = L::PDH;
     constexpr bool SW = sizeof(T) == 2;   // bf16: transpose reads of row tiles
     static_assert(96 * D <= L::SOFF, "K / Q rows must not reach the scores");
+    static_assert(!SW || DH * D <= L::CPART, "swizzled state parts fit the transposed ones' space");
     __shared__ float bS[GC * D];
     __shared__ float rho[D], Ep[D];
     __shared__ __attribute__((aligned(16))) char U_raw[L::BYTES];
@@ -825,19 +826,31 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
             f32x16 st;
             zero(st);
             if (!slow) gemm<T, D>(st, A, PD, 32 * ta, B, PD, brow(w));
+            const int b = 32 * tb + (l & 31);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int a = 32 * ta + crow(r), b = 32 * tb + (l & 31);
+                const int a = 32 * ta + crow(r);
                 float x = 0.f;
                 if (a < Ct && b < Ct && (upper ? b >= a : b <= a)) x = slow ? exact(a, b) : st[r];
-                Sc[tr ? b * PS + a : a * PS + b] = fromf<T>(x);
+                st[r] = x;
+                if (!tr) Sc[a * PS + b] = fromf<T>(x);
+            }
+            // transposed: the lane's 4 consecutive rows a of each group in one store
+            if (tr) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    store4(Sc + b * PS + 32 * ta + crow(4 * q), st[4 * q], st[4 * q + 1], st[4 * q + 2],
+                           st[4 * q + 3]);
             }
         } else if (w == 3 && zero_block) {
             const int ta = upper ? 1 : 0, tb = upper ? 0 : 1;
+            const int b = 32 * tb + (l & 31);
+            if (tr) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int a = 32 * ta + crow(r), b = 32 * tb + (l & 31);
-                Sc[tr ? b * PS + a : a * PS + b] = fromf<T>(0.f);
+                for (int q = 0; q < 4; ++q) store4(Sc + b * PS + 32 * ta + crow(4 * q), 0.f, 0.f, 0.f, 0.f);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Sc[(32 * ta + crow(r)) * PS + b] = fromf<T>(0.f);
             }
         }
     };
@@ -862,10 +875,13 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
         for (int hh = 0; hh < L::NHALF; ++hh) {
             const int dv0 = hh * DH;
             if (hh) __syncthreads();
+            // (bf16: P's rows [dv][dk] in a swizzled tile, read transposed;
+            // float32: a transposed copy [dk][dv])
             for_states<T, D, 2, 2, DH>(seg, loc, g, [&](int dv, int dk, const float (*x)[V]) {
+                if constexpr (SW) store_vec(Pk + sw_off<D>(dv - dv0, dk), x[0]);
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    Pk[(dk + j) * PDH + dv - dv0] = fromf<T>(x[0][j]);
+                    if constexpr (!SW) Pk[(dk + j) * PDH + dv - dv0] = fromf<T>(x[0][j]);
                     racc[j] += x[0][j] * x[1][j];
                 }
             }, dv0);
@@ -873,7 +889,12 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
 #pragma unroll
             for (int k = 0; k < TO::PER_WAVE; ++k) {
                 int mi, ni;
-                if (TO::get(k, mi, ni)) gemm<T, DH>(dq[k], dOr + dv0, PD, mi * 32, Pk, PDH, ni * 32);
+                if (!TO::get(k, mi, ni)) continue;
+                if constexpr (SW)
+                    gemm_rc<D, DH>(dq[k], (const bf16 *)dOr + dv0, PD, mi * 32, (const bf16 *)Pk, ni * 32,
+                                   frag_offs<D>(l));
+                else
+                    gemm<T, DH>(dq[k], dOr + dv0, PD, mi * 32, Pk, PDH, ni * 32);
             }
         }
         // the threads sharing a dk group sum in a fixed order (no atomics:
@@ -1039,15 +1060,25 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
             for (int hh = 0; hh < L::NHALF; ++hh) {
                 const int dv0 = hh * DH;
                 if (hh) __syncthreads();
+                // (stored like P in phase A)
                 for_states<T, D, 1, 2, DH>(seg, loc, g, [&](int dvv, int dkk, const float (*x)[V]) {
+                    if constexpr (SW) {
+                        store_vec(RT + sw_off<D>(dvv - dv0, dkk), x[0]);
+                    } else {
 #pragma unroll
-                    for (int j = 0; j < V; ++j) RT[(dkk + j) * PDH + dvv - dv0] = fromf<T>(x[0][j]);
+                        for (int j = 0; j < V; ++j) RT[(dkk + j) * PDH + dvv - dv0] = fromf<T>(x[0][j]);
+                    }
                 }, dv0);
                 __syncthreads();
 #pragma unroll
                 for (int k = 0; k < TO::PER_WAVE; ++k) {
                     int mi, ni;
-                    if (TO::get(k, mi, ni)) gemm<T, DH>(dk[k], Vr + dv0, PD, mi * 32, RT, PDH, ni * 32);
+                    if (!TO::get(k, mi, ni)) continue;
+                    if constexpr (SW)
+                        gemm_rc<D, DH>(dk[k], (const bf16 *)Vr + dv0, PD, mi * 32, (const bf16 *)RT, ni * 32,
+                                       frag_offs<D>(l));
+                    else
+                        gemm<T, DH>(dk[k], Vr + dv0, PD, mi * 32, RT, PDH, ni * 32);
                 }
             }
         }
