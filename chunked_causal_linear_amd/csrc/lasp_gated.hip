@@ -50,8 +50,13 @@ template <int D>
 __device__ __forceinline__ void cumlog_load(LogRows<D> &lr, const float *lg, int Ct) {
     constexpr int RP = LogRows<D>::RP;
     const int c = threadIdx.x % D, r0 = (threadIdx.x / D) * RP;
+    // the thread's offset, opaque to the compiler: the loads' addresses are
+    // then formed here, not hoisted out of the caller's loop into registers
+    int off = r0 * D + c;
+    asm volatile("" : "+v"(off));
+    const float *src = lg + off;
 #pragma unroll
-    for (int j = 0; j < RP; ++j) lr.x[j] = r0 + j < Ct ? lg[(int64_t)(r0 + j) * D + c] : 0.f;
+    for (int j = 0; j < RP; ++j) lr.x[j] = r0 + j < Ct ? src[j * D] : 0.f;
 }
 
 template <int D>
@@ -234,6 +239,24 @@ __device__ __forceinline__ void gemm_rc(f32x16 &acc, const bf16 *A, int pa, int 
         mma(acc, *(const bf16x8_t *)(ap + k), frag_cols_sw<D, false>(Y, fo, y0 + k, n0));
 }
 
+// f *= 2^(b[GC-1] - b[r]) for a thread's raw_store items, which all sit at the
+// same channels c .. c+V-1 (NTHR is a multiple of the pieces per row): the
+// reference row's V values are read once.
+template <int D, int V>
+struct LastRowScale {
+    const float *bS;
+    float bl[V];
+    __device__ LastRowScale(const float *b) : bS(b) {
+        const int c = (threadIdx.x % (D / V)) * V;
+#pragma unroll
+        for (int e = 0; e < V; ++e) bl[e] = bS[(GC - 1) * D + c + e];
+    }
+    __device__ void operator()(int, int r, int c, float *f) const {
+#pragma unroll
+        for (int e = 0; e < V; ++e) f[e] *= ex2(bl[e] - bS[r * D + c + e]);
+    }
+};
+
 struct NoScale {
     template <typename F> __device__ void operator()(int, int, int, F) const {}
 };
@@ -355,7 +378,6 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params 
     __shared__ __attribute__((aligned(16))) T KT_s[SW ? GC * D : D * PT];
     __shared__ __attribute__((aligned(16))) T VT_s[SW ? GC * D : D * PT];
     using TL = Tiles<D / 32, D / 32>;
-    const FragOffs<D> fo = frag_offs<D>(lane_id());
 
     const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
     Seq s;
@@ -399,8 +421,8 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params 
         cumlog_scan<D>(bS, rl);
         __syncthreads();
         if constexpr (SW) {
-            raw_store_sw<D, GC>(rk, (bf16 *)KT_s, Ct, RowId(),
-                                gate_scale<T>(bS, D, [](int) { return GC - 1; }));
+            static_assert(NTHR % (D / 8) == 0, "a thread's items share their channels");
+            raw_store_sw<D, GC>(rk, (bf16 *)KT_s, Ct, RowId(), LastRowScale<D, 8>(bS));
             raw_store_sw<D, GC>(rv, (bf16 *)VT_s, Ct, RowId(), NoScale());
         } else {
             raw_store<T, D, GC, true>(rk, KT_s, PT, Ct, RowId(),
@@ -421,7 +443,8 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[k][r] *= ex2(bS[(GC - 1) * D + mi * 32 + crow(r)]);
                 if constexpr (SW)
-                    gemm_cc<D, GC>(acc[k], (const bf16 *)KT_s, mi * 32, (const bf16 *)VT_s, ni * 32, fo);
+                    gemm_cc<D, GC>(acc[k], (const bf16 *)KT_s, mi * 32, (const bf16 *)VT_s, ni * 32,
+                                   opaque(frag_offs<D>(lane_id())));
                 else
                     gemm<T, GC>(acc[k], KT_s, PT, mi * 32, VT_s, PT, ni * 32);
             }
@@ -1179,10 +1202,14 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
         __syncthreads();
         float off = ex2(bS[(GC - 1) * D + c]) * rho[c] + Ep[c];
         for (int q = part + 1; q < NP; ++q) off += dBs[q * D + c];
-        float *out = p.dLG + rb * D;
+        // (the row offsets formed here, opaque to the compiler, rather than
+        // computed at the kernel start and kept in registers throughout)
+        int o0 = r0 * D + c, nrow = Ct - r0;
+        asm volatile("" : "+v"(o0), "+v"(nrow));
+        float *out = p.dLG + rb * D + o0;
 #pragma unroll
         for (int j = 0; j < RPP; ++j)
-            if (r0 + j < Ct) out[(int64_t)(r0 + j) * D + c] = x[j] + off;
+            if (j < nrow) out[j * D] = x[j] + off;
     }
 }
 
