@@ -1073,6 +1073,7 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
     for (int k = 0; k < TO::PER_WAVE; ++k) zero(dk[k]);
     raw_load(rv, Vg, Ct, RowId());
     raw_load(rk96, Q, Ct, qrow);   // Q rows of the three versions (the K registers are free)
+    raw_load(rkq, K, Ct, RowId());   // K rows for the X term
     {
         T *Vr = U, *RT = U + L::ROWS;   // V rows; R_t as [dk][dv part]
         raw_store<T, D, GC, false>(rv, Vr, PD, Ct, RowId(), NoScale());
@@ -1105,6 +1106,12 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
                 }
             }
         }
+        // K rows where R_t was (the products above have read it)
+        T *Kx = U + L::ROWS;
+        static_assert(2 * L::ROWS <= L::SOFF, "K rows must not reach the scores");
+        __syncthreads();
+        raw_store<T, D, GC, false>(rkq, Kx, PD, Ct, RowId(), NoScale());
+        __syncthreads();
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
@@ -1116,7 +1123,7 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = mi * 32 + crow(r);
-                if (i < Ct) ep += tof(K[(int64_t)i * D + c]) * ex2(bl - bS[i * D + c]) * dk[k][r];
+                if (i < Ct) ep += tof(Kx[i * PD + c]) * ex2(bl - bS[i * D + c]) * dk[k][r];
             }
             ep += __shfl_xor(ep, 32);
             if (l < 32) atomicAdd(&Ep[c], ep);
