@@ -239,6 +239,63 @@ __device__ __forceinline__ void gemm_rc(f32x16 &acc, const bf16 *A, int pa, int 
         mma(acc, *(const bf16x8_t *)(ap + k), frag_cols_sw<D, false>(Y, fo, y0 + k, n0));
 }
 
+// Transposed accumulation (bf16): the same products as gemm / gemm_rc with the
+// MFMA operands swapped, so that acc holds the 32x32 tile transposed (lane =
+// output row, its 16 values = columns crow(r)); store_tile1_t then writes it
+// with 16-byte stores.
+template <int K>
+__device__ __forceinline__ void gemm_t(f32x16 &acc, const bf16 *As, int pa, int m0, const bf16 *Bs,
+                                       int pb, int n0) {
+    const int l = lane_id();
+    const bf16 *ap = As + (m0 + (l & 31)) * pa + (l >> 5) * 8;
+    const bf16 *bp = Bs + (n0 + (l & 31)) * pb + (l >> 5) * 8;
+#pragma unroll
+    for (int k = 0; k < K; k += 16)
+        mma(acc, *(const bf16x8_t *)(bp + k), *(const bf16x8_t *)(ap + k));
+}
+template <int D, int K>
+__device__ __forceinline__ void gemm_rc_t(f32x16 &acc, const bf16 *A, int pa, int m0, const bf16 *Y,
+                                          int n0, const FragOffs<D> &fo) {
+    const int l = lane_id();
+    const bf16 *ap = A + (m0 + (l & 31)) * pa + (l >> 5) * 8;
+#pragma unroll
+    for (int k = 0; k < K; k += 16)
+        mma(acc, frag_cols_sw<D, false>(Y, fo, k, n0), *(const bf16x8_t *)(ap + k));
+}
+// rows m0 + lane%32 (those below nrow), columns n0 .. n0+31 of G (row pitch
+// ld) from a transposed accumulator: after one permlane32 exchange each lane
+// holds 8 consecutive columns of its row twice over.  The buffer range ends
+// at row nrow, so rows past it are dropped by the range check.
+__device__ __forceinline__ void store_tile1_t(const f32x16 &acc, bf16 *G, int ld, int m0, int n0,
+                                              int nrow) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    const int rows = nrow - m0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        G + (int64_t)m0 * ld + n0, 0, __builtin_amdgcn_readfirstlane(rows > 0 ? rows * ld * 2 : 0),
+        0x00020000);
+    const int l = lane_id();
+    const int off = ((l & 31) * ld + (l >> 5) * 8) * 2;
+    unsigned r[8];   // r[2j], r[2j+1]: columns 8j + 4*(lane/32) + [0,4), packed
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const bf16x2_t v = {(__bf16)acc[2 * q], (__bf16)acc[2 * q + 1]};
+        r[q] = __builtin_bit_cast(unsigned, v);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; q += 4) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const auto x = __builtin_amdgcn_permlane32_swap(r[q + e], r[q + 2 + e], false, false);
+            r[q + e] = x[0];
+            r[q + 2 + e] = x[1];
+        }
+    }
+    const u32x4_t v0 = {r[0], r[1], r[2], r[3]}, v1 = {r[4], r[5], r[6], r[7]};
+    __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off + 32, 0, 0);
+}
+
 // f *= 2^(b[GC-1] - b[r]) for a thread's raw_store items, which all sit at the
 // same channels c .. c+V-1 (NTHR is a multiple of the pieces per row): the
 // reference row's V values are read once.
@@ -1024,8 +1081,13 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
 #pragma unroll
                 for (int k = 0; k < TO::PER_WAVE; ++k) {
                     int mi, ni;
-                    if (TO::get(k, mi, ni) && ni * 32 >= dv0 && ni * 32 < dv0 + DH)
-                        gemm<T, D>(dv[k], Kl, PD, mi * 32, Rv, PD, ni * 32 - dv0);
+                    if (TO::get(k, mi, ni) && ni * 32 >= dv0 && ni * 32 < dv0 + DH) {
+                        // (bf16: dV accumulated transposed)
+                        if constexpr (SW)
+                            gemm_t<D>(dv[k], (const bf16 *)Kl, PD, mi * 32, (const bf16 *)Rv, PD, ni * 32 - dv0);
+                        else
+                            gemm<T, D>(dv[k], Kl, PD, mi * 32, Rv, PD, ni * 32 - dv0);
+                    }
                 }
             }
         }
@@ -1058,11 +1120,13 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
             if (!TO::get(k, mi, ni)) continue;
-            if constexpr (SW)
-                gemm_rc<D, GC>(dv[k], (const bf16 *)Sc, PS, mi * 32, (const bf16 *)OT, ni * 32, frag_offs<D>(l));
-            else
+            if constexpr (SW) {
+                gemm_rc_t<D, GC>(dv[k], (const bf16 *)Sc, PS, mi * 32, (const bf16 *)OT, ni * 32, frag_offs<D>(l));
+                store_tile1_t(dv[k], (bf16 *)p.dV + rb * D, D, mi * 32, ni * 32, Ct);
+            } else {
                 gemm<T, GC>(dv[k], Sc, PS, mi * 32, OT, PS, ni * 32);
-            store_rows(dv[k], (T *)p.dV + rb * D, D, mi * 32, ni * 32, Ct);
+                store_rows(dv[k], (T *)p.dV + rb * D, D, mi * 32, ni * 32, Ct);
+            }
         }
         __syncthreads();
     }
