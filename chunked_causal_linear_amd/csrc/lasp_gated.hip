@@ -622,8 +622,13 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_out(Params p)
 #pragma unroll
             for (int k = 0; k < TO::PER_WAVE; ++k) {
                 int mi, ni;
-                if (TO::get(k, mi, ni) && ni * 32 >= dv0 && ni * 32 < dv0 + DH)
-                    gemm<T, D>(o[k], Qh, PD, mi * 32, Ph, PD, ni * 32 - dv0);
+                if (TO::get(k, mi, ni) && ni * 32 >= dv0 && ni * 32 < dv0 + DH) {
+                    // (bf16: O accumulated transposed)
+                    if constexpr (sizeof(T) == 2)
+                        gemm_t<D>(o[k], (const bf16 *)Qh, PD, mi * 32, (const bf16 *)Ph, PD, ni * 32 - dv0);
+                    else
+                        gemm<T, D>(o[k], Qh, PD, mi * 32, Ph, PD, ni * 32 - dv0);
+                }
             }
         }
     }
@@ -679,11 +684,13 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_out(Params p)
     for (int k = 0; k < TO::PER_WAVE; ++k) {
         int mi, ni;
         if (TO::get(k, mi, ni)) {
-            if constexpr (SW)
-                gemm_rc<D, GC>(o[k], (const bf16 *)Sc, PS, mi * 32, (const bf16 *)VT, ni * 32, fo);
-            else
+            if constexpr (SW) {
+                gemm_rc_t<D, GC>(o[k], (const bf16 *)Sc, PS, mi * 32, (const bf16 *)VT, ni * 32, fo);
+                store_tile1_t(o[k], (bf16 *)O, D, mi * 32, ni * 32, Ct);
+            } else {
                 gemm<T, GC>(o[k], Sc, PS, mi * 32, VT, PS, ni * 32);
-            store_rows(o[k], O, D, mi * 32, ni * 32, Ct);
+                store_rows(o[k], O, D, mi * 32, ni * 32, Ct);
+            }
         }
     }
 }
