@@ -18,10 +18,13 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Text of the last HIP error seen by a call on this thread (for
+// lasp_status_string); the only state the library keeps between calls.
 thread_local std::string g_hip_error;
 
 // Sizes derived from the shape.  G (chunks per segment) is a pure function of
-// the shape so that lasp_fwd and lasp_bwd agree on the state-cache layout.
+// the shape, or the caller's explicit segment_chunks, so that lasp_fwd and
+// lasp_bwd agree on the state-cache layout whenever they get the same arguments.
 struct Plan {
     int D, C, G, H, nseq, T_fixed, S_fixed, n_chunks_ub, n_segs_ub;
     bool varlen;
@@ -35,8 +38,10 @@ struct Plan {
     size_t cache_b;      // state cache = [Lc][Pseg][Pfin][Gc][Gs]
 };
 
-// gated: the per-channel gated form (chunk 64).
-int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false) {
+// gated: the per-channel gated form (chunk 64).  seg_chunks: 0, or the
+// number of chunks per segment to use instead of the library's choice.
+int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false,
+              int seg_chunks = 0) {
     if (!s) return LASP_EINVAL;
     if (s->B <= 0 || s->H <= 0 || s->N <= 0 || s->d <= 0 || s->chunk <= 0 || s->nseq < 0)
         return LASP_EINVAL;
@@ -45,6 +50,7 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false) 
     if (s->d != 32 && s->d != 64 && s->d != 128) return LASP_EUNSUPPORTED;
     if (s->chunk != 64 && s->chunk != 128 && s->chunk != 256) return LASP_EUNSUPPORTED;
     if (gated && s->chunk != 64) return LASP_EUNSUPPORTED;
+    if (seg_chunks < 0 || seg_chunks > (1 << 20)) return LASP_EINVAL;
     pl.D = s->d;
     pl.C = s->chunk;
     pl.H = s->H;
@@ -81,12 +87,7 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false) 
             }
         }
     }
-    // Test hook: LASP_SEGMENT_CHUNKS overrides G (must be the same for the
-    // forward and backward calls that share a state cache).
-    if (const char *e = getenv("LASP_SEGMENT_CHUNKS")) {
-        const long v = strtol(e, nullptr, 10);
-        if (v >= 1 && v <= (1 << 20)) pl.G = (int)v;
-    }
+    if (seg_chunks > 0) pl.G = seg_chunks;
     int64_t segs_ub;
     if (pl.varlen) {
         segs_ub = chunks_ub / pl.G + s->nseq;
@@ -209,20 +210,46 @@ size_t lasp_bwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype, int w
     return make_plan(shape, dtype, pl) == LASP_OK ? bwd_ws(pl, with_state_cache != 0) : 0;
 }
 
-// With LASP_DEBUG=1 in the environment, a packed batch's cu_seqlens is copied
-// to the host (after the work already on the stream) and checked: cu[0] = 0,
-// non-decreasing, cu[nseq] = N.  Otherwise its contents are trusted.
-static int debug_check_cu(const lasp_shape *shape, const int32_t *cu, hipStream_t stream) {
+int lasp_query_sizes(const lasp_shape *shape, lasp_dtype dtype, int form, int segment_chunks,
+                     lasp_sizes *out) {
+    if (!out || (form != 0 && form != 1)) return LASP_EINVAL;
+    Plan pl;
+    const int rc = make_plan(shape, dtype, pl, form == 1, segment_chunks);
+    if (rc != LASP_OK) return rc;
+    out->state_cache = pl.cache_b;
+    out->fwd_workspace[0] = fwd_ws(pl, false);
+    out->fwd_workspace[1] = fwd_ws(pl, true);
+    out->bwd_workspace[0] = bwd_ws(pl, false);
+    out->bwd_workspace[1] = bwd_ws(pl, true);
+    return LASP_OK;
+}
+
+// With LASP_DEBUG=1 in the environment, the contents of a packed batch's
+// cu_seqlens and of the decay array are copied to the host (after the work
+// already on the stream) and checked: cu[0] = 0, non-decreasing, cu[nseq] = N;
+// every lambda in [0, 1].  Otherwise their contents are trusted.
+static int debug_check(const lasp_shape *shape, const int32_t *cu, const float *decay,
+                       hipStream_t stream) {
     const char *e = getenv("LASP_DEBUG");
-    if (!cu || !e || strcmp(e, "1") != 0) return LASP_OK;
-    std::vector<int32_t> h((size_t)shape->nseq + 1);
-    hipError_t err = hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t),
-                                    hipMemcpyDeviceToHost, stream);
+    if ((!cu && !decay) || !e || strcmp(e, "1") != 0) return LASP_OK;
+    std::vector<int32_t> h(cu ? (size_t)shape->nseq + 1 : 0);
+    std::vector<float> lam(decay ? (size_t)shape->H : 0);
+    hipError_t err = hipSuccess;
+    if (cu)
+        err = hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                             stream);
+    if (err == hipSuccess && decay)
+        err = hipMemcpyAsync(lam.data(), decay, lam.size() * sizeof(float), hipMemcpyDeviceToHost,
+                             stream);
     if (err == hipSuccess) err = hipStreamSynchronize(stream);
     if (err != hipSuccess) return hip_status(err);
-    if (h[0] != 0 || h.back() != shape->N) return LASP_EINVAL;
-    for (size_t i = 1; i < h.size(); ++i)
-        if (h[i] < h[i - 1]) return LASP_EINVAL;
+    if (cu) {
+        if (h[0] != 0 || h.back() != shape->N) return LASP_EINVAL;
+        for (size_t i = 1; i < h.size(); ++i)
+            if (h[i] < h[i - 1]) return LASP_EINVAL;
+    }
+    for (float x : lam)
+        if (!(x >= 0.f && x <= 1.f)) return LASP_EINVAL;   // NaN fails too
     return LASP_OK;
 }
 
@@ -236,9 +263,9 @@ int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
                const void *V, const float *decay, const float *log_g,
                const int32_t *cu_seqlens, const float *M_in, void *O, float *M_out,
                void *state_cache, void *workspace, size_t workspace_bytes, void *stream,
-               void **events, Mode mode) {
+               void **events, int seg_chunks, Mode mode) {
     Plan pl;
-    int rc = make_plan(shape, dtype, pl, mode == GATED);
+    int rc = make_plan(shape, dtype, pl, mode == GATED, seg_chunks);
     if (rc != LASP_OK) return rc;
     if (mode == BIDIR && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
     if (!Q || !K || !V || !O || (mode == GATED && !log_g)) return LASP_EINVAL;
@@ -261,7 +288,7 @@ int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     const Range outs[] = {{O, tens}, {M_out, st}, {state_cache, cache ? pl.cache_b : 0},
                           {workspace, need}};
     if (any_overlap(outs, 4, ins, 7)) return LASP_EINVAL;
-    if ((rc = debug_check_cu(shape, cu_seqlens, (hipStream_t)stream)) != LASP_OK) return rc;
+    if ((rc = debug_check(shape, cu_seqlens, decay, (hipStream_t)stream)) != LASP_OK) return rc;
 
     lasp::Params p;
     fill_common(p, shape, pl, cu_seqlens, decay);
@@ -283,7 +310,8 @@ int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     p.Lc = pl.local_b ? c : nullptr;
     p.Pseg = (float *)(c + pl.local_b);
     p.Pfin = pl.fin_b ? (float *)(c + pl.local_b + pl.seg_b) : nullptr;
-    if (mode == BIDIR) return hip_status(lasp::launch_fwd_bidir(p, true, (hipStream_t)stream));
+    if (mode == BIDIR)
+        return hip_status(lasp::launch_fwd_bidir(p, true, (hipStream_t)stream, (hipEvent_t *)events));
     if (mode == GATED) {
         p.LG = log_g;
         p.Gc = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b);
@@ -302,25 +330,37 @@ extern "C" {
 int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
                 const void *V, const float *decay, const int32_t *cu_seqlens, const float *M_in,
                 void *O, float *M_out, void *state_cache, void *workspace,
-                size_t workspace_bytes, void *stream, void **events) {
+                size_t workspace_bytes, void *stream, void **events, int segment_chunks) {
     return fwd_common(shape, dtype, Q, K, V, decay, nullptr, cu_seqlens, M_in, O, M_out,
-                      state_cache, workspace, workspace_bytes, stream, events, CAUSAL);
+                      state_cache, workspace, workspace_bytes, stream, events, segment_chunks,
+                      CAUSAL);
+}
+
+int lasp_fwd_bidir_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                      const void *V, const int32_t *cu_seqlens, const float *M_in, void *O,
+                      float *M_out, void *state_cache, void *workspace, size_t workspace_bytes,
+                      void *stream, void **events, int segment_chunks) {
+    return fwd_common(shape, dtype, Q, K, V, nullptr, nullptr, cu_seqlens, M_in, O, M_out,
+                      state_cache, workspace, workspace_bytes, stream, events, segment_chunks,
+                      BIDIR);
 }
 
 int lasp_fwd_bidir(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
                    const void *V, const int32_t *cu_seqlens, const float *M_in, void *O,
                    float *M_out, void *state_cache, void *workspace, size_t workspace_bytes,
                    void *stream) {
-    return fwd_common(shape, dtype, Q, K, V, nullptr, nullptr, cu_seqlens, M_in, O, M_out,
-                      state_cache, workspace, workspace_bytes, stream, nullptr, BIDIR);
+    return lasp_fwd_bidir_ex(shape, dtype, Q, K, V, cu_seqlens, M_in, O, M_out, state_cache,
+                             workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 int lasp_fwd_gated_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
                       const void *V, const float *log_g, const int32_t *cu_seqlens,
                       const float *M_in, void *O, float *M_out, void *state_cache,
-                      void *workspace, size_t workspace_bytes, void *stream, void **events) {
+                      void *workspace, size_t workspace_bytes, void *stream, void **events,
+                      int segment_chunks) {
     return fwd_common(shape, dtype, Q, K, V, nullptr, log_g, cu_seqlens, M_in, O, M_out,
-                      state_cache, workspace, workspace_bytes, stream, events, GATED);
+                      state_cache, workspace, workspace_bytes, stream, events, segment_chunks,
+                      GATED);
 }
 
 int lasp_fwd_gated(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
@@ -328,7 +368,7 @@ int lasp_fwd_gated(const lasp_shape *shape, lasp_dtype dtype, const void *Q, con
                    const float *M_in, void *O, float *M_out, void *state_cache, void *workspace,
                    size_t workspace_bytes, void *stream) {
     return lasp_fwd_gated_ex(shape, dtype, Q, K, V, log_g, cu_seqlens, M_in, O, M_out,
-                             state_cache, workspace, workspace_bytes, stream, nullptr);
+                             state_cache, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
@@ -336,7 +376,7 @@ int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const voi
              void *O, float *M_out, void *state_cache, void *workspace, size_t workspace_bytes,
              void *stream) {
     return lasp_fwd_ex(shape, dtype, Q, K, V, decay, cu_seqlens, M_in, O, M_out, state_cache,
-                       workspace, workspace_bytes, stream, nullptr);
+                       workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 }  // extern "C"
@@ -348,9 +388,9 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
                const int32_t *cu_seqlens, const float *M_in, const float *dM_out,
                const void *state_cache, void *dQ, void *dK, void *dV, float *dlog_g,
                float *dM_in, void *workspace, size_t workspace_bytes, void *stream,
-               void **events, Mode mode) {
+               void **events, int seg_chunks, Mode mode) {
     Plan pl;
-    int rc = make_plan(shape, dtype, pl, mode == GATED);
+    int rc = make_plan(shape, dtype, pl, mode == GATED, seg_chunks);
     if (rc != LASP_OK) return rc;
     if (mode == BIDIR && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
     if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return LASP_EINVAL;
@@ -376,7 +416,7 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     const Range outs[] = {{dQ, tens}, {dK, tens}, {dV, tens}, {dM_in, st}, {workspace, need},
                           {dlog_g, mode == GATED ? gates : 0}};
     if (any_overlap(outs, 6, ins, 10)) return LASP_EINVAL;
-    if ((rc = debug_check_cu(shape, cu_seqlens, (hipStream_t)stream)) != LASP_OK) return rc;
+    if ((rc = debug_check(shape, cu_seqlens, decay, (hipStream_t)stream)) != LASP_OK) return rc;
 
     lasp::Params p;
     fill_common(p, shape, pl, cu_seqlens, decay);
@@ -425,7 +465,7 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
                                         : lasp::launch_fwd(p, bf, false, hs));
         if (rc != LASP_OK) return rc;
     }
-    if (mode == BIDIR) return hip_status(lasp::launch_bwd_bidir(p, hs));
+    if (mode == BIDIR) return hip_status(lasp::launch_bwd_bidir(p, hs, (hipEvent_t *)events));
     if (mode == GATED)
         return hip_status(lasp::launch_bwd_gated(p, dtype == LASP_BF16, hs, (hipEvent_t *)events));
     return hip_status(lasp::launch_bwd(p, dtype == LASP_BF16, hs, (hipEvent_t *)events));
@@ -439,19 +479,28 @@ int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const 
                 const void *V, const void *dO, const float *decay, const int32_t *cu_seqlens,
                 const float *M_in, const float *dM_out, const void *state_cache, void *dQ,
                 void *dK, void *dV, float *dM_in, void *workspace, size_t workspace_bytes,
-                void *stream, void **events) {
+                void *stream, void **events, int segment_chunks) {
     return bwd_common(shape, dtype, Q, K, V, dO, decay, nullptr, cu_seqlens, M_in, dM_out,
                       state_cache, dQ, dK, dV, nullptr, dM_in, workspace, workspace_bytes, stream,
-                      events, CAUSAL);
+                      events, segment_chunks, CAUSAL);
+}
+
+int lasp_bwd_bidir_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                      const void *V, const void *dO, const int32_t *cu_seqlens,
+                      const float *M_in, const float *dM_out, const void *state_cache, void *dQ,
+                      void *dK, void *dV, float *dM_in, void *workspace, size_t workspace_bytes,
+                      void *stream, void **events, int segment_chunks) {
+    return bwd_common(shape, dtype, Q, K, V, dO, nullptr, nullptr, cu_seqlens, M_in, dM_out,
+                      state_cache, dQ, dK, dV, nullptr, dM_in, workspace, workspace_bytes, stream,
+                      events, segment_chunks, BIDIR);
 }
 
 int lasp_bwd_bidir(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
                    const void *V, const void *dO, const int32_t *cu_seqlens, const float *M_in,
                    const float *dM_out, const void *state_cache, void *dQ, void *dK, void *dV,
                    float *dM_in, void *workspace, size_t workspace_bytes, void *stream) {
-    return bwd_common(shape, dtype, Q, K, V, dO, nullptr, nullptr, cu_seqlens, M_in, dM_out,
-                      state_cache, dQ, dK, dV, nullptr, dM_in, workspace, workspace_bytes, stream,
-                      nullptr, BIDIR);
+    return lasp_bwd_bidir_ex(shape, dtype, Q, K, V, dO, cu_seqlens, M_in, dM_out, state_cache,
+                             dQ, dK, dV, dM_in, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 int lasp_bwd_gated_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
@@ -459,10 +508,10 @@ int lasp_bwd_gated_ex(const lasp_shape *shape, lasp_dtype dtype, const void *Q, 
                       const int32_t *cu_seqlens, const float *M_in, const float *dM_out,
                       const void *state_cache, void *dQ, void *dK, void *dV, float *dlog_g,
                       float *dM_in, void *workspace, size_t workspace_bytes, void *stream,
-                      void **events) {
+                      void **events, int segment_chunks) {
     return bwd_common(shape, dtype, Q, K, V, dO, nullptr, log_g, cu_seqlens, M_in, dM_out,
                       state_cache, dQ, dK, dV, dlog_g, dM_in, workspace, workspace_bytes, stream,
-                      events, GATED);
+                      events, segment_chunks, GATED);
 }
 
 int lasp_bwd_gated(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
@@ -472,7 +521,7 @@ int lasp_bwd_gated(const lasp_shape *shape, lasp_dtype dtype, const void *Q, con
                    size_t workspace_bytes, void *stream) {
     return lasp_bwd_gated_ex(shape, dtype, Q, K, V, log_g, dO, cu_seqlens, M_in, dM_out,
                              state_cache, dQ, dK, dV, dlog_g, dM_in, workspace, workspace_bytes,
-                             stream, nullptr);
+                             stream, nullptr, 0);
 }
 
 int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
@@ -480,7 +529,7 @@ int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const voi
              const float *M_in, const float *dM_out, const void *state_cache, void *dQ, void *dK,
              void *dV, float *dM_in, void *workspace, size_t workspace_bytes, void *stream) {
     return lasp_bwd_ex(shape, dtype, Q, K, V, dO, decay, cu_seqlens, M_in, dM_out, state_cache,
-                       dQ, dK, dV, dM_in, workspace, workspace_bytes, stream, nullptr);
+                       dQ, dK, dV, dM_in, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 const char *lasp_status_string(int status) {
@@ -496,6 +545,6 @@ const char *lasp_status_string(int status) {
     return "unknown status";
 }
 
-int lasp_version(void) { return 100; }
+int lasp_version(void) { return 200; }
 
 }  // extern "C"

@@ -45,6 +45,26 @@ __device__ __forceinline__ void mma(f32x16 &c, const f32x4 &a, const f32x4 &b) {
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], b[3], c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Host side: launch a kernel that takes Params by value and return that
+// launch's own status (no hipGetLastError: an error the caller left pending is
+// neither reported nor cleared here).
+// ---------------------------------------------------------------------------
+template <typename Kern>
+inline hipError_t launch_k(Kern kernel, dim3 grid, dim3 block, hipStream_t st, const Params &p) {
+    void *args[] = {const_cast<Params *>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, st);
+}
+// Record event i of ev (if any) on st.
+inline hipError_t rec_event(hipEvent_t *ev, int i, hipStream_t st) {
+    return ev ? hipEventRecord(ev[i], st) : hipSuccess;
+}
+#define LASP_TRY(x)                                  \
+    do {                                             \
+        const hipError_t lasp_e_ = (x);              \
+        if (lasp_e_ != hipSuccess) return lasp_e_;   \
+    } while (0)
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // Row (within the 32x32 tile) of accumulator element r for this lane.

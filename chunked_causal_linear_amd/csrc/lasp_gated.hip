@@ -1295,37 +1295,32 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
 // Launchers
 // ---------------------------------------------------------------------------
 static inline int round8g(int n) { return (n + 7) & ~7; }
-static inline void grec(hipEvent_t *ev, int i, hipStream_t st) {
-    if (ev) (void)hipEventRecord(ev[i], st);
-}
 
 template <typename T, int D>
 static hipError_t gfwd(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
-    if (p.varlen) launch_setup(p, st);
-    grec(ev, 0, st);
-    hipLaunchKernelGGL((k_gfwd_local<T, D>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
-    grec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_gfwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
-    grec(ev, 2, st);
+    if (p.varlen) LASP_TRY(launch_setup(p, st));
+    LASP_TRY(rec_event(ev, 0, st));
+    LASP_TRY(launch_k(k_gfwd_local<T, D>, dim3(p.n_segs_ub * p.H), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 1, st));
+    LASP_TRY(launch_k(k_gfwd_segscan<D>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 2, st));
     if (with_output)
-        hipLaunchKernelGGL((k_gfwd_out<T, D>), dim3(round8g(p.n_chunks_ub * p.H)), dim3(NTHR), 0, st, p);
-    grec(ev, 3, st);
-    return hipGetLastError();
+        LASP_TRY(launch_k(k_gfwd_out<T, D>, dim3(round8g(p.n_chunks_ub * p.H)), dim3(NTHR), st, p));
+    return rec_event(ev, 3, st);
 }
 
 template <typename T, int D>
 static hipError_t gbwd(const Params &p, hipStream_t st, hipEvent_t *ev) {
-    if (p.varlen) launch_setup(p, st);
-    grec(ev, 0, st);
-    hipLaunchKernelGGL((k_gbwd_local<T, D>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
-    grec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_gbwd_segscan<D>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
-    grec(ev, 2, st);
-    hipLaunchKernelGGL((k_gbwd_grads<T, D>), dim3(round8g(p.n_chunks_ub * p.H)), dim3(NTHR), 0, st, p);
-    grec(ev, 3, st);
-    return hipGetLastError();
+    if (p.varlen) LASP_TRY(launch_setup(p, st));
+    LASP_TRY(rec_event(ev, 0, st));
+    LASP_TRY(launch_k(k_gbwd_local<T, D>, dim3(p.n_segs_ub * p.H), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 1, st));
+    LASP_TRY(launch_k(k_gbwd_segscan<D>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 2, st));
+    LASP_TRY(launch_k(k_gbwd_grads<T, D>, dim3(round8g(p.n_chunks_ub * p.H)), dim3(NTHR), st, p));
+    return rec_event(ev, 3, st);
 }
 
 hipError_t launch_fwd_gated(const Params &p, bool bf, bool with_output, hipStream_t st, hipEvent_t *ev) {

@@ -66,9 +66,11 @@ hipError_t launch_fwd_gated(const Params &p, bool bf16, bool with_output, hipStr
 hipError_t launch_bwd_gated(const Params &p, bool bf16, hipStream_t stream, hipEvent_t *ev = nullptr);
 
 // Packed-batch tables (chunk_prefix, seg_prefix) on the stream.
-void launch_setup(const Params &p, hipStream_t stream);
+hipError_t launch_setup(const Params &p, hipStream_t stream);
 
-hipError_t launch_fwd_bidir(const Params &p, bool with_output, hipStream_t stream);
-hipError_t launch_bwd_bidir(const Params &p, hipStream_t stream);
+// ev as for launch_fwd / launch_bwd (totals, scan, row-block products).
+hipError_t launch_fwd_bidir(const Params &p, bool with_output, hipStream_t stream,
+                            hipEvent_t *ev = nullptr);
+hipError_t launch_bwd_bidir(const Params &p, hipStream_t stream, hipEvent_t *ev = nullptr);
 
 }  // namespace lasp

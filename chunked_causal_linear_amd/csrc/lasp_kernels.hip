@@ -1507,114 +1507,101 @@ template <typename T, int D> struct Block {
     static constexpr int BT = (sizeof(T) == 4 && D == 128) ? 32 : 64;
 };
 
-void launch_setup(const Params &p, hipStream_t st) {
-    hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
-}
-
-static inline void rec(hipEvent_t *ev, int i, hipStream_t st) {
-    if (ev) (void)hipEventRecord(ev[i], st);
+hipError_t launch_setup(const Params &p, hipStream_t st) {
+    return launch_k(k_setup, dim3(1), dim3(NTHR), st, p);
 }
 
 template <typename T, int D>
 static hipError_t fwd_impl(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
     constexpr int BT = Block<T, D>::BT;
-    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
-    rec(ev, 0, st);
-    hipLaunchKernelGGL((k_fwd_local<T, D, BT>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
-    rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_fwd_segscan<D, T>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
-    rec(ev, 2, st);
+    if (p.varlen) LASP_TRY(launch_setup(p, st));
+    LASP_TRY(rec_event(ev, 0, st));
+    LASP_TRY(launch_k(k_fwd_local<T, D, BT>, dim3(p.n_segs_ub * p.H), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 1, st));
+    LASP_TRY(launch_k(k_fwd_segscan<D, T>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 2, st));
     if (with_output)
-        hipLaunchKernelGGL((k_fwd_out<T, D, BT>), dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), 0,
-                           st, p);
-    rec(ev, 3, st);
-    return hipGetLastError();
+        LASP_TRY(launch_k(k_fwd_out<T, D, BT>, dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), st, p));
+    return rec_event(ev, 3, st);
 }
 
 template <typename T, int D>
 static hipError_t bwd_impl(const Params &p, hipStream_t st, hipEvent_t *ev) {
     constexpr int BT = Block<T, D>::BT;
-    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
-    rec(ev, 0, st);
-    hipLaunchKernelGGL((k_bwd_local<T, D, BT>), dim3(p.n_segs_ub * p.H), dim3(NTHR), 0, st, p);
-    rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_bwd_segscan<D, T>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
-    rec(ev, 2, st);
-    hipLaunchKernelGGL((k_bwd_grads<T, D, BT>), dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), 0, st,
-                       p);
-    rec(ev, 3, st);
-    return hipGetLastError();
+    if (p.varlen) LASP_TRY(launch_setup(p, st));
+    LASP_TRY(rec_event(ev, 0, st));
+    LASP_TRY(launch_k(k_bwd_local<T, D, BT>, dim3(p.n_segs_ub * p.H), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 1, st));
+    LASP_TRY(launch_k(k_bwd_segscan<D, T>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 2, st));
+    LASP_TRY(launch_k(k_bwd_grads<T, D, BT>, dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), st, p));
+    return rec_event(ev, 3, st);
 }
 
 // bf16: segment totals, segment scan, sweep.
 template <int D, int C, int KIND>
-static void sweep_launch(const Params &p, hipStream_t st) {
+static hipError_t sweep_launch(const Params &p, hipStream_t st) {
     const int roles = KIND == SWEEP_GRADS ? 3 : 1;
     const dim3 grid(round8(p.n_segs_ub * p.H * roles)), block(SweepCfg<C>::NT);
     if (p.decay) {
         if constexpr (KIND == SWEEP_GRADS) {
-            hipLaunchKernelGGL((k_sweep_bf16<D, C, SWEEP_DVDK, true>),
-                               dim3(round8(p.n_segs_ub * p.H * 2)), block, 0, st, p);
-            hipLaunchKernelGGL((k_sweep_bf16<D, C, SWEEP_DQ, true>), dim3(round8(p.n_segs_ub * p.H)),
-                               block, 0, st, p);
+            LASP_TRY(launch_k(k_sweep_bf16<D, C, SWEEP_DVDK, true>, dim3(round8(p.n_segs_ub * p.H * 2)),
+                              block, st, p));
+            return launch_k(k_sweep_bf16<D, C, SWEEP_DQ, true>, dim3(round8(p.n_segs_ub * p.H)), block,
+                            st, p);
         } else {
-            hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND, true>), grid, block, 0, st, p);
+            return launch_k(k_sweep_bf16<D, C, KIND, true>, grid, block, st, p);
         }
-    } else {
-        hipLaunchKernelGGL((k_sweep_bf16<D, C, KIND, false>), grid, block, 0, st, p);
     }
+    return launch_k(k_sweep_bf16<D, C, KIND, false>, grid, block, st, p);
 }
 
 template <int D, int KIND>
-static void segtot_launch(const Params &p, hipStream_t st) {
+static hipError_t segtot_launch(const Params &p, hipStream_t st) {
     const dim3 grid(round8(p.n_segs_ub * p.H)), block(SegTotCfg<D>::NT);
-    if (p.decay)
-        hipLaunchKernelGGL((k_segtot_bf16<D, KIND, true>), grid, block, 0, st, p);
-    else
-        hipLaunchKernelGGL((k_segtot_bf16<D, KIND, false>), grid, block, 0, st, p);
+    if (p.decay) return launch_k(k_segtot_bf16<D, KIND, true>, grid, block, st, p);
+    return launch_k(k_segtot_bf16<D, KIND, false>, grid, block, st, p);
 }
 
 template <int D, int KIND>
-static void sweep_dispatch(const Params &p, hipStream_t st) {
+static hipError_t sweep_dispatch(const Params &p, hipStream_t st) {
     switch (p.C) {
-    case 64: sweep_launch<D, 64, KIND>(p, st); break;
-    case 128: sweep_launch<D, 128, KIND>(p, st); break;
-    default: sweep_launch<D, 256, KIND>(p, st); break;
+    case 64: return sweep_launch<D, 64, KIND>(p, st);
+    case 128: return sweep_launch<D, 128, KIND>(p, st);
+    default: return sweep_launch<D, 256, KIND>(p, st);
     }
 }
 
 template <int D>
 static hipError_t fwd_bf16(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
-    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
-    rec(ev, 0, st);
-    segtot_launch<D, TOT_F>(p, st);
-    rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_fwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
-    rec(ev, 2, st);
-    if (with_output) sweep_dispatch<D, SWEEP_OUT>(p, st);
-    rec(ev, 3, st);
-    return hipGetLastError();
+    if (p.varlen) LASP_TRY(launch_setup(p, st));
+    LASP_TRY(rec_event(ev, 0, st));
+    LASP_TRY((segtot_launch<D, TOT_F>(p, st)));
+    LASP_TRY(rec_event(ev, 1, st));
+    LASP_TRY(launch_k(k_fwd_segscan<D, float>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 2, st));
+    if (with_output) LASP_TRY((sweep_dispatch<D, SWEEP_OUT>(p, st)));
+    return rec_event(ev, 3, st);
 }
 
 template <int D>
 static hipError_t bwd_bf16(const Params &p, hipStream_t st, hipEvent_t *ev) {
-    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
-    rec(ev, 0, st);
-    segtot_launch<D, TOT_B>(p, st);
-    rec(ev, 1, st);
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_bwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
-    rec(ev, 2, st);
-    sweep_dispatch<D, SWEEP_GRADS>(p, st);
-    rec(ev, 3, st);
-    return hipGetLastError();
+    if (p.varlen) LASP_TRY(launch_setup(p, st));
+    LASP_TRY(rec_event(ev, 0, st));
+    LASP_TRY((segtot_launch<D, TOT_B>(p, st)));
+    LASP_TRY(rec_event(ev, 1, st));
+    LASP_TRY(launch_k(k_bwd_segscan<D, float>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 2, st));
+    LASP_TRY((sweep_dispatch<D, SWEEP_GRADS>(p, st)));
+    return rec_event(ev, 3, st);
 }
 
 template <int D, int KIND>
-static void rowmat_launch(const Params &p0, hipStream_t st) {
+static hipError_t rowmat_launch(const Params &p0, hipStream_t st) {
     const int prods = KIND == RM_BWD ? 3 : 1;
     // about 1024 workgroups (four per CU), parts of at least 8 tiles
     Params p = p0;
@@ -1622,45 +1609,51 @@ static void rowmat_launch(const Params &p0, hipStream_t st) {
     const int by_wg = (int)((1024 + wg - 1) / wg);
     const int by_rows = (p.G * p.C / 32) / 8;
     p.parts = by_wg < 1 ? 1 : (by_wg < by_rows ? by_wg : (by_rows < 1 ? 1 : by_rows));
-    hipLaunchKernelGGL((k_rowmat_bf16<D, KIND>), dim3(round8(wg * p.parts)), dim3(64 * RM_NW), 0, st, p);
+    return launch_k(k_rowmat_bf16<D, KIND>, dim3(round8(wg * p.parts)), dim3(64 * RM_NW), st, p);
 }
 
 template <int D>
-static hipError_t fwd_bidir(const Params &p, bool with_output, hipStream_t st) {
-    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
-    segtot_launch<D, TOT_F>(p, st);
+static hipError_t fwd_bidir(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_fwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
-    if (with_output) rowmat_launch<D, RM_FWD>(p, st);
-    return hipGetLastError();
+    if (p.varlen) LASP_TRY(launch_setup(p, st));
+    LASP_TRY(rec_event(ev, 0, st));
+    LASP_TRY((segtot_launch<D, TOT_F>(p, st)));
+    LASP_TRY(rec_event(ev, 1, st));
+    LASP_TRY(launch_k(k_fwd_segscan<D, float>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 2, st));
+    if (with_output) LASP_TRY((rowmat_launch<D, RM_FWD>(p, st)));
+    return rec_event(ev, 3, st);
 }
 
 template <int D>
-static hipError_t bwd_bidir(const Params &p, hipStream_t st) {
-    if (p.varlen) hipLaunchKernelGGL(k_setup, dim3(1), dim3(NTHR), 0, st, p);
-    segtot_launch<D, TOT_B>(p, st);
+static hipError_t bwd_bidir(const Params &p, hipStream_t st, hipEvent_t *ev) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
-    hipLaunchKernelGGL((k_bwd_segscan<D, float>), dim3(p.nseq * p.H * NB), dim3(NTHR), 0, st, p);
-    rowmat_launch<D, RM_BWD>(p, st);
-    return hipGetLastError();
+    if (p.varlen) LASP_TRY(launch_setup(p, st));
+    LASP_TRY(rec_event(ev, 0, st));
+    LASP_TRY((segtot_launch<D, TOT_B>(p, st)));
+    LASP_TRY(rec_event(ev, 1, st));
+    LASP_TRY(launch_k(k_bwd_segscan<D, float>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
+    LASP_TRY(rec_event(ev, 2, st));
+    LASP_TRY((rowmat_launch<D, RM_BWD>(p, st)));
+    return rec_event(ev, 3, st);
 }
 
-hipError_t launch_fwd_bidir(const Params &p, bool with_output, hipStream_t st) {
+hipError_t launch_fwd_bidir(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
     if (p.decay || !p.Pfin) return hipErrorInvalidValue;
     switch (p.D) {
-    case 32: return fwd_bidir<32>(p, with_output, st);
-    case 64: return fwd_bidir<64>(p, with_output, st);
-    case 128: return fwd_bidir<128>(p, with_output, st);
+    case 32: return fwd_bidir<32>(p, with_output, st, ev);
+    case 64: return fwd_bidir<64>(p, with_output, st, ev);
+    case 128: return fwd_bidir<128>(p, with_output, st, ev);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_bidir(const Params &p, hipStream_t st) {
+hipError_t launch_bwd_bidir(const Params &p, hipStream_t st, hipEvent_t *ev) {
     if (p.decay || !p.Pfin || !p.Rfin) return hipErrorInvalidValue;
     switch (p.D) {
-    case 32: return bwd_bidir<32>(p, st);
-    case 64: return bwd_bidir<64>(p, st);
-    case 128: return bwd_bidir<128>(p, st);
+    case 32: return bwd_bidir<32>(p, st, ev);
+    case 64: return bwd_bidir<64>(p, st, ev);
+    case 128: return bwd_bidir<128>(p, st, ev);
     }
     return hipErrorInvalidValue;
 }

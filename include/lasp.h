@@ -26,7 +26,8 @@
  *   M_in, M_out, dM_out, dM_in : [S, H, d, d] float32, row = key feature,
  *                                column = value feature; S = B, or nseq for a
  *                                packed batch
- *   decay                      : float32 [H] (lambda per head), or NULL (= 1)
+ *   decay                      : float32 [H] (lambda per head, in [0, 1]: the
+ *                                decay of LASP Sec. 3.2), or NULL (= 1)
  *   cu_seqlens                 : int32 [nseq + 1] for a packed batch (B = 1,
  *                                N = total tokens, sequence i = tokens
  *                                [cu[i], cu[i+1]) of every head), else NULL
@@ -34,19 +35,24 @@
  * be empty; N need not be a multiple of the chunk.
  *
  * Ownership and threading: the caller owns every buffer; the library never
- * allocates or frees memory and keeps no mutable global state.  Calls are
- * asynchronous on the given HIP stream (hipStream_t passed as void*, NULL = the
- * default stream): buffers must stay alive until the stream reaches them.
- * Outputs are fully overwritten; outputs must not overlap inputs.
+ * allocates or frees memory.  Between calls it keeps only a per-thread copy of
+ * the text of the last HIP error it saw (for lasp_status_string), so calls on
+ * different threads and streams are independent.  Calls are asynchronous on the
+ * given HIP stream (hipStream_t passed as void*, NULL = the default stream):
+ * buffers must stay alive until the stream reaches them.  Outputs are fully
+ * overwritten; outputs must not overlap inputs.
  *
  * Errors: every argument is checked before anything is enqueued; on error
- * nothing runs and a lasp_status code is returned.  cu_seqlens contents are
- * trusted (monotone, cu[0] = 0, cu[nseq] = N) unless the environment has
- * LASP_DEBUG=1: then each call copies cu_seqlens to the host (synchronizing
- * the stream) and returns LASP_EINVAL if it is malformed.  Even unchecked, a
- * malformed cu_seqlens cannot make the kernels access memory outside the
- * [B, H, N, d] tensors (sequence bounds are clamped to [0, N]); the results
- * are then meaningless.  NaN/Inf inputs propagate.
+ * nothing runs and a lasp_status code is returned.  A launch that fails returns
+ * LASP_EHIP with that launch's own error (an error left pending by the caller's
+ * earlier HIP calls is neither reported nor cleared).  The contents of
+ * cu_seqlens (monotone, cu[0] = 0, cu[nseq] = N) and of decay (every lambda in
+ * [0, 1]) are trusted unless the environment has LASP_DEBUG=1: then each call
+ * copies them to the host (synchronizing the stream) and returns LASP_EINVAL
+ * if they are malformed.  Even unchecked, a malformed cu_seqlens cannot make
+ * the kernels access memory outside the [B, H, N, d] tensors (sequence bounds
+ * are clamped to [0, N]); the results are then meaningless, as they are for a
+ * lambda outside [0, 1].  NaN/Inf inputs propagate.
  * Numbers: bf16 inputs are multiplied on bf16 MFMA with float32 accumulation;
  * states are float32 in HBM between kernels and rounded to bf16 where they are
  * MFMA operands.  float32 inputs use float32 MFMA throughout.
@@ -93,6 +99,23 @@ size_t lasp_fwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype,
 size_t lasp_bwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype,
                                 int with_state_cache);
 
+/* All sizes at once, for an explicit segment length.  Work is split into
+ * segments of G consecutive chunks (one workgroup sweeps a segment; states are
+ * scanned across segments: the one-device form of LASP-2's prefix sum over the
+ * gathered chunk states).  segment_chunks = 0 gives the library's choice of G,
+ * a pure function of the shape and dtype, which the plain entry points and the
+ * queries above use; segment_chunks > 0 forces G (a tuning and testing knob of
+ * the _ex entry points).  form: 0 = causal and unmasked entry points, 1 = gated.
+ * Returns LASP_OK and fills *out, or the status lasp_fwd would return for the
+ * shape (LASP_EINVAL also for a negative segment_chunks or a NULL out). */
+typedef struct {
+    size_t state_cache;        /* bytes of the state cache */
+    size_t fwd_workspace[2];   /* forward workspace: [0] without, [1] with a state cache */
+    size_t bwd_workspace[2];   /* backward workspace: [0] without, [1] with a state cache */
+} lasp_sizes;
+int lasp_query_sizes(const lasp_shape *shape, lasp_dtype dtype, int form, int segment_chunks,
+                     lasp_sizes *out);
+
 /* Forward pass (LASP Alg. 2 on one device; LASP-2 prefix sums of M_t).
  *   Q, K, V     inputs (required)
  *   decay       device float32 [H] or NULL
@@ -126,21 +149,30 @@ int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype,
              void *dQ, void *dK, void *dV, float *dM_in,
              void *workspace, size_t workspace_bytes, void *stream);
 
-/* As lasp_fwd / lasp_bwd, plus per-kernel timing: events is NULL or an array of
- * 4 hipEvent_t (created by the caller) that are recorded on the stream before
- * the local chunk-state kernel, before the cross-segment scan, before the last
- * kernel (output, resp. gradients) and after it.  Nothing else changes. */
+/* As lasp_fwd / lasp_bwd, plus two knobs:
+ *   events          NULL, or an array of 4 hipEvent_t (created by the caller)
+ *                   recorded on the stream before the segment-total kernel,
+ *                   before the cross-segment scan, before the last kernel
+ *                   (output, resp. gradients) and after it (per-kernel timing);
+ *   segment_chunks  0 (the library's segment length, as lasp_fwd / lasp_bwd),
+ *                   or G > 0 chunks per segment.  The state cache and the
+ *                   workspace must then be sized by lasp_query_sizes with the
+ *                   same G, and a lasp_bwd_ex that reads a state cache must get
+ *                   the G of the lasp_fwd_ex that wrote it.
+ * Nothing else changes. */
 int lasp_fwd_ex(const lasp_shape *shape, lasp_dtype dtype,
                 const void *Q, const void *K, const void *V,
                 const float *decay, const int32_t *cu_seqlens, const float *M_in,
                 void *O, float *M_out, void *state_cache,
-                void *workspace, size_t workspace_bytes, void *stream, void **events);
+                void *workspace, size_t workspace_bytes, void *stream, void **events,
+                int segment_chunks);
 int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype,
                 const void *Q, const void *K, const void *V, const void *dO,
                 const float *decay, const int32_t *cu_seqlens, const float *M_in,
                 const float *dM_out, const void *state_cache,
                 void *dQ, void *dK, void *dV, float *dM_in,
-                void *workspace, size_t workspace_bytes, void *stream, void **events);
+                void *workspace, size_t workspace_bytes, void *stream, void **events,
+                int segment_chunks);
 
 /* Unmasked (bidirectional) form: LASP Eq. 3 without Norm, every token attends
  * to every token of its sequence, no decay; with sequence parallelism each
@@ -170,6 +202,21 @@ int lasp_bwd_bidir(const lasp_shape *shape, lasp_dtype dtype,
                    const float *dM_out, const void *state_cache,
                    void *dQ, void *dK, void *dV, float *dM_in,
                    void *workspace, size_t workspace_bytes, void *stream);
+/* The unmasked form with the knobs of lasp_fwd_ex / lasp_bwd_ex (the events
+ * bracket the same three kernels: totals, scan, row-block products). */
+int lasp_fwd_bidir_ex(const lasp_shape *shape, lasp_dtype dtype,
+                      const void *Q, const void *K, const void *V,
+                      const int32_t *cu_seqlens, const float *M_in,
+                      void *O, float *M_out, void *state_cache,
+                      void *workspace, size_t workspace_bytes, void *stream, void **events,
+                      int segment_chunks);
+int lasp_bwd_bidir_ex(const lasp_shape *shape, lasp_dtype dtype,
+                      const void *Q, const void *K, const void *V, const void *dO,
+                      const int32_t *cu_seqlens, const float *M_in,
+                      const float *dM_out, const void *state_cache,
+                      void *dQ, void *dK, void *dV, float *dM_in,
+                      void *workspace, size_t workspace_bytes, void *stream, void **events,
+                      int segment_chunks);
 
 /* Gated form: a per-token, per-key-channel gate g_p in (0, 1]^d (LASP
  * Appendix A.4: the general recurrence of Eq. 24 with the GLA / GateLoop row
@@ -192,9 +239,10 @@ int lasp_bwd_bidir(const lasp_shape *shape, lasp_dtype dtype,
  * 2^(b_m - b_i) (b: running log2 of the gates; m: the first row of a 32-row
  * query tile), each at most 1 off the diagonal tiles; a diagonal tile whose
  * gates fall by more than 2^80 is summed pair by pair in float32 instead.
- * Sizes come from the lasp_gated_* queries (the gated state cache also holds
- * per-chunk gate products); buffers, pointers, alignment, errors and the events
- * of the _ex variants are as for lasp_fwd / lasp_bwd (no decay argument). */
+ * Sizes come from the lasp_gated_* queries or lasp_query_sizes with form 1 (the
+ * gated state cache also holds per-chunk gate products); buffers, pointers,
+ * alignment, errors and the knobs of the _ex variants are as for lasp_fwd /
+ * lasp_bwd (no decay argument). */
 size_t lasp_gated_state_cache_bytes(const lasp_shape *shape, lasp_dtype dtype);
 size_t lasp_gated_fwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype,
                                       int with_state_cache);
@@ -215,13 +263,15 @@ int lasp_fwd_gated_ex(const lasp_shape *shape, lasp_dtype dtype,
                       const void *Q, const void *K, const void *V, const float *log_g,
                       const int32_t *cu_seqlens, const float *M_in,
                       void *O, float *M_out, void *state_cache,
-                      void *workspace, size_t workspace_bytes, void *stream, void **events);
+                      void *workspace, size_t workspace_bytes, void *stream, void **events,
+                      int segment_chunks);
 int lasp_bwd_gated_ex(const lasp_shape *shape, lasp_dtype dtype,
                       const void *Q, const void *K, const void *V, const float *log_g,
                       const void *dO, const int32_t *cu_seqlens, const float *M_in,
                       const float *dM_out, const void *state_cache,
                       void *dQ, void *dK, void *dV, float *dlog_g, float *dM_in,
-                      void *workspace, size_t workspace_bytes, void *stream, void **events);
+                      void *workspace, size_t workspace_bytes, void *stream, void **events,
+                      int segment_chunks);
 
 /* Human-readable text for a status code (for LASP_EHIP: the last HIP error of
  * the calling thread). */

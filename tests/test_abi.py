@@ -212,3 +212,94 @@ def test_gated_rejects_bad_arguments(L):
     # the gated state cache also holds per-chunk states and gate products
     assert (L.lasp_gated_state_cache_bytes(ctypes.byref(s), 1)
             > L.lasp_state_cache_bytes(ctypes.byref(s), 1))
+
+
+SHAPES = [Shape(1, 32, 131072, 128, 256, 0), Shape(4, 16, 8192, 128, 256, 0),
+          Shape(2, 16, 32768, 128, 256, 0), Shape(1, 32, 69632, 64, 128, 8),
+          Shape(1, 2, 256, 32, 64, 0), Shape(3, 5, 1000, 64, 128, 0), Shape(1, 4, 777, 32, 64, 5)]
+
+
+def all_sizes(L, s, dt, form):
+    if form == 1:
+        return (L.lasp_gated_state_cache_bytes(ctypes.byref(s), dt),
+                L.lasp_gated_fwd_workspace_bytes(ctypes.byref(s), dt, 0),
+                L.lasp_gated_fwd_workspace_bytes(ctypes.byref(s), dt, 1),
+                L.lasp_gated_bwd_workspace_bytes(ctypes.byref(s), dt, 0),
+                L.lasp_gated_bwd_workspace_bytes(ctypes.byref(s), dt, 1))
+    return (L.lasp_state_cache_bytes(ctypes.byref(s), dt),
+            L.lasp_fwd_workspace_bytes(ctypes.byref(s), dt, 0),
+            L.lasp_fwd_workspace_bytes(ctypes.byref(s), dt, 1),
+            L.lasp_bwd_workspace_bytes(ctypes.byref(s), dt, 0),
+            L.lasp_bwd_workspace_bytes(ctypes.byref(s), dt, 1))
+
+
+def test_sizes_do_not_depend_on_the_environment(L, monkeypatch):
+    """The state-cache layout (and so every size) is a pure function of the
+    call's arguments: environment variables, including the names a segment
+    override or a debug switch might use, change nothing."""
+    cases = [(s, dt, form) for s in SHAPES for dt in (0, 1) for form in (0, 1)
+             if form == 0 or s.chunk == 64]
+    before = [all_sizes(L, *c) for c in cases]
+    for k, v in (("LASP_SEGMENT_CHUNKS", "3"), ("LASP_DEBUG", "1"), ("LASP_G", "7"),
+                 ("HIP_VISIBLE_DEVICES", "0")):
+        monkeypatch.setenv(k, v)
+    after = [all_sizes(L, *c) for c in cases]
+    assert before == after
+
+
+def test_query_sizes_agrees_with_the_plain_queries(L):
+    """lasp_query_sizes with segment_chunks = 0 reports what the plain size
+    queries report (the forward and backward use one plan), and an explicit
+    segment length changes the layout consistently for both directions."""
+    for s in SHAPES:
+        for dt in (0, 1):
+            for form in ((0, 1) if s.chunk == 64 else (0,)):
+                q = cca.query_sizes(s, dt, form, 0)
+                assert (q.state_cache, q.fwd_workspace[0], q.fwd_workspace[1], q.bwd_workspace[0],
+                        q.bwd_workspace[1]) == all_sizes(L, s, dt, form)
+                for G in (1, 2, 3, 16):
+                    g = cca.query_sizes(s, dt, form, G)
+                    # without a cache buffer, each workspace holds the whole cache
+                    assert g.fwd_workspace[0] - g.fwd_workspace[1] == g.state_cache
+                    assert g.bwd_workspace[0] - g.bwd_workspace[1] >= g.state_cache
+    out = cca.Sizes()
+    assert L.lasp_query_sizes(ctypes.byref(SHAPES[0]), 1, 0, -1, ctypes.byref(out)) == EINVAL
+    assert L.lasp_query_sizes(ctypes.byref(SHAPES[0]), 1, 2, 0, ctypes.byref(out)) == EINVAL
+    assert L.lasp_query_sizes(ctypes.byref(SHAPES[0]), 1, 0, 0, None) == EINVAL
+    assert L.lasp_query_sizes(ctypes.byref(Shape(1, 1, 8, 48, 64, 0)), 1, 0, 0,
+                              ctypes.byref(out)) == EUNSUP
+
+
+def test_binding_rejects_bad_out_and_host_tensors():
+    """The binding validates a preallocated O / dQ, dK, dV like every other
+    tensor (so a wrong buffer never reaches the kernels), and refuses host
+    tensors outright."""
+    import torch
+    q = torch.zeros(1, 2, 64, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        cca.fwd(q, q, q, 64)                                  # host tensors
+    meta = torch.device("meta")
+    qm = torch.empty(1, 2, 64, 32, dtype=torch.bfloat16, device=meta)
+    with pytest.raises(ValueError):
+        cca.fwd(qm, qm, qm, 64)
+
+
+def _no_gpu_here():
+    if os.path.exists("/dev/kfd"):
+        return False
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu_here(), reason="needs a host without a GPU (fake pointers)")
+def test_validated_call_without_a_gpu_reports_ehip(L):
+    """A call whose arguments pass every check reaches the first launch; on a
+    host without a GPU that launch fails and the call returns LASP_EHIP with
+    the HIP error text, without raising or crashing."""
+    s = Shape(1, 2, 300, 64, 64, 0)
+    assert fwd_call(L, s) == EHIP
+    msg = L.lasp_status_string(EHIP)
+    assert isinstance(msg, bytes) and len(msg) > 0

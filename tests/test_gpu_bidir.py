@@ -22,13 +22,14 @@ def gpu():
     yield
 
 
-def run_bidir(inp, use_cache=True):
+def run_bidir(inp, use_cache=True, seg=0):
     sh = inp["shape"]
     Q, K, V = dev(inp["Q"]), dev(inp["K"]), dev(inp["V"])
     cu, M_in = dev(inp["cu_seqlens"]), dev(inp["M_in"])
-    O, M_out, cache = cca.fwd_bidir(Q, K, V, sh["chunk"], cu, M_in, want_state_cache=use_cache)
+    O, M_out, cache = cca.fwd_bidir(Q, K, V, sh["chunk"], cu, M_in, want_state_cache=use_cache,
+                                    segment_chunks=seg)
     dQ, dK, dV, dM_in = cca.bwd_bidir(Q, K, V, dev(inp["dO"]), sh["chunk"], cu, M_in,
-                                      dev(inp["dM_out"]), cache)
+                                      dev(inp["dM_out"]), cache, segment_chunks=seg)
     torch.cuda.synchronize()
     return dict(O=O, M_out=M_out, dQ=dQ, dK=dK, dV=dV, dM_in=dM_in)
 
@@ -61,14 +62,13 @@ def test_bidir_small(w):
     check(w.name, run_bidir(inp), oracle_bidir(inp), TOL["bf16"])
 
 
-@pytest.mark.parametrize("G", ["1", "3"])
-def test_bidir_segment_sizes(G, monkeypatch):
-    monkeypatch.setenv("LASP_SEGMENT_CHUNKS", G)
+@pytest.mark.parametrize("G", [1, 3])
+def test_bidir_segment_sizes(G):
     w = small("bidir bf16 d64 C64 many chunks", "bf16", B=2, H=2, N=64 * 11 + 17, d=64, chunk=64,
               seed=55, m_in_scale=0.1, dm_out_scale=0.1)
     say("case: bidir segment chunks", G)
     inp = make_inputs(w)
-    check("bidir G=" + G, run_bidir(inp), oracle_bidir(inp), TOL["bf16"])
+    check("bidir G=%d" % G, run_bidir(inp, seg=G), oracle_bidir(inp), TOL["bf16"])
 
 
 def test_bidir_recompute_equals_cache():

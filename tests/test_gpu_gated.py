@@ -26,13 +26,14 @@ def gpu():
     yield
 
 
-def run_gated(inp, use_cache=True):
+def run_gated(inp, use_cache=True, seg=0):
     sh = inp["shape"]
     Q, K, V, LG = dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(inp["log_g"])
     cu, M_in = dev(inp["cu_seqlens"]), dev(inp["M_in"])
-    O, M_out, cache = cca.fwd_gated(Q, K, V, LG, sh["chunk"], cu, M_in, want_state_cache=use_cache)
+    O, M_out, cache = cca.fwd_gated(Q, K, V, LG, sh["chunk"], cu, M_in, want_state_cache=use_cache,
+                                    segment_chunks=seg)
     dQ, dK, dV, dLG, dM_in = cca.bwd_gated(Q, K, V, LG, dev(inp["dO"]), sh["chunk"], cu, M_in,
-                                           dev(inp["dM_out"]), cache)
+                                           dev(inp["dM_out"]), cache, segment_chunks=seg)
     torch.cuda.synchronize()
     return dict(O=O, M_out=M_out, dQ=dQ, dK=dK, dV=dV, dLG=dLG, dM_in=dM_in)
 
@@ -76,25 +77,23 @@ def test_gated_small(w):
     check(w.name, run_gated(inp), oracle_gated(inp), TOL[w.dtype])
 
 
-@pytest.mark.parametrize("G", ["1", "3"])
-def test_gated_segment_sizes(G, monkeypatch):
-    monkeypatch.setenv("LASP_SEGMENT_CHUNKS", G)
+@pytest.mark.parametrize("G", [1, 3])
+def test_gated_segment_sizes(G):
     w = small("gated fp32 d32 many chunks", "fp32", B=2, H=2, N=64 * 11 + 17, d=32, seed=70,
               gates="mixed", m_in_scale=0.1, dm_out_scale=0.1)
     say("case: gated segment chunks", G)
     inp = make_inputs(w)
-    check("gated G=" + G, run_gated(inp), oracle_gated(inp), TOL["fp32"])
+    check("gated G=%d" % G, run_gated(inp, seg=G), oracle_gated(inp), TOL["fp32"])
 
 
-def test_gated_medium_multi_segment(monkeypatch):
+def test_gated_medium_multi_segment():
     """bf16 B2 H4 N4096 d128 (64 chunks per sequence) in segments of 8 chunks,
     every element against the oracle's recurrence."""
-    monkeypatch.setenv("LASP_SEGMENT_CHUNKS", "8")
     w = small("gated bf16 d128 B2 H4 N4096 G8", "bf16", B=2, H=4, N=4096, d=128, seed=76,
               gates="mixed", m_in_scale=0.05, dm_out_scale=0.05)
     say("case:", w.name)
     inp = make_inputs(w)
-    check(w.name, run_gated(inp), oracle_gated(inp), TOL["bf16"])
+    check(w.name, run_gated(inp, seg=8), oracle_gated(inp), TOL["bf16"])
 
 
 def test_gated_recompute_equals_cache():

@@ -48,16 +48,16 @@ def rel(a, ref):
     return float(np.abs(a - ref).max() / (den if den > 0 else 1.0))
 
 
-def run_gpu(inp, backward=True, use_cache=True):
+def run_gpu(inp, backward=True, use_cache=True, seg=0):
     sh = inp["shape"]
     Q, K, V = dev(inp["Q"]), dev(inp["K"]), dev(inp["V"])
     decay, cu, M_in = dev(inp["decay"]), dev(inp["cu_seqlens"]), dev(inp["M_in"])
     O, M_out, cache = cca.fwd(Q, K, V, sh["chunk"], decay, cu, M_in,
-                              want_state_cache=backward and use_cache)
+                              want_state_cache=backward and use_cache, segment_chunks=seg)
     out = {"O": O, "M_out": M_out}
     if backward:
         dQ, dK, dV, dM_in = cca.bwd(Q, K, V, dev(inp["dO"]), sh["chunk"], decay, cu, M_in,
-                                    dev(inp["dM_out"]), cache)
+                                    dev(inp["dM_out"]), cache, segment_chunks=seg)
         out.update(dQ=dQ, dK=dK, dV=dV, dM_in=dM_in)
     torch.cuda.synchronize()
     return out
@@ -124,29 +124,47 @@ def test_small_parity(w):
     check(w.name, out, ref, TOL[w.dtype])
 
 
+# Every (dtype, d, chunk, decay) the library accepts: each selects its own kernel
+# instantiation (the bf16 sweep and segment-total kernels are compiled per d,
+# chunk and decay variant; the float32 kernels per d).  Four chunks and a
+# ragged tail in segments of two chunks, so that every kernel walks more than
+# one chunk and the scans cross segments; M_in and dM_out on.
+MATRIX = [(dt, d, C, dec) for dt in ("bf16", "fp32") for d in (32, 64, 128)
+          for C in (64, 128, 256) for dec in ("none", "lightning")]
+
+
+@pytest.mark.parametrize("dt,d,C,dec", MATRIX,
+                         ids=["%s-d%d-C%d-%s" % m for m in MATRIX])
+def test_every_accepted_configuration(dt, d, C, dec):
+    w = small("%s d%d C%d %s" % (dt, d, C, dec), dt, B=1, H=2, N=3 * C + C // 2 + 7, d=d,
+              chunk=C, seed=1000 + d + C + (dt == "fp32") * 7 + (dec != "none") * 3, decay=dec,
+              m_in_scale=0.1, dm_out_scale=0.1)
+    say("case:", w.name)
+    inp = make_inputs(w)
+    check(w.name, run_gpu(inp, seg=2), oracle_full(inp), TOL[dt])
+
+
 @pytest.mark.parametrize("decay", ["lightning", "none"])
-@pytest.mark.parametrize("G", ["1", "3", "16"])
-def test_segment_sizes(G, decay, monkeypatch):
+@pytest.mark.parametrize("G", [1, 3, 16])
+def test_segment_sizes(G, decay):
     """The two-level scan gives the same result for any segment length (without
     decay the dQ walk starts from the next segment's state or the final one)."""
-    monkeypatch.setenv("LASP_SEGMENT_CHUNKS", G)
     w = small("bf16 d64 C64 many chunks", "bf16", B=2, H=2, N=64 * 11 + 17, d=64, chunk=64,
               seed=20, decay=decay, m_in_scale=0.1, dm_out_scale=0.1)
     say("case: segment chunks", G, decay)
     inp = make_inputs(w)
-    check("G=" + G, run_gpu(inp), oracle_full(inp), TOL["bf16"])
+    check("G=%d" % G, run_gpu(inp, seg=G), oracle_full(inp), TOL["bf16"])
 
 
-def test_mixed_decay_heads(monkeypatch):
+def test_mixed_decay_heads():
     """Heads with and without decay in one launch (their dQ walks run in
     opposite directions), packed sequences spanning several segments."""
-    monkeypatch.setenv("LASP_SEGMENT_CHUNKS", "3")
     w = small("bf16 packed d128 C128", "bf16", H=4, d=128, chunk=128, seed=25,
               lengths=[700, 129, 1, 2000], m_in_scale=0.1, dm_out_scale=0.1)
     inp = make_inputs(w)
     inp["decay"] = torch.tensor([1.0, 0.995, 1.0, 0.0], dtype=torch.float32)
     say("case: mixed decay heads")
-    check("mixed decay", run_gpu(inp), oracle_full(inp), TOL["bf16"])
+    check("mixed decay", run_gpu(inp, seg=3), oracle_full(inp), TOL["bf16"])
 
 
 def test_zero_decay():
@@ -294,6 +312,94 @@ def test_debug_rejects_bad_cu_seqlens(monkeypatch):
     monkeypatch.setenv("LASP_DEBUG", "1")
     cca.fwd(Q, K, V, 64, None, good)
     torch.cuda.synchronize()
+
+
+def test_debug_rejects_bad_decay(monkeypatch):
+    """LASP_DEBUG=1: a decay outside [0, 1] (or NaN) is rejected before anything runs."""
+    w = small("decay check", "bf16", B=1, H=2, N=100, d=64, chunk=64, seed=26)
+    inp = make_inputs(w)
+    Q, K, V = dev(inp["Q"]), dev(inp["K"]), dev(inp["V"])
+    monkeypatch.setenv("LASP_DEBUG", "1")
+    for bad in ([0.5, -0.1], [1.5, 0.9], [float("nan"), 0.9]):
+        with pytest.raises(cca.LaspError) as e:
+            cca.fwd(Q, K, V, 64, torch.tensor(bad, dtype=torch.float32, device="cuda"))
+        assert e.value.status == 1
+    cca.fwd(Q, K, V, 64, torch.tensor([0.0, 1.0], dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_ragged_outputs_stay_in_bounds():
+    """O, dQ, dK, dV placed inside larger buffers whose guard bands hold a
+    pattern: a packed batch of ragged sequences (tails of 1 to 127 rows in the
+    last chunk of a sequence, and of the whole tensor) leaves every guard
+    element untouched and still matches the oracle."""
+    w = small("bf16 packed d128 C128 ragged guards", "bf16", H=3, d=128, chunk=128, seed=27,
+              lengths=[1, 127, 129, 300, 0, 77], decay="lightning", m_in_scale=0.1,
+              dm_out_scale=0.1)
+    inp = make_inputs(w)
+    Q, K, V, dO = (dev(inp[k]) for k in ("Q", "K", "V", "dO"))
+    decay, cu, M_in, dM_out = (dev(inp[k]) for k in ("decay", "cu_seqlens", "M_in", "dM_out"))
+    n, G = Q.numel(), 4096
+    pattern = torch.tensor([0x7FA5], dtype=torch.int16).view(torch.bfloat16)   # a NaN payload
+    bufs = [pattern.to("cuda").repeat(n + 2 * G) for _ in range(4)]
+    views = [b[G:G + n].view(Q.shape) for b in bufs]
+    say("case: guard bands")
+    O, M_out, cache = cca.fwd(Q, K, V, 128, decay, cu, M_in, out=views[0])
+    dQ, dK, dV, dM_in = cca.bwd(Q, K, V, dO, 128, decay, cu, M_in, dM_out, cache,
+                                out=views[1:])
+    torch.cuda.synchronize()
+    for name, b in zip(("O", "dQ", "dK", "dV"), bufs):
+        raw = b.view(torch.int16)
+        assert bool((raw[:G] == 0x7FA5).all()) and bool((raw[G + n:] == 0x7FA5).all()), name
+    check("guarded", dict(O=O, M_out=M_out, dQ=dQ, dK=dK, dV=dV, dM_in=dM_in), oracle_full(inp),
+          TOL["bf16"])
+
+
+@pytest.mark.parametrize("cfg,shards", [(3, 4), (4, 4)])
+def test_split_invariance_full_size(cfg, shards):
+    """One device's share run whole, and again as `shards` consecutive pieces of
+    the sequence run one after another: the forward hands each piece's M_out to
+    the next piece as M_in, the backward hands each piece's dM_in to the piece
+    before it as dM_out (the state exchange of LASP Alg. 2 and 3 between
+    neighbouring ranks, done in sequence on one GPU).  Outputs and the end
+    states agree with the whole run."""
+    import dataclasses
+    w = dataclasses.replace(CONFIGS[cfg], m_in_scale=0.01, dm_out_scale=0.01, seed=40 + cfg)
+    say("case: split invariance, config", cfg, "in", shards, "shards")
+    inp = make_inputs(w, device="cuda")
+    Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
+    decay, M_in, dM_out, C = inp["decay"], inp["M_in"], inp["dM_out"], w.chunk
+    whole = run_gpu(inp)
+    N = Q.shape[2]
+    cuts = [N * r // shards for r in range(shards + 1)]
+    piece = lambda x, r: x[:, :, cuts[r]:cuts[r + 1]].contiguous()
+    m, m_ins, caches, outs = M_in, [], [], {k: [] for k in ("O", "dQ", "dK", "dV")}
+    for r in range(shards):
+        m_ins.append(m)
+        O, m, cache = cca.fwd(piece(Q, r), piece(K, r), piece(V, r), C, decay, None, m)
+        outs["O"].append(O)
+        caches.append(cache)
+    M_out = m
+    dm = dM_out
+    grads = [None] * shards
+    for r in reversed(range(shards)):
+        dQ, dK, dV, dm = cca.bwd(piece(Q, r), piece(K, r), piece(V, r), piece(dO, r), C, decay,
+                                 None, m_ins[r], dm, caches[r])
+        grads[r] = (dQ, dK, dV)
+    for r in range(shards):
+        for k, t in zip(("dQ", "dK", "dV"), grads[r]):
+            outs[k].append(t)
+    torch.cuda.synchronize()
+    errs = {}
+    for k in ("O", "dQ", "dK", "dV"):
+        a, b = torch.cat(outs[k], dim=2).float(), whole[k].float()
+        errs[k] = float((a - b).abs().max() / b.abs().max())
+    for k, a in (("M_out", M_out), ("dM_in", dm)):
+        b = whole[k]
+        errs[k] = float((a - b).abs().max() / b.abs().max())
+    say("split", cfg, " ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {k: e for k, e in errs.items() if not e <= TOL["bf16"]}
+    assert not bad, bad
 
 
 def test_config3_with_dm_out():
