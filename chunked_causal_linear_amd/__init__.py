@@ -18,7 +18,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "bwd", "fwd_bidir", "bwd_bidir", "fwd_gated", "bwd_gated", "LaspError", "lib",
+__all__ = ["fwd", "fwd_noalloc", "bwd", "fwd_bidir", "bwd_bidir", "fwd_gated", "bwd_gated", "LaspError", "lib",
            "Shape", "Sizes", "LASP_FP32", "LASP_BF16", "query_sizes", "state_cache_bytes",
            "fwd_workspace_bytes", "bwd_workspace_bytes", "gated_state_cache_bytes",
            "gated_fwd_workspace_bytes", "gated_bwd_workspace_bytes"]
@@ -76,6 +76,8 @@ def lib():
         for n in ("fwd", "bwd", "fwd_bidir", "bwd_bidir", "fwd_gated", "bwd_gated"):
             base = getattr(L, "lasp_" + n)
             sig(getattr(L, "lasp_%s_ex" % n), base.argtypes + [P, I])
+        sig(L.lasp_fwd_noalloc, [SP, I] + [P] * 9 + [P])
+        sig(L.lasp_noalloc_scratch_bytes, [], S)
         sig(L.lasp_status_string, [I], ctypes.c_char_p)
         sig(L.lasp_version, [])
         _lib = L
@@ -239,6 +241,24 @@ def fwd(Q, K, V, chunk, decay=None, cu_seqlens=None, M_in=None, *, want_m_out=Tr
     _run("lasp_fwd", c, [_ptr(Q), _ptr(K), _ptr(V), _ptr(decay), _ptr(cu_seqlens), _ptr(M_in),
                          _ptr(O), _ptr(M_out), _ptr(cache)], ws, need, events)
     return O, M_out, cache
+
+
+def fwd_noalloc(Q, K, V, chunk, decay=None, cu_seqlens=None, M_in=None, *, out, M_out=None,
+                state_cache=None):
+    """Allocation-free forward (lasp_fwd_noalloc): the caller passes every
+    output buffer (O; optionally M_out and a state cache of the call's
+    state-cache size) and the library takes its scratch from a static device
+    array, so the call itself allocates nothing.  Returns (O, M_out, state_cache)."""
+    import torch
+    c = _Call(Q, chunk, cu_seqlens, [("Q", Q), ("K", K), ("V", V), ("out", out)],
+              [("M_in", M_in), ("M_out", M_out)], FORM_CAUSAL, 0, decay=decay)
+    c.check_cache(state_cache)
+    rc = lib().lasp_fwd_noalloc(ctypes.byref(c.S), c.dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(decay),
+                                _ptr(cu_seqlens), _ptr(M_in), _ptr(out), _ptr(M_out),
+                                _ptr(state_cache), _stream(c.dev))
+    if rc != 0:
+        raise LaspError(rc, "lasp_fwd_noalloc")
+    return out, M_out, state_cache
 
 
 def bwd(Q, K, V, dO, chunk, decay=None, cu_seqlens=None, M_in=None, dM_out=None,

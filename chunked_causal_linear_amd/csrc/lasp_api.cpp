@@ -379,6 +379,24 @@ int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const voi
                        workspace, workspace_bytes, stream, nullptr, 0);
 }
 
+size_t lasp_noalloc_scratch_bytes(void) { return lasp::kStaticScratchBytes; }
+
+int lasp_fwd_noalloc(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                     const void *V, const float *decay, const int32_t *cu_seqlens,
+                     const float *M_in, void *O, float *M_out, void *state_cache, void *stream) {
+    Plan pl;
+    const int rc = make_plan(shape, dtype, pl);
+    if (rc != LASP_OK) return rc;
+    // the scratch takes what lasp_fwd's workspace would hold; checked before
+    // the device is touched
+    if (fwd_ws(pl, state_cache != nullptr) > lasp::kStaticScratchBytes) return LASP_ESCRATCH;
+    void *ws = nullptr;
+    const int st = hip_status(lasp::static_scratch((hipStream_t)stream, &ws));
+    if (st != LASP_OK) return st;
+    return fwd_common(shape, dtype, Q, K, V, decay, nullptr, cu_seqlens, M_in, O, M_out,
+                      state_cache, ws, lasp::kStaticScratchBytes, stream, nullptr, 0, CAUSAL);
+}
+
 }  // extern "C"
 
 namespace {
@@ -541,6 +559,9 @@ const char *lasp_status_string(int status) {
                "gated form: chunk 64; unmasked form: bf16)";
     case LASP_EWORKSPACE: return "workspace too small";
     case LASP_EHIP: return g_hip_error.empty() ? "HIP error" : g_hip_error.c_str();
+    case LASP_ESCRATCH:
+        return "the call needs more scratch than lasp_fwd_noalloc's static array holds "
+               "(lasp_noalloc_scratch_bytes); use lasp_fwd with a workspace";
     }
     return "unknown status";
 }

@@ -65,6 +65,11 @@ hipError_t launch_fwd_gated(const Params &p, bool bf16, bool with_output, hipStr
                             hipEvent_t *ev = nullptr);
 hipError_t launch_bwd_gated(const Params &p, bool bf16, hipStream_t stream, hipEvent_t *ev = nullptr);
 
+// Bytes of the static scratch array used by lasp_fwd_noalloc, and the device
+// address of the copy on the stream's GPU (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t static_scratch(hipStream_t stream, void **ptr);
+
 // Packed-batch tables (chunk_prefix, seg_prefix) on the stream.
 hipError_t launch_setup(const Params &p, hipStream_t stream);
 

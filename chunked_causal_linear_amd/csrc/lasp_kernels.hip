@@ -28,6 +28,8 @@
 // staged in LDS so that the contraction index is contiguous for every operand.
 #include "lasp_device.h"
 
+#include <mutex>
+
 namespace lasp {
 
 // ---------------------------------------------------------------------------
@@ -1506,6 +1508,39 @@ static inline int round8(int n) { return (n + 7) & ~7; }
 template <typename T, int D> struct Block {
     static constexpr int BT = (sizeof(T) == 4 && D == 128) ? 32 : 64;
 };
+
+// ---------------------------------------------------------------------------
+// Scratch memory of the allocation-free forward entry point: a file-scope
+// device array, one copy on every GPU the library runs on (held until the
+// process ends).  Host code never passes `scratch` itself to a kernel (its
+// host-side name is not a device address): the device address of each GPU's
+// copy is looked up once per device with hipGetSymbolAddress, with that device
+// current, and kept in a small table.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(hipStream_t st, void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    hipDevice_t dev = 0;
+    LASP_TRY(hipStreamGetDevice(st, &dev));
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        int cur = 0;
+        LASP_TRY(hipGetDevice(&cur));
+        if (cur != dev) LASP_TRY(hipSetDevice(dev));
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) LASP_TRY(hipSetDevice(cur));
+        LASP_TRY(e);
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_setup(const Params &p, hipStream_t st) {
     return launch_k(k_setup, dim3(1), dim3(NTHR), st, p);

@@ -36,8 +36,10 @@
  *
  * Ownership and threading: the caller owns every buffer; the library never
  * allocates or frees memory.  Between calls it keeps only a per-thread copy of
- * the text of the last HIP error it saw (for lasp_status_string), so calls on
- * different threads and streams are independent.  Calls are asynchronous on the
+ * the text of the last HIP error it saw (for lasp_status_string) and, once
+ * lasp_fwd_noalloc has run on a GPU, that GPU's address of the static scratch
+ * array (see there); calls of every other entry point on different threads and
+ * streams are independent.  Calls are asynchronous on the
  * given HIP stream (hipStream_t passed as void*, NULL = the default stream):
  * buffers must stay alive until the stream reaches them.  Outputs are fully
  * overwritten; outputs must not overlap inputs.
@@ -75,7 +77,9 @@ typedef enum {
     LASP_EUNSUPPORTED = 2,  /* d not in {32,64,128}, chunk not in {64,128,256}, dtype;
                                the gated and unmasked forms' own limits */
     LASP_EWORKSPACE = 3,    /* workspace_bytes smaller than the size query returns */
-    LASP_EHIP = 4           /* a HIP call or kernel launch failed */
+    LASP_EHIP = 4,          /* a HIP call or kernel launch failed */
+    LASP_ESCRATCH = 5       /* lasp_fwd_noalloc: the call needs more scratch than its
+                               static array holds */
 } lasp_status;
 
 /* B: batch; H: heads; N: tokens per sequence (packed batch: total tokens);
@@ -133,6 +137,28 @@ int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype,
              const float *decay, const int32_t *cu_seqlens, const float *M_in,
              void *O, float *M_out, void *state_cache,
              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments and results as lasp_fwd, without the workspace: the
+ * scratch lasp_fwd would take from its workspace (segment totals, packed-batch
+ * tables, and the states when state_cache is NULL) lives in a static device
+ * array of lasp_noalloc_scratch_bytes() bytes (64 MiB), one copy per GPU,
+ * which each GPU the library runs on holds until the process ends.  The call
+ * makes no hipMalloc / hipFree or other allocating call; its first call on a
+ * GPU looks up that GPU's copy (hipGetSymbolAddress).  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind (nothing in it needs
+ * to start at zero): calls that overlap in time on one GPU (other streams,
+ * other threads) race and must not be issued.  Returns LASP_ESCRATCH, before
+ * touching the device, when lasp_fwd_workspace_bytes(shape, dtype,
+ * state_cache != NULL) exceeds the array (at d = 128, chunk 256: B1 H32 with
+ * N up to 2^20 needs 16 to 32 MiB with a state cache, 34 to 66 MiB without).
+ * A state cache written here is read by lasp_bwd as usual. */
+size_t lasp_noalloc_scratch_bytes(void);
+int lasp_fwd_noalloc(const lasp_shape *shape, lasp_dtype dtype,
+                     const void *Q, const void *K, const void *V,
+                     const float *decay, const int32_t *cu_seqlens, const float *M_in,
+                     void *O, float *M_out, void *state_cache, void *stream);
 
 /* Backward pass (LASP Alg. 3 on one device; LASP-2 suffix sums of dM_t) for the
  * loss l = <dO, O> + <dM_out, M_out>.
@@ -273,8 +299,8 @@ int lasp_bwd_gated_ex(const lasp_shape *shape, lasp_dtype dtype,
                       void *workspace, size_t workspace_bytes, void *stream, void **events,
                       int segment_chunks);
 
-/* Human-readable text for a status code (for LASP_EHIP: the last HIP error of
- * the calling thread). */
+/* Human-readable text for a status code (for LASP_EHIP: the HIP error text of
+ * the last call on the calling thread that returned LASP_EHIP). */
 const char *lasp_status_string(int status);
 
 /* Library version, major * 10000 + minor * 100 + patch. */

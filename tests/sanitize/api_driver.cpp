@@ -128,6 +128,10 @@ hipError_t launch_bwd_gated(const Params &p, bool bf16, hipStream_t, hipEvent_t 
     return hipSuccess;
 }
 hipError_t launch_setup(const Params &, hipStream_t) { return hipSuccess; }
+hipError_t static_scratch(hipStream_t, void **ptr) {
+    *ptr = (void *)((uintptr_t)20 << 40);   // a fake device address for the static array
+    return hipSuccess;
+}
 hipError_t launch_fwd_bidir(const Params &p, bool, hipStream_t, hipEvent_t *) {
     check_params(p, true, true, false, true);
     return hipSuccess;
@@ -231,6 +235,21 @@ int main() {
                             }
                             ++cases;
                         }
+    // allocation-free forward: the plan's arrays stay inside the static array;
+    // a shape that needs more is refused before anything else happens
+    for (const lasp_shape &s : shapes)
+        for (int wc = 0; wc < 2; ++wc) {
+            lasp_sizes z;
+            if (lasp_query_sizes(&s, LASP_BF16, 0, 0, &z) != LASP_OK) continue;
+            g_bufs = {{(uintptr_t)20 << 40, lasp_noalloc_scratch_bytes(), "static scratch"},
+                      {U(fake(9)), wc ? z.state_cache : 0, "cache"}};
+            const int rc = lasp_fwd_noalloc(&s, LASP_BF16, fake(0), fake(1), fake(2), nullptr,
+                                            s.nseq ? (const int32_t *)CU : nullptr, nullptr,
+                                            fake(4), nullptr, wc ? fake(9) : nullptr, nullptr);
+            const bool fits = z.fwd_workspace[wc] <= lasp_noalloc_scratch_bytes();
+            if (rc != (fits ? LASP_OK : LASP_ESCRATCH)) fail("noalloc status", "noalloc");
+            ++cases;
+        }
     // debug path: malformed cu_seqlens and decay are rejected, good ones pass
     setenv("LASP_DEBUG", "1", 1);
     const lasp_shape pk = {1, 2, 300, 64, 64, 3};
