@@ -18,7 +18,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "fwd_noalloc", "bwd", "fwd_bidir", "bwd_bidir", "fwd_gated", "bwd_gated", "LaspError", "lib",
+__all__ = ["fwd", "fwd_noalloc", "bwd", "fwd_norm", "bwd_norm", "fwd_bidir", "bwd_bidir", "fwd_gated", "bwd_gated", "LaspError", "lib",
            "Shape", "Sizes", "LASP_FP32", "LASP_BF16", "query_sizes", "state_cache_bytes",
            "fwd_workspace_bytes", "bwd_workspace_bytes", "gated_state_cache_bytes",
            "gated_fwd_workspace_bytes", "gated_bwd_workspace_bytes"]
@@ -26,7 +26,7 @@ __all__ = ["fwd", "fwd_noalloc", "bwd", "fwd_bidir", "bwd_bidir", "fwd_gated", "
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblasp.so")
 LASP_FP32, LASP_BF16 = 0, 1
-FORM_CAUSAL, FORM_GATED = 0, 1
+FORM_CAUSAL, FORM_GATED, FORM_NORM = 0, 1, 2
 _lib = None
 
 
@@ -77,6 +77,8 @@ def lib():
             base = getattr(L, "lasp_" + n)
             sig(getattr(L, "lasp_%s_ex" % n), base.argtypes + [P, I])
         sig(L.lasp_fwd_noalloc, [SP, I] + [P] * 9 + [P])
+        sig(L.lasp_fwd_norm, [SP, I] + [P] * 11 + [S, P])
+        sig(L.lasp_bwd_norm, [SP, I] + [P] * 16 + [S, P])
         sig(L.lasp_noalloc_scratch_bytes, [], S)
         sig(L.lasp_status_string, [I], ctypes.c_char_p)
         sig(L.lasp_version, [])
@@ -281,6 +283,50 @@ def bwd(Q, K, V, dO, chunk, decay=None, cu_seqlens=None, M_in=None, dM_out=None,
     _run("lasp_bwd", c, [_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(decay), _ptr(cu_seqlens),
                          _ptr(M_in), _ptr(dM_out), _ptr(state_cache), _ptr(dQ), _ptr(dK),
                          _ptr(dV), _ptr(dM_in)], ws, need, events)
+    return dQ, dK, dV, dM_in
+
+
+def fwd_norm(Q, K, V, chunk, decay=None, cu_seqlens=None, M_in=None, *, want_m_out=True,
+             want_state_cache=True, workspace=None):
+    """Forward with the output normalised row by row (lasp_fwd_norm: Norm of LASP
+    Eq. 2 read as an RMS normalisation over d, eps 1e-6, no gain).
+    Returns (Y, rstd, M_out, state_cache); rstd is float32 [B, H, N]."""
+    import torch
+    c = _Call(Q, chunk, cu_seqlens, [("Q", Q), ("K", K), ("V", V)], [("M_in", M_in)],
+              FORM_NORM, 0, decay=decay)
+    Y = torch.empty_like(Q)
+    rstd = torch.empty(Q.shape[:3], dtype=torch.float32, device=c.dev)
+    M_out = c.empty_state(want_m_out)
+    cache = c.new_cache(want_state_cache)
+    need = c.sizes.fwd_workspace[cache is not None]
+    ws = c.workspace(need, workspace)
+    rc = lib().lasp_fwd_norm(ctypes.byref(c.S), c.dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(decay),
+                             _ptr(cu_seqlens), _ptr(M_in), _ptr(Y), _ptr(rstd), _ptr(M_out),
+                             _ptr(cache), _ptr(ws), need, _stream(c.dev))
+    if rc != 0:
+        raise LaspError(rc, "lasp_fwd_norm")
+    return Y, rstd, M_out, cache
+
+
+def bwd_norm(Q, K, V, Y, rstd, dY, chunk, decay=None, cu_seqlens=None, M_in=None, dM_out=None,
+             state_cache=None, *, want_dm_in=True, workspace=None):
+    """Backward of the normalised form for l = <dY, Y> + <dM_out, M_out>
+    (lasp_bwd_norm), given the forward's Y and rstd.  Returns (dQ, dK, dV, dM_in)."""
+    import torch
+    c = _Call(Q, chunk, cu_seqlens, [("Q", Q), ("K", K), ("V", V), ("Y", Y), ("dY", dY)],
+              [("M_in", M_in), ("dM_out", dM_out)], FORM_NORM, 0, decay=decay)
+    _check_dev("rstd", rstd, c.dev, torch.float32, Q.shape[:3])
+    c.check_cache(state_cache)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    dM_in = c.empty_state(want_dm_in)
+    need = c.sizes.bwd_workspace[state_cache is not None]
+    ws = c.workspace(need, workspace)
+    rc = lib().lasp_bwd_norm(ctypes.byref(c.S), c.dt, _ptr(Q), _ptr(K), _ptr(V), _ptr(Y),
+                             _ptr(rstd), _ptr(dY), _ptr(decay), _ptr(cu_seqlens), _ptr(M_in),
+                             _ptr(dM_out), _ptr(state_cache), _ptr(dQ), _ptr(dK), _ptr(dV),
+                             _ptr(dM_in), _ptr(ws), need, _stream(c.dev))
+    if rc != 0:
+        raise LaspError(rc, "lasp_bwd_norm")
     return dQ, dK, dV, dM_in
 
 

@@ -127,6 +127,11 @@ size_t bwd_ws(const Plan &pl, bool cache) {
            (cache ? 0 : pl.cache_b + pl.seg_b /*Lc, Pseg, Pfin, Z*/);
 }
 
+// bytes of one [B, H, N, d] token array, aligned
+size_t norm_bwd_extra(const lasp_shape *s, const Plan &pl) {
+    return align_up((size_t)s->B * s->H * s->N * s->d * pl.esz);
+}
+
 bool misaligned(const void *p, size_t a) { return p && ((uintptr_t)p % a) != 0; }
 
 struct Range {
@@ -212,15 +217,18 @@ size_t lasp_bwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype, int w
 
 int lasp_query_sizes(const lasp_shape *shape, lasp_dtype dtype, int form, int segment_chunks,
                      lasp_sizes *out) {
-    if (!out || (form != 0 && form != 1)) return LASP_EINVAL;
+    if (!out || form < 0 || form > 2 || (form == 2 && segment_chunks != 0)) return LASP_EINVAL;
     Plan pl;
     const int rc = make_plan(shape, dtype, pl, form == 1, segment_chunks);
     if (rc != LASP_OK) return rc;
+    // the normalised form's backward also holds the un-normalised output's
+    // gradient (one token array)
+    const size_t extra = form == 2 ? norm_bwd_extra(shape, pl) : 0;
     out->state_cache = pl.cache_b;
     out->fwd_workspace[0] = fwd_ws(pl, false);
     out->fwd_workspace[1] = fwd_ws(pl, true);
-    out->bwd_workspace[0] = bwd_ws(pl, false);
-    out->bwd_workspace[1] = bwd_ws(pl, true);
+    out->bwd_workspace[0] = bwd_ws(pl, false) + extra;
+    out->bwd_workspace[1] = bwd_ws(pl, true) + extra;
     return LASP_OK;
 }
 
@@ -257,18 +265,20 @@ static int debug_check(const lasp_shape *shape, const int32_t *cu, const float *
 
 namespace {
 
-enum Mode { CAUSAL, BIDIR, GATED };
+enum Mode { CAUSAL, BIDIR, GATED, NORM };
 
 int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
                const void *V, const float *decay, const float *log_g,
                const int32_t *cu_seqlens, const float *M_in, void *O, float *M_out,
                void *state_cache, void *workspace, size_t workspace_bytes, void *stream,
-               void **events, int seg_chunks, Mode mode) {
+               void **events, int seg_chunks, Mode mode, float *rstd = nullptr) {
     Plan pl;
     int rc = make_plan(shape, dtype, pl, mode == GATED, seg_chunks);
     if (rc != LASP_OK) return rc;
     if (mode == BIDIR && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
-    if (!Q || !K || !V || !O || (mode == GATED && !log_g)) return LASP_EINVAL;
+    if (!Q || !K || !V || !O || (mode == GATED && !log_g) || (mode == NORM && !rstd))
+        return LASP_EINVAL;
+    if (misaligned(rstd, 4)) return LASP_EINVAL;
     if ((shape->nseq > 0) != (cu_seqlens != nullptr)) return LASP_EINVAL;
     const void *a16[] = {Q, K, V, O, M_in, M_out, state_cache, workspace, log_g};
     for (const void *ptr : a16)
@@ -285,9 +295,10 @@ int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
                          {decay, (size_t)pl.H * 4},
                          {cu_seqlens, cu_seqlens ? ((size_t)pl.nseq + 1) * 4 : 0},
                          {log_g, log_g ? gates : 0}};
+    const size_t rows_b = (size_t)shape->B * shape->H * shape->N * sizeof(float);
     const Range outs[] = {{O, tens}, {M_out, st}, {state_cache, cache ? pl.cache_b : 0},
-                          {workspace, need}};
-    if (any_overlap(outs, 4, ins, 7)) return LASP_EINVAL;
+                          {workspace, need}, {rstd, rstd ? rows_b : 0}};
+    if (any_overlap(outs, 5, ins, 7)) return LASP_EINVAL;
     if ((rc = debug_check(shape, cu_seqlens, decay, (hipStream_t)stream)) != LASP_OK) return rc;
 
     lasp::Params p;
@@ -298,6 +309,7 @@ int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     p.O = O;
     p.M_in = M_in;
     p.M_out = M_out;
+    p.rstd = rstd;
     char *w = (char *)workspace;
     if (pl.varlen) {
         p.chunk_prefix = (int32_t *)w;
@@ -379,6 +391,14 @@ int lasp_fwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const voi
                        workspace, workspace_bytes, stream, nullptr, 0);
 }
 
+int lasp_fwd_norm(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                  const void *V, const float *decay, const int32_t *cu_seqlens,
+                  const float *M_in, void *Y, float *rstd, float *M_out, void *state_cache,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+    return fwd_common(shape, dtype, Q, K, V, decay, nullptr, cu_seqlens, M_in, Y, M_out,
+                      state_cache, workspace, workspace_bytes, stream, nullptr, 0, NORM, rstd);
+}
+
 size_t lasp_noalloc_scratch_bytes(void) { return lasp::kStaticScratchBytes; }
 
 int lasp_fwd_noalloc(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
@@ -406,13 +426,16 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
                const int32_t *cu_seqlens, const float *M_in, const float *dM_out,
                const void *state_cache, void *dQ, void *dK, void *dV, float *dlog_g,
                float *dM_in, void *workspace, size_t workspace_bytes, void *stream,
-               void **events, int seg_chunks, Mode mode) {
+               void **events, int seg_chunks, Mode mode, const void *Y = nullptr,
+               const float *rstd = nullptr) {
     Plan pl;
     int rc = make_plan(shape, dtype, pl, mode == GATED, seg_chunks);
     if (rc != LASP_OK) return rc;
     if (mode == BIDIR && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
     if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return LASP_EINVAL;
     if (mode == GATED && (!log_g || !dlog_g)) return LASP_EINVAL;
+    if (mode == NORM && (!Y || !rstd)) return LASP_EINVAL;
+    if (misaligned(Y, 16) || misaligned(rstd, 4)) return LASP_EINVAL;
     if ((shape->nseq > 0) != (cu_seqlens != nullptr)) return LASP_EINVAL;
     const void *a16[] = {Q,  K,  V,  dO,    M_in,      dM_out, state_cache,
                          dQ, dK, dV, dM_in, workspace, log_g,  dlog_g};
@@ -420,20 +443,23 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
         if (misaligned(ptr, 16)) return LASP_EINVAL;
     if (misaligned(decay, 4) || misaligned(cu_seqlens, 4)) return LASP_EINVAL;
     const bool cache = state_cache != nullptr;
-    const size_t need = bwd_ws(pl, cache);
+    const size_t extra = mode == NORM ? norm_bwd_extra(shape, pl) : 0;
+    const size_t need = bwd_ws(pl, cache) + extra;
     if (workspace_bytes < need || (need && !workspace)) return LASP_EWORKSPACE;
 
     const size_t tens = (size_t)shape->B * shape->H * shape->N * shape->d * pl.esz;
     const size_t gates = (size_t)shape->B * shape->H * shape->N * shape->d * sizeof(float);
     const size_t st = (size_t)pl.nseq * pl.H * pl.D * pl.D * sizeof(float);
+    const size_t rows_b = (size_t)shape->B * shape->H * shape->N * sizeof(float);
     const Range ins[] = {{Q, tens}, {K, tens}, {V, tens}, {dO, tens}, {M_in, st}, {dM_out, st},
                          {state_cache, cache ? pl.cache_b : 0},
                          {decay, (size_t)pl.H * 4},
                          {cu_seqlens, cu_seqlens ? ((size_t)pl.nseq + 1) * 4 : 0},
-                         {log_g, log_g ? gates : 0}};
+                         {log_g, log_g ? gates : 0}, {Y, Y ? tens : 0},
+                         {rstd, rstd ? rows_b : 0}};
     const Range outs[] = {{dQ, tens}, {dK, tens}, {dV, tens}, {dM_in, st}, {workspace, need},
                           {dlog_g, mode == GATED ? gates : 0}};
-    if (any_overlap(outs, 6, ins, 10)) return LASP_EINVAL;
+    if (any_overlap(outs, 6, ins, 12)) return LASP_EINVAL;
     if ((rc = debug_check(shape, cu_seqlens, decay, (hipStream_t)stream)) != LASP_OK) return rc;
 
     lasp::Params p;
@@ -474,6 +500,16 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     if (mode == GATED) {
         p.Gc = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b);
         p.Gs = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b + pl.gate_c);
+    }
+    if (mode == NORM) {   // the gradient of the un-normalised output, into the workspace's end
+        p.Yn = Y;
+        p.dYn = dO;
+        p.rstd_in = rstd;
+        p.dOn = (char *)workspace + (need - extra);
+        rc = hip_status(lasp::launch_norm_bwd_prep(p, dtype == LASP_BF16, hs));
+        if (rc != LASP_OK) return rc;
+        p.dO = p.dOn;
+        p.dq_forward = 1;   // dO rows scaled by 1/rms of each output row: no subtraction walk
     }
     if (!cache) {   // recompute the forward states (no output, no M_out)
         p.Z = (float *)(w + pl.cache_b);
@@ -540,6 +576,16 @@ int lasp_bwd_gated(const lasp_shape *shape, lasp_dtype dtype, const void *Q, con
     return lasp_bwd_gated_ex(shape, dtype, Q, K, V, log_g, dO, cu_seqlens, M_in, dM_out,
                              state_cache, dQ, dK, dV, dlog_g, dM_in, workspace, workspace_bytes,
                              stream, nullptr, 0);
+}
+
+int lasp_bwd_norm(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,
+                  const void *V, const void *Y, const float *rstd, const void *dY,
+                  const float *decay, const int32_t *cu_seqlens, const float *M_in,
+                  const float *dM_out, const void *state_cache, void *dQ, void *dK, void *dV,
+                  float *dM_in, void *workspace, size_t workspace_bytes, void *stream) {
+    return bwd_common(shape, dtype, Q, K, V, dY, decay, nullptr, cu_seqlens, M_in, dM_out,
+                      state_cache, dQ, dK, dV, nullptr, dM_in, workspace, workspace_bytes, stream,
+                      nullptr, 0, NORM, Y, rstd);
 }
 
 int lasp_bwd(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const void *K,

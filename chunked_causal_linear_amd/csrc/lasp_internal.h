@@ -37,6 +37,13 @@ struct Params {
     float *W;      // [segs][H][D][D] f32: local reverse state at each segment start
     float *Rfin;   // [nseq][H][D][D] f32 or null: reverse state before each sequence's first token, [dv][dk]
     int parts;     // row-block products: workgroups per (segment, head, product)
+    // output normalisation (Norm of LASP Eq. 2, read as a row-wise RMS norm)
+    float *rstd;        // [B, H, N] f32: forward output 1/sqrt(mean(o^2) + eps) per row, or null
+    const float *rstd_in;   // [B, H, N] f32: the forward's rstd (backward preparation)
+    const void *Yn, *dYn;   // [B, H, N, d]: normalised output and its gradient
+    void *dOn;              // [B, H, N, d]: gradient of the un-normalised output
+    int dq_forward;         // 1: dQ walks forwards from the entering states even without
+                            // decay (no subtraction walk; see the sweep kernel)
     // gated form
     const float *LG;   // [B, H, N, D] f32 log-gates (key channels)
     float *dLG;        // [B, H, N, D] f32 log-gate gradient
@@ -69,6 +76,11 @@ hipError_t launch_bwd_gated(const Params &p, bool bf16, hipStream_t stream, hipE
 // address of the copy on the stream's GPU (looked up once per device).
 constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
 hipError_t static_scratch(hipStream_t stream, void **ptr);
+
+// Output normalisation: Norm(o) = o / sqrt(mean_j o_j^2 + kNormEps) per row.
+constexpr float kNormEps = 1e-6f;
+// dOn = rstd_in * (dYn - Yn * mean(dYn . Yn)) per row (before launch_bwd).
+hipError_t launch_norm_bwd_prep(const Params &p, bool bf16, hipStream_t stream);
 
 // Packed-batch tables (chunk_prefix, seg_prefix) on the stream.
 hipError_t launch_setup(const Params &p, hipStream_t stream);

@@ -701,6 +701,27 @@ __device__ __forceinline__ void store_tile_t(const f32x16 *acc, bf16 *tile, int 
     }
 }
 
+// Norm of LASP Eq. 2 on the rows of a 32-row output tile accumulated
+// transposed (acc[nt] = [feature nt*32 + crow(e)][row lane%32]): lanes l and
+// l^32 hold the two halves of row l%32's features, so the row's sum of squares
+// is the lane's own sum plus its partner's.  Every acc element is scaled by
+// r = 1/sqrt(mean(o^2) + eps); lanes < 32 write r for their row (rows below
+// `rows` only).
+template <int D>
+__device__ __forceinline__ void norm_rows(f32x16 *acc, float *rstd, int rows, int lz) {
+    constexpr int NDT = D / 32;
+    float ss = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NDT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss += acc[nt][e] * acc[nt][e];
+    ss += __shfl_xor(ss, 32);
+    const float r = rsqrtf(ss * (1.f / D) + kNormEps);
+#pragma unroll
+    for (int nt = 0; nt < NDT; ++nt) acc[nt] *= r;
+    if (lz < 32 && lz < rows) rstd[lz] = r;
+}
+
 // ---------------------------------------------------------------------------
 // Segment sweep (bf16).  One workgroup per (segment, head, role) walks the
 // segment's chunks in sweep order (forward for O and dQ, backward for dV and
@@ -731,7 +752,11 @@ __device__ __forceinline__ void store_tile_t(const f32x16 *acc, bf16 *tile, int 
 // starts at minus the state after the segment (the next segment's entering
 // state, or the sequence's final state) and accumulates as usual, and the
 // output negated.  (With decay the subtraction would divide by lambda^Ct,
-// which is not stable; those heads keep the forward walk.)
+// which is not stable; those heads keep the forward walk.)  The subtraction
+// costs precision where P_t is small next to the segment's final state: the
+// rounding error of a row is of order 2^-9 |dO_r| |P_(t+1)|.  Callers whose dO
+// rows differ widely in size (the normalised form's dO is scaled by 1/rms of
+// each output row) set dq_forward, and dQ then walks forwards as with decay.
 //
 // Work split.  Wave w owns one 32-row tile of every chunk (its A rows live in
 // registers, loaded one chunk ahead) and a fixed share of the 32x32 state
@@ -843,7 +868,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     if (nch <= 0) return;
     const float l2 = DEC ? head_log2_decay(p, h) : 0.f;
     const bool decay = DEC && l2 != 0.f;
-    const bool sub = role == 1 && !decay;      // dQ by subtraction, walked backwards
+    const bool sub = role == 1 && !decay && !p.dq_forward;   // dQ by subtraction, walked backwards
     const bool rev = role >= 2 || sub;         // chunks swept backwards
     const int dmin = sub ? 1 : 0;              // causal range: dist(r, c) >= dmin
     const bool xt = role & 1;                  // the role uses X^T: state tiles accumulated transposed
@@ -1221,7 +1246,11 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         run_group(IC<1>(), Ct, upd, [&]() __attribute__((always_inline)) {
             if (i + 1 < nch) load_a(i + 1, af);
         });
-        // rows out (the tile's rows past the chunk end are dropped)
+        // rows out (the tile's rows past the chunk end are dropped); the
+        // output role normalises its rows first when asked to
+        if (role == 0 && p.rstd)
+            norm_rows<D>(acc, p.rstd + rbase + (int64_t)t * p.C + rt * 32,
+                         rt >= 0 ? Ct - rt * 32 : 0, opaque_lane());
         store_tile_t<D>(acc, Out + ((int64_t)t * p.C + rt * 32) * D, rt >= 0 ? Ct - rt * 32 : 0,
                         opaque_lane(), sub ? 0x80008000u : 0u);
         if (upd) write_state();
@@ -1500,6 +1529,73 @@ __global__ __launch_bounds__(64 * RM_NW) void k_rowmat_bf16(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Row-wise output normalisation (Norm of LASP Sec. 3.1, Eq. 2, read as
+// o / sqrt(mean_j o_j^2 + eps) per row of d features), over all B*H*N rows;
+// each row is handled by D/VEC lanes (16 bytes each) that reduce by shuffles.
+//   forward  (float32 path; the bf16 sweep does this in its store):
+//            O <- O r in place, rstd[row] = r
+//   backward preparation: dOn = r (dYn - Yn mean(dYn . Yn)), the gradient of
+//            the un-normalised output, which the backward then consumes as dO.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void store16(T *dst, const float *f);
+template <>
+__device__ __forceinline__ void store16<float>(float *dst, const float *f) {
+    *(float4 *)dst = make_float4(f[0], f[1], f[2], f[3]);
+}
+template <>
+__device__ __forceinline__ void store16<bf16>(bf16 *dst, const float *f) {
+    *(bf16x8_t *)dst = pack8(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+}
+
+template <typename T, int D, bool BWD>
+__global__ __launch_bounds__(NTHR) void k_rownorm(Params p) {
+    constexpr int V = Tr<T>::VEC, LPR = D / V;   // lanes per row (a power of two <= 64)
+    const int64_t nrows = (int64_t)p.B * p.H * p.N;
+    const int64_t row = ((int64_t)blockIdx.x * NTHR + threadIdx.x) / LPR;
+    const int64_t off = row * D + (threadIdx.x % LPR) * V;
+    const bool ok = row < nrows;
+    float a[V], b[V];
+    float s = 0.f;
+    if (ok) {
+        if (BWD) {
+            load16((const T *)p.Yn + off, a);
+            load16((const T *)p.dYn + off, b);
+#pragma unroll
+            for (int e = 0; e < V; ++e) s += a[e] * b[e];
+        } else {
+            load16((const T *)p.O + off, a);
+#pragma unroll
+            for (int e = 0; e < V; ++e) s += a[e] * a[e];
+        }
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);   // every lane takes part
+    if (!ok) return;
+    if (BWD) {
+        const float r = p.rstd_in[row], mean = s * (1.f / D);
+#pragma unroll
+        for (int e = 0; e < V; ++e) a[e] = r * (b[e] - a[e] * mean);
+        store16((T *)p.dOn + off, a);
+    } else {
+        const float r = rsqrtf(s * (1.f / D) + kNormEps);
+#pragma unroll
+        for (int e = 0; e < V; ++e) a[e] *= r;
+        store16((T *)p.O + off, a);
+        if (threadIdx.x % LPR == 0) p.rstd[row] = r;
+    }
+}
+
+template <typename T, int D, bool BWD>
+static hipError_t rownorm_launch(const Params &p, hipStream_t st) {
+    constexpr int LPR = D / Tr<T>::VEC;
+    const int64_t threads = (int64_t)p.B * p.H * p.N * LPR;
+    if (threads == 0) return hipSuccess;
+    return launch_k(k_rownorm<T, D, BWD>, dim3((unsigned)((threads + NTHR - 1) / NTHR)), dim3(NTHR),
+                    st, p);
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 static inline int round8(int n) { return (n + 7) & ~7; }
@@ -1556,8 +1652,10 @@ static hipError_t fwd_impl(const Params &p, bool with_output, hipStream_t st, hi
     LASP_TRY(rec_event(ev, 1, st));
     LASP_TRY(launch_k(k_fwd_segscan<D, T>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
     LASP_TRY(rec_event(ev, 2, st));
-    if (with_output)
+    if (with_output) {
         LASP_TRY(launch_k(k_fwd_out<T, D, BT>, dim3(round8(p.n_chunks_ub * p.H)), dim3(NTHR), st, p));
+        if (p.rstd) LASP_TRY((rownorm_launch<T, D, false>(p, st)));
+    }
     return rec_event(ev, 3, st);
 }
 
@@ -1580,7 +1678,7 @@ template <int D, int C, int KIND>
 static hipError_t sweep_launch(const Params &p, hipStream_t st) {
     const int roles = KIND == SWEEP_GRADS ? 3 : 1;
     const dim3 grid(round8(p.n_segs_ub * p.H * roles)), block(SweepCfg<C>::NT);
-    if (p.decay) {
+    if (p.decay || (KIND == SWEEP_GRADS && p.dq_forward)) {
         if constexpr (KIND == SWEEP_GRADS) {
             LASP_TRY(launch_k(k_sweep_bf16<D, C, SWEEP_DVDK, true>, dim3(round8(p.n_segs_ub * p.H * 2)),
                               block, st, p));
@@ -1689,6 +1787,16 @@ hipError_t launch_bwd_bidir(const Params &p, hipStream_t st, hipEvent_t *ev) {
     case 32: return bwd_bidir<32>(p, st, ev);
     case 64: return bwd_bidir<64>(p, st, ev);
     case 128: return bwd_bidir<128>(p, st, ev);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_norm_bwd_prep(const Params &p, bool bf, hipStream_t st) {
+    if (!p.Yn || !p.dYn || !p.rstd_in || !p.dOn) return hipErrorInvalidValue;
+    switch (p.D) {
+    case 32: return bf ? rownorm_launch<bf16, 32, true>(p, st) : rownorm_launch<float, 32, true>(p, st);
+    case 64: return bf ? rownorm_launch<bf16, 64, true>(p, st) : rownorm_launch<float, 64, true>(p, st);
+    case 128: return bf ? rownorm_launch<bf16, 128, true>(p, st) : rownorm_launch<float, 128, true>(p, st);
     }
     return hipErrorInvalidValue;
 }

@@ -109,7 +109,8 @@ size_t lasp_bwd_workspace_bytes(const lasp_shape *shape, lasp_dtype dtype,
  * gathered chunk states).  segment_chunks = 0 gives the library's choice of G,
  * a pure function of the shape and dtype, which the plain entry points and the
  * queries above use; segment_chunks > 0 forces G (a tuning and testing knob of
- * the _ex entry points).  form: 0 = causal and unmasked entry points, 1 = gated.
+ * the _ex entry points).  form: 0 = causal and unmasked entry points, 1 = gated,
+ * 2 = normalised (lasp_fwd_norm / lasp_bwd_norm: segment_chunks must be 0).
  * Returns LASP_OK and fills *out, or the status lasp_fwd would return for the
  * shape (LASP_EINVAL also for a negative segment_chunks or a NULL out). */
 typedef struct {
@@ -199,6 +200,37 @@ int lasp_bwd_ex(const lasp_shape *shape, lasp_dtype dtype,
                 void *dQ, void *dK, void *dV, float *dM_in,
                 void *workspace, size_t workspace_bytes, void *stream, void **events,
                 int segment_chunks);
+
+/* Normalised output: LASP Sec. 3.1, Eq. 2, O = Norm((Q K^T . M) V), which the
+ * pages define only as "a normalization operation" and leave out of every
+ * derivation.  Reading implemented: a root-mean-square normalisation of each
+ * output row (one token of one head) over its d features, without a gain,
+ *
+ *   Y_p = o_p * rstd_p,   rstd_p = 1 / sqrt(mean_j o_pj^2 + LASP_NORM_EPS),
+ *
+ * o_p the causal output of lasp_fwd (decay, M_in, packed batches as there).
+ * M_out is the carried state, not normalised.
+ *   lasp_fwd_norm: as lasp_fwd, writing Y (the layout and dtype of O) and rstd
+ *     (device float32 [B, H, N], one value per row, 4-byte aligned) instead of O.
+ *   lasp_bwd_norm: as lasp_bwd for l = <dY, Y> + <dM_out, M_out>, given the
+ *     forward's Y and rstd and the gradient dY (the layout of Y); it first
+ *     forms dO = rstd (dY - Y mean_j(dY_j Y_j)) per row in the workspace, then
+ *     runs lasp_bwd's kernels on it.  Its workspace is lasp_query_sizes(form
+ *     2).bwd_workspace: lasp_bwd's plus one [B, H, N, d] array.
+ * Errors as lasp_fwd / lasp_bwd (Y, rstd required). */
+#define LASP_NORM_EPS 1e-6f
+int lasp_fwd_norm(const lasp_shape *shape, lasp_dtype dtype,
+                  const void *Q, const void *K, const void *V,
+                  const float *decay, const int32_t *cu_seqlens, const float *M_in,
+                  void *Y, float *rstd, float *M_out, void *state_cache,
+                  void *workspace, size_t workspace_bytes, void *stream);
+int lasp_bwd_norm(const lasp_shape *shape, lasp_dtype dtype,
+                  const void *Q, const void *K, const void *V,
+                  const void *Y, const float *rstd, const void *dY,
+                  const float *decay, const int32_t *cu_seqlens, const float *M_in,
+                  const float *dM_out, const void *state_cache,
+                  void *dQ, void *dK, void *dV, float *dM_in,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Unmasked (bidirectional) form: LASP Eq. 3 without Norm, every token attends
  * to every token of its sequence, no decay; with sequence parallelism each

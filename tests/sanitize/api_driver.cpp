@@ -105,6 +105,7 @@ void check_params(const lasp::Params &p, bool fwd, bool bf16, bool gated, bool b
         fail("packed bounds", "ub");
     }
     (void)bidir;
+    if (p.dOn) ex.push_back({U(p.dOn), (size_t)p.B * H * p.N * D * esz, "dOn"});
     check_extents(ex);
 }
 
@@ -128,6 +129,10 @@ hipError_t launch_bwd_gated(const Params &p, bool bf16, hipStream_t, hipEvent_t 
     return hipSuccess;
 }
 hipError_t launch_setup(const Params &, hipStream_t) { return hipSuccess; }
+hipError_t launch_norm_bwd_prep(const Params &p, bool, hipStream_t) {
+    if (!p.Yn || !p.dYn || !p.rstd_in || !p.dOn) fail("norm preparation arguments", "dOn");
+    return hipSuccess;
+}
 hipError_t static_scratch(hipStream_t, void **ptr) {
     *ptr = (void *)((uintptr_t)20 << 40);   // a fake device address for the static array
     return hipSuccess;
@@ -168,7 +173,8 @@ const void *DECAY = (const void *)(uintptr_t)0x50000000u;
 
 int run_case(const lasp_shape &s, lasp_dtype dt, int form, int G, bool with_cache, bool decay) {
     lasp_sizes z;
-    int rc = lasp_query_sizes(&s, dt, form == 2 ? 0 : form, G, &z);
+    if (form == 3 && G) return LASP_OK;   // the normalised form has no segment knob
+    int rc = lasp_query_sizes(&s, dt, form == 2 ? 0 : form == 3 ? 2 : form, G, &z);
     if (rc != LASP_OK) return rc;
     const size_t tens = (size_t)s.B * s.H * s.N * s.d * (dt == LASP_BF16 ? 2 : 4);
     const size_t nS = s.nseq ? s.nseq : s.B;
@@ -182,7 +188,10 @@ int run_case(const lasp_shape &s, lasp_dtype dt, int form, int G, bool with_cach
     void *c = with_cache ? cache : nullptr;
     (void)tens;
     g_bufs = {{U(ws), fw, "fwd workspace"}, {U(cache), with_cache ? z.state_cache : 0, "cache"}};
-    if (form == 0)
+    if (form == 3)
+        rc = lasp_fwd_norm(&s, dt, Q, K, V, dec, cu, (float *)Min, O, (float *)fake(16),
+                           (float *)Mout, c, ws, fw, nullptr);
+    else if (form == 0)
         rc = lasp_fwd_ex(&s, dt, Q, K, V, dec, cu, (float *)Min, O, (float *)Mout, c, ws, fw, nullptr,
                          nullptr, G);
     else if (form == 1)
@@ -193,7 +202,10 @@ int run_case(const lasp_shape &s, lasp_dtype dt, int form, int G, bool with_cach
                                nullptr, nullptr, G);
     if (rc != LASP_OK) return rc;
     g_bufs = {{U(ws), bw, "bwd workspace"}, {U(cache), with_cache ? z.state_cache : 0, "cache"}};
-    if (form == 0)
+    if (form == 3)
+        rc = lasp_bwd_norm(&s, dt, Q, K, V, O, (const float *)fake(16), dO, dec, cu, (float *)Min,
+                           (float *)dMout, c, dQ, dK, dV, (float *)dMin, ws, bw, nullptr);
+    else if (form == 0)
         rc = lasp_bwd_ex(&s, dt, Q, K, V, dO, dec, cu, (float *)Min, (float *)dMout, c, dQ, dK, dV,
                          (float *)dMin, ws, bw, nullptr, nullptr, G);
     else if (form == 1)
@@ -218,12 +230,12 @@ int main() {
         {2, 64, 1 << 20, 128, 256, 0}, {1, 96, 1 << 21, 64, 64, 300}};
     for (const lasp_shape &s : shapes)
         for (int dti = 0; dti < 2; ++dti)
-            for (int form = 0; form < 3; ++form)
+            for (int form = 0; form < 4; ++form)
                 for (int G : {0, 1, 3, 64})
                     for (int wc = 0; wc < 2; ++wc)
                         for (int dec = 0; dec < 2; ++dec) {
                             const lasp_dtype dt = dti ? LASP_BF16 : LASP_FP32;
-                            if (form != 0 && dec) continue;
+                            if (form != 0 && form != 3 && dec) continue;
                             const int rc = run_case(s, dt, form, G, wc, dec);
                             const bool expect_ok = (form != 1 || s.chunk == 64) &&
                                                    (form != 2 || dt == LASP_BF16);

@@ -264,7 +264,16 @@ def test_query_sizes_agrees_with_the_plain_queries(L):
                     assert g.bwd_workspace[0] - g.bwd_workspace[1] >= g.state_cache
     out = cca.Sizes()
     assert L.lasp_query_sizes(ctypes.byref(SHAPES[0]), 1, 0, -1, ctypes.byref(out)) == EINVAL
-    assert L.lasp_query_sizes(ctypes.byref(SHAPES[0]), 1, 2, 0, ctypes.byref(out)) == EINVAL
+    assert L.lasp_query_sizes(ctypes.byref(SHAPES[0]), 1, 3, 0, ctypes.byref(out)) == EINVAL
+    assert L.lasp_query_sizes(ctypes.byref(SHAPES[0]), 1, 2, 4, ctypes.byref(out)) == EINVAL
+    # the normalised form: the causal sizes, plus one token array in the backward
+    for s in SHAPES:
+        for dt in (0, 1):
+            a, b = cca.query_sizes(s, dt, 0), cca.query_sizes(s, dt, 2)
+            tens = s.B * s.H * s.N * s.d * (2 if dt else 4)
+            assert a.state_cache == b.state_cache and list(a.fwd_workspace) == list(b.fwd_workspace)
+            for i in (0, 1):
+                assert tens <= b.bwd_workspace[i] - a.bwd_workspace[i] < tens + 256
     assert L.lasp_query_sizes(ctypes.byref(SHAPES[0]), 1, 0, 0, None) == EINVAL
     assert L.lasp_query_sizes(ctypes.byref(Shape(1, 1, 8, 48, 64, 0)), 1, 0, 0,
                               ctypes.byref(out)) == EUNSUP
@@ -303,3 +312,27 @@ def test_validated_call_without_a_gpu_reports_ehip(L):
     assert fwd_call(L, s) == EHIP
     msg = L.lasp_status_string(EHIP)
     assert isinstance(msg, bytes) and len(msg) > 0
+
+
+def declared_arity():
+    """Number of parameters of every function include/lasp.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(lasp_\w+)\s*\(([^;{]*?)\)\s*;", text):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_the_header(L):
+    """Every function the binding gives argtypes to takes as many arguments as
+    include/lasp.h declares (a miscounted ctypes signature would pass pointers
+    in the wrong slots)."""
+    arity = declared_arity()
+    checked = 0
+    for name, n in arity.items():
+        f = getattr(L, name)
+        if f.argtypes is not None:
+            assert len(f.argtypes) == n, (name, len(f.argtypes), n)
+            checked += 1
+    assert checked >= 20

@@ -167,6 +167,21 @@ def test_mixed_decay_heads():
     check("mixed decay", run_gpu(inp, seg=3), oracle_full(inp), TOL["bf16"])
 
 
+@pytest.mark.parametrize("decay", ["none", "lightning"])
+def test_uneven_do_rows(decay):
+    """dO rows of very different sizes (the first rows of each sequence up to
+    100 times the last ones): every gradient stays within the bar of its
+    largest element."""
+    w = small("bf16 d64 C64 uneven dO", "bf16", B=1, H=2, N=64 * 6 + 9, d=64, chunk=64, seed=28,
+              decay=decay, m_in_scale=0.1, dm_out_scale=0.1)
+    inp = make_inputs(w)
+    n = torch.arange(inp["shape"]["N"], dtype=torch.float32)
+    scale = 1.0 + 99.0 * torch.exp(-n / 10.0)
+    inp["dO"] = (inp["dO"].float() * scale[None, None, :, None]).to(torch.bfloat16)
+    say("case: uneven dO rows", decay)
+    check("uneven dO " + decay, run_gpu(inp, seg=3), oracle_full(inp), TOL["bf16"])
+
+
 def test_zero_decay():
     """lambda = 0: only the current token contributes."""
     w = small("bf16 d64 C64", "bf16", B=1, H=2, N=130, d=64, chunk=64, seed=21, m_in_scale=0.1,
