@@ -756,7 +756,8 @@ __device__ __forceinline__ void norm_rows(f32x16 *acc, float *rstd, int rows, in
 // costs precision where P_t is small next to the segment's final state: the
 // rounding error of a row is of order 2^-9 |dO_r| |P_(t+1)|.  Callers whose dO
 // rows differ widely in size (the normalised form's dO is scaled by 1/rms of
-// each output row) set dq_forward, and dQ then walks forwards as with decay.
+// each output row) set dq_forward: dQ then runs in its own launch and walks
+// forwards, as with decay.
 //
 // Work split.  Wave w owns one 32-row tile of every chunk (its A rows live in
 // registers, loaded one chunk ahead) and a fixed share of the 32x32 state
@@ -832,13 +833,14 @@ enum SweepKind {
     // at other speeds: in one launch the three drift apart and share nothing.
     // Such calls launch dV + dK together (they keep in step) and dQ after them.
     SWEEP_DQ = 2,      // role 1
-    SWEEP_DVDK = 3     // roles 2-3
+    SWEEP_DVDK = 3,    // roles 2-3
+    SWEEP_OUT_NORM = 4 // role 0, rows normalised (Norm of LASP Eq. 2) in the store
 };
 // DEC = false: the call has no decay array (every lambda is 1); the decay
 // arithmetic is compiled out.
 template <int D, int C, int KIND, bool DEC>
 __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
-    constexpr int role0 = KIND == SWEEP_GRADS || KIND == SWEEP_DQ ? 1 : KIND == SWEEP_DVDK ? 2 : 0;
+    constexpr int role0 = KIND == SWEEP_GRADS || KIND == SWEEP_DQ ? 1 : KIND == SWEEP_DVDK ? 2 : 0;   // OUT, OUT_NORM: 0
     constexpr int nroles = KIND == SWEEP_GRADS ? 3 : KIND == SWEEP_DVDK ? 2 : 1;
     using Cfg = SweepCfg<C>;
     constexpr int NCT = Cfg::NCT, NW = Cfg::NW, NG = Cfg::NG;
@@ -868,7 +870,11 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     if (nch <= 0) return;
     const float l2 = DEC ? head_log2_decay(p, h) : 0.f;
     const bool decay = DEC && l2 != 0.f;
-    const bool sub = role == 1 && !decay && !p.dq_forward;   // dQ by subtraction, walked backwards
+    // dQ by subtraction, walked backwards, for heads without decay; the
+    // separate dQ launch serves calls with a decay array (its heads with
+    // lambda = 1 still subtract, so that an all-ones array gives the bits of
+    // no array) and calls with dq_forward (never subtracts)
+    const bool sub = role == 1 && !decay && (KIND == SWEEP_GRADS || !p.dq_forward);
     const bool rev = role >= 2 || sub;         // chunks swept backwards
     const int dmin = sub ? 1 : 0;              // causal range: dist(r, c) >= dmin
     const bool xt = role & 1;                  // the role uses X^T: state tiles accumulated transposed
@@ -1248,7 +1254,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         });
         // rows out (the tile's rows past the chunk end are dropped); the
         // output role normalises its rows first when asked to
-        if (role == 0 && p.rstd)
+        if (KIND == SWEEP_OUT_NORM)
             norm_rows<D>(acc, p.rstd + rbase + (int64_t)t * p.C + rt * 32,
                          rt >= 0 ? Ct - rt * 32 : 0, opaque_lane());
         store_tile_t<D>(acc, Out + ((int64_t)t * p.C + rt * 32) * D, rt >= 0 ? Ct - rt * 32 : 0,
@@ -1678,6 +1684,10 @@ template <int D, int C, int KIND>
 static hipError_t sweep_launch(const Params &p, hipStream_t st) {
     const int roles = KIND == SWEEP_GRADS ? 3 : 1;
     const dim3 grid(round8(p.n_segs_ub * p.H * roles)), block(SweepCfg<C>::NT);
+    if (KIND == SWEEP_OUT && p.rstd) {   // normalised output rows
+        if (p.decay) return launch_k(k_sweep_bf16<D, C, SWEEP_OUT_NORM, true>, grid, block, st, p);
+        return launch_k(k_sweep_bf16<D, C, SWEEP_OUT_NORM, false>, grid, block, st, p);
+    }
     if (p.decay || (KIND == SWEEP_GRADS && p.dq_forward)) {
         if constexpr (KIND == SWEEP_GRADS) {
             LASP_TRY(launch_k(k_sweep_bf16<D, C, SWEEP_DVDK, true>, dim3(round8(p.n_segs_ub * p.H * 2)),

@@ -28,6 +28,7 @@ import numpy as np
 __all__ = [
     "gated_recurrent_fwd", "gated_recurrent_bwd", "gated_unrolled_fwd",
     "batched_gated_fwd", "batched_gated_bwd", "gated_sampled", "gated_closed_states",
+    "gated_sampled_sweep",
 ]
 
 
@@ -197,3 +198,62 @@ def gated_closed_states(q, k, v, log_g, do, m_in=None, dm_out=None):
     m_out = (k * np.exp(B[L - 1][None, :] - B)).T @ v + np.exp(B[L - 1])[:, None] * m
     dm_in = (q * np.exp(B)).T @ do + np.exp(B[L - 1])[:, None] * dm
     return m_out, dm_in
+
+
+def gated_sampled_sweep(q, k, v, log_g, do, rows, m_in=None, dm_out=None):
+    """The rows of gated_sampled and the states of gated_closed_states at once,
+    the same sums regrouped over the sorted rows: one pass forwards carries
+    kv_{p-1} from one row to the next, one pass backwards carries G_p (the
+    gradient of l w.r.t. kv_p), O(L d^2) in all instead of per row:
+
+        kv_{p-1} = Diag(exp(B_{p-1} - B_{a-1})) kv_{a-1}
+                   + sum_{a <= i < p} Diag(exp(B_{p-1} - B_i)) k_i^T v_i      (a < p)
+        G_p      = Diag(exp(B_b - B_p)) G_b
+                   + sum_{p <= u < b} Diag(exp(B_u - B_p)) q_u^T do_u          (p < b)
+
+    with B the running sum of the log-gates, B_{-1} = 0, and G_L = dM_out,
+    B_L = B_{L-1}; kv_{L-1} is M_out and G_{-1} is dM_in.  Every exponent is
+    <= 0 for log-gates <= 0.  Returns (rows dict as gated_sampled, M_out, dM_in)."""
+    q, k, v, lg, do = _f64(q), _f64(k), _f64(v), _f64(log_g), _f64(do)
+    L, d = q.shape
+    rows = np.unique(np.asarray(rows, dtype=np.int64))
+    B = np.cumsum(lg, axis=0)
+    zero = np.zeros(d)
+
+    def b_before(p):          # B_{p-1}
+        return B[p - 1] if p > 0 else zero
+
+    kv_prev = {}
+    cur, a = _state(d, m_in), 0            # cur = kv_{a-1}
+    for p in [int(r) for r in rows] + [L]:
+        if p > a:
+            e = b_before(p)
+            cur = (np.exp(e - b_before(a))[:, None] * cur
+                   + (k[a:p] * np.exp(e[None, :] - B[a:p])).T @ v[a:p])
+            a = p
+        kv_prev[p] = cur
+    m_out = kv_prev[L]
+
+    def b_at(p):              # B_p, with B_L = B_{L-1} and B_{-1} = 0
+        return zero if p < 0 else B[min(p, L - 1)]
+
+    G = {}
+    cur, b = _state(d, dm_out), L          # cur = G_b
+    for p in [int(r) for r in rows[::-1]] + [-1]:
+        e = b_at(p)
+        lo = max(p, 0)
+        cur = (np.exp(b_at(b) - e)[:, None] * cur
+               + (q[lo:b] * np.exp(B[lo:b] - e[None, :])).T @ do[lo:b])
+        b = lo if p >= 0 else 0
+        G[p] = cur
+    dm_in = G[-1]
+
+    out = {n: np.zeros((len(rows), d)) for n in ("O", "dQ", "dK", "dV", "dLG")}
+    for n, p in enumerate(int(r) for r in rows):
+        kv_p = np.exp(lg[p])[:, None] * kv_prev[p] + np.outer(k[p], v[p])
+        out["O"][n] = q[p] @ kv_p
+        out["dQ"][n] = do[p] @ kv_p.T
+        out["dK"][n] = v[p] @ G[p].T
+        out["dV"][n] = k[p] @ G[p]
+        out["dLG"][n] = np.exp(lg[p]) * np.sum(G[p] * kv_prev[p], axis=1)
+    return out, m_out, dm_in

@@ -319,3 +319,23 @@ def test_log_gate_gradient_as_a_suffix_sum():
     _, ma = go.gated_recurrent_fwd(q[:s], k[:s], v[:s], lg[:s], m)
     R = go.gated_recurrent_bwd(q[s:], k[s:], v[s:], lg[s:], do[s:], ma, dm)[4]
     np.testing.assert_allclose(np.sum(R * ma, axis=1), dB[s:].sum(axis=0), rtol=1e-9, atol=1e-10)
+
+
+@pytest.mark.parametrize("L,d,seed", [(1, 4, 0), (7, 3, 1), (200, 8, 2), (600, 16, 3)])
+def test_sampled_sweep_matches_rows_and_closed_states(L, d, seed):
+    """gated_sampled_sweep regroups the sums of gated_sampled (rows) and
+    gated_closed_states (M_out, dM_in), both pinned above, into one pass each
+    way: it must give the same values, rows 0 and L-1 and repeated rows
+    included."""
+    r = np.random.default_rng(seed)
+    q, k, v, do = (r.standard_normal((L, d)) for _ in range(4))
+    lg = np.log(1 / (1 + np.exp(-r.standard_normal((L, d))))) * 0.7
+    mi, dmo = r.standard_normal((d, d)), r.standard_normal((d, d))
+    rows = np.concatenate([[0, L - 1, L - 1], r.integers(0, L, 6)])
+    a = go.gated_sampled(q, k, v, lg, do, np.unique(rows), mi, dmo)
+    mo, dmi = go.gated_closed_states(q, k, v, lg, do, mi, dmo)
+    b, mo2, dmi2 = go.gated_sampled_sweep(q, k, v, lg, do, rows, mi, dmo)
+    for n in a:
+        assert np.abs(a[n] - b[n]).max() <= 1e-12 * max(1.0, np.abs(a[n]).max()), n
+    assert np.abs(mo - mo2).max() <= 1e-12 * max(1.0, np.abs(mo).max())
+    assert np.abs(dmi - dmi2).max() <= 1e-12 * max(1.0, np.abs(dmi).max())

@@ -136,24 +136,23 @@ def test_gated_rejects_bad_configurations():
 
 def test_gated_full_size_sampled():
     """bf16 B1 H32 N131072 d128 C64 with GLA gates, M_in and dM_out (the
-    benchmark's gated workload): sampled rows of O, dQ, dK, dV and dlog_g from
-    the oracle's prefix / suffix sums, and the full M_out and dM_in, on four
-    heads."""
+    benchmark's gated workload): on every one of the 32 heads, sampled rows of
+    O, dQ, dK, dV and dlog_g and the full M_out and dM_in, against the
+    oracle's prefix / suffix sums (gated_sampled_sweep)."""
     w = dataclasses.replace(GATED, dm_out_scale=0.01, seed=75)
     say("case:", w.name)
     inp = make_inputs(w)
     out = run_gated(inp)
     r = np.random.default_rng(175)
     L = w.N
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, L - 65, L - 1], r.integers(0, L, 10)]))
-    idx = torch.as_tensor(rows)
     names = ("O", "dQ", "dK", "dV", "dLG")
     acc = {k: ([], []) for k in names + ("M_out", "dM_in")}
-    for h in (0, 9, 22, 31):
+    for h in range(w.H):
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, L - 65, L - 1], r.integers(0, L, 10)]))
+        idx = torch.as_tensor(rows)
         q, k, v, lg, do = (np64(inp[x][0, h]) for x in ("Q", "K", "V", "log_g", "dO"))
         mi, dmo = np64(inp["M_in"][0, h]), np64(inp["dM_out"][0, h])
-        ref = go.gated_sampled(q, k, v, lg, do, rows, mi, dmo)
-        mo, dmi = go.gated_closed_states(q, k, v, lg, do, mi, dmo)
+        ref, mo, dmi = go.gated_sampled_sweep(q, k, v, lg, do, rows, mi, dmo)
         for name in names:
             acc[name][0].append(np64(out[name][0, h].index_select(0, idx.to(out[name].device))))
             acc[name][1].append(ref[name])
@@ -161,6 +160,8 @@ def test_gated_full_size_sampled():
         acc["M_out"][1].append(mo)
         acc["dM_in"][0].append(np64(out["dM_in"][0, h]))
         acc["dM_in"][1].append(dmi)
+        if h % 8 == 7:
+            say("  heads checked:", h + 1)
     errs = {k: rel(np.concatenate(g), np.concatenate(rv)) for k, (g, rv) in acc.items()}
     say(w.name, " ".join("%s=%.2e" % kv for kv in errs.items()))
     bad = {k: e for k, e in errs.items() if not e <= TOL["bf16"]}
