@@ -855,7 +855,10 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
     static_assert(96 * D <= L::SOFF, "K / Q rows must not reach the scores");
     static_assert(!SW || DH * D <= L::CPART, "swizzled state parts fit the transposed ones' space");
     __shared__ float bS[GC * D];
-    __shared__ float rho[D], Ep[D];
+    // Ep[mi][c]: row block mi's part of rowsum(R_t . P_{t+1}) for channel c,
+    // each written by exactly one wave and summed in block order afterwards
+    // (a fixed order, so the result does not depend on wave timing)
+    __shared__ float rho[D], Ep[GC / 32][D];
     __shared__ __attribute__((aligned(16))) char U_raw[L::BYTES];
     T *U = (T *)U_raw;
     T *Sc = U + L::SOFF;   // score tiles (every phase)
@@ -891,7 +894,6 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
     // from L2 rather than kept live across phases: registers bound the
     // workgroups per CU)
     chunk_cumlog<D>(bS, p.LG + rb * D, Ct);   // (its registers are free before the rows load)
-    if (threadIdx.x < D) Ep[threadIdx.x] = 0.f;
     Raw<T, D, GC> rdo, rv, rkq;
     Raw<T, D, 96> rk96;
     raw_load(rdo, dO, Ct, RowId());
@@ -1197,7 +1199,7 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
                 if (i < Ct) ep += tof(Kx[i * PD + c]) * ex2(bl - bS[i * D + c]) * dk[k][r];
             }
             ep += __shfl_xor(ep, 32);
-            if (l < 32) atomicAdd(&Ep[c], ep);
+            if (l < 32) Ep[mi][c] = ep;
             const float sc = ex2(bl - bS[mJ * D + c]);
 #pragma unroll
             for (int r = 0; r < 16; ++r) dk[k][r] *= sc;
@@ -1278,7 +1280,10 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
         __syncthreads();
         dBs[part * D + c] = x[0];
         __syncthreads();
-        float off = ex2(bS[(GC - 1) * D + c]) * rho[c] + Ep[c];
+        float ep = 0.f;
+#pragma unroll
+        for (int mi = 0; mi < GC / 32; ++mi) ep += Ep[mi][c];
+        float off = ex2(bS[(GC - 1) * D + c]) * rho[c] + ep;
         for (int q = part + 1; q < NP; ++q) off += dBs[q * D + c];
         // (the row offsets formed here, opaque to the compiler, rather than
         // computed at the kernel start and kept in registers throughout)
