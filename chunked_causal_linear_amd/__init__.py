@@ -9,6 +9,9 @@ The binding raises if the library is missing: there is no fallback path.
   fwd_bidir / bwd_bidir: the unmasked (bidirectional) form, bf16, no decay
   fwd_gated / bwd_gated: per-token, per-key-channel gates (log-gates in, their
                          gradient out), chunk 64
+  fwd_norm / bwd_norm: output rows normalised (Norm of LASP Eq. 2)
+  autograd (submodule): lasp_attention, lasp_gated_attention and
+                        lasp_bidir_attention as torch.autograd.Functions
 
 Semantics, layouts and error codes are those of include/lasp.h ("Linear Attention
 Sequence Parallelism", arXiv 2404.02882, Sec. 3.2, Algorithms 2 and 3).

@@ -336,3 +336,18 @@ def test_binding_signatures_match_the_header(L):
             assert len(f.argtypes) == n, (name, len(f.argtypes), n)
             checked += 1
     assert checked >= 20
+
+
+def test_autograd_wrappers_reject_host_tensors():
+    """The autograd wrappers go through the same argument checks: host tensors
+    are refused before the library is touched."""
+    import torch
+    from chunked_causal_linear_amd.autograd import (lasp_attention, lasp_bidir_attention,
+                                                    lasp_gated_attention)
+    Q = torch.zeros(1, 1, 64, 32)
+    with pytest.raises(ValueError, match="GPU"):
+        lasp_attention(Q, Q, Q, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        lasp_bidir_attention(Q, Q, Q, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        lasp_gated_attention(Q, Q, Q, Q, 64)
