@@ -6,7 +6,7 @@ The binding raises if the library is missing: there is no fallback path.
 
   fwd(Q, K, V, chunk, ...) -> (O, M_out, state_cache)
   bwd(Q, K, V, dO, chunk, ...) -> (dQ, dK, dV, dM_in)
-  fwd_bidir / bwd_bidir: the unmasked (bidirectional) form, bf16, no decay
+  fwd_bidir / bwd_bidir: the unmasked (bidirectional) form, no decay
   fwd_gated / bwd_gated: per-token, per-key-channel gates (log-gates in, their
                          gradient out), chunk 64
   fwd_norm / bwd_norm: output rows normalised (Norm of LASP Eq. 2)
@@ -335,7 +335,7 @@ def bwd_norm(Q, K, V, Y, rstd, dY, chunk, decay=None, cu_seqlens=None, M_in=None
 
 def fwd_bidir(Q, K, V, chunk=256, cu_seqlens=None, M_in=None, *, want_m_out=True,
               want_state_cache=True, workspace=None, events=None, segment_chunks=0):
-    """Unmasked (bidirectional) forward, bf16: O = Q (M_in + sum_i k_i^T v_i) per
+    """Unmasked (bidirectional) forward: O = Q (M_in + sum_i k_i^T v_i) per
     sequence and head (lasp_fwd_bidir).  chunk only sets the work split.
     Returns (O, M_out, state_cache)."""
     import torch

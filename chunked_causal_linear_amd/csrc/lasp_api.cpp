@@ -109,9 +109,9 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false,
     pl.local_b = (dt == LASP_BF16 && !gated)
                      ? 0 : align_up((size_t)pl.n_chunks_ub * pl.H * dd * pl.esz);
     pl.seg_b = align_up((size_t)pl.n_segs_ub * pl.H * dd * sizeof(float));
-    // final states: the bf16 backward starts its subtraction walk of dQ from them
-    pl.fin_b = (dt == LASP_BF16 && !gated)
-                   ? align_up((size_t)pl.nseq * pl.H * dd * sizeof(float)) : 0;
+    // final states: the bf16 backward starts its subtraction walk of dQ from
+    // them, and the unmasked form's row products read them (both dtypes)
+    pl.fin_b = !gated ? align_up((size_t)pl.nseq * pl.H * dd * sizeof(float)) : 0;
     pl.gate_c = gated ? align_up((size_t)pl.n_chunks_ub * pl.H * pl.D * sizeof(float)) : 0;
     pl.gate_s = gated ? align_up((size_t)pl.n_segs_ub * pl.H * pl.D * sizeof(float)) : 0;
     pl.cache_b = pl.local_b + pl.seg_b + pl.fin_b + pl.gate_c + pl.gate_s;
@@ -275,7 +275,6 @@ int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     Plan pl;
     int rc = make_plan(shape, dtype, pl, mode == GATED, seg_chunks);
     if (rc != LASP_OK) return rc;
-    if (mode == BIDIR && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
     if (!Q || !K || !V || !O || (mode == GATED && !log_g) || (mode == NORM && !rstd))
         return LASP_EINVAL;
     if (misaligned(rstd, 4)) return LASP_EINVAL;
@@ -323,7 +322,8 @@ int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     p.Pseg = (float *)(c + pl.local_b);
     p.Pfin = pl.fin_b ? (float *)(c + pl.local_b + pl.seg_b) : nullptr;
     if (mode == BIDIR)
-        return hip_status(lasp::launch_fwd_bidir(p, true, (hipStream_t)stream, (hipEvent_t *)events));
+        return hip_status(lasp::launch_fwd_bidir(p, dtype == LASP_BF16, true, (hipStream_t)stream,
+                                                 (hipEvent_t *)events));
     if (mode == GATED) {
         p.LG = log_g;
         p.Gc = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b);
@@ -431,7 +431,6 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     Plan pl;
     int rc = make_plan(shape, dtype, pl, mode == GATED, seg_chunks);
     if (rc != LASP_OK) return rc;
-    if (mode == BIDIR && dtype != LASP_BF16) return LASP_EUNSUPPORTED;
     if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return LASP_EINVAL;
     if (mode == GATED && (!log_g || !dlog_g)) return LASP_EINVAL;
     if (mode == NORM && (!Y || !rstd)) return LASP_EINVAL;
@@ -514,12 +513,13 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     if (!cache) {   // recompute the forward states (no output, no M_out)
         p.Z = (float *)(w + pl.cache_b);
         const bool bf = dtype == LASP_BF16;
-        rc = hip_status(mode == BIDIR   ? lasp::launch_fwd_bidir(p, false, hs)
+        rc = hip_status(mode == BIDIR   ? lasp::launch_fwd_bidir(p, bf, false, hs)
                         : mode == GATED ? lasp::launch_fwd_gated(p, bf, false, hs)
                                         : lasp::launch_fwd(p, bf, false, hs));
         if (rc != LASP_OK) return rc;
     }
-    if (mode == BIDIR) return hip_status(lasp::launch_bwd_bidir(p, hs, (hipEvent_t *)events));
+    if (mode == BIDIR)
+        return hip_status(lasp::launch_bwd_bidir(p, dtype == LASP_BF16, hs, (hipEvent_t *)events));
     if (mode == GATED)
         return hip_status(lasp::launch_bwd_gated(p, dtype == LASP_BF16, hs, (hipEvent_t *)events));
     return hip_status(lasp::launch_bwd(p, dtype == LASP_BF16, hs, (hipEvent_t *)events));

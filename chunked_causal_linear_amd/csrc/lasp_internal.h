@@ -86,8 +86,8 @@ hipError_t launch_norm_bwd_prep(const Params &p, bool bf16, hipStream_t stream);
 hipError_t launch_setup(const Params &p, hipStream_t stream);
 
 // ev as for launch_fwd / launch_bwd (totals, scan, row-block products).
-hipError_t launch_fwd_bidir(const Params &p, bool with_output, hipStream_t stream,
+hipError_t launch_fwd_bidir(const Params &p, bool bf16, bool with_output, hipStream_t stream,
                             hipEvent_t *ev = nullptr);
-hipError_t launch_bwd_bidir(const Params &p, hipStream_t stream, hipEvent_t *ev = nullptr);
+hipError_t launch_bwd_bidir(const Params &p, bool bf16, hipStream_t stream, hipEvent_t *ev = nullptr);
 
 }  // namespace lasp

@@ -1701,6 +1701,76 @@ static hipError_t sweep_launch(const Params &p, hipStream_t st) {
     return launch_k(k_sweep_bf16<D, C, KIND, false>, grid, block, st, p);
 }
 
+// ---------------------------------------------------------------------------
+// Row-block products of the unmasked form in float32: the same products as
+// k_rowmat_bf16 (Out = A X over the rows of a segment part, X = the summed
+// state Pfin or Rfin, or its transpose), as 32x32x2 f32 MFMAs with both
+// operands staged in LDS with the contracted feature contiguous.  Its
+// template arguments are those of the float32 causal kernels.
+// ---------------------------------------------------------------------------
+template <int D, int KIND>
+__global__ __launch_bounds__(NTHR) void k_rowmat_f32(Params p) {
+    constexpr int BT = (D == 128) ? 32 : 64;        // rows per block
+    constexpr int V = Tr<float>::VEC;
+    constexpr int PD = D + V;                        // LDS pitch
+    constexpr int nprod = KIND == RM_BWD ? 3 : 1;
+    __shared__ __attribute__((aligned(16))) float X_s[D * PD];   // [n][k]
+    __shared__ __attribute__((aligned(16))) float A_s[BT * PD];  // [row][k]
+    using TO = Tiles<BT / 32, D / 32>;
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int prod = lid % nprod, rest0 = lid / nprod;
+    const int part = rest0 % p.parts, rest = rest0 / p.parts;
+    const int h = rest % p.H, gs = rest / p.H;
+    Seq s;
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    if (t1 <= t0) return;
+    const int seg_rows = min(t1 * p.C, s.len) - t0 * p.C;
+    const int bpp = ((seg_rows + BT - 1) / BT + p.parts - 1) / p.parts;   // blocks per part
+    const int row0 = t0 * p.C + part * bpp * BT;
+    const int nrows = min(seg_rows - part * bpp * BT, bpp * BT);
+    if (nrows <= 0) return;
+    const int64_t rbase = (row_base(p, s, h) + row0) * D;
+    const float *X = (KIND == RM_FWD || prod == 0 ? p.Pfin : p.Rfin) + ((int64_t)s.i * p.H + h) * D * D;
+    const bool trans = KIND == RM_BWD && prod != 1;            // dQ, dK use the transpose
+    const float *A;
+    float *Out;
+    if (KIND == RM_FWD) {
+        A = (const float *)p.Q + rbase; Out = (float *)p.O + rbase;
+    } else if (prod == 0) {
+        A = (const float *)p.dO + rbase; Out = (float *)p.dQ + rbase;
+    } else if (prod == 1) {
+        A = (const float *)p.K + rbase; Out = (float *)p.dV + rbase;
+    } else {
+        A = (const float *)p.V + rbase; Out = (float *)p.dK + rbase;
+    }
+    // X_s[n][k] = X[n][k], or X[k][n] for the transpose (reads of X rows
+    // coalesced either way)
+    for (int e = threadIdx.x; e < D * D; e += NTHR) {
+        const int r = e / D, c = e % D;
+        const float x = X[e];
+        if (trans) X_s[c * PD + r] = x;
+        else X_s[r * PD + c] = x;
+    }
+    for (int b0 = 0; b0 < nrows; b0 += BT) {
+        const int nv = min(BT, nrows - b0);
+        __syncthreads();   // X_s written; A_s free
+        stage_rows<float, BT, D>(A_s, PD, A + (int64_t)b0 * D, nv);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (!TO::get(k, mi, ni)) continue;
+            f32x16 acc;
+            zero(acc);
+            gemm<float, D>(acc, A_s, PD, mi * 32, X_s, PD, ni * 32);
+            store_rows(acc, Out + (int64_t)b0 * D, D, mi * 32, ni * 32, nv);
+        }
+    }
+}
+
 template <int D, int KIND>
 static hipError_t segtot_launch(const Params &p, hipStream_t st) {
     const dim3 grid(round8(p.n_segs_ub * p.H)), block(SegTotCfg<D>::NT);
@@ -1744,7 +1814,7 @@ static hipError_t bwd_bf16(const Params &p, hipStream_t st, hipEvent_t *ev) {
 }
 
 template <int D, int KIND>
-static hipError_t rowmat_launch(const Params &p0, hipStream_t st) {
+static hipError_t rowmat_launch(const Params &p0, bool bf, hipStream_t st) {
     const int prods = KIND == RM_BWD ? 3 : 1;
     // about 1024 workgroups (four per CU), parts of at least 8 tiles
     Params p = p0;
@@ -1752,51 +1822,63 @@ static hipError_t rowmat_launch(const Params &p0, hipStream_t st) {
     const int by_wg = (int)((1024 + wg - 1) / wg);
     const int by_rows = (p.G * p.C / 32) / 8;
     p.parts = by_wg < 1 ? 1 : (by_wg < by_rows ? by_wg : (by_rows < 1 ? 1 : by_rows));
+    if (!bf) return launch_k(k_rowmat_f32<D, KIND>, dim3(round8(wg * p.parts)), dim3(NTHR), st, p);
     return launch_k(k_rowmat_bf16<D, KIND>, dim3(round8(wg * p.parts)), dim3(64 * RM_NW), st, p);
 }
 
+// The summed states come from the causal path's totals and scans (bf16:
+// segment totals; float32: the per-chunk local kernels, whose chunk states go
+// unused here), then one row-block product launch.
 template <int D>
-static hipError_t fwd_bidir(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
+static hipError_t fwd_bidir(const Params &p, bool bf, bool with_output, hipStream_t st, hipEvent_t *ev) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    constexpr int BT = Block<float, D>::BT;
     if (p.varlen) LASP_TRY(launch_setup(p, st));
     LASP_TRY(rec_event(ev, 0, st));
-    LASP_TRY((segtot_launch<D, TOT_F>(p, st)));
+    if (bf)
+        LASP_TRY((segtot_launch<D, TOT_F>(p, st)));
+    else
+        LASP_TRY(launch_k(k_fwd_local<float, D, BT>, dim3(p.n_segs_ub * p.H), dim3(NTHR), st, p));
     LASP_TRY(rec_event(ev, 1, st));
     LASP_TRY(launch_k(k_fwd_segscan<D, float>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
     LASP_TRY(rec_event(ev, 2, st));
-    if (with_output) LASP_TRY((rowmat_launch<D, RM_FWD>(p, st)));
+    if (with_output) LASP_TRY((rowmat_launch<D, RM_FWD>(p, bf, st)));
     return rec_event(ev, 3, st);
 }
 
 template <int D>
-static hipError_t bwd_bidir(const Params &p, hipStream_t st, hipEvent_t *ev) {
+static hipError_t bwd_bidir(const Params &p, bool bf, hipStream_t st, hipEvent_t *ev) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    constexpr int BT = Block<float, D>::BT;
     if (p.varlen) LASP_TRY(launch_setup(p, st));
     LASP_TRY(rec_event(ev, 0, st));
-    LASP_TRY((segtot_launch<D, TOT_B>(p, st)));
+    if (bf)
+        LASP_TRY((segtot_launch<D, TOT_B>(p, st)));
+    else
+        LASP_TRY(launch_k(k_bwd_local<float, D, BT>, dim3(p.n_segs_ub * p.H), dim3(NTHR), st, p));
     LASP_TRY(rec_event(ev, 1, st));
     LASP_TRY(launch_k(k_bwd_segscan<D, float>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
     LASP_TRY(rec_event(ev, 2, st));
-    LASP_TRY((rowmat_launch<D, RM_BWD>(p, st)));
+    LASP_TRY((rowmat_launch<D, RM_BWD>(p, bf, st)));
     return rec_event(ev, 3, st);
 }
 
-hipError_t launch_fwd_bidir(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
-    if (p.decay || !p.Pfin) return hipErrorInvalidValue;
+hipError_t launch_fwd_bidir(const Params &p, bool bf, bool with_output, hipStream_t st, hipEvent_t *ev) {
+    if (p.decay || !p.Pfin || (!bf && !p.Lc)) return hipErrorInvalidValue;
     switch (p.D) {
-    case 32: return fwd_bidir<32>(p, with_output, st, ev);
-    case 64: return fwd_bidir<64>(p, with_output, st, ev);
-    case 128: return fwd_bidir<128>(p, with_output, st, ev);
+    case 32: return fwd_bidir<32>(p, bf, with_output, st, ev);
+    case 64: return fwd_bidir<64>(p, bf, with_output, st, ev);
+    case 128: return fwd_bidir<128>(p, bf, with_output, st, ev);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_bidir(const Params &p, hipStream_t st, hipEvent_t *ev) {
-    if (p.decay || !p.Pfin || !p.Rfin) return hipErrorInvalidValue;
+hipError_t launch_bwd_bidir(const Params &p, bool bf, hipStream_t st, hipEvent_t *ev) {
+    if (p.decay || !p.Pfin || !p.Rfin || (!bf && !p.Rc)) return hipErrorInvalidValue;
     switch (p.D) {
-    case 32: return bwd_bidir<32>(p, st, ev);
-    case 64: return bwd_bidir<64>(p, st, ev);
-    case 128: return bwd_bidir<128>(p, st, ev);
+    case 32: return bwd_bidir<32>(p, bf, st, ev);
+    case 64: return bwd_bidir<64>(p, bf, st, ev);
+    case 128: return bwd_bidir<128>(p, bf, st, ev);
     }
     return hipErrorInvalidValue;
 }

@@ -92,7 +92,7 @@ typedef struct {
 /* Size in bytes of the state cache written by lasp_fwd and read by lasp_bwd:
  * the states the backward pass reuses (LASP Sec. 3.2, the cached KV_{t-1}):
  * per-chunk states (fp32) or the states entering each segment of chunks, and
- * (bf16) each sequence's final state.  Depends only on the shape and dtype. */
+ * each sequence's final state.  Depends only on the shape and dtype. */
 size_t lasp_state_cache_bytes(const lasp_shape *shape, lasp_dtype dtype);
 
 /* Workspace needed by lasp_fwd / lasp_bwd.  with_state_cache != 0 means the
@@ -247,8 +247,8 @@ int lasp_bwd_norm(const lasp_shape *shape, lasp_dtype dtype,
  * Arguments, layouts, size queries (the same shape gives the same workspace
  * and state-cache sizes as lasp_fwd / lasp_bwd; shape->chunk only sets the
  * work split) and errors as for lasp_fwd / lasp_bwd; there is no decay
- * argument.  dtype must be LASP_BF16 (else LASP_EUNSUPPORTED).  The state
- * cache carries M from lasp_fwd_bidir to lasp_bwd_bidir. */
+ * argument.  Both dtypes (float32 computes the products in float32 MFMAs).
+ * The state cache carries M from lasp_fwd_bidir to lasp_bwd_bidir. */
 int lasp_fwd_bidir(const lasp_shape *shape, lasp_dtype dtype,
                    const void *Q, const void *K, const void *V,
                    const int32_t *cu_seqlens, const float *M_in,

@@ -143,8 +143,8 @@ def test_sizes_follow_the_shape(L):
 
 
 def test_bidir_rejects_bad_arguments(L):
-    """The unmasked entry points share the checks of lasp_fwd / lasp_bwd and take
-    bf16 only (every case here fails before anything is enqueued)."""
+    """The unmasked entry points share the checks of lasp_fwd / lasp_bwd (every
+    case here fails before anything is enqueued)."""
     s = Shape(1, 2, 300, 64, 128, 0)
     p = [fake(i) for i in range(12)]
     nf = L.lasp_fwd_workspace_bytes(ctypes.byref(s), 1, 0)
@@ -164,7 +164,7 @@ def test_bidir_rejects_bad_arguments(L):
                                 a["M_in"], a["dM_out"], a["cache"], a["dQ"], a["dK"], a["dV"],
                                 a["dM_in"], a["ws"], ws_bytes, None)
 
-    assert fwd(dt=0) == EUNSUP and bwd(dt=0) == EUNSUP          # float32: not in this form
+    assert fwd(dt=2) == EUNSUP and bwd(dt=2) == EUNSUP          # no such dtype
     assert fwd(shape=Shape(1, 2, 300, 48, 128, 0)) == EUNSUP
     assert fwd(O=None) == EINVAL and bwd(dV=None) == EINVAL
     assert fwd(O=p[1]) == EINVAL and bwd(dK=p[0]) == EINVAL    # output aliases an input
