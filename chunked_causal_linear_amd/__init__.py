@@ -8,7 +8,7 @@ The binding raises if the library is missing: there is no fallback path.
   bwd(Q, K, V, dO, chunk, ...) -> (dQ, dK, dV, dM_in)
   fwd_bidir / bwd_bidir: the unmasked (bidirectional) form, no decay
   fwd_gated / bwd_gated: per-token, per-key-channel gates (log-gates in, their
-                         gradient out), chunk 64
+                         gradient out); the kernels use 64-token chunks
   fwd_norm / bwd_norm: output rows normalised (Norm of LASP Eq. 2)
   autograd (submodule): lasp_attention, lasp_gated_attention and
                         lasp_bidir_attention as torch.autograd.Functions

@@ -38,8 +38,9 @@ struct Plan {
     size_t cache_b;      // state cache = [Lc][Pseg][Pfin][Gc][Gs]
 };
 
-// gated: the per-channel gated form (chunk 64).  seg_chunks: 0, or the
-// number of chunks per segment to use instead of the library's choice.
+// gated: the per-channel gated form (its kernels use chunks of 64 tokens
+// whatever shape->chunk names).  seg_chunks: 0, or the number of chunks per
+// segment to use instead of the library's choice.
 int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false,
               int seg_chunks = 0) {
     if (!s) return LASP_EINVAL;
@@ -49,16 +50,18 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false,
     if (dt != LASP_FP32 && dt != LASP_BF16) return LASP_EUNSUPPORTED;
     if (s->d != 32 && s->d != 64 && s->d != 128) return LASP_EUNSUPPORTED;
     if (s->chunk != 64 && s->chunk != 128 && s->chunk != 256) return LASP_EUNSUPPORTED;
-    if (gated && s->chunk != 64) return LASP_EUNSUPPORTED;
     if (seg_chunks < 0 || seg_chunks > (1 << 20)) return LASP_EINVAL;
+    // the gated kernels always work on chunks of 64 tokens (the result does
+    // not depend on the chunking; shape->chunk only names a supported length)
+    const int chunk = gated ? 64 : s->chunk;
     pl.D = s->d;
-    pl.C = s->chunk;
+    pl.C = chunk;
     pl.H = s->H;
     pl.varlen = s->nseq > 0;
     pl.nseq = pl.varlen ? s->nseq : s->B;
     pl.esz = dt == LASP_BF16 ? 2 : 4;
-    const int64_t per_seq_chunks = ((int64_t)s->N + s->chunk - 1) / s->chunk;
-    int64_t chunks_ub = pl.varlen ? (int64_t)s->N / s->chunk + s->nseq
+    const int64_t per_seq_chunks = ((int64_t)s->N + chunk - 1) / chunk;
+    int64_t chunks_ub = pl.varlen ? (int64_t)s->N / chunk + s->nseq
                                   : per_seq_chunks * (int64_t)s->B;
     // Segments of G chunks: one sweep workgroup each per (segment, head, role),
     // one resident per CU (256 CUs on MI355X), each taking a time about

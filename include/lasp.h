@@ -291,8 +291,9 @@ int lasp_bwd_bidir_ex(const lasp_shape *shape, lasp_dtype dtype,
  *           overflow.
  * The backward, for l = <dO, O> + <dM_out, M_out>, also returns
  *   dlog_g  device float32 [B, H, N, d]: dl/d(log g_p).
- * Restriction: shape->chunk must be 64, the kernels' chunk length (else
- * LASP_EUNSUPPORTED).  Numbers: inside a chunk
+ * Chunking: the gated kernels work on chunks of 64 tokens whatever supported
+ * length shape->chunk names (64, 128 or 256: the result does not depend on
+ * it); sizes and segment_chunks count 64-token chunks.  Numbers: inside a chunk
  * the gates enter the bf16 MFMA operands as factors 2^(b_s - b_m) and
  * 2^(b_m - b_i) (b: running log2 of the gates; m: the first row of a 32-row
  * query tile), each at most 1 off the diagonal tiles; a diagonal tile whose

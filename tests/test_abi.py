@@ -173,8 +173,9 @@ def test_bidir_rejects_bad_arguments(L):
 
 
 def test_gated_rejects_bad_arguments(L):
-    """The gated entry points: chunk 64 only, log_g
-    (and dlog_g) required, aligned and disjoint from the outputs."""
+    """The gated entry points: chunks of 64 tokens whatever supported length the
+    shape names (sizes equal for 64, 128, 256), log_g (and dlog_g) required,
+    aligned and disjoint from the outputs."""
     s = Shape(1, 2, 300, 64, 64, 0)
     p = [fake(i) for i in range(14)]
     nf = L.lasp_gated_fwd_workspace_bytes(ctypes.byref(s), 1, 0)
@@ -197,10 +198,17 @@ def test_gated_rejects_bad_arguments(L):
                                 a["dV"], a["dLG"], a["dM_in"], a["ws"], ws_bytes, None)
 
     for c in (128, 256):
+        sc = Shape(1, 2, 300, 64, c, 0)
+        for dt in (0, 1):
+            for q in (L.lasp_gated_state_cache_bytes,):
+                assert q(ctypes.byref(sc), dt) == q(ctypes.byref(s), dt)
+            for q in (L.lasp_gated_fwd_workspace_bytes, L.lasp_gated_bwd_workspace_bytes):
+                assert q(ctypes.byref(sc), dt, 0) == q(ctypes.byref(s), dt, 0)
+                assert q(ctypes.byref(sc), dt, 1) == q(ctypes.byref(s), dt, 1)
+    for c in (32, 96, 512):
         assert fwd(shape=Shape(1, 2, 300, 64, c, 0)) == EUNSUP
         assert bwd(shape=Shape(1, 2, 300, 64, c, 0)) == EUNSUP
     assert fwd(shape=Shape(1, 2, 300, 48, 64, 0)) == EUNSUP
-    assert L.lasp_gated_state_cache_bytes(ctypes.byref(Shape(1, 2, 300, 128, 128, 0)), 1) == 0
     for dt in (0, 1):
         assert L.lasp_gated_state_cache_bytes(ctypes.byref(Shape(1, 2, 300, 128, 64, 0)), dt) > 0
     assert fwd(LG=None) == EINVAL and bwd(LG=None) == EINVAL and bwd(dLG=None) == EINVAL

@@ -128,10 +128,28 @@ def test_constant_gates_match_the_decayed_path():
 
 
 def test_gated_rejects_bad_configurations():
-    inp = make_inputs(small("bf16 C128", "bf16", B=1, H=1, N=64, d=64, seed=74, gates="gla"))
+    inp = make_inputs(small("bf16 C96", "bf16", B=1, H=1, N=64, d=64, seed=74, gates="gla"))
     with pytest.raises(cca.LaspError) as e:
-        cca.fwd_gated(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(inp["log_g"]), 128)
+        cca.fwd_gated(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(inp["log_g"]), 96)
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("chunk", [128, 256])
+def test_gated_other_chunk_lengths_equal_64(chunk):
+    """The gated kernels work on 64-token chunks whatever supported length the
+    call names: chunk 128 and 256 give the bits of chunk 64 (and so the oracle's
+    values at the parity bar)."""
+    import dataclasses
+    w = small("gated bf16 d64 ragged Min dMout", "bf16", B=2, H=2, N=300, d=64, chunk=64, seed=75,
+              gates="mixed", m_in_scale=0.1, dm_out_scale=0.1)
+    inp = make_inputs(w)
+    say("case: gated chunk", chunk)
+    a = run_gated(inp)
+    inp_c = dict(inp, shape=dict(inp["shape"], chunk=chunk))
+    b = run_gated(inp_c)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    check("gated chunk %d" % chunk, b, oracle_gated(inp), TOL["bf16"])
 
 
 def test_gated_full_size_sampled():
