@@ -663,19 +663,26 @@ template <int N> struct IC { static constexpr int value = N; };
 // Rows out of a 32-row output tile accumulated transposed: acc[nt] holds
 // [feature nt*32 + crow(e)][row lane%32], i.e. each lane holds 4-feature
 // pieces of one row.  Lanes l and l+32 exchange halves (permlane32 swap) so
-// that each lane holds two 8-feature pieces of its row, stored with 16-byte
-// stores: lanes < 32 features 0-7 and 16-23 of a 32-feature block, lanes >= 32
-// features 8-15 and 24-31.  The stores go through a buffer descriptor that
-// covers exactly the tile's `rows` valid rows (none when rows <= 0): the
-// hardware drops stores past its end, so every wave issues the same NDT*2
-// stores and the count of memory operations in flight after them is known.
-// neg = 0x80008000 flips the sign of every packed bf16 pair.
+// that each lane holds two 8-feature pieces of its row: lanes < 32 features
+// 0-7 and 16-23 of a 32-feature block, lanes >= 32 features 8-15 and 24-31.
+// A second exchange between neighbouring 16-lane rows (permlane16 swap: the
+// odd rows of the first operand with the even rows of the second) gathers,
+// in the first register group, the four 16-byte pieces of the block for rows
+// 0-15 and, in the second, those of rows 16-31: lane l then writes row l%16
+// (+16) at byte 16 * (2 (l/16 % 2) + l/32) of the block, so that each 16-byte
+// store covers 16 rows x 64 contiguous bytes rather than 32 rows x 32.  The
+// stores go through a buffer descriptor that covers exactly the tile's `rows`
+// valid rows (none when rows <= 0): the hardware drops stores past its end,
+// so every wave issues the same NDT*2 stores and the count of memory
+// operations in flight after them is known.  neg = 0x80008000 flips the sign
+// of every packed bf16 pair.
 template <int D>
 __device__ __forceinline__ void store_tile_t(const f32x16 *acc, bf16 *tile, int rows, int lz, unsigned neg) {
     constexpr int NDT = D / 32;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         tile, 0, __builtin_amdgcn_readfirstlane(rows > 0 ? rows * D * 2 : 0), 0x00020000);
-    const int off = ((lz & 31) * D + (lz >> 5) * 8) * 2;
+    const int g = lz >> 4;
+    const int off = (lz & 15) * D * 2 + 16 * ((g & 1) * 2 + (g >> 1));
 #pragma unroll
     for (int nt = 0; nt < NDT; ++nt) {
         typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -695,9 +702,16 @@ __device__ __forceinline__ void store_tile_t(const f32x16 *acc, bf16 *tile, int 
                 r[q + 2 + e] = x[1];
             }
         }
+        // r[0..3]: features 0-7 (lanes < 32) or 8-15; r[4..7]: 16-23 or 24-31
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const auto x = __builtin_amdgcn_permlane16_swap(r[e], r[4 + e], false, false);
+            r[e] = x[0];
+            r[4 + e] = x[1];
+        }
         const u32x4_t v0 = {r[0], r[1], r[2], r[3]}, v1 = {r[4], r[5], r[6], r[7]};
         __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off + nt * 64, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off + nt * 64 + 32, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off + 16 * D * 2 + nt * 64, 0, 0);
     }
 }
 
