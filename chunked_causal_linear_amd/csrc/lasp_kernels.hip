@@ -850,6 +850,15 @@ enum SweepKind {
     SWEEP_DVDK = 3,    // roles 2-3
     SWEEP_OUT_NORM = 4 // role 0, rows normalised (Norm of LASP Eq. 2) in the store
 };
+// The role of a sweep workgroup from its index within the launch's roles:
+// fixed at compile time, or the launch's first role plus that index.
+template <int R> struct FixedRole {
+    __device__ constexpr int operator()(int) const { return R; }
+};
+struct RoleOf {
+    int first;
+    __device__ int operator()(int sel) const { return first + sel; }
+};
 // DEC = false: the call has no decay array (every lambda is 1); the decay
 // arithmetic is compiled out.
 template <int D, int C, int KIND, bool DEC>
@@ -873,8 +882,14 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     __shared__ __attribute__((aligned(16))) bf16 BG1[NG * 2 * TILE];
 
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int role = role0 + lid % nroles;
+    const int rsel = lid % nroles;
     const int rest = lid / nroles;
+    // The body, once per role with the role a compile-time constant (FixedRole)
+    // for the three-role launch, which then gets registers sized for each
+    // role's own code; the other launches keep one body (RoleOf): for the
+    // decayed dV + dK launch two specialised bodies needed more registers.
+    auto body = [&](auto RS) __attribute__((always_inline)) {
+    const int role = RS(rsel);
     const int h = rest % p.H, gs = rest / p.H;
     Seq s;
     int sl;
@@ -1274,6 +1289,14 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         store_tile_t<D>(acc, Out + ((int64_t)t * p.C + rt * 32) * D, rt >= 0 ? Ct - rt * 32 : 0,
                         opaque_lane(), sub ? 0x80008000u : 0u);
         if (upd) write_state();
+    }
+    };
+    if constexpr (KIND == SWEEP_GRADS) {
+        if (rsel == 0) body(FixedRole<1>());
+        else if (rsel == 1) body(FixedRole<2>());
+        else body(FixedRole<3>());
+    } else {
+        body(RoleOf{role0});
     }
 }
 
