@@ -152,6 +152,8 @@ __global__ __launch_bounds__(NTHR) void k_fwd_local(Params p) {
 //   Pseg[0] = M_in;  Pseg[s+1] = lambda^len_s Pseg[s] + Z[s];  M_out = Pfin = last.
 // (LASP-2 prefix sum of gathered states; LASP Alg. 2 receive/send as a scan.)
 // ---------------------------------------------------------------------------
+constexpr int SCAN_BATCH = 8;   // segment totals loaded per round trip in the scans
+
 template <int D, typename T>
 __global__ __launch_bounds__(NTHR) void k_fwd_segscan(Params p) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
@@ -167,11 +169,23 @@ __global__ __launch_bounds__(NTHR) void k_fwd_segscan(Params p) {
     float P = p.M_in ? p.M_in[mo] : 0.f;
     const int seg_tokens = p.G * p.C;
     const int nS = min(s.S, p.n_segs_ub - s.s0);
-    for (int sl = 0; sl < nS; ++sl) {
-        const int64_t idx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D + e;
-        ((T *)p.Pseg)[idx] = fromf<T>(P);
-        const int len_s = min(seg_tokens, s.len - sl * seg_tokens);
-        P = dpow(l2, (float)len_s) * P + p.Z[idx];
+    // the totals are loaded SCAN_BATCH segments at a time, ahead of the
+    // stores: one memory latency per batch instead of one per segment
+    for (int b0 = 0; b0 < nS; b0 += SCAN_BATCH) {
+        float z[SCAN_BATCH];
+#pragma unroll
+        for (int j = 0; j < SCAN_BATCH; ++j)
+            z[j] = b0 + j < nS ? p.Z[((int64_t)(s.s0 + b0 + j) * p.H + h) * D * D + e] : 0.f;
+#pragma unroll
+        for (int j = 0; j < SCAN_BATCH; ++j) {
+            const int sl = b0 + j;
+            if (sl < nS) {
+                const int64_t idx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D + e;
+                ((T *)p.Pseg)[idx] = fromf<T>(P);
+                const int len_s = min(seg_tokens, s.len - sl * seg_tokens);
+                P = dpow(l2, (float)len_s) * P + z[j];
+            }
+        }
     }
     if (p.M_out) p.M_out[mo] = P;
     if (p.Pfin) p.Pfin[(int64_t)ih * D * D + e] = P;
@@ -370,11 +384,21 @@ __global__ __launch_bounds__(NTHR) void k_bwd_segscan(Params p) {
     float R = p.dM_out ? p.dM_out[mo] : 0.f;
     const int seg_tokens = p.G * p.C;
     const int nS = min(s.S, p.n_segs_ub - s.s0);
-    for (int sl = nS - 1; sl >= 0; --sl) {
-        const int64_t idx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D + e;
-        ((T *)p.Rseg)[idx] = fromf<T>(R);
-        const int len_s = min(seg_tokens, s.len - sl * seg_tokens);
-        R = dpow(l2, (float)len_s) * R + p.W[idx];
+    for (int b0 = nS - 1; b0 >= 0; b0 -= SCAN_BATCH) {   // batches as in the forward scan
+        float wv[SCAN_BATCH];
+#pragma unroll
+        for (int j = 0; j < SCAN_BATCH; ++j)
+            wv[j] = b0 - j >= 0 ? p.W[((int64_t)(s.s0 + b0 - j) * p.H + h) * D * D + e] : 0.f;
+#pragma unroll
+        for (int j = 0; j < SCAN_BATCH; ++j) {
+            const int sl = b0 - j;
+            if (sl >= 0) {
+                const int64_t idx = ((int64_t)(s.s0 + sl) * p.H + h) * D * D + e;
+                ((T *)p.Rseg)[idx] = fromf<T>(R);
+                const int len_s = min(seg_tokens, s.len - sl * seg_tokens);
+                R = dpow(l2, (float)len_s) * R + wv[j];
+            }
+        }
     }
     if (p.dM_in) p.dM_in[mo] = R;
     if (p.Rfin) p.Rfin[(int64_t)ih * D * D + e] = R;
@@ -1319,7 +1343,10 @@ template <int D> struct SegTotCfg {
     static constexpr int TILE = 32 * D;                            // elements of one 32-token tile
     static constexpr int TPS = 2;                                  // tiles per step (one barrier each)
     static constexpr int SLOT = 2 * TILE * TPS;                    // U tiles, W tiles of one step
-    static constexpr int NSLOT = (160 * 1024) / (SLOT * 2);        // slots in 160 KiB of LDS
+    // slots in 160 KiB of LDS at d = 128; in 80 KiB at smaller d, whose
+    // segments are short (packed batches): two workgroups then share a CU and
+    // one's ring fill overlaps the other's stream (totals -12 % at d = 64)
+    static constexpr int NSLOT = ((D == 128 ? 160 : 80) * 1024) / (SLOT * 2);
     static constexpr int CPT = TILE / 512;                         // 1 KiB wave copies per tile
     static constexpr int CPS = 2 * CPT * TPS;                      // copies per slot
     static constexpr int CPW = (CPS + NW - 1) / NW;                // copies per wave per slot (at most)
