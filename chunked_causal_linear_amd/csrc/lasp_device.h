@@ -67,6 +67,17 @@ inline hipError_t rec_event(hipEvent_t *ev, int i, hipStream_t st) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// A buffer descriptor for `bytes` bytes from p, made from lane 0's address and
+// size: every caller passes an address and size that are the same on all
+// lanes of the wave, and saying so spares the compiler a loop over lanes
+// around each buffer access.  Stores past `bytes` are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_buffer(const void *p, int bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)u, 0, __builtin_amdgcn_readfirstlane(bytes),
+                                             0x00020000);
+}
 // Row (within the 32x32 tile) of accumulator element r for this lane.
 __device__ __forceinline__ int crow(int r, int l = threadIdx.x & 63) {
     return (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);

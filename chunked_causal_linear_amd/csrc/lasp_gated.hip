@@ -271,9 +271,7 @@ __device__ __forceinline__ void store_tile1_t(const f32x16 &acc, bf16 *G, int ld
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
     const int rows = nrow - m0;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        G + (int64_t)m0 * ld + n0, 0, __builtin_amdgcn_readfirstlane(rows > 0 ? rows * ld * 2 : 0),
-        0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = wave_buffer(G + (int64_t)m0 * ld + n0, rows > 0 ? rows * ld * 2 : 0);
     const int l = lane_id();
     const int off = ((l & 31) * ld + (l >> 5) * 8) * 2;
     unsigned r[8];   // r[2j], r[2j+1]: columns 8j + 4*(lane/32) + [0,4), packed

@@ -703,8 +703,7 @@ template <int N> struct IC { static constexpr int value = N; };
 template <int D>
 __device__ __forceinline__ void store_tile_t(const f32x16 *acc, bf16 *tile, int rows, int lz, unsigned neg) {
     constexpr int NDT = D / 32;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        tile, 0, __builtin_amdgcn_readfirstlane(rows > 0 ? rows * D * 2 : 0), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = wave_buffer(tile, rows > 0 ? rows * D * 2 : 0);
     const int g = lz >> 4;
     const int off = (lz & 15) * D * 2 + 16 * ((g & 1) * 2 + (g >> 1));
 #pragma unroll
