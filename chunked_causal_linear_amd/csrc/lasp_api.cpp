@@ -33,9 +33,9 @@ struct Plan {
     size_t local_b;      // per-chunk local states (Lc or Rc)
     size_t seg_b;        // per-segment f32 states (Pseg, Z, Rseg or W)
     size_t fin_b;        // per-sequence f32 final states (Pfin)
-    size_t gate_c;       // gated form: per-chunk f32 gate products (Gc, Hc)
+    size_t chunk_v;      // gated backward: per-chunk f32 vectors of D (Tq)
     size_t gate_s;       // gated form: per-segment f32 gate products (Gs)
-    size_t cache_b;      // state cache = [Lc][Pseg][Pfin][Gc][Gs]
+    size_t cache_b;      // state cache = [Lc][Pseg][Pfin][Gs]
 };
 
 // gated: the per-channel gated form (its kernels use chunks of 64 tokens
@@ -107,17 +107,18 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false,
     pl.n_segs_ub = (int)segs_ub;
     const size_t dd = (size_t)pl.D * pl.D;
     pl.table_b = pl.varlen ? align_up(2 * sizeof(int32_t) * ((size_t)pl.nseq + 1)) : 0;
-    // per-chunk local states: only the float32 and gated paths keep them (the
-    // bf16 path recomputes chunk states inside its segment sweep)
-    pl.local_b = (dt == LASP_BF16 && !gated)
+    // per-chunk local states: only the float32 causal path keeps them (the bf16
+    // path and the gated walks carry chunk states in registers)
+    pl.local_b = (dt == LASP_BF16 || gated)
                      ? 0 : align_up((size_t)pl.n_chunks_ub * pl.H * dd * pl.esz);
     pl.seg_b = align_up((size_t)pl.n_segs_ub * pl.H * dd * sizeof(float));
     // final states: the bf16 backward starts its subtraction walk of dQ from
-    // them, and the unmasked form's row products read them (both dtypes)
-    pl.fin_b = !gated ? align_up((size_t)pl.nseq * pl.H * dd * sizeof(float)) : 0;
-    pl.gate_c = gated ? align_up((size_t)pl.n_chunks_ub * pl.H * pl.D * sizeof(float)) : 0;
+    // them, the unmasked form's row products read them, and the gated
+    // backward's log-gate gradient of a sequence's last segment (both dtypes)
+    pl.fin_b = align_up((size_t)pl.nseq * pl.H * dd * sizeof(float));
+    pl.chunk_v = gated ? align_up((size_t)pl.n_chunks_ub * pl.H * pl.D * sizeof(float)) : 0;
     pl.gate_s = gated ? align_up((size_t)pl.n_segs_ub * pl.H * pl.D * sizeof(float)) : 0;
-    pl.cache_b = pl.local_b + pl.seg_b + pl.fin_b + pl.gate_c + pl.gate_s;
+    pl.cache_b = pl.local_b + pl.seg_b + pl.fin_b + pl.gate_s;
     return LASP_OK;
 }
 
@@ -126,7 +127,7 @@ size_t fwd_ws(const Plan &pl, bool cache) {
 }
 size_t bwd_ws(const Plan &pl, bool cache) {
     return pl.table_b + pl.local_b /*Rc*/ + 2 * pl.seg_b /*Rseg, W*/ + pl.fin_b /*Rfin*/ +
-           pl.gate_c /*Hc*/ +
+           pl.chunk_v /*Tq*/ +
            (cache ? 0 : pl.cache_b + pl.seg_b /*Lc, Pseg, Pfin, Z*/);
 }
 
@@ -329,8 +330,7 @@ int fwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
                                                  (hipEvent_t *)events));
     if (mode == GATED) {
         p.LG = log_g;
-        p.Gc = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b);
-        p.Gs = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b + pl.gate_c);
+        p.Gs = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b);
         return hip_status(lasp::launch_fwd_gated(p, dtype == LASP_BF16, true, (hipStream_t)stream,
                                                  (hipEvent_t *)events));
     }
@@ -490,8 +490,8 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     w += pl.seg_b;
     p.Rfin = pl.fin_b ? (float *)w : nullptr;
     w += pl.fin_b;
-    p.Hc = pl.gate_c ? (float *)w : nullptr;
-    w += pl.gate_c;
+    p.Tq = pl.chunk_v ? (float *)w : nullptr;
+    w += pl.chunk_v;
     p.LG = log_g;
     p.dLG = dlog_g;
     const hipStream_t hs = (hipStream_t)stream;
@@ -499,10 +499,7 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     p.Lc = pl.local_b ? c : nullptr;
     p.Pseg = (float *)(c + pl.local_b);
     p.Pfin = pl.fin_b ? (float *)(c + pl.local_b + pl.seg_b) : nullptr;
-    if (mode == GATED) {
-        p.Gc = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b);
-        p.Gs = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b + pl.gate_c);
-    }
+    if (mode == GATED) p.Gs = (float *)(c + pl.local_b + pl.seg_b + pl.fin_b);
     if (mode == NORM) {   // the gradient of the un-normalised output, into the workspace's end
         p.Yn = Y;
         p.dYn = dO;

@@ -267,10 +267,9 @@ struct One {
 // contraction index contiguous (pitches pa, pb in elements).
 template <typename T, int K>
 __device__ __forceinline__ void gemm(f32x16 &acc, const T *As, int pa, int m0, const T *Bs,
-                                     int pb, int n0) {
+                                     int pb, int n0, int l = lane_id()) {
     constexpr int V = Tr<T>::VEC;
     using Fr = typename Tr<T>::frag;
-    const int l = lane_id();
     const T *ap = As + (m0 + (l & 31)) * pa + (l >> 5) * V;
     const T *bp = Bs + (n0 + (l & 31)) * pb + (l >> 5) * V;
 #pragma unroll
@@ -303,11 +302,11 @@ struct Ident {
 // G[(m0+row)][n0+col] = acc for rows < nvalid (row-major global store).
 template <typename T>
 __device__ __forceinline__ void store_rows(const f32x16 &acc, T *G, int64_t ld, int m0, int n0,
-                                           int nvalid) {
-    const int col = lane_id() & 31;
+                                           int nvalid, int l = lane_id()) {
+    const int col = l & 31;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int row = m0 + crow(r);
+        const int row = m0 + crow(r, l);
         if (row < nvalid) G[(int64_t)row * ld + n0 + col] = fromf<T>(acc[r]);
     }
 }
@@ -317,8 +316,8 @@ template <int MT, int NT>
 struct Tiles {
     static constexpr int N = MT * NT;
     static constexpr int PER_WAVE = (N + NWAVE - 1) / NWAVE;
-    __device__ static bool get(int k, int &mi, int &ni) {
-        const int tile = wave_id() + k * NWAVE;
+    __device__ static bool get(int k, int &mi, int &ni, int w = wave_id()) {
+        const int tile = w + k * NWAVE;
         mi = tile / NT;
         ni = tile % NT;
         return tile < N;

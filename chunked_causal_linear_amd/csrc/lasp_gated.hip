@@ -36,6 +36,17 @@ constexpr float SPAN2 = 80.f;     // largest log2-gate drop inside a factorised 
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The thread's index and lane, opaque to the compiler: the offsets derived
+// from them are formed where they are used instead of being hoisted out of the
+// chunk loops and kept in registers across them.
+__device__ __forceinline__ int otid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+__device__ __forceinline__ int olane() { return otid() & 63; }
+__device__ __forceinline__ int owave() { return __builtin_amdgcn_readfirstlane(otid() >> 6); }
+
 // bS[r][c] = log2(g_0 ... g_r) for channel c of the chunk whose first log-gate
 // row is lg; rows at or past Ct repeat the last valid one (gate 1).  All
 // threads take part: NTHR / D parts of the rows per channel, each summed in
@@ -49,21 +60,25 @@ template <int D> struct LogRows {
 template <int D>
 __device__ __forceinline__ void cumlog_load(LogRows<D> &lr, const float *lg, int Ct) {
     constexpr int RP = LogRows<D>::RP;
-    const int c = threadIdx.x % D, r0 = (threadIdx.x / D) * RP;
+    const int c = otid() % D, r0 = (otid() / D) * RP;
     // the thread's offset, opaque to the compiler: the loads' addresses are
     // then formed here, not hoisted out of the caller's loop into registers
-    int off = r0 * D + c;
+    // (a buffer over the chunk's Ct valid rows: loads past them return zero,
+    // so the loads need no branches; every offset sits in the per-lane operand,
+    // which the range check covers)
+    int off = (r0 * D + c) * 4;
     asm volatile("" : "+v"(off));
-    const float *src = lg + off;
+    const __amdgpu_buffer_rsrc_t rs = wave_buffer(lg, Ct > 0 ? Ct * D * 4 : 0);
 #pragma unroll
-    for (int j = 0; j < RP; ++j) lr.x[j] = r0 + j < Ct ? src[j * D] : 0.f;
+    for (int j = 0; j < RP; ++j)
+        lr.x[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off + j * D * 4, 0, 0));
 }
 
 template <int D>
 __device__ __forceinline__ void cumlog_scan(float *bS, const LogRows<D> &lr) {
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr int RP = LogRows<D>::RP;
-    const int c = threadIdx.x % D, r0 = (threadIdx.x / D) * RP;
+    const int c = otid() % D, r0 = (otid() / D) * RP;
     float x[RP];
     x[0] = lr.x[0] * LOG2E;
 #pragma unroll
@@ -75,38 +90,6 @@ __device__ __forceinline__ void cumlog_scan(float *bS, const LogRows<D> &lr) {
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < RP; ++j) bS[(r0 + j) * D + c] = x[j] + off;
-}
-
-// The same in blocks of 16 rows (fewer registers live; the kernels that use
-// it keep their other tiles in registers meanwhile).
-template <int D>
-__device__ __forceinline__ void chunk_cumlog(float *bS, const float *lg, int Ct) {
-    constexpr float LOG2E = 1.4426950408889634f;
-    constexpr int RP = LogRows<D>::RP, B = RP < 16 ? RP : 16;
-    const int c = threadIdx.x % D, r0 = (threadIdx.x / D) * RP;
-    float run = 0.f;
-#pragma unroll
-    for (int b0 = 0; b0 < RP; b0 += B) {
-        float x[B];
-#pragma unroll
-        for (int j = 0; j < B; ++j) {
-            const int r = r0 + b0 + j;
-            x[j] = r < Ct ? lg[(int64_t)r * D + c] * LOG2E : 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < B; ++j) {
-            run += x[j];
-            bS[(r0 + b0 + j) * D + c] = run;
-        }
-    }
-    __syncthreads();
-    float off = 0.f;
-    for (int q = RP - 1; q < r0; q += RP) off += bS[q * D + c];
-    __syncthreads();
-    if (off != 0.f) {
-#pragma unroll 8
-        for (int j = 0; j < RP; ++j) bS[(r0 + j) * D + c] += off;
-    }
 }
 
 // 16 bytes of V converted values at p.
@@ -147,16 +130,24 @@ __device__ __forceinline__ void unpack16(const uint4 &v, float *f, const bf16 *)
     }
 }
 
+// (src is the chunk's first row, the same on every lane; the loads go through a
+// buffer over its Ct valid rows, so rows at or past Ct read as zero without
+// branches)
 template <typename T, int D, int R, typename RowF>
 __device__ __forceinline__ void raw_load(Raw<T, D, R> &raw, const T *src, int Ct, RowF row) {
     using RW = Raw<T, D, R>;
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t rs = wave_buffer(src, Ct > 0 ? Ct * D * (int)sizeof(T) : 0);
 #pragma unroll
     for (int u = 0; u < RW::IT; ++u) {
-        const int i = u * NTHR + threadIdx.x;
+        const int i = u * NTHR + otid();
         const int j = i / RW::PR, c = (i % RW::PR) * RW::V;
-        const int r = row(j);
-        raw.v[u] = (i < RW::N && r < Ct) ? *(const uint4 *)(src + (int64_t)r * D + c)
-                                         : make_uint4(0u, 0u, 0u, 0u);
+        if (i < RW::N) {
+            const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, (row(j) * D + c) * (int)sizeof(T), 0, 0);
+            raw.v[u] = make_uint4(x[0], x[1], x[2], x[3]);
+        } else {
+            raw.v[u] = make_uint4(0u, 0u, 0u, 0u);
+        }
     }
 }
 
@@ -168,7 +159,7 @@ __device__ __forceinline__ void raw_store_map(const Raw<T, D, R> &raw, T *dst, i
     constexpr int V = RW::V;
 #pragma unroll
     for (int u = 0; u < RW::IT; ++u) {
-        const int i = u * NTHR + threadIdx.x;
+        const int i = u * NTHR + otid();
         if (i >= RW::N) continue;
         const int j = i / RW::PR, c = (i % RW::PR) * V;
         const int dj = dst_row(j);
@@ -202,7 +193,7 @@ __device__ __forceinline__ void raw_store_sw(const Raw<bf16, D, R> &raw, bf16 *d
     constexpr int V = RW::V;
 #pragma unroll
     for (int u = 0; u < RW::IT; ++u) {
-        const int i = u * NTHR + threadIdx.x;
+        const int i = u * NTHR + otid();
         if (i >= RW::N) continue;
         const int j = i / RW::PR, c = (i % RW::PR) * V;
         const int dj = dst_row(j);
@@ -225,28 +216,16 @@ __device__ __forceinline__ void gemm_cc(f32x16 &acc, const bf16 *X, int m0, cons
         mma(acc, frag_cols_sw<D, false>(X, fo, k, m0), frag_cols_sw<D, false>(Y, fo, k, n0));
 }
 
-// acc += A[m0 + i][k] Y[k][n0 + j] summed over k < K: A bf16 rows with the
-// contraction index contiguous (pitch pa), Y a swizzled bf16 tile whose rows
-// are the contraction index (transpose reads).
-template <int D, int K>
-__device__ __forceinline__ void gemm_rc(f32x16 &acc, const bf16 *A, int pa, int m0, const bf16 *Y,
-                                        int n0, const FragOffs<D> &fo, int y0 = 0) {
-    // (Y's rows y0 .. y0 + K - 1; y0 a multiple of 16)
-    const int l = lane_id();
-    const bf16 *ap = A + (m0 + (l & 31)) * pa + (l >> 5) * 8;
-#pragma unroll
-    for (int k = 0; k < K; k += 16)
-        mma(acc, *(const bf16x8_t *)(ap + k), frag_cols_sw<D, false>(Y, fo, y0 + k, n0));
-}
-
-// Transposed accumulation (bf16): the same products as gemm / gemm_rc with the
-// MFMA operands swapped, so that acc holds the 32x32 tile transposed (lane =
-// output row, its 16 values = columns crow(r)); store_tile1_t then writes it
-// with 16-byte stores.
+// Transposed accumulation (bf16): acc += A[m0 + i][k] B[n0 + j][k] (gemm_t: A
+// and B rows with the contraction index contiguous) or A[m0 + i][k] Y[k][n0 + j]
+// (gemm_rc_t: Y a swizzled tile whose rows are the contraction index, read
+// transposed) with the MFMA operands swapped, so that acc holds the 32x32 tile
+// transposed (lane = output row, its 16 values = columns crow(r));
+// store_tile1_t then writes it with 16-byte stores.
 template <int K>
 __device__ __forceinline__ void gemm_t(f32x16 &acc, const bf16 *As, int pa, int m0, const bf16 *Bs,
                                        int pb, int n0) {
-    const int l = lane_id();
+    const int l = olane();
     const bf16 *ap = As + (m0 + (l & 31)) * pa + (l >> 5) * 8;
     const bf16 *bp = Bs + (n0 + (l & 31)) * pb + (l >> 5) * 8;
 #pragma unroll
@@ -255,12 +234,45 @@ __device__ __forceinline__ void gemm_t(f32x16 &acc, const bf16 *As, int pa, int 
 }
 template <int D, int K>
 __device__ __forceinline__ void gemm_rc_t(f32x16 &acc, const bf16 *A, int pa, int m0, const bf16 *Y,
-                                          int n0, const FragOffs<D> &fo) {
-    const int l = lane_id();
+                                          int n0, const FragOffs<D> &fo, int y0 = 0) {
+    // (Y's rows y0 .. y0 + K - 1; y0 a multiple of 16)
+    const int l = olane();
     const bf16 *ap = A + (m0 + (l & 31)) * pa + (l >> 5) * 8;
 #pragma unroll
     for (int k = 0; k < K; k += 16)
-        mma(acc, frag_cols_sw<D, false>(Y, fo, k, n0), *(const bf16x8_t *)(ap + k));
+        mma(acc, frag_cols_sw<D, false>(Y, fo, y0 + k, n0), *(const bf16x8_t *)(ap + k));
+}
+
+// Rows m0 + lane%32 (those below nrow), columns n0 .. n0+31 of G (row pitch
+// ld, float32 or bf16) from a transposed accumulator: the lane's 4 groups of
+// 4 consecutive columns, one store each.
+template <typename T>
+__device__ __forceinline__ void store_rows_t(const f32x16 &acc, T *G, int ld, int m0, int n0, int nrow,
+                                             int l) {
+    const int row = m0 + (l & 31);
+    if (row >= nrow) return;
+    T *g = G + (int64_t)row * ld + n0 + (l >> 5) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store4(g + q * 8, acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+}
+
+// The sum over the 32 lanes of x's half of the wave (lanes 0-31 or 32-63),
+// in every lane of that half.
+__device__ __forceinline__ float half_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+// 4 consecutive elements of a bf16 or float32 row as floats.
+__device__ __forceinline__ void load4f(const bf16 *p, float *f) {
+    const uint2 v = *(const uint2 *)p;
+    f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load4f(const float *p, float *f) {
+    const float4 v = *(const float4 *)p;
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
 }
 // rows m0 + lane%32 (those below nrow), columns n0 .. n0+31 of G (row pitch
 // ld) from a transposed accumulator: after one permlane32 exchange each lane
@@ -272,7 +284,7 @@ __device__ __forceinline__ void store_tile1_t(const f32x16 &acc, bf16 *G, int ld
     typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
     const int rows = nrow - m0;
     const __amdgpu_buffer_rsrc_t rs = wave_buffer(G + (int64_t)m0 * ld + n0, rows > 0 ? rows * ld * 2 : 0);
-    const int l = lane_id();
+    const int l = olane();
     const int off = ((l & 31) * ld + (l >> 5) * 8) * 2;
     unsigned r[8];   // r[2j], r[2j+1]: columns 8j + 4*(lane/32) + [0,4), packed
 #pragma unroll
@@ -302,7 +314,7 @@ struct LastRowScale {
     const float *bS;
     float bl[V];
     __device__ LastRowScale(const float *b) : bS(b) {
-        const int c = (threadIdx.x % (D / V)) * V;
+        const int c = (otid() % (D / V)) * V;
 #pragma unroll
         for (int e = 0; e < V; ++e) bl[e] = bS[(GC - 1) * D + c + e];
     }
@@ -341,64 +353,11 @@ __device__ __forceinline__ GateScale<Tr<T>::VEC, RefF> gate_scale(const float *b
     return GateScale<Tr<T>::VEC, RefF>{bS, ref, invert, D};
 }
 
-// The D x D states entering (or leaving) a chunk, combined from the segment
-// state and the local one, NS of them side by side:
-//   x_s[dv][dk] = g_s[dk] seg_s[dv][dk] + loc_s[dv][dk]    (loc_s null: 0)
-// in the [dv][dk] layout of the state arrays.  f(dv, dk0, x) receives V
-// consecutive dk of every state; loads are issued in batches of IB groups.
-template <typename T, int D, int NS, int BUDGET = 8, int NDV = D, typename F>
-__device__ __forceinline__ void for_states(const float *const *seg, const void *const *loc,
-                                           const float *const *g, F f, int dv0 = 0) {
-    // rows dv0 .. dv0 + NDV - 1 of the [dv][dk] states
-    constexpr int V = Tr<T>::VEC, IT = (NDV * D + NTHR * V - 1) / (NTHR * V);
-    constexpr int IB = IT < BUDGET / NS ? IT : BUDGET / NS;
-    static_assert(IT % IB == 0, "batches");
-    // NTHR * V is a multiple of D: a thread's dk group is the same in every batch
-    const int dk0 = (threadIdx.x * V) % D;
-    float gg[NS][V];
-#pragma unroll
-    for (int q = 0; q < NS; ++q)
-#pragma unroll
-        for (int j = 0; j < V; j += 4) load16(g[q] + dk0 + j, gg[q] + j);
-    for (int b = 0; b < IT; b += IB) {
-        uint4 sr[IB][NS][V / 4], lr[IB][NS];
-#pragma unroll
-        for (int u = 0; u < IB; ++u) {
-            const int e = dv0 * D + ((b + u) * NTHR + threadIdx.x) * V;
-#pragma unroll
-            for (int q = 0; q < NS; ++q) {
-                const bool in = e < (dv0 + NDV) * D;
-#pragma unroll
-                for (int j = 0; j < V / 4; ++j)
-                    sr[u][q][j] = in ? *(const uint4 *)(seg[q] + e + 4 * j) : make_uint4(0u, 0u, 0u, 0u);
-                lr[u][q] = (in && loc[q]) ? *(const uint4 *)((const T *)loc[q] + e)
-                                          : make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < IB; ++u) {
-            const int e = dv0 * D + ((b + u) * NTHR + threadIdx.x) * V;
-            if (e >= (dv0 + NDV) * D) continue;
-            float x[NS][V];
-#pragma unroll
-            for (int q = 0; q < NS; ++q) {
-                float sg[V], lc[V];
-#pragma unroll
-                for (int j = 0; j < V / 4; ++j) unpack16(sr[u][q][j], sg + 4 * j, (const float *)nullptr);
-                unpack16(lr[u][q], lc, (const T *)nullptr);
-#pragma unroll
-                for (int j = 0; j < V; ++j) x[q][j] = gg[q][j] * sg[j] + lc[j];
-            }
-            f(e / D, dk0, x);
-        }
-    }
-}
-
 // Span test of the two 32-row tiles of a chunk (uniform over the workgroup).
 template <int D>
 __device__ __forceinline__ void tile_spans(const float *bS, bool &slow0, bool &slow1) {
     bool s0 = false, s1 = false;
-    for (int c = threadIdx.x; c < D; c += NTHR) {
+    for (int c = otid(); c < D; c += NTHR) {
         s0 |= bS[c] - bS[31 * D + c] > SPAN2;
         s1 |= bS[32 * D + c] - bS[63 * D + c] > SPAN2;
     }
@@ -442,7 +401,7 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params 
     const T *K = (const T *)p.K + rb * D;
     const T *Vg = (const T *)p.V + rb * D;
     const float *LG = p.LG + rb * D;
-    const bool store_local = p.G > 1;
+    const bool store_local = p.Lc && p.G > 1;
 
     f32x16 acc[TL::PER_WAVE];
 #pragma unroll
@@ -468,10 +427,10 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params 
 #pragma unroll
             for (int k = 0; k < TL::PER_WAVE; ++k) {
                 int mi, ni;
-                if (TL::get(k, mi, ni)) store_T(acc[k], Lt, D, mi * 32, ni * 32, Ident());
+                if (TL::get(k, mi, ni, owave())) store_T(acc[k], Lt, D, mi * 32, ni * 32, Ident());
             }
         }
-        if (threadIdx.x < D) p.Gc[ch * D + threadIdx.x] = gcum;
+        if (p.Gc && otid() < D) p.Gc[ch * D + otid()] = gcum;
         __syncthreads();
         cumlog_scan<D>(bS, rl);
         __syncthreads();
@@ -494,26 +453,26 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params 
 #pragma unroll
         for (int k = 0; k < TL::PER_WAVE; ++k) {
             int mi, ni;
-            if (TL::get(k, mi, ni)) {
+            if (TL::get(k, mi, ni, owave())) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[k][r] *= ex2(bS[(GC - 1) * D + mi * 32 + crow(r)]);
+                for (int r = 0; r < 16; ++r) acc[k][r] *= ex2(bS[(GC - 1) * D + mi * 32 + crow(r, olane())]);
                 if constexpr (SW)
                     gemm_cc<D, GC>(acc[k], (const bf16 *)KT_s, mi * 32, (const bf16 *)VT_s, ni * 32,
-                                   opaque(frag_offs<D>(lane_id())));
+                                   opaque(frag_offs<D>(olane())));
                 else
-                    gemm<T, GC>(acc[k], KT_s, PT, mi * 32, VT_s, PT, ni * 32);
+                    gemm<T, GC>(acc[k], KT_s, PT, mi * 32, VT_s, PT, ni * 32, olane());
             }
         }
-        if (threadIdx.x < D) gcum *= ex2(bS[(GC - 1) * D + threadIdx.x]);
+        if (otid() < D) gcum *= ex2(bS[(GC - 1) * D + otid()]);
     }
     const int64_t sh = (int64_t)gs * p.H + h;
     float *Zs = p.Z + sh * D * D;
 #pragma unroll
     for (int k = 0; k < TL::PER_WAVE; ++k) {
         int mi, ni;
-        if (TL::get(k, mi, ni)) store_T(acc[k], Zs, D, mi * 32, ni * 32, Ident());
+        if (TL::get(k, mi, ni, owave())) store_T(acc[k], Zs, D, mi * 32, ni * 32, Ident());
     }
-    if (threadIdx.x < D) p.Gs[sh * D + threadIdx.x] = gcum;
+    if (otid() < D) p.Gs[sh * D + otid()] = gcum;
 }
 
 // ---------------------------------------------------------------------------
@@ -524,7 +483,7 @@ template <int D>
 __global__ __launch_bounds__(NTHR) void k_gfwd_segscan(Params p) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     const int ih = blockIdx.x / NB;
-    const int e = (blockIdx.x % NB) * NTHR + threadIdx.x;
+    const int e = (blockIdx.x % NB) * NTHR + otid();
     if (e >= D * D) return;
     const int i = ih / p.H, h = ih % p.H;
     Seq s;
@@ -539,14 +498,10 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_segscan(Params p) {
         P = p.Gs[sh * D + dk] * P + p.Z[sh * D * D + e];
     }
     if (p.M_out) p.M_out[mo] = P;
+    if (p.Pfin) p.Pfin[(int64_t)ih * D * D + e] = P;   // [dv][dk], as Pseg
 }
 
-// ---------------------------------------------------------------------------
-// Forward 3: output, one workgroup per (chunk, head).
-//   O = (Q 2^b) P_t + sum over tile pairs J <= I of
-//       [(Q_I 2^(b - b_mI)) (K_J 2^(b_mI - b))^T masked] V_J
-// ---------------------------------------------------------------------------
-// LDS plan of the output kernel: the running log-gates (float32) and one
+// LDS plan of the output walk: the running log-gates (float32) and one
 // scratch area reused by three phases, small enough for two workgroups per CU:
 //   1  Q 2^b rows | P_t^T rows (half of them at a time when d = 128)
 //   2  Q_I 2^(b - b_mI) rows | K rows 0..63 (ref 32; then rows 0..31 with ref 0) | scores
@@ -560,59 +515,159 @@ template <typename T, int D> struct OutLds {
     static_assert(D * PS <= SOFF, "V^T must not reach the scores");
 };
 
+// LDS plan of the gradient walks: the running log-gates (float32), a small
+// per-channel sum and one scratch area reused by every phase, small enough
+// for two workgroups per CU.  A d x d state operand is staged in NHALF parts
+// (d = 128): split along the contraction index where the product allows it
+// (dQ's dO P_t^T, dK's V R_t^T), along the output columns otherwise (dV's
+// K R_t).  Score tiles are formed before the next product's operands are
+// staged over the rows they came from.
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_out(Params p) {
+struct GradLds {
+    static constexpr int V = Tr<T>::VEC, PD = D + V, PS = GC + V, PK = 96 + V;
+    static constexpr int NHALF = D * PD * (int)sizeof(T) > 20000 ? 2 : 1, DH = D / NHALF;
+    static constexpr int PDH = DH + V;                    // pitch of a contraction-split part
+    static constexpr int ROWS = GC * PD, SC = GC * PS, SOFF = 2 * ROWS;
+    static constexpr int CPART = D * PDH, RPART = DH * PD;
+    static constexpr int A1 = ROWS + CPART;               // dO rows, P part
+    static constexpr int B1 = RPART + ROWS;               // R part, K rows
+    static constexpr int C1 = ROWS + CPART;               // V rows, R^T part
+    static constexpr int S2 = SOFF + SC;                  // two row arrays + scores
+    static constexpr int M1 = A1 > B1 ? A1 : B1, M2 = C1 > S2 ? C1 : S2;
+    static constexpr int ELEMS = M1 > M2 ? M1 : M2;
+    static constexpr int BYTES = ELEMS * (int)sizeof(T) > GC * D * 4 ? ELEMS * (int)sizeof(T) : GC * D * 4;
+    static_assert(D * PK <= SOFF && D * PS <= SOFF, "K^T / Q^T / dO^T must not reach the scores");
+};
+
+// ---------------------------------------------------------------------------
+// A D x D state carried in registers by the walks below: tile k of the wave
+// (Tiles<D/32, D/32>) holds S[dk block mi][dv block ni] as a float32 MFMA
+// accumulator (element r: dk = 32 mi + crow(r), dv = 32 ni + lane % 32).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void state_load(f32x16 *S, const float *src) {   // src [dv][dk]
+    using TL = Tiles<D / 32, D / 32>;
+    const int l = olane();
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) {
+        int mi, ni;
+        if (!TL::get(k, mi, ni, owave())) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[k][r] = src[(ni * 32 + (l & 31)) * D + mi * 32 + crow(r, l)];
+    }
+}
+
+// Rows dv0 .. dv0 + DH - 1 of the state's [dv][dk] form: f(dv - dv0, dk, x)
+// receives 4 consecutive dk of one row.
+template <int D, int DH, typename F>
+__device__ __forceinline__ void state_rows(const f32x16 *S, int dv0, F f) {
+    using TL = Tiles<D / 32, D / 32>;
+    const int l = olane();
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) {
+        int mi, ni;
+        if (!TL::get(k, mi, ni, owave()) || ni * 32 < dv0 || ni * 32 >= dv0 + DH) continue;
+        const int dv = ni * 32 + (l & 31) - dv0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float x[4] = {S[k][4 * q], S[k][4 * q + 1], S[k][4 * q + 2], S[k][4 * q + 3]};
+            f(dv, mi * 32 + q * 8 + (l >> 5) * 4, x);
+        }
+    }
+}
+
+// S <- Diag(2^(b_last)) S: row dk scaled by the chunk's gate product.
+template <int D>
+__device__ __forceinline__ void state_decay(f32x16 *S, const float *bS) {
+    using TL = Tiles<D / 32, D / 32>;
+    const int l = olane();
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) {
+        int mi, ni;
+        if (!TL::get(k, mi, ni, owave())) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[k][r] *= ex2(bS[(GC - 1) * D + mi * 32 + crow(r, l)]);
+    }
+}
+
+// The running sums of the chunk's log-gates into bS (the caller synchronizes
+// before anyone reads them): loaded here, at the chunk's start (a prefetch
+// held in registers across the chunk would not fit beside the state).
+template <int D>
+__device__ __forceinline__ void chunk_gates(float *bS, const float *lg, int Ct) {
+    LogRows<D> rl;
+    cumlog_load<D>(rl, lg, Ct);
+    __syncthreads();   // the previous chunk's readers of bS are done
+    cumlog_scan<D>(bS, rl);
+}
+
+// ---------------------------------------------------------------------------
+// Forward 3: output, one workgroup per (segment, head), walking the segment's
+// chunks in order with the state P in registers (float32 MFMA accumulators,
+// tile (mi, ni) = P[dk block mi][dv block ni]), from the segment's entering
+// state Pseg:
+//   O_t = (Q 2^b) P + sum over tile pairs J <= I of
+//         [(Q_I 2^(b - b_mI)) (K_J 2^(b_mI - b))^T masked] V_J
+//   P  <- Diag(2^(b_last)) P + (K 2^(b_last - b))^T V
+// The next chunk's rows are loaded while the current one is worked on, each
+// set once its registers have been staged for the last time.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_walk(Params p) {
     using L = OutLds<T, D>;
     constexpr int PD = L::PD, PS = L::PS, DH = L::DH;
+    constexpr bool SW = sizeof(T) == 2;
+    constexpr int KOFF = SW ? GC * D : D * PS;   // K 2^(b_last - b) for the update, past V
+    static_assert(KOFF + (SW ? GC * D : D * PS) <= L::ELEMS, "update operands fit");
     __shared__ float bS[GC * D];
     __shared__ __attribute__((aligned(16))) T U[L::ELEMS];
     using TO = Tiles<GC / 32, D / 32>;
+    using TL = Tiles<D / 32, D / 32>;
 
-    // consecutive workgroups (on one XCD) take consecutive chunks of one head:
-    // the chunks of a segment then read its segment states from that XCD's L2
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = lid / p.n_chunks_ub, gc = lid % p.n_chunks_ub;
-    if (h >= p.H) return;
+    const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
     Seq s;
-    int t;
-    if (!chunk_seq(p, gc, s, t)) return;
-    const int tok = t * GC;
-    const int Ct = min(GC, s.len - tok);
-    const int sl = t / p.G;
-    if (s.s0 + sl >= p.n_segs_ub) return;   // only with malformed cu_seqlens
-    const int64_t rb = row_base(p, s, h) + tok;
-    const T *Q = (const T *)p.Q + rb * D;
-    const T *K = (const T *)p.K + rb * D;
-    const T *Vg = (const T *)p.V + rb * D;
-    T *O = (T *)p.O + rb * D;
-    const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
-    const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
-    const int w = wave_id(), l = lane_id();
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const int64_t rb0 = row_base(p, s, h);
+    const int64_t sh = (int64_t)gs * p.H + h;
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    const int w = owave();
 
-    // every token load of the kernel, issued up front
-    auto krow = [](int j) { return j < 64 ? (j & 31) : j - 32; };   // K rows: (0|ref 0), (0|32), (1|32)
-    Raw<T, D, GC> rq, rv;
-    Raw<T, D, 96> rk;
-    raw_load(rq, Q, Ct, RowId());
-    raw_load(rk, K, Ct, krow);
-    raw_load(rv, Vg, Ct, RowId());
-    chunk_cumlog<D>(bS, p.LG + rb * D, Ct);
+    f32x16 P[TL::PER_WAVE];
+    state_load<D>(P, p.Pseg + sh * D * D);
 
-    // 1: o = (Q 2^b) P_t
-    T *Qh = U, *Ph = U + L::ROWS;
-    f32x16 o[TO::PER_WAVE];
+    Raw<T, D, GC> rq, rk, rv;
+    if (t0 < t1) {
+        const int64_t rb = rb0 + (int64_t)t0 * GC;
+        const int Ct0 = min(GC, s.len - t0 * GC);
+        raw_load(rq, (const T *)p.Q + rb * D, Ct0, RowId());
+        raw_load(rk, (const T *)p.K + rb * D, Ct0, RowId());
+        raw_load(rv, (const T *)p.V + rb * D, Ct0, RowId());
+    }
+    for (int t = t0; t < t1; ++t) {
+        const int tok = t * GC;
+        const int Ct = min(GC, s.len - tok);
+        const bool more = t + 1 < t1;
+        const int Cn = more ? min(GC, s.len - tok - GC) : 0;
+        const int64_t rb = rb0 + tok;
+        const T *Q = (const T *)p.Q + rb * D;
+        const T *K = (const T *)p.K + rb * D;
+        T *O = (T *)p.O + rb * D;
+        const int l = olane();   // (once per chunk: see otid)
+        chunk_gates<D>(bS, p.LG + rb * D, Ct);   // (its first barrier also frees U)
+        __syncthreads();
+
+        // 1: o = (Q 2^b) P, P^T rows [dv][dk] written from the registers
+        T *Qh = U, *Ph = U + L::ROWS;
+        f32x16 o[TO::PER_WAVE];
 #pragma unroll
-    for (int k = 0; k < TO::PER_WAVE; ++k) zero(o[k]);
-    {
-        const float *seg[1] = {p.Pseg + sh * D * D};
-        const void *loc[1] = {p.G > 1 ? (const void *)((const T *)p.Lc + ch * D * D) : nullptr};
-        const float *g[1] = {p.Gc + ch * D};
+        for (int k = 0; k < TO::PER_WAVE; ++k) zero(o[k]);
         for (int hh = 0; hh < L::NHALF; ++hh) {
             const int dv0 = hh * DH;
             if (hh) __syncthreads();
-            for_states<T, D, 1, 8, DH>(seg, loc, g, [&](int dv, int dk, const float (*x)[Tr<T>::VEC]) {
-                store_vec(Ph + (dv - dv0) * PD + dk, x[0]);
-            }, dv0);
+            state_rows<D, DH>(P, dv0, [&](int dv, int dk, const float *x) {
+                store4(Ph + dv * PD + dk, x[0], x[1], x[2], x[3]);
+            });
             if (!hh)
                 raw_store<T, D, GC, false>(rq, Qh, PD, Ct, RowId(),
                                            gate_scale<T>(bS, D, [](int) { return -1; }));
@@ -620,76 +675,100 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_out(Params p)
 #pragma unroll
             for (int k = 0; k < TO::PER_WAVE; ++k) {
                 int mi, ni;
-                if (TO::get(k, mi, ni) && ni * 32 >= dv0 && ni * 32 < dv0 + DH) {
+                if (TO::get(k, mi, ni, owave()) && ni * 32 >= dv0 && ni * 32 < dv0 + DH) {
                     // (bf16: O accumulated transposed)
-                    if constexpr (sizeof(T) == 2)
+                    if constexpr (SW)
                         gemm_t<D>(o[k], (const bf16 *)Qh, PD, mi * 32, (const bf16 *)Ph, PD, ni * 32 - dv0);
                     else
-                        gemm<T, D>(o[k], Qh, PD, mi * 32, Ph, PD, ni * 32 - dv0);
+                        gemm<T, D>(o[k], Qh, PD, mi * 32, Ph, PD, ni * 32 - dv0, olane());
                 }
             }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // 2: masked gated scores into Sc
-    T *Qt = U, *K64 = U + L::ROWS, *Sc = U + L::SOFF;
-    raw_store<T, D, GC, false>(rq, Qt, PD, Ct, RowId(),
-                               gate_scale<T>(bS, D, [](int j) { return j & ~31; }, true));
-    raw_store_map<T, D, 96, false>(rk, K64, PD, Ct, krow,
-                                   gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }),
-                                   [](int j) { return j - 32; });   // rows 0..63 with ref 32
-    bool slow0, slow1;
-    tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
-    auto score_tile = [&](int I, int J, int krow0, bool slow) __attribute__((always_inline)) {
-        f32x16 st;
-        zero(st);
-        if (!slow) gemm<T, D>(st, Qt, PD, 32 * I, K64, PD, krow0);
+        // 2: masked gated scores into Sc
+        T *Qt = U, *K64 = U + L::ROWS, *Sc = U + L::SOFF;
+        raw_store<T, D, GC, false>(rq, Qt, PD, Ct, RowId(),
+                                   gate_scale<T>(bS, D, [](int j) { return j & ~31; }, true));
+        raw_store<T, D, GC, false>(rk, K64, PD, Ct, RowId(),
+                                   gate_scale<T>(bS, D, [](int) { return 32; }));   // rows 0..63 with ref 32
+        bool slow0, slow1;
+        tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
+        auto score_tile = [&](int I, int J, int krow0, bool slow) __attribute__((always_inline)) {
+            f32x16 st;
+            zero(st);
+            if (!slow) gemm<T, D>(st, Qt, PD, 32 * I, K64, PD, krow0, olane());
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qs = 32 * I + crow(r), ki = 32 * J + (l & 31);
-            float x = 0.f;
-            if (qs < Ct && ki < Ct && ki <= qs) x = slow ? exact_score<T, D>(Q, K, bS, qs, ki) : st[r];
-            Sc[qs * PS + ki] = fromf<T>(x);
+            for (int r = 0; r < 16; ++r) {
+                const int qs = 32 * I + crow(r, olane()), ki = 32 * J + (l & 31);
+                float x = 0.f;
+                if (qs < Ct && ki < Ct && ki <= qs) x = slow ? exact_score<T, D>(Q, K, bS, qs, ki) : st[r];
+                Sc[qs * PS + ki] = fromf<T>(x);
+            }
+        };
+        if (w == 1) score_tile(1, 0, 0, false);
+        if (w == 2) score_tile(1, 1, 32, slow1);
+        if (w == 3) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Sc[crow(r, olane()) * PS + 32 + (l & 31)] = fromf<T>(0.f);
         }
-    };
-    if (w == 1) score_tile(1, 0, 0, false);
-    if (w == 2) score_tile(1, 1, 32, slow1);
-    if (w == 3) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Sc[crow(r) * PS + 32 + (l & 31)] = fromf<T>(0.f);
-    }
-    __syncthreads();
-    raw_store_map<T, D, 96, false>(rk, K64, PD, Ct, krow,
-                                   gate_scale<T>(bS, D, [](int) { return 0; }),
-                                   [](int j) { return j < 32 ? j : -1; });   // rows 0..31 with ref 0
-    __syncthreads();
-    if (w == 0) score_tile(0, 0, 0, slow0);
-    __syncthreads();
+        __syncthreads();
+        raw_store_map<T, D, GC, false>(rk, K64, PD, Ct, RowId(),
+                                       gate_scale<T>(bS, D, [](int) { return 0; }),
+                                       [](int j) { return j < 32 ? j : -1; });   // rows 0..31 with ref 0
+        __syncthreads();
+        if (w == 0) score_tile(0, 0, 0, slow0);
+        __syncthreads();
 
-    // 3: o += Sc V (bf16: V rows in a swizzled tile, read transposed;
-    // float32: a transposed copy)
-    constexpr bool SW = sizeof(T) == 2;
-    static_assert(GC * D <= L::SOFF, "V must not reach the scores");
-    T *VT = U;
-    if constexpr (SW)
-        raw_store_sw<D, GC>(rv, (bf16 *)VT, Ct, RowId(), NoScale());
-    else
-        raw_store<T, D, GC, true>(rv, VT, PS, Ct, RowId(), NoScale());
-    __syncthreads();
-    const FragOffs<D> fo = frag_offs<D>(l);
+        // 3: o += Sc V (bf16: V rows in a swizzled tile, read transposed;
+        // float32: a transposed copy); V stays for the state update
+        static_assert(GC * D <= L::SOFF && D * PS <= L::SOFF, "V must not reach the scores");
+        T *VT = U;
+        if constexpr (SW)
+            raw_store_sw<D, GC>(rv, (bf16 *)VT, Ct, RowId(), NoScale());
+        else
+            raw_store<T, D, GC, true>(rv, VT, PS, Ct, RowId(), NoScale());
+        if (more) {
+            raw_load(rq, Q + GC * D, Cn, RowId());
+            raw_load(rv, (const T *)p.V + (rb + GC) * D, Cn, RowId());
+        }
+        __syncthreads();
+        const FragOffs<D> fo = frag_offs<D>(l);
 #pragma unroll
-    for (int k = 0; k < TO::PER_WAVE; ++k) {
-        int mi, ni;
-        if (TO::get(k, mi, ni)) {
-            if constexpr (SW) {
-                gemm_rc_t<D, GC>(o[k], (const bf16 *)Sc, PS, mi * 32, (const bf16 *)VT, ni * 32, fo);
-                store_tile1_t(o[k], (bf16 *)O, D, mi * 32, ni * 32, Ct);
-            } else {
-                gemm<T, GC>(o[k], Sc, PS, mi * 32, VT, PS, ni * 32);
-                store_rows(o[k], O, D, mi * 32, ni * 32, Ct);
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (TO::get(k, mi, ni, owave())) {
+                if constexpr (SW) {
+                    gemm_rc_t<D, GC>(o[k], (const bf16 *)Sc, PS, mi * 32, (const bf16 *)VT, ni * 32, fo);
+                    store_tile1_t(o[k], (bf16 *)O, D, mi * 32, ni * 32, Ct);
+                } else {
+                    gemm<T, GC>(o[k], Sc, PS, mi * 32, VT, PS, ni * 32, olane());
+                    store_rows(o[k], O, D, mi * 32, ni * 32, Ct, olane());
+                }
             }
         }
+        if (!more) break;   // (the state after the segment comes from the scan)
+
+        // 4: P <- Diag(2^(b_last)) P + (K 2^(b_last - b))^T V
+        __syncthreads();   // the products above have read Sc
+        T *KT = U + KOFF;
+        if constexpr (SW)
+            raw_store_sw<D, GC>(rk, (bf16 *)KT, Ct, RowId(), LastRowScale<D, 8>(bS));
+        else
+            raw_store<T, D, GC, true>(rk, KT, PS, Ct, RowId(),
+                                      gate_scale<T>(bS, D, [](int) { return GC - 1; }));
+        __syncthreads();
+        state_decay<D>(P, bS);
+#pragma unroll
+        for (int k = 0; k < TL::PER_WAVE; ++k) {
+            int mi, ni;
+            if (!TL::get(k, mi, ni, owave())) continue;
+            if constexpr (SW)
+                gemm_cc<D, GC>(P[k], (const bf16 *)KT, mi * 32, (const bf16 *)VT, ni * 32, opaque(fo));
+            else
+                gemm<T, GC>(P[k], KT, PS, mi * 32, VT, PS, ni * 32, olane());
+        }
+        raw_load(rk, K + GC * D, Cn, RowId());
     }
 }
 
@@ -707,7 +786,7 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params 
     __shared__ __attribute__((aligned(16))) T QT_s[SW ? GC * D : D * PT];
     __shared__ __attribute__((aligned(16))) T OT_s[SW ? GC * D : D * PT];
     using TL = Tiles<D / 32, D / 32>;
-    const FragOffs<D> fo = frag_offs<D>(lane_id());
+    const FragOffs<D> fo = frag_offs<D>(olane());
 
     const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
     Seq s;
@@ -717,7 +796,7 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params 
     const T *Q = (const T *)p.Q + rb * D;
     const T *dO = (const T *)p.dO + rb * D;
     const float *LG = p.LG + rb * D;
-    const bool store_local = p.G > 1;
+    const bool store_local = p.Rc && p.G > 1;
 
     f32x16 acc[TL::PER_WAVE];
 #pragma unroll
@@ -742,10 +821,10 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params 
 #pragma unroll
             for (int k = 0; k < TL::PER_WAVE; ++k) {
                 int mi, ni;
-                if (TL::get(k, mi, ni)) store_T(acc[k], Rt, D, mi * 32, ni * 32, Ident());
+                if (TL::get(k, mi, ni, owave())) store_T(acc[k], Rt, D, mi * 32, ni * 32, Ident());
             }
         }
-        if (threadIdx.x < D) p.Hc[ch * D + threadIdx.x] = hcum;
+        if (p.Hc && otid() < D) p.Hc[ch * D + otid()] = hcum;
         __syncthreads();
         cumlog_scan<D>(bS, rl);
         __syncthreads();
@@ -767,22 +846,22 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params 
 #pragma unroll
         for (int k = 0; k < TL::PER_WAVE; ++k) {
             int mi, ni;
-            if (TL::get(k, mi, ni)) {
+            if (TL::get(k, mi, ni, owave())) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[k][r] *= ex2(bS[(GC - 1) * D + mi * 32 + crow(r)]);
+                for (int r = 0; r < 16; ++r) acc[k][r] *= ex2(bS[(GC - 1) * D + mi * 32 + crow(r, olane())]);
                 if constexpr (SW)
                     gemm_cc<D, GC>(acc[k], (const bf16 *)QT_s, mi * 32, (const bf16 *)OT_s, ni * 32, fo);
                 else
-                    gemm<T, GC>(acc[k], QT_s, PT, mi * 32, OT_s, PT, ni * 32);
+                    gemm<T, GC>(acc[k], QT_s, PT, mi * 32, OT_s, PT, ni * 32, olane());
             }
         }
-        if (threadIdx.x < D) hcum *= ex2(bS[(GC - 1) * D + threadIdx.x]);
+        if (otid() < D) hcum *= ex2(bS[(GC - 1) * D + otid()]);
     }
     float *Ws = p.W + ((int64_t)gs * p.H + h) * D * D;
 #pragma unroll
     for (int k = 0; k < TL::PER_WAVE; ++k) {
         int mi, ni;
-        if (TL::get(k, mi, ni)) store_T(acc[k], Ws, D, mi * 32, ni * 32, Ident());
+        if (TL::get(k, mi, ni, owave())) store_T(acc[k], Ws, D, mi * 32, ni * 32, Ident());
     }
 }
 
@@ -794,7 +873,7 @@ template <int D>
 __global__ __launch_bounds__(NTHR) void k_gbwd_segscan(Params p) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
     const int ih = blockIdx.x / NB;
-    const int e = (blockIdx.x % NB) * NTHR + threadIdx.x;
+    const int e = (blockIdx.x % NB) * NTHR + otid();
     if (e >= D * D) return;
     const int i = ih / p.H, h = ih % p.H;
     Seq s;
@@ -812,237 +891,213 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_segscan(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Backward 3: gradients, one workgroup per (chunk, head), with D_ = dO V^T:
-//   dQ = 2^b . (dO P_t^T) + sum_{J<=I} 2^(b - b_mI) . ([D_ masked]_IJ (K_J 2^(b_mI - b)))
-//   dV = (K 2^(b_last - b)) R_t + sum_{I>=J} [A masked]_IJ^T dO_I   (A: the gated scores)
-//   dK = 2^(b_last - b) . (V R_t^T)
-//        + sum_{I>=J} 2^(b_mJ' - b) . ([D_ masked]_IJ^T (Q_I 2^(b - b_mJ')))
-//   dlog_g[s] = sum_{u>=s in chunk} (q_u dq_u - k_u dk_u) + rowsum(R_t . P_{t+1})
-// with m_I the first row of query tile I and m'_J the last row of key tile J.
+// Masked 32x32 score tiles A_a . B_b^T into Sc (pitch PS; A and B rows of
+// pitch PD): tiles (a, b) = (0,0), (1,0), (1,1) (lower: b <= a kept) or
+// (0,0), (0,1), (1,1) (upper: b >= a kept), the tiles of mask bit w (bit i:
+// tile i) on waves 0..2; wave 3 zeroes the remaining block when zero_block.
+// B's rows for tile i start at brow(i).  Gated diagonal tiles over the span
+// limit (slow0 / slow1) take exact(a, b) instead of the product.  tr stores
+// Sc[b][a].
 // ---------------------------------------------------------------------------
-// LDS plan of the gradient kernel: the running log-gates (float32), two small
-// per-channel sums and one scratch area reused by every phase, small enough
-// for two workgroups per CU.  A d x d state operand is staged in NHALF parts
-// (d = 128): split along the contraction index where the product allows it
-// (dQ's dO P_t^T, dK's V R_t^T), along the output columns otherwise (dV's
-// K R_t).  Score tiles are formed before the next product's operands are
-// staged over the rows they came from.
-template <typename T, int D>
-struct GradLds {
-    static constexpr int V = Tr<T>::VEC, PD = D + V, PS = GC + V, PK = 96 + V;
-    static constexpr int NHALF = D * PD * (int)sizeof(T) > 20000 ? 2 : 1, DH = D / NHALF;
-    static constexpr int PDH = DH + V;                    // pitch of a contraction-split part
-    static constexpr int ROWS = GC * PD, SC = GC * PS, SOFF = 2 * ROWS;
-    static constexpr int CPART = D * PDH, RPART = DH * PD;
-    static constexpr int RP = NTHR * V * 4 / (int)sizeof(T);   // float partial sums of rho
-    static constexpr int A1 = ROWS + CPART + RP;          // dO rows, P part, rho partials
-    static constexpr int B1 = RPART + ROWS;               // R part, K rows
-    static constexpr int C1 = ROWS + CPART;               // V rows, R^T part
-    static constexpr int S2 = SOFF + SC;                  // two row arrays + scores
-    static constexpr int M1 = A1 > B1 ? A1 : B1, M2 = C1 > S2 ? C1 : S2;
-    static constexpr int ELEMS = M1 > M2 ? M1 : M2;
-    static constexpr int BYTES = ELEMS * (int)sizeof(T) > GC * D * 4 ? ELEMS * (int)sizeof(T) : GC * D * 4;
-    static_assert(D * PK <= SOFF && D * PS <= SOFF, "K^T / Q^T / dO^T must not reach the scores");
-};
+template <typename T, int D, int PD, int PS, typename BRow, typename Exact>
+__device__ __forceinline__ void score_tiles(T *Sc, const T *A, const T *B, BRow brow, bool upper, bool tr,
+                                            bool gated, Exact exact, int mask, bool zero_block, int Ct,
+                                            bool slow0, bool slow1) {
+    const int w = owave(), l = olane();
+    if (w < 3 && ((mask >> w) & 1)) {
+        const int ta = upper ? (w == 2 ? 1 : 0) : (w == 0 ? 0 : 1);
+        const int tb = upper ? (w == 0 ? 0 : 1) : (w == 2 ? 1 : 0);
+        const bool slow = gated && ta == tb && (ta == 0 ? slow0 : slow1);
+        f32x16 st;
+        zero(st);
+        if (!slow) gemm<T, D>(st, A, PD, 32 * ta, B, PD, brow(w), l);
+        const int b = 32 * tb + (l & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int a = 32 * ta + crow(r, l);
+            float x = 0.f;
+            if (a < Ct && b < Ct && (upper ? b >= a : b <= a)) x = slow ? exact(a, b) : st[r];
+            st[r] = x;
+            if (!tr) Sc[a * PS + b] = fromf<T>(x);
+        }
+        // transposed: the lane's 4 consecutive rows a of each group in one store
+        if (tr) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                store4(Sc + b * PS + 32 * ta + crow(4 * q, l), st[4 * q], st[4 * q + 1], st[4 * q + 2],
+                       st[4 * q + 3]);
+        }
+    } else if (w == 3 && zero_block) {
+        const int ta = upper ? 1 : 0, tb = upper ? 0 : 1;
+        const int b = 32 * tb + (l & 31);
+        if (tr) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) store4(Sc + b * PS + 32 * ta + crow(4 * q, l), 0.f, 0.f, 0.f, 0.f);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Sc[(32 * ta + crow(r, l)) * PS + b] = fromf<T>(0.f);
+        }
+    }
+}
 
+// ---------------------------------------------------------------------------
+// Backward 3: dQ, one workgroup per (segment, head), walking the segment's
+// chunks in order with the forward state P in registers (as the output walk),
+// from Pseg; with D_ = dO V^T and m_I the first row of query tile I:
+//   dQ = 2^b . (dO P^T) + sum_{J<=I} 2^(b - b_mI) . ([D_ masked]_IJ (K_J 2^(b_mI - b)))
+//   P <- Diag(2^(b_last)) P + (K 2^(b_last - b))^T V
+// q . dq goes to the log-gate gradient's rows, where the reverse walk reads it.
+// ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params p) {
+__global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_walk_q(Params p) {
     using L = GradLds<T, D>;
-    constexpr int V = Tr<T>::VEC, PD = L::PD, PS = L::PS, PK = L::PK, DH = L::DH, PDH = L::PDH;
+    constexpr int PD = L::PD, PS = L::PS, PK = L::PK, DH = L::DH, PDH = L::PDH;
     constexpr bool SW = sizeof(T) == 2;   // bf16: transpose reads of row tiles
-    static_assert(96 * D <= L::SOFF, "K / Q rows must not reach the scores");
-    static_assert(!SW || DH * D <= L::CPART, "swizzled state parts fit the transposed ones' space");
+    constexpr int UPD = SW ? GC * D : D * PS;   // one operand of the state update
+    static_assert(96 * D <= L::SOFF && D * PK <= L::SOFF, "K versions must not reach the scores");
+    static_assert(2 * UPD * (int)sizeof(T) <= L::BYTES, "update operands fit");
     __shared__ float bS[GC * D];
-    // Ep[mi][c]: row block mi's part of rowsum(R_t . P_{t+1}) for channel c,
-    // each written by exactly one wave and summed in block order afterwards
-    // (a fixed order, so the result does not depend on wave timing)
-    __shared__ float rho[D], Ep[GC / 32][D];
+    __shared__ float Ap[GC / 32][D];   // row block mi's part of the chunk's q . dq-inter sums
     __shared__ __attribute__((aligned(16))) char U_raw[L::BYTES];
     T *U = (T *)U_raw;
-    T *Sc = U + L::SOFF;   // score tiles (every phase)
+    T *Sc = U + L::SOFF;
     using TO = Tiles<GC / 32, D / 32>;
+    using TL = Tiles<D / 32, D / 32>;
 
-    // consecutive workgroups (on one XCD) take consecutive chunks of one head:
-    // the chunks of a segment then read its segment states from that XCD's L2
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = lid / p.n_chunks_ub, gc = lid % p.n_chunks_ub;
-    if (h >= p.H) return;
+    const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
     Seq s;
-    int t;
-    if (!chunk_seq(p, gc, s, t)) return;
-    const int tok = t * GC;
-    const int Ct = min(GC, s.len - tok);
-    const int sl = t / p.G;
-    if (s.s0 + sl >= p.n_segs_ub) return;
-    const int64_t rb = row_base(p, s, h) + tok;
-    const T *Q = (const T *)p.Q + rb * D;
-    const T *K = (const T *)p.K + rb * D;
-    const T *Vg = (const T *)p.V + rb * D;
-    const T *dO = (const T *)p.dO + rb * D;
-    const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
-    const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
-    const float *Ps = p.Pseg + sh * D * D, *Rs = p.Rseg + sh * D * D;
-    const void *Lt = p.G > 1 ? (const void *)((const T *)p.Lc + ch * D * D) : nullptr;
-    const void *Rt = p.G > 1 ? (const void *)((const T *)p.Rc + ch * D * D) : nullptr;
-    const float *gP = p.Gc + ch * D, *gR = p.Hc + ch * D;
-    const int w = wave_id(), l = lane_id();
-    auto krow = [](int j) { return j < 64 ? (j & 31) : j - 32; };   // K rows of the 3 versions
-    auto qrow = [](int j) { return j < 64 ? j : j - 32; };          // Q rows of the 3 versions
-    // token rows in registers, loaded a phase ahead of their use (reloaded
-    // from L2 rather than kept live across phases: registers bound the
-    // workgroups per CU)
-    chunk_cumlog<D>(bS, p.LG + rb * D, Ct);   // (its registers are free before the rows load)
-    Raw<T, D, GC> rdo, rv, rkq;
-    Raw<T, D, 96> rk96;
-    raw_load(rdo, dO, Ct, RowId());
-    raw_load(rv, Vg, Ct, RowId());
-    raw_load(rk96, K, Ct, krow);
-    bool slow0 = false, slow1 = false;
-    // Masked 32x32 score tiles A_a . B_b^T into Sc: tiles (a, b) = (0,0), (1,0),
-    // (1,1) (lower: b <= a kept) or (0,0), (0,1), (1,1) (upper: b >= a kept),
-    // the tiles of mask bit w (bit i: tile i) on waves 0..2; wave 3 zeroes the
-    // remaining block when zero_block.  B's rows for tile i start at brow(i).
-    // Gated diagonal tiles over the span limit take exact(a, b) instead of the
-    // product.  tr stores Sc[b][a].
-    auto scores = [&](const T *A, const T *B, auto brow, bool upper, bool tr, bool gated,
-                      auto exact, int mask, bool zero_block) __attribute__((always_inline)) {
-        if (w < 3 && ((mask >> w) & 1)) {
-            const int ta = upper ? (w == 2 ? 1 : 0) : (w == 0 ? 0 : 1);
-            const int tb = upper ? (w == 0 ? 0 : 1) : (w == 2 ? 1 : 0);
-            const bool slow = gated && ta == tb && (ta == 0 ? slow0 : slow1);
-            f32x16 st;
-            zero(st);
-            if (!slow) gemm<T, D>(st, A, PD, 32 * ta, B, PD, brow(w));
-            const int b = 32 * tb + (l & 31);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int a = 32 * ta + crow(r);
-                float x = 0.f;
-                if (a < Ct && b < Ct && (upper ? b >= a : b <= a)) x = slow ? exact(a, b) : st[r];
-                st[r] = x;
-                if (!tr) Sc[a * PS + b] = fromf<T>(x);
-            }
-            // transposed: the lane's 4 consecutive rows a of each group in one store
-            if (tr) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    store4(Sc + b * PS + 32 * ta + crow(4 * q), st[4 * q], st[4 * q + 1], st[4 * q + 2],
-                           st[4 * q + 3]);
-            }
-        } else if (w == 3 && zero_block) {
-            const int ta = upper ? 1 : 0, tb = upper ? 0 : 1;
-            const int b = 32 * tb + (l & 31);
-            if (tr) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) store4(Sc + b * PS + 32 * ta + crow(4 * q), 0.f, 0.f, 0.f, 0.f);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) Sc[(32 * ta + crow(r)) * PS + b] = fromf<T>(0.f);
-            }
-        }
-    };
-    auto no_exact = [](int, int) { return 0.f; };
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const int64_t rb0 = row_base(p, s, h);
+    const int64_t sh = (int64_t)gs * p.H + h;
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
 
-    // ---- A: dQ -------------------------------------------------------------
-    {
+    f32x16 P[TL::PER_WAVE];
+    state_load<D>(P, p.Pseg + sh * D * D);
+
+    Raw<T, D, GC> rdo, rv, rk;   // the chunk's dO, V, K rows (the next chunk's, loaded ahead)
+    if (t0 < t1) {
+        const int64_t rb = rb0 + (int64_t)t0 * GC;
+        const int Ct0 = min(GC, s.len - t0 * GC);
+        raw_load(rdo, (const T *)p.dO + rb * D, Ct0, RowId());
+        raw_load(rv, (const T *)p.V + rb * D, Ct0, RowId());
+        raw_load(rk, (const T *)p.K + rb * D, Ct0, RowId());
+    }
+    for (int t = t0; t < t1; ++t) {
+        const int tok = t * GC;
+        const int Ct = min(GC, s.len - tok);
+        const bool more = t + 1 < t1;
+        const int Cn = more ? min(GC, s.len - tok - GC) : 0;
+        const int64_t rb = rb0 + tok;
+        const T *Q = (const T *)p.Q + rb * D;
+        const T *K = (const T *)p.K + rb * D;
+        const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
+        const int l = olane();   // (once per chunk: see otid)
+        chunk_gates<D>(bS, p.LG + rb * D, Ct);
+        auto no_exact = [](int, int) { return 0.f; };
+
+        // dO P^T over the state's dv halves
         f32x16 dq[TO::PER_WAVE];
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) zero(dq[k]);
-        T *dOr = U, *Pk = U + L::ROWS;   // dO rows; P_t as [dk][dv part]
-        float *rpart = (float *)(U + L::ROWS + L::CPART);
+        T *dOr = U, *Pk = U + L::ROWS;   // dO rows; P as [dk][dv part]
         raw_store<T, D, GC, false>(rdo, dOr, PD, Ct, RowId(), NoScale());
-        // rho[dk] = sum_dv R_t[dk][dv] P_t[dk][dv]; each thread keeps one group
-        // of V consecutive dk (NTHR * V is a multiple of D)
-        float racc[V];
-#pragma unroll
-        for (int j = 0; j < V; ++j) racc[j] = 0.f;
-        const float *seg[2] = {Ps, Rs};
-        const void *loc[2] = {Lt, Rt};
-        const float *g[2] = {gP, gR};
         for (int hh = 0; hh < L::NHALF; ++hh) {
             const int dv0 = hh * DH;
-            if (hh) __syncthreads();
+            __syncthreads();   // (first half: bS is written; later: the last products are done)
             // (bf16: P's rows [dv][dk] in a swizzled tile, read transposed;
             // float32: a transposed copy [dk][dv])
-            for_states<T, D, 2, 2, DH>(seg, loc, g, [&](int dv, int dk, const float (*x)[V]) {
-                if constexpr (SW) store_vec(Pk + sw_off<D>(dv - dv0, dk), x[0]);
+            state_rows<D, DH>(P, dv0, [&](int dv, int dk, const float *x) {
+                if constexpr (SW) {
+                    store4(Pk + sw_off<D>(dv, dk), x[0], x[1], x[2], x[3]);
+                } else {
 #pragma unroll
-                for (int j = 0; j < V; ++j) {
-                    if constexpr (!SW) Pk[(dk + j) * PDH + dv - dv0] = fromf<T>(x[0][j]);
-                    racc[j] += x[0][j] * x[1][j];
+                    for (int j = 0; j < 4; ++j) Pk[(dk + j) * PDH + dv] = x[j];
                 }
-            }, dv0);
+            });
             __syncthreads();
 #pragma unroll
             for (int k = 0; k < TO::PER_WAVE; ++k) {
                 int mi, ni;
-                if (!TO::get(k, mi, ni)) continue;
+                if (!TO::get(k, mi, ni, owave())) continue;
+                // (dQ accumulated transposed: lane = token row, 4 groups of 4
+                // consecutive channels)
                 if constexpr (SW)
-                    gemm_rc<D, DH>(dq[k], (const bf16 *)dOr + dv0, PD, mi * 32, (const bf16 *)Pk, ni * 32,
-                                   frag_offs<D>(l));
+                    gemm_rc_t<D, DH>(dq[k], (const bf16 *)dOr + dv0, PD, mi * 32, (const bf16 *)Pk, ni * 32,
+                                     frag_offs<D>(l));
                 else
-                    gemm<T, DH>(dq[k], dOr + dv0, PD, mi * 32, Pk, PDH, ni * 32);
+                    gemm<T, DH>(dq[k], Pk, PDH, ni * 32, dOr + dv0, PD, mi * 32, l);
             }
         }
-        // the threads sharing a dk group sum in a fixed order (no atomics:
-        // the result must not depend on timing)
-        constexpr int SLOTS = (NTHR * V < D * D ? NTHR * V : D * D) / D;
-        if (threadIdx.x * V < D * D) {
-#pragma unroll
-            for (int j = 0; j < V; ++j) rpart[threadIdx.x * V + j] = racc[j];
-        }
-        __syncthreads();
-        if (threadIdx.x < D) {
-            float r = 0.f;
-            for (int q = 0; q < SLOTS; ++q) r += rpart[q * D + threadIdx.x];
-            rho[threadIdx.x] = r;
-        }
+        // the chunk's sum over its tokens of q . 2^b (dO P^T), per channel: with
+        // the reverse walk's sum of k . 2^(b_last - b) (V R^T) it is the chunk's
+        // total of q dq - k dk exactly (the terms between the chunk's own tokens
+        // cancel over the whole chunk, a shift of all its running log-gates
+        // leaving them unchanged), free of those terms' rounding
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
-            if (TO::get(k, mi, ni)) {
-                const float sc = ex2(bS[mi * 32 * D + ni * 32 + (l & 31)]);   // 2^(b_mI) of column c
+            if (!TO::get(k, mi, ni, owave())) continue;
+            const int qs = mi * 32 + (l & 31), c0 = ni * 32 + (l >> 5) * 4;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dq[k][r] *= sc;
+            for (int q = 0; q < 4; ++q) {
+                float qv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (qs < Ct) load4f(Q + (int64_t)qs * D + c0 + 8 * q, qv);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a = half_sum(qv[e] * ex2(bS[qs * D + c0 + 8 * q + e]) * dq[k][4 * q + e]);
+                    if ((l & 31) == 0) Ap[mi][c0 + 8 * q + e] = a;
+                }
             }
+            // 2^(b_mI) of each column
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dq[k][r] *= ex2(bS[mi * 32 * D + ni * 32 + crow(r, l)]);
         }
-        // D_ = dO V^T (no gates), then K^T in three versions over the rows
-        __syncthreads();   // rho's partial sums are read before V's rows overwrite them
+        // D_ = dO V^T (no gates), then K^T in three versions
+        __syncthreads();
         T *Vr = U + L::ROWS;
         raw_store<T, D, GC, false>(rv, Vr, PD, Ct, RowId(), NoScale());
+        bool slow0, slow1;
         tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
-        scores(dOr, Vr, [](int ww) { return ww == 2 ? 32 : 0; }, false, false, false, no_exact, 7, true);
+        if (otid() < D) p.Tq[ch * D + otid()] = Ap[0][otid()] + Ap[1][otid()];
+        score_tiles<T, D, PD, PS>(Sc, dOr, Vr, [](int ww) { return ww == 2 ? 32 : 0; }, false, false, false,
+                                  no_exact, 7, true, Ct, slow0, slow1);
         __syncthreads();
-        // (bf16: the three versions as rows of a swizzled tile, read
-        // transposed; float32: transposed copies)
-        T *KT3 = U;   // (J=0 | ref row 0), (J=0 | ref 32), (J=1 | ref 32)
-        if constexpr (SW)
-            raw_store_sw<D, 96>(rk96, (bf16 *)KT3, Ct, krow,
-                                gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
-        else
-            raw_store<T, D, 96, true>(rk96, KT3, PK, Ct, krow,
-                                      gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }));
-        raw_load(rkq, K, Ct, RowId());   // K rows for B, in flight during A
+        // (bf16: the versions as rows of a swizzled tile, read transposed;
+        // float32: transposed copies) rows 0..31 with ref row 0 as tile rows
+        // 0..31, rows 0..63 with ref 32 as tile rows 32..95
+        T *KT3 = U;
+        if constexpr (SW) {
+            raw_store_sw<D, GC>(rk, (bf16 *)KT3, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return 0; }),
+                                [](int j) { return j < 32 ? j : -1; });
+            raw_store_sw<D, GC>(rk, (bf16 *)KT3, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return 32; }),
+                                [](int j) { return j + 32; });
+        } else {
+            raw_store_map<T, D, GC, true>(rk, KT3, PK, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return 0; }),
+                                          [](int j) { return j < 32 ? j : -1; });
+            raw_store_map<T, D, GC, true>(rk, KT3, PK, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return 32; }),
+                                          [](int j) { return j + 32; });
+        }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
-            if (!TO::get(k, mi, ni)) continue;
+            if (!TO::get(k, mi, ni, owave())) continue;
             const bool slow = mi == 0 ? slow0 : slow1;
             if constexpr (SW) {
                 const FragOffs<D> fo = frag_offs<D>(l);
-                if (mi == 1) gemm_rc<D, 32>(dq[k], (const bf16 *)Sc, PS, 32, (const bf16 *)KT3, ni * 32, fo, 32);
+                if (mi == 1) gemm_rc_t<D, 32>(dq[k], (const bf16 *)Sc, PS, 32, (const bf16 *)KT3, ni * 32, fo, 32);
                 if (!slow)
-                    gemm_rc<D, 32>(dq[k], (const bf16 *)Sc + 32 * mi, PS, 32 * mi, (const bf16 *)KT3, ni * 32,
-                                   fo, mi ? 64 : 0);
+                    gemm_rc_t<D, 32>(dq[k], (const bf16 *)Sc + 32 * mi, PS, 32 * mi, (const bf16 *)KT3, ni * 32,
+                                     fo, mi ? 64 : 0);
             } else {
-                if (mi == 1) gemm<T, 32>(dq[k], Sc, PS, 32, KT3 + 32, PK, ni * 32);
-                if (!slow) gemm<T, 32>(dq[k], Sc + 32 * mi, PS, 32 * mi, KT3 + (mi ? 64 : 0), PK, ni * 32);
+                if (mi == 1) gemm<T, 32>(dq[k], KT3 + 32, PK, ni * 32, Sc, PS, 32, l);
+                if (!slow) gemm<T, 32>(dq[k], KT3 + (mi ? 64 : 0), PK, ni * 32, Sc + 32 * mi, PS, 32 * mi, l);
             }
-            const int c = ni * 32 + (l & 31), m = mi * 32;
+            const int qs = mi * 32 + (l & 31), m = mi * 32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int qs = m + crow(r);
+                const int c = ni * 32 + crow(r, l);
                 dq[k][r] *= ex2(bS[qs * D + c] - bS[m * D + c]);
                 if (slow && qs < Ct) {
                     float acc = 0.f;
@@ -1052,48 +1107,159 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
                     dq[k][r] += acc;
                 }
             }
-            store_rows(dq[k], (T *)p.dQ + rb * D, D, mi * 32, ni * 32, Ct);
-            // q . dq goes to the log-gate gradient's rows for now (each element
-            // is read back by the lane that wrote it); dq's registers are then free
+            if constexpr (SW)
+                store_tile1_t(dq[k], (bf16 *)p.dQ + rb * D, D, mi * 32, ni * 32, Ct);
+            else
+                store_rows_t(dq[k], (T *)p.dQ + rb * D, D, mi * 32, ni * 32, Ct, l);
+            if (qs < Ct) {
+                const int c0 = ni * 32 + (l >> 5) * 4;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qs = m + crow(r);
-                if (qs < Ct) p.dLG[(rb + qs) * D + c] = tof(Q[(int64_t)qs * D + c]) * dq[k][r];
+                for (int q = 0; q < 4; ++q) {
+                    float qv[4];
+                    load4f(Q + (int64_t)qs * D + c0 + 8 * q, qv);
+                    store4(p.dLG + (rb + qs) * D + c0 + 8 * q, qv[0] * dq[k][4 * q], qv[1] * dq[k][4 * q + 1],
+                           qv[2] * dq[k][4 * q + 2], qv[3] * dq[k][4 * q + 3]);
+                }
             }
         }
+        if (!more) break;   // (the state after the segment is not needed)
+
+        // P <- Diag(2^(b_last)) P + (K 2^(b_last - b))^T V
+        __syncthreads();   // the products above have read KT3 and Sc
+        T *KU = U, *VU = U + UPD;
+        if constexpr (SW) {
+            raw_store_sw<D, GC>(rk, (bf16 *)KU, Ct, RowId(), LastRowScale<D, 8>(bS));
+            raw_store_sw<D, GC>(rv, (bf16 *)VU, Ct, RowId(), NoScale());
+        } else {
+            raw_store<T, D, GC, true>(rk, KU, PS, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return GC - 1; }));
+            raw_store<T, D, GC, true>(rv, VU, PS, Ct, RowId(), NoScale());
+        }
+        raw_load(rdo, (const T *)p.dO + (rb + GC) * D, Cn, RowId());
+        raw_load(rv, (const T *)p.V + (rb + GC) * D, Cn, RowId());
+        raw_load(rk, K + GC * D, Cn, RowId());
         __syncthreads();
+        state_decay<D>(P, bS);
+#pragma unroll
+        for (int k = 0; k < TL::PER_WAVE; ++k) {
+            int mi, ni;
+            if (!TL::get(k, mi, ni, owave())) continue;
+            if constexpr (SW)
+                gemm_cc<D, GC>(P[k], (const bf16 *)KU, mi * 32, (const bf16 *)VU, ni * 32, opaque(frag_offs<D>(l)));
+            else
+                gemm<T, GC>(P[k], KU, PS, mi * 32, VU, PS, ni * 32, l);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward 4: dV, dK and dlog_g, one workgroup per (segment, head), walking
+// the segment's chunks last to first with the reverse state R in registers,
+// from the segment's state Rseg; m'_J the last row of key tile J:
+//   dV = (K 2^(b_last - b)) R + sum_{I>=J} [A masked]_IJ^T dO_I   (A: the gated scores)
+//   dK = 2^(b_last - b) . (V R^T)
+//        + sum_{I>=J} 2^(b_mJ' - b) . ([D_ masked]_IJ^T (Q_I 2^(b - b_mJ')))
+//   dlog_g[s] = sum over the sequence's u >= s of (q_u dq_u - k_u dk_u)
+//   R <- Diag(2^(b_last)) R + (Q 2^b)^T dO
+// The suffix sum of dlog_g runs inside the chunk over the tokens' q dq - k dk
+// and is carried from chunk to chunk in registers as the chunks' totals,
+// formed from the inter-chunk terms only.  Its part beyond the segment is the
+// log-gate gradient of everything after it, rowsum(R . P) over the states at
+// the segment's end (the reverse state entering it from the right and the
+// forward state leaving it: the next segment's Pseg, or the sequence's final
+// state).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_walk_kv(Params p) {
+    using L = GradLds<T, D>;
+    constexpr int PD = L::PD, PS = L::PS, PK = L::PK, DH = L::DH, PDH = L::PDH;
+    constexpr bool SW = sizeof(T) == 2;
+    constexpr int UPD = SW ? GC * D : D * PS;
+    static_assert(96 * D <= L::SOFF && D * PK <= L::SOFF, "Q versions must not reach the scores");
+    static_assert(GC * D * 4 <= L::BYTES, "the log-gate rows fit");
+    static_assert(2 * UPD * (int)sizeof(T) <= L::BYTES, "update operands fit");
+    __shared__ float bS[GC * D];
+    __shared__ float Ep[GC / 32][D];   // row block mi's part of the chunk's k . dk-inter sums
+    __shared__ __attribute__((aligned(16))) char U_raw[L::BYTES];
+    T *U = (T *)U_raw;
+    T *Sc = U + L::SOFF;
+    using TO = Tiles<GC / 32, D / 32>;
+    using TL = Tiles<D / 32, D / 32>;
+    constexpr int NP = NTHR / D, RPP = GC / NP;   // log-gate gradient: parts of the rows per channel
+
+    const int h = blockIdx.x % p.H, gs = blockIdx.x / p.H;
+    Seq s;
+    int sl;
+    if (!seg_seq(p, gs, s, sl)) return;
+    const int64_t rb0 = row_base(p, s, h);
+    const int64_t sh = (int64_t)gs * p.H + h;
+    const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    const int nS = min(s.S, p.n_segs_ub - s.s0);
+
+    f32x16 R[TL::PER_WAVE];
+    state_load<D>(R, p.Rseg + sh * D * D);
+    // thread (channel c, part): the log-gate gradient beyond the current chunk
+    float carry;
+    {
+        const float *Rs = p.Rseg + sh * D * D;
+        const float *Pa = sl + 1 < nS ? p.Pseg + (sh + p.H) * D * D
+                                      : p.Pfin + ((int64_t)s.i * p.H + h) * D * D;
+        const int c = otid() % D, part = otid() / D;
+        float x = 0.f;
+        for (int dv = part; dv < D; dv += NP) x += Rs[dv * D + c] * Pa[dv * D + c];
+        bS[part * D + c] = x;
+        __syncthreads();
+        carry = 0.f;
+        for (int q = 0; q < NP; ++q) carry += bS[q * D + c];
     }
 
-    // ---- B: dV -------------------------------------------------------------
-    {
+    // the chunk's Q, K, dO rows (the next chunk's, loaded ahead) and V rows
+    // (loaded once K's have been staged for the last time)
+    Raw<T, D, GC> rq, rk, rdo, rv;
+    if (t0 < t1) {
+        const int64_t rb = rb0 + (int64_t)(t1 - 1) * GC;
+        const int Cl = min(GC, s.len - (t1 - 1) * GC);
+        raw_load(rq, (const T *)p.Q + rb * D, Cl, RowId());
+        raw_load(rk, (const T *)p.K + rb * D, Cl, RowId());
+        raw_load(rdo, (const T *)p.dO + rb * D, Cl, RowId());
+    }
+    for (int t = t1 - 1; t >= t0; --t) {
+        const int tok = t * GC;
+        const int Ct = min(GC, s.len - tok);
+        const bool more = t - 1 >= t0;   // (chunk t - 1 is full)
+        const int64_t rb = rb0 + tok;
+        const T *Q = (const T *)p.Q + rb * D;
+        const T *K = (const T *)p.K + rb * D;
+        const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
+        const int l = olane();   // (once per chunk: see otid)
+        chunk_gates<D>(bS, p.LG + rb * D, Ct);
+        auto exact = [&](int a, int b) { return exact_score<T, D>(Q, K, bS, a, b); };
+        auto no_exact = [](int, int) { return 0.f; };
+
+        // ---- dV ------------------------------------------------------------
         f32x16 dv[TO::PER_WAVE];
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) zero(dv[k]);
-        T *Rv = U, *Kl = U + L::RPART;   // R_t rows dv part [dv][dk]; K 2^(b_last - b) rows
-        raw_store<T, D, GC, false>(rkq, Kl, PD, Ct, RowId(),
-                                   gate_scale<T>(bS, D, [](int) { return GC - 1; }));
-        raw_load(rkq, Q, Ct, RowId());   // Q rows for B's scores
-        raw_load(rdo, dO, Ct, RowId());  // dO rows for dV, and for C
         {
-            const float *seg[1] = {Rs};
-            const void *loc[1] = {Rt};
-            const float *g[1] = {gR};
+            T *Rv = U, *Kl = U + L::RPART;   // R rows [dv part][dk]; K 2^(b_last - b) rows
             for (int hh = 0; hh < L::NHALF; ++hh) {
                 const int dv0 = hh * DH;
-                if (hh) __syncthreads();
-                for_states<T, D, 1, 2, DH>(seg, loc, g, [&](int dvv, int dk, const float (*x)[V]) {
-                    store_vec(Rv + (dvv - dv0) * PD + dk, x[0]);
-                }, dv0);
+                __syncthreads();   // (first half: bS is written; later: the last products are done)
+                if (!hh)
+                    raw_store<T, D, GC, false>(rk, Kl, PD, Ct, RowId(),
+                                               gate_scale<T>(bS, D, [](int) { return GC - 1; }));
+                state_rows<D, DH>(R, dv0, [&](int dvv, int dk, const float *x) {
+                    store4(Rv + dvv * PD + dk, x[0], x[1], x[2], x[3]);
+                });
                 __syncthreads();
 #pragma unroll
                 for (int k = 0; k < TO::PER_WAVE; ++k) {
                     int mi, ni;
-                    if (TO::get(k, mi, ni) && ni * 32 >= dv0 && ni * 32 < dv0 + DH) {
+                    if (TO::get(k, mi, ni, owave()) && ni * 32 >= dv0 && ni * 32 < dv0 + DH) {
                         // (bf16: dV accumulated transposed)
                         if constexpr (SW)
                             gemm_t<D>(dv[k], (const bf16 *)Kl, PD, mi * 32, (const bf16 *)Rv, PD, ni * 32 - dv0);
                         else
-                            gemm<T, D>(dv[k], Kl, PD, mi * 32, Rv, PD, ni * 32 - dv0);
+                            gemm<T, D>(dv[k], Kl, PD, mi * 32, Rv, PD, ni * 32 - dv0, l);
                     }
                 }
             }
@@ -1102,20 +1268,20 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
         // gated scores A (stored transposed, [key][query]): tiles (1,0), (1,1)
         // from K rows 0..63 with ref 32, then (0,0) from K rows 0..31 with ref 0
         T *Qg = U, *K64 = U + L::ROWS;
-        raw_store<T, D, GC, false>(rkq, Qg, PD, Ct, RowId(),
+        raw_store<T, D, GC, false>(rq, Qg, PD, Ct, RowId(),
                                    gate_scale<T>(bS, D, [](int j) { return j & ~31; }, true));
-        raw_store_map<T, D, 96, false>(rk96, K64, PD, Ct, krow,
-                                       gate_scale<T>(bS, D, [](int j) { return j < 32 ? 0 : 32; }),
-                                       [](int j) { return j - 32; });
+        raw_store<T, D, GC, false>(rk, K64, PD, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return 32; }));
+        bool slow0, slow1;
+        tile_spans<D>(bS, slow0, slow1);   // (its barrier also ends the staging)
+        score_tiles<T, D, PD, PS>(Sc, Qg, K64, [](int ww) { return ww == 2 ? 32 : 0; }, false, true, true,
+                                  exact, 6, true, Ct, slow0, slow1);
         __syncthreads();
-        auto exact = [&](int a, int b) { return exact_score<T, D>(Q, K, bS, a, b); };
-        scores(Qg, K64, [](int ww) { return ww == 2 ? 32 : 0; }, false, true, true, exact, 6, true);
-        __syncthreads();
-        raw_store_map<T, D, 96, false>(rk96, K64, PD, Ct, krow,
-                                       gate_scale<T>(bS, D, [](int) { return 0; }),
+        raw_store_map<T, D, GC, false>(rk, K64, PD, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return 0; }),
                                        [](int j) { return j < 32 ? j : -1; });
+        raw_load(rv, (const T *)p.V + rb * D, Ct, RowId());
         __syncthreads();
-        scores(Qg, K64, [](int) { return 0; }, false, true, true, exact, 1, false);
+        score_tiles<T, D, PD, PS>(Sc, Qg, K64, [](int) { return 0; }, false, true, true, exact, 1, false, Ct,
+                                  slow0, slow1);
         __syncthreads();
         T *OT = U;   // dO^T [dv][query] (bf16: dO rows, swizzled, read transposed)
         if constexpr (SW)
@@ -1126,115 +1292,112 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
-            if (!TO::get(k, mi, ni)) continue;
+            if (!TO::get(k, mi, ni, owave())) continue;
             if constexpr (SW) {
                 gemm_rc_t<D, GC>(dv[k], (const bf16 *)Sc, PS, mi * 32, (const bf16 *)OT, ni * 32, frag_offs<D>(l));
                 store_tile1_t(dv[k], (bf16 *)p.dV + rb * D, D, mi * 32, ni * 32, Ct);
             } else {
-                gemm<T, GC>(dv[k], Sc, PS, mi * 32, OT, PS, ni * 32);
-                store_rows(dv[k], (T *)p.dV + rb * D, D, mi * 32, ni * 32, Ct);
+                gemm<T, GC>(dv[k], Sc, PS, mi * 32, OT, PS, ni * 32, l);
+                store_rows(dv[k], (T *)p.dV + rb * D, D, mi * 32, ni * 32, Ct, olane());
             }
         }
         __syncthreads();
-    }
 
-    // ---- C: dK -------------------------------------------------------------
-    f32x16 dk[TO::PER_WAVE];
+        // ---- dK ------------------------------------------------------------
+        f32x16 dk[TO::PER_WAVE];
 #pragma unroll
-    for (int k = 0; k < TO::PER_WAVE; ++k) zero(dk[k]);
-    raw_load(rv, Vg, Ct, RowId());
-    raw_load(rk96, Q, Ct, qrow);   // Q rows of the three versions (the K registers are free)
-    raw_load(rkq, K, Ct, RowId());   // K rows for the X term
-    {
-        T *Vr = U, *RT = U + L::ROWS;   // V rows; R_t as [dk][dv part]
+        for (int k = 0; k < TO::PER_WAVE; ++k) zero(dk[k]);
+        T *Vr = U, *RT = U + L::ROWS;   // V rows; R as [dk][dv part]
         raw_store<T, D, GC, false>(rv, Vr, PD, Ct, RowId(), NoScale());
-        {
-            const float *seg[1] = {Rs};
-            const void *loc[1] = {Rt};
-            const float *g[1] = {gR};
-            for (int hh = 0; hh < L::NHALF; ++hh) {
-                const int dv0 = hh * DH;
-                if (hh) __syncthreads();
-                // (stored like P in phase A)
-                for_states<T, D, 1, 2, DH>(seg, loc, g, [&](int dvv, int dkk, const float (*x)[V]) {
-                    if constexpr (SW) {
-                        store_vec(RT + sw_off<D>(dvv - dv0, dkk), x[0]);
-                    } else {
+        for (int hh = 0; hh < L::NHALF; ++hh) {
+            const int dv0 = hh * DH;
+            if (hh) __syncthreads();
+            // (stored like P in the dQ walk)
+            state_rows<D, DH>(R, dv0, [&](int dvv, int dkk, const float *x) {
+                if constexpr (SW) {
+                    store4(RT + sw_off<D>(dvv, dkk), x[0], x[1], x[2], x[3]);
+                } else {
 #pragma unroll
-                        for (int j = 0; j < V; ++j) RT[(dkk + j) * PDH + dvv - dv0] = fromf<T>(x[0][j]);
-                    }
-                }, dv0);
-                __syncthreads();
+                    for (int j = 0; j < 4; ++j) RT[(dkk + j) * PDH + dvv] = x[j];
+                }
+            });
+            __syncthreads();
 #pragma unroll
-                for (int k = 0; k < TO::PER_WAVE; ++k) {
-                    int mi, ni;
-                    if (!TO::get(k, mi, ni)) continue;
-                    if constexpr (SW)
-                        gemm_rc<D, DH>(dk[k], (const bf16 *)Vr + dv0, PD, mi * 32, (const bf16 *)RT, ni * 32,
-                                       frag_offs<D>(l));
-                    else
-                        gemm<T, DH>(dk[k], Vr + dv0, PD, mi * 32, RT, PDH, ni * 32);
+            for (int k = 0; k < TO::PER_WAVE; ++k) {
+                int mi, ni;
+                if (!TO::get(k, mi, ni, owave())) continue;
+                // (dK accumulated transposed, as dQ in the dQ walk)
+                if constexpr (SW)
+                    gemm_rc_t<D, DH>(dk[k], (const bf16 *)Vr + dv0, PD, mi * 32, (const bf16 *)RT, ni * 32,
+                                     frag_offs<D>(l));
+                else
+                    gemm<T, DH>(dk[k], RT, PDH, ni * 32, Vr + dv0, PD, mi * 32, l);
+            }
+        }
+        // the chunk's sum over its tokens of k . 2^(b_last - b) (V R^T), per
+        // channel (see the dQ walk), then dk's scale for the in-chunk terms
+#pragma unroll
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (!TO::get(k, mi, ni, owave())) continue;
+            const int i = mi * 32 + (l & 31), mJ = mi * 32 + 31, c0 = ni * 32 + (l >> 5) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float kv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (i < Ct) load4f(K + (int64_t)i * D + c0 + 8 * q, kv);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = c0 + 8 * q + e;
+                    const float bl = bS[(GC - 1) * D + c];
+                    const float ep = half_sum(kv[e] * ex2(bl - bS[i * D + c]) * dk[k][4 * q + e]);
+                    if ((l & 31) == 0) Ep[mi][c] = ep;
+                    dk[k][4 * q + e] *= ex2(bl - bS[mJ * D + c]);
                 }
             }
         }
-        // K rows where R_t was (the products above have read it)
-        T *Kx = U + L::ROWS;
-        static_assert(2 * L::ROWS <= L::SOFF, "K rows must not reach the scores");
-        __syncthreads();
-        raw_store<T, D, GC, false>(rkq, Kx, PD, Ct, RowId(), NoScale());
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < TO::PER_WAVE; ++k) {
-            int mi, ni;
-            if (!TO::get(k, mi, ni)) continue;
-            // X = V R^T is in dk; rowsum(R_t . P_{t+1}) gets sum_i k_i 2^(b_last - b_i) X_i
-            const int c = ni * 32 + (l & 31), mJ = mi * 32 + 31;
-            const float bl = bS[(GC - 1) * D + c];
-            float ep = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = mi * 32 + crow(r);
-                if (i < Ct) ep += tof(Kx[i * PD + c]) * ex2(bl - bS[i * D + c]) * dk[k][r];
-            }
-            ep += __shfl_xor(ep, 32);
-            if (l < 32) Ep[mi][c] = ep;
-            const float sc = ex2(bl - bS[mJ * D + c]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dk[k][r] *= sc;
-        }
-        __syncthreads();
+        __syncthreads();   // R's parts have been read
         T *dOr = U + L::ROWS;   // D_^T = V dO^T (upper tiles), then Q^T in three versions
         raw_store<T, D, GC, false>(rdo, dOr, PD, Ct, RowId(), NoScale());
         __syncthreads();
-        scores(Vr, dOr, [](int ww) { return ww == 0 ? 0 : 32; }, true, false, false, no_exact, 7, true);
+        score_tiles<T, D, PD, PS>(Sc, Vr, dOr, [](int ww) { return ww == 0 ? 0 : 32; }, true, false, false,
+                                  no_exact, 7, true, Ct, slow0, slow1);
         __syncthreads();
-        T *QT3 = U;   // (I=0 | ref row 31), (I=1 | ref 31), (I=1 | ref 63), stored as KT3
-        if constexpr (SW)
-            raw_store_sw<D, 96>(rk96, (bf16 *)QT3, Ct, qrow,
-                                gate_scale<T>(bS, D, [](int j) { return j < 64 ? 31 : 63; }, true));
-        else
-            raw_store<T, D, 96, true>(rk96, QT3, PK, Ct, qrow,
-                                      gate_scale<T>(bS, D, [](int j) { return j < 64 ? 31 : 63; }, true));
+        // rows 0..63 with ref row 31 as tile rows 0..63, rows 32..63 with ref
+        // 63 as tile rows 64..95 (stored as the K versions of the dQ walk)
+        T *QT3 = U;
+        if constexpr (SW) {
+            raw_store_sw<D, GC>(rq, (bf16 *)QT3, Ct, RowId(),
+                                gate_scale<T>(bS, D, [](int) { return 31; }, true));
+            raw_store_sw<D, GC>(rq, (bf16 *)QT3, Ct, RowId(),
+                                gate_scale<T>(bS, D, [](int) { return 63; }, true),
+                                [](int j) { return j >= 32 ? j + 32 : -1; });
+        } else {
+            raw_store<T, D, GC, true>(rq, QT3, PK, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return 31; }, true));
+            raw_store_map<T, D, GC, true>(rq, QT3, PK, Ct, RowId(),
+                                          gate_scale<T>(bS, D, [](int) { return 63; }, true),
+                                          [](int j) { return j >= 32 ? j + 32 : -1; });
+        }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TO::PER_WAVE; ++k) {
             int mi, ni;
-            if (!TO::get(k, mi, ni)) continue;
+            if (!TO::get(k, mi, ni, owave())) continue;
             const bool slow = mi == 0 ? slow0 : slow1;
             if constexpr (SW) {
                 const FragOffs<D> fo = frag_offs<D>(l);
-                if (mi == 0) gemm_rc<D, 32>(dk[k], (const bf16 *)Sc + 32, PS, 0, (const bf16 *)QT3, ni * 32, fo, 32);
+                if (mi == 0)
+                    gemm_rc_t<D, 32>(dk[k], (const bf16 *)Sc + 32, PS, 0, (const bf16 *)QT3, ni * 32, fo, 32);
                 if (!slow)
-                    gemm_rc<D, 32>(dk[k], (const bf16 *)Sc + 32 * mi, PS, 32 * mi, (const bf16 *)QT3, ni * 32,
-                                   fo, mi ? 64 : 0);
+                    gemm_rc_t<D, 32>(dk[k], (const bf16 *)Sc + 32 * mi, PS, 32 * mi, (const bf16 *)QT3, ni * 32,
+                                     fo, mi ? 64 : 0);
             } else {
-                if (mi == 0) gemm<T, 32>(dk[k], Sc + 32, PS, 0, QT3 + 32, PK, ni * 32);
-                if (!slow) gemm<T, 32>(dk[k], Sc + 32 * mi, PS, 32 * mi, QT3 + (mi ? 64 : 0), PK, ni * 32);
+                if (mi == 0) gemm<T, 32>(dk[k], QT3 + 32, PK, ni * 32, Sc + 32, PS, 0, l);
+                if (!slow) gemm<T, 32>(dk[k], QT3 + (mi ? 64 : 0), PK, ni * 32, Sc + 32 * mi, PS, 32 * mi, l);
             }
-            const int c = ni * 32 + (l & 31), mJ = mi * 32 + 31;
+            const int i = mi * 32 + (l & 31), mJ = mi * 32 + 31;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int i = mi * 32 + crow(r);
+                const int c = ni * 32 + crow(r, l);
                 dk[k][r] *= ex2(bS[mJ * D + c] - bS[i * D + c]);
                 if (slow && i < Ct) {
                     float acc = 0.f;
@@ -1245,60 +1408,87 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_grads(Params 
                     dk[k][r] += acc;
                 }
             }
-            store_rows(dk[k], (T *)p.dK + rb * D, D, mi * 32, ni * 32, Ct);
+            if constexpr (SW)
+                store_tile1_t(dk[k], (bf16 *)p.dK + rb * D, D, mi * 32, ni * 32, Ct);
+            else
+                store_rows_t(dk[k], (T *)p.dK + rb * D, D, mi * 32, ni * 32, Ct, l);
         }
         __syncthreads();
-    }
 
-    // ---- D: log-gate gradient ------------------------------------------------
-    float *dBs = (float *)U_raw;   // [GC][D]: q dq - k dk
+        // ---- log-gate gradient ---------------------------------------------
+        float *dBs = (float *)U_raw;   // [GC][D]: q dq - k dk
 #pragma unroll
-    for (int k = 0; k < TO::PER_WAVE; ++k) {
-        int mi, ni;
-        if (!TO::get(k, mi, ni)) continue;
-        const int c = ni * 32 + (l & 31);
+        for (int k = 0; k < TO::PER_WAVE; ++k) {
+            int mi, ni;
+            if (!TO::get(k, mi, ni, owave())) continue;
+            const int su = mi * 32 + (l & 31), c0 = ni * 32 + (l >> 5) * 4;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int su = mi * 32 + crow(r);
-            float x = 0.f;
-            if (su < Ct) x = p.dLG[(rb + su) * D + c] - tof(K[(int64_t)su * D + c]) * dk[k][r];
-            dBs[su * D + c] = x;
+            for (int q = 0; q < 4; ++q) {
+                float x[4] = {0.f, 0.f, 0.f, 0.f};
+                if (su < Ct) {
+                    float kv[4];
+                    load4f(K + (int64_t)su * D + c0 + 8 * q, kv);
+                    load4f(p.dLG + (rb + su) * D + c0 + 8 * q, x);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] -= kv[e] * dk[k][4 * q + e];
+                }
+                store4(dBs + su * D + c0 + 8 * q, x[0], x[1], x[2], x[3]);
+            }
         }
-    }
-    __syncthreads();
-    {   // suffix sums over the chunk's rows, NTHR / D parts per channel, plus
-        // rowsum(R_t . P_{t+1}) = 2^(b_last) rho + Ep
-        constexpr int NP = NTHR / D, RPP = GC / NP;
-        const int c = threadIdx.x % D, part = threadIdx.x / D, r0 = part * RPP;
-        float x[RPP];
-#pragma unroll
-        for (int j = 0; j < RPP; ++j) x[j] = dBs[(r0 + j) * D + c];
-#pragma unroll
-        for (int j = RPP - 2; j >= 0; --j) x[j] += x[j + 1];
         __syncthreads();
-        dBs[part * D + c] = x[0];
+        {   // suffix sums over the chunk's rows, NP parts per channel, plus the carry
+            const int c = otid() % D, part = otid() / D, r0 = part * RPP;
+            float x[RPP];
+#pragma unroll
+            for (int j = 0; j < RPP; ++j) x[j] = dBs[(r0 + j) * D + c];
+#pragma unroll
+            for (int j = RPP - 2; j >= 0; --j) x[j] += x[j + 1];
+            __syncthreads();
+            dBs[part * D + c] = x[0];
+            __syncthreads();
+            float off = carry;
+            for (int q = part + 1; q < NP; ++q) off += dBs[q * D + c];
+            // the chunk's total of q dq - k dk from the inter terms (see above)
+            carry += p.Tq[ch * D + c] - (Ep[0][c] + Ep[1][c]);
+            int o0 = r0 * D + c, nrow = Ct - r0;
+            asm volatile("" : "+v"(o0), "+v"(nrow));
+            float *out = p.dLG + rb * D + o0;
+#pragma unroll
+            for (int j = 0; j < RPP; ++j)
+                if (j < nrow) out[j * D] = x[j] + off;
+        }
+        if (!more) break;
+
+        // R <- Diag(2^(b_last)) R + (Q 2^b)^T dO
+        __syncthreads();   // the part sums have been read
+        T *QU = U, *OU = U + UPD;
+        if constexpr (SW) {
+            raw_store_sw<D, GC>(rq, (bf16 *)QU, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return -1; }));
+            raw_store_sw<D, GC>(rdo, (bf16 *)OU, Ct, RowId(), NoScale());
+        } else {
+            raw_store<T, D, GC, true>(rq, QU, PS, Ct, RowId(), gate_scale<T>(bS, D, [](int) { return -1; }));
+            raw_store<T, D, GC, true>(rdo, OU, PS, Ct, RowId(), NoScale());
+        }
+        raw_load(rq, Q - GC * D, GC, RowId());
+        raw_load(rk, K - GC * D, GC, RowId());
+        raw_load(rdo, (const T *)p.dO + (rb - GC) * D, GC, RowId());
         __syncthreads();
-        float ep = 0.f;
+        state_decay<D>(R, bS);
 #pragma unroll
-        for (int mi = 0; mi < GC / 32; ++mi) ep += Ep[mi][c];
-        float off = ex2(bS[(GC - 1) * D + c]) * rho[c] + ep;
-        for (int q = part + 1; q < NP; ++q) off += dBs[q * D + c];
-        // (the row offsets formed here, opaque to the compiler, rather than
-        // computed at the kernel start and kept in registers throughout)
-        int o0 = r0 * D + c, nrow = Ct - r0;
-        asm volatile("" : "+v"(o0), "+v"(nrow));
-        float *out = p.dLG + rb * D + o0;
-#pragma unroll
-        for (int j = 0; j < RPP; ++j)
-            if (j < nrow) out[j * D] = x[j] + off;
+        for (int k = 0; k < TL::PER_WAVE; ++k) {
+            int mi, ni;
+            if (!TL::get(k, mi, ni, owave())) continue;
+            if constexpr (SW)
+                gemm_cc<D, GC>(R[k], (const bf16 *)QU, mi * 32, (const bf16 *)OU, ni * 32, opaque(frag_offs<D>(l)));
+            else
+                gemm<T, GC>(R[k], QU, PS, mi * 32, OU, PS, ni * 32, l);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-static inline int round8g(int n) { return (n + 7) & ~7; }
-
 template <typename T, int D>
 static hipError_t gfwd(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
@@ -1308,8 +1498,7 @@ static hipError_t gfwd(const Params &p, bool with_output, hipStream_t st, hipEve
     LASP_TRY(rec_event(ev, 1, st));
     LASP_TRY(launch_k(k_gfwd_segscan<D>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
     LASP_TRY(rec_event(ev, 2, st));
-    if (with_output)
-        LASP_TRY(launch_k(k_gfwd_out<T, D>, dim3(round8g(p.n_chunks_ub * p.H)), dim3(NTHR), st, p));
+    if (with_output) LASP_TRY(launch_k(k_gfwd_walk<T, D>, dim3(p.n_segs_ub * p.H), dim3(NTHR), st, p));
     return rec_event(ev, 3, st);
 }
 
@@ -1322,12 +1511,13 @@ static hipError_t gbwd(const Params &p, hipStream_t st, hipEvent_t *ev) {
     LASP_TRY(rec_event(ev, 1, st));
     LASP_TRY(launch_k(k_gbwd_segscan<D>, dim3(p.nseq * p.H * NB), dim3(NTHR), st, p));
     LASP_TRY(rec_event(ev, 2, st));
-    LASP_TRY(launch_k(k_gbwd_grads<T, D>, dim3(round8g(p.n_chunks_ub * p.H)), dim3(NTHR), st, p));
+    LASP_TRY(launch_k(k_gbwd_walk_q<T, D>, dim3(p.n_segs_ub * p.H), dim3(NTHR), st, p));
+    LASP_TRY(launch_k(k_gbwd_walk_kv<T, D>, dim3(p.n_segs_ub * p.H), dim3(NTHR), st, p));
     return rec_event(ev, 3, st);
 }
 
 hipError_t launch_fwd_gated(const Params &p, bool bf, bool with_output, hipStream_t st, hipEvent_t *ev) {
-    if (p.C != GC || !p.LG || !p.Gc || !p.Gs) return hipErrorInvalidValue;
+    if (p.C != GC || !p.LG || !p.Gs || !p.Pfin) return hipErrorInvalidValue;
     switch (p.D) {
     case 32: return bf ? gfwd<bf16, 32>(p, with_output, st, ev) : gfwd<float, 32>(p, with_output, st, ev);
     case 64: return bf ? gfwd<bf16, 64>(p, with_output, st, ev) : gfwd<float, 64>(p, with_output, st, ev);
@@ -1337,7 +1527,7 @@ hipError_t launch_fwd_gated(const Params &p, bool bf, bool with_output, hipStrea
 }
 
 hipError_t launch_bwd_gated(const Params &p, bool bf, hipStream_t st, hipEvent_t *ev) {
-    if (p.C != GC || !p.LG || !p.dLG || !p.Gc || !p.Gs || !p.Hc) return hipErrorInvalidValue;
+    if (p.C != GC || !p.LG || !p.dLG || !p.Gs || !p.Pfin || !p.Tq) return hipErrorInvalidValue;
     switch (p.D) {
     case 32: return bf ? gbwd<bf16, 32>(p, st, ev) : gbwd<float, 32>(p, st, ev);
     case 64: return bf ? gbwd<bf16, 64>(p, st, ev) : gbwd<float, 64>(p, st, ev);

@@ -47,9 +47,10 @@ struct Params {
     // gated form
     const float *LG;   // [B, H, N, D] f32 log-gates (key channels)
     float *dLG;        // [B, H, N, D] f32 log-gate gradient
-    float *Gc;         // [chunks][H][D] f32: gate product of the segment's chunks before each chunk
+    float *Gc;         // [chunks][H][D] f32 or null: gate product of the segment's chunks before each chunk
     float *Gs;         // [segs][H][D] f32: gate product of each segment
-    float *Hc;         // [chunks][H][D] f32: gate product of the segment's chunks after each chunk
+    float *Hc;         // [chunks][H][D] f32 or null: gate product of the segment's chunks after each chunk
+    float *Tq;         // [chunks][H][D] f32: per chunk, sum over its tokens of q . (2^b (dO P_t^T))
 };
 
 // Enqueue the forward kernels: (packed-batch tables), local chunk states,

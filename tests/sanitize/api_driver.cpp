@@ -74,15 +74,15 @@ void check_params(const lasp::Params &p, bool fwd, bool bf16, bool gated, bool b
         ex.push_back({U(p.seg_prefix), (nseq + 1) * 4, "seg_prefix"});
         if (!p.chunk_prefix || !p.seg_prefix) fail("packed tables missing", "tables");
     }
-    const bool local = !bf16 || gated;
+    const bool local = !bf16 && !gated;   // float32 causal and unmasked forms
     if (local && !p.Lc) fail("per-chunk states missing", "Lc");
     ex.push_back({U(p.Lc), local ? chunks * H * dd * esz : 0, "Lc"});
     ex.push_back({U(p.Pseg), segs * H * dd * 4, "Pseg"});
-    const bool fin = !gated;   // both dtypes: the unmasked form's row products read them
+    const bool fin = true;   // every form and dtype keeps the final states
     if (fin && !p.Pfin) fail("final states missing", "Pfin");
     ex.push_back({U(p.Pfin), fin ? nseq * H * dd * 4 : 0, "Pfin"});
     if (gated) {
-        ex.push_back({U(p.Gc), chunks * H * D * 4, "Gc"});
+        if (!p.Gs) fail("segment gate products missing", "Gs");
         ex.push_back({U(p.Gs), segs * H * D * 4, "Gs"});
     }
     if (fwd || p.Z) ex.push_back({U(p.Z), segs * H * dd * 4, "Z"});
@@ -92,7 +92,6 @@ void check_params(const lasp::Params &p, bool fwd, bool bf16, bool gated, bool b
         ex.push_back({U(p.W), segs * H * dd * 4, "W"});
         ex.push_back({U(p.Rfin), fin ? nseq * H * dd * 4 : 0, "Rfin"});
         if (fin && !p.Rfin) fail("reverse final states missing", "Rfin");
-        if (gated) ex.push_back({U(p.Hc), chunks * H * D * 4, "Hc"});
     }
     // the chunk and segment bounds cover every split of the tokens
     const int64_t T = ((int64_t)p.N + p.C - 1) / p.C;

@@ -217,9 +217,14 @@ def test_gated_rejects_bad_arguments(L):
     assert bwd(dLG=p[9]) == EINVAL and bwd(dLG=p[4]) == EINVAL       # dlog_g aliases
     assert fwd(ws_bytes=nf - 1) == EWS and bwd(ws_bytes=nb - 1) == EWS
     assert fwd(cu=p[8]) == EINVAL
-    # the gated state cache also holds per-chunk states and gate products
-    assert (L.lasp_gated_state_cache_bytes(ctypes.byref(s), 1)
-            > L.lasp_state_cache_bytes(ctypes.byref(s), 1))
+    # the gated state cache: the segments' entering states, each sequence's
+    # final state and the segments' gate products (float32), no per-chunk
+    # states (B1 H2 N300 d64: 5 chunks of 64, one chunk per segment)
+    def al(n):
+        return (n + 255) // 256 * 256
+    for dt in (0, 1):
+        assert (L.lasp_gated_state_cache_bytes(ctypes.byref(s), dt)
+                == al(5 * 2 * 64 * 64 * 4) + al(2 * 64 * 64 * 4) + al(5 * 2 * 64 * 4))
 
 
 SHAPES = [Shape(1, 32, 131072, 128, 256, 0), Shape(4, 16, 8192, 128, 256, 0),
