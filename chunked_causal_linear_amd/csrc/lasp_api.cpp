@@ -34,6 +34,7 @@ struct Plan {
     size_t seg_b;        // per-segment f32 states (Pseg, Z, Rseg or W)
     size_t fin_b;        // per-sequence f32 final states (Pfin)
     size_t chunk_v;      // gated backward: per-chunk f32 vectors of D (Tq)
+    size_t ck_b;         // gated backward: forward states at checkpoints inside segments (Pck)
     size_t gate_s;       // gated form: per-segment f32 gate products (Gs)
     size_t cache_b;      // state cache = [Lc][Pseg][Pfin][Gs]
 };
@@ -117,6 +118,8 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false,
     // backward's log-gate gradient of a sequence's last segment (both dtypes)
     pl.fin_b = align_up((size_t)pl.nseq * pl.H * dd * sizeof(float));
     pl.chunk_v = gated ? align_up((size_t)pl.n_chunks_ub * pl.H * pl.D * sizeof(float)) : 0;
+    pl.ck_b = gated ? align_up((size_t)pl.n_segs_ub * pl.H * ((pl.G - 1) / lasp::GATED_CK) * dd * sizeof(float))
+                    : 0;
     pl.gate_s = gated ? align_up((size_t)pl.n_segs_ub * pl.H * pl.D * sizeof(float)) : 0;
     pl.cache_b = pl.local_b + pl.seg_b + pl.fin_b + pl.gate_s;
     return LASP_OK;
@@ -127,7 +130,7 @@ size_t fwd_ws(const Plan &pl, bool cache) {
 }
 size_t bwd_ws(const Plan &pl, bool cache) {
     return pl.table_b + pl.local_b /*Rc*/ + 2 * pl.seg_b /*Rseg, W*/ + pl.fin_b /*Rfin*/ +
-           pl.chunk_v /*Tq*/ +
+           pl.chunk_v /*Tq*/ + pl.ck_b /*Pck*/ +
            (cache ? 0 : pl.cache_b + pl.seg_b /*Lc, Pseg, Pfin, Z*/);
 }
 
@@ -492,6 +495,8 @@ int bwd_common(const lasp_shape *shape, lasp_dtype dtype, const void *Q, const v
     w += pl.fin_b;
     p.Tq = pl.chunk_v ? (float *)w : nullptr;
     w += pl.chunk_v;
+    p.Pck = pl.ck_b ? (float *)w : nullptr;
+    w += pl.ck_b;
     p.LG = log_g;
     p.dLG = dlog_g;
     const hipStream_t hs = (hipStream_t)stream;

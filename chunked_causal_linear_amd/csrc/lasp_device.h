@@ -65,6 +65,8 @@ inline hipError_t rec_event(hipEvent_t *ev, int i, hipStream_t st) {
         if (lasp_e_ != hipSuccess) return lasp_e_;   \
     } while (0)
 
+constexpr int SCAN_BATCH = 8;   // segment totals loaded per round trip in the segment scans
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // A buffer descriptor for `bytes` bytes from p, made from lane 0's address and

@@ -492,10 +492,23 @@ __global__ __launch_bounds__(NTHR) void k_gfwd_segscan(Params p) {
     const int64_t mo = ((int64_t)ih * D + dk) * D + dv;   // [dk][dv] of the API states
     float P = p.M_in ? p.M_in[mo] : 0.f;
     const int nS = min(s.S, p.n_segs_ub - s.s0);
-    for (int sl = 0; sl < nS; ++sl) {
-        const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
-        p.Pseg[sh * D * D + e] = P;
-        P = p.Gs[sh * D + dk] * P + p.Z[sh * D * D + e];
+    // totals and gates loaded SCAN_BATCH segments at a time, ahead of the stores
+    for (int b0 = 0; b0 < nS; b0 += SCAN_BATCH) {
+        float z[SCAN_BATCH], g[SCAN_BATCH];
+#pragma unroll
+        for (int j = 0; j < SCAN_BATCH; ++j) {
+            const int64_t sh = (int64_t)(s.s0 + b0 + j) * p.H + h;
+            const bool in = b0 + j < nS;
+            z[j] = in ? p.Z[sh * D * D + e] : 0.f;
+            g[j] = in ? p.Gs[sh * D + dk] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < SCAN_BATCH; ++j) {
+            if (b0 + j < nS) {
+                p.Pseg[((int64_t)(s.s0 + b0 + j) * p.H + h) * D * D + e] = P;
+                P = g[j] * P + z[j];
+            }
+        }
     }
     if (p.M_out) p.M_out[mo] = P;
     if (p.Pfin) p.Pfin[(int64_t)ih * D * D + e] = P;   // [dv][dk], as Pseg
@@ -552,8 +565,56 @@ __device__ __forceinline__ void state_load(f32x16 *S, const float *src) {   // s
     for (int k = 0; k < TL::PER_WAVE; ++k) {
         int mi, ni;
         if (!TL::get(k, mi, ni, owave())) continue;
+        // (the lane's dk are 4 runs of 4 consecutive channels: 16-byte loads)
+        const float *row = src + (ni * 32 + (l & 31)) * D + mi * 32 + (l >> 5) * 4;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[k][r] = src[(ni * 32 + (l & 31)) * D + mi * 32 + crow(r, l)];
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = *(const float4 *)(row + 8 * q);
+            S[k][4 * q] = v.x;
+            S[k][4 * q + 1] = v.y;
+            S[k][4 * q + 2] = v.z;
+            S[k][4 * q + 3] = v.w;
+        }
+    }
+}
+
+// The state into dst [dv][dk] (float32), 16-byte stores.
+template <int D>
+__device__ __forceinline__ void state_store(const f32x16 *S, float *dst) {
+    using TL = Tiles<D / 32, D / 32>;
+    const int l = olane();
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) {
+        int mi, ni;
+        if (!TL::get(k, mi, ni, owave())) continue;
+        float *row = dst + (ni * 32 + (l & 31)) * D + mi * 32 + (l >> 5) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) store4(row + 8 * q, S[k][4 * q], S[k][4 * q + 1], S[k][4 * q + 2], S[k][4 * q + 3]);
+    }
+}
+
+// part[ni][dk] = sum over the dv of block ni of S[dk][dv] X[dk][dv], X given
+// as src [dv][dk] (float32): the row sums of S . X once the D/32 parts of each
+// dk are added (by the caller, after a barrier).
+template <int D>
+__device__ __forceinline__ void state_rowdot(const f32x16 *S, const float *src, float (*part)[D]) {
+    using TL = Tiles<D / 32, D / 32>;
+    const int l = olane();
+#pragma unroll
+    for (int k = 0; k < TL::PER_WAVE; ++k) {
+        int mi, ni;
+        if (!TL::get(k, mi, ni, owave())) continue;
+        const float *row = src + (ni * 32 + (l & 31)) * D + mi * 32 + (l >> 5) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = *(const float4 *)(row + 8 * q);
+            const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float y = half_sum(S[k][4 * q + e] * x[e]);
+                if ((l & 31) == 0) part[ni][mi * 32 + 8 * q + (l >> 5) * 4 + e] = y;
+            }
+        }
     }
 }
 
@@ -882,10 +943,23 @@ __global__ __launch_bounds__(NTHR) void k_gbwd_segscan(Params p) {
     const int64_t mo = ((int64_t)ih * D + dk) * D + dv;
     float R = p.dM_out ? p.dM_out[mo] : 0.f;
     const int nS = min(s.S, p.n_segs_ub - s.s0);
-    for (int sl = nS - 1; sl >= 0; --sl) {
-        const int64_t sh = (int64_t)(s.s0 + sl) * p.H + h;
-        p.Rseg[sh * D * D + e] = R;
-        R = p.Gs[sh * D + dk] * R + p.W[sh * D * D + e];
+    // (last segment first; loads batched as in the forward scan)
+    for (int b0 = nS - 1; b0 >= 0; b0 -= SCAN_BATCH) {
+        float wv[SCAN_BATCH], g[SCAN_BATCH];
+#pragma unroll
+        for (int j = 0; j < SCAN_BATCH; ++j) {
+            const int64_t sh = (int64_t)(s.s0 + b0 - j) * p.H + h;
+            const bool in = b0 - j >= 0;
+            wv[j] = in ? p.W[sh * D * D + e] : 0.f;
+            g[j] = in ? p.Gs[sh * D + dk] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < SCAN_BATCH; ++j) {
+            if (b0 - j >= 0) {
+                p.Rseg[((int64_t)(s.s0 + b0 - j) * p.H + h) * D * D + e] = R;
+                R = g[j] * R + wv[j];
+            }
+        }
     }
     if (p.dM_in) p.dM_in[mo] = R;
 }
@@ -1148,6 +1222,11 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_walk_q(Params
             else
                 gemm<T, GC>(P[k], KU, PS, mi * 32, VU, PS, ni * 32, l);
         }
+        // every GATED_CK chunks inside the segment: P for the reverse walk's
+        // exact reset of its log-gate gradient sum
+        const int done = t - t0 + 1;
+        if (p.Pck && done % GATED_CK == 0)
+            state_store<D>(P, p.Pck + (sh * ((p.G - 1) / GATED_CK) + done / GATED_CK - 1) * D * D);
     }
 }
 
@@ -1179,6 +1258,7 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_walk_kv(Param
     static_assert(2 * UPD * (int)sizeof(T) <= L::BYTES, "update operands fit");
     __shared__ float bS[GC * D];
     __shared__ float Ep[GC / 32][D];   // row block mi's part of the chunk's k . dk-inter sums
+    __shared__ float Cp[D / 32][D];    // dv block ni's part of rowsum(R . P) at a checkpoint
     __shared__ __attribute__((aligned(16))) char U_raw[L::BYTES];
     T *U = (T *)U_raw;
     T *Sc = U + L::SOFF;
@@ -1231,7 +1311,18 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_walk_kv(Param
         const T *K = (const T *)p.K + rb * D;
         const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
         const int l = olane();   // (once per chunk: see otid)
-        chunk_gates<D>(bS, p.LG + rb * D, Ct);
+        // a checkpoint after this chunk: the carry is reset there to its exact
+        // value, rowsum(R_t . P_{t+1}), the running sum's rounding dropped
+        const int done = t - t0 + 1;
+        const bool ck = p.Pck && done % GATED_CK == 0 && t + 1 < t1;
+        if (ck) state_rowdot<D>(R, p.Pck + (sh * ((p.G - 1) / GATED_CK) + done / GATED_CK - 1) * D * D, Cp);
+        chunk_gates<D>(bS, p.LG + rb * D, Ct);   // (its barriers also publish Cp)
+        if (ck) {
+            const int c = otid() % D;
+            carry = 0.f;
+#pragma unroll
+            for (int q = 0; q < D / 32; ++q) carry += Cp[q][c];
+        }
         auto exact = [&](int a, int b) { return exact_score<T, D>(Q, K, bS, a, b); };
         auto no_exact = [](int, int) { return 0.f; };
 

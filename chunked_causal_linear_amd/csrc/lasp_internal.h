@@ -6,6 +6,11 @@
 
 namespace lasp {
 
+// Gated backward: the forward state is kept at every GATED_CK-th chunk boundary
+// inside a segment, where the log-gate gradient's running sum is reset to its
+// exact value.
+constexpr int GATED_CK = 8;
+
 // Everything a kernel needs, by value in the kernel argument segment.
 //
 // Work decomposition (one head h of one sequence i, T chunks of length C, the
@@ -51,6 +56,8 @@ struct Params {
     float *Gs;         // [segs][H][D] f32: gate product of each segment
     float *Hc;         // [chunks][H][D] f32 or null: gate product of the segment's chunks after each chunk
     float *Tq;         // [chunks][H][D] f32: per chunk, sum over its tokens of q . (2^b (dO P_t^T))
+    float *Pck;        // [segs][H][(G-1)/GATED_CK][D][D] f32: forward states at every GATED_CK-th
+                       // chunk boundary inside each segment, [dv][dk]
 };
 
 // Enqueue the forward kernels: (packed-batch tables), local chunk states,

@@ -152,8 +152,6 @@ __global__ __launch_bounds__(NTHR) void k_fwd_local(Params p) {
 //   Pseg[0] = M_in;  Pseg[s+1] = lambda^len_s Pseg[s] + Z[s];  M_out = Pfin = last.
 // (LASP-2 prefix sum of gathered states; LASP Alg. 2 receive/send as a scan.)
 // ---------------------------------------------------------------------------
-constexpr int SCAN_BATCH = 8;   // segment totals loaded per round trip in the scans
-
 template <int D, typename T>
 __global__ __launch_bounds__(NTHR) void k_fwd_segscan(Params p) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;

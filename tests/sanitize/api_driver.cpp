@@ -92,6 +92,11 @@ void check_params(const lasp::Params &p, bool fwd, bool bf16, bool gated, bool b
         ex.push_back({U(p.W), segs * H * dd * 4, "W"});
         ex.push_back({U(p.Rfin), fin ? nseq * H * dd * 4 : 0, "Rfin"});
         if (fin && !p.Rfin) fail("reverse final states missing", "Rfin");
+        if (gated) {
+            if (!p.Tq) fail("per-chunk sums missing", "Tq");
+            ex.push_back({U(p.Tq), chunks * H * D * 4, "Tq"});
+            ex.push_back({U(p.Pck), segs * H * ((p.G - 1) / lasp::GATED_CK) * dd * 4, "Pck"});
+        }
     }
     // the chunk and segment bounds cover every split of the tokens
     const int64_t T = ((int64_t)p.N + p.C - 1) / p.C;
