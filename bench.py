@@ -344,31 +344,35 @@ def bench_bidir(a, w, sh, inp, torch, cca):
 def gated_work(sh, P):
     """Algorithmic HBM bytes and flops per launch of the gated kernels (U token-
     heads, e element bytes, log-gates and their gradient float32).  P: the
-    library's array sizes (local_b per-chunk states, seg_b per-segment float32
-    states, gate_c / gate_s per-chunk / per-segment gate products).  Flops count
-    useful causal work: intra-chunk products over c <= r (2d(C+1) per output
-    role) and the d x d state products (2d^2 each)."""
+    library's array sizes (seg_b per-segment float32 states, gate_s per-segment
+    gate products, fin_b final states).  Bytes: the token rows each kernel needs,
+    its outputs and the segment states it reads or writes; the backward walks'
+    intermediate arrays (q . dq parked in the log-gate gradient, per-chunk sums,
+    state checkpoints) are overhead, not counted.  Flops count useful causal
+    work: intra-chunk products over c <= r (2d(C+1) per output role) and the
+    d x d state products (2d^2 each)."""
     B, H, N, d, C = sh["B"], sh["H"], sh["N"], sh["d"], sh["chunk"]
     e = 2 if sh["dtype"] == "bf16" else 4
     U = B * H * N
     nS = sh["nseq"] or B
     st_io = nS * H * d * d * 4
     T, G = U * d * e, U * d * 4                  # one token array, the log-gate array
-    lb, sb, gc, gs = P["local_b"], P["seg_b"], P["gate_c"], P["gate_s"]
+    sb, gs, fb = P["seg_b"], P["gate_s"], P["fin_b"]
     intra = 2 * d * (C + 1)
     return {
-        "fwd_local": (2 * T + G + lb + sb + gc + gs, 2 * U * d * d),
-        "fwd_scan": (2 * sb + gs + 2 * st_io, sb // 2),
-        "fwd_out": (4 * T + G + lb + sb + gc, U * (intra + 2 * d * d)),
-        "bwd_local": (2 * T + G + lb + sb + gc, 2 * U * d * d),
+        "fwd_local": (2 * T + G + sb + gs, 2 * U * d * d),
+        "fwd_scan": (2 * sb + gs + fb + 2 * st_io, sb // 2),
+        "fwd_out": (4 * T + G + sb, U * (intra + 4 * d * d)),
+        "bwd_local": (2 * T + G + sb, 2 * U * d * d),
         "bwd_scan": (2 * sb + gs + 2 * st_io, sb // 2),
-        "bwd_grads": (7 * T + 2 * G + 2 * lb + 2 * sb + 2 * gc, U * (3 * intra + 8 * d * d)),
+        "bwd_grads": (11 * T + 3 * G + 2 * sb, U * (3 * intra + 10 * d * d)),
     }
 
 
 def bench_gated(a, w, sh, inp, torch, cca):
-    """One step = lasp_fwd_gated + lasp_bwd_gated (local states, scan, output;
-    reverse local states, reverse scan, gradients incl. the log-gate gradient),
+    """One step = lasp_fwd_gated + lasp_bwd_gated (segment totals, scan, output
+    walk; reverse segment totals, reverse scan, the dQ walk and the dV / dK /
+    log-gate gradient walk, timed together as bwd_grads),
     with per-kernel HIP events recorded on the launch stream inside the library."""
     Q, K, V, dO, LG = inp["Q"], inp["K"], inp["V"], inp["dO"], inp["log_g"]
     cu, M_in, dM_out = inp["cu_seqlens"], inp["M_in"], inp["dM_out"]
@@ -406,19 +410,15 @@ def bench_gated(a, w, sh, inp, torch, cca):
             kms[names[j]] += elapsed(L, evf[i][j], evf[i][j + 1]) / a.steps
             kms[names[3 + j]] += elapsed(L, evb[i][j], evb[i][j + 1]) / a.steps
     # array sizes from the size queries: fwd workspace with a cache = tables + Z;
-    # cache = Lc + Pseg + Gc + Gs; bwd workspace adds Rc, Rseg, W, Hc
+    # cache = Pseg + Pfin + Gs
     U, d = sh["B"] * sh["H"] * sh["N"], sh["d"]
     e = 2 if w.dtype == "bf16" else 4
     table_b = 0 if not sh["nseq"] else -(-8 * (sh["nseq"] + 1) // 256) * 256
     seg_b = cca.gated_fwd_workspace_bytes(S, dt_code, True) - table_b
     cache_b = cca.gated_state_cache_bytes(S, dt_code)
-    bws = cca.gated_bwd_workspace_bytes(S, dt_code, True) - table_b
-    # bws = local_b + 2 seg_b + gate_c;  cache_b = local_b + seg_b + gate_c + gate_s
-    chunks = (sh["N"] + C - 1) // C * sh["B"] if not sh["nseq"] else sh["N"] // C + sh["nseq"]
-    gate_c = -(-chunks * sh["H"] * d * 4 // 256) * 256
-    local_b = bws - 2 * seg_b - gate_c
-    gate_s = cache_b - local_b - seg_b - gate_c
-    work = gated_work(sh, dict(local_b=local_b, seg_b=seg_b, gate_c=gate_c, gate_s=gate_s))
+    fin_b = -(-(sh["nseq"] or sh["B"]) * sh["H"] * d * d * 4 // 256) * 256
+    gate_s = cache_b - seg_b - fin_b
+    work = gated_work(sh, dict(seg_b=seg_b, gate_s=gate_s, fin_b=fin_b))
     dom = max(names, key=lambda k: kms[k])
     bytes_, flops = work[dom]
     t_dom = kms[dom] * 1e-3

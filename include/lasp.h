@@ -298,8 +298,14 @@ int lasp_bwd_bidir_ex(const lasp_shape *shape, lasp_dtype dtype,
  * 2^(b_m - b_i) (b: running log2 of the gates; m: the first row of a 32-row
  * query tile), each at most 1 off the diagonal tiles; a diagonal tile whose
  * gates fall by more than 2^80 is summed pair by pair in float32 instead.
+ * The log-gate gradient of a token is a suffix sum over the sequence; inside
+ * a chunk it is summed token by token, across chunks it is carried from the
+ * chunks' totals formed from the inter-chunk terms alone, and reset to its
+ * exact value rowsum(R . P) of the states at every 8th chunk boundary and at
+ * each segment's end.
  * Sizes come from the lasp_gated_* queries or lasp_query_sizes with form 1 (the
- * gated state cache also holds per-chunk gate products); buffers, pointers,
+ * gated state cache holds the segment states, each sequence's final state and
+ * the segments' gate products: no per-chunk data); buffers, pointers,
  * alignment, errors and the knobs of the _ex variants are as for lasp_fwd /
  * lasp_bwd (no decay argument). */
 size_t lasp_gated_state_cache_bytes(const lasp_shape *shape, lasp_dtype dtype);
