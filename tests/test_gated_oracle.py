@@ -321,6 +321,32 @@ def test_log_gate_gradient_as_a_suffix_sum():
     np.testing.assert_allclose(np.sum(R * ma, axis=1), dB[s:].sum(axis=0), rtol=1e-9, atol=1e-10)
 
 
+@pytest.mark.parametrize("a,b", [(0, 21), (5, 13), (20, 21), (0, 1), (7, 8)])
+def test_span_total_from_the_inter_span_terms(a, b):
+    """The identity the HIP backward carries its log-gate gradient sum with:
+    over a span of tokens [a, b), the total of q_u dq_u - k_u dk_u equals that
+    of the terms through the states at the span's ends only,
+        sum_u q_u exp(C_u) (dO_u P^T) - k_u exp(C_last - C_u) (V_u R^T),
+    C_u the running log-gate from the span start to u, P the state entering
+    the span, R the gradient reaching the state after it (the terms between
+    two tokens of the span cancel: a common shift of the span's running
+    log-gates leaves them unchanged)."""
+    L, d = 21, 4
+    q, k, v, lg, do, m, dm = case(L, d, 19, strong=True)
+    dq, dk, _, _, _ = go.gated_recurrent_bwd(q, k, v, lg, do, m, dm)
+    P = go.gated_recurrent_fwd(q[:a], k[:a], v[:a], lg[:a], m)[1] if a else m
+    _, mb = go.gated_recurrent_fwd(q[:b], k[:b], v[:b], lg[:b], m)
+    R = go.gated_recurrent_bwd(q[b:], k[b:], v[b:], lg[b:], do[b:], mb, dm)[4] if b < L else dm
+    C = np.cumsum(lg[a:b], axis=0)
+    rhs = (q[a:b] * np.exp(C) * (do[a:b] @ P.T) - k[a:b] * np.exp(C[-1] - C) * (v[a:b] @ R.T)).sum(axis=0)
+    lhs = (q[a:b] * dq[a:b] - k[a:b] * dk[a:b]).sum(axis=0)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-9, atol=1e-10)
+    # and not with the in-span terms: they do not vanish token by token
+    if b - a > 1:
+        assert not np.allclose(q[a:b] * dq[a:b] - k[a:b] * dk[a:b],
+                               q[a:b] * np.exp(C) * (do[a:b] @ P.T) - k[a:b] * np.exp(C[-1] - C) * (v[a:b] @ R.T))
+
+
 @pytest.mark.parametrize("L,d,seed", [(1, 4, 0), (7, 3, 1), (200, 8, 2), (600, 16, 3)])
 def test_sampled_sweep_matches_rows_and_closed_states(L, d, seed):
     """gated_sampled_sweep regroups the sums of gated_sampled (rows) and
