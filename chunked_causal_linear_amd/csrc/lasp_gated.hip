@@ -264,6 +264,24 @@ __device__ __forceinline__ float half_sum(float x) {
     return x;
 }
 
+// x[0..15] summed over the 32 lanes of each half of the wave, 16 exchanges in
+// all: at each step a lane keeps half of its values and adds its partner's
+// copy of them (partner lane ^ 16, 8, 4, 2), then the pair (lane ^ 1) adds.
+// Returns, in lanes 2r and 2r + 1 of each half, the sum of x[r].
+__device__ __forceinline__ float half_colsum16(float *x, int l) {
+#pragma unroll
+    for (int m = 16, n = 8; m >= 2; m >>= 1, n >>= 1) {
+        const bool hi = (l & m) != 0;
+#pragma unroll
+        for (int j = 0; j < n; ++j) {
+            const float send = hi ? x[j] : x[j + n];
+            const float keep = hi ? x[j + n] : x[j];
+            x[j] = keep + __shfl_xor(send, m);
+        }
+    }
+    return x[0] + __shfl_xor(x[0], 1);
+}
+
 // 4 consecutive elements of a bf16 or float32 row as floats.
 __device__ __forceinline__ void load4f(const bf16 *p, float *f) {
     const uint2 v = *(const uint2 *)p;
@@ -1113,16 +1131,16 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_walk_q(Params
             int mi, ni;
             if (!TO::get(k, mi, ni, owave())) continue;
             const int qs = mi * 32 + (l & 31), c0 = ni * 32 + (l >> 5) * 4;
+            float x[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float qv[4] = {0.f, 0.f, 0.f, 0.f};
                 if (qs < Ct) load4f(Q + (int64_t)qs * D + c0 + 8 * q, qv);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float a = half_sum(qv[e] * ex2(bS[qs * D + c0 + 8 * q + e]) * dq[k][4 * q + e]);
-                    if ((l & 31) == 0) Ap[mi][c0 + 8 * q + e] = a;
-                }
+                for (int e = 0; e < 4; ++e) x[4 * q + e] = qv[e] * ex2(bS[qs * D + c0 + 8 * q + e]) * dq[k][4 * q + e];
             }
+            const float a = half_colsum16(x, l);
+            if (!(l & 1)) Ap[mi][ni * 32 + crow((l >> 1) & 15, l)] = a;
             // 2^(b_mI) of each column
 #pragma unroll
             for (int r = 0; r < 16; ++r) dq[k][r] *= ex2(bS[mi * 32 * D + ni * 32 + crow(r, l)]);
@@ -1432,6 +1450,7 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_walk_kv(Param
             int mi, ni;
             if (!TO::get(k, mi, ni, owave())) continue;
             const int i = mi * 32 + (l & 31), mJ = mi * 32 + 31, c0 = ni * 32 + (l >> 5) * 4;
+            float x[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float kv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1440,11 +1459,12 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_walk_kv(Param
                 for (int e = 0; e < 4; ++e) {
                     const int c = c0 + 8 * q + e;
                     const float bl = bS[(GC - 1) * D + c];
-                    const float ep = half_sum(kv[e] * ex2(bl - bS[i * D + c]) * dk[k][4 * q + e]);
-                    if ((l & 31) == 0) Ep[mi][c] = ep;
+                    x[4 * q + e] = kv[e] * ex2(bl - bS[i * D + c]) * dk[k][4 * q + e];
                     dk[k][4 * q + e] *= ex2(bl - bS[mJ * D + c]);
                 }
             }
+            const float ep = half_colsum16(x, l);
+            if (!(l & 1)) Ep[mi][ni * 32 + crow((l >> 1) & 15, l)] = ep;
         }
         __syncthreads();   // R's parts have been read
         T *dOr = U + L::ROWS;   // D_^T = V dO^T (upper tiles), then Q^T in three versions
