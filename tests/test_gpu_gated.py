@@ -96,6 +96,29 @@ def test_gated_medium_multi_segment():
     check(w.name, run_gated(inp, seg=8), oracle_gated(inp), TOL["bf16"])
 
 
+CKPT = [
+    (16, small("gated fp32 d64 41 chunks Min dMout", "fp32", B=1, H=2, N=64 * 40 + 13, d=64, seed=80,
+               gates="mixed", m_in_scale=0.1, dm_out_scale=0.1)),
+    (17, small("gated bf16 d128 41 chunks Min dMout", "bf16", B=1, H=2, N=64 * 40 + 13, d=128, seed=81,
+               gates="gla", m_in_scale=0.1, dm_out_scale=0.1)),
+    (9, small("gated bf16 packed d64", "bf16", H=2, d=64, seed=82, gates="mixed",
+              lengths=[700, 1100, 64 * 8, 1], m_in_scale=0.1, dm_out_scale=0.1)),
+]
+
+
+@pytest.mark.parametrize("G,w", CKPT, ids=["G%d %s" % (g, w.name) for g, w in CKPT])
+def test_gated_checkpointed_segments(G, w):
+    """Segments long enough to hold forward-state checkpoints (every 8 chunks
+    inside a segment), where the reverse walk resets its log-gate gradient
+    carry: G = 16 puts the second one on the segment end (none kept there),
+    G = 17 keeps two per full segment and none in the short last one, G = 9
+    one per full segment of a packed batch.  Every element against the
+    oracle."""
+    say("case:", w.name, "G", G)
+    inp = make_inputs(w)
+    check("%s G=%d" % (w.name, G), run_gated(inp, seg=G), oracle_gated(inp), TOL[w.dtype])
+
+
 def test_gated_recompute_equals_cache():
     w = small("gated bf16 d128", "bf16", B=1, H=2, N=900, d=128, seed=71, gates="gla",
               m_in_scale=0.1, dm_out_scale=0.1)
