@@ -395,9 +395,8 @@ __device__ float exact_score(const T *Q, const T *K, const float *bS, int s, int
 }
 
 // ---------------------------------------------------------------------------
-// Forward 1: local states, one workgroup per (segment, head), chunks in order
-// from a zero state at the segment start:
-//   Lc[t] = L, Gc[t] = gate product of the segment's chunks before t;
+// Forward 1: segment totals, one workgroup per (segment, head), chunks in
+// order from a zero state at the segment start:
 //   L = Diag(gam_t) L + (K_t 2^(b_last - b))^T V_t;   Z = L, Gs = all gates.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
@@ -419,7 +418,6 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params 
     const T *K = (const T *)p.K + rb * D;
     const T *Vg = (const T *)p.V + rb * D;
     const float *LG = p.LG + rb * D;
-    const bool store_local = p.Lc && p.G > 1;
 
     f32x16 acc[TL::PER_WAVE];
 #pragma unroll
@@ -439,16 +437,6 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_local(Params 
     for (int t = t0; t < t1; ++t) {
         const int tok = t * GC;
         const int Ct = min(GC, s.len - tok);
-        const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
-        if (store_local) {
-            T *Lt = (T *)p.Lc + ch * D * D;
-#pragma unroll
-            for (int k = 0; k < TL::PER_WAVE; ++k) {
-                int mi, ni;
-                if (TL::get(k, mi, ni, owave())) store_T(acc[k], Lt, D, mi * 32, ni * 32, Ident());
-            }
-        }
-        if (p.Gc && otid() < D) p.Gc[ch * D + otid()] = gcum;
         __syncthreads();
         cumlog_scan<D>(bS, rl);
         __syncthreads();
@@ -852,9 +840,8 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gfwd_walk(Params p
 }
 
 // ---------------------------------------------------------------------------
-// Backward 1: local reverse states, one workgroup per (segment, head), chunks
-// last to first from a zero state at the segment end:
-//   Rc[t] = R, Hc[t] = gate product of the segment's chunks after t;
+// Backward 1: reverse segment totals, one workgroup per (segment, head),
+// chunks last to first from a zero state at the segment end:
 //   R = Diag(gam_t) R + (Q_t 2^b)^T dO_t;   W = R.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
@@ -875,12 +862,10 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params 
     const T *Q = (const T *)p.Q + rb * D;
     const T *dO = (const T *)p.dO + rb * D;
     const float *LG = p.LG + rb * D;
-    const bool store_local = p.Rc && p.G > 1;
 
     f32x16 acc[TL::PER_WAVE];
 #pragma unroll
     for (int k = 0; k < TL::PER_WAVE; ++k) zero(acc[k]);
-    float hcum = 1.f;
 
     const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
     Raw<T, D, GC> rq, ro;   // the next (earlier) chunk's rows, loaded ahead
@@ -894,16 +879,6 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params 
     for (int t = t1 - 1; t >= t0; --t) {
         const int tok = t * GC;
         const int Ct = min(GC, s.len - tok);
-        const int64_t ch = (int64_t)(s.c0 + t) * p.H + h;
-        if (store_local) {
-            T *Rt = (T *)p.Rc + ch * D * D;
-#pragma unroll
-            for (int k = 0; k < TL::PER_WAVE; ++k) {
-                int mi, ni;
-                if (TL::get(k, mi, ni, owave())) store_T(acc[k], Rt, D, mi * 32, ni * 32, Ident());
-            }
-        }
-        if (p.Hc && otid() < D) p.Hc[ch * D + otid()] = hcum;
         __syncthreads();
         cumlog_scan<D>(bS, rl);
         __syncthreads();
@@ -934,7 +909,6 @@ __global__ __launch_bounds__(NTHR, (WgPerCu<T, D>::N)) void k_gbwd_local(Params 
                     gemm<T, GC>(acc[k], QT_s, PT, mi * 32, OT_s, PT, ni * 32, olane());
             }
         }
-        if (otid() < D) hcum *= ex2(bS[(GC - 1) * D + otid()]);
     }
     float *Ws = p.W + ((int64_t)gs * p.H + h) * D * D;
 #pragma unroll

@@ -52,9 +52,7 @@ struct Params {
     // gated form
     const float *LG;   // [B, H, N, D] f32 log-gates (key channels)
     float *dLG;        // [B, H, N, D] f32 log-gate gradient
-    float *Gc;         // [chunks][H][D] f32 or null: gate product of the segment's chunks before each chunk
     float *Gs;         // [segs][H][D] f32: gate product of each segment
-    float *Hc;         // [chunks][H][D] f32 or null: gate product of the segment's chunks after each chunk
     float *Tq;         // [chunks][H][D] f32: per chunk, sum over its tokens of q . (2^b (dO P_t^T))
     float *Pck;        // [segs][H][(G-1)/GATED_CK][D][D] f32: forward states at every GATED_CK-th
                        // chunk boundary inside each segment, [dv][dk]
@@ -74,8 +72,11 @@ hipError_t launch_bwd(const Params &p, bool bf16, hipStream_t stream, hipEvent_t
 // totals, segment scan (Pfin = the summed state), O = Q M.  Backward: (tables),
 // reverse totals, reverse scan (Rfin = the summed gradient state), then
 // dQ = dO M^T, dV = K dM, dK = V dM^T; Pfin must be valid.
-// Gated form (per-token, per-key-channel gates given as logs; chunk 64).  Same kernel sequence and events as launch_fwd /
-// launch_bwd; the forward also fills Gc and Gs, the backward Hc.
+// Gated form (per-token, per-key-channel gates given as logs; chunk 64): segment
+// totals, segment scan (Pseg, Pfin, with the segments' gate products Gs), the
+// output walk; backward: reverse totals, reverse scan, the dQ walk (Tq, Pck),
+// then the dV / dK / dlog_g walk, with the events of launch_fwd / launch_bwd
+// (the two backward walks between the last two).
 hipError_t launch_fwd_gated(const Params &p, bool bf16, bool with_output, hipStream_t stream,
                             hipEvent_t *ev = nullptr);
 hipError_t launch_bwd_gated(const Params &p, bool bf16, hipStream_t stream, hipEvent_t *ev = nullptr);
