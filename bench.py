@@ -62,7 +62,20 @@ def elapsed(L, a, b):
     return ms.value
 
 
-def kernel_work(sh, local_b, seg_b, fin_b):
+def end_segment_tokens(lengths, C, G):
+    """Tokens of the sequences' last segments and of their first segments (G
+    chunks of C tokens; a sequence's last segment may be short)."""
+    last = first = 0
+    for n in lengths:
+        if n > 0:
+            T = -(-n // C)
+            S = -(-T // G)
+            last += n - (S - 1) * G * C
+            first += min(n, G * C)
+    return last, first
+
+
+def kernel_work(sh, local_b, seg_b, fin_b, G=0, lengths=None):
     """Algorithmic HBM bytes and flops per launch of every kernel of a step.
 
     U = token-heads, e = element bytes; local_b / seg_b / fin_b: bytes of the
@@ -70,11 +83,16 @@ def kernel_work(sh, local_b, seg_b, fin_b):
     per-sequence final (float32, bf16 only) state arrays, from the library's
     size queries.  Bytes count every distinct array once:
       local  : reads 2 token arrays (K,V resp. Q,dO), writes the local states
-      scan   : reads and writes the segment states, M_in/M_out (dM_out/dM_in),
-               writes the final states
+      scan   : reads and writes the segment states, M_in/M_out (dM_out/dM_in)
       out    : reads Q,K,V and the segment states, writes O
-      grads  : reads Q,K,V,dO, both segment-state arrays and the final states,
-               writes dQ,dK,dV
+      grads  : reads Q,K,V,dO and both segment-state arrays, writes dQ,dK,dV
+    In the bf16 path (fin_b > 0) the sweeps write the end states: the output
+    sweep M_out and the final states, the gradient sweep dM_in and the reverse
+    final states (and it reads the forward's final states).
+    The bf16 path (fin_b > 0) writes the end states from the sweeps and skips
+    the totals of each sequence's last segment (forward) and first segment
+    (backward): with G (chunks per segment) and the sequence lengths, the
+    local kernels' token reads leave those segments out.
     Flops count the useful causal work per token-head and output role: the
     intra-chunk products over c <= r (2d(C+1) on average: QK^T and SV), the
     inter-chunk product A.X (2d^2) and the state update (2d^2)."""
@@ -84,13 +102,20 @@ def kernel_work(sh, local_b, seg_b, fin_b):
     nS = sh["nseq"] or B
     st_io = nS * H * d * d * 4                    # M_in / M_out, dM_out / dM_in
     role = U * (2 * d * (C + 1) + 4 * d * d)      # one output role (O, dQ, dK or dV)
+    Uf = Ub = U
+    ends = 0                                      # end-state bytes moved from the scans to the sweeps
+    if fin_b:
+        ends = st_io
+        if G:
+            last, first = end_segment_tokens(lengths or [N] * B, C, G)
+            Uf, Ub = U - H * last, U - H * first
     return {
-        "fwd_local": (2 * U * d * e + local_b + seg_b, 2 * U * d * d),
-        "fwd_scan": (2 * seg_b + 2 * st_io + fin_b, seg_b // 2),
-        "fwd_out": (4 * U * d * e + local_b + seg_b, role),
-        "bwd_local": (2 * U * d * e + local_b + seg_b, 2 * U * d * d),
-        "bwd_scan": (2 * seg_b + 2 * st_io, seg_b // 2),
-        "bwd_grads": (7 * U * d * e + 2 * local_b + 2 * seg_b + fin_b, 3 * role),
+        "fwd_local": (2 * Uf * d * e + local_b + seg_b, 2 * Uf * d * d),
+        "fwd_scan": (2 * seg_b + 2 * st_io - ends, seg_b // 2),
+        "fwd_out": (4 * U * d * e + local_b + seg_b + ends + fin_b, role),
+        "bwd_local": (2 * Ub * d * e + local_b + seg_b, 2 * Ub * d * d),
+        "bwd_scan": (2 * seg_b + 2 * st_io - ends, seg_b // 2),
+        "bwd_grads": (7 * U * d * e + 2 * local_b + 2 * seg_b + 2 * fin_b + ends, 3 * role),
     }
 
 
@@ -240,7 +265,9 @@ def main():
     seg_b = cca.fwd_workspace_bytes(S, dt_code, True) - table_b
     fin_b = 0 if sh["dtype"] != "bf16" else -(-(sh["nseq"] or sh["B"]) * sh["H"] * sh["d"] ** 2 * 4 // 256) * 256
     local_b = cca.state_cache_bytes(S, dt_code) - seg_b - fin_b
-    work = kernel_work(sh, local_b, seg_b, fin_b)
+    lengths = None if cu is None else [int(x) for x in (cu[1:] - cu[:-1]).tolist()]
+    G = cca.query_sizes(S, dt_code).segment_chunks
+    work = kernel_work(sh, local_b, seg_b, fin_b, G, lengths)
     dom = max(names, key=lambda k: kms[k])
     bytes_, flops = work[dom]
     t_dom = kms[dom] * 1e-3

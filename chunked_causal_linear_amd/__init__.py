@@ -45,7 +45,7 @@ class Shape(ctypes.Structure):
 
 class Sizes(ctypes.Structure):
     _fields_ = [("state_cache", ctypes.c_size_t), ("fwd_workspace", ctypes.c_size_t * 2),
-                ("bwd_workspace", ctypes.c_size_t * 2)]
+                ("bwd_workspace", ctypes.c_size_t * 2), ("segment_chunks", ctypes.c_int)]
 
 
 def lib():

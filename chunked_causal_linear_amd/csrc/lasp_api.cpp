@@ -236,6 +236,7 @@ int lasp_query_sizes(const lasp_shape *shape, lasp_dtype dtype, int form, int se
     out->fwd_workspace[1] = fwd_ws(pl, true);
     out->bwd_workspace[0] = bwd_ws(pl, false) + extra;
     out->bwd_workspace[1] = bwd_ws(pl, true) + extra;
+    out->segment_chunks = pl.G;
     return LASP_OK;
 }
 

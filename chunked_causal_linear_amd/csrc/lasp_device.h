@@ -210,6 +210,20 @@ __device__ __forceinline__ bool seg_seq(const Params &p, int gs, Seq &s, int &sl
     return gs < p.n_segs_ub;
 }
 
+// With p.end_by_sweep the sweep whose walk ends at a sequence's end writes the
+// state there, and that segment's total is skipped: forwards, the sequence's
+// last segment (when it reaches the sequence's last chunk); backwards, its
+// first.  nS: the sequence's segments, min(s.S, p.n_segs_ub - s.s0).
+__device__ __forceinline__ bool fwd_end_by_sweep(const Params &p, const Seq &s, int nS) {
+    if (!p.end_by_sweep || nS <= 0) return false;
+    const int t0 = (nS - 1) * p.G;
+    const int t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
+    return t1 == s.T && t1 > t0;
+}
+__device__ __forceinline__ bool bwd_end_by_sweep(const Params &p, const Seq &s, int nS) {
+    return p.end_by_sweep && nS > 0 && min(min(p.G, s.T), p.n_chunks_ub - s.c0) > 0;
+}
+
 // First row (token) of sequence s, head h, in the [B, H, N, d] layout.
 __device__ __forceinline__ int64_t row_base(const Params &p, const Seq &s, int h) {
     return p.varlen ? ((int64_t)h * p.N + s.tok0) : (((int64_t)s.i * p.H + h) * p.N);

@@ -49,6 +49,10 @@ struct Params {
     void *dOn;              // [B, H, N, d]: gradient of the un-normalised output
     int dq_forward;         // 1: dQ walks forwards from the entering states even without
                             // decay (no subtraction walk; see the sweep kernel)
+    int end_by_sweep;       // 1 (bf16 causal path): the sweeps write each sequence's end
+                            // states (Pfin and M_out after the forward walk of its last
+                            // segment, Rfin and dM_in after the dV walk of its first), so
+                            // the totals of those segments are neither computed nor scanned
     // gated form
     const float *LG;   // [B, H, N, D] f32 log-gates (key channels)
     float *dLG;        // [B, H, N, D] f32 log-gate gradient

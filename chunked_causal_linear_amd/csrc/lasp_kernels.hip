@@ -167,13 +167,17 @@ __global__ __launch_bounds__(NTHR) void k_fwd_segscan(Params p) {
     float P = p.M_in ? p.M_in[mo] : 0.f;
     const int seg_tokens = p.G * p.C;
     const int nS = min(s.S, p.n_segs_ub - s.s0);
+    // with end_by_sweep the last segment's total is not computed: the state
+    // after it comes from the output sweep
+    const bool by_sweep = fwd_end_by_sweep(p, s, nS);
+    const int nZ = by_sweep ? nS - 1 : nS;
     // the totals are loaded SCAN_BATCH segments at a time, ahead of the
     // stores: one memory latency per batch instead of one per segment
     for (int b0 = 0; b0 < nS; b0 += SCAN_BATCH) {
         float z[SCAN_BATCH];
 #pragma unroll
         for (int j = 0; j < SCAN_BATCH; ++j)
-            z[j] = b0 + j < nS ? p.Z[((int64_t)(s.s0 + b0 + j) * p.H + h) * D * D + e] : 0.f;
+            z[j] = b0 + j < nZ ? p.Z[((int64_t)(s.s0 + b0 + j) * p.H + h) * D * D + e] : 0.f;
 #pragma unroll
         for (int j = 0; j < SCAN_BATCH; ++j) {
             const int sl = b0 + j;
@@ -185,6 +189,7 @@ __global__ __launch_bounds__(NTHR) void k_fwd_segscan(Params p) {
             }
         }
     }
+    if (by_sweep) return;
     if (p.M_out) p.M_out[mo] = P;
     if (p.Pfin) p.Pfin[(int64_t)ih * D * D + e] = P;
 }
@@ -382,11 +387,15 @@ __global__ __launch_bounds__(NTHR) void k_bwd_segscan(Params p) {
     float R = p.dM_out ? p.dM_out[mo] : 0.f;
     const int seg_tokens = p.G * p.C;
     const int nS = min(s.S, p.n_segs_ub - s.s0);
+    // with end_by_sweep the first segment's total is not computed: the state
+    // before it comes from the dV sweep
+    const bool by_sweep = bwd_end_by_sweep(p, s, nS);
+    const int w0 = by_sweep ? 1 : 0;
     for (int b0 = nS - 1; b0 >= 0; b0 -= SCAN_BATCH) {   // batches as in the forward scan
         float wv[SCAN_BATCH];
 #pragma unroll
         for (int j = 0; j < SCAN_BATCH; ++j)
-            wv[j] = b0 - j >= 0 ? p.W[((int64_t)(s.s0 + b0 - j) * p.H + h) * D * D + e] : 0.f;
+            wv[j] = b0 - j >= w0 ? p.W[((int64_t)(s.s0 + b0 - j) * p.H + h) * D * D + e] : 0.f;
 #pragma unroll
         for (int j = 0; j < SCAN_BATCH; ++j) {
             const int sl = b0 - j;
@@ -398,6 +407,7 @@ __global__ __launch_bounds__(NTHR) void k_bwd_segscan(Params p) {
             }
         }
     }
+    if (by_sweep) return;
     if (p.dM_in) p.dM_in[mo] = R;
     if (p.Rfin) p.Rfin[(int64_t)ih * D * D + e] = R;
 }
@@ -925,6 +935,16 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     if (nch <= 0) return;
     const float l2 = DEC ? head_log2_decay(p, h) : 0.f;
     const bool decay = DEC && l2 != 0.f;
+    // The walk ends at the sequence's end (the output walk of its last
+    // segment, the dV walk of its first): with end_by_sweep it carries the
+    // state through its last chunk as well and writes the end state, whose
+    // segment total is then skipped.
+    // fin_ih: that sequence's (sequence, head) index, else -1 (one scalar kept
+    // across the walk).
+    const int nS = min(s.S, p.n_segs_ub - s.s0);
+    const int fin_ih = (role == 0 && sl == nS - 1 && fwd_end_by_sweep(p, s, nS)) ||
+                               (role == 2 && sl == 0 && bwd_end_by_sweep(p, s, nS))
+                           ? s.i * p.H + h : -1;
     // dQ by subtraction, walked backwards, for heads without decay; the
     // separate dQ launch serves calls with a decay array (its heads with
     // lambda = 1 still subtract, so that an all-ones array gives the bits of
@@ -949,7 +969,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     const int64_t seg_off = ((int64_t)(s.s0 + sl) * p.H + h) * D * D;
     const float *seg = role >= 2 ? p.Rseg + seg_off : p.Pseg + seg_off;
     if (sub)   // the state after this segment
-        seg = sl + 1 < min(s.S, p.n_segs_ub - s.s0) ? seg + (int64_t)p.H * D * D
+        seg = sl + 1 < nS ? seg + (int64_t)p.H * D * D
                                                     : p.Pfin + ((int64_t)s.i * p.H + h) * D * D;
     const float sgn = sub ? -1.f : 1.f;
     const float lam = dpow(l2, 1.f);
@@ -1245,9 +1265,9 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
 #pragma unroll 1
     for (int i = 0; i < nch; ++i) {
         const int t = chunk_t(i), Ct = chunk_len(t);
-        // (the state after the segment's last chunk is not needed: the segment
-        // totals come from their own kernel)
-        const bool upd = i + 1 < nch;
+        // (the state after the segment's last chunk is needed only at the
+        // sequence's end; the other segment totals come from their own kernel)
+        const bool upd = i + 1 < nch || fin_ih >= 0;
         // chunk start: this chunk's first group and A rows have landed (only the
         // previous chunk's NDT*2 output stores, issued after them, may still be
         // in flight), every wave has published the state into XS
@@ -1314,7 +1334,36 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
                          rt >= 0 ? Ct - rt * 32 : 0, opaque_lane());
         store_tile_t<D>(acc, Out + ((int64_t)t * p.C + rt * 32) * D, rt >= 0 ? Ct - rt * 32 : 0,
                         opaque_lane(), sub ? 0x80008000u : 0u);
-        if (upd) write_state();
+        if (i + 1 < nch) write_state();
+    }
+    if (fin_ih >= 0) {
+        // the end state: P after the sequence's last token (role 0) or R
+        // before its first (role 2), as Pfin / Rfin ([dv][dk], the tile
+        // layout of the entering state read above) and M_out / dM_in ([dk][dv])
+        const int64_t so = (int64_t)fin_ih * D * D;
+        float *fs = role == 0 ? p.Pfin : p.Rfin;
+        float *api = role == 0 ? p.M_out : p.dM_in;
+        const int lz = opaque_lane();
+        const int lc = lz & 31, lg = lz >> 5;
+#pragma unroll
+        for (int k = 0; k < STW; ++k) {
+            const int tl = w + k * NW;
+            if (tl < NSTT) {
+                const int mi = tl / NDT, ni = tl % NDT;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int dk = mi * 32 + q * 8 + lg * 4, dv = ni * 32 + lc;
+                    if (fs)
+                        *(float4 *)(fs + so + (int64_t)dv * D + dk) =
+                            make_float4(sacc[k][q * 4 + 0], sacc[k][q * 4 + 1], sacc[k][q * 4 + 2],
+                                        sacc[k][q * 4 + 3]);
+                    if (api) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) api[so + (int64_t)(dk + j) * D + dv] = sacc[k][q * 4 + j];
+                    }
+                }
+            }
+        }
     }
     };
     if constexpr (KIND == SWEEP_GRADS) {
@@ -1377,6 +1426,12 @@ __global__ __launch_bounds__(SegTotCfg<D>::NT) void k_segtot_bf16(Params p) {
     if (!seg_seq(p, gs, s, sl)) return;
     const int t0 = sl * p.G, t1 = min(min(t0 + p.G, s.T), p.n_chunks_ub - s.c0);
     if (t1 <= t0) return;
+    {   // a total that the sweeps make unnecessary (they write the end state)
+        const int nS = min(s.S, p.n_segs_ub - s.s0);
+        if (BWD ? (sl == 0 && bwd_end_by_sweep(p, s, nS))
+                : (sl == nS - 1 && fwd_end_by_sweep(p, s, nS)))
+            return;
+    }
     const int tok0 = t0 * p.C;                                     // first token of the segment
     const int L = min(t1 * p.C, s.len) - tok0;                     // tokens in the segment
     const int nsteps = (L + 32 * TPS - 1) / (32 * TPS);
@@ -1858,8 +1913,10 @@ static hipError_t sweep_dispatch(const Params &p, hipStream_t st) {
 }
 
 template <int D>
-static hipError_t fwd_bf16(const Params &p, bool with_output, hipStream_t st, hipEvent_t *ev) {
+static hipError_t fwd_bf16(const Params &p0, bool with_output, hipStream_t st, hipEvent_t *ev) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    Params p = p0;
+    p.end_by_sweep = with_output ? 1 : 0;   // the output sweep writes Pfin and M_out
     if (p.varlen) LASP_TRY(launch_setup(p, st));
     LASP_TRY(rec_event(ev, 0, st));
     LASP_TRY((segtot_launch<D, TOT_F>(p, st)));
@@ -1871,8 +1928,10 @@ static hipError_t fwd_bf16(const Params &p, bool with_output, hipStream_t st, hi
 }
 
 template <int D>
-static hipError_t bwd_bf16(const Params &p, hipStream_t st, hipEvent_t *ev) {
+static hipError_t bwd_bf16(const Params &p0, hipStream_t st, hipEvent_t *ev) {
     constexpr int NB = (D * D + NTHR - 1) / NTHR;
+    Params p = p0;
+    p.end_by_sweep = 1;   // the dV sweep writes Rfin and dM_in
     if (p.varlen) LASP_TRY(launch_setup(p, st));
     LASP_TRY(rec_event(ev, 0, st));
     LASP_TRY((segtot_launch<D, TOT_B>(p, st)));

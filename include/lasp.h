@@ -117,6 +117,8 @@ typedef struct {
     size_t state_cache;        /* bytes of the state cache */
     size_t fwd_workspace[2];   /* forward workspace: [0] without, [1] with a state cache */
     size_t bwd_workspace[2];   /* backward workspace: [0] without, [1] with a state cache */
+    int segment_chunks;        /* G: chunks per segment used (the chunks of the gated
+                                  form count 64 tokens) */
 } lasp_sizes;
 int lasp_query_sizes(const lasp_shape *shape, lasp_dtype dtype, int form, int segment_chunks,
                      lasp_sizes *out);

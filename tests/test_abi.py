@@ -260,6 +260,16 @@ def test_sizes_do_not_depend_on_the_environment(L, monkeypatch):
     assert before == after
 
 
+def test_segment_length_of_the_benchmark_shapes(L):
+    """The library's segment lengths at the benchmark-sized shapes: every
+    segment sweep of a launch in one round of 256 workgroups where the
+    sequences allow it (config 3: 8 segments of 64 chunks per head)."""
+    bf16 = 1
+    assert cca.query_sizes(Shape(1, 32, 131072, 128, 256, 0), bf16).segment_chunks == 64
+    assert cca.query_sizes(Shape(4, 16, 8192, 128, 256, 0), bf16).segment_chunks == 8
+    assert cca.query_sizes(Shape(2, 16, 32768, 128, 256, 0), bf16).segment_chunks == 16
+
+
 def test_query_sizes_agrees_with_the_plain_queries(L):
     """lasp_query_sizes with segment_chunks = 0 reports what the plain size
     queries report (the forward and backward use one plan), and an explicit
@@ -270,8 +280,10 @@ def test_query_sizes_agrees_with_the_plain_queries(L):
                 q = cca.query_sizes(s, dt, form, 0)
                 assert (q.state_cache, q.fwd_workspace[0], q.fwd_workspace[1], q.bwd_workspace[0],
                         q.bwd_workspace[1]) == all_sizes(L, s, dt, form)
+                assert q.segment_chunks >= 1
                 for G in (1, 2, 3, 16):
                     g = cca.query_sizes(s, dt, form, G)
+                    assert g.segment_chunks == G
                     # without a cache buffer, each workspace holds the whole cache
                     assert g.fwd_workspace[0] - g.fwd_workspace[1] == g.state_cache
                     assert g.bwd_workspace[0] - g.bwd_workspace[1] >= g.state_cache

@@ -33,6 +33,24 @@ def test_kernel_work_counts_every_array_once():
     assert work["fwd_out"][1] == role and work["bwd_grads"][1] == 3 * role
 
 
+def test_kernel_work_leaves_out_the_skipped_totals():
+    """With the end states written by the sweeps, the forward totals read no
+    token of a sequence's last segment and the backward totals none of its
+    first."""
+    assert bench.end_segment_tokens([131072], 256, 64) == (16384, 16384)
+    # 300 tokens in chunks of 64: 5 chunks, segments of 2 chunks: 128 | 128 | 44
+    assert bench.end_segment_tokens([300, 0, 1], 64, 2) == (44 + 1, 128 + 1)
+    sh = dict(B=1, H=32, N=131072, d=128, chunk=256, dtype="bf16", nseq=0)
+    U, d, e = 32 * 131072, 128, 2
+    seg_b, fin_b, st = 1 << 20, 1 << 16, 32 * 128 * 128 * 4
+    work = bench.kernel_work(sh, 0, seg_b, fin_b, G=64)
+    assert work["fwd_local"][0] == 2 * (U * 7 // 8) * d * e + seg_b
+    assert work["bwd_local"][0] == 2 * (U * 7 // 8) * d * e + seg_b
+    assert work["fwd_out"][0] == 4 * U * d * e + seg_b + st + fin_b      # M_out, Pfin out
+    assert work["bwd_grads"][0] == 7 * U * d * e + 2 * seg_b + 2 * fin_b + st
+    assert work["fwd_scan"][0] == 2 * seg_b + st                          # M_in in
+
+
 def test_counters_only_for_their_source_and_workload(tmp_path):
     f = tmp_path / "t.json"
     json.dump({"source_sha256": bench.src_sha(), "workload": CONFIGS[3].name,

@@ -205,6 +205,26 @@ def test_recompute_equals_cache_and_determinism():
         assert torch.equal(a[k], c[k]), k     # deterministic reruns
 
 
+@pytest.mark.parametrize("G", [0, 2])
+def test_recompute_without_decay(G):
+    """Without decay the dQ walk of a sequence's last segment starts from the
+    final state, which the output sweep writes when the forward runs with its
+    output and the totals scan writes when the backward recomputes the states:
+    the two results then differ by rounding only, and both meet the bar.  The
+    packed batch has a sequence of one segment, of several, and an empty one."""
+    w = small("bf16 packed d64 C64", "bf16", H=2, d=64, chunk=64, seed=26,
+              lengths=[50, 64 * 7 + 3, 0, 200], m_in_scale=0.1, dm_out_scale=0.1)
+    inp = make_inputs(w)
+    say("case: recompute vs cache, no decay, G", G)
+    ref = oracle_full(inp)
+    a = run_gpu(inp, use_cache=True, seg=G)
+    b = run_gpu(inp, use_cache=False, seg=G)
+    check("cache", a, ref, TOL["bf16"])
+    check("recompute", b, ref, TOL["bf16"])
+    for k in ("O", "M_out", "dK", "dV", "dM_in"):   # no final state involved
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_decay_none_equals_ones():
     w = small("bf16 d64 C64", "bf16", B=1, H=2, N=200, d=64, chunk=64, seed=23)
     inp = make_inputs(w)
