@@ -73,9 +73,11 @@ int make_plan(const lasp_shape *s, lasp_dtype dt, Plan &pl, bool gated = false,
     // G = 16, 32, 48, 64 -> 4.30, 4.24, 5.09, 4.25 ms per forward+backward
     // (48 leaves the second round nearly empty).
     if (gated) {
-        // the gated local-state kernels walk G chunks per (segment, head):
-        // about 2048 of them, segments of 1 to 64 chunks
-        const int64_t g = chunks_ub * s->H / 2048;
+        // the gated walks take G chunks per (segment, head): about 1024 of
+        // them (two rounds of two workgroups per CU at d = 128; measured at
+        // B1 H32 N131072 d128: G = 16, 32, 64, 128 -> 14.42, 14.20, 13.98,
+        // 14.00 ms per forward+backward), segments of 1 to 64 chunks
+        const int64_t g = chunks_ub * s->H / 1024;
         pl.G = (int)(g < 1 ? 1 : (g > 64 ? 64 : g));
     } else {
         const int64_t seqs = pl.varlen ? 1 : s->B;
