@@ -97,6 +97,25 @@ def test_norm_small(w):
     check(w.name, run_norm(inp), oracle_norm(inp), TOL[w.dtype])
 
 
+# Every (dtype, d, chunk, decay) the normalised entry points accept: the bf16
+# forward sweep that normalises its rows is compiled per d, chunk and decay
+# variant, the float32 row-norm pass per d, and the backward runs the gradient
+# sweeps with the forward-walking dQ.  Four chunks and a ragged tail (the
+# library then sweeps segments of one chunk); M_in and dM_out on.
+MATRIX = [(dt, d, C, dec) for dt in ("bf16", "fp32") for d in (32, 64, 128)
+          for C in (64, 128, 256) for dec in ("none", "lightning")]
+
+
+@pytest.mark.parametrize("dt,d,C,dec", MATRIX, ids=["%s-d%d-C%d-%s" % m for m in MATRIX])
+def test_norm_every_accepted_configuration(dt, d, C, dec):
+    w = small("norm %s d%d C%d %s" % (dt, d, C, dec), dt, B=1, H=2, N=3 * C + C // 2 + 7, d=d,
+              chunk=C, seed=2000 + d + C + (dt == "fp32") * 7 + (dec != "none") * 3, decay=dec,
+              m_in_scale=0.1, dm_out_scale=0.1)
+    say("case:", w.name)
+    inp = make_inputs(w)
+    check(w.name, run_norm(inp), oracle_norm(inp), TOL[dt])
+
+
 def test_norm_one_token_bf16_cancellation():
     """One token, no M_in: o = (q.k) v, and the gradient dO of the normalised
     output is orthogonal to o, so dQ = (dO.v) k and dK = (dO.v) q vanish up to
