@@ -73,6 +73,22 @@ def test_bidir_small(w):
     check(w.name, run_bidir(inp), oracle_bidir(inp), TOL[w.dtype])
 
 
+# Every (dtype, d, chunk) the unmasked entry points accept (no decay): the
+# kernels are compiled per d; the chunk sets the segments the totals and the
+# row-block products work on.  Four chunks and a ragged tail in segments of two
+# chunks; M_in and dM_out on.
+MATRIX = [(dt, d, C) for dt in ("bf16", "fp32") for d in (32, 64, 128) for C in (64, 128, 256)]
+
+
+@pytest.mark.parametrize("dt,d,C", MATRIX, ids=["%s-d%d-C%d" % m for m in MATRIX])
+def test_bidir_every_accepted_configuration(dt, d, C):
+    w = small("bidir %s d%d C%d" % (dt, d, C), dt, B=1, H=2, N=3 * C + C // 2 + 7, d=d, chunk=C,
+              seed=3000 + d + C + (dt == "fp32") * 7, m_in_scale=0.1, dm_out_scale=0.1)
+    say("case:", w.name)
+    inp = make_inputs(w)
+    check(w.name, run_bidir(inp, seg=2), oracle_bidir(inp), TOL[dt])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("G", [1, 3])
 def test_bidir_segment_sizes(G, dtype):
