@@ -663,15 +663,22 @@ __global__ __launch_bounds__(NTHR) void k_bwd_grads(Params p) {
 // cannot prove disjoint (it cannot for the transpose reads).  The caller waits
 // (vmcnt) and synchronizes before reading the destination, like for any
 // asynchronous copy.  M0 holds the LDS address; the kernels that use this
-// leave M0 to these copies alone.
-__device__ __forceinline__ void dma16(const void *src, const bf16 *dst) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)dst);
+// leave M0 to these copies alone.  lds: the destination's LDS byte address
+// (the same on every lane), formed from lds_addr of a shared array plus an
+// offset, so that it stays a 32-bit scalar: a generic pointer into LDS would
+// be held in two VGPRs and converted back (with its null check) per copy.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // M0 is clobbered on purpose
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
                  : "memory", "m0");
 #pragma clang diagnostic pop
+}
+
+// LDS byte address of a shared array (a constant once the kernel is laid out).
+__device__ __forceinline__ uint32_t lds_addr(const bf16 *a) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)a;
 }
 
 // s_waitcnt: vmcnt(vm), no wait on the other counters.
@@ -918,6 +925,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     __shared__ __attribute__((aligned(16))) bf16 BG0[NG * 2 * TILE];
     __shared__ __attribute__((aligned(16))) bf16 BG1[NG * 2 * TILE];
 
+    const uint32_t bg0_l = lds_addr(BG0), bg1_l = lds_addr(BG1);
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int rsel = lid % nroles;
     const int rest = lid / nroles;
@@ -991,7 +999,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     // group g of chunk i: 32-token tiles of B and Cv (swizzled rows) into their slots
     auto dma_group = [&](int i, auto G) __attribute__((always_inline)) {
         constexpr int g = decltype(G)::value;
-        bf16 *BG = g == 0 ? BG0 : BG1;
+        const uint32_t bg = g == 0 ? bg0_l : bg1_l;
         const int lz = opaque_lane();
         const int t = chunk_t(i);
         const int tok = t * p.C, Ct = chunk_len(t);
@@ -1005,7 +1013,7 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
                 const int r = slot / PR, pc = (slot % PR) ^ sw_key<D>(r);
                 const int row = tok + min(ct * 32 + r, Ct - 1);   // rows past Ct: a valid row
                 const bf16 *src = (half ? Cv : Bm) + (int64_t)row * D + pc * 8;
-                dma16(src, BG + ti * 2 * TILE + half * TILE + pc0 * 512);
+                dma16(src, bg + 2u * (uint32_t)(ti * 2 * TILE + half * TILE + pc0 * 512));
             }
         }
     };
@@ -1418,6 +1426,7 @@ __global__ __launch_bounds__(SegTotCfg<D>::NT) void k_segtot_bf16(Params p) {
     // the wait below keeps (NSLOT - 2) slots of copies of this wave in flight
     static_assert((NSLOT - 2) * CPW <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(16))) bf16 ring[NSLOT * SLOT];
+    const uint32_t ring_l = lds_addr(ring);
 
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int h = lid % p.H, gs = lid / p.H;
@@ -1453,7 +1462,7 @@ __global__ __launch_bounds__(SegTotCfg<D>::NT) void k_segtot_bf16(Params p) {
     auto issue = [&](int j) __attribute__((always_inline)) {
         int lz = l;
         asm volatile("" : "+v"(lz));
-        bf16 *dst = ring + (j % NSLOT) * SLOT;
+        const uint32_t dst = ring_l + 2u * (uint32_t)((j % NSLOT) * SLOT);
 #pragma unroll
         for (int k = 0; k < CPW; ++k) {
             const int jj = w + k * NW;
@@ -1463,7 +1472,7 @@ __global__ __launch_bounds__(SegTotCfg<D>::NT) void k_segtot_bf16(Params p) {
                 const int r = slot / PR, pc = (slot % PR) ^ sw_key<D>(r);
                 const int row = min((j * TPS + q) * 32 + r, L - 1);
                 dma16((half ? Wm : U) + (int64_t)row * D + pc * 8,
-                      dst + q * 2 * TILE + half * TILE + pc0 * 512);
+                      dst + 2u * (uint32_t)(q * 2 * TILE + half * TILE + pc0 * 512));
             }
         }
     };
