@@ -883,15 +883,17 @@ enum SweepKind {
                        // share their reads of Q, K, V, dO in L2
     // With decay the dQ role walks forwards while dV and dK walk backwards,
     // at other speeds: in one launch the three drift apart and share nothing.
-    // Such calls launch dV, dK and dQ as three single-role kernels: with the
-    // decay arithmetic a kernel holding the dV and dK roles together spills
-    // registers (25 VGPRs at d128 C256, reloaded inside the chunk loop behind
-    // waits that drain the copies in flight), while each role alone compiles
-    // without spills — faster although dV and dK then read Q and dO each.
+    // Such calls launch dV and dK together (each workgroup's body compiled
+    // with its role fixed, so registers are sized per role), then dQ alone.
+    // At C = 64 the two-role kernel spills SGPRs, so there dV and dK run as
+    // single-role launches and read Q and dO each.
     SWEEP_DQ = 2,       // role 1
     SWEEP_DV = 3,       // role 2
     SWEEP_OUT_NORM = 4, // role 0, rows normalised (Norm of LASP Eq. 2) in the store
-    SWEEP_DK = 5        // role 3
+    SWEEP_DK = 5,       // role 3
+    SWEEP_DVDK = 6      // roles 2 and 3 (dV, dK), neighbours in launch order: both
+                        // walk backwards at one speed and share their reads of
+                        // Q and dO in L2
 };
 // The role of a sweep workgroup: fixed at compile time, or the launch's
 // first role plus the workgroup's index within the launch's roles.
@@ -907,8 +909,8 @@ struct RoleOf {
 template <int D, int C, int KIND, bool DEC>
 __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
     constexpr int role0 = KIND == SWEEP_GRADS || KIND == SWEEP_DQ ? 1
-                          : KIND == SWEEP_DV ? 2 : KIND == SWEEP_DK ? 3 : 0;   // OUT, OUT_NORM: 0
-    constexpr int nroles = KIND == SWEEP_GRADS ? 3 : 1;
+                          : KIND == SWEEP_DV || KIND == SWEEP_DVDK ? 2 : KIND == SWEEP_DK ? 3 : 0;   // OUT, OUT_NORM: 0
+    constexpr int nroles = KIND == SWEEP_GRADS ? 3 : KIND == SWEEP_DVDK ? 2 : 1;
     using Cfg = SweepCfg<C>;
     constexpr int NCT = Cfg::NCT, NW = Cfg::NW, NG = Cfg::NG;
     constexpr int PR = D / 8, KS = D / 16, NDT = D / 32;
@@ -1378,6 +1380,9 @@ __global__ __launch_bounds__(SweepCfg<C>::NT) void k_sweep_bf16(Params p) {
         if (rsel == 0) body(FixedRole<1>());
         else if (rsel == 1) body(FixedRole<2>());
         else body(FixedRole<3>());
+    } else if constexpr (KIND == SWEEP_DVDK) {
+        if (rsel == 0) body(FixedRole<2>());
+        else body(FixedRole<3>());
     } else if constexpr (KIND == SWEEP_DV || KIND == SWEEP_DK) {
         body(FixedRole<role0>());
     } else {
@@ -1822,10 +1827,15 @@ static hipError_t sweep_launch(const Params &p, hipStream_t st) {
     }
     if (p.decay || (KIND == SWEEP_GRADS && p.dq_forward)) {
         if constexpr (KIND == SWEEP_GRADS) {
-            LASP_TRY(launch_k(k_sweep_bf16<D, C, SWEEP_DV, true>, dim3(round8(p.n_segs_ub * p.H)), block,
-                              st, p));
-            LASP_TRY(launch_k(k_sweep_bf16<D, C, SWEEP_DK, true>, dim3(round8(p.n_segs_ub * p.H)), block,
-                              st, p));
+            if constexpr (C >= 128) {   // dV and dK in one launch (C = 64: it spills SGPRs)
+                LASP_TRY(launch_k(k_sweep_bf16<D, C, SWEEP_DVDK, true>,
+                                  dim3(round8(p.n_segs_ub * p.H * 2)), block, st, p));
+            } else {
+                LASP_TRY(launch_k(k_sweep_bf16<D, C, SWEEP_DV, true>, dim3(round8(p.n_segs_ub * p.H)),
+                                  block, st, p));
+                LASP_TRY(launch_k(k_sweep_bf16<D, C, SWEEP_DK, true>, dim3(round8(p.n_segs_ub * p.H)),
+                                  block, st, p));
+            }
             return launch_k(k_sweep_bf16<D, C, SWEEP_DQ, true>, dim3(round8(p.n_segs_ub * p.H)), block,
                             st, p);
         } else {
